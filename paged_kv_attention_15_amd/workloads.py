@@ -1,0 +1,352 @@
+"""Seeded synthetic inputs for paged-KV attention.
+
+This module only draws random numbers and lays them out in memory: it rounds
+fp32 draws to the storage dtypes (bf16, OCP e4m3) and scatters per-request KV
+rows into a shuffled page pool with a block table.  It holds none of the
+attention arithmetic, so both the CPU oracle and the HIP path can consume its
+arrays without sharing any code with each other.
+
+Layout facts it follows (cited from the pages):
+  * flashinfer.cake_fmha API page, paragraph on the BF16 context profiles and
+    the FP8 qualification: HND pages, a shared K/V page table, page sizes 32 /
+    64, a batch-four q511/KV2047 context profile.
+  * PR #5952 page (fused QK RMSNorm + RoPE + paged KV append), summary: a dense
+    [B, max_pages] page table; FP8 append contract (PR #5956 section
+    "Contract"): NHD caches [num_pages, page_size, Hkv, D], K/V stored as
+    x / scale with round-to-nearest saturating e4m3 (max 448), seq_lens is the
+    total length including the rows being appended.
+  * PR #4557 page, MLA decode description: one latent KV head, 512 latent +
+    64 rope channels, V is the latent part of the same row.
+
+Draw order for every workload: seq_lens (ragged workloads only), then the
+page permutation, then Q, K and V, each standard normal in fp32, from one
+numpy.random.default_rng(seed).
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Dict, Optional
+
+import numpy as np
+
+# dtype tags shared by the binding, the oracle wrapper and the tests
+F32, BF16, E4M3 = "f32", "bf16", "e4m3"
+HND, NHD = "HND", "NHD"
+
+E4M3_MAX = 448.0
+_NAN_BITS = {BF16: np.uint16(0x7FC0), E4M3: np.uint8(0x7F)}
+
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """fp32 -> bf16 bit patterns, round to nearest even (inputs are finite)."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    rounded = u + (np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1)))
+    return (rounded >> np.uint32(16)).astype(np.uint16)
+
+
+def e4m3_bytes(x: np.ndarray) -> np.ndarray:
+    """fp32 -> OCP e4m3 ("fn", max 448) bytes, round to nearest even, saturated.
+
+    Uses torch's float8_e4m3fn cast as the rounding primitive after clamping to
+    the finite range (the pages' "RN satfinite" storage rule)."""
+    import torch
+
+    t = torch.from_numpy(np.clip(np.ascontiguousarray(x, dtype=np.float32), -E4M3_MAX, E4M3_MAX))
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def _store(x: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == F32:
+        return np.ascontiguousarray(x, dtype=np.float32)
+    if dtype == BF16:
+        return bf16_bits(x)
+    raise ValueError(dtype)
+
+
+def _nan_fill(arr: np.ndarray, dtype: str) -> None:
+    if dtype == F32:
+        arr[...] = np.float32(np.nan)
+    else:
+        arr[...] = _NAN_BITS[dtype]
+
+
+def _np_storage(dtype: str):
+    return {F32: np.float32, BF16: np.uint16, E4M3: np.uint8}[dtype]
+
+
+@dataclasses.dataclass
+class Problem:
+    """One paged attention call, held in host memory.
+
+    Arrays hold raw storage: float32 values, uint16 bf16 bit patterns or uint8
+    e4m3 codes.  Shapes:
+      q            [T_q, Hq, D_qk]       rows of request b are q_indptr[b]..q_indptr[b+1]
+      k_pool       HND [num_pages, Hkv, P, D_qk]  or  NHD [num_pages, P, Hkv, D_qk]
+      v_pool       same with D_v, or None when V is the first D_v channels of K (MLA)
+      block_tables int32 [B, max_pages]  (shared by K and V)
+      seq_lens     int32 [B]  total KV length, including the request's own q rows
+      q_indptr     int32 [B+1]
+    """
+
+    name: str
+    batch: int
+    num_qo_heads: int
+    num_kv_heads: int
+    head_dim_qk: int
+    head_dim_v: int
+    page_size: int
+    layout: str
+    q_dtype: str
+    kv_dtype: str
+    o_dtype: str
+    q: np.ndarray
+    k_pool: np.ndarray
+    v_pool: Optional[np.ndarray]
+    block_tables: np.ndarray
+    seq_lens: np.ndarray
+    q_indptr: np.ndarray
+    scale: float
+    k_scale: float = 1.0
+    v_scale: float = 1.0
+    causal: bool = True
+    is_decode: bool = True      # uniform q rows per request (decode / speculative rows)
+    mla: bool = False           # V shares the K rows
+    num_splits: int = 0         # 0 = let the planner choose
+
+    @property
+    def num_pages(self) -> int:
+        return int(self.k_pool.shape[0])
+
+    @property
+    def max_pages(self) -> int:
+        return int(self.block_tables.shape[1])
+
+    @property
+    def q_len(self) -> int:
+        """Uniform q rows per request (decode); for context, the maximum."""
+        d = np.diff(self.q_indptr)
+        return int(d.max()) if d.size else 0
+
+    @property
+    def total_q(self) -> int:
+        return int(self.q_indptr[-1])
+
+    @property
+    def max_kv_len(self) -> int:
+        return int(self.seq_lens.max()) if self.seq_lens.size else 0
+
+    def kv_bytes(self) -> int:
+        """Algorithmic KV bytes: every visible token of every request once per
+        KV head (MLA rows counted once since V shares them)."""
+        eb = {F32: 4, BF16: 2, E4M3: 1}[self.kv_dtype]
+        per_tok = self.head_dim_qk * eb if self.mla else (self.head_dim_qk + self.head_dim_v) * eb
+        return int(self.seq_lens.astype(np.int64).sum()) * self.num_kv_heads * per_tok
+
+    def flops(self) -> int:
+        """2*(D_qk + D_v) per visible (query row, head, key) triple."""
+        total = 0
+        for b in range(self.batch):
+            n = int(self.q_indptr[b + 1] - self.q_indptr[b])
+            L = int(self.seq_lens[b])
+            for i in range(n):
+                c = (L - n + i + 1) if self.causal else L
+                total += max(0, min(c, L))
+        return 2 * (self.head_dim_qk + self.head_dim_v) * self.num_qo_heads * total
+
+
+def make_problem(
+    *,
+    name: str,
+    seed: int,
+    batch: int,
+    seq_lens,
+    q_lens,
+    num_qo_heads: int,
+    num_kv_heads: int,
+    head_dim_qk: int,
+    head_dim_v: int,
+    page_size: int,
+    layout: str = HND,
+    q_dtype: str = BF16,
+    kv_dtype: str = BF16,
+    o_dtype: Optional[str] = None,
+    scale: Optional[float] = None,
+    causal: bool = True,
+    is_decode: bool = True,
+    mla: bool = False,
+    poison: bool = False,
+    extra_page_frac: float = 0.0,
+    table_slack_pages: int = 0,
+    rng: Optional[np.random.Generator] = None,
+    num_splits: int = 0,
+) -> Problem:
+    """Draw one problem.  `seq_lens` / `q_lens` are int sequences of length B.
+
+    poison=True fills page tails (tokens >= L in a request's last page), the
+    extra pages and the unused block-table slots' target pages with NaN, so a
+    kernel that reads anything it should not turns the output non-finite."""
+    if rng is None:
+        rng = np.random.default_rng(seed)
+    seq_lens = np.asarray(seq_lens, dtype=np.int32).reshape(batch)
+    q_lens = np.asarray(q_lens, dtype=np.int32).reshape(batch)
+    q_indptr = np.zeros(batch + 1, dtype=np.int32)
+    q_indptr[1:] = np.cumsum(q_lens)
+    P = page_size
+    Hkv = num_kv_heads
+    pages_per_req = [(int(L) + P - 1) // P for L in seq_lens]
+    needed = int(sum(pages_per_req))
+    extra = int(math.ceil(needed * extra_page_frac))
+    if poison and extra == 0:
+        extra = 1
+    num_pages = needed + extra
+    max_pages = max(pages_per_req + [1]) + table_slack_pages
+
+    perm = rng.permutation(num_pages).astype(np.int32)
+
+    if o_dtype is None:
+        o_dtype = q_dtype
+    if scale is None:
+        scale = 1.0 / math.sqrt(head_dim_qk)
+
+    T_q = int(q_indptr[-1])
+    q = _store(rng.standard_normal((T_q, num_qo_heads, head_dim_qk), dtype=np.float32), q_dtype)
+
+    # logical page i of the concatenated requests lives at physical page perm[i]
+    def draw_pool(dim: int, dtype_tag: str):
+        store_dtype = F32 if dtype_tag == E4M3 else dtype_tag
+        pool = np.zeros((num_pages, Hkv, P, dim), dtype=_np_storage(store_dtype))
+        chunk = max(1, (1 << 24) // max(1, Hkv * P * dim))
+        for start in range(0, needed, chunk):
+            stop = min(needed, start + chunk)
+            vals = rng.standard_normal((stop - start, Hkv, P, dim), dtype=np.float32)
+            pool[perm[start:stop]] = _store(vals, store_dtype)
+        return pool
+
+    k_pool = draw_pool(head_dim_qk, kv_dtype)
+    v_pool = None if mla else draw_pool(head_dim_v, kv_dtype)
+
+    k_scale = v_scale = 1.0
+    if kv_dtype == E4M3:
+        # per-tensor scalar scale s = max|x| / 448 over the needed pages; stored = x / s
+        used = perm[:needed]
+        k_scale = float(np.abs(k_pool[used]).max()) / E4M3_MAX
+        k_pool = e4m3_bytes(k_pool / np.float32(k_scale))
+        if v_pool is not None:
+            v_scale = float(np.abs(v_pool[used]).max()) / E4M3_MAX
+            v_pool = e4m3_bytes(v_pool / np.float32(v_scale))
+
+    block_tables = np.zeros((batch, max_pages), dtype=np.int32)
+    poison_page = int(perm[needed]) if extra > 0 else 0
+    cursor = 0
+    for b, npg in enumerate(pages_per_req):
+        block_tables[b, :npg] = perm[cursor:cursor + npg]
+        block_tables[b, npg:] = poison_page
+        cursor += npg
+
+    if poison:
+        for pool in (k_pool, v_pool):
+            if pool is None:
+                continue
+            for phys in perm[needed:]:
+                _nan_fill(pool[phys], kv_dtype)
+            cursor = 0
+            for b, npg in enumerate(pages_per_req):
+                L = int(seq_lens[b])
+                if npg > 0 and L % P != 0:
+                    _nan_fill(pool[perm[cursor + npg - 1], :, L % P:, :], kv_dtype)
+                cursor += npg
+
+    if layout == NHD:
+        k_pool = np.ascontiguousarray(k_pool.transpose(0, 2, 1, 3))
+        if v_pool is not None:
+            v_pool = np.ascontiguousarray(v_pool.transpose(0, 2, 1, 3))
+    elif layout != HND:
+        raise ValueError(layout)
+
+    return Problem(
+        name=name, batch=batch, num_qo_heads=num_qo_heads, num_kv_heads=Hkv,
+        head_dim_qk=head_dim_qk, head_dim_v=head_dim_v, page_size=P, layout=layout,
+        q_dtype=q_dtype, kv_dtype=kv_dtype, o_dtype=o_dtype, q=q, k_pool=k_pool,
+        v_pool=v_pool, block_tables=block_tables, seq_lens=seq_lens, q_indptr=q_indptr,
+        scale=float(scale), k_scale=k_scale, v_scale=v_scale, causal=causal,
+        is_decode=is_decode, mla=mla, num_splits=num_splits,
+    )
+
+
+def ragged_log_uniform_lens(rng: np.random.Generator, n: int, lo: int, hi: int) -> np.ndarray:
+    """L = floor(exp(U(ln lo, ln hi))), drawn before anything else."""
+    return np.floor(np.exp(rng.uniform(math.log(lo), math.log(hi), size=n))).astype(np.int32)
+
+
+# ---------------------------------------------------------------------------
+# The five workloads.  Sizes are the method's decode / context profiles; the
+# names say what each one is.
+# ---------------------------------------------------------------------------
+
+def tiny_gqa_fp32(seed: int = 0, poison: bool = True) -> Problem:
+    """B=2, one q row, Hq=8 on one KV head, D=128, pages of 16, L={37,100},
+    fp32 end to end, a 16-page pool (10 used + 6 NaN pages), two KV splits."""
+    return make_problem(
+        name="tiny-gqa-fp32-b2", seed=seed, batch=2, seq_lens=[37, 100], q_lens=[1, 1],
+        num_qo_heads=8, num_kv_heads=1, head_dim_qk=128, head_dim_v=128, page_size=16,
+        q_dtype=F32, kv_dtype=F32, poison=poison, extra_page_frac=0.6, num_splits=2,
+    )
+
+
+def gqa_bf16_b32_kv4096(seed: int = 0, poison: bool = False) -> Problem:
+    """B=32, one q row, Hq=32 / Hkv=8, D=128, HND pages of 32, L=4096, bf16."""
+    return make_problem(
+        name="bf16-gqa-b32-h32x8-kv4096-p32", seed=seed, batch=32, seq_lens=[4096] * 32,
+        q_lens=[1] * 32, num_qo_heads=32, num_kv_heads=8, head_dim_qk=128, head_dim_v=128,
+        page_size=32, q_dtype=BF16, kv_dtype=BF16, poison=poison,
+        extra_page_frac=0.25 if poison else 0.0,
+    )
+
+
+def gqa_fp8_b16_ragged(seed: int = 0, poison: bool = False) -> Problem:
+    """B=16, one q row, Hq=64 / Hkv=8, D=128, HND pages of 64, e4m3 K/V with
+    per-tensor scales, bf16 Q and output, L log-uniform in [512, 32768]."""
+    rng = np.random.default_rng(seed)
+    lens = ragged_log_uniform_lens(rng, 16, 512, 32768)
+    return make_problem(
+        name="fp8-gqa-b16-h64x8-ragged-p64", seed=seed, batch=16, seq_lens=lens, q_lens=[1] * 16,
+        num_qo_heads=64, num_kv_heads=8, head_dim_qk=128, head_dim_v=128, page_size=64,
+        q_dtype=BF16, kv_dtype=E4M3, o_dtype=BF16, poison=poison,
+        extra_page_frac=0.25 if poison else 0.0, rng=rng,
+    )
+
+
+def mla_b512_kv4096(seed: int = 0, q_len: int = 1, batch: int = 512, seq_len: int = 4096,
+                    poison: bool = False) -> Problem:
+    """MLA decode: Hq=128 on one shared latent head, D_qk=576 (512+64),
+    D_v=512 (V = first 512 channels of the K row), pages of 64, bf16,
+    q_len in {1, 2} (speculative rows are causal within the draft)."""
+    return make_problem(
+        name=f"mla-b{batch}-q{q_len}-h128-kv{seq_len}-p64", seed=seed, batch=batch,
+        seq_lens=[seq_len] * batch, q_lens=[q_len] * batch, num_qo_heads=128, num_kv_heads=1,
+        head_dim_qk=576, head_dim_v=512, page_size=64, q_dtype=BF16, kv_dtype=BF16,
+        scale=1.0 / math.sqrt(576.0), mla=True, poison=poison,
+        extra_page_frac=0.25 if poison else 0.0,
+    )
+
+
+def context_b4_q511_kv2047(seed: int = 0, poison: bool = False) -> Problem:
+    """Causal paged context: B=4, 511 new rows per request whose total KV
+    length (including those rows) is 2047, Hq=64 / Hkv=8, D=128, HND pages
+    of 32, bf16, explicit q_indptr {0,511,1022,1533,2044}."""
+    return make_problem(
+        name="ctx-b4-q511-kv2047-h64x8-p32", seed=seed, batch=4, seq_lens=[2047] * 4,
+        q_lens=[511] * 4, num_qo_heads=64, num_kv_heads=8, head_dim_qk=128, head_dim_v=128,
+        page_size=32, q_dtype=BF16, kv_dtype=BF16, is_decode=False, poison=poison,
+        extra_page_frac=0.25 if poison else 0.0,
+    )
+
+
+WORKLOADS: Dict[str, callable] = {
+    "tiny-gqa-fp32": tiny_gqa_fp32,
+    "bf16-gqa-b32-kv4096": gqa_bf16_b32_kv4096,
+    "fp8-gqa-b16-ragged": gqa_fp8_b16_ragged,
+    "mla-b512-kv4096": mla_b512_kv4096,
+    "ctx-b4-q511-kv2047": context_b4_q511_kv2047,
+}

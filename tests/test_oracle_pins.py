@@ -1,0 +1,323 @@
+"""Pins for the CPU oracle (no GPU).
+
+Each test ties the oracle to something other than itself: a dense unpaged
+brute force, torch's fp64 scaled_dot_product_attention, closed forms,
+invariants of the method, torch's e4m3 decoding, or values fixed by the
+pages (tests/golden).  Together they are chosen so that a dropped term, a
+wrong sign, a wrong index or a transposed operand in the oracle fails at
+least one of them (tests/test_oracle_mutations.py checks exactly that).
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from paged_kv_attention_15_amd import workloads as W
+from tests import _refs as R
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rand_dense(rng, B, Hkv, lens, Dqk, Dv, T_q, Hq):
+    ks = [rng.standard_normal((Hkv, L, Dqk)).astype(np.float32) for L in lens]
+    vs = [rng.standard_normal((Hkv, L, Dv)).astype(np.float32) for L in lens]
+    q = rng.standard_normal((T_q, Hq, Dqk)).astype(np.float32)
+    return ks, vs, q
+
+
+# --------------------------------------------------------------------------
+# storage decoding
+# --------------------------------------------------------------------------
+
+def test_e4m3_all_codes_match_torch():
+    table = oracle.e4m3_table()
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(table), nan)
+    assert np.flatnonzero(nan).tolist() == [0x7F, 0xFF]
+    assert np.array_equal(table[~nan], ref[~nan])
+
+
+def test_e4m3_golden_points():
+    g = json.load(open(os.path.join(GOLD, "e4m3_points.json")))
+    for pt in g["points"]:
+        assert oracle.e4m3_to_double(int(pt["code"], 16)) == pt["value"], pt
+    for c in g["nan_codes"]:
+        assert math.isnan(oracle.e4m3_to_double(int(c, 16)))
+    assert max(abs(v) for v in oracle.e4m3_table() if not math.isnan(v)) == 448.0
+
+
+def test_bf16_decode_matches_torch():
+    rng = np.random.default_rng(3)
+    bits = rng.integers(0, 1 << 16, size=4000, dtype=np.uint32).astype(np.uint16)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    got = np.array([oracle.bf16_to_double(int(b)) for b in bits])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+
+
+# --------------------------------------------------------------------------
+# paging: oracle over pages == dense brute force over the pre-scatter arrays
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("layout", [W.HND, W.NHD])
+@pytest.mark.parametrize("P", [1, 5, 16])
+def test_paged_equals_dense_bruteforce(layout, P):
+    rng = np.random.default_rng(10 + P)
+    lens, Hq, Hkv, D, Dv = [37, 1, 100, 16], 6, 2, 24, 20
+    ks, vs, q = _rand_dense(rng, 4, Hkv, lens, D, Dv, 4, Hq)
+    prob = R.paged_problem_from_dense(ks, vs, q, lens, [1] * 4, P, rng=rng, layout=layout)
+    out, lse = oracle.attention(prob)
+    for b, L in enumerate(lens):
+        ref_o, ref_l = R.dense_attention(q[b:b + 1].astype(np.float64), ks[b].astype(np.float64),
+                                         vs[b].astype(np.float64), prob.scale)
+        np.testing.assert_allclose(out.reshape(4, Hq, Dv)[b], ref_o[0], rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(lse.reshape(4, Hq)[b], ref_l[0], rtol=1e-12, atol=1e-13)
+
+
+def test_tiny_workload_matches_dense_gather_reference():
+    prob = W.tiny_gqa_fp32(poison=True)
+    out, lse = oracle.attention(prob)
+    ref_o, ref_l = R.problem_dense_reference(prob)
+    assert np.isfinite(out).all()
+    np.testing.assert_allclose(out, ref_o.reshape(out.shape), rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(lse, ref_l.reshape(lse.shape), rtol=1e-12, atol=1e-13)
+
+
+def test_poisoned_tails_and_pages_do_not_change_result():
+    a = W.tiny_gqa_fp32(poison=True)
+    b = W.tiny_gqa_fp32(poison=False)
+    oa, la = oracle.attention(a)
+    ob, lb = oracle.attention(b)
+    assert np.isfinite(oa).all()
+    assert np.array_equal(oa, ob) and np.array_equal(la, lb)
+
+
+def test_page_permutation_invariance_bitwise():
+    prob = W.make_problem(name="perm", seed=5, batch=3, seq_lens=[50, 7, 64], q_lens=[1, 1, 1],
+                          num_qo_heads=4, num_kv_heads=2, head_dim_qk=32, head_dim_v=32,
+                          page_size=8, q_dtype=W.BF16, kv_dtype=W.BF16, extra_page_frac=0.5)
+    out, _ = oracle.attention(prob)
+    rng = np.random.default_rng(99)
+    relabel = rng.permutation(prob.num_pages)  # new physical index of old page p
+    k2 = np.empty_like(prob.k_pool)
+    v2 = np.empty_like(prob.v_pool)
+    k2[relabel] = prob.k_pool
+    v2[relabel] = prob.v_pool
+    import dataclasses
+    p2 = dataclasses.replace(prob, k_pool=k2, v_pool=v2,
+                             block_tables=relabel[prob.block_tables].astype(np.int32))
+    out2, _ = oracle.attention(p2)
+    assert np.array_equal(out, out2)
+
+
+def test_hnd_and_nhd_give_identical_results():
+    rng = np.random.default_rng(4)
+    lens = [33, 9]
+    ks, vs, q = _rand_dense(rng, 2, 3, lens, 16, 16, 2, 6)
+    a = R.paged_problem_from_dense(ks, vs, q, lens, [1, 1], 8, rng=np.random.default_rng(1), layout=W.HND)
+    b = R.paged_problem_from_dense(ks, vs, q, lens, [1, 1], 8, rng=np.random.default_rng(1), layout=W.NHD)
+    assert np.array_equal(oracle.attention(a)[0], oracle.attention(b)[0])
+
+
+# --------------------------------------------------------------------------
+# attention values: library routine and closed forms
+# --------------------------------------------------------------------------
+
+def _sdpa(q, k, v, scale, causal=False):
+    # q [n, Hq, D], k/v [Hkv, L, D] fp64 -> [n, Hq, Dv]
+    Hq, Hkv = q.shape[1], k.shape[0]
+    kk = torch.from_numpy(k).repeat_interleave(Hq // Hkv, dim=0)
+    vv = torch.from_numpy(v).repeat_interleave(Hq // Hkv, dim=0)
+    qq = torch.from_numpy(q).permute(1, 0, 2)
+    o = torch.nn.functional.scaled_dot_product_attention(qq, kk, vv, scale=scale, is_causal=causal)
+    return o.permute(1, 0, 2).numpy()
+
+
+def test_decode_matches_torch_sdpa_fp64_with_scales():
+    rng = np.random.default_rng(7)
+    lens, Hq, Hkv, D = [40, 13], 8, 2, 32
+    ks, vs, q = _rand_dense(rng, 2, Hkv, lens, D, D, 2, Hq)
+    ksc, vsc = 0.37, 2.5
+    prob = R.paged_problem_from_dense(ks, vs, q, lens, [1, 1], 16, rng=rng, k_scale=ksc, v_scale=vsc,
+                                      scale=0.11)
+    out, _ = oracle.attention(prob)
+    out = out.reshape(2, Hq, D)
+    for b in range(2):
+        ref = _sdpa(q[b:b + 1].astype(np.float64), ks[b].astype(np.float64) * ksc,
+                    vs[b].astype(np.float64) * vsc, 0.11)
+        np.testing.assert_allclose(out[b], ref[0], rtol=1e-11, atol=1e-12)
+
+
+def test_full_causal_block_matches_sdpa_is_causal():
+    # q_len == seq_len: every key is one of the request's own rows -> plain causal self-attention
+    rng = np.random.default_rng(8)
+    L, Hq, Hkv, D = 21, 4, 2, 16
+    ks, vs, q = _rand_dense(rng, 1, Hkv, [L], D, D, L, Hq)
+    prob = R.paged_problem_from_dense(ks, vs, q, [L], [L], 4, rng=rng, causal=True)
+    out, _ = oracle.attention(prob)
+    ref = _sdpa(q.astype(np.float64), ks[0].astype(np.float64), vs[0].astype(np.float64), prob.scale,
+                causal=True)
+    np.testing.assert_allclose(out.reshape(L, Hq, D), ref, rtol=1e-11, atol=1e-12)
+
+
+def test_ragged_context_matches_bruteforce():
+    rng = np.random.default_rng(9)
+    lens, qls, Hq, Hkv, D = [70, 33], [20, 3], 4, 2, 16
+    ks, vs, q = _rand_dense(rng, 2, Hkv, lens, D, D, sum(qls), Hq)
+    prob = R.paged_problem_from_dense(ks, vs, q, lens, qls, 16, rng=rng, causal=True)
+    out, lse = oracle.attention(prob)
+    ref_o, ref_l = R.problem_dense_reference(prob)
+    np.testing.assert_allclose(out, ref_o.reshape(out.shape), rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(lse, ref_l.reshape(lse.shape), rtol=1e-12, atol=1e-13)
+
+
+def test_causal_rule_golden():
+    g = json.load(open(os.path.join(GOLD, "causal_rule.json")))
+    for case in g["cases"]:
+        L, n, i = case["seq_len"], case["q_len"], case["row"]
+        # one head, D=1, q=0 so every visible key has weight 1; V[j] = j -> out = mean of visible j
+        ks = [np.zeros((1, L, 1), np.float32)]
+        vs = [np.arange(L, dtype=np.float32).reshape(1, L, 1)]
+        q = np.zeros((n, 1, 1), np.float32)
+        prob = R.paged_problem_from_dense(ks, vs, q, [L], [n], 64, rng=np.random.default_rng(0))
+        out, _ = oracle.attention(prob, np.array([[i, 0]]))
+        c = case["visible"]
+        assert out[0, 0] == pytest.approx((c - 1) / 2.0, abs=1e-9), case
+
+
+def test_single_key_returns_scaled_value_row_exactly():
+    rng = np.random.default_rng(11)
+    ks, vs, q = _rand_dense(rng, 1, 1, [1], 8, 8, 1, 2)
+    prob = R.paged_problem_from_dense(ks, vs, q, [1], [1], 4, rng=rng, v_scale=3.0, k_scale=0.5)
+    out, lse = oracle.attention(prob)
+    assert np.array_equal(out[0], 3.0 * vs[0][0, 0].astype(np.float64))
+    s0 = prob.scale * 0.5 * float(np.dot(q[0, 0].astype(np.float64), ks[0][0, 0].astype(np.float64)))
+    assert lse[0] == pytest.approx(s0, rel=1e-14, abs=1e-14)
+
+
+def test_two_keys_closed_form():
+    # softmax over two logits = sigmoid of their difference
+    q = np.array([[[1.0, 2.0]]], np.float32)
+    k = [np.array([[[0.5, -1.0], [2.0, 0.25]]], np.float32)]
+    v = [np.array([[[1.0, 0.0], [0.0, 1.0]]], np.float32)]
+    prob = R.paged_problem_from_dense(k, v, q, [2], [1], 1, rng=np.random.default_rng(0), scale=0.7)
+    out, lse = oracle.attention(prob)
+    s = 0.7 * np.array([0.5 - 2.0, 2.0 + 0.5])
+    w1 = 1.0 / (1.0 + math.exp(s[0] - s[1]))
+    assert out[0, 0] == pytest.approx(1 - w1, rel=1e-14)
+    assert out[0, 1] == pytest.approx(w1, rel=1e-14)
+    assert lse[0] == pytest.approx(math.log(math.exp(s[0]) + math.exp(s[1])), rel=1e-14)
+
+
+def test_equal_keys_or_zero_query_give_mean_of_values():
+    rng = np.random.default_rng(12)
+    L = 23
+    kz = [np.repeat(rng.standard_normal((1, 1, 8)).astype(np.float32), L, axis=1)]
+    vs = [rng.standard_normal((1, L, 8)).astype(np.float32)]
+    q = rng.standard_normal((1, 3, 8)).astype(np.float32)
+    prob = R.paged_problem_from_dense(kz, vs, q, [L], [1], 5, rng=rng)
+    out, _ = oracle.attention(prob)
+    np.testing.assert_allclose(out, np.repeat(vs[0][0].astype(np.float64).mean(0)[None], 3, 0), rtol=1e-12)
+    ks = [rng.standard_normal((1, L, 8)).astype(np.float32)]
+    prob0 = R.paged_problem_from_dense(ks, vs, np.zeros_like(q), [L], [1], 5, rng=rng)
+    out0, lse0 = oracle.attention(prob0)
+    np.testing.assert_allclose(out0, np.repeat(vs[0][0].astype(np.float64).mean(0)[None], 3, 0), rtol=1e-12)
+    np.testing.assert_allclose(lse0, math.log(L), rtol=1e-14)
+
+
+def test_gqa_head_to_group_map():
+    rng = np.random.default_rng(13)
+    Hq, Hkv, L, D = 12, 3, 9, 4
+    for g_probe in range(Hkv):
+        ks = [rng.standard_normal((Hkv, L, D)).astype(np.float32)]
+        v = np.zeros((Hkv, L, D), np.float32)
+        v[g_probe] = 1.0 + rng.random((L, D)).astype(np.float32)
+        q = rng.standard_normal((1, Hq, D)).astype(np.float32)
+        prob = R.paged_problem_from_dense(ks, [v], q, [L], [1], 4, rng=rng)
+        out, _ = oracle.attention(prob)
+        nonzero = [h for h in range(Hq) if np.abs(out[h]).sum() > 0]
+        assert nonzero == [h for h in range(Hq) if h // (Hq // Hkv) == g_probe]
+
+
+def test_mla_shared_rows_equal_explicit_value_copy():
+    rng = np.random.default_rng(14)
+    lens, Hq, Dqk, Dv = [19, 40], 8, 24, 16
+    ks = [rng.standard_normal((1, L, Dqk)).astype(np.float32) for L in lens]
+    q = rng.standard_normal((4, Hq, Dqk)).astype(np.float32)
+    mla = R.paged_problem_from_dense(ks, None, q, lens, [2, 2], 8, rng=np.random.default_rng(2), mla=True,
+                                     head_dim_v=Dv)
+    vs = [k[:, :, :Dv].copy() for k in ks]
+    sep = R.paged_problem_from_dense(ks, vs, q, lens, [2, 2], 8, rng=np.random.default_rng(2))
+    assert np.array_equal(oracle.attention(mla)[0], oracle.attention(sep)[0])
+
+
+def test_speculative_rows_see_one_more_key_each():
+    # q_len = 2 decode rows of a request with L keys: row 0 sees L-1, row 1 sees L
+    rng = np.random.default_rng(15)
+    L, D = 17, 8
+    ks, vs, q = _rand_dense(rng, 1, 1, [L], D, D, 2, 1)
+    prob = R.paged_problem_from_dense(ks, vs, q, [L], [2], 4, rng=rng)
+    out, _ = oracle.attention(prob)
+    for i, c in enumerate([L - 1, L]):
+        ref, _ = R.dense_attention(q[i:i + 1].astype(np.float64), ks[0][:, :c].astype(np.float64),
+                                   vs[0][:, :c].astype(np.float64), prob.scale)
+        np.testing.assert_allclose(out[i], ref[0, 0], rtol=1e-12)
+
+
+def test_no_visible_key_gives_zero_and_neg_inf():
+    rng = np.random.default_rng(16)
+    ks, vs, q = _rand_dense(rng, 1, 1, [2], 4, 4, 3, 1)
+    prob = R.paged_problem_from_dense(ks, vs, q, [2], [3], 4, rng=rng)  # row 0 has c = 0
+    out, lse = oracle.attention(prob)
+    assert np.array_equal(out[0], np.zeros(4)) and lse[0] == -np.inf
+    assert np.isfinite(out[1:]).all()
+
+
+# --------------------------------------------------------------------------
+# Split-KV + LSE merge identity
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("S", [1, 2, 3, 16, 40])
+def test_split_merge_equals_unsplit(S):
+    prob = W.make_problem(name="split", seed=20 + S, batch=3, seq_lens=[37, 100, 5], q_lens=[2, 2, 2],
+                          num_qo_heads=4, num_kv_heads=1, head_dim_qk=32, head_dim_v=32, page_size=16,
+                          q_dtype=W.F32, kv_dtype=W.F32)
+    full_o, full_l = oracle.attention(prob)
+    o_part, l_part = oracle.attention_split(prob, S)
+    mo, ml = oracle.merge(o_part, l_part)
+    np.testing.assert_allclose(mo, full_o, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(ml, full_l, rtol=1e-12, atol=1e-13)
+    if S >= 16:
+        assert np.isneginf(l_part).any()  # empty partitions carry no weight
+
+
+def test_split_boundaries_are_page_aligned_for_tiny_workload():
+    # L=37 pages of 16 -> 3 pages -> 2 per split: [0,32) + [32,37); L=100 -> 7 pages -> 4 per split
+    prob = W.tiny_gqa_fp32(poison=False)
+    o_part, l_part = oracle.attention_split(prob, 2)
+    for b, cut in [(0, 32), (1, 64)]:
+        pairs = np.array([[b, 0]])
+        L = int(prob.seq_lens[b])
+        lo, _ = oracle.attention_split(prob, 2, pairs)
+        # partition 0 alone equals attention over the first `cut` keys
+        import dataclasses
+        trunc = dataclasses.replace(prob, seq_lens=np.array([cut if i == b else int(prob.seq_lens[i])
+                                                             for i in range(prob.batch)], np.int32))
+        ref, _ = oracle.attention(trunc, pairs)
+        np.testing.assert_allclose(lo[0, 0], ref[0], rtol=1e-12)
+        assert L > cut
+
+
+def test_merge_with_all_empty_partitions():
+    o = np.zeros((3, 2, 4))
+    l = np.full((3, 2), -np.inf)
+    mo, ml = oracle.merge(o, l)
+    assert np.array_equal(mo, np.zeros((2, 4))) and np.isneginf(ml).all()
