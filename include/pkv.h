@@ -1,0 +1,206 @@
+/*
+ * pkv.h -- C ABI of libpkv.so, an MI355X (gfx950) paged-KV attention library.
+ *
+ * The library runs batched attention over a paged KV cache: every query row
+ * reads its request's keys and values through a block table of fixed-size,
+ * arbitrarily placed pages, runs an online softmax, and (when the planner
+ * splits the KV range) writes per-partition partial outputs that a separate
+ * log-sum-exp reducer merges.
+ *
+ * The call contract follows the paged decode and context ABIs described on
+ * the flashinfer.cake_fmha API page: query, paged K/V cache (HND or NHD),
+ * block_tables, seq_lens, max_kv_len, the softmax scale and optional scalar
+ * FP8 scales go in; a caller-owned output comes out, enqueued on the caller's
+ * stream.  The MLA form (one latent KV head whose first 512 channels are V)
+ * follows the PR #4557 page's MLA decode description.
+ *
+ * Ownership and threading
+ *   - Every pointer in pkv_args is a DEVICE pointer owned by the caller, except
+ *     the pkv_args struct itself (host memory, read during the call only).
+ *   - The library allocates nothing on the device and never synchronizes the
+ *     host with the device.  Work is enqueued on `stream` (a hipStream_t passed
+ *     as void*; NULL = the null stream) and may still be running on return.
+ *   - Split-KV partials live in a caller-owned workspace whose size comes from
+ *     pkv_workspace_bytes() for the same arguments.
+ *   - Nothing is cached between calls: device values (seq_lens, tables,
+ *     q_indptr) are read by the kernels on every call.
+ *   - Entry points are thread-safe; pkv_last_error() is per host thread.
+ *
+ * Errors
+ *   Host-checkable argument problems return PKV_ERR_INVALID_ARG before anything
+ *   is enqueued.  Shapes or dtypes with no kernel return PKV_ERR_UNSUPPORTED
+ *   (fail closed).  Device values are never trusted for addressing: a request
+ *   uses L = min(seq_lens[b], max_pages_per_seq * page_size) keys, and page
+ *   indices are clamped to [0, num_pages) when num_pages > 0.  A request with
+ *   seq_lens[b] < its query rows, seq_lens[b] > max_pages_per_seq * page_size,
+ *   or a referenced table entry outside [0, num_pages) sets the optional device
+ *   error word (bit flags PKV_DEVERR_*); rows with no visible key produce zeros
+ *   and lse = -inf.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PKV_ABI_VERSION 1
+
+typedef enum pkv_status {
+  PKV_OK = 0,
+  PKV_ERR_INVALID_ARG = 1, /* host-checkable argument violation */
+  PKV_ERR_UNSUPPORTED = 2, /* valid arguments, but no kernel for them (fail closed) */
+  PKV_ERR_WORKSPACE = 3,   /* workspace missing or smaller than pkv_workspace_bytes() */
+  PKV_ERR_HIP = 4          /* a HIP launch or runtime call failed */
+} pkv_status;
+
+typedef enum pkv_dtype {
+  PKV_DTYPE_F32 = 0,
+  PKV_DTYPE_BF16 = 1,
+  PKV_DTYPE_FP8_E4M3 = 2 /* OCP e4m3 ("fn": max 448, no inf, 0x7F/0xFF NaN); KV only */
+} pkv_dtype;
+
+typedef enum pkv_layout {
+  PKV_LAYOUT_HND = 0, /* pool [num_pages, Hkv, page_size, D]: one contiguous block per (page, head) */
+  PKV_LAYOUT_NHD = 1  /* pool [num_pages, page_size, Hkv, D] */
+} pkv_layout;
+
+/* device error word bits (OR-ed; 0 = every request was well formed) */
+#define PKV_DEVERR_SEQ_LT_QLEN 0x1    /* seq_lens[b] smaller than the request's query rows */
+#define PKV_DEVERR_SEQ_GT_TABLE 0x2   /* seq_lens[b] > max_pages_per_seq * page_size (clamped) */
+#define PKV_DEVERR_PAGE_RANGE 0x4     /* a referenced page index outside [0, num_pages) (clamped) */
+#define PKV_DEVERR_QINDPTR 0x8        /* q_indptr not monotone, or rows exceed max_q_len / total_q */
+
+/*
+ * Arguments of one attention call.  Strides are in ELEMENTS of the tensor's
+ * dtype; the innermost (head-dim) stride is always 1.
+ *
+ * Query / output rows.  Decode (pkv_decode): request b owns rows
+ * b*q_len .. b*q_len+q_len-1 (q_len = 1 is plain decode, q_len > 1 are
+ * speculative rows).  Context (pkv_context): request b owns rows
+ * q_indptr[b] .. q_indptr[b+1]-1.  Row t, head h lives at
+ * q + t*q_stride_tok + h*q_stride_head (likewise out / o_stride_*).
+ *
+ * Keys.  seq_lens[b] is the request's total KV length INCLUDING its own query
+ * rows.  With causal != 0, row i (0-based within the request, n rows) sees keys
+ * 0 .. seq_lens[b] - n + i (inclusive); otherwise all seq_lens[b] keys.  Key j
+ * of request b is token j % page_size of page block_tables[b*table_stride + j/page_size];
+ * its K row for KV head g starts at
+ *     k_pages + page*k_stride_page + g*k_stride_head + (j % page_size)*k_stride_tok.
+ * Query head h uses KV head h / (num_qo_heads / num_kv_heads).
+ *
+ * Scores and output:
+ *     s_j = scale * k_scale * <q, k_j>,   out = v_scale * sum_j softmax(s)_j v_j
+ * k_scale / v_scale are 1 except for FP8 KV (stored value = x / scale).  When
+ * k_scale_dev / v_scale_dev are non-NULL they point to device float scalars
+ * that replace k_scale / v_scale.  lse_out (optional, fp32 [total_q, Hq] with
+ * row stride num_qo_heads) receives the natural-log log-sum-exp of the scores.
+ */
+typedef struct pkv_args {
+  int32_t batch;             /* B >= 0; B == 0 is a no-op */
+  int32_t q_len;             /* decode: query rows per request (>= 1); context: ignored */
+  int32_t num_qo_heads;      /* Hq, a multiple of num_kv_heads */
+  int32_t num_kv_heads;      /* Hkv >= 1 */
+  int32_t head_dim_qk;       /* D_qk, multiple of 8 */
+  int32_t head_dim_v;        /* D_v, multiple of 8, <= head_dim_qk when v_shares_k */
+  int32_t page_size;         /* P >= 1 */
+  int32_t max_pages_per_seq; /* readable width of each block-table row */
+  int32_t max_kv_len;        /* host upper bound on seq_lens (sizes the Split-KV plan) */
+  int32_t max_q_len;         /* context: host upper bound on rows per request */
+  int32_t total_q;           /* context: rows of q / out (= q_indptr[B]); decode: ignored */
+  int32_t num_pages;         /* pool size in pages for clamping, 0 = unchecked */
+  int32_t q_dtype;           /* pkv_dtype: F32 or BF16 */
+  int32_t kv_dtype;          /* pkv_dtype: F32, BF16 or FP8_E4M3 */
+  int32_t o_dtype;           /* pkv_dtype: F32 or BF16 */
+  int32_t layout;            /* pkv_layout (only used to validate strides) */
+  int32_t causal;            /* 1: inclusive causal bound for multi-row requests */
+  int32_t num_splits;        /* Split-KV partitions per (request, KV head); 0 = planner */
+  int32_t v_shares_k;        /* 1: V is the first head_dim_v channels of the K rows (MLA) */
+  int32_t reserved0;
+
+  const void* q;
+  const void* k_pages;
+  const void* v_pages;       /* ignored when v_shares_k */
+  const int32_t* block_tables;
+  const int32_t* seq_lens;   /* [B] */
+  const int32_t* q_indptr;   /* context: [B + 1]; decode: ignored */
+  void* out;
+  float* lse_out;            /* optional */
+  int32_t* err_word;         /* optional device word, OR-ed with PKV_DEVERR_* bits */
+  const float* k_scale_dev;  /* optional */
+  const float* v_scale_dev;  /* optional */
+
+  int64_t q_stride_tok, q_stride_head;
+  int64_t o_stride_tok, o_stride_head;
+  int64_t k_stride_page, k_stride_head, k_stride_tok;
+  int64_t v_stride_page, v_stride_head, v_stride_tok;
+  int64_t table_stride;
+
+  float scale;
+  float k_scale;
+  float v_scale;
+  float reserved1;
+} pkv_args;
+
+/* Planner result (host only, no device access). */
+typedef struct pkv_plan_info {
+  int32_t kernel;          /* internal kernel family id (stable within one ABI version) */
+  int32_t num_splits;      /* partitions per (request, KV head) */
+  int32_t pages_per_split; /* page-aligned partition length, in pages */
+  int32_t grid_x, grid_y, grid_z;
+  int32_t block_threads;
+  int32_t reserved;
+  size_t workspace_bytes;  /* 0 when num_splits == 1 */
+} pkv_plan_info;
+
+/* ABI version of the loaded library (PKV_ABI_VERSION of the headers it was built from). */
+int pkv_abi_version(void);
+
+/* Message for the last non-OK status returned on this host thread ("" if none). */
+const char* pkv_last_error(void);
+
+/*
+ * Host-only planning for pkv_decode (is_context = 0) or pkv_context (1):
+ * validates the host-visible arguments, picks the kernel, the Split-KV
+ * partition count sized to the device's compute units (num_cus <= 0 = 256) and
+ * the workspace size.  Pointers are not dereferenced.
+ */
+pkv_status pkv_plan(const pkv_args* args, int is_context, int num_cus, pkv_plan_info* info);
+
+/* Workspace bytes pkv_decode / pkv_context need for these arguments (0 if unsplit). */
+pkv_status pkv_workspace_bytes(const pkv_args* args, int is_context, size_t* bytes);
+
+/*
+ * Paged decode: B requests with q_len uniform query rows each (speculative rows
+ * are causal within the draft when args->causal).  The Split-KV partials go
+ * into `workspace` (device, >= pkv_workspace_bytes bytes, 256-byte aligned) and
+ * are merged by the log-sum-exp reducer in the same call.
+ */
+pkv_status pkv_decode(const pkv_args* args, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Paged causal context (prefill): variable rows per request through args->q_indptr. */
+pkv_status pkv_context(const pkv_args* args, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The log-sum-exp reducer on its own (Split-KV merge, PR #4557 page: split
+ * partitions merged by a separate reducer kernel).
+ *   o_part   fp32 [num_splits, num_rows, head_dim_v], each partition normalized
+ *   lse_part fp32 [num_splits, num_rows] natural log, -inf = empty partition
+ * Row r is (query row r / num_qo_heads, head r % num_qo_heads); the merged
+ * row goes to out + (r / Hq)*o_stride_tok + (r % Hq)*o_stride_head in o_dtype
+ * and its log-sum-exp to lse_out[r] when lse_out is non-NULL.  Rows whose
+ * partitions are all empty produce zeros and -inf.
+ */
+pkv_status pkv_lse_merge(int32_t num_splits, int32_t num_rows, int32_t num_qo_heads,
+                         int32_t head_dim_v, const float* o_part, const float* lse_part,
+                         void* out, int32_t o_dtype, int64_t o_stride_tok, int64_t o_stride_head,
+                         float* lse_out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

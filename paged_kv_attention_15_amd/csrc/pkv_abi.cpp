@@ -1,0 +1,377 @@
+// pkv_abi.cpp -- the extern "C" boundary of libpkv.so: validation, planning, launches.
+//
+// The call contract (query, paged K/V, block tables, seq_lens, max_kv_len,
+// scale and scalar FP8 scales in, caller-owned output out, on the caller's
+// stream) follows the flashinfer.cake_fmha API page; unsupported combinations
+// fail closed with PKV_ERR_UNSUPPORTED as that page's optimized routes do.
+// Nothing here reads device memory, allocates, synchronizes, or caches state
+// keyed on pointers (PR #4557 page: host metadata must stay bound to the
+// tensors of the current call).
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/pkv.h"
+#include "pkv_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+pkv_status fail(pkv_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+pkv_status fail(pkv_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+pkv_status ok() {
+  g_last_error.clear();
+  return PKV_OK;
+}
+
+int elem_bytes(int32_t dt) {
+  switch (dt) {
+    case PKV_DTYPE_F32: return 4;
+    case PKV_DTYPE_BF16: return 2;
+    case PKV_DTYPE_FP8_E4M3: return 1;
+  }
+  return 0;
+}
+
+bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+
+int ilog2(int64_t x) {
+  int l = 0;
+  while ((int64_t(1) << l) < x) ++l;
+  return l;
+}
+
+bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+constexpr int kMaxSplits = 256;
+constexpr int kMaxPagesPerSplit = 4096;  // bounds the LDS page list of the MFMA kernels
+
+// Host-visible argument checks shared by plan / decode / context.
+pkv_status validate(const pkv_args* a, bool is_context) {
+  if (!a) return fail(PKV_ERR_INVALID_ARG, "args is NULL");
+  if (a->batch < 0) return fail(PKV_ERR_INVALID_ARG, "batch must be >= 0 (got %d)", a->batch);
+  if (a->num_kv_heads < 1 || a->num_qo_heads < 1 || a->num_qo_heads % a->num_kv_heads != 0)
+    return fail(PKV_ERR_INVALID_ARG, "num_qo_heads (%d) must be a positive multiple of num_kv_heads (%d)",
+                a->num_qo_heads, a->num_kv_heads);
+  if (a->head_dim_qk < 8 || a->head_dim_qk % 8 != 0 || a->head_dim_v < 8 || a->head_dim_v % 8 != 0)
+    return fail(PKV_ERR_INVALID_ARG, "head dims must be positive multiples of 8 (qk %d, v %d)", a->head_dim_qk,
+                a->head_dim_v);
+  if (a->v_shares_k && a->head_dim_v > a->head_dim_qk)
+    return fail(PKV_ERR_INVALID_ARG, "v_shares_k needs head_dim_v <= head_dim_qk");
+  if (a->page_size < 1) return fail(PKV_ERR_INVALID_ARG, "page_size must be >= 1 (got %d)", a->page_size);
+  if (a->max_pages_per_seq < 0) return fail(PKV_ERR_INVALID_ARG, "max_pages_per_seq must be >= 0");
+  if (a->max_kv_len < 0) return fail(PKV_ERR_INVALID_ARG, "max_kv_len must be >= 0");
+  if ((int64_t)a->max_kv_len > (int64_t)a->max_pages_per_seq * a->page_size)
+    return fail(PKV_ERR_INVALID_ARG, "max_kv_len %d exceeds the table capacity %lld", a->max_kv_len,
+                (long long)a->max_pages_per_seq * a->page_size);
+  if (a->num_pages < 0) return fail(PKV_ERR_INVALID_ARG, "num_pages must be >= 0");
+  if (a->q_dtype != PKV_DTYPE_F32 && a->q_dtype != PKV_DTYPE_BF16)
+    return fail(PKV_ERR_UNSUPPORTED, "q_dtype %d not supported (F32 or BF16)", a->q_dtype);
+  if (a->o_dtype != PKV_DTYPE_F32 && a->o_dtype != PKV_DTYPE_BF16)
+    return fail(PKV_ERR_UNSUPPORTED, "o_dtype %d not supported (F32 or BF16)", a->o_dtype);
+  if (elem_bytes(a->kv_dtype) == 0) return fail(PKV_ERR_UNSUPPORTED, "kv_dtype %d not supported", a->kv_dtype);
+  if (a->layout != PKV_LAYOUT_HND && a->layout != PKV_LAYOUT_NHD)
+    return fail(PKV_ERR_INVALID_ARG, "layout %d unknown", a->layout);
+  if (!(a->scale > 0.f) || !(a->k_scale > 0.f) || !(a->v_scale > 0.f))
+    return fail(PKV_ERR_INVALID_ARG, "scale, k_scale and v_scale must be positive and finite");
+  if (a->num_splits < 0 || a->num_splits > kMaxSplits)
+    return fail(PKV_ERR_INVALID_ARG, "num_splits must be in [0, %d]", kMaxSplits);
+  if (is_context) {
+    if (a->max_q_len < 0 || a->total_q < 0) return fail(PKV_ERR_INVALID_ARG, "max_q_len / total_q must be >= 0");
+  } else {
+    if (a->q_len < 1) return fail(PKV_ERR_INVALID_ARG, "q_len must be >= 1 for decode (got %d)", a->q_len);
+    if ((int64_t)a->q_len > (int64_t)a->max_pages_per_seq * a->page_size && a->batch > 0)
+      return fail(PKV_ERR_INVALID_ARG, "q_len exceeds the table capacity");
+  }
+  // layout consistency of the strides (innermost dimension contiguous)
+  const int64_t D_qk = a->head_dim_qk, D_v = a->head_dim_v, P = a->page_size, H = a->num_kv_heads;
+  auto check_pool = [&](int64_t sp, int64_t sh, int64_t st, int64_t D, const char* name) -> pkv_status {
+    if (sp <= 0 || sh < 0 || st <= 0)
+      return fail(PKV_ERR_INVALID_ARG, "%s strides must be positive", name);
+    if (a->layout == PKV_LAYOUT_HND) {
+      if (st < D || (H > 1 && sh < P * st) || sp < H * std::max<int64_t>(sh, P * st))
+        return fail(PKV_ERR_INVALID_ARG, "%s strides do not describe an HND [pages, Hkv, P, D] pool", name);
+    } else {
+      if ((H > 1 && sh < D) || st < H * std::max<int64_t>(sh, D) || sp < P * st)
+        return fail(PKV_ERR_INVALID_ARG, "%s strides do not describe an NHD [pages, P, Hkv, D] pool", name);
+    }
+    return PKV_OK;
+  };
+  pkv_status st = check_pool(a->k_stride_page, a->k_stride_head, a->k_stride_tok, D_qk, "k");
+  if (st != PKV_OK) return st;
+  if (!a->v_shares_k) {
+    st = check_pool(a->v_stride_page, a->v_stride_head, a->v_stride_tok, D_v, "v");
+    if (st != PKV_OK) return st;
+  }
+  if (a->table_stride < a->max_pages_per_seq)
+    return fail(PKV_ERR_INVALID_ARG, "table_stride %lld < max_pages_per_seq %d", (long long)a->table_stride,
+                a->max_pages_per_seq);
+  if (a->q_stride_head < D_qk || a->q_stride_tok < D_qk)
+    return fail(PKV_ERR_INVALID_ARG, "q strides too small for head_dim_qk");
+  if (a->o_stride_head < D_v || a->o_stride_tok < D_v)
+    return fail(PKV_ERR_INVALID_ARG, "out strides too small for head_dim_v");
+  if (a->batch == 0) return PKV_OK;
+  if (!a->q || !a->k_pages || (!a->v_shares_k && !a->v_pages) || !a->block_tables || !a->seq_lens || !a->out)
+    return fail(PKV_ERR_INVALID_ARG, "q, k_pages, v_pages, block_tables, seq_lens and out are required");
+  if (is_context && !a->q_indptr) return fail(PKV_ERR_INVALID_ARG, "q_indptr is required for context");
+  return PKV_OK;
+}
+
+// Pick the kernel family for host-visible shapes (fail-closed routing: anything
+// the MFMA families cannot prove safe goes to the generic kernel).
+int32_t choose_kernel(const pkv_args* a, bool is_context) {
+  const bool bf16_q = a->q_dtype == PKV_DTYPE_BF16;
+  const bool mfma_kv = a->kv_dtype == PKV_DTYPE_BF16 || a->kv_dtype == PKV_DTYPE_FP8_E4M3;
+  const bool fp8 = a->kv_dtype == PKV_DTYPE_FP8_E4M3;
+  const int eb = elem_bytes(a->kv_dtype);
+  if (!bf16_q || !mfma_kv || !is_pow2(a->page_size)) return pkv::KERNEL_GENERIC;
+  // 16-byte alignment of every row the MFMA kernels load / store as vectors
+  auto al = [&](int64_t stride_elems, int bytes) { return (stride_elems * bytes) % 16 == 0; };
+  if (!aligned16(a->q) || !aligned16(a->k_pages) || !aligned16(a->out)) return pkv::KERNEL_GENERIC;
+  if (!a->v_shares_k && !aligned16(a->v_pages)) return pkv::KERNEL_GENERIC;
+  if (!al(a->q_stride_tok, 2) || !al(a->q_stride_head, 2)) return pkv::KERNEL_GENERIC;
+  const int ob = elem_bytes(a->o_dtype);
+  if ((a->o_stride_tok * ob) % 8 != 0 || (a->o_stride_head * ob) % 8 != 0) return pkv::KERNEL_GENERIC;
+  if (!al(a->k_stride_page, eb) || !al(a->k_stride_head, eb) || !al(a->k_stride_tok, eb)) return pkv::KERNEL_GENERIC;
+  if (!a->v_shares_k && (!al(a->v_stride_page, eb) || !al(a->v_stride_head, eb) || !al(a->v_stride_tok, eb)))
+    return pkv::KERNEL_GENERIC;
+  const int G = a->num_qo_heads / a->num_kv_heads;
+  if (a->head_dim_qk == 128 && a->head_dim_v == 128 && !a->v_shares_k) {
+    const int64_t rows = is_context ? (int64_t)a->max_q_len * G : (int64_t)a->q_len * G;
+    if (!is_context && rows <= 16) return fp8 ? pkv::KERNEL_GQA_FP8 : pkv::KERNEL_GQA_BF16;
+    return fp8 ? pkv::KERNEL_WIDE_FP8 : pkv::KERNEL_WIDE_BF16;
+  }
+  if (a->head_dim_qk == 576 && a->head_dim_v == 512 && a->v_shares_k)
+    return fp8 ? pkv::KERNEL_MLA_FP8 : pkv::KERNEL_MLA_BF16;
+  return pkv::KERNEL_GENERIC;
+}
+
+pkv_status make_plan(const pkv_args* a, bool is_context, int num_cus, pkv_plan_info* info) {
+  pkv_status st = validate(a, is_context);
+  if (st != PKV_OK) return st;
+  if (num_cus <= 0) num_cus = 256;
+  std::memset(info, 0, sizeof *info);
+  const int32_t kernel = choose_kernel(a, is_context);
+  if (kernel == pkv::KERNEL_GENERIC && (a->head_dim_qk > 1024 || a->head_dim_v > 512))
+    return fail(PKV_ERR_UNSUPPORTED, "head dims above 1024 (qk) / 512 (v) have no kernel");
+  info->kernel = kernel;
+  const int G = a->num_qo_heads / a->num_kv_heads;
+  const int64_t rows_per_kv = is_context ? (int64_t)a->max_q_len * G : (int64_t)a->q_len * G;
+  const int64_t total_rows = is_context ? a->total_q : (int64_t)a->batch * a->q_len;
+  const int64_t max_pages = (a->max_kv_len + a->page_size - 1) / a->page_size;
+
+  int tile_tokens = 64, rows_per_block = 1, threads = 64;
+  int64_t units;  // independent (request, KV head, row block) work items before splitting
+  pkv::MfmaShape shp;
+  if (kernel != pkv::KERNEL_GENERIC && pkv::mfma_shape(kernel, &shp)) {
+    tile_tokens = shp.tile_tokens;
+    rows_per_block = shp.rows_per_block;
+    threads = shp.threads;
+    const int64_t rb = std::max<int64_t>(1, (rows_per_kv + rows_per_block - 1) / rows_per_block);
+    units = (int64_t)a->batch * a->num_kv_heads * rb;
+    info->grid_y = (int32_t)(a->num_kv_heads * rb);
+    info->grid_z = a->batch;
+  } else {
+    units = total_rows * a->num_qo_heads;
+    info->grid_x = (int32_t)total_rows;
+    info->grid_y = a->num_qo_heads;
+  }
+
+  // Split-KV sizing: enough partitions that the grid covers the CUs about
+  // twice, each partition a whole number of pages and at least one tile long.
+  int S = a->num_splits;
+  int64_t pps;
+  if (S == 0) {
+    const int64_t want = std::max<int64_t>(1, (2 * (int64_t)num_cus + units - 1) / std::max<int64_t>(units, 1));
+    // at least four tiles per partition
+    const int64_t min_pages = std::max<int64_t>(1, (4 * (int64_t)tile_tokens + a->page_size - 1) / a->page_size);
+    int64_t s_cap = std::max<int64_t>(1, max_pages / min_pages);
+    S = (int)std::min<int64_t>(std::min<int64_t>(want, s_cap), kMaxSplits);
+    S = std::max(S, 1);
+  }
+  pps = std::max<int64_t>(1, (max_pages + S - 1) / S);
+  // round partitions up to whole tiles when pages are smaller than a tile
+  if (a->page_size < tile_tokens) {
+    const int64_t ppt = tile_tokens / a->page_size;
+    pps = (pps + ppt - 1) / ppt * ppt;
+  }
+  if (kernel != pkv::KERNEL_GENERIC) {
+    // the partition's page list sits in LDS after the KV stages: keep the total within 160 KiB
+    const int64_t lds_room = (int64_t)(160 * 1024 - shp.lds_static) / 4 - 8;
+    const int64_t cap_pages = std::min<int64_t>(kMaxPagesPerSplit, lds_room);
+    if (cap_pages < 1) return fail(PKV_ERR_UNSUPPORTED, "no LDS left for the page list");
+    if (pps > cap_pages) pps = cap_pages;
+  }
+  S = (int)std::max<int64_t>(1, (max_pages + pps - 1) / pps);
+  if (a->num_splits > 0 && S < a->num_splits) S = a->num_splits;  // honour an explicit request
+  if (S > kMaxSplits) return fail(PKV_ERR_UNSUPPORTED, "plan needs %d partitions (max %d)", S, kMaxSplits);
+
+  info->num_splits = S;
+  info->pages_per_split = (int32_t)pps;
+  info->block_threads = threads;
+  if (kernel == pkv::KERNEL_GENERIC) {
+    info->grid_z = S;
+  } else {
+    info->grid_x = S;
+  }
+  info->workspace_bytes =
+      S > 1 ? (size_t)S * (size_t)total_rows * a->num_qo_heads * (size_t)(a->head_dim_v + 1) * sizeof(float) + 256
+            : 0;
+  return PKV_OK;
+}
+
+pkv_status run(const pkv_args* a, bool is_context, void* ws, size_t ws_bytes, void* stream) {
+  int dev = 0, cus = 256;
+  pkv_plan_info plan;
+  // CU count of the current device sizes the plan (host query, no device sync)
+  if (hipGetDevice(&dev) == hipSuccess) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
+  }
+  pkv_status st = make_plan(a, is_context, cus, &plan);
+  if (st != PKV_OK) return st;
+  if (a->batch == 0) return ok();
+  if (plan.workspace_bytes > 0) {
+    if (!ws || ws_bytes < plan.workspace_bytes)
+      return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", plan.workspace_bytes, ws_bytes);
+  }
+  const int G = a->num_qo_heads / a->num_kv_heads;
+  const int64_t total_rows = is_context ? a->total_q : (int64_t)a->batch * a->q_len;
+
+  pkv::KParams p;
+  std::memset(&p, 0, sizeof p);
+  p.batch = a->batch;
+  p.q_len = is_context ? 0 : a->q_len;
+  p.num_qo_heads = a->num_qo_heads;
+  p.num_kv_heads = a->num_kv_heads;
+  p.group = G;
+  p.head_dim_qk = a->head_dim_qk;
+  p.head_dim_v = a->head_dim_v;
+  p.page_size = a->page_size;
+  p.log2_page = is_pow2(a->page_size) ? ilog2(a->page_size) : 0;
+  p.max_pages_per_seq = a->max_pages_per_seq;
+  p.num_pages = a->num_pages;
+  p.is_context = is_context ? 1 : 0;
+  p.causal = a->causal ? 1 : 0;
+  p.num_splits = plan.num_splits;
+  p.pages_per_split = plan.pages_per_split;
+  p.row_blocks = 1;
+  if (plan.kernel != pkv::KERNEL_GENERIC) p.row_blocks = plan.grid_y / a->num_kv_heads;
+  p.total_q = is_context ? a->total_q : a->batch * a->q_len;
+  p.max_q_len = is_context ? a->max_q_len : a->q_len;
+  p.q_dtype = a->q_dtype;
+  p.kv_dtype = a->kv_dtype;
+  p.o_dtype = a->o_dtype;
+  p.q = a->q;
+  p.k = a->k_pages;
+  p.v = a->v_shares_k ? a->k_pages : a->v_pages;
+  p.table = a->block_tables;
+  p.seq_lens = a->seq_lens;
+  p.q_indptr = is_context ? a->q_indptr : nullptr;
+  p.out = a->out;
+  p.lse_out = a->lse_out;
+  p.err_word = a->err_word;
+  p.k_scale_dev = a->k_scale_dev;
+  p.v_scale_dev = a->v_scale_dev;
+  p.q_st = a->q_stride_tok;
+  p.q_sh = a->q_stride_head;
+  p.o_st = a->o_stride_tok;
+  p.o_sh = a->o_stride_head;
+  p.k_sp = a->k_stride_page;
+  p.k_sh = a->k_stride_head;
+  p.k_stok = a->k_stride_tok;
+  p.v_sp = a->v_shares_k ? a->k_stride_page : a->v_stride_page;
+  p.v_sh = a->v_shares_k ? a->k_stride_head : a->v_stride_head;
+  p.v_stok = a->v_shares_k ? a->k_stride_tok : a->v_stride_tok;
+  p.table_stride = a->table_stride;
+  p.rows_total = total_rows * a->num_qo_heads;
+  p.scale = a->scale;
+  p.k_scale = a->k_scale;
+  p.v_scale = a->v_scale;
+  if (plan.num_splits > 1) {
+    uintptr_t base = (reinterpret_cast<uintptr_t>(ws) + 255) & ~uintptr_t(255);
+    p.ws_o = reinterpret_cast<float*>(base);
+    p.ws_lse = p.ws_o + (size_t)plan.num_splits * p.rows_total * a->head_dim_v;
+  }
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = plan.kernel == pkv::KERNEL_GENERIC ? pkv::launch_generic(p, s) : pkv::launch_mfma(plan.kernel, p, s);
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "attention launch failed: %s", hipGetErrorString(e));
+  if (plan.num_splits > 1) {
+    e = pkv::launch_merge(plan.num_splits, p.rows_total, a->num_qo_heads, a->head_dim_v, p.ws_o, p.ws_lse, a->out,
+                          a->o_dtype, a->o_stride_tok, a->o_stride_head, a->lse_out, s);
+    if (e != hipSuccess) return fail(PKV_ERR_HIP, "merge launch failed: %s", hipGetErrorString(e));
+  }
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_abi_version(void) { return PKV_ABI_VERSION; }
+
+const char* pkv_last_error(void) { return g_last_error.c_str(); }
+
+pkv_status pkv_plan(const pkv_args* args, int is_context, int num_cus, pkv_plan_info* info) {
+  if (!info) return fail(PKV_ERR_INVALID_ARG, "info is NULL");
+  pkv_status st = make_plan(args, is_context != 0, num_cus, info);
+  return st == PKV_OK ? ok() : st;
+}
+
+pkv_status pkv_workspace_bytes(const pkv_args* args, int is_context, size_t* bytes) {
+  if (!bytes) return fail(PKV_ERR_INVALID_ARG, "bytes is NULL");
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
+  }
+  pkv_plan_info info;
+  pkv_status st = make_plan(args, is_context != 0, cus, &info);
+  if (st != PKV_OK) return st;
+  *bytes = info.workspace_bytes;
+  return ok();
+}
+
+pkv_status pkv_decode(const pkv_args* args, void* workspace, size_t workspace_bytes, void* stream) {
+  return run(args, false, workspace, workspace_bytes, stream);
+}
+
+pkv_status pkv_context(const pkv_args* args, void* workspace, size_t workspace_bytes, void* stream) {
+  return run(args, true, workspace, workspace_bytes, stream);
+}
+
+pkv_status pkv_lse_merge(int32_t num_splits, int32_t num_rows, int32_t num_qo_heads, int32_t head_dim_v,
+                         const float* o_part, const float* lse_part, void* out, int32_t o_dtype,
+                         int64_t o_stride_tok, int64_t o_stride_head, float* lse_out, void* stream) {
+  if (num_splits < 1 || num_splits > kMaxSplits)
+    return fail(PKV_ERR_INVALID_ARG, "num_splits must be in [1, %d]", kMaxSplits);
+  if (num_rows < 0 || num_qo_heads < 1 || head_dim_v < 1 || head_dim_v > 512)
+    return fail(PKV_ERR_INVALID_ARG, "need num_rows >= 0, num_qo_heads >= 1, 1 <= head_dim_v <= 512");
+  if (o_dtype != PKV_DTYPE_F32 && o_dtype != PKV_DTYPE_BF16)
+    return fail(PKV_ERR_UNSUPPORTED, "o_dtype %d not supported", o_dtype);
+  if (o_stride_head < head_dim_v || o_stride_tok < head_dim_v)
+    return fail(PKV_ERR_INVALID_ARG, "out strides too small for head_dim_v");
+  if (num_rows == 0) return ok();
+  if (!o_part || !lse_part || !out) return fail(PKV_ERR_INVALID_ARG, "o_part, lse_part and out are required");
+  hipError_t e = pkv::launch_merge(num_splits, num_rows, num_qo_heads, head_dim_v, o_part, lse_part, out, o_dtype,
+                                   o_stride_tok, o_stride_head, lse_out, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "merge launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"

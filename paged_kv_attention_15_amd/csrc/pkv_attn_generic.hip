@@ -1,0 +1,232 @@
+// pkv_attn_generic.hip -- the complete-domain VALU kernel and the log-sum-exp reducer.
+//
+// attn_generic_kernel covers every argument combination the MFMA families do
+// not (fp32 queries or caches, head dims other than 128 / 576+512, page sizes
+// that are not powers of two, ...), the way the flashinfer.cake_fmha API page
+// keeps a complete-domain component behind its optimized routes.  One wavefront
+// owns one (query row, query head, Split-KV partition); per 64-key chunk:
+//   lane-per-key scores (q in LDS, the key row decoded from its storage dtype),
+//   a wavefront max / sum (online softmax in the exp2 domain), then
+//   lane-per-channel accumulation of p_j * v_j with p broadcast through LDS.
+//
+// lse_merge_kernel is the Split-KV reducer (PR #4557 page: partitions merged
+// by a separate reducer): per row, L* = max_s lse_s, w_s = exp(lse_s - L*)
+// (empty partitions, lse = -inf, are selected out and their rows never read),
+// out = sum_s w_s O_s / sum_s w_s, lse = L* + ln(sum_s w_s).
+
+#include "pkv_device.h"
+#include "pkv_internal.h"
+
+namespace pkv {
+
+__device__ __forceinline__ float load_elem(const void* base, int64_t idx, int dtype) {
+  if (dtype == PKV_DTYPE_F32) return ((const float*)base)[idx];
+  if (dtype == PKV_DTYPE_BF16) return bf16_bits_to_f32(((const uint16_t*)base)[idx]);
+  return e4m3_to_f32(((const uint8_t*)base)[idx]);
+}
+
+constexpr int kGenericMaxDqk = 1024;
+constexpr int kGenericMaxDv = 512;
+
+__global__ __launch_bounds__(64) void attn_generic_kernel(const KParams p) {
+  __shared__ float s_q[kGenericMaxDqk];
+  __shared__ float s_p[64];
+  __shared__ int64_t s_voff[64];
+
+  const int lane = threadIdx.x;
+  const int t = blockIdx.x;
+  const int h = blockIdx.y;
+  const int split = blockIdx.z;
+  const int G = p.group;
+  const int g = h / G;
+
+  // ---- which request owns query row t
+  int b, t0, n_b;
+  if (p.is_context) {
+    int lo = 0, hi = p.batch - 1;
+    while (lo < hi) {  // last b with q_indptr[b] <= t
+      int mid = (lo + hi + 1) >> 1;
+      if (p.q_indptr[mid] <= t) lo = mid; else hi = mid - 1;
+    }
+    b = lo;
+    t0 = p.q_indptr[b];
+    const int a1 = p.q_indptr[b + 1];
+    const bool bad = (t0 < 0) || (a1 < t0) || (a1 - t0 > p.max_q_len) || (a1 > p.total_q);
+    if (bad || t < t0 || t >= a1) {
+      if (bad && split == 0 && h == 0 && lane == 0) flag_error(p.err_word, PKV_DEVERR_QINDPTR);
+      return;  // row owned by no well-formed request
+    }
+    n_b = a1 - t0;
+  } else {
+    b = t / p.q_len;
+    t0 = b * p.q_len;
+    n_b = p.q_len;
+  }
+  const int i = t - t0;
+  int L = p.seq_lens[b];
+  const int cap = p.max_pages_per_seq * p.page_size;
+  if (split == 0 && h == 0 && i == 0 && lane == 0) {
+    if (L > cap) flag_error(p.err_word, PKV_DEVERR_SEQ_GT_TABLE);
+    if (L < n_b) flag_error(p.err_word, PKV_DEVERR_SEQ_LT_QLEN);
+  }
+  L = max(0, min(L, cap));
+  const int c = p.causal ? min(L, max(0, L - n_b + i + 1)) : L;
+  const int kv_lo = split * p.pages_per_split * p.page_size;
+  const int kv_hi = min(kv_lo + p.pages_per_split * p.page_size, c);
+
+  const float k_scale = p.k_scale_dev ? *p.k_scale_dev : p.k_scale;
+  const float v_scale = p.v_scale_dev ? *p.v_scale_dev : p.v_scale;
+  const float sc2 = p.scale * k_scale * kLog2e;
+
+  for (int d = lane; d < p.head_dim_qk; d += 64)
+    s_q[d] = load_elem(p.q, t * p.q_st + h * p.q_sh + d, p.q_dtype);
+  __syncthreads();
+
+  float m_run = -INFINITY, l_run = 0.f;
+  float o[kGenericMaxDv / 64];
+#pragma unroll
+  for (int k = 0; k < kGenericMaxDv / 64; ++k) o[k] = 0.f;
+
+  for (int j0 = kv_lo; j0 < kv_hi; j0 += 64) {
+    const int tok = j0 + lane;
+    const bool valid = tok < kv_hi;
+    float s = -INFINITY;
+    int64_t voff = 0;
+    if (valid) {
+      int pg = p.table[(int64_t)b * p.table_stride + tok / p.page_size];
+      if (p.num_pages > 0 && (pg < 0 || pg >= p.num_pages)) {
+        flag_error(p.err_word, PKV_DEVERR_PAGE_RANGE);
+        pg = min(max(pg, 0), p.num_pages - 1);
+      }
+      const int off = tok % p.page_size;
+      const int64_t koff = (int64_t)pg * p.k_sp + (int64_t)g * p.k_sh + (int64_t)off * p.k_stok;
+      voff = (int64_t)pg * p.v_sp + (int64_t)g * p.v_sh + (int64_t)off * p.v_stok;
+      float dot = 0.f;
+      for (int d = 0; d < p.head_dim_qk; ++d) dot += s_q[d] * load_elem(p.k, koff + d, p.kv_dtype);
+      s = dot * sc2;
+    }
+    const float mx = wave_max(s);
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = exp2f(m_run - m_use);
+    const float pj = valid ? exp2f(s - m_use) : 0.f;
+    l_run = l_run * alpha + wave_sum(pj);
+    m_run = m_new;
+#pragma unroll
+    for (int k = 0; k < kGenericMaxDv / 64; ++k) o[k] *= alpha;
+    s_p[lane] = pj;
+    s_voff[lane] = voff;
+    __syncthreads();
+    const int n = min(64, kv_hi - j0);
+    for (int jj = 0; jj < n; ++jj) {
+      const float w = s_p[jj];
+      const int64_t vo = s_voff[jj];
+#pragma unroll
+      for (int k = 0; k < kGenericMaxDv / 64; ++k) {
+        const int d = lane + 64 * k;
+        if (d < p.head_dim_v) o[k] += w * load_elem(p.v, vo + d, p.kv_dtype);
+      }
+    }
+    __syncthreads();
+  }
+
+  const bool empty = !(l_run > 0.f);
+  const float inv = empty ? 0.f : v_scale / l_run;
+  const float lse = empty ? -INFINITY : (m_run * kLn2 + __logf(l_run));
+  const int64_t row_g = (int64_t)t * p.num_qo_heads + h;
+  if (p.ws_o != nullptr) {
+    if (lane == 0) p.ws_lse[(int64_t)split * p.rows_total + row_g] = lse;
+    if (!empty) {
+      float* dst = p.ws_o + ((int64_t)split * p.rows_total + row_g) * p.head_dim_v;
+#pragma unroll
+      for (int k = 0; k < kGenericMaxDv / 64; ++k) {
+        const int d = lane + 64 * k;
+        if (d < p.head_dim_v) dst[d] = o[k] * inv;
+      }
+    }
+  } else {
+    if (p.lse_out && lane == 0) p.lse_out[row_g] = lse;
+#pragma unroll
+    for (int k = 0; k < kGenericMaxDv / 64; ++k) {
+      const int d = lane + 64 * k;
+      if (d >= p.head_dim_v) continue;
+      const float v = o[k] * inv;
+      const int64_t oi = t * p.o_st + h * p.o_sh + d;
+      if (p.o_dtype == PKV_DTYPE_BF16) {
+        ((__bf16*)p.out)[oi] = (__bf16)v;
+      } else {
+        ((float*)p.out)[oi] = v;
+      }
+    }
+  }
+}
+
+hipError_t launch_generic(const KParams& p, hipStream_t s) {
+  int rows = p.is_context ? p.total_q : p.batch * p.q_len;
+  if (rows == 0) return hipSuccess;
+  dim3 grid(rows, p.num_qo_heads, p.num_splits);
+  hipLaunchKernelGGL(attn_generic_kernel, grid, dim3(64), 0, s, p);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- LSE merge
+// one wavefront per merged row; each lane owns channels lane, lane+64, ...
+constexpr int kMergeRowsPerBlock = 4;
+
+__global__ __launch_bounds__(64 * kMergeRowsPerBlock) void lse_merge_kernel(
+    int32_t num_splits, int64_t num_rows, int32_t num_qo_heads, int32_t dv, const float* __restrict__ o_part,
+    const float* __restrict__ lse_part, void* out, int32_t o_dtype, int64_t o_st, int64_t o_sh,
+    float* lse_out) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * kMergeRowsPerBlock + (threadIdx.x >> 6);
+  if (r >= num_rows) return;
+  float M = -INFINITY;
+  for (int s = 0; s < num_splits; ++s) M = fmaxf(M, lse_part[(int64_t)s * num_rows + r]);
+  const int64_t t = r / num_qo_heads;
+  const int h = (int)(r % num_qo_heads);
+  float wsum = 0.f;
+  float acc[8];
+  const int per_lane = (dv + 63) / 64;  // <= 8 (head_dim_v <= 512)
+#pragma unroll
+  for (int k = 0; k < 8; ++k) acc[k] = 0.f;
+  if (M != -INFINITY) {
+    for (int s = 0; s < num_splits; ++s) {
+      const float ls = lse_part[(int64_t)s * num_rows + r];
+      if (ls == -INFINITY) continue;  // empty partition: weight 0, row never read
+      const float w = __expf(ls - M);
+      wsum += w;
+      const float* src = o_part + ((int64_t)s * num_rows + r) * dv;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int d = lane + 64 * k;
+        if (k < per_lane && d < dv) acc[k] += w * src[d];
+      }
+    }
+  }
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int d = lane + 64 * k;
+    if (k >= per_lane || d >= dv) continue;
+    const float v = acc[k] * inv;
+    const int64_t oi = t * o_st + (int64_t)h * o_sh + d;
+    if (o_dtype == PKV_DTYPE_BF16) {
+      ((__bf16*)out)[oi] = (__bf16)v;
+    } else {
+      ((float*)out)[oi] = v;
+    }
+  }
+  if (lse_out && lane == 0) lse_out[r] = (M == -INFINITY) ? -INFINITY : M + __logf(wsum);
+}
+
+hipError_t launch_merge(int32_t num_splits, int64_t num_rows, int32_t num_qo_heads, int32_t head_dim_v,
+                        const float* o_part, const float* lse_part, void* out, int32_t o_dtype,
+                        int64_t o_st, int64_t o_sh, float* lse_out, hipStream_t s) {
+  if (num_rows == 0) return hipSuccess;
+  dim3 grid((unsigned)((num_rows + kMergeRowsPerBlock - 1) / kMergeRowsPerBlock));
+  hipLaunchKernelGGL(lse_merge_kernel, grid, dim3(64 * kMergeRowsPerBlock), 0, s, num_splits, num_rows,
+                     num_qo_heads, head_dim_v, o_part, lse_part, out, o_dtype, o_st, o_sh, lse_out);
+  return hipGetLastError();
+}
+
+}  // namespace pkv

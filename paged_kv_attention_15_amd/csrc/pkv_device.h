@@ -1,0 +1,113 @@
+// pkv_device.h -- device-side building blocks for the gfx950 paged-KV kernels.
+//
+// Storage decoding (bf16, OCP e4m3), wavefront reductions, the 16x16x32 bf16
+// MFMA wrapper and the LDS transpose read.  Operand layouts below were
+// measured on gfx950 (see the kernel comments for how each is used):
+//   v_mfma_f32_16x16x32_bf16  A: lane l holds row l%16, k = 8*(l/16)+e (e=0..7)
+//                             B: lane l holds col l%16, k = 8*(l/16)+e
+//                             C: lane l, element e is (row 4*(l/16)+e, col l%16)
+//   ds_read_b64_tr_b16        inside each 16-lane group, lane i receives
+//                             element i%4 of the 8-byte rows addressed by lanes
+//                             (i/4) + 4k, k = 0..3.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ---------------------------------------------------------------- decoding
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// two e4m3 bytes (selected half of a 32-bit word) -> two bf16 (exact: e4m3 is a subset of bf16)
+template <bool HI>
+__device__ __forceinline__ bf16x2 e4m3x2_to_bf16x2(uint32_t word) {
+  return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, 1.0f, HI);
+}
+
+// two e4m3 bytes -> two fp32
+template <bool HI>
+__device__ __forceinline__ f32x2 e4m3x2_to_f32x2(uint32_t word) {
+  return __builtin_amdgcn_cvt_pk_f32_fp8(word, HI);
+}
+
+__device__ __forceinline__ float e4m3_to_f32(uint32_t byte) {
+  f32x2 v = e4m3x2_to_f32x2<false>(byte & 0xFFu);
+  return v[0];
+}
+
+// 16 e4m3 codes (one 16-byte load) -> 16 bf16 (two 16-byte LDS chunks)
+__device__ __forceinline__ void e4m3x16_to_bf16x16(u32x4 src, u32x4& lo, u32x4& hi) {
+  bf16x2 t[8];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    t[2 * w] = e4m3x2_to_bf16x2<false>(src[w]);
+    t[2 * w + 1] = e4m3x2_to_bf16x2<true>(src[w]);
+  }
+  lo = u32x4{__builtin_bit_cast(uint32_t, t[0]), __builtin_bit_cast(uint32_t, t[1]),
+             __builtin_bit_cast(uint32_t, t[2]), __builtin_bit_cast(uint32_t, t[3])};
+  hi = u32x4{__builtin_bit_cast(uint32_t, t[4]), __builtin_bit_cast(uint32_t, t[5]),
+             __builtin_bit_cast(uint32_t, t[6]), __builtin_bit_cast(uint32_t, t[7])};
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  bf16x2 v = __builtin_convertvector(f32x2{a, b}, bf16x2);  // round to nearest even
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// ---------------------------------------------------------------- MFMA / LDS
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ s16x4 lds_read_tr16(const void* lds_ptr) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds_ptr));
+}
+
+// ---------------------------------------------------------------- reductions
+__device__ __forceinline__ float xor_max(float v, int mask) {
+  return fmaxf(v, __shfl_xor(v, mask, 64));
+}
+__device__ __forceinline__ float xor_sum(float v, int mask) {
+  return v + __shfl_xor(v, mask, 64);
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = xor_max(v, m);
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = xor_sum(v, m);
+  return v;
+}
+
+// s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// ---------------------------------------------------------------- error word
+__device__ __forceinline__ void flag_error(int32_t* err_word, int32_t bits) {
+  if (err_word) atomicOr(err_word, bits);
+}
+
+}  // namespace pkv

@@ -1,0 +1,72 @@
+// pkv_internal.h -- what the C-ABI layer hands to the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/pkv.h"
+
+namespace pkv {
+
+// Kernel families picked by the planner (reported through pkv_plan_info.kernel).
+enum KernelId : int32_t {
+  KERNEL_NONE = 0,
+  KERNEL_GENERIC = 1,     // VALU, one wavefront per (query row, head, split); any dtype / head dim
+  KERNEL_GQA_BF16 = 2,    // MFMA, <= 16 packed rows per KV head, D = 128, bf16 KV
+  KERNEL_GQA_FP8 = 3,     // same with e4m3 KV
+  KERNEL_WIDE_BF16 = 4,   // MFMA, 128 packed rows per workgroup (context / large groups), D = 128
+  KERNEL_WIDE_FP8 = 5,
+  KERNEL_MLA_BF16 = 6,    // MFMA, 128 heads on one latent KV head, D_qk = 576, D_v = 512
+  KERNEL_MLA_FP8 = 7,
+};
+
+// Everything a kernel reads, by value.  Element strides as in pkv_args.
+struct KParams {
+  int32_t batch, q_len, num_qo_heads, num_kv_heads, group;
+  int32_t head_dim_qk, head_dim_v, page_size, log2_page;
+  int32_t max_pages_per_seq, num_pages, is_context, causal;
+  int32_t num_splits, pages_per_split, row_blocks, total_q, max_q_len;
+  int32_t q_dtype, kv_dtype, o_dtype, pad0;
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* table;
+  const int32_t* seq_lens;
+  const int32_t* q_indptr;
+  void* out;
+  float* lse_out;
+  int32_t* err_word;
+  const float* k_scale_dev;
+  const float* v_scale_dev;
+  float* ws_o;    // [num_splits, rows_total, head_dim_v] when split
+  float* ws_lse;  // [num_splits, rows_total]
+  int64_t q_st, q_sh, o_st, o_sh;
+  int64_t k_sp, k_sh, k_stok, v_sp, v_sh, v_stok, table_stride;
+  int64_t rows_total;  // total query rows * num_qo_heads
+  float scale, k_scale, v_scale, pad1;
+};
+
+struct LaunchShape {
+  dim3 grid;
+  dim3 block;
+  size_t lds_bytes;
+};
+
+// Launchers (return hipSuccess or the launch error).
+hipError_t launch_generic(const KParams& p, hipStream_t s);
+hipError_t launch_mfma(int32_t kernel, const KParams& p, hipStream_t s);
+hipError_t launch_merge(int32_t num_splits, int64_t num_rows, int32_t num_qo_heads, int32_t head_dim_v,
+                        const float* o_part, const float* lse_part, void* out, int32_t o_dtype,
+                        int64_t o_st, int64_t o_sh, float* lse_out, hipStream_t s);
+
+// Static shape facts of the MFMA kernel families (host-side planner input).
+struct MfmaShape {
+  int rows_per_block;    // packed query rows per workgroup
+  int tile_tokens;       // KV tokens per pipeline stage
+  int threads;           // workgroup size
+  size_t lds_static;     // LDS for the KV stages and reductions (page list excluded)
+};
+bool mfma_shape(int32_t kernel, MfmaShape* out);
+
+}  // namespace pkv

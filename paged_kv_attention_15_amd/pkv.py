@@ -1,0 +1,279 @@
+"""ctypes binding of libpkv.so -- argument marshalling only.
+
+Every function here has the name of the C entry point it calls (see
+include/pkv.h) and does nothing but pack arguments; all attention work runs in
+the library's HIP kernels.  Loading fails loudly when libpkv.so is missing:
+there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libpkv.so")
+
+PKV_OK, PKV_ERR_INVALID_ARG, PKV_ERR_UNSUPPORTED, PKV_ERR_WORKSPACE, PKV_ERR_HIP = range(5)
+PKV_DTYPE_F32, PKV_DTYPE_BF16, PKV_DTYPE_FP8_E4M3 = range(3)
+PKV_LAYOUT_HND, PKV_LAYOUT_NHD = range(2)
+PKV_DEVERR_SEQ_LT_QLEN, PKV_DEVERR_SEQ_GT_TABLE, PKV_DEVERR_PAGE_RANGE, PKV_DEVERR_QINDPTR = 1, 2, 4, 8
+
+KERNEL_NAMES = {0: "none", 1: "generic", 2: "gqa_bf16", 3: "gqa_fp8", 4: "wide_bf16", 5: "wide_fp8",
+                6: "mla_bf16", 7: "mla_fp8"}
+
+DTYPE_CODES = {"f32": PKV_DTYPE_F32, "bf16": PKV_DTYPE_BF16, "e4m3": PKV_DTYPE_FP8_E4M3}
+EXPORTED = ["pkv_abi_version", "pkv_last_error", "pkv_plan", "pkv_workspace_bytes", "pkv_decode",
+            "pkv_context", "pkv_lse_merge"]
+
+
+class PkvArgs(C.Structure):
+    """Mirror of `pkv_args` in include/pkv.h (field order and types must match)."""
+    _fields_ = [
+        ("batch", C.c_int32), ("q_len", C.c_int32), ("num_qo_heads", C.c_int32),
+        ("num_kv_heads", C.c_int32), ("head_dim_qk", C.c_int32), ("head_dim_v", C.c_int32),
+        ("page_size", C.c_int32), ("max_pages_per_seq", C.c_int32), ("max_kv_len", C.c_int32),
+        ("max_q_len", C.c_int32), ("total_q", C.c_int32), ("num_pages", C.c_int32),
+        ("q_dtype", C.c_int32), ("kv_dtype", C.c_int32), ("o_dtype", C.c_int32),
+        ("layout", C.c_int32), ("causal", C.c_int32), ("num_splits", C.c_int32),
+        ("v_shares_k", C.c_int32), ("reserved0", C.c_int32),
+        ("q", C.c_void_p), ("k_pages", C.c_void_p), ("v_pages", C.c_void_p),
+        ("block_tables", C.c_void_p), ("seq_lens", C.c_void_p), ("q_indptr", C.c_void_p),
+        ("out", C.c_void_p), ("lse_out", C.c_void_p), ("err_word", C.c_void_p),
+        ("k_scale_dev", C.c_void_p), ("v_scale_dev", C.c_void_p),
+        ("q_stride_tok", C.c_int64), ("q_stride_head", C.c_int64),
+        ("o_stride_tok", C.c_int64), ("o_stride_head", C.c_int64),
+        ("k_stride_page", C.c_int64), ("k_stride_head", C.c_int64), ("k_stride_tok", C.c_int64),
+        ("v_stride_page", C.c_int64), ("v_stride_head", C.c_int64), ("v_stride_tok", C.c_int64),
+        ("table_stride", C.c_int64),
+        ("scale", C.c_float), ("k_scale", C.c_float), ("v_scale", C.c_float), ("reserved1", C.c_float),
+    ]
+
+
+class PkvPlanInfo(C.Structure):
+    _fields_ = [
+        ("kernel", C.c_int32), ("num_splits", C.c_int32), ("pages_per_split", C.c_int32),
+        ("grid_x", C.c_int32), ("grid_y", C.c_int32), ("grid_z", C.c_int32),
+        ("block_threads", C.c_int32), ("reserved", C.c_int32), ("workspace_bytes", C.c_size_t),
+    ]
+
+
+class PkvError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"pkv status {status}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libpkv.so (raises if it was not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(path):
+            raise RuntimeError(f"libpkv.so not found at {path}; build it with "
+                               f"`python -m paged_kv_attention_15_amd.build`")
+        lib = C.CDLL(path)
+        lib.pkv_abi_version.restype = C.c_int
+        lib.pkv_last_error.restype = C.c_char_p
+        lib.pkv_plan.argtypes = [C.POINTER(PkvArgs), C.c_int, C.c_int, C.POINTER(PkvPlanInfo)]
+        lib.pkv_plan.restype = C.c_int
+        lib.pkv_workspace_bytes.argtypes = [C.POINTER(PkvArgs), C.c_int, C.POINTER(C.c_size_t)]
+        lib.pkv_workspace_bytes.restype = C.c_int
+        for fn in (lib.pkv_decode, lib.pkv_context):
+            fn.argtypes = [C.POINTER(PkvArgs), C.c_void_p, C.c_size_t, C.c_void_p]
+            fn.restype = C.c_int
+        lib.pkv_lse_merge.argtypes = [C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p,
+                                      C.c_void_p, C.c_int32, C.c_int64, C.c_int64, C.c_void_p, C.c_void_p]
+        lib.pkv_lse_merge.restype = C.c_int
+        _lib = lib
+    return _lib
+
+
+def _check(status: int) -> int:
+    if status != PKV_OK:
+        raise PkvError(status, pkv_last_error())
+    return status
+
+
+# ---------------------------------------------------------------- entry points
+
+def pkv_abi_version() -> int:
+    return int(load_library().pkv_abi_version())
+
+
+def pkv_last_error() -> str:
+    return load_library().pkv_last_error().decode()
+
+
+def pkv_plan(args: PkvArgs, is_context: bool = False, num_cus: int = 0, check: bool = True) -> PkvPlanInfo:
+    info = PkvPlanInfo()
+    st = load_library().pkv_plan(C.byref(args), int(is_context), int(num_cus), C.byref(info))
+    if check:
+        _check(st)
+    info.status = st
+    return info
+
+
+def pkv_workspace_bytes(args: PkvArgs, is_context: bool = False) -> int:
+    n = C.c_size_t(0)
+    _check(load_library().pkv_workspace_bytes(C.byref(args), int(is_context), C.byref(n)))
+    return int(n.value)
+
+
+def pkv_decode(args: PkvArgs, workspace: int, workspace_bytes: int, stream: int, check: bool = True) -> int:
+    st = load_library().pkv_decode(C.byref(args), C.c_void_p(workspace or None), workspace_bytes,
+                                   C.c_void_p(stream or None))
+    return _check(st) if check else st
+
+
+def pkv_context(args: PkvArgs, workspace: int, workspace_bytes: int, stream: int, check: bool = True) -> int:
+    st = load_library().pkv_context(C.byref(args), C.c_void_p(workspace or None), workspace_bytes,
+                                    C.c_void_p(stream or None))
+    return _check(st) if check else st
+
+
+def pkv_lse_merge(num_splits: int, num_rows: int, num_qo_heads: int, head_dim_v: int, o_part: int,
+                  lse_part: int, out: int, o_dtype: int, o_stride_tok: int, o_stride_head: int,
+                  lse_out: int, stream: int, check: bool = True) -> int:
+    st = load_library().pkv_lse_merge(num_splits, num_rows, num_qo_heads, head_dim_v, C.c_void_p(o_part or None),
+                                      C.c_void_p(lse_part or None), C.c_void_p(out or None), o_dtype,
+                                      o_stride_tok, o_stride_head, C.c_void_p(lse_out or None),
+                                      C.c_void_p(stream or None))
+    return _check(st) if check else st
+
+
+# ---------------------------------------------------------------- torch marshalling
+
+def _torch():
+    import torch
+    return torch
+
+
+@dataclass
+class DeviceProblem:
+    """A workloads.Problem copied to device tensors plus the matching pkv_args."""
+    args: PkvArgs
+    is_context: bool
+    tensors: dict
+    workspace: Optional[object]
+    workspace_bytes: int
+
+    @property
+    def out(self):
+        return self.tensors["out"]
+
+    @property
+    def lse(self):
+        return self.tensors.get("lse")
+
+    @property
+    def err(self):
+        return self.tensors.get("err")
+
+    def stream_ptr(self, stream=None) -> int:
+        torch = _torch()
+        s = stream if stream is not None else torch.cuda.current_stream()
+        return int(s.cuda_stream)
+
+    def run(self, stream=None, check: bool = True) -> int:
+        ws = int(self.workspace.data_ptr()) if self.workspace is not None else 0
+        fn = pkv_context if self.is_context else pkv_decode
+        return fn(self.args, ws, self.workspace_bytes, self.stream_ptr(stream), check=check)
+
+
+def _to_device(arr, device):
+    import numpy as np
+    torch = _torch()
+    if arr.dtype == np.uint16:
+        return torch.from_numpy(arr.view(np.int16)).to(device).view(torch.bfloat16)
+    if arr.dtype == np.uint8:
+        return torch.from_numpy(arr).to(device)
+    return torch.from_numpy(arr).to(device)
+
+
+def upload(prob, device="cuda", with_lse: bool = True, with_err: bool = True, num_splits: Optional[int] = None,
+           device_scales: bool = False) -> DeviceProblem:
+    """Copy a workloads.Problem to `device` and fill pkv_args for it."""
+    torch = _torch()
+    t = {}
+    t["q"] = _to_device(prob.q, device)
+    t["k"] = _to_device(prob.k_pool, device)
+    if not prob.mla:
+        t["v"] = _to_device(prob.v_pool, device)
+    t["table"] = torch.from_numpy(prob.block_tables).to(device)
+    t["seq_lens"] = torch.from_numpy(prob.seq_lens).to(device)
+    t["q_indptr"] = torch.from_numpy(prob.q_indptr).to(device)
+    odt = torch.bfloat16 if prob.o_dtype == "bf16" else torch.float32
+    t["out"] = torch.full((prob.total_q, prob.num_qo_heads, prob.head_dim_v), float("nan"), dtype=odt, device=device)
+    if with_lse:
+        t["lse"] = torch.full((prob.total_q, prob.num_qo_heads), float("nan"), dtype=torch.float32, device=device)
+    if with_err:
+        t["err"] = torch.zeros(1, dtype=torch.int32, device=device)
+    if device_scales:
+        t["k_scale"] = torch.tensor([prob.k_scale], dtype=torch.float32, device=device)
+        t["v_scale"] = torch.tensor([prob.v_scale], dtype=torch.float32, device=device)
+    a = fill_args(prob, t, num_splits=num_splits)
+    is_ctx = not prob.is_decode
+    ws_bytes = pkv_workspace_bytes(a, is_ctx)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=device) if ws_bytes > 0 else None
+    return DeviceProblem(args=a, is_context=is_ctx, tensors=t, workspace=ws, workspace_bytes=ws_bytes)
+
+
+def fill_args(prob, t: dict, num_splits: Optional[int] = None) -> PkvArgs:
+    """pkv_args for a workloads.Problem whose arrays live in the tensors of `t`."""
+    a = PkvArgs()
+    H, P = prob.num_kv_heads, prob.page_size
+    a.batch = prob.batch
+    a.q_len = prob.q_len if prob.is_decode else 0
+    a.num_qo_heads = prob.num_qo_heads
+    a.num_kv_heads = H
+    a.head_dim_qk = prob.head_dim_qk
+    a.head_dim_v = prob.head_dim_v
+    a.page_size = P
+    a.max_pages_per_seq = prob.max_pages
+    a.max_kv_len = prob.max_kv_len
+    a.max_q_len = prob.q_len
+    a.total_q = prob.total_q
+    a.num_pages = prob.num_pages
+    a.q_dtype = DTYPE_CODES[prob.q_dtype]
+    a.kv_dtype = DTYPE_CODES[prob.kv_dtype]
+    a.o_dtype = DTYPE_CODES[prob.o_dtype]
+    a.layout = PKV_LAYOUT_HND if prob.layout == "HND" else PKV_LAYOUT_NHD
+    a.causal = 1 if prob.causal else 0
+    a.num_splits = prob.num_splits if num_splits is None else num_splits
+    a.v_shares_k = 1 if prob.mla else 0
+    a.q = t["q"].data_ptr()
+    a.k_pages = t["k"].data_ptr()
+    a.v_pages = t["v"].data_ptr() if "v" in t else 0
+    a.block_tables = t["table"].data_ptr()
+    a.seq_lens = t["seq_lens"].data_ptr()
+    a.q_indptr = t["q_indptr"].data_ptr()
+    a.out = t["out"].data_ptr()
+    a.lse_out = t["lse"].data_ptr() if t.get("lse") is not None else 0
+    a.err_word = t["err"].data_ptr() if t.get("err") is not None else 0
+    a.k_scale_dev = t["k_scale"].data_ptr() if "k_scale" in t else 0
+    a.v_scale_dev = t["v_scale"].data_ptr() if "v_scale" in t else 0
+    D, Dv = prob.head_dim_qk, prob.head_dim_v
+    a.q_stride_tok = prob.num_qo_heads * D
+    a.q_stride_head = D
+    a.o_stride_tok = prob.num_qo_heads * Dv
+    a.o_stride_head = Dv
+    if prob.layout == "HND":
+        k_sp, k_sh, k_st = H * P * D, P * D, D
+    else:
+        k_sp, k_sh, k_st = P * H * D, D, H * D
+    a.k_stride_page, a.k_stride_head, a.k_stride_tok = k_sp, k_sh, k_st
+    if prob.mla:
+        a.v_stride_page, a.v_stride_head, a.v_stride_tok = k_sp, k_sh, k_st
+    elif prob.layout == "HND":
+        a.v_stride_page, a.v_stride_head, a.v_stride_tok = H * P * Dv, P * Dv, Dv
+    else:
+        a.v_stride_page, a.v_stride_head, a.v_stride_tok = P * H * Dv, Dv, H * Dv
+    a.table_stride = prob.block_tables.shape[1]
+    a.scale = prob.scale
+    a.k_scale = prob.k_scale
+    a.v_scale = prob.v_scale
+    return a

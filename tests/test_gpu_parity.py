@@ -1,0 +1,244 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Small problems are compared on every output element; the full-size workloads
+are compared on sampled (row, head) pairs that the oracle computes one by one,
+in the launch configuration the benchmark times.  Tolerances are the pages'
+(tests/golden/tolerances.json).  Inputs poison page tails, spare pages and
+unused table slots with NaN where noted, so any stray read shows up as a
+non-finite output.
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from paged_kv_attention_15_amd import pkv, workloads as W
+from tests._gpu import compare, run_gpu, sample_pairs, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    pkv.load_library()
+    torch.cuda.init()
+
+
+def _gqa(seq_lens, hq=32, hkv=8, P=32, kv=W.BF16, poison=True, layout=W.HND, seed=1, q_lens=None, **kw):
+    B = len(seq_lens)
+    return W.make_problem(name=f"gqa-{kv}-P{P}-h{hq}x{hkv}", seed=seed, batch=B, seq_lens=seq_lens,
+                          q_lens=q_lens or [1] * B, num_qo_heads=hq, num_kv_heads=hkv, head_dim_qk=128,
+                          head_dim_v=128, page_size=P, kv_dtype=kv, q_dtype=W.BF16, o_dtype=W.BF16,
+                          poison=poison, extra_page_frac=0.25, table_slack_pages=2, layout=layout, **kw)
+
+
+# ----------------------------------------------------------------- the five workloads
+
+def test_tiny_gqa_fp32_workload():
+    prob = W.tiny_gqa_fp32(poison=True)
+    say(f"case {prob.name}")
+    dp = run_gpu(prob)
+    assert dp.workspace_bytes > 0  # two KV partitions + the reducer
+    compare(prob, dp)
+
+
+@pytest.mark.parametrize("splits", [None, 1, 3])
+def test_gqa_bf16_ragged_small(splits):
+    prob = _gqa([1, 31, 32, 33, 700, 129])
+    say(f"case {prob.name} splits={splits}")
+    compare(prob, run_gpu(prob, num_splits=splits))
+
+
+@pytest.mark.parametrize("splits", [None, 1, 4])
+def test_gqa_fp8_ragged_small(splits):
+    prob = _gqa([5, 64, 65, 1500], hq=64, hkv=8, P=64, kv=W.E4M3)
+    say(f"case {prob.name} splits={splits}")
+    compare(prob, run_gpu(prob, num_splits=splits))
+
+
+def test_gqa_bf16_full_size():
+    prob = W.gqa_bf16_b32_kv4096()
+    say(f"case {prob.name} (sampled)")
+    dp = run_gpu(prob)
+    compare(prob, dp, sample_pairs(prob, 96))
+
+
+def test_gqa_fp8_full_size():
+    prob = W.gqa_fp8_b16_ragged()
+    say(f"case {prob.name} (sampled)")
+    dp = run_gpu(prob)
+    compare(prob, dp, sample_pairs(prob, 96))
+
+
+@pytest.mark.parametrize("q_len", [1, 2])
+def test_mla_small(q_len):
+    prob = W.make_problem(name=f"mla-small-q{q_len}", seed=3, batch=3, seq_lens=[2, 70, 300],
+                          q_lens=[q_len] * 3, num_qo_heads=128, num_kv_heads=1, head_dim_qk=576,
+                          head_dim_v=512, page_size=64, mla=True, scale=1 / 24.0, poison=True,
+                          extra_page_frac=0.3, table_slack_pages=1)
+    say(f"case {prob.name}")
+    compare(prob, run_gpu(prob))
+
+
+@pytest.mark.parametrize("q_len", [1, 2])
+def test_mla_full_size(q_len):
+    prob = W.mla_b512_kv4096(q_len=q_len)
+    say(f"case {prob.name} (sampled)")
+    dp = run_gpu(prob)
+    compare(prob, dp, sample_pairs(prob, 48))
+
+
+def test_context_small_ragged():
+    prob = W.make_problem(name="ctx-small", seed=4, batch=3, seq_lens=[50, 1, 300], q_lens=[20, 1, 70],
+                          num_qo_heads=64, num_kv_heads=8, head_dim_qk=128, head_dim_v=128, page_size=32,
+                          is_decode=False, poison=True, extra_page_frac=0.3, table_slack_pages=1)
+    say(f"case {prob.name}")
+    compare(prob, run_gpu(prob))
+
+
+def test_context_full_size():
+    prob = W.context_b4_q511_kv2047()
+    say(f"case {prob.name} (sampled)")
+    dp = run_gpu(prob)
+    compare(prob, dp, sample_pairs(prob, 96))
+
+
+# ----------------------------------------------------------------- reducer, codec, invariants
+
+def test_lse_merge_entry_point_matches_oracle_merge():
+    prob = W.make_problem(name="merge", seed=5, batch=3, seq_lens=[37, 100, 5], q_lens=[1, 1, 1],
+                          num_qo_heads=4, num_kv_heads=1, head_dim_qk=64, head_dim_v=64, page_size=16,
+                          q_dtype=W.F32, kv_dtype=W.F32, o_dtype=W.F32)
+    S = 5  # includes empty partitions for the short requests
+    o_part, l_part = oracle.attention_split(prob, S)
+    ref_o, ref_l = oracle.merge(o_part, l_part)
+    n = o_part.shape[1]
+    o_dev = torch.from_numpy(o_part.astype(np.float32)).cuda()
+    l_dev = torch.from_numpy(l_part.astype(np.float32)).cuda()
+    out = torch.full((prob.total_q, prob.num_qo_heads, 64), float("nan"), device="cuda")
+    lse = torch.full((n,), float("nan"), device="cuda")
+    pkv.pkv_lse_merge(S, n, prob.num_qo_heads, 64, o_dev.data_ptr(), l_dev.data_ptr(), out.data_ptr(),
+                      pkv.PKV_DTYPE_F32, prob.num_qo_heads * 64, 64, lse.data_ptr(),
+                      torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(out.cpu().numpy().reshape(n, 64), ref_o, atol=1e-5, rtol=1e-5)
+    np.testing.assert_allclose(lse.cpu().numpy(), ref_l, atol=1e-5, rtol=1e-5)
+
+
+def test_fp8_dequant_all_256_codes_exact():
+    # one key per request, v_scale = 1: the output row is the decoded value row itself
+    prob = _gqa([1, 1], hq=8, hkv=1, P=64, kv=W.E4M3, poison=False)
+    codes = np.arange(256, dtype=np.uint8).reshape(2, 128)
+    for b in range(2):
+        page = prob.block_tables[b, 0]
+        prob.v_pool[page, 0, 0, :] = codes[b]
+    prob = dataclasses.replace(prob, v_scale=1.0)
+    dp = run_gpu(prob)
+    got = dp.out.float().cpu().numpy()  # [2, 8, 128]
+    table = oracle.e4m3_table()
+    for b in range(2):
+        exp = table[codes[b].astype(int)]
+        for h in range(8):
+            nan = np.isnan(exp)
+            assert np.array_equal(np.isnan(got[b, h]), nan)
+            assert np.array_equal(got[b, h][~nan], exp[~nan])
+
+
+def test_page_permutation_invariance_bitwise():
+    prob = _gqa([300, 77], poison=False)
+    dp1 = run_gpu(prob)
+    rng = np.random.default_rng(7)
+    relabel = rng.permutation(prob.num_pages)
+    k2 = np.empty_like(prob.k_pool)
+    v2 = np.empty_like(prob.v_pool)
+    k2[relabel] = prob.k_pool
+    v2[relabel] = prob.v_pool
+    p2 = dataclasses.replace(prob, k_pool=k2, v_pool=v2, block_tables=relabel[prob.block_tables].astype(np.int32))
+    dp2 = run_gpu(p2)
+    assert torch.equal(dp1.out, dp2.out)
+
+
+def test_repeated_calls_are_bitwise_deterministic():
+    prob = _gqa([513, 1000], poison=True)
+    dp = pkv.upload(prob, "cuda")
+    dp.run()
+    first = dp.out.clone()
+    for _ in range(3):
+        dp.run()
+    torch.cuda.synchronize()
+    assert torch.equal(first, dp.out)
+
+
+def test_nhd_layout_matches_oracle():
+    prob = _gqa([40, 129], layout=W.NHD)
+    say(f"case {prob.name} NHD")
+    compare(prob, run_gpu(prob))
+
+
+def test_device_scalar_fp8_scales():
+    prob = _gqa([100, 260], hq=64, hkv=8, P=64, kv=W.E4M3)
+    compare(prob, run_gpu(prob, device_scales=True))
+
+
+@pytest.mark.parametrize("kv,P,D,qd", [(W.F32, 24, 64, W.F32), (W.BF16, 16, 96, W.BF16), (W.E4M3, 8, 64, W.BF16)])
+def test_generic_kernel_other_shapes(kv, P, D, qd):
+    prob = W.make_problem(name=f"generic-{kv}-P{P}-D{D}", seed=6, batch=3, seq_lens=[1, 47, 130],
+                          q_lens=[2, 2, 2], num_qo_heads=6, num_kv_heads=2, head_dim_qk=D, head_dim_v=D,
+                          page_size=P, q_dtype=qd, kv_dtype=kv, o_dtype=W.F32 if qd == W.F32 else W.BF16,
+                          poison=True, extra_page_frac=0.3)
+    say(f"case {prob.name}")
+    # the first request holds one key for two query rows: its first row sees nothing (flagged, zeros)
+    compare(prob, run_gpu(prob), expect_err=pkv.PKV_DEVERR_SEQ_LT_QLEN)
+
+
+def test_speculative_rows_on_gqa_kernel():
+    prob = _gqa([3, 90, 400], q_lens=[3, 3, 3], hq=32, hkv=8)  # 3 rows x 4 heads = 12 packed rows
+    compare(prob, run_gpu(prob))
+    short = _gqa([2, 90, 400], q_lens=[3, 3, 3], hq=32, hkv=8)  # 2 keys for 3 rows: flagged
+    compare(short, run_gpu(short), expect_err=pkv.PKV_DEVERR_SEQ_LT_QLEN)
+
+
+# ----------------------------------------------------------------- device-side validation
+
+def test_error_word_flags_and_clamping():
+    prob = _gqa([60, 100], poison=False)
+    dp = pkv.upload(prob, "cuda")
+    # seq_lens beyond the table capacity: flagged, clamped to capacity
+    cap = prob.max_pages * prob.page_size
+    dp.tensors["seq_lens"][1] = cap + 50
+    dp.run()
+    torch.cuda.synchronize()
+    assert int(dp.err.item()) & pkv.PKV_DEVERR_SEQ_GT_TABLE
+    assert torch.isfinite(dp.out.float()).all()
+    # a page index outside the pool: flagged, clamped
+    dp.tensors["err"].zero_()
+    dp.tensors["seq_lens"][1] = 100
+    dp.tensors["table"][0, 0] = prob.num_pages + 1000
+    dp.run()
+    torch.cuda.synchronize()
+    assert int(dp.err.item()) & pkv.PKV_DEVERR_PAGE_RANGE
+    # fewer keys than query rows
+    dp.tensors["err"].zero_()
+    dp.tensors["table"][0, 0] = int(prob.block_tables[0, 0])
+    dp.tensors["seq_lens"][0] = 0
+    dp.run()
+    torch.cuda.synchronize()
+    assert int(dp.err.item()) & pkv.PKV_DEVERR_SEQ_LT_QLEN
+    assert torch.all(dp.out[0].float() == 0)
+    assert torch.isneginf(dp.lse[0]).all()
+
+
+def test_malformed_q_indptr_flagged_without_writes():
+    prob = W.make_problem(name="ctx-bad", seed=8, batch=2, seq_lens=[40, 50], q_lens=[10, 12],
+                          num_qo_heads=16, num_kv_heads=2, head_dim_qk=128, head_dim_v=128, page_size=32,
+                          is_decode=False)
+    dp = pkv.upload(prob, "cuda")
+    dp.tensors["q_indptr"][1] = 50  # > total_q (22) and rows > max_q_len
+    dp.run()
+    torch.cuda.synchronize()
+    assert int(dp.err.item()) & pkv.PKV_DEVERR_QINDPTR
