@@ -1,0 +1,206 @@
+"""Benchmark: paged decode latency and achieved HBM bandwidth on KV bytes.
+
+One step is one pkv_decode call (attention kernel plus, when the planner
+splits the KV range, the log-sum-exp reducer) over the headline workload:
+bf16 paged GQA decode, B=32, one query row, Hq=32 / Hkv=8, D=128, HND pages of
+32 tokens, 4096 keys per request, pages shuffled across the pool.  Inputs are
+seeded synthetic draws already resident in HBM when timing starts.
+
+Prints ONE JSON line.  `value` is KV GB/s (algorithmic KV bytes of the call /
+wall time per call).  `roofline` reports the dominant kernel against the
+MI355X HBM peak (8 TB/s); `cpu_baseline` is the fp64 CPU oracle timed on a
+bounded sample of the same workload on the host.  `secondary` holds the same
+measurements for the other four workloads (FP8 ragged split decode, MLA decode
+q=1 / q=2, causal context) unless --no-secondary is given.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+METRIC = "paged decode µs/call + achieved HBM GB/s (KV bytes) as % of MI355X peak"
+KERNEL_SRC = os.path.join(ROOT, "paged_kv_attention_15_amd", "csrc", "pkv_attn_mfma.hip")
+
+
+def _src_hash() -> str:
+    h = hashlib.sha256()
+    for name in ("pkv_attn_mfma.hip", "pkv_attn_generic.hip", "pkv_device.h", "pkv_abi.cpp"):
+        with open(os.path.join(ROOT, "paged_kv_attention_15_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, or None when
+    they are missing or were taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("src_hash") != _src_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def time_calls(dp, steps: int, warmup: int):
+    """Wall time per call and per-call event time on the launch stream."""
+    import torch
+
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        dp.run(stream)
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record(stream)
+        dp.run(stream)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    ev = sorted(s.elapsed_time(e) / 1e3 for s, e in zip(starts, ends))
+    return wall, sum(ev) / len(ev), ev[len(ev) // 2]
+
+
+def measure(prob, steps: int, warmup: int, num_splits=None):
+    from paged_kv_attention_15_amd import pkv
+
+    dp = pkv.upload(prob, "cuda", with_lse=False, with_err=False, num_splits=num_splits)
+    info = pkv.pkv_plan(dp.args, dp.is_context)
+    wall, ev_mean, ev_med = time_calls(dp, steps, warmup)
+    return dp, info, wall, ev_mean, ev_med
+
+
+def cpu_baseline(prob, max_pairs: int):
+    import numpy as np
+
+    import oracle
+
+    pairs = oracle.all_pairs(prob)
+    if len(pairs) > max_pairs:
+        idx = np.linspace(0, len(pairs) - 1, max_pairs).astype(np.int64)
+        pairs = pairs[idx]
+    t0 = time.perf_counter()
+    oracle.attention(prob, pairs)
+    dt = time.perf_counter() - t0
+    frac = len(pairs) / (prob.total_q * prob.num_qo_heads)
+    kv_bytes = prob.kv_bytes() * frac  # bytes the sample's rows read, counted like the GPU metric
+    return {"value": round(kv_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{len(pairs)} of {prob.total_q * prob.num_qo_heads} (query row, head) pairs of the "
+                      f"same workload, single-threaded fp64 C oracle, {dt:.1f} s"}
+
+
+def secondary_results(steps: int, warmup: int):
+    import torch
+
+    from paged_kv_attention_15_amd import pkv, workloads as W
+
+    out = {}
+    cases = [
+        ("fp8-gqa-b16-ragged", lambda: W.gqa_fp8_b16_ragged(), "hbm"),
+        ("mla-b512-kv4096-q1", lambda: W.mla_b512_kv4096(q_len=1), "hbm"),
+        ("mla-b512-kv4096-q2", lambda: W.mla_b512_kv4096(q_len=2), "mfma"),
+        ("ctx-b4-q511-kv2047", lambda: W.context_b4_q511_kv2047(), "mfma"),
+    ]
+    for name, make, bound in cases:
+        prob = make()
+        dp, info, wall, ev_mean, ev_med = measure(prob, steps, warmup)
+        gbs = prob.kv_bytes() / ev_mean / 1e9
+        tflops = prob.flops() / ev_mean / 1e12
+        rec = {"us_per_call": round(ev_mean * 1e6, 3), "us_median": round(ev_med * 1e6, 3),
+               "kernel": pkv.KERNEL_NAMES[info.kernel], "num_splits": info.num_splits,
+               "kv_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+               "tflops": round(tflops, 2), "mfma_frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
+               "bound": bound, "kv_bytes": prob.kv_bytes(), "flops": prob.flops()}
+        out[name] = rec
+        del dp
+        torch.cuda.empty_cache()
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--num-splits", type=int, default=None)
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-pairs", type=int, default=1024)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 1 GiB device-to-device copy (known bytes) to scale HBM counters")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}). "
+              f"Decode shards over requests or KV heads with no exchange; see the sharding note of the design.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from paged_kv_attention_15_amd import pkv, workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    pkv.load_library()
+    prob = W.gqa_bf16_b32_kv4096()
+    dp, info, wall, ev_mean, ev_med = measure(prob, args.steps, args.warmup, args.num_splits)
+    kv = prob.kv_bytes()
+    value = kv / wall / 1e9
+    achieved = kv / ev_mean / 1e9
+    single_kernel = info.num_splits == 1
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3, 5),
+        "us_per_call": round(ev_mean * 1e6, 3),
+        "us_per_call_median": round(ev_med * 1e6, 3),
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "bf16-gqa-b32-kv4096", "batch": 32, "q_len": 1, "num_qo_heads": 32,
+                   "num_kv_heads": 8, "head_dim": 128, "page_size": 32, "kv_len": 4096, "layout": "HND",
+                   "kv_dtype": "bf16", "kernel": pkv.KERNEL_NAMES[info.kernel], "num_splits": info.num_splits,
+                   "kv_bytes_per_call": kv},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": _traffic("bf16-gqa-b32-kv4096"),
+                     "kernel": "attn_mfma_kernel<gqa_bf16>" + ("" if single_kernel else " + lse_merge_kernel"),
+                     "timing": "HIP events on the launch stream around each call, mean over the timed steps"},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(prob, args.cpu_pairs)
+    del dp
+    torch.cuda.empty_cache()
+    if args.calibrate_copy:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        line["calibration_copy_bytes"] = src.numel() * 4
+        del src, dst
+        torch.cuda.empty_cache()
+    if not args.no_secondary:
+        line["secondary"] = secondary_results(max(20, args.steps // 4), max(5, args.warmup // 2))
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

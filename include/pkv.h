@@ -119,7 +119,8 @@ typedef struct pkv_args {
   int32_t causal;            /* 1: inclusive causal bound for multi-row requests */
   int32_t num_splits;        /* Split-KV partitions per (request, KV head); 0 = planner */
   int32_t v_shares_k;        /* 1: V is the first head_dim_v channels of the K rows (MLA) */
-  int32_t reserved0;
+  int32_t kernel_hint;       /* 0: planner picks; else a pkv_plan_info.kernel id to force
+                                (PKV_ERR_UNSUPPORTED when that family cannot run the shape) */
 
   const void* q;
   const void* k_pages;

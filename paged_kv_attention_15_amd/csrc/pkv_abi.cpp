@@ -132,24 +132,49 @@ pkv_status validate(const pkv_args* a, bool is_context) {
   return PKV_OK;
 }
 
-// Pick the kernel family for host-visible shapes (fail-closed routing: anything
-// the MFMA families cannot prove safe goes to the generic kernel).
-int32_t choose_kernel(const pkv_args* a, bool is_context) {
-  const bool bf16_q = a->q_dtype == PKV_DTYPE_BF16;
+// Can the MFMA families run these arguments at all (dtypes, power-of-two pages,
+// 16-byte aligned rows)?  Anything they cannot prove safe goes to the generic
+// kernel (fail-closed routing).
+bool mfma_eligible(const pkv_args* a) {
   const bool mfma_kv = a->kv_dtype == PKV_DTYPE_BF16 || a->kv_dtype == PKV_DTYPE_FP8_E4M3;
-  const bool fp8 = a->kv_dtype == PKV_DTYPE_FP8_E4M3;
   const int eb = elem_bytes(a->kv_dtype);
-  if (!bf16_q || !mfma_kv || !is_pow2(a->page_size)) return pkv::KERNEL_GENERIC;
-  // 16-byte alignment of every row the MFMA kernels load / store as vectors
+  if (a->q_dtype != PKV_DTYPE_BF16 || !mfma_kv || !is_pow2(a->page_size)) return false;
   auto al = [&](int64_t stride_elems, int bytes) { return (stride_elems * bytes) % 16 == 0; };
-  if (!aligned16(a->q) || !aligned16(a->k_pages) || !aligned16(a->out)) return pkv::KERNEL_GENERIC;
-  if (!a->v_shares_k && !aligned16(a->v_pages)) return pkv::KERNEL_GENERIC;
-  if (!al(a->q_stride_tok, 2) || !al(a->q_stride_head, 2)) return pkv::KERNEL_GENERIC;
+  if (!aligned16(a->q) || !aligned16(a->k_pages) || !aligned16(a->out)) return false;
+  if (!a->v_shares_k && !aligned16(a->v_pages)) return false;
+  if (!al(a->q_stride_tok, 2) || !al(a->q_stride_head, 2)) return false;
   const int ob = elem_bytes(a->o_dtype);
-  if ((a->o_stride_tok * ob) % 8 != 0 || (a->o_stride_head * ob) % 8 != 0) return pkv::KERNEL_GENERIC;
-  if (!al(a->k_stride_page, eb) || !al(a->k_stride_head, eb) || !al(a->k_stride_tok, eb)) return pkv::KERNEL_GENERIC;
+  if ((a->o_stride_tok * ob) % 8 != 0 || (a->o_stride_head * ob) % 8 != 0) return false;
+  if (!al(a->k_stride_page, eb) || !al(a->k_stride_head, eb) || !al(a->k_stride_tok, eb)) return false;
   if (!a->v_shares_k && (!al(a->v_stride_page, eb) || !al(a->v_stride_head, eb) || !al(a->v_stride_tok, eb)))
-    return pkv::KERNEL_GENERIC;
+    return false;
+  return true;
+}
+
+// Does kernel family k cover these arguments?
+bool kernel_supports(int32_t k, const pkv_args* a, bool is_context) {
+  if (k == pkv::KERNEL_GENERIC) return a->head_dim_qk <= 1024 && a->head_dim_v <= 512;
+  if (k <= pkv::KERNEL_GENERIC || k >= pkv::KERNEL_COUNT || !mfma_eligible(a)) return false;
+  const bool fp8 = a->kv_dtype == PKV_DTYPE_FP8_E4M3;
+  const int G = a->num_qo_heads / a->num_kv_heads;
+  const bool d128 = a->head_dim_qk == 128 && a->head_dim_v == 128 && !a->v_shares_k;
+  const bool mla = a->head_dim_qk == 576 && a->head_dim_v == 512 && a->v_shares_k;
+  switch (k) {
+    case pkv::KERNEL_GQA_BF16:
+    case pkv::KERNEL_GQA_BF16_T256:
+      return d128 && !fp8 && !is_context && (int64_t)a->q_len * G <= 16;
+    case pkv::KERNEL_GQA_FP8: return d128 && fp8 && !is_context && (int64_t)a->q_len * G <= 16;
+    case pkv::KERNEL_WIDE_BF16: return d128 && !fp8;
+    case pkv::KERNEL_WIDE_FP8: return d128 && fp8;
+    case pkv::KERNEL_MLA_BF16: return mla && !fp8;
+    case pkv::KERNEL_MLA_FP8: return mla && fp8;
+  }
+  return false;
+}
+
+int32_t choose_kernel(const pkv_args* a, bool is_context) {
+  if (!mfma_eligible(a)) return pkv::KERNEL_GENERIC;
+  const bool fp8 = a->kv_dtype == PKV_DTYPE_FP8_E4M3;
   const int G = a->num_qo_heads / a->num_kv_heads;
   if (a->head_dim_qk == 128 && a->head_dim_v == 128 && !a->v_shares_k) {
     const int64_t rows = is_context ? (int64_t)a->max_q_len * G : (int64_t)a->q_len * G;
@@ -166,9 +191,10 @@ pkv_status make_plan(const pkv_args* a, bool is_context, int num_cus, pkv_plan_i
   if (st != PKV_OK) return st;
   if (num_cus <= 0) num_cus = 256;
   std::memset(info, 0, sizeof *info);
-  const int32_t kernel = choose_kernel(a, is_context);
-  if (kernel == pkv::KERNEL_GENERIC && (a->head_dim_qk > 1024 || a->head_dim_v > 512))
-    return fail(PKV_ERR_UNSUPPORTED, "head dims above 1024 (qk) / 512 (v) have no kernel");
+  const int32_t kernel = a->kernel_hint ? a->kernel_hint : choose_kernel(a, is_context);
+  if (!kernel_supports(kernel, a, is_context))
+    return fail(PKV_ERR_UNSUPPORTED, a->kernel_hint ? "kernel_hint %d cannot run these arguments"
+                                                    : "no kernel for these arguments (family %d)", kernel);
   info->kernel = kernel;
   const int G = a->num_qo_heads / a->num_kv_heads;
   const int64_t rows_per_kv = is_context ? (int64_t)a->max_q_len * G : (int64_t)a->q_len * G;
@@ -192,17 +218,23 @@ pkv_status make_plan(const pkv_args* a, bool is_context, int num_cus, pkv_plan_i
     info->grid_y = a->num_qo_heads;
   }
 
-  // Split-KV sizing: enough partitions that the grid covers the CUs about
-  // twice, each partition a whole number of pages and at least one tile long.
+  // Split-KV sizing.  When the (request, KV head, row block) units already
+  // fill the CUs, one partition per unit streams each request's pages once and
+  // needs no reducer.  Otherwise cut every unit into page-aligned partitions so
+  // the longest request yields about four partitions per CU: the planner only
+  // knows max_kv_len, so shorter requests simply own fewer live partitions
+  // (the rest exit at once and are never merged).
   int S = a->num_splits;
   int64_t pps;
   if (S == 0) {
-    const int64_t want = std::max<int64_t>(1, (2 * (int64_t)num_cus + units - 1) / std::max<int64_t>(units, 1));
-    // at least four tiles per partition
-    const int64_t min_pages = std::max<int64_t>(1, (4 * (int64_t)tile_tokens + a->page_size - 1) / a->page_size);
-    int64_t s_cap = std::max<int64_t>(1, max_pages / min_pages);
-    S = (int)std::min<int64_t>(std::min<int64_t>(want, s_cap), kMaxSplits);
-    S = std::max(S, 1);
+    if (units >= num_cus) {
+      S = 1;
+    } else {
+      const int64_t want = (4 * (int64_t)num_cus + units - 1) / std::max<int64_t>(units, 1);
+      const int64_t min_pages = std::max<int64_t>(1, (tile_tokens + a->page_size - 1) / a->page_size);
+      const int64_t s_cap = std::max<int64_t>(1, max_pages / min_pages);
+      S = (int)std::max<int64_t>(1, std::min<int64_t>(std::min<int64_t>(want, s_cap), kMaxSplits));
+    }
   }
   pps = std::max<int64_t>(1, (max_pages + S - 1) / S);
   // round partitions up to whole tiles when pages are smaller than a tile
@@ -312,8 +344,30 @@ pkv_status run(const pkv_args* a, bool is_context, void* ws, size_t ws_bytes, vo
   hipError_t e = plan.kernel == pkv::KERNEL_GENERIC ? pkv::launch_generic(p, s) : pkv::launch_mfma(plan.kernel, p, s);
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "attention launch failed: %s", hipGetErrorString(e));
   if (plan.num_splits > 1) {
-    e = pkv::launch_merge(plan.num_splits, p.rows_total, a->num_qo_heads, a->head_dim_v, p.ws_o, p.ws_lse, a->out,
-                          a->o_dtype, a->o_stride_tok, a->o_stride_head, a->lse_out, s);
+    pkv::MergeParams mp;
+    std::memset(&mp, 0, sizeof mp);
+    mp.num_splits = plan.num_splits;
+    mp.num_qo_heads = a->num_qo_heads;
+    mp.dv = a->head_dim_v;
+    mp.o_dtype = a->o_dtype;
+    mp.num_rows = p.rows_total;
+    mp.o_st = a->o_stride_tok;
+    mp.o_sh = a->o_stride_head;
+    mp.o_part = p.ws_o;
+    mp.lse_part = p.ws_lse;
+    mp.out = a->out;
+    mp.lse_out = a->lse_out;
+    mp.seq_lens = a->seq_lens;
+    mp.q_indptr = p.q_indptr;
+    mp.batch = a->batch;
+    mp.q_len = p.q_len;
+    mp.causal = p.causal;
+    mp.is_context = p.is_context;
+    mp.split_tokens = plan.pages_per_split * a->page_size;
+    mp.cap_tokens = a->max_pages_per_seq * a->page_size;
+    mp.max_q_len = p.max_q_len;
+    mp.total_q = p.total_q;
+    e = pkv::launch_merge(mp, s);
     if (e != hipSuccess) return fail(PKV_ERR_HIP, "merge launch failed: %s", hipGetErrorString(e));
   }
   return ok();
@@ -368,8 +422,20 @@ pkv_status pkv_lse_merge(int32_t num_splits, int32_t num_rows, int32_t num_qo_he
     return fail(PKV_ERR_INVALID_ARG, "out strides too small for head_dim_v");
   if (num_rows == 0) return ok();
   if (!o_part || !lse_part || !out) return fail(PKV_ERR_INVALID_ARG, "o_part, lse_part and out are required");
-  hipError_t e = pkv::launch_merge(num_splits, num_rows, num_qo_heads, head_dim_v, o_part, lse_part, out, o_dtype,
-                                   o_stride_tok, o_stride_head, lse_out, reinterpret_cast<hipStream_t>(stream));
+  pkv::MergeParams mp;
+  std::memset(&mp, 0, sizeof mp);
+  mp.num_splits = num_splits;
+  mp.num_qo_heads = num_qo_heads;
+  mp.dv = head_dim_v;
+  mp.o_dtype = o_dtype;
+  mp.num_rows = num_rows;
+  mp.o_st = o_stride_tok;
+  mp.o_sh = o_stride_head;
+  mp.o_part = o_part;
+  mp.lse_part = lse_part;
+  mp.out = out;
+  mp.lse_out = lse_out;
+  hipError_t e = pkv::launch_merge(mp, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "merge launch failed: %s", hipGetErrorString(e));
   return ok();
 }

@@ -74,6 +74,8 @@ __global__ __launch_bounds__(64) void attn_generic_kernel(const KParams p) {
   const int kv_lo = split * p.pages_per_split * p.page_size;
   const int kv_hi = min(kv_lo + p.pages_per_split * p.page_size, c);
 
+  if (kv_hi <= kv_lo && p.ws_o != nullptr) return;  // partition the reducer never reads
+
   const float k_scale = p.k_scale_dev ? *p.k_scale_dev : p.k_scale;
   const float v_scale = p.v_scale_dev ? *p.v_scale_dev : p.v_scale;
   const float sc2 = p.scale * k_scale * kLog2e;
@@ -170,62 +172,108 @@ hipError_t launch_generic(const KParams& p, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------- LSE merge
-// one wavefront per merged row; each lane owns channels lane, lane+64, ...
+// One wavefront per merged row; lane k first loads partition k's LSE (so all
+// statistics arrive together), the weights are then broadcast with readlane
+// and every lane accumulates channels lane, lane+64, ...  The partial rows are
+// loaded unconditionally (their addresses do not depend on earlier values, so
+// the loads pipeline) and an empty partition is selected out, never multiplied.
+// With request geometry attached (decode / context calls) a row reads only
+// the partitions that can hold one of its visible keys: the attention kernel
+// skips the rest without writing them.
 constexpr int kMergeRowsPerBlock = 4;
 
-__global__ __launch_bounds__(64 * kMergeRowsPerBlock) void lse_merge_kernel(
-    int32_t num_splits, int64_t num_rows, int32_t num_qo_heads, int32_t dv, const float* __restrict__ o_part,
-    const float* __restrict__ lse_part, void* out, int32_t o_dtype, int64_t o_st, int64_t o_sh,
-    float* lse_out) {
+__device__ __forceinline__ float readlane_f(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+__global__ __launch_bounds__(64 * kMergeRowsPerBlock) void lse_merge_kernel(const MergeParams mp) {
   const int lane = threadIdx.x & 63;
   const int64_t r = (int64_t)blockIdx.x * kMergeRowsPerBlock + (threadIdx.x >> 6);
-  if (r >= num_rows) return;
+  if (r >= mp.num_rows) return;
+  const int64_t t = r / mp.num_qo_heads;
+  const int h = (int)(r % mp.num_qo_heads);
+  const int dv = mp.dv;
+
+  int live = mp.num_splits;
+  if (mp.seq_lens) {
+    int b, t0, n;
+    if (mp.is_context) {
+      int lo = 0, hi = mp.batch - 1;
+      while (lo < hi) {
+        int mid = (lo + hi + 1) >> 1;
+        if (mp.q_indptr[mid] <= t) lo = mid; else hi = mid - 1;
+      }
+      b = lo;
+      t0 = mp.q_indptr[b];
+      const int a1 = mp.q_indptr[b + 1];
+      const bool bad = (t0 < 0) || (a1 < t0) || (a1 - t0 > mp.max_q_len) || (a1 > mp.total_q);
+      if (bad || t < t0 || t >= a1) return;  // the attention kernel skipped this row too
+      n = a1 - t0;
+    } else {
+      b = (int)(t / mp.q_len);
+      t0 = b * mp.q_len;
+      n = mp.q_len;
+    }
+    const int i = (int)(t - t0);
+    const int L = max(0, min(mp.seq_lens[b], mp.cap_tokens));
+    const int c = mp.causal ? min(L, max(0, L - n + i + 1)) : L;
+    live = min(mp.num_splits, (c + mp.split_tokens - 1) / mp.split_tokens);
+  }
+
   float M = -INFINITY;
-  for (int s = 0; s < num_splits; ++s) M = fmaxf(M, lse_part[(int64_t)s * num_rows + r]);
-  const int64_t t = r / num_qo_heads;
-  const int h = (int)(r % num_qo_heads);
-  float wsum = 0.f;
+  for (int s0 = 0; s0 < live; s0 += 64) {
+    const int s = s0 + lane;
+    if (s < live) M = fmaxf(M, mp.lse_part[(int64_t)s * mp.num_rows + r]);
+  }
+  M = wave_max(M);
+
   float acc[8];
-  const int per_lane = (dv + 63) / 64;  // <= 8 (head_dim_v <= 512)
 #pragma unroll
   for (int k = 0; k < 8; ++k) acc[k] = 0.f;
+  float wlane = 0.f;
   if (M != -INFINITY) {
-    for (int s = 0; s < num_splits; ++s) {
-      const float ls = lse_part[(int64_t)s * num_rows + r];
-      if (ls == -INFINITY) continue;  // empty partition: weight 0, row never read
-      const float w = __expf(ls - M);
-      wsum += w;
-      const float* src = o_part + ((int64_t)s * num_rows + r) * dv;
+    for (int s0 = 0; s0 < live; s0 += 64) {
+      const int s = s0 + lane;
+      const float ls = s < live ? mp.lse_part[(int64_t)s * mp.num_rows + r] : -INFINITY;
+      const float w = (ls == -INFINITY) ? 0.f : __expf(ls - M);
+      wlane += w;
+      const int nsp = min(64, live - s0);
+#pragma unroll 4
+      for (int j = 0; j < nsp; ++j) {
+        const float wj = readlane_f(w, j);
+        const float* src = mp.o_part + ((int64_t)(s0 + j) * mp.num_rows + r) * dv;
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int d = lane + 64 * k;
-        if (k < per_lane && d < dv) acc[k] += w * src[d];
+        for (int k = 0; k < 8; ++k) {
+          const int d = lane + 64 * k;
+          if (d < dv) {
+            const float v = src[d];
+            acc[k] = (wj > 0.f) ? fmaf(wj, v, acc[k]) : acc[k];
+          }
+        }
       }
     }
   }
+  const float wsum = wave_sum(wlane);
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     const int d = lane + 64 * k;
-    if (k >= per_lane || d >= dv) continue;
+    if (d >= dv) continue;
     const float v = acc[k] * inv;
-    const int64_t oi = t * o_st + (int64_t)h * o_sh + d;
-    if (o_dtype == PKV_DTYPE_BF16) {
-      ((__bf16*)out)[oi] = (__bf16)v;
+    const int64_t oi = t * mp.o_st + (int64_t)h * mp.o_sh + d;
+    if (mp.o_dtype == PKV_DTYPE_BF16) {
+      ((__bf16*)mp.out)[oi] = (__bf16)v;
     } else {
-      ((float*)out)[oi] = v;
+      ((float*)mp.out)[oi] = v;
     }
   }
-  if (lse_out && lane == 0) lse_out[r] = (M == -INFINITY) ? -INFINITY : M + __logf(wsum);
+  if (mp.lse_out && lane == 0) mp.lse_out[r] = (M == -INFINITY) ? -INFINITY : M + __logf(wsum);
 }
 
-hipError_t launch_merge(int32_t num_splits, int64_t num_rows, int32_t num_qo_heads, int32_t head_dim_v,
-                        const float* o_part, const float* lse_part, void* out, int32_t o_dtype,
-                        int64_t o_st, int64_t o_sh, float* lse_out, hipStream_t s) {
-  if (num_rows == 0) return hipSuccess;
-  dim3 grid((unsigned)((num_rows + kMergeRowsPerBlock - 1) / kMergeRowsPerBlock));
-  hipLaunchKernelGGL(lse_merge_kernel, grid, dim3(64 * kMergeRowsPerBlock), 0, s, num_splits, num_rows,
-                     num_qo_heads, head_dim_v, o_part, lse_part, out, o_dtype, o_st, o_sh, lse_out);
+hipError_t launch_merge(const MergeParams& mp, hipStream_t s) {
+  if (mp.num_rows == 0) return hipSuccess;
+  dim3 grid((unsigned)((mp.num_rows + kMergeRowsPerBlock - 1) / kMergeRowsPerBlock));
+  hipLaunchKernelGGL(lse_merge_kernel, grid, dim3(64 * kMergeRowsPerBlock), 0, s, mp);
   return hipGetLastError();
 }
 

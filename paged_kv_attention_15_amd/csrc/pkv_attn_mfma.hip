@@ -36,9 +36,9 @@
 
 namespace pkv {
 
-template <int DQK_, int DV_, bool FP8_, bool VSHARE_, int RT_, int NWR_, int NWT_, int TT_>
+template <int DQK_, int DV_, bool FP8_, bool VSHARE_, int RT_, int NWR_, int NWT_, int TT_, int NSTAGE_ = 2>
 struct TileCfg {
-  static constexpr int DQK = DQK_, DV = DV_, RT = RT_, NWR = NWR_, NWT = NWT_, TT = TT_;
+  static constexpr int DQK = DQK_, DV = DV_, RT = RT_, NWR = NWR_, NWT = NWT_, TT = TT_, NSTAGE = NSTAGE_;
   static constexpr bool FP8 = FP8_, VSHARE = VSHARE_;
   static constexpr int NW = NWR * NWT;
   static constexpr int NTHR = 64 * NW;
@@ -60,7 +60,8 @@ struct TileCfg {
   // reduction scratch when several waves split the tile's tokens
   static constexpr int RED_O = NWT > 1 ? NW * RT * NDB * 64 * 16 : 0;
   static constexpr int RED_ML = NWT > 1 ? NW * RT * 64 * 2 * 4 : 0;
-  static constexpr int LDS = (2 * STAGE > RED_O + RED_ML) ? 2 * STAGE : RED_O + RED_ML;
+  static constexpr int LDS = (NSTAGE * STAGE > RED_O + RED_ML) ? NSTAGE * STAGE : RED_O + RED_ML;
+  static_assert(NSTAGE == 1 || NSTAGE == 2, "one or two LDS stages");
   static_assert((T * SCK) % NTHR == 0, "K gather must split evenly");
   static_assert(VSHARE || (T * SCV) % NTHR == 0, "V gather must split evenly");
   static_assert(TT % 32 == 0 && DQK % 32 == 0 && DV % 16 == 0, "MFMA tiling");
@@ -141,6 +142,8 @@ __global__ __launch_bounds__(C::NTHR) void attn_mfma_kernel(const KParams p) {
   const int kv_lo = split * p.pages_per_split * p.page_size;
   const int kv_hi = min(kv_lo + p.pages_per_split * p.page_size, c_max);
   const int n_tiles = kv_hi > kv_lo ? (kv_hi - kv_lo + C::T - 1) / C::T : 0;
+  // a partition past every row's visible keys: the reducer never reads it
+  if (n_tiles == 0 && p.ws_o != nullptr) return;
 
   // ---- page list of the partition -> LDS (clamped to the pool)
   const int pg_lo = kv_lo >> p.log2_page;
@@ -265,7 +268,7 @@ __global__ __launch_bounds__(C::NTHR) void attn_mfma_kernel(const KParams p) {
   __syncthreads();
 
   for (int tile = 0; tile < n_tiles; ++tile) {
-    const int stage = tile & 1;
+    const int stage = C::NSTAGE == 2 ? (tile & 1) : 0;
     if (tile + 1 < n_tiles) gather(tile + 1);
 
     const unsigned char* kst = smem + stage * C::STAGE;
@@ -349,8 +352,16 @@ __global__ __launch_bounds__(C::NTHR) void attn_mfma_kernel(const KParams p) {
       }
     }
 
-    if (tile + 1 < n_tiles) stash(stage ^ 1);
-    __syncthreads();
+    if constexpr (C::NSTAGE == 2) {
+      if (tile + 1 < n_tiles) stash(stage ^ 1);
+      __syncthreads();
+    } else {
+      if (tile + 1 < n_tiles) {
+        __syncthreads();  // every wave is done reading the stage
+        stash(0);
+        __syncthreads();
+      }
+    }
   }
 
   // ---- full row sums (the 4 lanes of a row hold partial sums)
@@ -451,7 +462,8 @@ __global__ __launch_bounds__(C::NTHR) void attn_mfma_kernel(const KParams p) {
 
 // ---------------------------------------------------------------- instances
 using CfgGqaBf16 = TileCfg<128, 128, false, false, 1, 1, 4, 32>;
-using CfgGqaFp8 = TileCfg<128, 128, true, false, 1, 1, 4, 32>;
+using CfgGqaFp8 = TileCfg<128, 128, true, false, 1, 1, 4, 64, 1>;
+using CfgGqaBf16T256 = TileCfg<128, 128, false, false, 1, 1, 4, 64, 1>;
 using CfgWideBf16 = TileCfg<128, 128, false, false, 2, 4, 1, 64>;
 using CfgWideFp8 = TileCfg<128, 128, true, false, 2, 4, 1, 64>;
 using CfgMlaBf16 = TileCfg<576, 512, false, true, 2, 4, 1, 32>;
@@ -469,6 +481,7 @@ bool mfma_shape(int32_t kernel, MfmaShape* s) {
   switch (kernel) {
     case KERNEL_GQA_BF16: fill_shape<CfgGqaBf16>(s); return true;
     case KERNEL_GQA_FP8: fill_shape<CfgGqaFp8>(s); return true;
+    case KERNEL_GQA_BF16_T256: fill_shape<CfgGqaBf16T256>(s); return true;
     case KERNEL_WIDE_BF16: fill_shape<CfgWideBf16>(s); return true;
     case KERNEL_WIDE_FP8: fill_shape<CfgWideFp8>(s); return true;
     case KERNEL_MLA_BF16: fill_shape<CfgMlaBf16>(s); return true;
@@ -496,6 +509,7 @@ hipError_t launch_mfma(int32_t kernel, const KParams& p, hipStream_t s) {
   switch (kernel) {
     case KERNEL_GQA_BF16: return launch_cfg<CfgGqaBf16>(p, s);
     case KERNEL_GQA_FP8: return launch_cfg<CfgGqaFp8>(p, s);
+    case KERNEL_GQA_BF16_T256: return launch_cfg<CfgGqaBf16T256>(p, s);
     case KERNEL_WIDE_BF16: return launch_cfg<CfgWideBf16>(p, s);
     case KERNEL_WIDE_FP8: return launch_cfg<CfgWideFp8>(p, s);
     case KERNEL_MLA_BF16: return launch_cfg<CfgMlaBf16>(p, s);

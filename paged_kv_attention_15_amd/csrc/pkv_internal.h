@@ -19,6 +19,8 @@ enum KernelId : int32_t {
   KERNEL_WIDE_FP8 = 5,
   KERNEL_MLA_BF16 = 6,    // MFMA, 128 heads on one latent KV head, D_qk = 576, D_v = 512
   KERNEL_MLA_FP8 = 7,
+  KERNEL_GQA_BF16_T256 = 8,  // GQA bf16 with 256-token tiles in one LDS stage
+  KERNEL_COUNT = 9,
 };
 
 // Everything a kernel reads, by value.  Element strides as in pkv_args.
@@ -56,9 +58,22 @@ struct LaunchShape {
 // Launchers (return hipSuccess or the launch error).
 hipError_t launch_generic(const KParams& p, hipStream_t s);
 hipError_t launch_mfma(int32_t kernel, const KParams& p, hipStream_t s);
-hipError_t launch_merge(int32_t num_splits, int64_t num_rows, int32_t num_qo_heads, int32_t head_dim_v,
-                        const float* o_part, const float* lse_part, void* out, int32_t o_dtype,
-                        int64_t o_st, int64_t o_sh, float* lse_out, hipStream_t s);
+// Split-KV reducer arguments.  seq_lens == nullptr: every partition of every
+// row is live (the standalone entry point); otherwise the request geometry
+// gives each row its live partition count.
+struct MergeParams {
+  int32_t num_splits, num_qo_heads, dv, o_dtype;
+  int64_t num_rows, o_st, o_sh;
+  const float* o_part;
+  const float* lse_part;
+  void* out;
+  float* lse_out;
+  const int32_t* seq_lens;
+  const int32_t* q_indptr;
+  int32_t batch, q_len, causal, is_context;
+  int32_t split_tokens, cap_tokens, max_q_len, total_q;
+};
+hipError_t launch_merge(const MergeParams& mp, hipStream_t s);
 
 // Static shape facts of the MFMA kernel families (host-side planner input).
 struct MfmaShape {

@@ -21,7 +21,8 @@ PKV_LAYOUT_HND, PKV_LAYOUT_NHD = range(2)
 PKV_DEVERR_SEQ_LT_QLEN, PKV_DEVERR_SEQ_GT_TABLE, PKV_DEVERR_PAGE_RANGE, PKV_DEVERR_QINDPTR = 1, 2, 4, 8
 
 KERNEL_NAMES = {0: "none", 1: "generic", 2: "gqa_bf16", 3: "gqa_fp8", 4: "wide_bf16", 5: "wide_fp8",
-                6: "mla_bf16", 7: "mla_fp8"}
+                6: "mla_bf16", 7: "mla_fp8", 8: "gqa_bf16_t256"}
+KERNEL_IDS = {v: k for k, v in KERNEL_NAMES.items()}
 
 DTYPE_CODES = {"f32": PKV_DTYPE_F32, "bf16": PKV_DTYPE_BF16, "e4m3": PKV_DTYPE_FP8_E4M3}
 EXPORTED = ["pkv_abi_version", "pkv_last_error", "pkv_plan", "pkv_workspace_bytes", "pkv_decode",
@@ -37,7 +38,7 @@ class PkvArgs(C.Structure):
         ("max_q_len", C.c_int32), ("total_q", C.c_int32), ("num_pages", C.c_int32),
         ("q_dtype", C.c_int32), ("kv_dtype", C.c_int32), ("o_dtype", C.c_int32),
         ("layout", C.c_int32), ("causal", C.c_int32), ("num_splits", C.c_int32),
-        ("v_shares_k", C.c_int32), ("reserved0", C.c_int32),
+        ("v_shares_k", C.c_int32), ("kernel_hint", C.c_int32),
         ("q", C.c_void_p), ("k_pages", C.c_void_p), ("v_pages", C.c_void_p),
         ("block_tables", C.c_void_p), ("seq_lens", C.c_void_p), ("q_indptr", C.c_void_p),
         ("out", C.c_void_p), ("lse_out", C.c_void_p), ("err_word", C.c_void_p),
@@ -195,7 +196,7 @@ def _to_device(arr, device):
 
 
 def upload(prob, device="cuda", with_lse: bool = True, with_err: bool = True, num_splits: Optional[int] = None,
-           device_scales: bool = False) -> DeviceProblem:
+           device_scales: bool = False, kernel: Optional[str] = None) -> DeviceProblem:
     """Copy a workloads.Problem to `device` and fill pkv_args for it."""
     torch = _torch()
     t = {}
@@ -216,6 +217,8 @@ def upload(prob, device="cuda", with_lse: bool = True, with_err: bool = True, nu
         t["k_scale"] = torch.tensor([prob.k_scale], dtype=torch.float32, device=device)
         t["v_scale"] = torch.tensor([prob.v_scale], dtype=torch.float32, device=device)
     a = fill_args(prob, t, num_splits=num_splits)
+    if kernel is not None:
+        a.kernel_hint = KERNEL_IDS[kernel]
     is_ctx = not prob.is_decode
     ws_bytes = pkv_workspace_bytes(a, is_ctx)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=device) if ws_bytes > 0 else None
