@@ -52,24 +52,27 @@ def _traffic(workload: str):
 
 
 def time_calls(dp, steps: int, warmup: int):
-    """Wall time per call and per-call event time on the launch stream."""
+    """Time `steps` back-to-back calls after `warmup` untimed ones.
+
+    Returns (wall seconds per call from the host clock between two device
+    synchronizations, device seconds per call from one pair of HIP events
+    recorded on the launch stream around the same calls)."""
     import torch
 
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
         dp.run(stream)
     torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    for i in range(steps):
-        starts[i].record(stream)
+    e0.record(stream)
+    for _ in range(steps):
         dp.run(stream)
-        ends[i].record(stream)
+    e1.record(stream)
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / steps
-    ev = sorted(s.elapsed_time(e) / 1e3 for s, e in zip(starts, ends))
-    return wall, sum(ev) / len(ev), ev[len(ev) // 2]
+    return wall, e0.elapsed_time(e1) / 1e3 / steps
 
 
 def measure(prob, steps: int, warmup: int, num_splits=None):
@@ -77,8 +80,8 @@ def measure(prob, steps: int, warmup: int, num_splits=None):
 
     dp = pkv.upload(prob, "cuda", with_lse=False, with_err=False, num_splits=num_splits)
     info = pkv.pkv_plan(dp.args, dp.is_context)
-    wall, ev_mean, ev_med = time_calls(dp, steps, warmup)
-    return dp, info, wall, ev_mean, ev_med
+    wall, ev_mean = time_calls(dp, steps, warmup)
+    return dp, info, wall, ev_mean
 
 
 def cpu_baseline(prob, max_pairs: int):
@@ -114,10 +117,10 @@ def secondary_results(steps: int, warmup: int):
     ]
     for name, make, bound in cases:
         prob = make()
-        dp, info, wall, ev_mean, ev_med = measure(prob, steps, warmup)
+        dp, info, wall, ev_mean = measure(prob, steps, warmup)
         gbs = prob.kv_bytes() / ev_mean / 1e9
         tflops = prob.flops() / ev_mean / 1e12
-        rec = {"us_per_call": round(ev_mean * 1e6, 3), "us_median": round(ev_med * 1e6, 3),
+        rec = {"us_per_call": round(ev_mean * 1e6, 3),
                "kernel": pkv.KERNEL_NAMES[info.kernel], "num_splits": info.num_splits,
                "kv_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
                "tflops": round(tflops, 2), "mfma_frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
@@ -154,7 +157,7 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     pkv.load_library()
     prob = W.gqa_bf16_b32_kv4096()
-    dp, info, wall, ev_mean, ev_med = measure(prob, args.steps, args.warmup, args.num_splits)
+    dp, info, wall, ev_mean = measure(prob, args.steps, args.warmup, args.num_splits)
     kv = prob.kv_bytes()
     value = kv / wall / 1e9
     achieved = kv / ev_mean / 1e9
@@ -168,7 +171,6 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(wall * 1e3, 5),
         "us_per_call": round(ev_mean * 1e6, 3),
-        "us_per_call_median": round(ev_med * 1e6, 3),
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "higher_is_better": True,
         "scaling": "weak",
@@ -182,7 +184,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": _traffic("bf16-gqa-b32-kv4096"),
                      "kernel": "attn_mfma_kernel<gqa_bf16>" + ("" if single_kernel else " + lse_merge_kernel"),
-                     "timing": "HIP events on the launch stream around each call, mean over the timed steps"},
+                     "timing": "one HIP event pair on the launch stream around the timed back-to-back calls"},
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(prob, args.cpu_pairs)
