@@ -33,7 +33,7 @@ KERNEL_SRC = os.path.join(ROOT, "paged_kv_attention_15_amd", "csrc", "pkv_attn_m
 
 def _src_hash() -> str:
     h = hashlib.sha256()
-    for name in ("pkv_attn_mfma.hip", "pkv_attn_generic.hip", "pkv_device.h", "pkv_abi.cpp"):
+    for name in ("pkv_attn_mfma.hip", "pkv_attn_dma.hip", "pkv_attn_generic.hip", "pkv_device.h", "pkv_abi.cpp"):
         with open(os.path.join(ROOT, "paged_kv_attention_15_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -183,7 +183,7 @@ def main():
                    "kv_bytes_per_call": kv},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": _traffic("bf16-gqa-b32-kv4096"),
-                     "kernel": "attn_mfma_kernel<gqa_bf16>" + ("" if single_kernel else " + lse_merge_kernel"),
+                     "kernel": f"{pkv.KERNEL_NAMES[info.kernel]} attention kernel" + ("" if single_kernel else " + lse_merge_kernel"),
                      "timing": "one HIP event pair on the launch stream around the timed back-to-back calls"},
     }
     if not args.no_cpu_baseline:

@@ -117,7 +117,8 @@ typedef struct pkv_args {
   int32_t o_dtype;           /* pkv_dtype: F32 or BF16 */
   int32_t layout;            /* pkv_layout (only used to validate strides) */
   int32_t causal;            /* 1: inclusive causal bound for multi-row requests */
-  int32_t num_splits;        /* Split-KV partitions per (request, KV head); 0 = planner */
+  int32_t num_splits;        /* Split-KV partitions per (request, KV head); 0 = planner;
+                                -1 = balanced decode schedule (GQA decode families only) */
   int32_t v_shares_k;        /* 1: V is the first head_dim_v channels of the K rows (MLA) */
   int32_t kernel_hint;       /* 0: planner picks; else a pkv_plan_info.kernel id to force
                                 (PKV_ERR_UNSUPPORTED when that family cannot run the shape) */
@@ -153,7 +154,9 @@ typedef struct pkv_plan_info {
   int32_t pages_per_split; /* page-aligned partition length, in pages */
   int32_t grid_x, grid_y, grid_z;
   int32_t block_threads;
-  int32_t reserved;
+  int32_t schedule;        /* 0: per-unit partitions, grid (num_splits, Hkv x row blocks, B);
+                              1: balanced decode schedule, grid_x workgroups own equal page
+                                 ranges of all requests; num_splits then counts partial slots */
   size_t workspace_bytes;  /* 0 when num_splits == 1 */
 } pkv_plan_info;
 

@@ -89,8 +89,9 @@ pkv_status validate(const pkv_args* a, bool is_context) {
     return fail(PKV_ERR_INVALID_ARG, "layout %d unknown", a->layout);
   if (!(a->scale > 0.f) || !(a->k_scale > 0.f) || !(a->v_scale > 0.f))
     return fail(PKV_ERR_INVALID_ARG, "scale, k_scale and v_scale must be positive and finite");
-  if (a->num_splits < 0 || a->num_splits > kMaxSplits)
-    return fail(PKV_ERR_INVALID_ARG, "num_splits must be in [0, %d]", kMaxSplits);
+  if (a->num_splits < -1 || a->num_splits > kMaxSplits)
+    return fail(PKV_ERR_INVALID_ARG, "num_splits must be -1 (balanced schedule), 0 (planner) or in [1, %d]",
+                kMaxSplits);
   if (is_context) {
     if (a->max_q_len < 0 || a->total_q < 0) return fail(PKV_ERR_INVALID_ARG, "max_q_len / total_q must be >= 0");
   } else {
@@ -162,27 +163,69 @@ bool kernel_supports(int32_t k, const pkv_args* a, bool is_context) {
   switch (k) {
     case pkv::KERNEL_GQA_BF16:
     case pkv::KERNEL_GQA_BF16_T256:
+    case pkv::KERNEL_GQA_BF16_S1:
+    case pkv::KERNEL_GQA_BF16_W2:
       return d128 && !fp8 && !is_context && (int64_t)a->q_len * G <= 16;
-    case pkv::KERNEL_GQA_FP8: return d128 && fp8 && !is_context && (int64_t)a->q_len * G <= 16;
+    case pkv::KERNEL_GQA_FP8:
+    case pkv::KERNEL_GQA_FP8_T128:
+    case pkv::KERNEL_GQA_FP8_S2:
+      return d128 && fp8 && !is_context && (int64_t)a->q_len * G <= 16;
     case pkv::KERNEL_WIDE_BF16: return d128 && !fp8;
     case pkv::KERNEL_WIDE_FP8: return d128 && fp8;
     case pkv::KERNEL_MLA_BF16: return mla && !fp8;
     case pkv::KERNEL_MLA_FP8: return mla && fp8;
+    case pkv::KERNEL_DMA_GQA_BF16:
+    case pkv::KERNEL_DMA_GQA_BF16_W4:
+    case pkv::KERNEL_DMA_GQA_BF16_S2:
+      return d128 && !fp8 && !is_context && (int64_t)a->q_len * G <= 16;
+    case pkv::KERNEL_DMA_GQA_FP8:
+    case pkv::KERNEL_DMA_GQA_FP8_W8:
+    case pkv::KERNEL_DMA_GQA_FP8_S2:
+      return d128 && fp8 && !is_context && (int64_t)a->q_len * G <= 16;
+    case pkv::KERNEL_DMA_WIDE_BF16: return d128 && !fp8;
+    case pkv::KERNEL_DMA_WIDE_FP8: return d128 && fp8;
+    case pkv::KERNEL_DMA_MLA_BF16: return mla && !fp8;
+    case pkv::KERNEL_DMA_MLA_FP8: return mla && fp8;
   }
   return false;
 }
+
+bool is_gqa_family(int32_t k) {
+  switch (k) {
+    case pkv::KERNEL_GQA_BF16:
+    case pkv::KERNEL_GQA_FP8:
+    case pkv::KERNEL_GQA_BF16_T256:
+    case pkv::KERNEL_GQA_BF16_S1:
+    case pkv::KERNEL_GQA_FP8_T128:
+    case pkv::KERNEL_GQA_BF16_W2:
+    case pkv::KERNEL_GQA_FP8_S2:
+    case pkv::KERNEL_DMA_GQA_BF16:
+    case pkv::KERNEL_DMA_GQA_FP8:
+    case pkv::KERNEL_DMA_GQA_FP8_W8:
+    case pkv::KERNEL_DMA_GQA_FP8_S2:
+    case pkv::KERNEL_DMA_GQA_BF16_W4:
+    case pkv::KERNEL_DMA_GQA_BF16_S2:
+      return true;
+  }
+  return false;
+}
+
+bool kernel_shape(int32_t k, pkv::MfmaShape* s) { return pkv::mfma_shape(k, s) || pkv::dma_shape(k, s); }
 
 int32_t choose_kernel(const pkv_args* a, bool is_context) {
   if (!mfma_eligible(a)) return pkv::KERNEL_GENERIC;
   const bool fp8 = a->kv_dtype == PKV_DTYPE_FP8_E4M3;
   const int G = a->num_qo_heads / a->num_kv_heads;
+  // Measured on MI355X (bf16 GQA decode B32/L4096, e4m3 ragged decode B16, MLA
+  // B512/L4096, causal context B4 q511/L2047): register-staged tiles win for
+  // bf16 decode, the direct-to-LDS ring for e4m3 decode, MLA and context.
   if (a->head_dim_qk == 128 && a->head_dim_v == 128 && !a->v_shares_k) {
     const int64_t rows = is_context ? (int64_t)a->max_q_len * G : (int64_t)a->q_len * G;
-    if (!is_context && rows <= 16) return fp8 ? pkv::KERNEL_GQA_FP8 : pkv::KERNEL_GQA_BF16;
-    return fp8 ? pkv::KERNEL_WIDE_FP8 : pkv::KERNEL_WIDE_BF16;
+    if (!is_context && rows <= 16) return fp8 ? pkv::KERNEL_DMA_GQA_FP8_S2 : pkv::KERNEL_GQA_BF16;
+    return fp8 ? pkv::KERNEL_DMA_WIDE_FP8 : pkv::KERNEL_DMA_WIDE_BF16;
   }
   if (a->head_dim_qk == 576 && a->head_dim_v == 512 && a->v_shares_k)
-    return fp8 ? pkv::KERNEL_MLA_FP8 : pkv::KERNEL_MLA_BF16;
+    return fp8 ? pkv::KERNEL_DMA_MLA_FP8 : pkv::KERNEL_DMA_MLA_BF16;
   return pkv::KERNEL_GENERIC;
 }
 
@@ -204,7 +247,7 @@ pkv_status make_plan(const pkv_args* a, bool is_context, int num_cus, pkv_plan_i
   int tile_tokens = 64, rows_per_block = 1, threads = 64;
   int64_t units;  // independent (request, KV head, row block) work items before splitting
   pkv::MfmaShape shp;
-  if (kernel != pkv::KERNEL_GENERIC && pkv::mfma_shape(kernel, &shp)) {
+  if (kernel != pkv::KERNEL_GENERIC && kernel_shape(kernel, &shp)) {
     tile_tokens = shp.tile_tokens;
     rows_per_block = shp.rows_per_block;
     threads = shp.threads;
@@ -218,13 +261,43 @@ pkv_status make_plan(const pkv_args* a, bool is_context, int num_cus, pkv_plan_i
     info->grid_y = a->num_qo_heads;
   }
 
+  // Balanced decode schedule (GQA families, rows of a KV head in one block):
+  // used when the units cannot fill the CUs, or on request (num_splits == -1).
+  const bool gqa = is_gqa_family(kernel);
+  if (a->num_splits == -1 || (a->num_splits == 0 && gqa && units < num_cus)) {
+    if (!gqa || is_context)
+      return fail(PKV_ERR_UNSUPPORTED, "the balanced schedule needs a GQA decode kernel family");
+    const int64_t extra = (int64_t)a->max_pages_per_seq + a->batch + 1 + 3;
+    const int64_t lds = (int64_t)shp.lds_static + extra * 4;
+    if (lds > 160 * 1024) {
+      if (a->num_splits == -1) return fail(PKV_ERR_UNSUPPORTED, "balanced schedule: page table too wide for LDS");
+    } else {
+      // resident workgroups per CU: LDS-limited, and at most 8 waves per CU
+      // (two per SIMD: these kernels use up to 256 VGPRs)
+      const int64_t per_cu_lds = std::max<int64_t>(1, (160 * 1024) / lds);
+      const int64_t per_cu_waves = std::max<int64_t>(1, 8 / std::max(1, threads / 64));
+      const int64_t W = (int64_t)num_cus * std::min(per_cu_lds, per_cu_waves);
+      const int64_t U = (int64_t)a->batch * a->num_kv_heads;
+      const int64_t slot_rows = (int64_t)a->q_len * G;
+      info->schedule = 1;
+      info->num_splits = (int32_t)(W + U);
+      info->pages_per_split = 0;
+      info->grid_x = (int32_t)W;
+      info->grid_y = info->grid_z = 1;
+      info->block_threads = threads;
+      info->workspace_bytes = (size_t)(W + U) * slot_rows * (size_t)(a->head_dim_v + 1) * sizeof(float) +
+                              (size_t)(a->batch + 1) * sizeof(int32_t) + 3 * 256;
+      return PKV_OK;
+    }
+  }
+
   // Split-KV sizing.  When the (request, KV head, row block) units already
   // fill the CUs, one partition per unit streams each request's pages once and
   // needs no reducer.  Otherwise cut every unit into page-aligned partitions so
   // the longest request yields about four partitions per CU: the planner only
   // knows max_kv_len, so shorter requests simply own fewer live partitions
   // (the rest exit at once and are never merged).
-  int S = a->num_splits;
+  int S = std::max(a->num_splits, 0);
   int64_t pps;
   if (S == 0) {
     if (units >= num_cus) {
@@ -335,13 +408,29 @@ pkv_status run(const pkv_args* a, bool is_context, void* ws, size_t ws_bytes, vo
   p.scale = a->scale;
   p.k_scale = a->k_scale;
   p.v_scale = a->v_scale;
-  if (plan.num_splits > 1) {
+  p.page_list_cap = plan.pages_per_split;
+  if (plan.schedule == 1) {
+    p.stream = 1;
+    p.num_wg = plan.grid_x;
+    p.slot_rows = a->q_len * G;
+    p.page_list_cap = a->max_pages_per_seq;
+    const size_t n_o = (size_t)plan.num_splits * p.slot_rows * a->head_dim_v;
+    const size_t n_l = (size_t)plan.num_splits * p.slot_rows;
+    uintptr_t base = (reinterpret_cast<uintptr_t>(ws) + 255) & ~uintptr_t(255);
+    p.ws_o = reinterpret_cast<float*>(base);
+    uintptr_t lse_base = (reinterpret_cast<uintptr_t>(p.ws_o + n_o) + 255) & ~uintptr_t(255);
+    p.ws_lse = reinterpret_cast<float*>(lse_base);
+    uintptr_t pfx_base = (reinterpret_cast<uintptr_t>(p.ws_lse + n_l) + 255) & ~uintptr_t(255);
+    p.ws_pfx = reinterpret_cast<int32_t*>(pfx_base);
+  } else if (plan.num_splits > 1) {
     uintptr_t base = (reinterpret_cast<uintptr_t>(ws) + 255) & ~uintptr_t(255);
     p.ws_o = reinterpret_cast<float*>(base);
     p.ws_lse = p.ws_o + (size_t)plan.num_splits * p.rows_total * a->head_dim_v;
   }
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  hipError_t e = plan.kernel == pkv::KERNEL_GENERIC ? pkv::launch_generic(p, s) : pkv::launch_mfma(plan.kernel, p, s);
+  hipError_t e = plan.kernel == pkv::KERNEL_GENERIC ? pkv::launch_generic(p, s)
+                 : plan.kernel >= pkv::KERNEL_DMA_GQA_BF16 ? pkv::launch_dma(plan.kernel, p, s)
+                                                           : pkv::launch_mfma(plan.kernel, p, s);
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "attention launch failed: %s", hipGetErrorString(e));
   if (plan.num_splits > 1) {
     pkv::MergeParams mp;
@@ -367,6 +456,16 @@ pkv_status run(const pkv_args* a, bool is_context, void* ws, size_t ws_bytes, vo
     mp.cap_tokens = a->max_pages_per_seq * a->page_size;
     mp.max_q_len = p.max_q_len;
     mp.total_q = p.total_q;
+    mp.err_word = a->err_word;
+    if (p.stream) {
+      mp.stream = 1;
+      mp.num_wg = p.num_wg;
+      mp.num_kv_heads = a->num_kv_heads;
+      mp.group = G;
+      mp.slot_rows = p.slot_rows;
+      mp.page_size = a->page_size;
+      mp.pfx = p.ws_pfx;
+    }
     e = pkv::launch_merge(mp, s);
     if (e != hipSuccess) return fail(PKV_ERR_HIP, "merge launch failed: %s", hipGetErrorString(e));
   }

@@ -194,8 +194,39 @@ __global__ __launch_bounds__(64 * kMergeRowsPerBlock) void lse_merge_kernel(cons
   const int h = (int)(r % mp.num_qo_heads);
   const int dv = mp.dv;
 
+  // partial rows of this output row: `live` slots, slot k at partial row
+  // prow0 + k*prow_step (Split-KV layout: [split][row]; stream layout: a row
+  // of slot (w + u) for the consecutive workgroups w that own unit u's pages)
   int live = mp.num_splits;
-  if (mp.seq_lens) {
+  int64_t prow0 = r, prow_step = mp.num_rows;
+  int64_t w_first = 0, TPs = 0;  // stream schedule: first owner workgroup, total pages
+  if (mp.stream) {
+    const int b = (int)(t / mp.q_len);
+    const int i = (int)(t % mp.q_len);
+    const int g = h / mp.group;
+    const int R = i * mp.group + (h % mp.group);
+    if (i == 0 && h == 0 && lane == 0) {
+      const int L0 = mp.seq_lens[b];
+      if (L0 > mp.cap_tokens) flag_error(mp.err_word, PKV_DEVERR_SEQ_GT_TABLE);
+      if (L0 < mp.q_len) flag_error(mp.err_word, PKV_DEVERR_SEQ_LT_QLEN);
+    }
+    const int64_t npg = mp.pfx[b + 1] - mp.pfx[b];
+    const int64_t TP = (int64_t)mp.pfx[mp.batch] * mp.num_kv_heads;
+    live = 0;
+    if (npg > 0) {
+      const int64_t u = (int64_t)b * mp.num_kv_heads + g;
+      const int64_t p_s = (int64_t)mp.pfx[b] * mp.num_kv_heads + g * npg;
+      const int64_t p_e = p_s + npg - 1;
+      const int64_t W = mp.num_wg;
+      const int64_t w_s = ((p_s + 1) * W - 1) / TP;
+      const int64_t w_e = ((p_e + 1) * W - 1) / TP;
+      live = (int)(w_e - w_s + 1);
+      prow0 = (w_s + u) * mp.slot_rows + R;
+      prow_step = mp.slot_rows;
+      w_first = w_s;
+      TPs = TP;
+    }
+  } else if (mp.seq_lens) {
     int b, t0, n;
     if (mp.is_context) {
       int lo = 0, hi = mp.batch - 1;
@@ -220,11 +251,18 @@ __global__ __launch_bounds__(64 * kMergeRowsPerBlock) void lse_merge_kernel(cons
     live = min(mp.num_splits, (c + mp.split_tokens - 1) / mp.split_tokens);
   }
 
+  // LSE of live slot s, or -inf for a slot nobody wrote: with fewer pages than
+  // workgroups (stream schedule) some owner workgroups in [w_s, w_e] own no page
+  auto slot_lse = [&](int s) -> float {
+    if (s >= live) return -INFINITY;
+    if (mp.stream) {
+      const int64_t W = mp.num_wg, w = w_first + s;
+      if ((w + 1) * TPs / W == w * TPs / W) return -INFINITY;
+    }
+    return mp.lse_part[prow0 + s * prow_step];
+  };
   float M = -INFINITY;
-  for (int s0 = 0; s0 < live; s0 += 64) {
-    const int s = s0 + lane;
-    if (s < live) M = fmaxf(M, mp.lse_part[(int64_t)s * mp.num_rows + r]);
-  }
+  for (int s0 = 0; s0 < live; s0 += 64) M = fmaxf(M, slot_lse(s0 + lane));
   M = wave_max(M);
 
   float acc[8];
@@ -234,14 +272,14 @@ __global__ __launch_bounds__(64 * kMergeRowsPerBlock) void lse_merge_kernel(cons
   if (M != -INFINITY) {
     for (int s0 = 0; s0 < live; s0 += 64) {
       const int s = s0 + lane;
-      const float ls = s < live ? mp.lse_part[(int64_t)s * mp.num_rows + r] : -INFINITY;
+      const float ls = slot_lse(s);
       const float w = (ls == -INFINITY) ? 0.f : __expf(ls - M);
       wlane += w;
       const int nsp = min(64, live - s0);
 #pragma unroll 4
       for (int j = 0; j < nsp; ++j) {
         const float wj = readlane_f(w, j);
-        const float* src = mp.o_part + ((int64_t)(s0 + j) * mp.num_rows + r) * dv;
+        const float* src = mp.o_part + (prow0 + (int64_t)(s0 + j) * prow_step) * dv;
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
           const int d = lane + 64 * k;

@@ -89,11 +89,15 @@ __device__ __forceinline__ uint32_t lds_v_off(int row, int chunk) {
   return (uint32_t)(row * C::VROWB + swz_chunk<C::VROWB / 16>(chunk, row) * 16);
 }
 
+// One piece of work: packed row block `rb` of KV head g of request b, over the
+// page-aligned key range [part_lo, part_hi) (cut further at the last key any of
+// its rows sees).  Writes the final rows, or a partial (O, LSE) into workspace
+// slot `slot` when the call runs in Split-KV mode.  `lead` marks the piece that
+// reports the request's device-side argument errors.
 template <class C>
-__global__ __launch_bounds__(C::NTHR) void attn_mfma_kernel(const KParams p) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  int32_t* s_pages = (int32_t*)(smem + C::LDS);
-
+__device__ __forceinline__ void attend_block(const KParams& p, unsigned char* smem, int32_t* s_pages, const int b,
+                                             const int g, const int rb, const int part_lo, const int part_hi,
+                                             const int slot, const bool lead) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int wr = wave / C::NWT;  // row wave
@@ -101,12 +105,9 @@ __global__ __launch_bounds__(C::NTHR) void attn_mfma_kernel(const KParams p) {
   const int tid = threadIdx.x;
   const int G4 = lane >> 4;      // 16-lane group
   const int l16 = lane & 15;
-
-  const int split = blockIdx.x;
-  const int g = blockIdx.y / p.row_blocks;
-  const int rb = blockIdx.y % p.row_blocks;
-  const int b = blockIdx.z;
   const int G = p.group;
+
+  __syncthreads();  // LDS of a previous piece (stream schedule) is free again
 
   // ---- request geometry (device values are clamped, never trusted for addressing)
   int t0, n_b;
@@ -114,7 +115,7 @@ __global__ __launch_bounds__(C::NTHR) void attn_mfma_kernel(const KParams p) {
     int a0 = p.q_indptr[b], a1 = p.q_indptr[b + 1];
     bool bad = (a0 < 0) || (a1 < a0) || (a1 - a0 > p.max_q_len) || (a1 > p.total_q);
     if (bad) {
-      if (split == 0 && g == 0 && rb == 0 && tid == 0) flag_error(p.err_word, PKV_DEVERR_QINDPTR);
+      if (lead && g == 0 && rb == 0 && tid == 0) flag_error(p.err_word, PKV_DEVERR_QINDPTR);
       return;
     }
     t0 = a0;
@@ -129,7 +130,7 @@ __global__ __launch_bounds__(C::NTHR) void attn_mfma_kernel(const KParams p) {
 
   int L = p.seq_lens[b];
   const int cap = p.max_pages_per_seq * p.page_size;
-  if (split == 0 && g == 0 && rb == 0 && tid == 0) {
+  if (lead && g == 0 && rb == 0 && tid == 0) {
     if (L > cap) flag_error(p.err_word, PKV_DEVERR_SEQ_GT_TABLE);
     if (L < n_b) flag_error(p.err_word, PKV_DEVERR_SEQ_LT_QLEN);
   }
@@ -139,8 +140,8 @@ __global__ __launch_bounds__(C::NTHR) void attn_mfma_kernel(const KParams p) {
   const int last_row = min(row0 + C::ROWS, row_space) - 1;
   const int i_max = last_row / G;
   const int c_max = p.causal ? min(L, max(0, L - n_b + i_max + 1)) : L;
-  const int kv_lo = split * p.pages_per_split * p.page_size;
-  const int kv_hi = min(kv_lo + p.pages_per_split * p.page_size, c_max);
+  const int kv_lo = part_lo;
+  const int kv_hi = min(part_hi, c_max);
   const int n_tiles = kv_hi > kv_lo ? (kv_hi - kv_lo + C::T - 1) / C::T : 0;
   // a partition past every row's visible keys: the reducer never reads it
   if (n_tiles == 0 && p.ws_o != nullptr) return;
@@ -162,12 +163,13 @@ __global__ __launch_bounds__(C::NTHR) void attn_mfma_kernel(const KParams p) {
   const float v_scale = p.v_scale_dev ? *p.v_scale_dev : p.v_scale;
   const float sc2 = p.scale * k_scale * kLog2e;
 
-  int row_t[C::RT], row_h[C::RT], row_c[C::RT];
+  int row_t[C::RT], row_h[C::RT], row_c[C::RT], row_R[C::RT];
   bool row_ok[C::RT];
   bf16x8 qB[C::RT][C::NKS];
 #pragma unroll
   for (int rt = 0; rt < C::RT; ++rt) {
     const int R = row0 + (wr * C::RT + rt) * 16 + l16;
+    row_R[rt] = R;
     row_ok[rt] = R < row_space;
     const int i = row_ok[rt] ? R / G : 0;
     row_t[rt] = t0 + i;
@@ -185,6 +187,12 @@ __global__ __launch_bounds__(C::NTHR) void attn_mfma_kernel(const KParams p) {
     }
   }
 
+  // smallest visible-key bound over this wave's real rows: slices below it need no mask
+  int c_lo = INT_MAX;
+#pragma unroll
+  for (int rt = 0; rt < C::RT; ++rt)
+    if (row_ok[rt]) c_lo = min(c_lo, row_c[rt]);
+  c_lo = -wave_max_i(-c_lo);
   float m_run[C::RT], l_run[C::RT];
   f32x4 O[C::RT][C::NDB];
 #pragma unroll
@@ -292,7 +300,9 @@ __global__ __launch_bounds__(C::NTHR) void attn_mfma_kernel(const KParams p) {
       }
     }
 
-    // ---- online softmax (log2 domain), one query row per lane and row tile
+    // ---- online softmax (exp2 domain); keys past a row's bound are selected to -inf,
+    // which only slices reaching past the wave's smallest bound need
+    const bool full_slice = tok_w + C::TT <= c_lo;
     float pr[C::RT][C::NNB][4];
 #pragma unroll
     for (int rt = 0; rt < C::RT; ++rt) {
@@ -301,28 +311,35 @@ __global__ __launch_bounds__(C::NTHR) void attn_mfma_kernel(const KParams p) {
       for (int nb = 0; nb < C::NNB; ++nb)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int tok = tok_w + nb * 16 + G4 * 4 + e;
           const float s = acc[rt][nb][e] * sc2;
-          pr[rt][nb][e] = (tok < row_c[rt]) ? s : -INFINITY;
+          if (full_slice) {
+            pr[rt][nb][e] = s;
+          } else {
+            const int tok = tok_w + nb * 16 + G4 * 4 + e;
+            pr[rt][nb][e] = (tok < row_c[rt]) ? s : -INFINITY;
+          }
           mx = fmaxf(mx, pr[rt][nb][e]);
         }
       mx = xor_max(mx, 16);
       mx = xor_max(mx, 32);
       const float m_new = fmaxf(m_run[rt], mx);
       const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = exp2f(m_run[rt] - m_use);
+      const float alpha = fast_exp2(m_run[rt] - m_use);
       float ps = 0.f;
 #pragma unroll
       for (int nb = 0; nb < C::NNB; ++nb)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          pr[rt][nb][e] = exp2f(pr[rt][nb][e] - m_use);
+          pr[rt][nb][e] = fast_exp2(pr[rt][nb][e] - m_use);
           ps += pr[rt][nb][e];
         }
       l_run[rt] = l_run[rt] * alpha + ps;
       m_run[rt] = m_new;
+      // alpha is exactly 1 wherever the running max did not move: rescale only if some lane's did
+      if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
 #pragma unroll
-      for (int d = 0; d < C::NDB; ++d) O[rt][d] *= alpha;
+        for (int d = 0; d < C::NDB; ++d) O[rt][d] *= alpha;
+      }
     }
 
     // ---- O^T += V^T P^T
@@ -398,7 +415,7 @@ __global__ __launch_bounds__(C::NTHR) void attn_mfma_kernel(const KParams p) {
       float wgt[C::NWT];
 #pragma unroll
       for (int w = 0; w < C::NWT; ++w) {
-        wgt[w] = exp2f(mw[w] - M_use);
+        wgt[w] = fast_exp2(mw[w] - M_use);
         lsum += wgt[w] * red_ml[(((wr * C::NWT + w) * C::RT + rt) * 64 + lane) * 2 + 1];
       }
       m_run[rt] = M;
@@ -427,9 +444,10 @@ __global__ __launch_bounds__(C::NTHR) void attn_mfma_kernel(const KParams p) {
     const float lse = empty ? -INFINITY : (m_run[rt] * kLn2 + __logf(l_run[rt]));
     const int64_t row_g = (int64_t)row_t[rt] * p.num_qo_heads + row_h[rt];
     if (split_mode) {
-      if (G4 == 0 && db_first == 0) p.ws_lse[(int64_t)split * p.rows_total + row_g] = lse;
+      const int64_t prow = p.stream ? (int64_t)slot * p.slot_rows + row_R[rt] : (int64_t)slot * p.rows_total + row_g;
+      if (G4 == 0 && db_first == 0) p.ws_lse[prow] = lse;
       if (!empty) {
-        float* dst = p.ws_o + ((int64_t)split * p.rows_total + row_g) * C::DV + G4 * 4;
+        float* dst = p.ws_o + prow * C::DV + G4 * 4;
 #pragma unroll
         for (int d = 0; d < C::NDB; ++d) {
           if (C::NWT > 1 && d % C::NWT != db_first) continue;
@@ -460,10 +478,90 @@ __global__ __launch_bounds__(C::NTHR) void attn_mfma_kernel(const KParams p) {
   (void)db_step;
 }
 
+// Per-partition grid: (partition, KV head x row block, request).
+template <class C>
+__global__ __launch_bounds__(C::NTHR) void attn_mfma_kernel(const KParams p) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  int32_t* s_pages = (int32_t*)(smem + C::LDS);
+  const int split = blockIdx.x;
+  const int span = p.pages_per_split * p.page_size;
+  attend_block<C>(p, smem, s_pages, blockIdx.z, blockIdx.y / p.row_blocks, blockIdx.y % p.row_blocks,
+                  split * span, split * span + span, split, split == 0);
+}
+
+// Balanced decode schedule.  The page streams of all (request, KV head) units,
+// laid end to end (unit u = b*Hkv + g owns ceil(L_b/P) pages), are cut into
+// gridDim.x equal page ranges, one per workgroup:  workgroup w owns global
+// pages [w*TP/W, (w+1)*TP/W).  Every maximal piece of one unit inside one
+// workgroup's range is a segment; segment (w, u) writes its partial rows to
+// workspace slot w + u, which is unique because moving from one segment to
+// the next increases w or u.  The reducer recovers a row's segments from the
+// same arithmetic: pages p of unit u belong to workgroups
+// owner(p) = ((p + 1)*W - 1) / TP.
+template <class C>
+__global__ __launch_bounds__(C::NTHR) void attn_mfma_stream_kernel(const KParams p) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  int32_t* s_pages = (int32_t*)(smem + C::LDS);
+  int32_t* s_pfx = s_pages + p.page_list_cap;  // [batch + 1] page prefix over requests
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int B = p.batch;
+  const int cap = p.max_pages_per_seq * p.page_size;
+  if (tid < 64) {
+    int carry = 0;
+    if (lane == 0) s_pfx[0] = 0;
+    for (int c0 = 0; c0 < B; c0 += 64) {
+      const int bb = c0 + lane;
+      int v = 0;
+      if (bb < B) {
+        const int L = max(0, min(p.seq_lens[bb], cap));
+        v = (L + p.page_size - 1) >> p.log2_page;
+      }
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(v, o, 64);
+        if (lane >= o) v += t;
+      }
+      if (bb < B) s_pfx[bb + 1] = carry + v;
+      carry += __shfl(v, 63, 64);
+    }
+  }
+  __syncthreads();
+  const int Hkv = p.num_kv_heads;
+  const int64_t TP = (int64_t)s_pfx[B] * Hkv;
+  const int64_t W = gridDim.x;
+  const int64_t w = blockIdx.x;
+  if (w == 0)
+    for (int i = tid; i <= B; i += C::NTHR) p.ws_pfx[i] = s_pfx[i];
+  int64_t pos = w * TP / W;
+  const int64_t end = (w + 1) * TP / W;
+  while (pos < end) {
+    // request b: s_pfx[b]*Hkv <= pos < s_pfx[b+1]*Hkv
+    int lo = 0, hi = B - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if ((int64_t)s_pfx[mid] * Hkv <= pos) lo = mid; else hi = mid - 1;
+    }
+    const int b = lo;
+    const int64_t npg = s_pfx[b + 1] - s_pfx[b];
+    const int64_t base = (int64_t)s_pfx[b] * Hkv;
+    const int g = (int)((pos - base) / npg);
+    const int64_t u_start = base + g * npg;
+    const int64_t seg_end = min(end, u_start + npg);
+    const int a = (int)(pos - u_start), e = (int)(seg_end - u_start);
+    attend_block<C>(p, smem, s_pages, b, g, 0, a * p.page_size, e * p.page_size, (int)(w + b * Hkv + g), a == 0);
+    pos = seg_end;
+  }
+}
+
 // ---------------------------------------------------------------- instances
 using CfgGqaBf16 = TileCfg<128, 128, false, false, 1, 1, 4, 32>;
 using CfgGqaFp8 = TileCfg<128, 128, true, false, 1, 1, 4, 64, 1>;
 using CfgGqaBf16T256 = TileCfg<128, 128, false, false, 1, 1, 4, 64, 1>;
+using CfgGqaBf16S1 = TileCfg<128, 128, false, false, 1, 1, 4, 32, 1>;
+using CfgGqaFp8T128 = TileCfg<128, 128, true, false, 1, 1, 4, 32, 1>;
+using CfgGqaBf16W2 = TileCfg<128, 128, false, false, 1, 1, 2, 32, 2>;
+using CfgGqaFp8S2 = TileCfg<128, 128, true, false, 1, 1, 4, 32, 2>;
 using CfgWideBf16 = TileCfg<128, 128, false, false, 2, 4, 1, 64>;
 using CfgWideFp8 = TileCfg<128, 128, true, false, 2, 4, 1, 64>;
 using CfgMlaBf16 = TileCfg<576, 512, false, true, 2, 4, 1, 32>;
@@ -482,6 +580,10 @@ bool mfma_shape(int32_t kernel, MfmaShape* s) {
     case KERNEL_GQA_BF16: fill_shape<CfgGqaBf16>(s); return true;
     case KERNEL_GQA_FP8: fill_shape<CfgGqaFp8>(s); return true;
     case KERNEL_GQA_BF16_T256: fill_shape<CfgGqaBf16T256>(s); return true;
+    case KERNEL_GQA_BF16_S1: fill_shape<CfgGqaBf16S1>(s); return true;
+    case KERNEL_GQA_FP8_T128: fill_shape<CfgGqaFp8T128>(s); return true;
+    case KERNEL_GQA_BF16_W2: fill_shape<CfgGqaBf16W2>(s); return true;
+    case KERNEL_GQA_FP8_S2: fill_shape<CfgGqaFp8S2>(s); return true;
     case KERNEL_WIDE_BF16: fill_shape<CfgWideBf16>(s); return true;
     case KERNEL_WIDE_FP8: fill_shape<CfgWideFp8>(s); return true;
     case KERNEL_MLA_BF16: fill_shape<CfgMlaBf16>(s); return true;
@@ -492,16 +594,24 @@ bool mfma_shape(int32_t kernel, MfmaShape* s) {
 
 template <class C>
 static hipError_t launch_cfg(const KParams& p, hipStream_t s) {
-  static bool attr_done = false;  // idempotent; a race only repeats the same call
-  const size_t lds = C::LDS + (size_t)((p.pages_per_split + 2 + 3) & ~3) * sizeof(int32_t);
+  static bool attr_done = false;  // idempotent; a race only repeats the same calls
+  const size_t extra = (size_t)p.page_list_cap + (p.stream ? (size_t)p.batch + 1 : 0);
+  const size_t lds = C::LDS + ((extra + 3) & ~size_t(3)) * sizeof(int32_t);
   if (!attr_done) {
     hipError_t e = hipFuncSetAttribute((const void*)attn_mfma_kernel<C>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (e != hipSuccess) return e;
+    e = hipFuncSetAttribute((const void*)attn_mfma_stream_kernel<C>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            160 * 1024);
+    if (e != hipSuccess) return e;
     attr_done = true;
   }
-  dim3 grid(p.num_splits, p.num_kv_heads * p.row_blocks, p.batch);
-  hipLaunchKernelGGL(attn_mfma_kernel<C>, grid, dim3(C::NTHR), lds, s, p);
+  if (p.stream) {
+    hipLaunchKernelGGL(attn_mfma_stream_kernel<C>, dim3(p.num_wg), dim3(C::NTHR), lds, s, p);
+  } else {
+    dim3 grid(p.num_splits, p.num_kv_heads * p.row_blocks, p.batch);
+    hipLaunchKernelGGL(attn_mfma_kernel<C>, grid, dim3(C::NTHR), lds, s, p);
+  }
   return hipGetLastError();
 }
 
@@ -510,6 +620,10 @@ hipError_t launch_mfma(int32_t kernel, const KParams& p, hipStream_t s) {
     case KERNEL_GQA_BF16: return launch_cfg<CfgGqaBf16>(p, s);
     case KERNEL_GQA_FP8: return launch_cfg<CfgGqaFp8>(p, s);
     case KERNEL_GQA_BF16_T256: return launch_cfg<CfgGqaBf16T256>(p, s);
+    case KERNEL_GQA_BF16_S1: return launch_cfg<CfgGqaBf16S1>(p, s);
+    case KERNEL_GQA_FP8_T128: return launch_cfg<CfgGqaFp8T128>(p, s);
+    case KERNEL_GQA_BF16_W2: return launch_cfg<CfgGqaBf16W2>(p, s);
+    case KERNEL_GQA_FP8_S2: return launch_cfg<CfgGqaFp8S2>(p, s);
     case KERNEL_WIDE_BF16: return launch_cfg<CfgWideBf16>(p, s);
     case KERNEL_WIDE_FP8: return launch_cfg<CfgWideFp8>(p, s);
     case KERNEL_MLA_BF16: return launch_cfg<CfgMlaBf16>(p, s);

@@ -20,7 +20,22 @@ enum KernelId : int32_t {
   KERNEL_MLA_BF16 = 6,    // MFMA, 128 heads on one latent KV head, D_qk = 576, D_v = 512
   KERNEL_MLA_FP8 = 7,
   KERNEL_GQA_BF16_T256 = 8,  // GQA bf16 with 256-token tiles in one LDS stage
-  KERNEL_COUNT = 9,
+  KERNEL_GQA_BF16_S1 = 9,    // GQA bf16, 128-token tiles, one LDS stage (64 KiB: two workgroups per CU)
+  KERNEL_GQA_FP8_T128 = 10,  // GQA e4m3, 128-token tiles, one LDS stage (64 KiB)
+  KERNEL_GQA_BF16_W2 = 11,   // GQA bf16, two token waves, 64-token tiles, two stages (64 KiB)
+  KERNEL_GQA_FP8_S2 = 12,    // GQA e4m3, 128-token tiles, two LDS stages (128 KiB)
+  // direct-to-LDS ring variants (pkv_attn_dma.hip); KV stays in its stored dtype in LDS
+  KERNEL_DMA_GQA_BF16 = 13,
+  KERNEL_DMA_GQA_FP8 = 14,
+  KERNEL_DMA_WIDE_BF16 = 15,
+  KERNEL_DMA_WIDE_FP8 = 16,
+  KERNEL_DMA_MLA_BF16 = 17,
+  KERNEL_DMA_MLA_FP8 = 18,
+  KERNEL_DMA_GQA_FP8_W8 = 19,   // 8 token waves, 256-key tiles, 2 stages (128 KiB)
+  KERNEL_DMA_GQA_FP8_S2 = 20,   // 4 token waves, 128-key tiles, 2 stages (64 KiB: two groups per CU)
+  KERNEL_DMA_GQA_BF16_W4 = 21,  // 4 token waves, 128-key tiles, 2 stages (128 KiB)
+  KERNEL_DMA_GQA_BF16_S2 = 22,  // 2 token waves, 64-key tiles, 2 stages (64 KiB)
+  KERNEL_COUNT = 23,
 };
 
 // Everything a kernel reads, by value.  Element strides as in pkv_args.
@@ -47,6 +62,11 @@ struct KParams {
   int64_t k_sp, k_sh, k_stok, v_sp, v_sh, v_stok, table_stride;
   int64_t rows_total;  // total query rows * num_qo_heads
   float scale, k_scale, v_scale, pad1;
+  // balanced decode schedule (stream != 0): num_wg workgroups, partial rows
+  // indexed [slot][packed row] with slot_rows packed rows per slot, and the
+  // per-request page prefix written to ws_pfx for the reducer
+  int32_t stream, num_wg, slot_rows, page_list_cap;
+  int32_t* ws_pfx;
 };
 
 struct LaunchShape {
@@ -72,6 +92,10 @@ struct MergeParams {
   const int32_t* q_indptr;
   int32_t batch, q_len, causal, is_context;
   int32_t split_tokens, cap_tokens, max_q_len, total_q;
+  // balanced decode schedule: row (t, h) of KV head g reads slots w + b*Hkv + g
+  int32_t stream, num_wg, num_kv_heads, group, slot_rows, page_size;
+  const int32_t* pfx;
+  int32_t* err_word;
 };
 hipError_t launch_merge(const MergeParams& mp, hipStream_t s);
 
@@ -83,5 +107,7 @@ struct MfmaShape {
   size_t lds_static;     // LDS for the KV stages and reductions (page list excluded)
 };
 bool mfma_shape(int32_t kernel, MfmaShape* out);
+bool dma_shape(int32_t kernel, MfmaShape* out);
+hipError_t launch_dma(int32_t kernel, const KParams& p, hipStream_t s);
 
 }  // namespace pkv

@@ -21,7 +21,10 @@ PKV_LAYOUT_HND, PKV_LAYOUT_NHD = range(2)
 PKV_DEVERR_SEQ_LT_QLEN, PKV_DEVERR_SEQ_GT_TABLE, PKV_DEVERR_PAGE_RANGE, PKV_DEVERR_QINDPTR = 1, 2, 4, 8
 
 KERNEL_NAMES = {0: "none", 1: "generic", 2: "gqa_bf16", 3: "gqa_fp8", 4: "wide_bf16", 5: "wide_fp8",
-                6: "mla_bf16", 7: "mla_fp8", 8: "gqa_bf16_t256"}
+                6: "mla_bf16", 7: "mla_fp8", 8: "gqa_bf16_t256", 9: "gqa_bf16_s1", 10: "gqa_fp8_t128",
+                11: "gqa_bf16_w2", 12: "gqa_fp8_s2", 13: "dma_gqa_bf16", 14: "dma_gqa_fp8", 15: "dma_wide_bf16",
+                16: "dma_wide_fp8", 17: "dma_mla_bf16", 18: "dma_mla_fp8", 19: "dma_gqa_fp8_w8",
+                20: "dma_gqa_fp8_s2", 21: "dma_gqa_bf16_w4", 22: "dma_gqa_bf16_s2"}
 KERNEL_IDS = {v: k for k, v in KERNEL_NAMES.items()}
 
 DTYPE_CODES = {"f32": PKV_DTYPE_F32, "bf16": PKV_DTYPE_BF16, "e4m3": PKV_DTYPE_FP8_E4M3}
@@ -56,7 +59,7 @@ class PkvPlanInfo(C.Structure):
     _fields_ = [
         ("kernel", C.c_int32), ("num_splits", C.c_int32), ("pages_per_split", C.c_int32),
         ("grid_x", C.c_int32), ("grid_y", C.c_int32), ("grid_z", C.c_int32),
-        ("block_threads", C.c_int32), ("reserved", C.c_int32), ("workspace_bytes", C.c_size_t),
+        ("block_threads", C.c_int32), ("schedule", C.c_int32), ("workspace_bytes", C.c_size_t),
     ]
 
 

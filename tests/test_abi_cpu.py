@@ -81,7 +81,7 @@ def test_kernel_choice_by_shape():
     a.q = a.k_pages = a.v_pages = a.out = 0x1000  # aligned dummy addresses (never dereferenced)
     assert pkv.KERNEL_NAMES[pkv.pkv_plan(a).kernel] == "gqa_bf16"
     a.kv_dtype = pkv.PKV_DTYPE_FP8_E4M3
-    assert pkv.KERNEL_NAMES[pkv.pkv_plan(a).kernel] == "gqa_fp8"
+    assert pkv.KERNEL_NAMES[pkv.pkv_plan(a).kernel] == "dma_gqa_fp8_s2"
     # fp32 queries, odd page sizes or misaligned pointers fall back to the generic kernel
     b = _args_for(_fake(page_size=24))
     b.q = b.k_pages = b.v_pages = b.out = 0x1000
@@ -93,12 +93,12 @@ def test_kernel_choice_by_shape():
     c = _args_for(_fake(q_lens=[20, 30], seq_lens=[40, 70], is_decode=False))
     c.q = c.k_pages = c.v_pages = c.out = 0x1000
     info = pkv.pkv_plan(c, True)
-    assert pkv.KERNEL_NAMES[info.kernel] == "wide_bf16"
+    assert pkv.KERNEL_NAMES[info.kernel] == "dma_wide_bf16"
     # MLA shape
     m = _args_for(_fake(num_qo_heads=16, num_kv_heads=1, head_dim_qk=576, head_dim_v=512, page_size=64,
                         mla=True))
     m.q = m.k_pages = m.v_pages = m.out = 0x1000
-    assert pkv.KERNEL_NAMES[pkv.pkv_plan(m).kernel] == "mla_bf16"
+    assert pkv.KERNEL_NAMES[pkv.pkv_plan(m).kernel] == "dma_mla_bf16"
 
 
 def test_split_plan_is_page_aligned_and_sized_to_cus():
@@ -164,3 +164,27 @@ def test_lse_merge_argument_checks():
     assert pkv.pkv_lse_merge(0, 4, 1, 8, 1, 1, 1, 0, 8, 8, 0, 0, check=False) == pkv.PKV_ERR_INVALID_ARG
     assert pkv.pkv_lse_merge(2, 4, 1, 1024, 1, 1, 1, 0, 1024, 1024, 0, 0, check=False) == pkv.PKV_ERR_INVALID_ARG
     assert pkv.pkv_lse_merge(2, 0, 1, 8, 0, 0, 0, 0, 8, 8, 0, 0) == pkv.PKV_OK
+
+
+def test_balanced_schedule_chosen_when_units_cannot_fill_the_cus():
+    a = _args_for(_fake(seq_lens=[5000, 300]))
+    a.q = a.k_pages = a.v_pages = a.out = 0x1000
+    info = pkv.pkv_plan(a, False, 256)
+    assert info.schedule == 1 and info.grid_x >= 256
+    U = 2 * 8
+    assert info.num_splits == info.grid_x + U
+    assert info.workspace_bytes >= info.num_splits * 4 * (128 + 1) * 4
+    a.num_splits = 5  # an explicit partition count keeps the per-unit grid
+    assert pkv.pkv_plan(a, False, 256).schedule == 0
+    a.num_splits = -1
+    assert pkv.pkv_plan(a, False, 256).schedule == 1
+    a.batch = 32
+    a.num_splits = 0
+    assert pkv.pkv_plan(a, False, 256).schedule == 0  # 256 units fill 256 CUs: one partition each
+
+
+def test_balanced_schedule_rejected_for_non_gqa_families():
+    a = _args_for(_fake(q_lens=[3, 4], is_decode=False))
+    a.q = a.k_pages = a.v_pages = a.out = 0x1000
+    a.num_splits = -1
+    assert pkv.pkv_context(a, 0, 0, 0, check=False) == pkv.PKV_ERR_UNSUPPORTED

@@ -47,14 +47,14 @@ def test_tiny_gqa_fp32_workload():
     compare(prob, dp)
 
 
-@pytest.mark.parametrize("splits", [None, 1, 3])
+@pytest.mark.parametrize("splits", [None, 1, 3, -1])
 def test_gqa_bf16_ragged_small(splits):
     prob = _gqa([1, 31, 32, 33, 700, 129])
     say(f"case {prob.name} splits={splits}")
     compare(prob, run_gpu(prob, num_splits=splits))
 
 
-@pytest.mark.parametrize("splits", [None, 1, 4])
+@pytest.mark.parametrize("splits", [None, 1, 4, -1])
 def test_gqa_fp8_ragged_small(splits):
     prob = _gqa([5, 64, 65, 1500], hq=64, hkv=8, P=64, kv=W.E4M3)
     say(f"case {prob.name} splits={splits}")
@@ -68,21 +68,56 @@ def test_gqa_bf16_full_size():
     compare(prob, dp, sample_pairs(prob, 96))
 
 
-def test_gqa_fp8_full_size():
+@pytest.mark.parametrize("splits", [None, 12])
+def test_gqa_fp8_full_size(splits):
     prob = W.gqa_fp8_b16_ragged()
-    say(f"case {prob.name} (sampled)")
-    dp = run_gpu(prob)
+    say(f"case {prob.name} splits={splits} (sampled)")
+    dp = run_gpu(prob, num_splits=splits)
     compare(prob, dp, sample_pairs(prob, 96))
 
 
-@pytest.mark.parametrize("q_len", [1, 2])
-def test_mla_small(q_len):
+def test_balanced_schedule_one_long_request():
+    # 8 units of 250 pages spread over every workgroup: each unit has ~32 partial slots
+    prob = _gqa([8000], hq=32, hkv=8, P=32)
+    dp = run_gpu(prob)
+    assert pkv.pkv_plan(dp.args).schedule == 1
+    compare(prob, dp)
+
+
+def test_balanced_schedule_fewer_pages_than_workgroups():
+    prob = _gqa([1, 2, 40], hq=16, hkv=2, P=16, q_lens=[1, 1, 1])
+    dp = run_gpu(prob, num_splits=-1)
+    compare(prob, dp)
+
+
+def test_balanced_schedule_speculative_rows_and_empty_request():
+    prob = _gqa([3, 0, 300, 77], q_lens=[3, 3, 3, 3], hq=16, hkv=4)
+    compare(prob, run_gpu(prob, num_splits=-1), expect_err=pkv.PKV_DEVERR_SEQ_LT_QLEN)
+
+
+@pytest.mark.parametrize("q_len,kernel", [(1, None), (2, None), (1, "dma_mla_bf16"), (2, "dma_mla_bf16"),
+                                          (1, "mla_bf16")])
+def test_mla_small(q_len, kernel):
     prob = W.make_problem(name=f"mla-small-q{q_len}", seed=3, batch=3, seq_lens=[2, 70, 300],
                           q_lens=[q_len] * 3, num_qo_heads=128, num_kv_heads=1, head_dim_qk=576,
                           head_dim_v=512, page_size=64, mla=True, scale=1 / 24.0, poison=True,
                           extra_page_frac=0.3, table_slack_pages=1)
-    say(f"case {prob.name}")
-    compare(prob, run_gpu(prob))
+    say(f"case {prob.name} kernel={kernel}")
+    dp = pkv.upload(prob, "cuda", kernel=kernel)
+    dp.run()
+    torch.cuda.synchronize()
+    compare(prob, dp)
+
+
+def test_mla_fp8_latent_small():
+    prob = W.make_problem(name="mla-fp8-small", seed=11, batch=2, seq_lens=[65, 200], q_lens=[2, 2],
+                          num_qo_heads=128, num_kv_heads=1, head_dim_qk=576, head_dim_v=512, page_size=64,
+                          mla=True, kv_dtype=W.E4M3, scale=1 / 24.0, poison=True, extra_page_frac=0.3)
+    for kernel in ["dma_mla_fp8", "mla_fp8"]:
+        dp = pkv.upload(prob, "cuda", kernel=kernel)
+        dp.run()
+        torch.cuda.synchronize()
+        compare(prob, dp, label=kernel)
 
 
 @pytest.mark.parametrize("q_len", [1, 2])
@@ -242,3 +277,45 @@ def test_malformed_q_indptr_flagged_without_writes():
     dp.run()
     torch.cuda.synchronize()
     assert int(dp.err.item()) & pkv.PKV_DEVERR_QINDPTR
+
+
+# ----------------------------------------------------------------- every kernel family on the same inputs
+
+@pytest.mark.parametrize("kernel,kv,splits", [
+    ("dma_gqa_bf16", W.BF16, None), ("dma_gqa_bf16", W.BF16, 1), ("dma_gqa_bf16", W.BF16, 3),
+    ("dma_gqa_fp8", W.E4M3, None), ("dma_gqa_fp8", W.E4M3, 1), ("dma_gqa_fp8", W.E4M3, 5),
+    ("gqa_bf16_s1", W.BF16, None), ("gqa_fp8_t128", W.E4M3, None), ("gqa_bf16_w2", W.BF16, None),
+    ("gqa_fp8_s2", W.E4M3, 2), ("gqa_bf16_t256", W.BF16, 2),
+    ("dma_gqa_fp8_w8", W.E4M3, None), ("dma_gqa_fp8_s2", W.E4M3, None), ("dma_gqa_bf16_w4", W.BF16, None),
+    ("dma_gqa_bf16_s2", W.BF16, None), ("dma_gqa_bf16_w4", W.BF16, 2),
+])
+def test_gqa_kernel_families_match_oracle(kernel, kv, splits):
+    P = 64 if kv == W.E4M3 else 32
+    prob = _gqa([1, 31, 64, 65, 700, 1300], hq=64 if kv == W.E4M3 else 32, hkv=8, P=P, kv=kv)
+    say(f"case {kernel} splits={splits}")
+    dp = pkv.upload(prob, "cuda", num_splits=splits, kernel=kernel)
+    dp.run()
+    torch.cuda.synchronize()
+    compare(prob, dp, label=f"{kernel}/{splits}")
+
+
+@pytest.mark.parametrize("kernel", ["dma_wide_bf16", "wide_bf16"])
+def test_context_kernel_families_match_oracle(kernel):
+    prob = W.make_problem(name="ctx-fam", seed=9, batch=3, seq_lens=[70, 5, 333], q_lens=[64, 5, 130],
+                          num_qo_heads=16, num_kv_heads=2, head_dim_qk=128, head_dim_v=128, page_size=16,
+                          is_decode=False, poison=True, extra_page_frac=0.3, table_slack_pages=1)
+    dp = pkv.upload(prob, "cuda", kernel=kernel)
+    dp.run()
+    torch.cuda.synchronize()
+    compare(prob, dp, label=kernel)
+
+
+def test_context_fp8_kv_families_match_oracle():
+    prob = W.make_problem(name="ctx-fp8", seed=10, batch=2, seq_lens=[90, 300], q_lens=[40, 100],
+                          num_qo_heads=16, num_kv_heads=2, head_dim_qk=128, head_dim_v=128, page_size=32,
+                          kv_dtype=W.E4M3, is_decode=False, poison=True, extra_page_frac=0.3)
+    for kernel in ["dma_wide_fp8", "wide_fp8"]:
+        dp = pkv.upload(prob, "cuda", kernel=kernel)
+        dp.run()
+        torch.cuda.synchronize()
+        compare(prob, dp, label=kernel)
