@@ -28,25 +28,29 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 METRIC = "paged decode µs/call + achieved HBM GB/s (KV bytes) as % of MI355X peak"
-KERNEL_SRC = os.path.join(ROOT, "paged_kv_attention_15_amd", "csrc", "pkv_attn_mfma.hip")
+
+
+# Sources the headline kernel (register-staged bf16 GQA decode) is built from;
+# a stored HBM-counter reading is used only while these are unchanged.
+HEADLINE_SOURCES = ("pkv_attn_mfma.hip", "pkv_device.h", "pkv_internal.h")
 
 
 def _src_hash() -> str:
     h = hashlib.sha256()
-    for name in ("pkv_attn_mfma.hip", "pkv_attn_dma.hip", "pkv_attn_generic.hip", "pkv_device.h", "pkv_abi.cpp"):
+    for name in HEADLINE_SOURCES:
         with open(os.path.join(ROOT, "paged_kv_attention_15_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def _traffic(workload: str):
+def _traffic(workload: str, kernel: str, num_splits: int):
     """HBM bytes per launch from committed rocprofv3 counter runs, or None when
-    they are missing or were taken on other kernel sources."""
+    they are missing, were taken on other kernel sources or on another plan."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if rec.get("src_hash") != _src_hash():
+    if rec.get("src_hash") != _src_hash() or rec.get("plan") != [kernel, num_splits]:
         return None
     return rec.get("bytes_per_launch")
 
@@ -182,7 +186,7 @@ def main():
                    "kv_dtype": "bf16", "kernel": pkv.KERNEL_NAMES[info.kernel], "num_splits": info.num_splits,
                    "kv_bytes_per_call": kv},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": _traffic("bf16-gqa-b32-kv4096"),
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": _traffic("bf16-gqa-b32-kv4096", pkv.KERNEL_NAMES[info.kernel], info.num_splits),
                      "kernel": f"{pkv.KERNEL_NAMES[info.kernel]} attention kernel" + ("" if single_kernel else " + lse_merge_kernel"),
                      "timing": "one HIP event pair on the launch stream around the timed back-to-back calls"},
     }
