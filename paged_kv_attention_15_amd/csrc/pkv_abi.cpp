@@ -186,6 +186,12 @@ bool kernel_supports(int32_t k, const pkv_args* a, bool is_context) {
     case pkv::KERNEL_DMA_WIDE_FP8: return d128 && fp8;
     case pkv::KERNEL_DMA_MLA_BF16: return mla && !fp8;
     case pkv::KERNEL_DMA_MLA_FP8: return mla && fp8;
+    case pkv::KERNEL_M32_CTX_BF16:
+    case pkv::KERNEL_M32_CTX_W8:
+    case pkv::KERNEL_M32_CTX_R1:
+    case pkv::KERNEL_M32_CTX_R1S3:
+      return d128 && !fp8;
+    case pkv::KERNEL_M32_MLA_BF16: return mla && !fp8;
   }
   return false;
 }
@@ -210,7 +216,9 @@ bool is_gqa_family(int32_t k) {
   return false;
 }
 
-bool kernel_shape(int32_t k, pkv::MfmaShape* s) { return pkv::mfma_shape(k, s) || pkv::dma_shape(k, s); }
+bool kernel_shape(int32_t k, pkv::MfmaShape* s) {
+  return pkv::mfma_shape(k, s) || pkv::dma_shape(k, s) || pkv::m32_shape(k, s);
+}
 
 int32_t choose_kernel(const pkv_args* a, bool is_context) {
   if (!mfma_eligible(a)) return pkv::KERNEL_GENERIC;
@@ -428,9 +436,10 @@ pkv_status run(const pkv_args* a, bool is_context, void* ws, size_t ws_bytes, vo
     p.ws_lse = p.ws_o + (size_t)plan.num_splits * p.rows_total * a->head_dim_v;
   }
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  hipError_t e = plan.kernel == pkv::KERNEL_GENERIC ? pkv::launch_generic(p, s)
-                 : plan.kernel >= pkv::KERNEL_DMA_GQA_BF16 ? pkv::launch_dma(plan.kernel, p, s)
-                                                           : pkv::launch_mfma(plan.kernel, p, s);
+  hipError_t e = plan.kernel == pkv::KERNEL_GENERIC          ? pkv::launch_generic(p, s)
+                 : plan.kernel >= pkv::KERNEL_M32_CTX_BF16    ? pkv::launch_m32(plan.kernel, p, s)
+                 : plan.kernel >= pkv::KERNEL_DMA_GQA_BF16    ? pkv::launch_dma(plan.kernel, p, s)
+                                                              : pkv::launch_mfma(plan.kernel, p, s);
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "attention launch failed: %s", hipGetErrorString(e));
   if (plan.num_splits > 1) {
     pkv::MergeParams mp;

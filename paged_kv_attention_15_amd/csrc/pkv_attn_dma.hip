@@ -27,6 +27,7 @@
 
 #include "pkv_device.h"
 #include "pkv_internal.h"
+#include "pkv_ring.h"
 
 namespace pkv {
 
@@ -69,15 +70,6 @@ struct DmaCfg {
   static_assert(!VSHARE || DV <= DQK, "shared V rows");
 };
 
-// XOR mask for chunk c of a row of NC chunks: swizzle inside aligned groups of 16, 8, 4 or 2
-template <int NC>
-__device__ __forceinline__ int swz_mask(int c) {
-  if ((c | 15) < NC) return 15;
-  if ((c | 7) < NC) return 7;
-  if ((c | 3) < NC) return 3;
-  if ((c | 1) < NC) return 1;
-  return 0;
-}
 // Swizzle keys.  K rows are read 16 at a time in the permuted order
 // {0-3, 8-11, 16-19, 24-27} (+4): key (r & 3) | ((r >> 1) & 12) gives those 16
 // rows 16 distinct keys.  Separate V buffers are read as runs of consecutive
@@ -89,38 +81,6 @@ template <int NC>
 __device__ __forceinline__ int phys_chunk(int c, int key) {
   return c ^ (key & swz_mask<NC>(c));
 }
-
-// s_barrier without the release/acquire fence of __syncthreads (the fence would
-// drain the load ring); compiler-only memory clobbers keep LDS accesses in order
-__device__ __forceinline__ void ring_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));  // lgkmcnt(0): own LDS writes done
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-template <int N>
-__device__ __forceinline__ void wait_loads() {
-  asm volatile("" ::: "memory");
-  wait_vmcnt<N>();
-  asm volatile("" ::: "memory");
-}
-
-__device__ __forceinline__ void dma16(const void* gptr, unsigned char* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(gptr, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
-}
-
-// 8 e4m3 codes (two dwords) -> 8 bf16
-__device__ __forceinline__ bf16x8 e4m3x8_to_bf16x8(u32x2 w) {
-  bf16x2 a = e4m3x2_to_bf16x2<false>(w[0]);
-  bf16x2 b = e4m3x2_to_bf16x2<true>(w[0]);
-  bf16x2 c = e4m3x2_to_bf16x2<false>(w[1]);
-  bf16x2 d = e4m3x2_to_bf16x2<true>(w[1]);
-  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
-}
-
-typedef int i32x2_t __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) i32x2_t lds_i32x2;
 
 template <class C>
 __device__ __forceinline__ void dma_block(const KParams& p, unsigned char* smem, int32_t* s_pages, const int b,

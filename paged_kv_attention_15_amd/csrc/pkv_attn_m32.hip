@@ -1,0 +1,551 @@
+// pkv_attn_m32.hip -- paged attention on v_mfma_f32_32x32x16_bf16 for the
+// compute-heavy shapes: causal context over a GQA group and MLA latent decode.
+//
+// Measured on gfx950, the 32x32x16 bf16 MFMA sustains one instruction per 32
+// cycles per SIMD from a single wave (the full bf16 matrix rate), while
+// back-to-back 16x16x32 instructions reach about half of it; so the products
+// that dominate these shapes use the 32x32 form.  Both are transposed, putting
+// the query rows on the column axis of the MFMA:
+//   S^T[keys x rows] = K[keys x d] Q^T[d x rows]          A = K rows (LDS), B = Q (registers)
+//   O^T[dv x rows]  += V^T[dv x keys] P^T[keys x rows]    A = V^T (LDS transpose reads), B = P
+// Operand element e of lane l is (row or column l%32, k 8(l/32)+e); result
+// element e of lane l is (row 8(e/4) + 4(l/32) + e%4, column l%32).  A row r of
+// the S^T product is fed the key whose index is r with bits 2 and 3 exchanged;
+// result elements 8s..8s+7 of lane l then hold keys 16s + 8(l/32) + 0..7, which
+// is exactly the B operand of the s-th 16-key step of the PV product: P^T goes
+// from the softmax to the second product without crossing lanes.
+//
+// Each wave owns RB blocks of 32 packed query rows (RB > 1 re-uses every K and
+// V^T operand read from LDS for RB products, which is what keeps LDS traffic
+// below the MFMA time).  KV tiles arrive through the direct-to-LDS ring of
+// pkv_ring.h.  The paging follows the flashinfer.cake_fmha API page's contract
+// (key j of request b is token j % P of page block_tables[b][j / P]); the
+// online softmax and the Split-KV partials follow the FlashInfer and
+// Flash-Decoding pages (running max, rescaled running sum, natural-log LSE).
+
+#include "pkv_device.h"
+#include "pkv_internal.h"
+#include "pkv_ring.h"
+
+namespace pkv {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+template <int DQK_, int DV_, bool VSHARE_, int RB_, int NW_, int KB_, int NS_, int OCC_ = 1>
+struct M32Cfg {
+  static constexpr int DQK = DQK_, DV = DV_, RB = RB_, NW = NW_, KB = KB_, NS = NS_;
+  static constexpr int OCC = OCC_;  // waves per SIMD the register budget is sized for
+  static constexpr bool VSHARE = VSHARE_;
+  static constexpr int NTHR = 64 * NW;
+  static constexpr int ROWS = NW * RB * 32;  // packed query rows per workgroup
+  static constexpr int T = KB * 32;          // keys per ring stage
+  static constexpr int KROWB = DQK * 2;
+  static constexpr int VROWB = VSHARE ? KROWB : DV * 2;
+  static constexpr int NCK = KROWB / 16;
+  static constexpr int NCV = VROWB / 16;
+  static constexpr int KTILE = T * KROWB;
+  static constexpr int VTILE = VSHARE ? 0 : T * VROWB;
+  static constexpr int STAGE = KTILE + VTILE;
+  static constexpr int KCH = T * NCK;
+  static constexpr int VCH = VSHARE ? 0 : T * NCV;
+  static constexpr int NI = (KCH + VCH) / 64;  // wave-instructions per stage
+  static constexpr int KPW = (NI + NW - 1) / NW;
+  static constexpr int NKS = DQK / 16;  // 16-wide k steps of S^T
+  static constexpr int NDB = DV / 32;   // 32-wide value blocks of O^T
+  static constexpr int LDS = NS * STAGE;
+  // long rows: recompute the loader's per-lane geometry every stage (registers are the limit)
+  static constexpr bool LEAN = DQK > 256;
+  static_assert(KCH % 64 == 0 && VCH % 64 == 0, "wave-instructions must not straddle K and V");
+  static_assert(KPW * (NS - 1) < 64, "vmcnt holds at most 63 outstanding loads");
+  static_assert(DQK % 16 == 0 && DV % 32 == 0 && NCK % 4 == 0 && NCV % 4 == 0, "tiling");
+  static_assert(NS >= 2 && NS <= 6, "ring depth");
+  static_assert(!VSHARE || DV <= DQK, "shared V rows");
+};
+
+// Swizzle key of LDS row r (K and V rows alike): 16-byte chunk c of the row is
+// stored at c ^ (key & group mask).  Chosen for the two read patterns: the
+// eight rows {0-3, 8-11} (+4, +16) that one ds_read_b128 serves together get
+// eight distinct keys, and the four rows of each 16-lane transpose read get
+// chunk pairs that do not overlap.
+__device__ __forceinline__ int m32_key(int r) { return 4 * (r & 3) + 2 * ((r >> 3) & 1); }
+
+// Physical chunk of logical chunk c_const + c_lane where c_lane < 4 never leaves
+// c_const's swizzle group.  With c_const a compile-time constant only the XOR of
+// the low bits depends on the lane, so offsets differing by whole groups fold
+// into instruction immediates.
+template <int NC>
+__device__ __forceinline__ int chunk_phys(int c_const, int c_lane, int key) {
+  const int m = swz_mask<NC>(c_const);
+  return (c_const & ~m) + (((c_const & m) + c_lane) ^ (key & m));
+}
+
+// Largest rise of a row's max (log2 units) absorbed without rescaling O
+constexpr float kLazyMax = 8.f;
+
+// A row r of S^T reads key r with bits 2 and 3 exchanged
+__device__ __forceinline__ int m32_perm(int r) { return (r & 0x13) | ((r & 4) << 1) | ((r & 8) >> 1); }
+
+template <class C>
+__device__ __forceinline__ void m32_block(const KParams& p, unsigned char* smem, int32_t* s_pages, const int b,
+                                          const int g, const int rblk, const int part_lo, const int part_hi,
+                                          const int slot, const bool lead) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int tid = threadIdx.x;
+  const int h = lane >> 5;   // k half of the operands, row quad of the results
+  const int c32 = lane & 31;  // query row inside a 32-row block
+  const int G = p.group;
+
+  __syncthreads();  // LDS of a previous piece is free again (no loads are in flight here)
+
+  int t0, n_b;
+  if (p.is_context) {
+    int a0 = p.q_indptr[b], a1 = p.q_indptr[b + 1];
+    bool bad = (a0 < 0) || (a1 < a0) || (a1 - a0 > p.max_q_len) || (a1 > p.total_q);
+    if (bad) {
+      if (lead && g == 0 && rblk == 0 && tid == 0) flag_error(p.err_word, PKV_DEVERR_QINDPTR);
+      return;
+    }
+    t0 = a0;
+    n_b = a1 - a0;
+  } else {
+    t0 = b * p.q_len;
+    n_b = p.q_len;
+  }
+  const int row_space = n_b * G;
+  const int row0 = rblk * C::ROWS;
+  if (row0 >= row_space) return;
+
+  int L = p.seq_lens[b];
+  const int cap = p.max_pages_per_seq * p.page_size;
+  if (lead && g == 0 && rblk == 0 && tid == 0) {
+    if (L > cap) flag_error(p.err_word, PKV_DEVERR_SEQ_GT_TABLE);
+    if (L < n_b) flag_error(p.err_word, PKV_DEVERR_SEQ_LT_QLEN);
+  }
+  L = max(0, min(L, cap));
+
+  const int last_row = min(row0 + C::ROWS, row_space) - 1;
+  const int i_max = last_row / G;
+  const int c_max = p.causal ? min(L, max(0, L - n_b + i_max + 1)) : L;
+  const int kv_lo = part_lo;
+  const int kv_hi = min(part_hi, c_max);
+  const int n_tiles = kv_hi > kv_lo ? (kv_hi - kv_lo + C::T - 1) / C::T : 0;
+  if (n_tiles == 0 && p.ws_o != nullptr) return;
+
+  const int pg_lo = kv_lo >> p.log2_page;
+  const int n_pg = n_tiles > 0 ? ((kv_hi - 1) >> p.log2_page) - pg_lo + 1 : 0;
+  for (int i = tid; i < n_pg; i += C::NTHR) {
+    int pg = p.table[(int64_t)b * p.table_stride + pg_lo + i];
+    if (p.num_pages > 0 && (pg < 0 || pg >= p.num_pages)) {
+      flag_error(p.err_word, PKV_DEVERR_PAGE_RANGE);
+      pg = min(max(pg, 0), p.num_pages - 1);
+    }
+    s_pages[i] = pg;
+  }
+
+  const float k_scale = p.k_scale_dev ? *p.k_scale_dev : p.k_scale;
+  const float v_scale = p.v_scale_dev ? *p.v_scale_dev : p.v_scale;
+  const float sc2 = p.scale * k_scale * kLog2e;
+
+  int row_t[C::RB], row_h[C::RB], row_c[C::RB];
+  bool row_ok[C::RB];
+  bf16x8 qB[C::RB][C::NKS];
+#pragma unroll
+  for (int rb = 0; rb < C::RB; ++rb) {
+    const int R = row0 + (wave * C::RB + rb) * 32 + c32;
+    row_ok[rb] = R < row_space;
+    const int i = row_ok[rb] ? R / G : 0;
+    row_t[rb] = t0 + i;
+    row_h[rb] = g * G + (row_ok[rb] ? R % G : 0);
+    const int c = p.causal ? L - n_b + i + 1 : L;
+    row_c[rb] = row_ok[rb] ? min(max(c, 0), kv_hi) : 0;
+    const __bf16* qrow = (const __bf16*)p.q + row_t[rb] * p.q_st + row_h[rb] * p.q_sh + 8 * h;
+#pragma unroll
+    for (int ks = 0; ks < C::NKS; ++ks) qB[rb][ks] = row_ok[rb] ? *(const bf16x8*)(qrow + 16 * ks) : bf16x8{};
+  }
+
+  // visible-key bounds over this wave's rows: blocks below c_lo need no mask,
+  // blocks at or past c_hi hold no visible key of any of its rows
+  int c_lo = INT_MAX, c_hi = 0;
+#pragma unroll
+  for (int rb = 0; rb < C::RB; ++rb)
+    if (row_ok[rb]) {
+      c_lo = min(c_lo, row_c[rb]);
+      c_hi = max(c_hi, row_c[rb]);
+    }
+  c_lo = -wave_max_i(-c_lo);
+  c_hi = wave_max_i(c_hi);
+
+  float m_run[C::RB], l_run[C::RB];
+  f32x16 O[C::RB][C::NDB];
+#pragma unroll
+  for (int rb = 0; rb < C::RB; ++rb) {
+    m_run[rb] = -INFINITY;
+    l_run[rb] = 0.f;
+#pragma unroll
+    for (int d = 0; d < C::NDB; ++d)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) O[rb][d][e] = 0.f;
+  }
+
+  __syncthreads();  // page list visible
+
+  // ---- loader: wave-instruction q of this wave fills chunks I*64 .. I*64+63 of the
+  // stage (I = wave*KPW + q); lane l fetches the global chunk whose swizzled LDS slot
+  // is I*64 + l.
+  const int pmask = p.page_size - 1;
+  const uint32_t k_tok_b = (uint32_t)(p.k_stok * 2), v_tok_b = (uint32_t)(p.v_stok * 2);
+  const uint32_t k_head_b = (uint32_t)(g * p.k_sh * 2), v_head_b = (uint32_t)(g * p.v_sh * 2);
+  const uint64_t k_pg_b = (uint64_t)p.k_sp * 2, v_pg_b = (uint64_t)p.v_sp * 2;
+  const uint64_t k_addr = (uint64_t)p.k, v_addr = (uint64_t)p.v;
+  auto geometry = [&](int ln, int* q_row, uint32_t* q_chunk) {
+#pragma unroll
+    for (int q = 0; q < C::KPW; ++q) {
+      const int I = min(wave * C::KPW + q, C::NI - 1);
+      const int P = I * 64 + ln;
+      if (I * 64 < C::KCH) {
+        const int r = P / C::NCK, ph = P % C::NCK;
+        q_row[q] = r;
+        q_chunk[q] = (uint32_t)((ph ^ (m32_key(r) & swz_mask<C::NCK>(ph))) * 16);
+      } else {
+        const int Pv = P - C::KCH;
+        const int r = Pv / C::NCV, ph = Pv % C::NCV;
+        q_row[q] = r;
+        q_chunk[q] = (uint32_t)((ph ^ (m32_key(r) & swz_mask<C::NCV>(ph))) * 16);
+      }
+    }
+  };
+  int g_row[C::LEAN ? 1 : C::KPW];
+  uint32_t g_chunk[C::LEAN ? 1 : C::KPW];
+  if constexpr (!C::LEAN) geometry(lane, g_row, g_chunk);
+  auto issue = [&](int tile, int stage) {
+    const int tok0 = kv_lo + tile * C::T;
+    unsigned char* st = smem + stage * C::STAGE;
+    int q_row_l[C::KPW];
+    uint32_t q_chunk_l[C::KPW];
+    const int* q_row = q_row_l;
+    const uint32_t* q_chunk = q_chunk_l;
+    if constexpr (C::LEAN) {
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      geometry(ln, q_row_l, q_chunk_l);
+    } else {
+      q_row = g_row;
+      q_chunk = g_chunk;
+    }
+    int pg[C::KPW];
+#pragma unroll
+    for (int q = 0; q < C::KPW; ++q) {
+      const int tok = min(tok0 + q_row[q], kv_hi - 1);
+      pg[q] = s_pages[(tok >> p.log2_page) - pg_lo];
+    }
+#pragma unroll
+    for (int q = 0; q < C::KPW; ++q) {
+      const int I = min(wave * C::KPW + q, C::NI - 1);
+      const int tok = min(tok0 + q_row[q], kv_hi - 1);
+      const bool is_k = I * 64 < C::KCH;
+      const uint64_t base = is_k ? k_addr : v_addr;
+      const uint64_t pgb = is_k ? k_pg_b : v_pg_b;
+      const uint32_t inpage = (uint32_t)(tok & pmask) * (is_k ? k_tok_b : v_tok_b) + (is_k ? k_head_b : v_head_b) +
+                              q_chunk[q];
+      const unsigned char* src =
+          (const unsigned char*)(base + ((uint64_t)(uint32_t)pg[q] * (uint32_t)pgb + inpage));
+      dma16(src, st + I * 1024);
+    }
+  };
+
+  // ---- per-lane operand offsets inside a stage (constant parts fold into immediates)
+  const int kkey = m32_perm(c32);  // key read by A row c32 of S^T, inside each 32-key block
+  const int kfk = m32_key(kkey);
+  const int kl_row = kkey * C::KROWB;
+  // V^T transpose reads: 16-lane group q = lane/16 covers values 16(q&1) .. +15 and
+  // keys 8(q>>1) + 4*half + (lane%16)/4; source lane j = lane%16 supplies 4 values
+  // of one key row at value offset 4(j%4)
+  const int vj = lane & 15;
+  const int vq = lane >> 4;
+  const int vrow = 8 * (vq >> 1) + (vj >> 2);
+  const int vfk = m32_key(vrow);
+  const int vc_lane = 2 * (vq & 1) + ((vj & 3) >> 1);
+  const int vl_row = vrow * C::VROWB + 8 * (vj & 1);
+
+  // prologue: the first NS-1 tiles in flight
+#pragma unroll
+  for (int t = 0; t < C::NS - 1; ++t)
+    if (t < n_tiles) issue(t, t);
+
+  for (int tile = 0; tile < n_tiles; ++tile) {
+    const int stage = tile % C::NS;
+    const int after = min(C::NS - 2, n_tiles - 1 - tile);
+    if constexpr (C::NS >= 5) {
+      if (after >= 3) wait_loads<3 * C::KPW>();
+      else if (after == 2) wait_loads<2 * C::KPW>();
+      else if (after == 1) wait_loads<C::KPW>();
+      else wait_loads<0>();
+    } else if constexpr (C::NS == 4) {
+      if (after >= 2) wait_loads<2 * C::KPW>();
+      else if (after == 1) wait_loads<C::KPW>();
+      else wait_loads<0>();
+    } else if constexpr (C::NS == 3) {
+      if (after >= 1) wait_loads<C::KPW>();
+      else wait_loads<0>();
+    } else {
+      wait_loads<0>();
+    }
+    ring_barrier();  // every wave's part of `tile` landed; every wave left tile-1's stage
+    if (tile + C::NS - 1 < n_tiles) issue(tile + C::NS - 1, (tile + C::NS - 1) % C::NS);
+
+    const unsigned char* kst = smem + stage * C::STAGE;
+    const unsigned char* vst = C::VSHARE ? kst : kst + C::KTILE;
+
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb) {
+      const int blk_tok = kv_lo + tile * C::T + kb * 32;
+      if (blk_tok >= c_hi) break;  // uniform: no row of this wave sees these keys
+      const unsigned char* kblk = kst + kb * 32 * C::KROWB + kl_row;
+      const unsigned char* vblk = vst + kb * 32 * C::VROWB + vl_row;
+
+      // ---- S^T = K Q^T over this 32-key block
+      f32x16 acc[C::RB];
+#pragma unroll
+      for (int rb = 0; rb < C::RB; ++rb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[rb][e] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < C::NKS; ++ks) {
+        if constexpr (C::NKS > 12) {
+          if (ks % 6 == 0) __builtin_amdgcn_sched_barrier(0);
+        }
+        const bf16x8 a = *(const bf16x8*)(kblk + chunk_phys<C::NCK>(2 * ks, h, kfk) * 16);
+#pragma unroll
+        for (int rb = 0; rb < C::RB; ++rb) acc[rb] = mfma32x32x16(a, qB[rb][ks], acc[rb]);
+      }
+
+      // ---- online softmax (exp2 domain); element e holds key 16(e/8) + 8h + e%8.
+      // The running max only moves when a score exceeds it by more than kLazyMax
+      // (log2 units): below that the stale max keeps every weight within 2^kLazyMax,
+      // and since the sum and O share that reference the result is unchanged --
+      // O is rescaled only on real jumps.
+      const bool full = blk_tok + 32 <= c_lo;
+      bf16x8 pb[C::RB][2];
+#pragma unroll
+      for (int rb = 0; rb < C::RB; ++rb) {
+        float w[16];
+        float mx;
+        if (full) {
+          // scores are acc * sc2: reduce the raw accumulators, scale once
+          float mr = acc[rb][0];
+          if (sc2 >= 0.f) {
+#pragma unroll
+            for (int e = 1; e < 16; ++e) mr = fmaxf(mr, acc[rb][e]);
+            mr = half_swap_max(mr);
+          } else {
+#pragma unroll
+            for (int e = 1; e < 16; ++e) mr = fminf(mr, acc[rb][e]);
+            mr = half_swap_min(mr);
+          }
+          mx = mr * sc2;
+        } else {
+          mx = -INFINITY;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int tok = blk_tok + 16 * (e >> 3) + 8 * h + (e & 7);
+            w[e] = tok < row_c[rb] ? acc[rb][e] * sc2 : -INFINITY;
+            mx = fmaxf(mx, w[e]);
+          }
+          mx = half_swap_max(mx);
+        }
+        const bool move = mx > m_run[rb] + kLazyMax;  // also true on a row's first visible key
+        const float m_new = move ? mx : m_run[rb];
+        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+        if (__builtin_amdgcn_ballot_w64(move) != 0) {
+          const float alpha = move ? fast_exp2(m_run[rb] - m_use) : 1.f;
+          l_run[rb] *= alpha;
+#pragma unroll
+          for (int d = 0; d < C::NDB; ++d) O[rb][d] *= alpha;
+        }
+        m_run[rb] = m_new;
+        float ps = 0.f;
+        if (full) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            w[e] = fast_exp2(fmaf(acc[rb][e], sc2, -m_use));
+            ps += w[e];
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            w[e] = fast_exp2(w[e] - m_use);
+            ps += w[e];
+          }
+        }
+        l_run[rb] += ps;
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          u32x4 wv{pack_bf16x2(w[8 * st + 0], w[8 * st + 1]), pack_bf16x2(w[8 * st + 2], w[8 * st + 3]),
+                   pack_bf16x2(w[8 * st + 4], w[8 * st + 5]), pack_bf16x2(w[8 * st + 6], w[8 * st + 7])};
+          pb[rb][st] = __builtin_bit_cast(bf16x8, wv);
+        }
+      }
+
+      // ---- O^T += V^T P^T, two 16-key steps per block
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db) {
+        if constexpr (C::NDB > 8) {
+          if (db % 4 == 0) __builtin_amdgcn_sched_barrier(0);
+        }
+        const int voff = chunk_phys<C::NCV>(4 * db, vc_lane, vfk) * 16;
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          const unsigned char* src = vblk + 16 * st * C::VROWB + voff;
+          const s16x4 lo = lds_read_tr16(src);
+          const s16x4 hi = lds_read_tr16(src + 4 * C::VROWB);
+          typedef short s16x8 __attribute__((ext_vector_type(8)));
+          const bf16x8 a = __builtin_bit_cast(bf16x8, s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+#pragma unroll
+          for (int rb = 0; rb < C::RB; ++rb) O[rb][db] = mfma32x32x16(a, pb[rb][st], O[rb][db]);
+        }
+      }
+    }
+  }
+
+  // ---- full row sums (each lane half summed its own 16 keys of every block)
+#pragma unroll
+  for (int rb = 0; rb < C::RB; ++rb) l_run[rb] = half_swap_sum(l_run[rb]);
+
+  // ---- epilogue: element e of O[rb][db] is value 32db + 8(e/4) + 4h + e%4 of row c32
+  const bool split_mode = p.ws_o != nullptr;
+#pragma unroll
+  for (int rb = 0; rb < C::RB; ++rb) {
+    if (!row_ok[rb]) continue;
+    const bool empty = !(l_run[rb] > 0.f);
+    const float inv = empty ? 0.f : v_scale / l_run[rb];
+    const float lse = empty ? -INFINITY : (m_run[rb] * kLn2 + __logf(l_run[rb]));
+    const int64_t row_g = (int64_t)row_t[rb] * p.num_qo_heads + row_h[rb];
+    if (split_mode) {
+      const int64_t prow = (int64_t)slot * p.rows_total + row_g;
+      if (h == 0) p.ws_lse[prow] = lse;
+      if (!empty) {
+        float* dst = p.ws_o + prow * C::DV + 4 * h;
+#pragma unroll
+        for (int d = 0; d < C::NDB; ++d)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            *(f32x4*)(dst + 32 * d + 8 * q) =
+                f32x4{O[rb][d][4 * q], O[rb][d][4 * q + 1], O[rb][d][4 * q + 2], O[rb][d][4 * q + 3]} * inv;
+      }
+    } else {
+      if (p.lse_out && h == 0) p.lse_out[row_g] = lse;
+      if (p.o_dtype == PKV_DTYPE_BF16) {
+        __bf16* dst = (__bf16*)p.out + row_t[rb] * p.o_st + row_h[rb] * p.o_sh + 4 * h;
+#pragma unroll
+        for (int d = 0; d < C::NDB; ++d)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            u32x2 w{pack_bf16x2(O[rb][d][4 * q] * inv, O[rb][d][4 * q + 1] * inv),
+                    pack_bf16x2(O[rb][d][4 * q + 2] * inv, O[rb][d][4 * q + 3] * inv)};
+            *(u32x2*)(dst + 32 * d + 8 * q) = w;
+          }
+      } else {
+        float* dst = (float*)p.out + row_t[rb] * p.o_st + row_h[rb] * p.o_sh + 4 * h;
+#pragma unroll
+        for (int d = 0; d < C::NDB; ++d)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            *(f32x4*)(dst + 32 * d + 8 * q) =
+                f32x4{O[rb][d][4 * q], O[rb][d][4 * q + 1], O[rb][d][4 * q + 2], O[rb][d][4 * q + 3]} * inv;
+      }
+    }
+  }
+}
+
+// Workgroup order.  The hardware hands workgroup i to XCD i % 8 and each XCD has
+// its own L2, so consecutive logical work items (the row blocks of one request
+// and KV head, which read the same pages) are placed on one XCD.  For causal
+// context the row blocks are also taken heaviest first (later query positions
+// see more keys), so that every CU receives a mix of long and short blocks.
+template <class C>
+__global__ __launch_bounds__(C::NTHR, C::OCC) void attn_m32_kernel(const KParams p) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  int32_t* s_pages = (int32_t*)(smem + C::LDS);
+  const int nx = gridDim.x, ny = gridDim.y, nz = gridDim.z;
+  const int rbc = p.row_blocks;
+  const int64_t N = (int64_t)nx * ny * nz;
+  const int64_t P = blockIdx.x + (int64_t)nx * (blockIdx.y + (int64_t)ny * blockIdx.z);
+  int split, y, z;
+  const int64_t per = N / 8;
+  if (N % 8 == 0 && nx == 1 && p.is_context && p.causal && per % rbc == 0) {
+    const int64_t groups = per / rbc;  // (request, KV head) groups per XCD
+    const int64_t xcd = P % 8, idx = P / 8;
+    const int rb = rbc - 1 - (int)(idx / groups);
+    const int64_t grp = xcd * groups + idx % groups;  // = b * Hkv + g
+    split = 0;
+    z = (int)(grp / p.num_kv_heads);
+    y = (int)(grp % p.num_kv_heads) * rbc + rb;
+  } else {
+    const int64_t Lg = N % 8 == 0 ? (P % 8) * per + P / 8 : P;
+    split = (int)(Lg % nx);
+    y = (int)((Lg / nx) % ny);
+    z = (int)(Lg / ((int64_t)nx * ny));
+  }
+  const int span = p.pages_per_split * p.page_size;
+  m32_block<C>(p, smem, s_pages, z, y / rbc, y % rbc, split * span, split * span + span, split, split == 0);
+}
+
+// ---------------------------------------------------------------- instances
+//                          DQK  DV   VSH    RB NW KB NS OCC
+using M32Ctx = M32Cfg<128, 128, false, 2, 4, 2, 4>;      // 256 rows, 64-key stages of 32 KiB
+using M32Mla = M32Cfg<576, 512, true, 1, 4, 1, 4>;       // 128 heads, 32-key stages of 36 KiB
+using M32CtxW8 = M32Cfg<128, 128, false, 1, 8, 2, 4, 2>;  // 256 rows on 8 waves (two per SIMD)
+using M32CtxR1 = M32Cfg<128, 128, false, 1, 4, 1, 4, 2>;  // 128 rows, 16 KiB stages: two workgroups per CU
+using M32CtxR1S3 = M32Cfg<128, 128, false, 1, 4, 1, 3, 3>;  // 128 rows, 48 KiB: three workgroups per CU
+
+template <class C>
+static void fill_m32_shape(MfmaShape* s) {
+  s->rows_per_block = C::ROWS;
+  s->tile_tokens = C::T;
+  s->threads = C::NTHR;
+  s->lds_static = C::LDS;
+}
+
+bool m32_shape(int32_t kernel, MfmaShape* s) {
+  switch (kernel) {
+    case KERNEL_M32_CTX_BF16: fill_m32_shape<M32Ctx>(s); return true;
+    case KERNEL_M32_MLA_BF16: fill_m32_shape<M32Mla>(s); return true;
+    case KERNEL_M32_CTX_W8: fill_m32_shape<M32CtxW8>(s); return true;
+    case KERNEL_M32_CTX_R1: fill_m32_shape<M32CtxR1>(s); return true;
+    case KERNEL_M32_CTX_R1S3: fill_m32_shape<M32CtxR1S3>(s); return true;
+    default: return false;
+  }
+}
+
+template <class C>
+static hipError_t launch_m32_cfg(const KParams& p, hipStream_t s) {
+  static bool attr_done = false;  // idempotent; a race only repeats the same call
+  const size_t lds = C::LDS + (((size_t)p.page_list_cap + 3) & ~size_t(3)) * sizeof(int32_t);
+  if (!attr_done) {
+    hipError_t e = hipFuncSetAttribute((const void*)attn_m32_kernel<C>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       160 * 1024);
+    if (e != hipSuccess) return e;
+    attr_done = true;
+  }
+  dim3 grid(p.num_splits, p.num_kv_heads * p.row_blocks, p.batch);
+  hipLaunchKernelGGL(attn_m32_kernel<C>, grid, dim3(C::NTHR), lds, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_m32(int32_t kernel, const KParams& p, hipStream_t s) {
+  switch (kernel) {
+    case KERNEL_M32_CTX_BF16: return launch_m32_cfg<M32Ctx>(p, s);
+    case KERNEL_M32_MLA_BF16: return launch_m32_cfg<M32Mla>(p, s);
+    case KERNEL_M32_CTX_W8: return launch_m32_cfg<M32CtxW8>(p, s);
+    case KERNEL_M32_CTX_R1: return launch_m32_cfg<M32CtxR1>(p, s);
+    case KERNEL_M32_CTX_R1S3: return launch_m32_cfg<M32CtxR1S3>(p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace pkv

@@ -98,6 +98,19 @@ __device__ __forceinline__ int wave_max_i(int v) {
   for (int m = 32; m >= 1; m >>= 1) v = max(v, __shfl_xor(v, m, 64));
   return v;
 }
+// max / sum of lane l and lane l ^ 32 in one v_permlane32_swap (no LDS round trip)
+__device__ __forceinline__ float half_swap_max(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_swap_min(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fminf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_swap_sum(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 // 2^x on v_exp_f32 directly (no denormal-range fix-up; 2^-inf = 0)
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float wave_sum(float v) {

@@ -35,7 +35,13 @@ enum KernelId : int32_t {
   KERNEL_DMA_GQA_FP8_S2 = 20,   // 4 token waves, 128-key tiles, 2 stages (64 KiB: two groups per CU)
   KERNEL_DMA_GQA_BF16_W4 = 21,  // 4 token waves, 128-key tiles, 2 stages (128 KiB)
   KERNEL_DMA_GQA_BF16_S2 = 22,  // 2 token waves, 64-key tiles, 2 stages (64 KiB)
-  KERNEL_COUNT = 23,
+  // 32x32x16 MFMA families (pkv_attn_m32.hip), bf16 KV
+  KERNEL_M32_CTX_BF16 = 23,  // D = 128, 4 waves x 64 packed rows, 64-key stages
+  KERNEL_M32_MLA_BF16 = 24,  // D_qk = 576 / D_v = 512 latent, 4 waves x 32 heads, 32-key stages
+  KERNEL_M32_CTX_W8 = 25,    // D = 128, 8 waves x 32 rows (two waves per SIMD)
+  KERNEL_M32_CTX_R1 = 26,    // D = 128, 4 waves x 32 rows, 4 x 16 KiB stages (two workgroups per CU)
+  KERNEL_M32_CTX_R1S3 = 27,  // D = 128, 4 waves x 32 rows, 3 x 16 KiB stages (three workgroups per CU)
+  KERNEL_COUNT = 28,
 };
 
 // Everything a kernel reads, by value.  Element strides as in pkv_args.
@@ -109,5 +115,7 @@ struct MfmaShape {
 bool mfma_shape(int32_t kernel, MfmaShape* out);
 bool dma_shape(int32_t kernel, MfmaShape* out);
 hipError_t launch_dma(int32_t kernel, const KParams& p, hipStream_t s);
+bool m32_shape(int32_t kernel, MfmaShape* out);
+hipError_t launch_m32(int32_t kernel, const KParams& p, hipStream_t s);
 
 }  // namespace pkv

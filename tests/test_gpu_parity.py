@@ -96,7 +96,7 @@ def test_balanced_schedule_speculative_rows_and_empty_request():
 
 
 @pytest.mark.parametrize("q_len,kernel", [(1, None), (2, None), (1, "dma_mla_bf16"), (2, "dma_mla_bf16"),
-                                          (1, "mla_bf16")])
+                                          (1, "mla_bf16"), (1, "m32_mla_bf16"), (2, "m32_mla_bf16")])
 def test_mla_small(q_len, kernel):
     prob = W.make_problem(name=f"mla-small-q{q_len}", seed=3, batch=3, seq_lens=[2, 70, 300],
                           q_lens=[q_len] * 3, num_qo_heads=128, num_kv_heads=1, head_dim_qk=576,
@@ -299,15 +299,27 @@ def test_gqa_kernel_families_match_oracle(kernel, kv, splits):
     compare(prob, dp, label=f"{kernel}/{splits}")
 
 
-@pytest.mark.parametrize("kernel", ["dma_wide_bf16", "wide_bf16"])
-def test_context_kernel_families_match_oracle(kernel):
+@pytest.mark.parametrize("kernel,splits", [("dma_wide_bf16", None), ("wide_bf16", None), ("m32_ctx_bf16", None),
+                                           ("m32_ctx_bf16", 3), ("m32_ctx_w8", None), ("m32_ctx_r1", None),
+                                           ("m32_ctx_r1s3", None), ("m32_ctx_r1", 2)])
+def test_context_kernel_families_match_oracle(kernel, splits):
     prob = W.make_problem(name="ctx-fam", seed=9, batch=3, seq_lens=[70, 5, 333], q_lens=[64, 5, 130],
                           num_qo_heads=16, num_kv_heads=2, head_dim_qk=128, head_dim_v=128, page_size=16,
                           is_decode=False, poison=True, extra_page_frac=0.3, table_slack_pages=1)
-    dp = pkv.upload(prob, "cuda", kernel=kernel)
+    say(f"case {kernel} splits={splits}")
+    dp = pkv.upload(prob, "cuda", kernel=kernel, num_splits=splits)
     dp.run()
     torch.cuda.synchronize()
-    compare(prob, dp, label=kernel)
+    compare(prob, dp, label=f"{kernel}/{splits}")
+
+
+def test_context_full_size_m32():
+    prob = W.context_b4_q511_kv2047()
+    say(f"case {prob.name} kernel=m32_ctx_bf16")
+    dp = pkv.upload(prob, "cuda", kernel="m32_ctx_bf16")
+    dp.run()
+    torch.cuda.synchronize()
+    compare(prob, dp, pairs=sample_pairs(prob, 512), label="m32_ctx_bf16")
 
 
 def test_context_fp8_kv_families_match_oracle():
