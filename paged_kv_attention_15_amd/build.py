@@ -16,6 +16,8 @@ FLAGS = [
     # no packed-fp32 instructions anywhere in the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-munsafe-fp-atomics", "-Wno-unused-result",
+    # the ring loads name M0 in their clobber list on purpose (see pkv_ring.h)
+    "-Wno-inline-asm",
     "-I", os.path.join(HERE, "..", "include"),
 ]
 

@@ -190,6 +190,8 @@ bool kernel_supports(int32_t k, const pkv_args* a, bool is_context) {
     case pkv::KERNEL_M32_CTX_W8:
     case pkv::KERNEL_M32_CTX_R1:
     case pkv::KERNEL_M32_CTX_R1S3:
+    case pkv::KERNEL_M32_CTX_R2:
+    case pkv::KERNEL_M32_CTX_R2W8:
       return d128 && !fp8;
     case pkv::KERNEL_M32_MLA_BF16: return mla && !fp8;
   }
@@ -226,10 +228,12 @@ int32_t choose_kernel(const pkv_args* a, bool is_context) {
   const int G = a->num_qo_heads / a->num_kv_heads;
   // Measured on MI355X (bf16 GQA decode B32/L4096, e4m3 ragged decode B16, MLA
   // B512/L4096, causal context B4 q511/L2047): register-staged tiles win for
-  // bf16 decode, the direct-to-LDS ring for e4m3 decode, MLA and context.
+  // bf16 decode, the direct-to-LDS ring for e4m3 decode and MLA, the 32x32 MFMA
+  // family with two waves per SIMD for bf16 context.
   if (a->head_dim_qk == 128 && a->head_dim_v == 128 && !a->v_shares_k) {
     const int64_t rows = is_context ? (int64_t)a->max_q_len * G : (int64_t)a->q_len * G;
     if (!is_context && rows <= 16) return fp8 ? pkv::KERNEL_DMA_GQA_FP8_S2 : pkv::KERNEL_GQA_BF16;
+    if (is_context && !fp8) return pkv::KERNEL_M32_CTX_W8;
     return fp8 ? pkv::KERNEL_DMA_WIDE_FP8 : pkv::KERNEL_DMA_WIDE_BF16;
   }
   if (a->head_dim_qk == 576 && a->head_dim_v == 512 && a->v_shares_k)

@@ -35,10 +35,14 @@ __device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-template <int DQK_, int DV_, bool VSHARE_, int RB_, int NW_, int KB_, int NS_, int OCC_ = 1>
+template <int DQK_, int DV_, bool VSHARE_, int RB_, int NW_, int KB_, int NS_, int OCC_ = 1, bool PREF_ = true>
 struct M32Cfg {
   static constexpr int DQK = DQK_, DV = DV_, RB = RB_, NW = NW_, KB = KB_, NS = NS_;
   static constexpr int OCC = OCC_;  // waves per SIMD the register budget is sized for
+  // PREF: software-pipeline the blocks, holding the next block's K operands and
+  // this block's V^T operands in registers; otherwise each block reads its
+  // operands as it goes and other waves of the SIMD cover the latency
+  static constexpr bool PREF = PREF_;
   static constexpr bool VSHARE = VSHARE_;
   static constexpr int NTHR = 64 * NW;
   static constexpr int ROWS = NW * RB * 32;  // packed query rows per workgroup
@@ -57,8 +61,9 @@ struct M32Cfg {
   static constexpr int NKS = DQK / 16;  // 16-wide k steps of S^T
   static constexpr int NDB = DV / 32;   // 32-wide value blocks of O^T
   static constexpr int LDS = NS * STAGE;
-  // long rows: recompute the loader's per-lane geometry every stage (registers are the limit)
-  static constexpr bool LEAN = DQK > 256;
+  // recompute the loader's per-lane geometry every stage instead of keeping it
+  // live: long rows, or more than one wave per SIMD (registers are the limit)
+  static constexpr bool LEAN = DQK > 256 || OCC > 1;
   static_assert(KCH % 64 == 0 && VCH % 64 == 0, "wave-instructions must not straddle K and V");
   static_assert(KPW * (NS - 1) < 64, "vmcnt holds at most 63 outstanding loads");
   static_assert(DQK % 16 == 0 && DV % 32 == 0 && NCK % 4 == 0 && NCV % 4 == 0, "tiling");
@@ -81,6 +86,29 @@ template <int NC>
 __device__ __forceinline__ int chunk_phys(int c_const, int c_lane, int key) {
   const int m = swz_mask<NC>(c_const);
   return (c_const & ~m) + (((c_const & m) + c_lane) ^ (key & m));
+}
+
+// Compile-time loop (the scheduling builtins below need literal arguments)
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f();
+    static_for<I + 1, N>(f);
+  }
+}
+
+// Instruction-scheduler hint for a product whose LDS operand reads and MFMAs
+// sit in one basic block: the reads run PD steps ahead of the MFMAs that use
+// them (R reads and M MFMAs per step), so each MFMA waits for a read issued
+// PD steps earlier instead of one issued just before it.
+template <int PD, int STEPS, int R, int M>
+__device__ __forceinline__ void sched_reads_ahead() {
+  static_for<0, (PD < STEPS ? PD : STEPS)>([] { __builtin_amdgcn_sched_group_barrier(0x100, R, 0); });
+  static_for<0, (PD < STEPS ? STEPS - PD : 0)>([] {
+    __builtin_amdgcn_sched_group_barrier(0x008, M, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
+  });
+  static_for<0, (PD < STEPS ? PD : STEPS)>([] { __builtin_amdgcn_sched_group_barrier(0x008, M, 0); });
 }
 
 // Largest rise of a row's max (log2 units) absorbed without rescaling O
@@ -272,14 +300,120 @@ __device__ __forceinline__ void m32_block(const KParams& p, unsigned char* smem,
   const int vc_lane = 2 * (vq & 1) + ((vj & 3) >> 1);
   const int vl_row = vrow * C::VROWB + 8 * (vj & 1);
 
-  // prologue: the first NS-1 tiles in flight
+  // ---- the pieces of one 32-key block
+  auto k_operands = [&](int j, bf16x8 (&ka)[C::NKS]) {
+    const unsigned char* kblk = smem + ((j / C::KB) % C::NS) * C::STAGE + (j % C::KB) * 32 * C::KROWB + kl_row;
 #pragma unroll
-  for (int t = 0; t < C::NS - 1; ++t)
-    if (t < n_tiles) issue(t, t);
-
-  for (int tile = 0; tile < n_tiles; ++tile) {
-    const int stage = tile % C::NS;
-    const int after = min(C::NS - 2, n_tiles - 1 - tile);
+    for (int ks = 0; ks < C::NKS; ++ks) ka[ks] = *(const bf16x8*)(kblk + chunk_phys<C::NCK>(2 * ks, h, kfk) * 16);
+  };
+  auto s_product = [&](const bf16x8 (&ka)[C::NKS], f32x16 (&acc)[C::RB]) {
+#pragma unroll
+    for (int rb = 0; rb < C::RB; ++rb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[rb][e] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < C::NKS; ++ks)
+#pragma unroll
+      for (int rb = 0; rb < C::RB; ++rb) acc[rb] = mfma32x32x16(ka[ks], qB[rb][ks], acc[rb]);
+  };
+  // V^T operand of value block db, 16-key step st: two transpose reads of four keys each
+  auto v_operands = [&](int j, bf16x8 (&va)[C::NDB][2]) {
+    const unsigned char* vst = smem + ((j / C::KB) % C::NS) * C::STAGE + (C::VSHARE ? 0 : C::KTILE);
+    const unsigned char* vblk = vst + (j % C::KB) * 32 * C::VROWB + vl_row;
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) {
+      const int voff = chunk_phys<C::NCV>(4 * db, vc_lane, vfk) * 16;
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const unsigned char* src = vblk + 16 * st * C::VROWB + voff;
+        const s16x4 lo = lds_read_tr16(src);
+        const s16x4 hi = lds_read_tr16(src + 4 * C::VROWB);
+        typedef short s16x8 __attribute__((ext_vector_type(8)));
+        va[db][st] = __builtin_bit_cast(bf16x8, s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+      }
+    }
+  };
+  // Online softmax (exp2 domain); element e of acc holds key 16(e/8) + 8h + e%8.
+  // The running max only moves when a score exceeds it by more than kLazyMax
+  // (log2 units): below that the stale max keeps every weight within
+  // 2^kLazyMax, and since the sum and O share that reference the result is
+  // unchanged -- O is rescaled only on real jumps.
+  auto softmax = [&](int j, const f32x16 (&acc)[C::RB], bf16x8 (&pb)[C::RB][2]) {
+    const int blk_tok = kv_lo + j * 32;
+    const bool full = blk_tok + 32 <= c_lo;
+#pragma unroll
+    for (int rb = 0; rb < C::RB; ++rb) {
+      float w[16];
+      float mx;
+      if (full) {
+        // scores are acc * sc2: reduce the raw accumulators, scale once
+        float mr = acc[rb][0];
+        if (sc2 >= 0.f) {
+#pragma unroll
+          for (int e = 1; e < 16; ++e) mr = fmaxf(mr, acc[rb][e]);
+          mr = half_swap_max(mr);
+        } else {
+#pragma unroll
+          for (int e = 1; e < 16; ++e) mr = fminf(mr, acc[rb][e]);
+          mr = half_swap_min(mr);
+        }
+        mx = mr * sc2;
+      } else {
+        mx = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int tok = blk_tok + 16 * (e >> 3) + 8 * h + (e & 7);
+          w[e] = tok < row_c[rb] ? acc[rb][e] * sc2 : -INFINITY;
+          mx = fmaxf(mx, w[e]);
+        }
+        mx = half_swap_max(mx);
+      }
+      const bool move = mx > m_run[rb] + kLazyMax;  // also true on a row's first visible key
+      const float m_new = move ? mx : m_run[rb];
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      if (__builtin_amdgcn_ballot_w64(move) != 0) {
+        const float alpha = move ? fast_exp2(m_run[rb] - m_use) : 1.f;
+        l_run[rb] *= alpha;
+#pragma unroll
+        for (int d = 0; d < C::NDB; ++d) O[rb][d] *= alpha;
+      }
+      m_run[rb] = m_new;
+      float ps = 0.f;
+      if (full) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          w[e] = fast_exp2(fmaf(acc[rb][e], sc2, -m_use));
+          ps += w[e];
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          w[e] = fast_exp2(w[e] - m_use);
+          ps += w[e];
+        }
+      }
+      l_run[rb] += ps;
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        u32x4 wv{pack_bf16x2(w[8 * st + 0], w[8 * st + 1]), pack_bf16x2(w[8 * st + 2], w[8 * st + 3]),
+                 pack_bf16x2(w[8 * st + 4], w[8 * st + 5]), pack_bf16x2(w[8 * st + 6], w[8 * st + 7])};
+        pb[rb][st] = __builtin_bit_cast(bf16x8, wv);
+      }
+    }
+  };
+  auto pv_product = [&](const bf16x8 (&va)[C::NDB][2], const bf16x8 (&pb)[C::RB][2]) {
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int rb = 0; rb < C::RB; ++rb) O[rb][db] = mfma32x32x16(va[db][st], pb[rb][st], O[rb][db]);
+  };
+  // Start of ring tile t: this wave's loads of t are complete once at most
+  // (tiles issued after t) * KPW remain; the barrier then publishes every wave's
+  // part and frees the stage of tile t-1, which the next issue refills.
+  auto tile_start = [&](int t) {
+    const int after = min(C::NS - 2, n_tiles - 1 - t);
     if constexpr (C::NS >= 5) {
       if (after >= 3) wait_loads<3 * C::KPW>();
       else if (after == 2) wait_loads<2 * C::KPW>();
@@ -295,118 +429,77 @@ __device__ __forceinline__ void m32_block(const KParams& p, unsigned char* smem,
     } else {
       wait_loads<0>();
     }
-    ring_barrier();  // every wave's part of `tile` landed; every wave left tile-1's stage
-    if (tile + C::NS - 1 < n_tiles) issue(tile + C::NS - 1, (tile + C::NS - 1) % C::NS);
+    ring_barrier();
+    if (t + C::NS - 1 < n_tiles) issue(t + C::NS - 1, (t + C::NS - 1) % C::NS);
+  };
 
-    const unsigned char* kst = smem + stage * C::STAGE;
-    const unsigned char* vst = C::VSHARE ? kst : kst + C::KTILE;
+  // prologue: the first NS-1 tiles in flight
+#pragma unroll
+  for (int t = 0; t < C::NS - 1; ++t)
+    if (t < n_tiles) issue(t, t);
 
-#pragma unroll
-    for (int kb = 0; kb < C::KB; ++kb) {
-      const int blk_tok = kv_lo + tile * C::T + kb * 32;
-      if (blk_tok >= c_hi) break;  // uniform: no row of this wave sees these keys
-      const unsigned char* kblk = kst + kb * 32 * C::KROWB + kl_row;
-      const unsigned char* vblk = vst + kb * 32 * C::VROWB + vl_row;
-
-      // ---- S^T = K Q^T over this 32-key block
-      f32x16 acc[C::RB];
-#pragma unroll
-      for (int rb = 0; rb < C::RB; ++rb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[rb][e] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < C::NKS; ++ks) {
-        if constexpr (C::NKS > 12) {
-          if (ks % 6 == 0) __builtin_amdgcn_sched_barrier(0);
-        }
-        const bf16x8 a = *(const bf16x8*)(kblk + chunk_phys<C::NCK>(2 * ks, h, kfk) * 16);
-#pragma unroll
-        for (int rb = 0; rb < C::RB; ++rb) acc[rb] = mfma32x32x16(a, qB[rb][ks], acc[rb]);
+  // Software pipeline over 32-key blocks j.  Step j first issues the LDS reads
+  // of the K operands of block j+1 and the V^T operands of block j, runs the
+  // softmax of block j on the VALU while those reads land, and then issues the
+  // S^T product of block j+1 and the PV product of block j back to back on
+  // the matrix core (the other wave of the SIMD fills its VALU meanwhile).  At a
+  // tile boundary the V^T reads of block j come first, so the barrier that
+  // frees block j's stage can be taken before the next tile's K reads.  Blocks
+  // past this wave's last visible key are skipped; every wave still takes
+  // every tile's barrier.
+  const int nblk = n_tiles * C::KB;
+  f32x16 accA[C::RB], accB[C::RB];
+  auto active = [&](int j) { return kv_lo + j * 32 < c_hi; };
+  auto step = [&](int j, f32x16 (&cur)[C::RB], f32x16 (&nxt)[C::RB]) {
+    bf16x8 va[C::NDB][2];
+    bf16x8 ka[C::NKS];
+    const bool act = active(j);
+    const bool act1 = j + 1 < nblk && active(j + 1);
+    if (j + 1 < nblk && (j + 1) % C::KB == 0) {
+      if (act) v_operands(j, va);
+      tile_start((j + 1) / C::KB);
+      if (act1) k_operands(j + 1, ka);
+    } else {
+      if (act1) k_operands(j + 1, ka);
+      if (act) v_operands(j, va);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    bf16x8 pb[C::RB][2];
+    if (act) softmax(j, cur, pb);
+    __builtin_amdgcn_sched_barrier(0);
+    if (act1) s_product(ka, nxt);
+    if (act) pv_product(va, pb);
+  };
+  if constexpr (C::PREF) {
+    if (nblk > 0) {
+      tile_start(0);
+      if (active(0)) {
+        bf16x8 ka[C::NKS];
+        k_operands(0, ka);
+        s_product(ka, accA);
       }
-
-      // ---- online softmax (exp2 domain); element e holds key 16(e/8) + 8h + e%8.
-      // The running max only moves when a score exceeds it by more than kLazyMax
-      // (log2 units): below that the stale max keeps every weight within 2^kLazyMax,
-      // and since the sum and O share that reference the result is unchanged --
-      // O is rescaled only on real jumps.
-      const bool full = blk_tok + 32 <= c_lo;
-      bf16x8 pb[C::RB][2];
-#pragma unroll
-      for (int rb = 0; rb < C::RB; ++rb) {
-        float w[16];
-        float mx;
-        if (full) {
-          // scores are acc * sc2: reduce the raw accumulators, scale once
-          float mr = acc[rb][0];
-          if (sc2 >= 0.f) {
-#pragma unroll
-            for (int e = 1; e < 16; ++e) mr = fmaxf(mr, acc[rb][e]);
-            mr = half_swap_max(mr);
-          } else {
-#pragma unroll
-            for (int e = 1; e < 16; ++e) mr = fminf(mr, acc[rb][e]);
-            mr = half_swap_min(mr);
-          }
-          mx = mr * sc2;
-        } else {
-          mx = -INFINITY;
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int tok = blk_tok + 16 * (e >> 3) + 8 * h + (e & 7);
-            w[e] = tok < row_c[rb] ? acc[rb][e] * sc2 : -INFINITY;
-            mx = fmaxf(mx, w[e]);
-          }
-          mx = half_swap_max(mx);
-        }
-        const bool move = mx > m_run[rb] + kLazyMax;  // also true on a row's first visible key
-        const float m_new = move ? mx : m_run[rb];
-        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        if (__builtin_amdgcn_ballot_w64(move) != 0) {
-          const float alpha = move ? fast_exp2(m_run[rb] - m_use) : 1.f;
-          l_run[rb] *= alpha;
-#pragma unroll
-          for (int d = 0; d < C::NDB; ++d) O[rb][d] *= alpha;
-        }
-        m_run[rb] = m_new;
-        float ps = 0.f;
-        if (full) {
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            w[e] = fast_exp2(fmaf(acc[rb][e], sc2, -m_use));
-            ps += w[e];
-          }
-        } else {
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            w[e] = fast_exp2(w[e] - m_use);
-            ps += w[e];
-          }
-        }
-        l_run[rb] += ps;
-#pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          u32x4 wv{pack_bf16x2(w[8 * st + 0], w[8 * st + 1]), pack_bf16x2(w[8 * st + 2], w[8 * st + 3]),
-                   pack_bf16x2(w[8 * st + 4], w[8 * st + 5]), pack_bf16x2(w[8 * st + 6], w[8 * st + 7])};
-          pb[rb][st] = __builtin_bit_cast(bf16x8, wv);
-        }
+      for (int j = 0; j < nblk; j += 2) {
+        step(j, accA, accB);
+        if (j + 1 < nblk) step(j + 1, accB, accA);
       }
-
-      // ---- O^T += V^T P^T, two 16-key steps per block
-#pragma unroll
-      for (int db = 0; db < C::NDB; ++db) {
-        if constexpr (C::NDB > 8) {
-          if (db % 4 == 0) __builtin_amdgcn_sched_barrier(0);
+    }
+  } else {
+    for (int j = 0; j < nblk; ++j) {
+      if (j % C::KB == 0) tile_start(j / C::KB);
+      if (active(j)) {
+        {
+          bf16x8 ka[C::NKS];
+          k_operands(j, ka);
+          s_product(ka, accA);
+          sched_reads_ahead<4, C::NKS, 1, C::RB>();
         }
-        const int voff = chunk_phys<C::NCV>(4 * db, vc_lane, vfk) * 16;
-#pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          const unsigned char* src = vblk + 16 * st * C::VROWB + voff;
-          const s16x4 lo = lds_read_tr16(src);
-          const s16x4 hi = lds_read_tr16(src + 4 * C::VROWB);
-          typedef short s16x8 __attribute__((ext_vector_type(8)));
-          const bf16x8 a = __builtin_bit_cast(bf16x8, s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
-#pragma unroll
-          for (int rb = 0; rb < C::RB; ++rb) O[rb][db] = mfma32x32x16(a, pb[rb][st], O[rb][db]);
+        bf16x8 pb[C::RB][2];
+        softmax(j, accA, pb);
+        {
+          bf16x8 va[C::NDB][2];
+          v_operands(j, va);
+          pv_product(va, pb);
+          sched_reads_ahead<3, 2 * C::NDB, 2, C::RB>();
         }
       }
     }
@@ -497,11 +590,13 @@ __global__ __launch_bounds__(C::NTHR, C::OCC) void attn_m32_kernel(const KParams
 
 // ---------------------------------------------------------------- instances
 //                          DQK  DV   VSH    RB NW KB NS OCC
-using M32Ctx = M32Cfg<128, 128, false, 2, 4, 2, 4>;      // 256 rows, 64-key stages of 32 KiB
-using M32Mla = M32Cfg<576, 512, true, 1, 4, 1, 4>;       // 128 heads, 32-key stages of 36 KiB
+using M32Ctx = M32Cfg<128, 128, false, 2, 4, 2, 4, 1, false>;  // 256 rows, 64-key stages of 32 KiB
+using M32Mla = M32Cfg<576, 512, true, 1, 4, 1, 4, 1, false>;  // 128 heads, 32-key stages of 36 KiB
 using M32CtxW8 = M32Cfg<128, 128, false, 1, 8, 2, 4, 2>;  // 256 rows on 8 waves (two per SIMD)
-using M32CtxR1 = M32Cfg<128, 128, false, 1, 4, 1, 4, 2>;  // 128 rows, 16 KiB stages: two workgroups per CU
+using M32CtxR1 = M32Cfg<128, 128, false, 1, 4, 1, 4, 2, false>;  // 128 rows, 16 KiB stages: two workgroups per CU
 using M32CtxR1S3 = M32Cfg<128, 128, false, 1, 4, 1, 3, 3>;  // 128 rows, 48 KiB: three workgroups per CU
+using M32CtxR2 = M32Cfg<128, 128, false, 2, 4, 1, 4, 2, false>;   // 256 rows, 64 rows per wave, 64 KiB
+using M32CtxR2W8 = M32Cfg<128, 128, false, 2, 8, 2, 4, 2, false>;  // 512 rows, 64 rows per wave, 128 KiB
 
 template <class C>
 static void fill_m32_shape(MfmaShape* s) {
@@ -518,6 +613,8 @@ bool m32_shape(int32_t kernel, MfmaShape* s) {
     case KERNEL_M32_CTX_W8: fill_m32_shape<M32CtxW8>(s); return true;
     case KERNEL_M32_CTX_R1: fill_m32_shape<M32CtxR1>(s); return true;
     case KERNEL_M32_CTX_R1S3: fill_m32_shape<M32CtxR1S3>(s); return true;
+    case KERNEL_M32_CTX_R2: fill_m32_shape<M32CtxR2>(s); return true;
+    case KERNEL_M32_CTX_R2W8: fill_m32_shape<M32CtxR2W8>(s); return true;
     default: return false;
   }
 }
@@ -544,6 +641,8 @@ hipError_t launch_m32(int32_t kernel, const KParams& p, hipStream_t s) {
     case KERNEL_M32_CTX_W8: return launch_m32_cfg<M32CtxW8>(p, s);
     case KERNEL_M32_CTX_R1: return launch_m32_cfg<M32CtxR1>(p, s);
     case KERNEL_M32_CTX_R1S3: return launch_m32_cfg<M32CtxR1S3>(p, s);
+    case KERNEL_M32_CTX_R2: return launch_m32_cfg<M32CtxR2>(p, s);
+    case KERNEL_M32_CTX_R2W8: return launch_m32_cfg<M32CtxR2W8>(p, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -41,7 +41,9 @@ enum KernelId : int32_t {
   KERNEL_M32_CTX_W8 = 25,    // D = 128, 8 waves x 32 rows (two waves per SIMD)
   KERNEL_M32_CTX_R1 = 26,    // D = 128, 4 waves x 32 rows, 4 x 16 KiB stages (two workgroups per CU)
   KERNEL_M32_CTX_R1S3 = 27,  // D = 128, 4 waves x 32 rows, 3 x 16 KiB stages (three workgroups per CU)
-  KERNEL_COUNT = 28,
+  KERNEL_M32_CTX_R2 = 28,    // D = 128, 4 waves x 64 rows, 4 x 16 KiB stages (two workgroups per CU)
+  KERNEL_M32_CTX_R2W8 = 29,  // D = 128, 8 waves x 64 rows, 4 x 32 KiB stages
+  KERNEL_COUNT = 30,
 };
 
 // Everything a kernel reads, by value.  Element strides as in pkv_args.

@@ -33,8 +33,20 @@ __device__ __forceinline__ void wait_loads() {
   asm volatile("" ::: "memory");
 }
 
+// One wave-instruction of the ring: lane l's 16 bytes at gptr land at
+// lds_wave_base + 16 l.  Issued through inline assembly on purpose: the
+// compiler treats a global_load_lds builtin as an LDS store of unknown address
+// and then waits for every outstanding one (vmcnt(0)) before any later LDS
+// read, which would drain the whole ring at each tile.  Here the kernels do
+// that bookkeeping themselves (wait_loads before the barrier that publishes a
+// stage).  M0 carries the LDS address; nothing else in these kernels uses M0.
 __device__ __forceinline__ void dma16(const void* gptr, unsigned char* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(gptr, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
+  const uint32_t lds = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)lds_wave_base);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gptr), "s"(lds)
+               : "memory", "m0");
 }
 
 // 8 e4m3 codes (two dwords) -> 8 bf16

@@ -93,7 +93,7 @@ def test_kernel_choice_by_shape():
     c = _args_for(_fake(q_lens=[20, 30], seq_lens=[40, 70], is_decode=False))
     c.q = c.k_pages = c.v_pages = c.out = 0x1000
     info = pkv.pkv_plan(c, True)
-    assert pkv.KERNEL_NAMES[info.kernel] == "dma_wide_bf16"
+    assert pkv.KERNEL_NAMES[info.kernel] == "m32_ctx_w8"
     # MLA shape
     m = _args_for(_fake(num_qo_heads=16, num_kv_heads=1, head_dim_qk=576, head_dim_v=512, page_size=64,
                         mla=True))
