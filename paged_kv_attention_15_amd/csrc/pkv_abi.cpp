@@ -186,14 +186,17 @@ bool kernel_supports(int32_t k, const pkv_args* a, bool is_context) {
     case pkv::KERNEL_DMA_WIDE_FP8: return d128 && fp8;
     case pkv::KERNEL_DMA_MLA_BF16: return mla && !fp8;
     case pkv::KERNEL_DMA_MLA_FP8: return mla && fp8;
+    // the 32x32 family loads each wave-instruction from one page: four rows
+    // per instruction for D = 128, a whole 32-key tile for the latent rows
     case pkv::KERNEL_M32_CTX_BF16:
     case pkv::KERNEL_M32_CTX_W8:
     case pkv::KERNEL_M32_CTX_R1:
     case pkv::KERNEL_M32_CTX_R1S3:
     case pkv::KERNEL_M32_CTX_R2:
     case pkv::KERNEL_M32_CTX_R2W8:
-      return d128 && !fp8;
-    case pkv::KERNEL_M32_MLA_BF16: return mla && !fp8;
+    case pkv::KERNEL_M32_CTX_PP:
+      return d128 && !fp8 && a->page_size >= 4;
+    case pkv::KERNEL_M32_MLA_BF16: return mla && !fp8 && a->page_size % 32 == 0;
   }
   return false;
 }
@@ -330,7 +333,8 @@ pkv_status make_plan(const pkv_args* a, bool is_context, int num_cus, pkv_plan_i
   if (kernel != pkv::KERNEL_GENERIC) {
     // the partition's page list sits in LDS after the KV stages: keep the total within 160 KiB
     const int64_t lds_room = (int64_t)(160 * 1024 - shp.lds_static) / 4 - 8;
-    const int64_t cap_pages = std::min<int64_t>(kMaxPagesPerSplit, lds_room);
+    int64_t cap_pages = std::min<int64_t>(kMaxPagesPerSplit, lds_room);
+    if (kernel >= pkv::KERNEL_M32_CTX_BF16) cap_pages = std::min<int64_t>(cap_pages, pkv::kM32MaxPages);
     if (cap_pages < 1) return fail(PKV_ERR_UNSUPPORTED, "no LDS left for the page list");
     if (pps > cap_pages) pps = cap_pages;
   }

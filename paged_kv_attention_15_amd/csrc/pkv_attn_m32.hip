@@ -35,17 +35,31 @@ __device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-template <int DQK_, int DV_, bool VSHARE_, int RB_, int NW_, int KB_, int NS_, int OCC_ = 1, bool PREF_ = true>
+template <int DQK_, int DV_, bool VSHARE_, int RB_, int NW_, int KB_, int NS_, int OCC_ = 1, bool PREF_ = true,
+          int DVS_ = 1, bool PP_ = false>
 struct M32Cfg {
+  // PP (ping-pong): waves w and w + NW/2 share a SIMD (measured on gfx950);
+  // the second half runs one phase behind the first, with a workgroup barrier
+  // between phases, so that on every SIMD one wave is in its MFMA phase while
+  // the other is in its LDS-read and softmax phase
+  static constexpr bool PP = PP_;
+  // DVS waves share each group of rows, each accumulating its own 1/DVS of the
+  // value columns (and each computing the whole S^T of those rows): for long
+  // value rows this trades duplicated QK^T work for a smaller O per wave
+  static constexpr int DVS = DVS_;
   static constexpr int DQK = DQK_, DV = DV_, RB = RB_, NW = NW_, KB = KB_, NS = NS_;
   static constexpr int OCC = OCC_;  // waves per SIMD the register budget is sized for
   // PREF: software-pipeline the blocks, holding the next block's K operands and
   // this block's V^T operands in registers; otherwise each block reads its
   // operands as it goes and other waves of the SIMD cover the latency
   static constexpr bool PREF = PREF_;
+  // read-ahead distance (in MFMA steps) of the K and V^T operand reads when not prefetching;
+  // shorter for long rows, whose Q and O already fill the register file
+  static constexpr int PDK = DQK > 256 ? 3 : 4;
+  static constexpr int PDV = DQK > 256 ? 3 : 4;
   static constexpr bool VSHARE = VSHARE_;
   static constexpr int NTHR = 64 * NW;
-  static constexpr int ROWS = NW * RB * 32;  // packed query rows per workgroup
+  static constexpr int ROWS = NW / DVS * RB * 32;  // packed query rows per workgroup
   static constexpr int T = KB * 32;          // keys per ring stage
   static constexpr int KROWB = DQK * 2;
   static constexpr int VROWB = VSHARE ? KROWB : DV * 2;
@@ -59,16 +73,21 @@ struct M32Cfg {
   static constexpr int NI = (KCH + VCH) / 64;  // wave-instructions per stage
   static constexpr int KPW = (NI + NW - 1) / NW;
   static constexpr int NKS = DQK / 16;  // 16-wide k steps of S^T
-  static constexpr int NDB = DV / 32;   // 32-wide value blocks of O^T
+  static constexpr int NDB = DV / 32 / DVS;  // 32-wide value blocks of O^T per wave
   static constexpr int LDS = NS * STAGE;
   // recompute the loader's per-lane geometry every stage instead of keeping it
   // live: long rows, or more than one wave per SIMD (registers are the limit)
   static constexpr bool LEAN = DQK > 256 || OCC > 1;
+  static constexpr bool ROW16 = NCK == 16 && (VSHARE || NCV == 16);  // closed-form loader geometry
   static_assert(KCH % 64 == 0 && VCH % 64 == 0, "wave-instructions must not straddle K and V");
   static_assert(KPW * (NS - 1) < 64, "vmcnt holds at most 63 outstanding loads");
   static_assert(DQK % 16 == 0 && DV % 32 == 0 && NCK % 4 == 0 && NCV % 4 == 0, "tiling");
   static_assert(NS >= 2 && NS <= 6, "ring depth");
+  static_assert(!PREF || KPW % KB == 0, "ring refill split over the blocks of a tile");
   static_assert(!VSHARE || DV <= DQK, "shared V rows");
+  // a wave's value slice starts on a 16-chunk swizzle group: its reads are the
+  // first slice's shifted by a whole number of groups
+  static_assert(NW % DVS == 0 && (DVS == 1 || (NDB % 4 == 0 && DV * 2 <= (NCV & ~15) * 16)), "value slices");
 };
 
 // Swizzle key of LDS row r (K and V rows alike): 16-byte chunk c of the row is
@@ -111,6 +130,10 @@ __device__ __forceinline__ void sched_reads_ahead() {
   static_for<0, (PD < STEPS ? PD : STEPS)>([] { __builtin_amdgcn_sched_group_barrier(0x008, M, 0); });
 }
 
+// Registers per wave holding the page list (64 pages each); the planner caps a
+// partition of these kernels at 64 * kPageRegs pages
+constexpr int kPageRegs = kM32MaxPages / 64;
+
 // Largest rise of a row's max (log2 units) absorbed without rescaling O
 constexpr float kLazyMax = 8.f;
 
@@ -127,6 +150,8 @@ __device__ __forceinline__ void m32_block(const KParams& p, unsigned char* smem,
   const int h = lane >> 5;   // k half of the operands, row quad of the results
   const int c32 = lane & 31;  // query row inside a 32-row block
   const int G = p.group;
+  const int wr = wave / C::DVS;         // row group of this wave
+  const int dvb0 = (wave % C::DVS) * C::NDB;  // first 32-wide value block of this wave
 
   __syncthreads();  // LDS of a previous piece is free again (no loads are in flight here)
 
@@ -184,7 +209,7 @@ __device__ __forceinline__ void m32_block(const KParams& p, unsigned char* smem,
   bf16x8 qB[C::RB][C::NKS];
 #pragma unroll
   for (int rb = 0; rb < C::RB; ++rb) {
-    const int R = row0 + (wave * C::RB + rb) * 32 + c32;
+    const int R = row0 + (wr * C::RB + rb) * 32 + c32;
     row_ok[rb] = R < row_space;
     const int i = row_ok[rb] ? R / G : 0;
     row_t[rb] = t0 + i;
@@ -208,8 +233,14 @@ __device__ __forceinline__ void m32_block(const KParams& p, unsigned char* smem,
   c_lo = -wave_max_i(-c_lo);
   c_hi = wave_max_i(c_hi);
 
+  // Row sums come from the matrix core: an all-ones A operand against the P^T
+  // operand of the PV product sums the bf16 weights actually used for O (every
+  // element of Lsum[rb] in a lane holds the sum of that lane's query row).
   float m_run[C::RB], l_run[C::RB];
   f32x16 O[C::RB][C::NDB];
+  f32x16 Lsum[C::RB];
+  const bf16x8 ones = {(__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f,
+                       (__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f};
 #pragma unroll
   for (int rb = 0; rb < C::RB; ++rb) {
     m_run[rb] = -INFINITY;
@@ -218,9 +249,26 @@ __device__ __forceinline__ void m32_block(const KParams& p, unsigned char* smem,
     for (int d = 0; d < C::NDB; ++d)
 #pragma unroll
       for (int e = 0; e < 16; ++e) O[rb][d][e] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) Lsum[rb][e] = 0.f;
   }
 
   __syncthreads();  // page list visible
+
+  // The validated page list also sits in registers, lane l of pl[k] holding
+  // page 64k + l (the planner keeps a partition within 64 * kPageRegs pages): a
+  // wave-instruction's page is then one v_readlane, with no memory access whose
+  // wait counter would also cover the ring's loads in flight.
+  int pl[kPageRegs];
+#pragma unroll
+  for (int k = 0; k < kPageRegs; ++k) pl[k] = 64 * k + lane < n_pg ? s_pages[64 * k + lane] : 0;
+  auto page_of = [&](int idx) -> uint32_t {
+    int v = __builtin_amdgcn_readlane(pl[0], idx & 63);
+#pragma unroll
+    for (int k = 1; k < kPageRegs; ++k)
+      if ((idx >> 6) == k) v = __builtin_amdgcn_readlane(pl[k], idx & 63);
+    return (uint32_t)v;
+  };
 
   // ---- loader: wave-instruction q of this wave fills chunks I*64 .. I*64+63 of the
   // stage (I = wave*KPW + q); lane l fetches the global chunk whose swizzled LDS slot
@@ -249,15 +297,34 @@ __device__ __forceinline__ void m32_block(const KParams& p, unsigned char* smem,
   };
   int g_row[C::LEAN ? 1 : C::KPW];
   uint32_t g_chunk[C::LEAN ? 1 : C::KPW];
-  if constexpr (!C::LEAN) geometry(lane, g_row, g_chunk);
-  auto issue = [&](int tile, int stage) {
+  if constexpr (!C::LEAN && !C::ROW16) geometry(lane, g_row, g_chunk);
+  // 16-chunk rows (D = 128, bf16): wave-instruction I' of a tile (counted
+  // within the K or the V part) fills rows 4I' .. 4I'+3, lane l taking row
+  // 4I' + l/16 and physical chunk l%16; the swizzle key of that row is
+  // 4(l/16) + 2((I'/2)%2), so the logical chunk is a lane constant XOR a
+  // uniform bit and no per-lane geometry needs to be stored or recomputed.
+  const int g16_row = lane >> 4;
+  const uint32_t g16_chunk = (uint32_t)((lane & 15) ^ (4 * (lane >> 4)));
+  // Every wave-instruction covers consecutive rows of one page (the planner
+  // guarantees it: rows per instruction divide the page, or the whole tile sits
+  // in one page), so its page base is wave-uniform: looked up once, added on
+  // the scalar unit, and each lane only supplies its 32-bit in-page offset.
+  auto issue = [&](int tile, int stage, int q_lo = 0, int q_hi = C::KPW) {
     const int tok0 = kv_lo + tile * C::T;
     unsigned char* st = smem + stage * C::STAGE;
     int q_row_l[C::KPW];
     uint32_t q_chunk_l[C::KPW];
     const int* q_row = q_row_l;
     const uint32_t* q_chunk = q_chunk_l;
-    if constexpr (C::LEAN) {
+    if constexpr (C::ROW16) {
+#pragma unroll
+      for (int q = 0; q < C::KPW; ++q) {
+        const int I = min(wave * C::KPW + q, C::NI - 1);
+        const int Ip = I * 64 < C::KCH ? I : I - C::KCH / 64;
+        q_row_l[q] = 4 * Ip + g16_row;
+        q_chunk_l[q] = (g16_chunk ^ (uint32_t)(2 * ((Ip >> 1) & 1))) * 16;
+      }
+    } else if constexpr (C::LEAN) {
       int ln = lane;
       asm volatile("" : "+v"(ln));
       geometry(ln, q_row_l, q_chunk_l);
@@ -265,24 +332,25 @@ __device__ __forceinline__ void m32_block(const KParams& p, unsigned char* smem,
       q_row = g_row;
       q_chunk = g_chunk;
     }
-    int pg[C::KPW];
+    uint32_t pgv[C::KPW];
 #pragma unroll
     for (int q = 0; q < C::KPW; ++q) {
-      const int tok = min(tok0 + q_row[q], kv_hi - 1);
-      pg[q] = s_pages[(tok >> p.log2_page) - pg_lo];
+      if (q < q_lo || q >= q_hi) continue;
+      const int I = min(wave * C::KPW + q, C::NI - 1);
+      const int r0 = I * 64 < C::KCH ? (I * 64) / C::NCK : (I * 64 - C::KCH) / C::NCV;
+      const int tokf = __builtin_amdgcn_readfirstlane(min(tok0 + r0, kv_hi - 1));
+      pgv[q] = page_of((tokf >> p.log2_page) - pg_lo);
     }
 #pragma unroll
     for (int q = 0; q < C::KPW; ++q) {
+      if (q < q_lo || q >= q_hi) continue;
       const int I = min(wave * C::KPW + q, C::NI - 1);
-      const int tok = min(tok0 + q_row[q], kv_hi - 1);
       const bool is_k = I * 64 < C::KCH;
-      const uint64_t base = is_k ? k_addr : v_addr;
-      const uint64_t pgb = is_k ? k_pg_b : v_pg_b;
-      const uint32_t inpage = (uint32_t)(tok & pmask) * (is_k ? k_tok_b : v_tok_b) + (is_k ? k_head_b : v_head_b) +
-                              q_chunk[q];
-      const unsigned char* src =
-          (const unsigned char*)(base + ((uint64_t)(uint32_t)pg[q] * (uint32_t)pgb + inpage));
-      dma16(src, st + I * 1024);
+      const uint32_t pg = pgv[q];
+      const uint64_t sbase = (is_k ? k_addr + k_head_b : v_addr + v_head_b) + (uint64_t)pg * (is_k ? k_pg_b : v_pg_b);
+      const int tok = min(tok0 + q_row[q], kv_hi - 1);
+      const uint32_t voff = (uint32_t)(tok & pmask) * (is_k ? k_tok_b : v_tok_b) + q_chunk[q];
+      dma16_saddr(sbase, voff, st + I * 1024);
     }
   };
 
@@ -298,7 +366,7 @@ __device__ __forceinline__ void m32_block(const KParams& p, unsigned char* smem,
   const int vrow = 8 * (vq >> 1) + (vj >> 2);
   const int vfk = m32_key(vrow);
   const int vc_lane = 2 * (vq & 1) + ((vj & 3) >> 1);
-  const int vl_row = vrow * C::VROWB + 8 * (vj & 1);
+  const int vl_row = vrow * C::VROWB + 8 * (vj & 1) + 64 * dvb0;
 
   // ---- the pieces of one 32-key block
   auto k_operands = [&](int j, bf16x8 (&ka)[C::NKS]) {
@@ -373,26 +441,18 @@ __device__ __forceinline__ void m32_block(const KParams& p, unsigned char* smem,
       const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
       if (__builtin_amdgcn_ballot_w64(move) != 0) {
         const float alpha = move ? fast_exp2(m_run[rb] - m_use) : 1.f;
-        l_run[rb] *= alpha;
+        Lsum[rb] *= alpha;
 #pragma unroll
         for (int d = 0; d < C::NDB; ++d) O[rb][d] *= alpha;
       }
       m_run[rb] = m_new;
-      float ps = 0.f;
       if (full) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          w[e] = fast_exp2(fmaf(acc[rb][e], sc2, -m_use));
-          ps += w[e];
-        }
+        for (int e = 0; e < 16; ++e) w[e] = fast_exp2(fmaf(acc[rb][e], sc2, -m_use));
       } else {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          w[e] = fast_exp2(w[e] - m_use);
-          ps += w[e];
-        }
+        for (int e = 0; e < 16; ++e) w[e] = fast_exp2(w[e] - m_use);
       }
-      l_run[rb] += ps;
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
         u32x4 wv{pack_bf16x2(w[8 * st + 0], w[8 * st + 1]), pack_bf16x2(w[8 * st + 2], w[8 * st + 3]),
@@ -401,7 +461,14 @@ __device__ __forceinline__ void m32_block(const KParams& p, unsigned char* smem,
       }
     }
   };
+  auto row_sums = [&](const bf16x8 (&pb)[C::RB][2]) {
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int rb = 0; rb < C::RB; ++rb) Lsum[rb] = mfma32x32x16(ones, pb[rb][st], Lsum[rb]);
+  };
   auto pv_product = [&](const bf16x8 (&va)[C::NDB][2], const bf16x8 (&pb)[C::RB][2]) {
+    row_sums(pb);
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
@@ -409,10 +476,57 @@ __device__ __forceinline__ void m32_block(const KParams& p, unsigned char* smem,
 #pragma unroll
         for (int rb = 0; rb < C::RB; ++rb) O[rb][db] = mfma32x32x16(va[db][st], pb[rb][st], O[rb][db]);
   };
+  // Products with their LDS operand reads interleaved: a ring of PD operands
+  // in registers, each read issued PD MFMA steps before the MFMA that uses it
+  // (registers stay at PD operands instead of a whole block's worth).
+  auto s_product_ring = [&](int j, f32x16 (&acc)[C::RB]) {
+    const unsigned char* kblk = smem + ((j / C::KB) % C::NS) * C::STAGE + (j % C::KB) * 32 * C::KROWB + kl_row;
+    auto rd = [&](int ks) { return *(const bf16x8*)(kblk + chunk_phys<C::NCK>(2 * ks, h, kfk) * 16); };
+    constexpr int PD = C::PDK < C::NKS ? C::PDK : C::NKS;
+    bf16x8 ring[PD];
+#pragma unroll
+    for (int q = 0; q < PD; ++q) ring[q] = rd(q);
+#pragma unroll
+    for (int rb = 0; rb < C::RB; ++rb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[rb][e] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < C::NKS; ++ks) {
+      const bf16x8 a = ring[ks % PD];
+      if (ks + PD < C::NKS) ring[ks % PD] = rd(ks + PD);
+#pragma unroll
+      for (int rb = 0; rb < C::RB; ++rb) acc[rb] = mfma32x32x16(a, qB[rb][ks], acc[rb]);
+    }
+  };
+  auto pv_product_ring = [&](int j, const bf16x8 (&pb)[C::RB][2]) {
+    const unsigned char* vst = smem + ((j / C::KB) % C::NS) * C::STAGE + (C::VSHARE ? 0 : C::KTILE);
+    const unsigned char* vblk = vst + (j % C::KB) * 32 * C::VROWB + vl_row;
+    auto rd = [&](int i) {  // i = 2 db + st
+      const int db = i >> 1, st = i & 1;
+      const unsigned char* src = vblk + 16 * st * C::VROWB + chunk_phys<C::NCV>(4 * db, vc_lane, vfk) * 16;
+      const s16x4 lo = lds_read_tr16(src);
+      const s16x4 hi = lds_read_tr16(src + 4 * C::VROWB);
+      typedef short s16x8 __attribute__((ext_vector_type(8)));
+      return __builtin_bit_cast(bf16x8, s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+    };
+    constexpr int N = 2 * C::NDB;
+    constexpr int PD = C::PDV < N ? C::PDV : N;
+    row_sums(pb);
+    bf16x8 ring[PD];
+#pragma unroll
+    for (int q = 0; q < PD; ++q) ring[q] = rd(q);
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const bf16x8 a = ring[i % PD];
+      if (i + PD < N) ring[i % PD] = rd(i + PD);
+#pragma unroll
+      for (int rb = 0; rb < C::RB; ++rb) O[rb][i >> 1] = mfma32x32x16(a, pb[rb][i & 1], O[rb][i >> 1]);
+    }
+  };
   // Start of ring tile t: this wave's loads of t are complete once at most
   // (tiles issued after t) * KPW remain; the barrier then publishes every wave's
   // part and frees the stage of tile t-1, which the next issue refills.
-  auto tile_start = [&](int t) {
+  auto tile_start = [&](int t, bool issue_now = true) {
     const int after = min(C::NS - 2, n_tiles - 1 - t);
     if constexpr (C::NS >= 5) {
       if (after >= 3) wait_loads<3 * C::KPW>();
@@ -430,7 +544,7 @@ __device__ __forceinline__ void m32_block(const KParams& p, unsigned char* smem,
       wait_loads<0>();
     }
     ring_barrier();
-    if (t + C::NS - 1 < n_tiles) issue(t + C::NS - 1, (t + C::NS - 1) % C::NS);
+    if (issue_now && t + C::NS - 1 < n_tiles) issue(t + C::NS - 1, (t + C::NS - 1) % C::NS);
   };
 
   // prologue: the first NS-1 tiles in flight
@@ -457,7 +571,7 @@ __device__ __forceinline__ void m32_block(const KParams& p, unsigned char* smem,
     const bool act1 = j + 1 < nblk && active(j + 1);
     if (j + 1 < nblk && (j + 1) % C::KB == 0) {
       if (act) v_operands(j, va);
-      tile_start((j + 1) / C::KB);
+      tile_start((j + 1) / C::KB, false);
       if (act1) k_operands(j + 1, ka);
     } else {
       if (act1) k_operands(j + 1, ka);
@@ -467,12 +581,84 @@ __device__ __forceinline__ void m32_block(const KParams& p, unsigned char* smem,
     bf16x8 pb[C::RB][2];
     if (act) softmax(j, cur, pb);
     __builtin_amdgcn_sched_barrier(0);
+    // part (j+1) % KB of the ring refill that follows the barrier of tile (j+1) / KB:
+    // the next tile's loads go out a slice per block instead of all at once
+    // after the barrier, when every wave would queue them at the same moment
+    {
+      const int u = (j + 1) / C::KB + C::NS - 1;
+      const int part = (j + 1) % C::KB;
+      if (u < n_tiles) issue(u, u % C::NS, part * C::KPW / C::KB, (part + 1) * C::KPW / C::KB);
+    }
     if (act1) s_product(ka, nxt);
     if (act) pv_product(va, pb);
   };
-  if constexpr (C::PREF) {
+  if constexpr (C::PP) {
+    // Slots of the ping-pong.  Phase 2j of a wave (its softmax phase) runs the
+    // softmax of block j on the VALU; phase 2j+1 (its matrix phase) runs the S^T
+    // product of block j+1 and the PV product of block j, their LDS operands
+    // read a few MFMA steps ahead.  The first half of the waves runs phase s in
+    // slot s, the second half in slot s+1; a barrier ends every slot.
+    // Ring: tile t is read from phase 2(t KB - 1) + 1 (the K reads of its first
+    // block; the prologue for t = 0) to phase 2(t KB + KB - 1) + 1 (the V^T reads
+    // of its last block), i.e. up to slot 2(t+1)KB for the lagging half.  So
+    // tile t+NS refills its stage after the barrier ending that slot, and tile t
+    // is waited for before the barrier ending slot 2 t KB - 3.  (The refill of
+    // tile u = t+NS happens after the barrier ending slot 2(t+1)KB.)
+    static_assert(C::NW % 2 == 0 && C::DVS == 1, "ping-pong halves");
+    const int lag = wave >= C::NW / 2 ? 1 : 0;
+    int issued = 0;
+#pragma unroll
+    for (int t = 0; t < C::NS; ++t)
+      if (t < n_tiles) {
+        issue(t, t);
+        ++issued;
+      }
+    auto wait_tile = [&](int t) {
+      const int after = issued - 1 - t;
+      if (after >= 5) wait_loads<5 * C::KPW < 63 ? 5 * C::KPW : 63>();
+      else if (after == 4) wait_loads<4 * C::KPW < 63 ? 4 * C::KPW : 63>();
+      else if (after == 3) wait_loads<3 * C::KPW < 63 ? 3 * C::KPW : 63>();
+      else if (after == 2) wait_loads<2 * C::KPW>();
+      else if (after == 1) wait_loads<C::KPW>();
+      else wait_loads<0>();
+    };
     if (nblk > 0) {
-      tile_start(0);
+      wait_tile(0);
+      ring_barrier();
+      if (active(0)) s_product_ring(0, accA);
+      bf16x8 pb[C::RB][2];
+      const int nslot = 2 * nblk + 1;
+      for (int slot = 0; slot < nslot; ++slot) {
+        const int ph = slot - lag;
+        if (ph >= 0 && ph < 2 * nblk) {
+          const int j = ph >> 1;
+          const bool act = active(j);
+          const bool act1 = j + 1 < nblk && active(j + 1);
+          if ((ph & 1) == 0) {
+            if (act) softmax(j, accA, pb);
+          } else {
+            if (act1) s_product_ring(j + 1, accA);  // block j's scores are consumed: reuse the registers
+            if (act) pv_product_ring(j, pb);
+          }
+        }
+        if ((slot + 3) % (2 * C::KB) == 0) {
+          const int t = (slot + 3) / (2 * C::KB);
+          if (t < n_tiles) wait_tile(t);
+        }
+        ring_barrier();
+        if (slot % (2 * C::KB) == 0 && slot > 0) {
+          const int u = slot / (2 * C::KB) - 1 + C::NS;
+          if (u < n_tiles) {
+            issue(u, u % C::NS);
+            ++issued;
+          }
+        }
+      }
+    }
+  } else if constexpr (C::PREF) {
+    if (nblk > 0) {
+      tile_start(0, false);
+      if (C::NS - 1 < n_tiles) issue(C::NS - 1, C::NS - 1, 0, C::KPW / C::KB);
       if (active(0)) {
         bf16x8 ka[C::NKS];
         k_operands(0, ka);
@@ -487,27 +673,17 @@ __device__ __forceinline__ void m32_block(const KParams& p, unsigned char* smem,
     for (int j = 0; j < nblk; ++j) {
       if (j % C::KB == 0) tile_start(j / C::KB);
       if (active(j)) {
-        {
-          bf16x8 ka[C::NKS];
-          k_operands(j, ka);
-          s_product(ka, accA);
-          sched_reads_ahead<4, C::NKS, 1, C::RB>();
-        }
+        s_product_ring(j, accA);
         bf16x8 pb[C::RB][2];
         softmax(j, accA, pb);
-        {
-          bf16x8 va[C::NDB][2];
-          v_operands(j, va);
-          pv_product(va, pb);
-          sched_reads_ahead<3, 2 * C::NDB, 2, C::RB>();
-        }
+        pv_product_ring(j, pb);
       }
     }
   }
 
-  // ---- full row sums (each lane half summed its own 16 keys of every block)
+  // ---- full row sums
 #pragma unroll
-  for (int rb = 0; rb < C::RB; ++rb) l_run[rb] = half_swap_sum(l_run[rb]);
+  for (int rb = 0; rb < C::RB; ++rb) l_run[rb] = Lsum[rb][0];
 
   // ---- epilogue: element e of O[rb][db] is value 32db + 8(e/4) + 4h + e%4 of row c32
   const bool split_mode = p.ws_o != nullptr;
@@ -520,9 +696,9 @@ __device__ __forceinline__ void m32_block(const KParams& p, unsigned char* smem,
     const int64_t row_g = (int64_t)row_t[rb] * p.num_qo_heads + row_h[rb];
     if (split_mode) {
       const int64_t prow = (int64_t)slot * p.rows_total + row_g;
-      if (h == 0) p.ws_lse[prow] = lse;
+      if (h == 0 && dvb0 == 0) p.ws_lse[prow] = lse;
       if (!empty) {
-        float* dst = p.ws_o + prow * C::DV + 4 * h;
+        float* dst = p.ws_o + prow * C::DV + 4 * h + 32 * dvb0;
 #pragma unroll
         for (int d = 0; d < C::NDB; ++d)
 #pragma unroll
@@ -531,9 +707,9 @@ __device__ __forceinline__ void m32_block(const KParams& p, unsigned char* smem,
                 f32x4{O[rb][d][4 * q], O[rb][d][4 * q + 1], O[rb][d][4 * q + 2], O[rb][d][4 * q + 3]} * inv;
       }
     } else {
-      if (p.lse_out && h == 0) p.lse_out[row_g] = lse;
+      if (p.lse_out && h == 0 && dvb0 == 0) p.lse_out[row_g] = lse;
       if (p.o_dtype == PKV_DTYPE_BF16) {
-        __bf16* dst = (__bf16*)p.out + row_t[rb] * p.o_st + row_h[rb] * p.o_sh + 4 * h;
+        __bf16* dst = (__bf16*)p.out + row_t[rb] * p.o_st + row_h[rb] * p.o_sh + 4 * h + 32 * dvb0;
 #pragma unroll
         for (int d = 0; d < C::NDB; ++d)
 #pragma unroll
@@ -543,7 +719,7 @@ __device__ __forceinline__ void m32_block(const KParams& p, unsigned char* smem,
             *(u32x2*)(dst + 32 * d + 8 * q) = w;
           }
       } else {
-        float* dst = (float*)p.out + row_t[rb] * p.o_st + row_h[rb] * p.o_sh + 4 * h;
+        float* dst = (float*)p.out + row_t[rb] * p.o_st + row_h[rb] * p.o_sh + 4 * h + 32 * dvb0;
 #pragma unroll
         for (int d = 0; d < C::NDB; ++d)
 #pragma unroll
@@ -591,12 +767,13 @@ __global__ __launch_bounds__(C::NTHR, C::OCC) void attn_m32_kernel(const KParams
 // ---------------------------------------------------------------- instances
 //                          DQK  DV   VSH    RB NW KB NS OCC
 using M32Ctx = M32Cfg<128, 128, false, 2, 4, 2, 4, 1, false>;  // 256 rows, 64-key stages of 32 KiB
-using M32Mla = M32Cfg<576, 512, true, 1, 4, 1, 4, 1, false>;  // 128 heads, 32-key stages of 36 KiB
-using M32CtxW8 = M32Cfg<128, 128, false, 1, 8, 2, 4, 2>;  // 256 rows on 8 waves (two per SIMD)
+using M32Mla = M32Cfg<576, 512, true, 1, 4, 1, 4, 1, false, 2>;  // 64 heads, two value halves, 36 KiB stages
+using M32CtxW8 = M32Cfg<128, 128, false, 1, 8, 2, 4, 2, false>;  // 256 rows on 8 waves (two per SIMD)
 using M32CtxR1 = M32Cfg<128, 128, false, 1, 4, 1, 4, 2, false>;  // 128 rows, 16 KiB stages: two workgroups per CU
 using M32CtxR1S3 = M32Cfg<128, 128, false, 1, 4, 1, 3, 3>;  // 128 rows, 48 KiB: three workgroups per CU
 using M32CtxR2 = M32Cfg<128, 128, false, 2, 4, 1, 4, 2, false>;   // 256 rows, 64 rows per wave, 64 KiB
 using M32CtxR2W8 = M32Cfg<128, 128, false, 2, 8, 2, 4, 2, false>;  // 512 rows, 64 rows per wave, 128 KiB
+using M32CtxPP = M32Cfg<128, 128, false, 1, 8, 2, 4, 2, false, 1, true>;  // 256 rows, ping-pong halves
 
 template <class C>
 static void fill_m32_shape(MfmaShape* s) {
@@ -615,6 +792,7 @@ bool m32_shape(int32_t kernel, MfmaShape* s) {
     case KERNEL_M32_CTX_R1S3: fill_m32_shape<M32CtxR1S3>(s); return true;
     case KERNEL_M32_CTX_R2: fill_m32_shape<M32CtxR2>(s); return true;
     case KERNEL_M32_CTX_R2W8: fill_m32_shape<M32CtxR2W8>(s); return true;
+    case KERNEL_M32_CTX_PP: fill_m32_shape<M32CtxPP>(s); return true;
     default: return false;
   }
 }
@@ -643,6 +821,7 @@ hipError_t launch_m32(int32_t kernel, const KParams& p, hipStream_t s) {
     case KERNEL_M32_CTX_R1S3: return launch_m32_cfg<M32CtxR1S3>(p, s);
     case KERNEL_M32_CTX_R2: return launch_m32_cfg<M32CtxR2>(p, s);
     case KERNEL_M32_CTX_R2W8: return launch_m32_cfg<M32CtxR2W8>(p, s);
+    case KERNEL_M32_CTX_PP: return launch_m32_cfg<M32CtxPP>(p, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -43,7 +43,8 @@ enum KernelId : int32_t {
   KERNEL_M32_CTX_R1S3 = 27,  // D = 128, 4 waves x 32 rows, 3 x 16 KiB stages (three workgroups per CU)
   KERNEL_M32_CTX_R2 = 28,    // D = 128, 4 waves x 64 rows, 4 x 16 KiB stages (two workgroups per CU)
   KERNEL_M32_CTX_R2W8 = 29,  // D = 128, 8 waves x 64 rows, 4 x 32 KiB stages
-  KERNEL_COUNT = 30,
+  KERNEL_M32_CTX_PP = 30,    // D = 128, 8 waves x 32 rows in two ping-pong halves
+  KERNEL_COUNT = 31,
 };
 
 // Everything a kernel reads, by value.  Element strides as in pkv_args.
@@ -118,6 +119,8 @@ bool mfma_shape(int32_t kernel, MfmaShape* out);
 bool dma_shape(int32_t kernel, MfmaShape* out);
 hipError_t launch_dma(int32_t kernel, const KParams& p, hipStream_t s);
 bool m32_shape(int32_t kernel, MfmaShape* out);
+// the 32x32 family keeps a partition's page list in registers: at most this many pages
+constexpr int kM32MaxPages = 128;
 hipError_t launch_m32(int32_t kernel, const KParams& p, hipStream_t s);
 
 }  // namespace pkv

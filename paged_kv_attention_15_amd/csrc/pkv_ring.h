@@ -49,6 +49,23 @@ __device__ __forceinline__ void dma16(const void* gptr, unsigned char* lds_wave_
                : "memory", "m0");
 }
 
+// Same with a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane offset
+// (global SADDR form): the 64-bit address arithmetic happens once per
+// wave-instruction on the scalar unit instead of in every lane.
+__device__ __forceinline__ void dma16_saddr(uint64_t base, uint32_t voff, unsigned char* lds_wave_base) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)lds_wave_base);
+  // the base must live in SGPRs for the SADDR form: make its uniformity explicit
+  // (readfirstlane returns int: go through uint32_t so the low word is not sign-extended)
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)base);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(base >> 32));
+  const uint64_t sbase = ((uint64_t)hi << 32) | (uint64_t)lo;
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(lds)
+               : "memory", "m0");
+}
+
 // 8 e4m3 codes (two dwords) -> 8 bf16
 __device__ __forceinline__ bf16x8 e4m3x8_to_bf16x8(u32x2 w) {
   bf16x2 a = e4m3x2_to_bf16x2<false>(w[0]);

@@ -121,6 +121,16 @@ def test_mla_fp8_latent_small():
 
 
 @pytest.mark.parametrize("q_len", [1, 2])
+def test_mla_full_size_m32(q_len):
+    prob = W.mla_b512_kv4096(q_len=q_len)
+    say(f"case {prob.name} kernel=m32_mla_bf16")
+    dp = pkv.upload(prob, "cuda", kernel="m32_mla_bf16")
+    dp.run()
+    torch.cuda.synchronize()
+    compare(prob, dp, pairs=sample_pairs(prob, 256), label="m32_mla_bf16")
+
+
+@pytest.mark.parametrize("q_len", [1, 2])
 def test_mla_full_size(q_len):
     prob = W.mla_b512_kv4096(q_len=q_len)
     say(f"case {prob.name} (sampled)")
@@ -302,7 +312,8 @@ def test_gqa_kernel_families_match_oracle(kernel, kv, splits):
 @pytest.mark.parametrize("kernel,splits", [("dma_wide_bf16", None), ("wide_bf16", None), ("m32_ctx_bf16", None),
                                            ("m32_ctx_bf16", 3), ("m32_ctx_w8", None), ("m32_ctx_r1", None),
                                            ("m32_ctx_r1s3", None), ("m32_ctx_r1", 2), ("m32_ctx_r2", None),
-                                           ("m32_ctx_r2w8", None), ("m32_ctx_w8", 2)])
+                                           ("m32_ctx_r2w8", None), ("m32_ctx_w8", 2), ("m32_ctx_pp", None),
+                                           ("m32_ctx_pp", 3)])
 def test_context_kernel_families_match_oracle(kernel, splits):
     prob = W.make_problem(name="ctx-fam", seed=9, batch=3, seq_lens=[70, 5, 333], q_lens=[64, 5, 130],
                           num_qo_heads=16, num_kv_heads=2, head_dim_qk=128, head_dim_v=128, page_size=16,
@@ -314,13 +325,14 @@ def test_context_kernel_families_match_oracle(kernel, splits):
     compare(prob, dp, label=f"{kernel}/{splits}")
 
 
-def test_context_full_size_m32():
+@pytest.mark.parametrize("kernel", ["m32_ctx_bf16", "m32_ctx_pp"])
+def test_context_full_size_m32(kernel):
     prob = W.context_b4_q511_kv2047()
-    say(f"case {prob.name} kernel=m32_ctx_bf16")
-    dp = pkv.upload(prob, "cuda", kernel="m32_ctx_bf16")
+    say(f"case {prob.name} kernel={kernel}")
+    dp = pkv.upload(prob, "cuda", kernel=kernel)
     dp.run()
     torch.cuda.synchronize()
-    compare(prob, dp, pairs=sample_pairs(prob, 512), label="m32_ctx_bf16")
+    compare(prob, dp, pairs=sample_pairs(prob, 512), label=kernel)
 
 
 def test_context_fp8_kv_families_match_oracle():
