@@ -177,10 +177,14 @@ bool kernel_supports(int32_t k, const pkv_args* a, bool is_context) {
     case pkv::KERNEL_DMA_GQA_BF16:
     case pkv::KERNEL_DMA_GQA_BF16_W4:
     case pkv::KERNEL_DMA_GQA_BF16_S2:
+    case pkv::KERNEL_DMA_GQA_BF16_N2:
       return d128 && !fp8 && !is_context && (int64_t)a->q_len * G <= 16;
     case pkv::KERNEL_DMA_GQA_FP8:
     case pkv::KERNEL_DMA_GQA_FP8_W8:
     case pkv::KERNEL_DMA_GQA_FP8_S2:
+    case pkv::KERNEL_DMA_GQA_FP8_N2:
+    case pkv::KERNEL_DMA_GQA_FP8_N1:
+    case pkv::KERNEL_DMA_GQA_FP8_N2S3:
       return d128 && fp8 && !is_context && (int64_t)a->q_len * G <= 16;
     case pkv::KERNEL_DMA_WIDE_BF16: return d128 && !fp8;
     case pkv::KERNEL_DMA_WIDE_FP8: return d128 && fp8;
@@ -216,6 +220,10 @@ bool is_gqa_family(int32_t k) {
     case pkv::KERNEL_DMA_GQA_FP8_S2:
     case pkv::KERNEL_DMA_GQA_BF16_W4:
     case pkv::KERNEL_DMA_GQA_BF16_S2:
+    case pkv::KERNEL_DMA_GQA_FP8_N2:
+    case pkv::KERNEL_DMA_GQA_BF16_N2:
+    case pkv::KERNEL_DMA_GQA_FP8_N1:
+    case pkv::KERNEL_DMA_GQA_FP8_N2S3:
       return true;
   }
   return false;
@@ -231,11 +239,11 @@ int32_t choose_kernel(const pkv_args* a, bool is_context) {
   const int G = a->num_qo_heads / a->num_kv_heads;
   // Measured on MI355X (bf16 GQA decode B32/L4096, e4m3 ragged decode B16, MLA
   // B512/L4096, causal context B4 q511/L2047): register-staged tiles win for
-  // bf16 decode, the direct-to-LDS ring for e4m3 decode and MLA, the 32x32 MFMA
-  // family with two waves per SIMD for bf16 context.
+  // bf16 decode, the direct-to-LDS ring for e4m3 decode (two-wave groups, four
+  // per CU) and MLA, the 32x32 MFMA family with two waves per SIMD for bf16 context.
   if (a->head_dim_qk == 128 && a->head_dim_v == 128 && !a->v_shares_k) {
     const int64_t rows = is_context ? (int64_t)a->max_q_len * G : (int64_t)a->q_len * G;
-    if (!is_context && rows <= 16) return fp8 ? pkv::KERNEL_DMA_GQA_FP8_S2 : pkv::KERNEL_GQA_BF16;
+    if (!is_context && rows <= 16) return fp8 ? pkv::KERNEL_DMA_GQA_FP8_N2 : pkv::KERNEL_GQA_BF16;
     if (is_context && !fp8) return pkv::KERNEL_M32_CTX_W8;
     return fp8 ? pkv::KERNEL_DMA_WIDE_FP8 : pkv::KERNEL_DMA_WIDE_BF16;
   }
@@ -290,7 +298,7 @@ pkv_status make_plan(const pkv_args* a, bool is_context, int num_cus, pkv_plan_i
       // resident workgroups per CU: LDS-limited, and at most 8 waves per CU
       // (two per SIMD: these kernels use up to 256 VGPRs)
       const int64_t per_cu_lds = std::max<int64_t>(1, (160 * 1024) / lds);
-      const int64_t per_cu_waves = std::max<int64_t>(1, 8 / std::max(1, threads / 64));
+      const int64_t per_cu_waves = std::max<int64_t>(1, shp.waves_per_cu / std::max(1, threads / 64));
       const int64_t W = (int64_t)num_cus * std::min(per_cu_lds, per_cu_waves);
       const int64_t U = (int64_t)a->batch * a->num_kv_heads;
       const int64_t slot_rows = (int64_t)a->q_len * G;
@@ -334,7 +342,8 @@ pkv_status make_plan(const pkv_args* a, bool is_context, int num_cus, pkv_plan_i
     // the partition's page list sits in LDS after the KV stages: keep the total within 160 KiB
     const int64_t lds_room = (int64_t)(160 * 1024 - shp.lds_static) / 4 - 8;
     int64_t cap_pages = std::min<int64_t>(kMaxPagesPerSplit, lds_room);
-    if (kernel >= pkv::KERNEL_M32_CTX_BF16) cap_pages = std::min<int64_t>(cap_pages, pkv::kM32MaxPages);
+    if (kernel >= pkv::KERNEL_M32_CTX_BF16 && kernel <= pkv::KERNEL_M32_CTX_PP)
+      cap_pages = std::min<int64_t>(cap_pages, pkv::kM32MaxPages);
     if (cap_pages < 1) return fail(PKV_ERR_UNSUPPORTED, "no LDS left for the page list");
     if (pps > cap_pages) pps = cap_pages;
   }
@@ -445,6 +454,7 @@ pkv_status run(const pkv_args* a, bool is_context, void* ws, size_t ws_bytes, vo
   }
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e = plan.kernel == pkv::KERNEL_GENERIC          ? pkv::launch_generic(p, s)
+                 : plan.kernel >= pkv::KERNEL_DMA_GQA_FP8_N2  ? pkv::launch_dma(plan.kernel, p, s)
                  : plan.kernel >= pkv::KERNEL_M32_CTX_BF16    ? pkv::launch_m32(plan.kernel, p, s)
                  : plan.kernel >= pkv::KERNEL_DMA_GQA_BF16    ? pkv::launch_dma(plan.kernel, p, s)
                                                               : pkv::launch_mfma(plan.kernel, p, s);

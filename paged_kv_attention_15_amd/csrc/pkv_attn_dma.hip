@@ -568,13 +568,17 @@ using DGqaFp8W8 = DmaCfg<128, 128, true, false, 1, 1, 8, 32, 2>;
 using DGqaFp8S2 = DmaCfg<128, 128, true, false, 1, 1, 4, 32, 2>;
 using DGqaBf16W4 = DmaCfg<128, 128, false, false, 1, 1, 4, 32, 2>;
 using DGqaBf16S2 = DmaCfg<128, 128, false, false, 1, 1, 2, 32, 2>;
+using DGqaFp8N2 = DmaCfg<128, 128, true, false, 1, 1, 2, 32, 2>;
+using DGqaFp8N1 = DmaCfg<128, 128, true, false, 1, 1, 1, 32, 3>;
+using DGqaFp8N2S3 = DmaCfg<128, 128, true, false, 1, 1, 2, 32, 3>;
 using DWideBf16 = DmaCfg<128, 128, false, false, 2, 4, 1, 64, 4>;
 using DWideFp8 = DmaCfg<128, 128, true, false, 2, 4, 1, 64, 4>;
 using DMlaBf16 = DmaCfg<576, 512, false, true, 1, 8, 1, 32, 4>;
 using DMlaFp8 = DmaCfg<576, 512, true, true, 1, 8, 1, 64, 4>;
 
 template <class C>
-static void fill_dma_shape(MfmaShape* s) {
+static void fill_dma_shape(MfmaShape* s, int waves_per_cu = 8) {
+  s->waves_per_cu = waves_per_cu;
   s->rows_per_block = C::ROWS;
   s->tile_tokens = C::T;
   s->threads = C::NTHR;
@@ -587,6 +591,11 @@ bool dma_shape(int32_t kernel, MfmaShape* s) {
     case KERNEL_DMA_GQA_FP8: fill_dma_shape<DGqaFp8>(s); return true;
     case KERNEL_DMA_GQA_FP8_W8: fill_dma_shape<DGqaFp8W8>(s); return true;
     case KERNEL_DMA_GQA_FP8_S2: fill_dma_shape<DGqaFp8S2>(s); return true;
+    // under 128 VGPRs: up to four waves per SIMD
+    case KERNEL_DMA_GQA_FP8_N2: fill_dma_shape<DGqaFp8N2>(s, 16); return true;
+    case KERNEL_DMA_GQA_BF16_N2: fill_dma_shape<DGqaBf16S2>(s, 16); return true;
+    case KERNEL_DMA_GQA_FP8_N1: fill_dma_shape<DGqaFp8N1>(s, 16); return true;
+    case KERNEL_DMA_GQA_FP8_N2S3: fill_dma_shape<DGqaFp8N2S3>(s, 16); return true;
     case KERNEL_DMA_GQA_BF16_W4: fill_dma_shape<DGqaBf16W4>(s); return true;
     case KERNEL_DMA_GQA_BF16_S2: fill_dma_shape<DGqaBf16S2>(s); return true;
     case KERNEL_DMA_WIDE_BF16: fill_dma_shape<DWideBf16>(s); return true;
@@ -626,6 +635,10 @@ hipError_t launch_dma(int32_t kernel, const KParams& p, hipStream_t s) {
     case KERNEL_DMA_GQA_FP8: return launch_dma_cfg<DGqaFp8>(p, s);
     case KERNEL_DMA_GQA_FP8_W8: return launch_dma_cfg<DGqaFp8W8>(p, s);
     case KERNEL_DMA_GQA_FP8_S2: return launch_dma_cfg<DGqaFp8S2>(p, s);
+    case KERNEL_DMA_GQA_FP8_N2: return launch_dma_cfg<DGqaFp8N2>(p, s);
+    case KERNEL_DMA_GQA_BF16_N2: return launch_dma_cfg<DGqaBf16S2>(p, s);
+    case KERNEL_DMA_GQA_FP8_N1: return launch_dma_cfg<DGqaFp8N1>(p, s);
+    case KERNEL_DMA_GQA_FP8_N2S3: return launch_dma_cfg<DGqaFp8N2S3>(p, s);
     case KERNEL_DMA_GQA_BF16_W4: return launch_dma_cfg<DGqaBf16W4>(p, s);
     case KERNEL_DMA_GQA_BF16_S2: return launch_dma_cfg<DGqaBf16S2>(p, s);
     case KERNEL_DMA_WIDE_BF16: return launch_dma_cfg<DWideBf16>(p, s);

@@ -172,23 +172,28 @@ hipError_t launch_generic(const KParams& p, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------- LSE merge
-// One wavefront per merged row; lane k first loads partition k's LSE (so all
-// statistics arrive together), the weights are then broadcast with readlane
-// and every lane accumulates channels lane, lane+64, ...  The partial rows are
-// loaded unconditionally (their addresses do not depend on earlier values, so
-// the loads pipeline) and an empty partition is selected out, never multiplied.
-// With request geometry attached (decode / context calls) a row reads only
-// the partitions that can hold one of its visible keys: the attention kernel
-// skips the rest without writing them.
-constexpr int kMergeRowsPerBlock = 4;
+// One workgroup of kMergeWaves wavefronts per merged row.  Lane k of every
+// wave first loads partition k's LSE (so all statistics arrive together and
+// every wave knows the row's max and total weight); wave w then accumulates the
+// partitions s = w, w + kMergeWaves, ... with their weights broadcast by
+// readlane, every lane covering channels lane, lane+64, ..., and the waves'
+// sums meet in LDS.  The partial rows are loaded unconditionally (their
+// addresses do not depend on earlier values, so the loads pipeline) and an
+// empty partition is selected out, never multiplied.  With request geometry
+// attached (decode / context calls) a row reads only the partitions that can
+// hold one of its visible keys: the attention kernel skips the rest without
+// writing them.
+constexpr int kMergeWaves = 4;
 
 __device__ __forceinline__ float readlane_f(float v, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }
 
-__global__ __launch_bounds__(64 * kMergeRowsPerBlock) void lse_merge_kernel(const MergeParams mp) {
+__global__ __launch_bounds__(64 * kMergeWaves) void lse_merge_kernel(const MergeParams mp) {
+  __shared__ float s_acc[kMergeWaves][kGenericMaxDv];
   const int lane = threadIdx.x & 63;
-  const int64_t r = (int64_t)blockIdx.x * kMergeRowsPerBlock + (threadIdx.x >> 6);
+  const int wv = threadIdx.x >> 6;
+  const int64_t r = blockIdx.x;
   if (r >= mp.num_rows) return;
   const int64_t t = r / mp.num_qo_heads;
   const int h = (int)(r % mp.num_qo_heads);
@@ -205,7 +210,7 @@ __global__ __launch_bounds__(64 * kMergeRowsPerBlock) void lse_merge_kernel(cons
     const int i = (int)(t % mp.q_len);
     const int g = h / mp.group;
     const int R = i * mp.group + (h % mp.group);
-    if (i == 0 && h == 0 && lane == 0) {
+    if (i == 0 && h == 0 && threadIdx.x == 0) {
       const int L0 = mp.seq_lens[b];
       if (L0 > mp.cap_tokens) flag_error(mp.err_word, PKV_DEVERR_SEQ_GT_TABLE);
       if (L0 < mp.q_len) flag_error(mp.err_word, PKV_DEVERR_SEQ_LT_QLEN);
@@ -277,7 +282,7 @@ __global__ __launch_bounds__(64 * kMergeRowsPerBlock) void lse_merge_kernel(cons
       wlane += w;
       const int nsp = min(64, live - s0);
 #pragma unroll 4
-      for (int j = 0; j < nsp; ++j) {
+      for (int j = wv; j < nsp; j += kMergeWaves) {
         const float wj = readlane_f(w, j);
         const float* src = mp.o_part + (prow0 + (int64_t)(s0 + j) * prow_step) * dv;
 #pragma unroll
@@ -291,13 +296,19 @@ __global__ __launch_bounds__(64 * kMergeRowsPerBlock) void lse_merge_kernel(cons
       }
     }
   }
-  const float wsum = wave_sum(wlane);
-  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     const int d = lane + 64 * k;
-    if (d >= dv) continue;
-    const float v = acc[k] * inv;
+    if (d < dv) s_acc[wv][d] = acc[k];
+  }
+  __syncthreads();
+  const float wsum = wave_sum(wlane);
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  for (int d = threadIdx.x; d < dv; d += 64 * kMergeWaves) {
+    float v = 0.f;
+#pragma unroll
+    for (int w2 = 0; w2 < kMergeWaves; ++w2) v += s_acc[w2][d];
+    v *= inv;
     const int64_t oi = t * mp.o_st + (int64_t)h * mp.o_sh + d;
     if (mp.o_dtype == PKV_DTYPE_BF16) {
       ((__bf16*)mp.out)[oi] = (__bf16)v;
@@ -305,13 +316,12 @@ __global__ __launch_bounds__(64 * kMergeRowsPerBlock) void lse_merge_kernel(cons
       ((float*)mp.out)[oi] = v;
     }
   }
-  if (mp.lse_out && lane == 0) mp.lse_out[r] = (M == -INFINITY) ? -INFINITY : M + __logf(wsum);
+  if (mp.lse_out && threadIdx.x == 0) mp.lse_out[r] = (M == -INFINITY) ? -INFINITY : M + __logf(wsum);
 }
 
 hipError_t launch_merge(const MergeParams& mp, hipStream_t s) {
   if (mp.num_rows == 0) return hipSuccess;
-  dim3 grid((unsigned)((mp.num_rows + kMergeRowsPerBlock - 1) / kMergeRowsPerBlock));
-  hipLaunchKernelGGL(lse_merge_kernel, grid, dim3(64 * kMergeRowsPerBlock), 0, s, mp);
+  hipLaunchKernelGGL(lse_merge_kernel, dim3((unsigned)mp.num_rows), dim3(64 * kMergeWaves), 0, s, mp);
   return hipGetLastError();
 }
 

@@ -44,7 +44,11 @@ enum KernelId : int32_t {
   KERNEL_M32_CTX_R2 = 28,    // D = 128, 4 waves x 64 rows, 4 x 16 KiB stages (two workgroups per CU)
   KERNEL_M32_CTX_R2W8 = 29,  // D = 128, 8 waves x 64 rows, 4 x 32 KiB stages
   KERNEL_M32_CTX_PP = 30,    // D = 128, 8 waves x 32 rows in two ping-pong halves
-  KERNEL_COUNT = 31,
+  KERNEL_DMA_GQA_FP8_N2 = 31,   // 2 token waves, 64-key tiles, 2 stages (32 KiB: four groups per CU)
+  KERNEL_DMA_GQA_BF16_N2 = 32,  // 2 token waves, 64-key tiles, 2 stages (64 KiB)
+  KERNEL_DMA_GQA_FP8_N1 = 33,   // 1 token wave, 32-key tiles, 3 stages (24 KiB: six groups per CU)
+  KERNEL_DMA_GQA_FP8_N2S3 = 34, // 2 token waves, 64-key tiles, 3 stages (48 KiB)
+  KERNEL_COUNT = 35,
 };
 
 // Everything a kernel reads, by value.  Element strides as in pkv_args.
@@ -114,6 +118,7 @@ struct MfmaShape {
   int tile_tokens;       // KV tokens per pipeline stage
   int threads;           // workgroup size
   size_t lds_static;     // LDS for the KV stages and reductions (page list excluded)
+  int waves_per_cu = 8;  // register-limited resident waves per CU (the balanced schedule sizes its grid by it)
 };
 bool mfma_shape(int32_t kernel, MfmaShape* out);
 bool dma_shape(int32_t kernel, MfmaShape* out);

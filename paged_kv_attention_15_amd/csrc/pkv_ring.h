@@ -41,8 +41,9 @@ __device__ __forceinline__ void wait_loads() {
 // that bookkeeping themselves (wait_loads before the barrier that publishes a
 // stage).  M0 carries the LDS address; nothing else in these kernels uses M0.
 __device__ __forceinline__ void dma16(const void* gptr, unsigned char* lds_wave_base) {
-  const uint32_t lds = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)lds_wave_base);
+  // low word of the flat address of an LDS location = its LDS offset (the
+  // shared aperture base has a zero low word); no address-space cast needed
+  const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_wave_base);
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                :
                : "v"(gptr), "s"(lds)
@@ -53,8 +54,9 @@ __device__ __forceinline__ void dma16(const void* gptr, unsigned char* lds_wave_
 // (global SADDR form): the 64-bit address arithmetic happens once per
 // wave-instruction on the scalar unit instead of in every lane.
 __device__ __forceinline__ void dma16_saddr(uint64_t base, uint32_t voff, unsigned char* lds_wave_base) {
-  const uint32_t lds = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)lds_wave_base);
+  // low word of the flat address of an LDS location = its LDS offset (the
+  // shared aperture base has a zero low word); no address-space cast needed
+  const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_wave_base);
   // the base must live in SGPRs for the SADDR form: make its uniformity explicit
   // (readfirstlane returns int: go through uint32_t so the low word is not sign-extended)
   const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)base);

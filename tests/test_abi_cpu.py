@@ -81,7 +81,7 @@ def test_kernel_choice_by_shape():
     a.q = a.k_pages = a.v_pages = a.out = 0x1000  # aligned dummy addresses (never dereferenced)
     assert pkv.KERNEL_NAMES[pkv.pkv_plan(a).kernel] == "gqa_bf16"
     a.kv_dtype = pkv.PKV_DTYPE_FP8_E4M3
-    assert pkv.KERNEL_NAMES[pkv.pkv_plan(a).kernel] == "dma_gqa_fp8_s2"
+    assert pkv.KERNEL_NAMES[pkv.pkv_plan(a).kernel] == "dma_gqa_fp8_n2"
     # fp32 queries, odd page sizes or misaligned pointers fall back to the generic kernel
     b = _args_for(_fake(page_size=24))
     b.q = b.k_pages = b.v_pages = b.out = 0x1000

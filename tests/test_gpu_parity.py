@@ -298,6 +298,8 @@ def test_malformed_q_indptr_flagged_without_writes():
     ("gqa_fp8_s2", W.E4M3, 2), ("gqa_bf16_t256", W.BF16, 2),
     ("dma_gqa_fp8_w8", W.E4M3, None), ("dma_gqa_fp8_s2", W.E4M3, None), ("dma_gqa_bf16_w4", W.BF16, None),
     ("dma_gqa_bf16_s2", W.BF16, None), ("dma_gqa_bf16_w4", W.BF16, 2),
+    ("dma_gqa_fp8_n2", W.E4M3, None), ("dma_gqa_fp8_n2", W.E4M3, -1), ("dma_gqa_bf16_n2", W.BF16, -1),
+    ("dma_gqa_fp8_n1", W.E4M3, -1), ("dma_gqa_fp8_n2s3", W.E4M3, -1),
 ])
 def test_gqa_kernel_families_match_oracle(kernel, kv, splits):
     P = 64 if kv == W.E4M3 else 32
