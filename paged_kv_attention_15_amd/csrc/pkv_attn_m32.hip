@@ -20,8 +20,8 @@
 // below the MFMA time).  KV tiles arrive through the direct-to-LDS ring of
 // pkv_ring.h.  The paging follows the flashinfer.cake_fmha API page's contract
 // (key j of request b is token j % P of page block_tables[b][j / P]); the
-// online softmax and the Split-KV partials follow the FlashInfer and
-// Flash-Decoding pages (running max, rescaled running sum, natural-log LSE).
+// Split-KV partials (normalized O and natural-log LSE per partition, merged
+// by the separate reducer) follow the PR #4557 page's Split-KV description.
 
 #include "pkv_device.h"
 #include "pkv_internal.h"
