@@ -82,7 +82,9 @@ def time_calls(dp, steps: int, warmup: int):
 def measure(prob, steps: int, warmup: int, num_splits=None):
     from paged_kv_attention_15_amd import pkv
 
-    dp = pkv.upload(prob, "cuda", with_lse=False, with_err=False, num_splits=num_splits)
+    # merge counters (zeroed once, like the workspace, outside the timed calls):
+    # the balanced decode schedule then reduces inside the attention kernel
+    dp = pkv.upload(prob, "cuda", with_lse=False, with_err=False, num_splits=num_splits, merge_counters=True)
     info = pkv.pkv_plan(dp.args, dp.is_context)
     wall, ev_mean = time_calls(dp, steps, warmup)
     return dp, info, wall, ev_mean
@@ -126,6 +128,7 @@ def secondary_results(steps: int, warmup: int):
         tflops = prob.flops() / ev_mean / 1e12
         rec = {"us_per_call": round(ev_mean * 1e6, 3),
                "kernel": pkv.KERNEL_NAMES[info.kernel], "num_splits": info.num_splits,
+               "fused_merge": int(info.fused_merge),
                "kv_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
                "tflops": round(tflops, 2), "mfma_frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
                "bound": bound, "kv_bytes": prob.kv_bytes(), "flops": prob.flops()}

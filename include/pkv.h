@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 1
+#define PKV_ABI_VERSION 2
 
 typedef enum pkv_status {
   PKV_OK = 0,
@@ -134,6 +134,16 @@ typedef struct pkv_args {
   int32_t* err_word;         /* optional device word, OR-ed with PKV_DEVERR_* bits */
   const float* k_scale_dev;  /* optional */
   const float* v_scale_dev;  /* optional */
+  /* Optional split counters for the balanced decode schedule (num_splits == -1,
+     or chosen by the planner): int32 [pkv_plan_info.counter_words], device
+     memory that must be all zero before its first use (e.g. allocated zeroed
+     once) and that every completed call leaves all zero again.  With it, the
+     last workgroup to finish a (request, KV head) merges that unit's partial
+     rows inside the attention kernel (the PR #4557 page: split counters in
+     caller-owned memory that reset themselves); NULL selects the separate
+     reducer kernel.  Calls that share one counter buffer must not overlap in
+     time (same stream, or otherwise ordered).  Ignored by every other plan. */
+  int32_t* merge_counters;
 
   int64_t q_stride_tok, q_stride_head;
   int64_t o_stride_tok, o_stride_head;
@@ -157,6 +167,8 @@ typedef struct pkv_plan_info {
   int32_t schedule;        /* 0: per-unit partitions, grid (num_splits, Hkv x row blocks, B);
                               1: balanced decode schedule, grid_x workgroups own equal page
                                  ranges of all requests; num_splits then counts partial slots */
+  int32_t counter_words;   /* schedule 1: int32 words merge_counters must hold (B x Hkv); else 0 */
+  int32_t fused_merge;     /* 1: the reducer runs inside the attention kernel (merge_counters given) */
   size_t workspace_bytes;  /* 0 when num_splits == 1 */
 } pkv_plan_info;
 

@@ -64,6 +64,8 @@ constexpr int kMaxPagesPerSplit = 4096;  // bounds the LDS page list of the MFMA
 // Host-visible argument checks shared by plan / decode / context.
 pkv_status validate(const pkv_args* a, bool is_context) {
   if (!a) return fail(PKV_ERR_INVALID_ARG, "args is NULL");
+  if ((reinterpret_cast<uintptr_t>(a->merge_counters) & 3u) != 0)
+    return fail(PKV_ERR_INVALID_ARG, "merge_counters must be 4-byte aligned");
   if (a->batch < 0) return fail(PKV_ERR_INVALID_ARG, "batch must be >= 0 (got %d)", a->batch);
   if (a->num_kv_heads < 1 || a->num_qo_heads < 1 || a->num_qo_heads % a->num_kv_heads != 0)
     return fail(PKV_ERR_INVALID_ARG, "num_qo_heads (%d) must be a positive multiple of num_kv_heads (%d)",
@@ -290,7 +292,7 @@ pkv_status make_plan(const pkv_args* a, bool is_context, int num_cus, pkv_plan_i
   if (a->num_splits == -1 || (a->num_splits == 0 && gqa && units < num_cus)) {
     if (!gqa || is_context)
       return fail(PKV_ERR_UNSUPPORTED, "the balanced schedule needs a GQA decode kernel family");
-    const int64_t extra = (int64_t)a->max_pages_per_seq + a->batch + 1 + 3;
+    const int64_t extra = (int64_t)a->max_pages_per_seq + a->batch + 2 + 3;  // page list, prefix, flag
     const int64_t lds = (int64_t)shp.lds_static + extra * 4;
     if (lds > 160 * 1024) {
       if (a->num_splits == -1) return fail(PKV_ERR_UNSUPPORTED, "balanced schedule: page table too wide for LDS");
@@ -303,6 +305,14 @@ pkv_status make_plan(const pkv_args* a, bool is_context, int num_cus, pkv_plan_i
       const int64_t U = (int64_t)a->batch * a->num_kv_heads;
       const int64_t slot_rows = (int64_t)a->q_len * G;
       info->schedule = 1;
+      info->counter_words = (int32_t)U;
+      // the fused reducer lives in the direct-to-LDS stream kernel and keeps its
+      // per-unit owner table in the ring's LDS.  Every owner of a unit owns at least
+      // one of its pages, and the kernels clamp a request to the table width, so
+      // a unit has at most min(W, max_pages_per_seq) owners.
+      const int64_t owners = std::min<int64_t>(W, std::max<int64_t>(a->max_pages_per_seq, 1));
+      const bool fits = owners <= (int64_t)shp.lds_static / 4;
+      info->fused_merge = a->merge_counters != nullptr && kernel >= pkv::KERNEL_DMA_GQA_BF16 && fits;
       info->num_splits = (int32_t)(W + U);
       info->pages_per_split = 0;
       info->grid_x = (int32_t)W;
@@ -447,6 +457,7 @@ pkv_status run(const pkv_args* a, bool is_context, void* ws, size_t ws_bytes, vo
     p.ws_lse = reinterpret_cast<float*>(lse_base);
     uintptr_t pfx_base = (reinterpret_cast<uintptr_t>(p.ws_lse + n_l) + 255) & ~uintptr_t(255);
     p.ws_pfx = reinterpret_cast<int32_t*>(pfx_base);
+    p.counters = plan.fused_merge ? a->merge_counters : nullptr;
   } else if (plan.num_splits > 1) {
     uintptr_t base = (reinterpret_cast<uintptr_t>(ws) + 255) & ~uintptr_t(255);
     p.ws_o = reinterpret_cast<float*>(base);
@@ -459,7 +470,7 @@ pkv_status run(const pkv_args* a, bool is_context, void* ws, size_t ws_bytes, vo
                  : plan.kernel >= pkv::KERNEL_DMA_GQA_BF16    ? pkv::launch_dma(plan.kernel, p, s)
                                                               : pkv::launch_mfma(plan.kernel, p, s);
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "attention launch failed: %s", hipGetErrorString(e));
-  if (plan.num_splits > 1) {
+  if (plan.num_splits > 1 && !plan.fused_merge) {
     pkv::MergeParams mp;
     std::memset(&mp, 0, sizeof mp);
     mp.num_splits = plan.num_splits;
@@ -484,6 +495,7 @@ pkv_status run(const pkv_args* a, bool is_context, void* ws, size_t ws_bytes, vo
     mp.max_q_len = p.max_q_len;
     mp.total_q = p.total_q;
     mp.err_word = a->err_word;
+    mp.vec4 = a->head_dim_v % 4 == 0;  // the workspace partials are 256-byte aligned
     if (p.stream) {
       mp.stream = 1;
       mp.num_wg = p.num_wg;
@@ -561,6 +573,7 @@ pkv_status pkv_lse_merge(int32_t num_splits, int32_t num_rows, int32_t num_qo_he
   mp.lse_part = lse_part;
   mp.out = out;
   mp.lse_out = lse_out;
+  mp.vec4 = head_dim_v % 4 == 0 && (reinterpret_cast<uintptr_t>(o_part) & 15u) == 0;
   hipError_t e = pkv::launch_merge(mp, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "merge launch failed: %s", hipGetErrorString(e));
   return ok();

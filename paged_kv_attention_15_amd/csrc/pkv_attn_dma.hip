@@ -82,10 +82,19 @@ __device__ __forceinline__ int phys_chunk(int c, int key) {
   return c ^ (key & swz_mask<NC>(c));
 }
 
+// Device-coherent word access (agent scope, relaxed): the value goes to or
+// comes from the device-wide coherence point rather than one XCD's L2.
+__device__ __forceinline__ void st_coherent(float* ptr, float v) {
+  __hip_atomic_store(ptr, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_coherent(const float* ptr) {
+  return __hip_atomic_load(const_cast<float*>(ptr), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 template <class C>
 __device__ __forceinline__ void dma_block(const KParams& p, unsigned char* smem, int32_t* s_pages, const int b,
                                           const int g, const int rb, const int part_lo, const int part_hi,
-                                          const int slot, const bool lead) {
+                                          const int slot, const bool lead, const bool direct = false) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar branches below
   const int wr = wave / C::NWT;
@@ -129,7 +138,9 @@ __device__ __forceinline__ void dma_block(const KParams& p, unsigned char* smem,
   const int kv_lo = part_lo;
   const int kv_hi = min(part_hi, c_max);
   const int n_tiles = kv_hi > kv_lo ? (kv_hi - kv_lo + C::T - 1) / C::T : 0;
-  if (n_tiles == 0 && p.ws_o != nullptr) return;
+  // partial rows go to the workspace unless this piece is the whole key range of its rows
+  const bool split_mode = p.ws_o != nullptr && !direct;
+  if (n_tiles == 0 && split_mode) return;
 
   const int pg_lo = kv_lo >> p.log2_page;
   const int n_pg = n_tiles > 0 ? ((kv_hi - 1) >> p.log2_page) - pg_lo + 1 : 0;
@@ -452,7 +463,6 @@ __device__ __forceinline__ void dma_block(const KParams& p, unsigned char* smem,
   }
 
   // ---- epilogue
-  const bool split_mode = p.ws_o != nullptr;
 #pragma unroll
   for (int rt = 0; rt < C::RT; ++rt) {
     if (!row_ok[rt]) continue;
@@ -462,6 +472,21 @@ __device__ __forceinline__ void dma_block(const KParams& p, unsigned char* smem,
     const int64_t row_g = (int64_t)row_t[rt] * p.num_qo_heads + row_h[rt];
     if (split_mode) {
       const int64_t prow = p.stream ? (int64_t)slot * p.slot_rows + row_R[rt] : (int64_t)slot * p.rows_total + row_g;
+      if (p.counters != nullptr) {
+        // read back inside this kernel by a workgroup that may run on another
+        // XCD: device-coherent stores that do not stay in this XCD's L2
+        if (G4_in == 0 && db_first == 0) st_coherent(p.ws_lse + prow, lse);
+        if (!empty) {
+          float* dst = p.ws_o + prow * C::DV + G4_in * 4;
+#pragma unroll
+          for (int d = 0; d < C::NDB; ++d) {
+            if (C::NWT > 1 && d % C::NWT != db_first) continue;
+            const f32x4 v = O[rt][d] * inv;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) st_coherent(dst + d * 16 + j, v[j]);
+          }
+        }
+      } else {
       if (G4_in == 0 && db_first == 0) p.ws_lse[prow] = lse;
       if (!empty) {
         float* dst = p.ws_o + prow * C::DV + G4_in * 4;
@@ -470,6 +495,7 @@ __device__ __forceinline__ void dma_block(const KParams& p, unsigned char* smem,
           if (C::NWT > 1 && d % C::NWT != db_first) continue;
           *(f32x4*)(dst + d * 16) = O[rt][d] * inv;
         }
+      }
       }
     } else {
       if (p.lse_out && G4_in == 0 && db_first == 0) p.lse_out[row_g] = lse;
@@ -504,12 +530,133 @@ __global__ __launch_bounds__(C::NTHR) void attn_dma_kernel(const KParams p) {
                split * span + span, split, split == 0);
 }
 
+// Fused reducer of the balanced schedule.  Unit u = (request b, KV head g) owns
+// the global pages [p_s, p_s + npg); its partial rows come from every workgroup
+// whose page range meets that interval, one segment each, in slots w + u.  Each
+// such workgroup publishes its partial rows (agent-scope release: the partials
+// may sit in another XCD's L2), then increments the unit's counter; the one
+// that brings it to the number of owners merges the unit's rows exactly as the
+// separate reducer does (L* = max lse_s, w_s = exp(lse_s - L*), out = sum w_s O_s
+// / sum w_s) and puts the counter back to zero, so the counter buffer is zero
+// between calls (the PR #4557 page: split counters in caller-owned memory that
+// reset themselves).  Nothing waits on another workgroup, so there is no
+// residency requirement and no spin.
+struct StreamUnit {
+  int b, g, u;
+  int64_t p_s, npg, TP, W;
+  // owner workgroup of global page q (the w with w*TP/W <= q < (w+1)*TP/W)
+  __device__ int64_t owner(int64_t q) const { return ((q + 1) * W - 1) / TP; }
+  // number of workgroups that own pages of the unit: all of [owner(p_s), owner(p_e)]
+  // when every workgroup owns a page (TP >= W), else one per page
+  __device__ int count() const { return TP >= W ? (int)(owner(p_s + npg - 1) - owner(p_s) + 1) : (int)npg; }
+  __device__ int64_t slot_wg(int k) const { return TP >= W ? owner(p_s) + k : owner(p_s + k); }
+};
+
+// The reducer for one unit: every thread owns J items (packed row, 4 value
+// channels) and walks the owners in batches of KB with the running-max update
+// of the online softmax (m, l, acc rescaled when the max grows), so each batch
+// issues all of its loads before the first result is needed.
+template <class C, int J, int KB>
+__device__ __forceinline__ void merge_unit(const KParams& p, const int* s_slot, const int n, const StreamUnit& su) {
+  const int SR = p.slot_rows, G = p.group;
+  constexpr int DV4 = C::DV / 4;
+  const int nitem = SR * DV4;
+  int R[J], c4[J];
+  float m[J], l[J];
+  f32x4 acc[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int idx = threadIdx.x + j * C::NTHR;
+    R[j] = idx < nitem ? idx / DV4 : 0;
+    c4[j] = idx % DV4;
+    m[j] = -INFINITY;
+    l[j] = 0.f;
+    acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  for (int k0 = 0; k0 < n; k0 += KB) {
+    float ls[J][KB];
+    f32x4 v[J][KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      const int slot = s_slot[min(k0 + kb, n - 1)];
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        const int64_t prow = (int64_t)slot * SR + R[j];
+        ls[j][kb] = ld_coherent(p.ws_lse + prow);
+        const float* src = p.ws_o + prow * C::DV + 4 * c4[j];
+        v[j][kb] = f32x4{ld_coherent(src), ld_coherent(src + 1), ld_coherent(src + 2), ld_coherent(src + 3)};
+      }
+    }
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        // owners past n and rows a segment left empty (lse = -inf, O unwritten) do not enter
+        const bool live = (k0 + kb < n) && ls[j][kb] != -INFINITY;
+        const float mn = live ? fmaxf(m[j], ls[j][kb]) : m[j];
+        const float a = (m[j] == -INFINITY) ? 0.f : __expf(m[j] - mn);
+        const float w = __expf(ls[j][kb] - mn);
+        l[j] = live ? l[j] * a + w : l[j];
+        acc[j] = live ? acc[j] * a + w * v[j][kb] : acc[j];
+        m[j] = mn;
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    if (threadIdx.x + j * C::NTHR >= nitem) continue;
+    const float inv = l[j] > 0.f ? 1.f / l[j] : 0.f;
+    const f32x4 o = acc[j] * inv;
+    const int64_t t = (int64_t)su.b * p.q_len + R[j] / G;
+    const int h = su.g * G + R[j] % G;
+    if (p.o_dtype == PKV_DTYPE_BF16) {
+      __bf16* dst = (__bf16*)p.out + t * p.o_st + h * p.o_sh + 4 * c4[j];
+      *(u32x2*)dst = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+    } else {
+      *(f32x4*)((float*)p.out + t * p.o_st + h * p.o_sh + 4 * c4[j]) = o;
+    }
+    if (c4[j] == 0 && p.lse_out)
+      p.lse_out[t * p.num_qo_heads + h] = (m[j] == -INFINITY) ? -INFINITY : m[j] + __logf(l[j]);
+  }
+}
+
+template <class C>
+__device__ __forceinline__ void stream_arrive(const KParams& p, unsigned char* smem, int* s_flag,
+                                              const StreamUnit& su) {
+  // The partial rows were written with device-coherent stores; once every
+  // thread has waited for its stores to complete they are visible device-wide,
+  // without writing back or invalidating any L2 (which would stall every
+  // workgroup of the XCD).  The counter update and the reads below are
+  // device-coherent too.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  const int n = su.count();
+  if (threadIdx.x == 0) {
+    const int old = __hip_atomic_fetch_add(p.counters + su.u, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *s_flag = (old + 1 == n);
+  }
+  __syncthreads();
+  if (!*s_flag) return;
+
+  // owner slots into LDS (the ring is idle here; the planner keeps n words within it)
+  int* s_slot = (int*)smem;
+  for (int k = threadIdx.x; k < n; k += C::NTHR) s_slot[k] = (int)(su.slot_wg(k) + su.u);
+  __syncthreads();
+  constexpr int DV4 = C::DV / 4;
+  const int J = (p.slot_rows * DV4 + C::NTHR - 1) / C::NTHR;  // items (row, 4 channels) per thread
+  if (J <= 1) merge_unit<C, 1, 16>(p, s_slot, n, su);
+  else if (J <= 2) merge_unit<C, 2, 8>(p, s_slot, n, su);
+  else merge_unit<C, 4, 4>(p, s_slot, n, su);
+  if (threadIdx.x == 0) __hip_atomic_store(p.counters + su.u, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Balanced schedule (see attn_mfma_stream_kernel): equal global page ranges per workgroup.
 template <class C>
 __global__ __launch_bounds__(C::NTHR) void attn_dma_stream_kernel(const KParams p) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   int32_t* s_pages = (int32_t*)(smem + C::LDS);
-  int32_t* s_pfx = s_pages + p.page_list_cap;
+  int32_t* s_pfx = s_pages + p.page_list_cap;  // [B + 1] page prefix, then the reducer's flag word
+  int* s_flag = s_pfx + p.batch + 1;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int B = p.batch;
@@ -538,8 +685,29 @@ __global__ __launch_bounds__(C::NTHR) void attn_dma_stream_kernel(const KParams 
   const int64_t TP = (int64_t)s_pfx[B] * Hkv;
   const int64_t W = gridDim.x;
   const int64_t w = blockIdx.x;
-  if (w == 0)
+  const bool fused = p.counters != nullptr;
+  if (!fused && w == 0)
     for (int i = tid; i <= B; i += C::NTHR) p.ws_pfx[i] = s_pfx[i];
+  if (fused) {
+    // requests with no page are streamed by nobody: their rows are written here
+    for (int64_t bb = w; bb < B; bb += W) {
+      if (s_pfx[bb + 1] != s_pfx[bb]) continue;
+      if (tid == 0) {
+        const int L0 = p.seq_lens[bb];
+        if (L0 > cap) flag_error(p.err_word, PKV_DEVERR_SEQ_GT_TABLE);
+        if (L0 < p.q_len) flag_error(p.err_word, PKV_DEVERR_SEQ_LT_QLEN);
+      }
+      const int nrow = p.q_len * p.num_qo_heads;
+      for (int idx = tid; idx < nrow * C::DV; idx += C::NTHR) {
+        const int rr = idx / C::DV, d = idx % C::DV;
+        const int64_t t = bb * p.q_len + rr / p.num_qo_heads;
+        const int h = rr % p.num_qo_heads;
+        if (p.o_dtype == PKV_DTYPE_BF16) ((__bf16*)p.out)[t * p.o_st + h * p.o_sh + d] = (__bf16)0.f;
+        else ((float*)p.out)[t * p.o_st + h * p.o_sh + d] = 0.f;
+        if (d == 0 && p.lse_out) p.lse_out[t * p.num_qo_heads + h] = -INFINITY;
+      }
+    }
+  }
   int64_t pos = w * TP / W;
   const int64_t end = (w + 1) * TP / W;
   while (pos < end) {
@@ -555,7 +723,20 @@ __global__ __launch_bounds__(C::NTHR) void attn_dma_stream_kernel(const KParams 
     const int64_t u_start = base + g * npg;
     const int64_t seg_end = min(end, u_start + npg);
     const int a = (int)(pos - u_start), e = (int)(seg_end - u_start);
-    dma_block<C>(p, smem, s_pages, b, g, 0, a * p.page_size, e * p.page_size, (int)(w + b * Hkv + g), a == 0);
+    const bool whole = fused && a == 0 && e == npg;  // sole owner: final rows straight from the epilogue
+    dma_block<C>(p, smem, s_pages, b, g, 0, a * p.page_size, e * p.page_size, (int)(w + b * Hkv + g), a == 0,
+                 whole);
+    if (fused && !whole) {
+      StreamUnit su;
+      su.b = b;
+      su.g = g;
+      su.u = b * Hkv + g;
+      su.p_s = u_start;
+      su.npg = npg;
+      su.TP = TP;
+      su.W = W;
+      stream_arrive<C>(p, smem, s_flag, su);
+    }
     pos = seg_end;
   }
 }
@@ -591,7 +772,7 @@ bool dma_shape(int32_t kernel, MfmaShape* s) {
     case KERNEL_DMA_GQA_FP8: fill_dma_shape<DGqaFp8>(s); return true;
     case KERNEL_DMA_GQA_FP8_W8: fill_dma_shape<DGqaFp8W8>(s); return true;
     case KERNEL_DMA_GQA_FP8_S2: fill_dma_shape<DGqaFp8S2>(s); return true;
-    // under 128 VGPRs: up to four waves per SIMD
+    // 128-thread groups whose LDS, not registers, limits residency (four per CU)
     case KERNEL_DMA_GQA_FP8_N2: fill_dma_shape<DGqaFp8N2>(s, 16); return true;
     case KERNEL_DMA_GQA_BF16_N2: fill_dma_shape<DGqaBf16S2>(s, 16); return true;
     case KERNEL_DMA_GQA_FP8_N1: fill_dma_shape<DGqaFp8N1>(s, 16); return true;
@@ -609,7 +790,7 @@ bool dma_shape(int32_t kernel, MfmaShape* s) {
 template <class C>
 static hipError_t launch_dma_cfg(const KParams& p, hipStream_t s) {
   static bool attr_done = false;  // idempotent; a race only repeats the same calls
-  const size_t extra = (size_t)p.page_list_cap + (p.stream ? (size_t)p.batch + 1 : 0);
+  const size_t extra = (size_t)p.page_list_cap + (p.stream ? (size_t)p.batch + 2 : 0);
   const size_t lds = C::LDS + ((extra + 3) & ~size_t(3)) * sizeof(int32_t);
   if (!attr_done) {
     hipError_t e = hipFuncSetAttribute((const void*)attn_dma_kernel<C>,

@@ -172,39 +172,143 @@ hipError_t launch_generic(const KParams& p, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------- LSE merge
-// One workgroup of kMergeWaves wavefronts per merged row.  Lane k of every
-// wave first loads partition k's LSE (so all statistics arrive together and
-// every wave knows the row's max and total weight); wave w then accumulates the
-// partitions s = w, w + kMergeWaves, ... with their weights broadcast by
-// readlane, every lane covering channels lane, lane+64, ..., and the waves'
-// sums meet in LDS.  The partial rows are loaded unconditionally (their
-// addresses do not depend on earlier values, so the loads pipeline) and an
-// empty partition is selected out, never multiplied.  With request geometry
-// attached (decode / context calls) a row reads only the partitions that can
-// hold one of its visible keys: the attention kernel skips the rest without
-// writing them.
-constexpr int kMergeWaves = 4;
+// One workgroup of kMergeThreads threads per merged row.  The row's value
+// channels are cut into items of CW channels; when there are fewer items than
+// threads, the threads of one item split the partitions between them
+// (partition s goes to subset s mod S_sub).  Each thread walks its partitions
+// with the running-max update of the online softmax (m, l and the channel sums
+// rescaled whenever the max grows), loading a batch of partitions' LSE and
+// partial channels before using any of them, so a row costs about one memory
+// round trip however many partitions it has; the subsets meet in LDS.  An
+// empty partition (lse = -inf, channels never written) is selected out, never
+// multiplied.  With request geometry attached (decode / context calls) a row
+// reads only the partitions that can hold one of its visible keys: the
+// attention kernel skips the rest without writing them.
+constexpr int kMergeThreads = 256;
+constexpr int kMergeBatch = 4;
 
-__device__ __forceinline__ float readlane_f(float v, int lane) {
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+struct MergeRow {
+  int live;               // partitions that may hold keys of this row
+  int64_t prow0, step;    // partial row of partition s: prow0 + s * step
+  int64_t w_first, TPs;   // balanced schedule: first owner workgroup and total pages (TPs = 0: unused)
+  int64_t num_wg;
+};
+
+template <int CW>
+__device__ __forceinline__ void merge_row(const MergeParams& mp, const MergeRow& mr, const int64_t r,
+                                          float* s_red) {
+  const int dv = mp.dv;
+  const int NQ = (dv + CW - 1) / CW;  // items
+  const int tid = threadIdx.x;
+  const int S_sub = NQ >= kMergeThreads ? 1 : kMergeThreads / NQ;
+  const int sub = NQ >= kMergeThreads ? 0 : tid / NQ;
+  if (sub >= S_sub) {
+    __syncthreads();  // matches the subsets' LDS exchange below
+    return;
+  }
+  const int64_t t = r / mp.num_qo_heads;
+  const int h = (int)(r % mp.num_qo_heads);
+  auto slot_lse = [&](int s) -> float {
+    if (mr.TPs > 0) {  // balanced schedule: an owner range may hold workgroups without pages
+      const int64_t w = mr.w_first + s;
+      if ((w + 1) * mr.TPs / mr.num_wg == w * mr.TPs / mr.num_wg) return -INFINITY;
+    }
+    return mp.lse_part[mr.prow0 + s * mr.step];
+  };
+  for (int q = (NQ >= kMergeThreads ? tid : tid % NQ); q < NQ; q += (NQ >= kMergeThreads ? kMergeThreads : NQ)) {
+    float m = -INFINITY, l = 0.f;
+    float acc[CW];
+#pragma unroll
+    for (int c = 0; c < CW; ++c) acc[c] = 0.f;
+    for (int s0 = sub; s0 < mr.live; s0 += S_sub * kMergeBatch) {
+      float ls[kMergeBatch];
+      float v[kMergeBatch][CW];
+#pragma unroll
+      for (int kb = 0; kb < kMergeBatch; ++kb) {
+        const int s = s0 + kb * S_sub;
+        const int sc = s < mr.live ? s : s0;
+        ls[kb] = s < mr.live ? slot_lse(sc) : -INFINITY;
+        const float* src = mp.o_part + (mr.prow0 + sc * mr.step) * dv + q * CW;
+        if constexpr (CW == 4) {
+          const f32x4 x = *(const f32x4*)src;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) v[kb][c] = x[c];
+        } else {
+          v[kb][0] = src[0];
+        }
+      }
+#pragma unroll
+      for (int kb = 0; kb < kMergeBatch; ++kb) {
+        const bool live = ls[kb] != -INFINITY;
+        const float mn = live ? fmaxf(m, ls[kb]) : m;
+        const float a = (m == -INFINITY) ? 0.f : __expf(m - mn);
+        const float w = __expf(ls[kb] - mn);
+        l = live ? l * a + w : l;
+#pragma unroll
+        for (int c = 0; c < CW; ++c) acc[c] = live ? acc[c] * a + w * v[kb][c] : acc[c];
+        m = mn;
+      }
+    }
+    if (S_sub > 1) {
+      float* e = s_red + (sub * NQ + q) * (CW + 2);
+      e[0] = m;
+      e[1] = l;
+#pragma unroll
+      for (int c = 0; c < CW; ++c) e[2 + c] = acc[c];
+    }
+    if (S_sub > 1) {
+      __syncthreads();
+      if (sub != 0) return;
+      float M = -INFINITY;
+      for (int k = 0; k < S_sub; ++k) M = fmaxf(M, s_red[(k * NQ + q) * (CW + 2)]);
+      l = 0.f;
+#pragma unroll
+      for (int c = 0; c < CW; ++c) acc[c] = 0.f;
+      if (M != -INFINITY) {
+        for (int k = 0; k < S_sub; ++k) {
+          const float* e = s_red + (k * NQ + q) * (CW + 2);
+          const float a = e[0] == -INFINITY ? 0.f : __expf(e[0] - M);
+          l += a * e[1];
+#pragma unroll
+          for (int c = 0; c < CW; ++c) acc[c] += a * e[2 + c];
+        }
+      }
+      m = M;
+    }
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+    for (int c = 0; c < CW; ++c) {
+      const int d = q * CW + c;
+      if (d >= dv) break;
+      const int64_t oi = t * mp.o_st + (int64_t)h * mp.o_sh + d;
+      if (mp.o_dtype == PKV_DTYPE_BF16) {
+        ((__bf16*)mp.out)[oi] = (__bf16)(acc[c] * inv);
+      } else {
+        ((float*)mp.out)[oi] = acc[c] * inv;
+      }
+    }
+    if (mp.lse_out && q == 0) mp.lse_out[r] = (m == -INFINITY) ? -INFINITY : m + __logf(l);
+  }
+  if (S_sub == 1) __syncthreads();  // matches the idle threads' barrier
 }
 
-__global__ __launch_bounds__(64 * kMergeWaves) void lse_merge_kernel(const MergeParams mp) {
-  __shared__ float s_acc[kMergeWaves][kGenericMaxDv];
-  const int lane = threadIdx.x & 63;
-  const int wv = threadIdx.x >> 6;
+__global__ __launch_bounds__(kMergeThreads) void lse_merge_kernel(const MergeParams mp) {
+  __shared__ float s_red[kMergeThreads * 6];
   const int64_t r = blockIdx.x;
   if (r >= mp.num_rows) return;
   const int64_t t = r / mp.num_qo_heads;
   const int h = (int)(r % mp.num_qo_heads);
-  const int dv = mp.dv;
 
   // partial rows of this output row: `live` slots, slot k at partial row
-  // prow0 + k*prow_step (Split-KV layout: [split][row]; stream layout: a row
+  // prow0 + k*step (Split-KV layout: [split][row]; stream layout: a row
   // of slot (w + u) for the consecutive workgroups w that own unit u's pages)
-  int live = mp.num_splits;
-  int64_t prow0 = r, prow_step = mp.num_rows;
-  int64_t w_first = 0, TPs = 0;  // stream schedule: first owner workgroup, total pages
+  MergeRow mr;
+  mr.live = mp.num_splits;
+  mr.prow0 = r;
+  mr.step = mp.num_rows;
+  mr.w_first = 0;
+  mr.TPs = 0;
+  mr.num_wg = mp.num_wg;
   if (mp.stream) {
     const int b = (int)(t / mp.q_len);
     const int i = (int)(t % mp.q_len);
@@ -217,7 +321,7 @@ __global__ __launch_bounds__(64 * kMergeWaves) void lse_merge_kernel(const Merge
     }
     const int64_t npg = mp.pfx[b + 1] - mp.pfx[b];
     const int64_t TP = (int64_t)mp.pfx[mp.batch] * mp.num_kv_heads;
-    live = 0;
+    mr.live = 0;
     if (npg > 0) {
       const int64_t u = (int64_t)b * mp.num_kv_heads + g;
       const int64_t p_s = (int64_t)mp.pfx[b] * mp.num_kv_heads + g * npg;
@@ -225,11 +329,11 @@ __global__ __launch_bounds__(64 * kMergeWaves) void lse_merge_kernel(const Merge
       const int64_t W = mp.num_wg;
       const int64_t w_s = ((p_s + 1) * W - 1) / TP;
       const int64_t w_e = ((p_e + 1) * W - 1) / TP;
-      live = (int)(w_e - w_s + 1);
-      prow0 = (w_s + u) * mp.slot_rows + R;
-      prow_step = mp.slot_rows;
-      w_first = w_s;
-      TPs = TP;
+      mr.live = (int)(w_e - w_s + 1);
+      mr.prow0 = (w_s + u) * mp.slot_rows + R;
+      mr.step = mp.slot_rows;
+      mr.w_first = w_s;
+      mr.TPs = TP;
     }
   } else if (mp.seq_lens) {
     int b, t0, n;
@@ -253,75 +357,15 @@ __global__ __launch_bounds__(64 * kMergeWaves) void lse_merge_kernel(const Merge
     const int i = (int)(t - t0);
     const int L = max(0, min(mp.seq_lens[b], mp.cap_tokens));
     const int c = mp.causal ? min(L, max(0, L - n + i + 1)) : L;
-    live = min(mp.num_splits, (c + mp.split_tokens - 1) / mp.split_tokens);
+    mr.live = min(mp.num_splits, (c + mp.split_tokens - 1) / mp.split_tokens);
   }
-
-  // LSE of live slot s, or -inf for a slot nobody wrote: with fewer pages than
-  // workgroups (stream schedule) some owner workgroups in [w_s, w_e] own no page
-  auto slot_lse = [&](int s) -> float {
-    if (s >= live) return -INFINITY;
-    if (mp.stream) {
-      const int64_t W = mp.num_wg, w = w_first + s;
-      if ((w + 1) * TPs / W == w * TPs / W) return -INFINITY;
-    }
-    return mp.lse_part[prow0 + s * prow_step];
-  };
-  float M = -INFINITY;
-  for (int s0 = 0; s0 < live; s0 += 64) M = fmaxf(M, slot_lse(s0 + lane));
-  M = wave_max(M);
-
-  float acc[8];
-#pragma unroll
-  for (int k = 0; k < 8; ++k) acc[k] = 0.f;
-  float wlane = 0.f;
-  if (M != -INFINITY) {
-    for (int s0 = 0; s0 < live; s0 += 64) {
-      const int s = s0 + lane;
-      const float ls = slot_lse(s);
-      const float w = (ls == -INFINITY) ? 0.f : __expf(ls - M);
-      wlane += w;
-      const int nsp = min(64, live - s0);
-#pragma unroll 4
-      for (int j = wv; j < nsp; j += kMergeWaves) {
-        const float wj = readlane_f(w, j);
-        const float* src = mp.o_part + (prow0 + (int64_t)(s0 + j) * prow_step) * dv;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const int d = lane + 64 * k;
-          if (d < dv) {
-            const float v = src[d];
-            acc[k] = (wj > 0.f) ? fmaf(wj, v, acc[k]) : acc[k];
-          }
-        }
-      }
-    }
-  }
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const int d = lane + 64 * k;
-    if (d < dv) s_acc[wv][d] = acc[k];
-  }
-  __syncthreads();
-  const float wsum = wave_sum(wlane);
-  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-  for (int d = threadIdx.x; d < dv; d += 64 * kMergeWaves) {
-    float v = 0.f;
-#pragma unroll
-    for (int w2 = 0; w2 < kMergeWaves; ++w2) v += s_acc[w2][d];
-    v *= inv;
-    const int64_t oi = t * mp.o_st + (int64_t)h * mp.o_sh + d;
-    if (mp.o_dtype == PKV_DTYPE_BF16) {
-      ((__bf16*)mp.out)[oi] = (__bf16)v;
-    } else {
-      ((float*)mp.out)[oi] = v;
-    }
-  }
-  if (mp.lse_out && threadIdx.x == 0) mp.lse_out[r] = (M == -INFINITY) ? -INFINITY : M + __logf(wsum);
+  if (mp.vec4) merge_row<4>(mp, mr, r, s_red);
+  else merge_row<1>(mp, mr, r, s_red);
 }
 
 hipError_t launch_merge(const MergeParams& mp, hipStream_t s) {
   if (mp.num_rows == 0) return hipSuccess;
-  hipLaunchKernelGGL(lse_merge_kernel, dim3((unsigned)mp.num_rows), dim3(64 * kMergeWaves), 0, s, mp);
+  hipLaunchKernelGGL(lse_merge_kernel, dim3((unsigned)mp.num_rows), dim3(kMergeThreads), 0, s, mp);
   return hipGetLastError();
 }
 

@@ -80,6 +80,9 @@ struct KParams {
   // per-request page prefix written to ws_pfx for the reducer
   int32_t stream, num_wg, slot_rows, page_list_cap;
   int32_t* ws_pfx;
+  // balanced schedule with the fused reducer: one zero-at-rest counter per
+  // (request, KV head); null selects the separate reducer kernel
+  int32_t* counters;
 };
 
 struct LaunchShape {
@@ -109,6 +112,8 @@ struct MergeParams {
   int32_t stream, num_wg, num_kv_heads, group, slot_rows, page_size;
   const int32_t* pfx;
   int32_t* err_word;
+  // 1: head_dim_v % 4 == 0 and o_part 16-byte aligned (partial rows read 16 bytes at a time)
+  int32_t vec4;
 };
 hipError_t launch_merge(const MergeParams& mp, hipStream_t s);
 

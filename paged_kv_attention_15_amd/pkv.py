@@ -49,7 +49,7 @@ class PkvArgs(C.Structure):
         ("q", C.c_void_p), ("k_pages", C.c_void_p), ("v_pages", C.c_void_p),
         ("block_tables", C.c_void_p), ("seq_lens", C.c_void_p), ("q_indptr", C.c_void_p),
         ("out", C.c_void_p), ("lse_out", C.c_void_p), ("err_word", C.c_void_p),
-        ("k_scale_dev", C.c_void_p), ("v_scale_dev", C.c_void_p),
+        ("k_scale_dev", C.c_void_p), ("v_scale_dev", C.c_void_p), ("merge_counters", C.c_void_p),
         ("q_stride_tok", C.c_int64), ("q_stride_head", C.c_int64),
         ("o_stride_tok", C.c_int64), ("o_stride_head", C.c_int64),
         ("k_stride_page", C.c_int64), ("k_stride_head", C.c_int64), ("k_stride_tok", C.c_int64),
@@ -63,7 +63,8 @@ class PkvPlanInfo(C.Structure):
     _fields_ = [
         ("kernel", C.c_int32), ("num_splits", C.c_int32), ("pages_per_split", C.c_int32),
         ("grid_x", C.c_int32), ("grid_y", C.c_int32), ("grid_z", C.c_int32),
-        ("block_threads", C.c_int32), ("schedule", C.c_int32), ("workspace_bytes", C.c_size_t),
+        ("block_threads", C.c_int32), ("schedule", C.c_int32), ("counter_words", C.c_int32),
+        ("fused_merge", C.c_int32), ("workspace_bytes", C.c_size_t),
     ]
 
 
@@ -203,8 +204,12 @@ def _to_device(arr, device):
 
 
 def upload(prob, device="cuda", with_lse: bool = True, with_err: bool = True, num_splits: Optional[int] = None,
-           device_scales: bool = False, kernel: Optional[str] = None) -> DeviceProblem:
-    """Copy a workloads.Problem to `device` and fill pkv_args for it."""
+           device_scales: bool = False, kernel: Optional[str] = None,
+           merge_counters: bool = False) -> DeviceProblem:
+    """Copy a workloads.Problem to `device` and fill pkv_args for it.
+
+    merge_counters: give the balanced decode schedule a zeroed counter buffer
+    (the in-kernel reducer); other plans ignore it."""
     torch = _torch()
     t = {}
     t["q"] = _to_device(prob.q, device)
@@ -227,6 +232,11 @@ def upload(prob, device="cuda", with_lse: bool = True, with_err: bool = True, nu
     if kernel is not None:
         a.kernel_hint = KERNEL_IDS[kernel]
     is_ctx = not prob.is_decode
+    if merge_counters:
+        words = pkv_plan(a, is_ctx).counter_words
+        if words > 0:
+            t["counters"] = torch.zeros(words, dtype=torch.int32, device=device)
+            a.merge_counters = t["counters"].data_ptr()
     ws_bytes = pkv_workspace_bytes(a, is_ctx)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=device) if ws_bytes > 0 else None
     return DeviceProblem(args=a, is_context=is_ctx, tensors=t, workspace=ws, workspace_bytes=ws_bytes)

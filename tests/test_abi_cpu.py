@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
     assert set(declared) == set(pkv.EXPORTED)
     for name in declared:
         assert hasattr(lib, name), name
-    assert pkv.pkv_abi_version() == 1
+    assert pkv.pkv_abi_version() == 2
 
 
 def test_ctypes_mirror_matches_c_layout(tmp_path):
@@ -181,6 +181,42 @@ def test_balanced_schedule_chosen_when_units_cannot_fill_the_cus():
     a.batch = 32
     a.num_splits = 0
     assert pkv.pkv_plan(a, False, 256).schedule == 0  # 256 units fill 256 CUs: one partition each
+
+
+def test_fused_merge_plan_needs_counters_and_a_ring_kernel():
+    a = _args_for(_fake(seq_lens=[5000, 300]))
+    a.q = a.k_pages = a.v_pages = a.out = 0x1000
+    info = pkv.pkv_plan(a, False, 256)
+    assert info.schedule == 1 and info.counter_words == 2 * 8 and info.fused_merge == 0
+    a.merge_counters = 0x2000
+    info = pkv.pkv_plan(a, False, 256)
+    assert info.fused_merge == (1 if info.kernel >= pkv.KERNEL_IDS["dma_gqa_bf16"] else 0)
+    a.kernel_hint = pkv.KERNEL_IDS["dma_gqa_fp8_n2"] if a.kv_dtype == pkv.PKV_DTYPE_FP8_E4M3 \
+        else pkv.KERNEL_IDS["dma_gqa_bf16_n2"]
+    assert pkv.pkv_plan(a, False, 256).fused_merge == 1
+    a.kernel_hint = pkv.KERNEL_IDS["gqa_bf16"] if a.kv_dtype == pkv.PKV_DTYPE_BF16 else pkv.KERNEL_IDS["gqa_fp8"]
+    assert pkv.pkv_plan(a, False, 256).fused_merge == 0  # register-staged kernels keep the separate reducer
+    a.kernel_hint = 0
+    a.num_splits = 5  # per-unit partitions: counters are not used
+    info = pkv.pkv_plan(a, False, 256)
+    assert info.schedule == 0 and info.fused_merge == 0 and info.counter_words == 0
+    a.num_splits = 0
+    a.merge_counters = 0x2002  # misaligned
+    assert pkv.pkv_plan(a, False, 256, check=False).status == pkv.PKV_ERR_INVALID_ARG
+
+
+def test_fused_merge_kept_for_wide_tables():
+    # the in-kernel reducer keeps one LDS word per owner of a unit, at most
+    # min(workgroups, table width): a wide table still fits the 32 KiB ring
+    a = _args_for(_fake(seq_lens=[40, 70], q_lens=[2, 2], num_qo_heads=64, kv_dtype=W.E4M3, page_size=64))
+    a.q = a.k_pages = a.v_pages = a.out = 0x1000
+    a.merge_counters = 0x2000
+    a.num_splits = -1
+    a.kernel_hint = pkv.KERNEL_IDS["dma_gqa_fp8_n2"]
+    assert pkv.pkv_plan(a, False, 256).fused_merge == 1
+    a.max_pages_per_seq = a.table_stride = 4000
+    info = pkv.pkv_plan(a, False, 256)
+    assert info.schedule == 1 and info.fused_merge == 1
 
 
 def test_balanced_schedule_rejected_for_non_gqa_families():

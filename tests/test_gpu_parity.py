@@ -95,6 +95,59 @@ def test_balanced_schedule_speculative_rows_and_empty_request():
     compare(prob, run_gpu(prob, num_splits=-1), expect_err=pkv.PKV_DEVERR_SEQ_LT_QLEN)
 
 
+# ----------------------------------------------------------------- balanced schedule with the in-kernel reducer
+
+def _fused_runs(prob, kernel=None, runs=3, expect_err=0, pairs=None):
+    """Run the balanced schedule with merge counters `runs` times on one counter
+    buffer: every run must match the oracle and leave the counters at zero."""
+    dp = pkv.upload(prob, "cuda", num_splits=-1, kernel=kernel, merge_counters=True)
+    plan = pkv.pkv_plan(dp.args)
+    assert plan.schedule == 1 and plan.fused_merge == 1, (plan.schedule, plan.fused_merge)
+    assert dp.tensors["counters"].numel() == prob.batch * prob.num_kv_heads
+    for r in range(runs):
+        dp.tensors["out"].fill_(float("nan"))
+        dp.tensors["lse"].fill_(float("nan"))
+        dp.run()
+        torch.cuda.synchronize()
+        compare(prob, dp, pairs=pairs, label=f"{kernel}/fused run {r}", expect_err=expect_err)
+        assert int(dp.tensors["counters"].abs().sum().item()) == 0, "counters not reset"
+    return dp
+
+
+@pytest.mark.parametrize("kernel,kv", [("dma_gqa_fp8_n2", W.E4M3), ("dma_gqa_bf16_n2", W.BF16),
+                                       ("dma_gqa_fp8_n1", W.E4M3), ("dma_gqa_fp8", W.E4M3),
+                                       ("dma_gqa_bf16", W.BF16)])
+def test_fused_merge_kernel_families(kernel, kv):
+    P = 64 if kv == W.E4M3 else 32
+    prob = _gqa([1, 31, 64, 65, 700, 1300], hq=64 if kv == W.E4M3 else 32, hkv=8, P=P, kv=kv)
+    say(f"case {kernel} fused merge")
+    _fused_runs(prob, kernel)
+
+
+def test_fused_merge_one_long_request():
+    prob = _gqa([8000], hq=32, hkv=8, P=32, kv=W.E4M3)
+    say("case fused one long request")
+    _fused_runs(prob, "dma_gqa_fp8_n2")
+
+
+def test_fused_merge_fewer_pages_than_workgroups():
+    prob = _gqa([1, 2, 40], hq=16, hkv=2, P=16, kv=W.E4M3)
+    say("case fused fewer pages than workgroups")
+    _fused_runs(prob, "dma_gqa_fp8_n2")
+
+
+def test_fused_merge_speculative_rows_and_empty_request():
+    prob = _gqa([3, 0, 300, 77], q_lens=[3, 3, 3, 3], hq=16, hkv=4, kv=W.E4M3, P=64)
+    say("case fused speculative rows + empty request")
+    _fused_runs(prob, "dma_gqa_fp8_n2", expect_err=pkv.PKV_DEVERR_SEQ_LT_QLEN)
+
+
+def test_fused_merge_full_size_fp8():
+    prob = W.gqa_fp8_b16_ragged()
+    say(f"case {prob.name} fused merge (sampled)")
+    _fused_runs(prob, None, runs=2, pairs=sample_pairs(prob, 96))
+
+
 @pytest.mark.parametrize("q_len,kernel", [(1, None), (2, None), (1, "dma_mla_bf16"), (2, "dma_mla_bf16"),
                                           (1, "mla_bf16"), (1, "m32_mla_bf16"), (2, "m32_mla_bf16")])
 def test_mla_small(q_len, kernel):
