@@ -82,9 +82,9 @@ def time_calls(dp, steps: int, warmup: int):
 def measure(prob, steps: int, warmup: int, num_splits=None):
     from paged_kv_attention_15_amd import pkv
 
-    # merge counters (zeroed once, like the workspace, outside the timed calls):
-    # the balanced decode schedule then reduces inside the attention kernel
-    dp = pkv.upload(prob, "cuda", with_lse=False, with_err=False, num_splits=num_splits, merge_counters=True)
+    # the separate reducer kernel: measured faster than the in-kernel reducer
+    # (merge_counters) on the ragged e4m3 workload
+    dp = pkv.upload(prob, "cuda", with_lse=False, with_err=False, num_splits=num_splits)
     info = pkv.pkv_plan(dp.args, dp.is_context)
     wall, ev_mean = time_calls(dp, steps, warmup)
     return dp, info, wall, ev_mean

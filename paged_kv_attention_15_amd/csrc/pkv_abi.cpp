@@ -235,6 +235,21 @@ bool kernel_shape(int32_t k, pkv::MfmaShape* s) {
   return pkv::mfma_shape(k, s) || pkv::dma_shape(k, s) || pkv::m32_shape(k, s);
 }
 
+// Balanced schedule: the fixed cost of starting a segment (page list and
+// query loads, pipeline fill and drain), charged as placeholder pages of this
+// request's page size.  48 KiB of K and V per segment start was the best of
+// 0, 16, 32, 48 and 64 KiB on MI355X for the ragged e4m3 decode (16 requests,
+// 8 KV heads, 64-token pages): 63.7, 61.5, 60.6, 59.3 and 59.6 us per call.
+#ifndef PKV_SEG_COST_BYTES
+#define PKV_SEG_COST_BYTES 49152
+#endif
+int32_t seg_cost_pages(const pkv_args* a) {
+  const int eb = a->kv_dtype == PKV_DTYPE_FP8_E4M3 ? 1 : (a->kv_dtype == PKV_DTYPE_BF16 ? 2 : 4);
+  const int64_t page_bytes =
+      (int64_t)a->page_size * (a->head_dim_qk + (a->v_shares_k ? 0 : a->head_dim_v)) * eb;
+  return (int32_t)std::min<int64_t>(64, (PKV_SEG_COST_BYTES + page_bytes / 2) / std::max<int64_t>(page_bytes, 1));
+}
+
 int32_t choose_kernel(const pkv_args* a, bool is_context) {
   if (!mfma_eligible(a)) return pkv::KERNEL_GENERIC;
   const bool fp8 = a->kv_dtype == PKV_DTYPE_FP8_E4M3;
@@ -446,6 +461,7 @@ pkv_status run(const pkv_args* a, bool is_context, void* ws, size_t ws_bytes, vo
   p.page_list_cap = plan.pages_per_split;
   if (plan.schedule == 1) {
     p.stream = 1;
+    p.seg_cost = seg_cost_pages(a);
     p.num_wg = plan.grid_x;
     p.slot_rows = a->q_len * G;
     p.page_list_cap = a->max_pages_per_seq;
@@ -504,6 +520,7 @@ pkv_status run(const pkv_args* a, bool is_context, void* ws, size_t ws_bytes, vo
       mp.slot_rows = p.slot_rows;
       mp.page_size = a->page_size;
       mp.pfx = p.ws_pfx;
+      mp.seg_cost = p.seg_cost;
     }
     e = pkv::launch_merge(mp, s);
     if (e != hipSuccess) return fail(PKV_ERR_HIP, "merge launch failed: %s", hipGetErrorString(e));

@@ -544,7 +544,7 @@ __global__ __launch_bounds__(C::NTHR) void attn_dma_kernel(const KParams p) {
 struct StreamUnit {
   int b, g, u;
   int64_t p_s, npg, TP, W;
-  // owner workgroup of global page q (the w with w*TP/W <= q < (w+1)*TP/W)
+  // owner workgroup of virtual page q (the w with w*TP/W <= q < (w+1)*TP/W; TP = virtual total)
   __device__ int64_t owner(int64_t q) const { return ((q + 1) * W - 1) / TP; }
   // number of workgroups that own pages of the unit: all of [owner(p_s), owner(p_e)]
   // when every workgroup owns a page (TP >= W), else one per page
@@ -682,8 +682,13 @@ __global__ __launch_bounds__(C::NTHR) void attn_dma_stream_kernel(const KParams 
   }
   __syncthreads();
   const int Hkv = p.num_kv_heads;
-  const int64_t TP = (int64_t)s_pfx[B] * Hkv;
-  const int64_t W = gridDim.x;
+  StreamGeom sg;
+  sg.pfx = s_pfx;
+  sg.Hkv = Hkv;
+  sg.A = p.seg_cost;
+  sg.TV = sg.request_start(B);
+  sg.W = gridDim.x;
+  const int64_t W = sg.W;
   const int64_t w = blockIdx.x;
   const bool fused = p.counters != nullptr;
   if (!fused && w == 0)
@@ -708,36 +713,37 @@ __global__ __launch_bounds__(C::NTHR) void attn_dma_stream_kernel(const KParams 
       }
     }
   }
-  int64_t pos = w * TP / W;
-  const int64_t end = (w + 1) * TP / W;
+  int64_t pos = w * sg.TV / W;
+  const int64_t end = (w + 1) * sg.TV / W;
   while (pos < end) {
-    int lo = 0, hi = B - 1;
+    int lo = 0, hi = B - 1;  // the last request whose units start at or before pos
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
-      if ((int64_t)s_pfx[mid] * Hkv <= pos) lo = mid; else hi = mid - 1;
+      if (sg.request_start(mid) <= pos) lo = mid; else hi = mid - 1;
     }
     const int b = lo;
-    const int64_t npg = s_pfx[b + 1] - s_pfx[b];
-    const int64_t base = (int64_t)s_pfx[b] * Hkv;
-    const int g = (int)((pos - base) / npg);
-    const int64_t u_start = base + g * npg;
-    const int64_t seg_end = min(end, u_start + npg);
-    const int a = (int)(pos - u_start), e = (int)(seg_end - u_start);
-    const bool whole = fused && a == 0 && e == npg;  // sole owner: final rows straight from the epilogue
-    dma_block<C>(p, smem, s_pages, b, g, 0, a * p.page_size, e * p.page_size, (int)(w + b * Hkv + g), a == 0,
-                 whole);
-    if (fused && !whole) {
-      StreamUnit su;
-      su.b = b;
-      su.g = g;
-      su.u = b * Hkv + g;
-      su.p_s = u_start;
-      su.npg = npg;
-      su.TP = TP;
-      su.W = W;
-      stream_arrive<C>(p, smem, s_flag, su);
+    const int64_t npg = sg.npg(b);
+    const int g = (int)((pos - sg.request_start(b)) / (npg + sg.A));
+    const int64_t rs = sg.real(b, g);
+    const int64_t seg_lo = max(pos, rs), seg_hi = min(end, rs + npg);
+    if (seg_lo < seg_hi) {
+      const int a = (int)(seg_lo - rs), e = (int)(seg_hi - rs);
+      const bool whole = fused && a == 0 && e == npg;  // sole owner: final rows straight from the epilogue
+      dma_block<C>(p, smem, s_pages, b, g, 0, a * p.page_size, e * p.page_size, (int)(w + b * Hkv + g), a == 0,
+                   whole);
+      if (fused && !whole) {
+        StreamUnit su;
+        su.b = b;
+        su.g = g;
+        su.u = b * Hkv + g;
+        su.p_s = rs;
+        su.npg = npg;
+        su.TP = sg.TV;
+        su.W = W;
+        stream_arrive<C>(p, smem, s_flag, su);
+      }
     }
-    pos = seg_end;
+    pos = rs + npg;
   }
 }
 

@@ -209,7 +209,7 @@ __device__ __forceinline__ void merge_row(const MergeParams& mp, const MergeRow&
   const int64_t t = r / mp.num_qo_heads;
   const int h = (int)(r % mp.num_qo_heads);
   auto slot_lse = [&](int s) -> float {
-    if (mr.TPs > 0) {  // balanced schedule: an owner range may hold workgroups without pages
+    if (mr.TPs > 0) {  // balanced schedule: an owner range may hold workgroups with an empty range
       const int64_t w = mr.w_first + s;
       if ((w + 1) * mr.TPs / mr.num_wg == w * mr.TPs / mr.num_wg) return -INFINITY;
     }
@@ -319,21 +319,24 @@ __global__ __launch_bounds__(kMergeThreads) void lse_merge_kernel(const MergePar
       if (L0 > mp.cap_tokens) flag_error(mp.err_word, PKV_DEVERR_SEQ_GT_TABLE);
       if (L0 < mp.q_len) flag_error(mp.err_word, PKV_DEVERR_SEQ_LT_QLEN);
     }
-    const int64_t npg = mp.pfx[b + 1] - mp.pfx[b];
-    const int64_t TP = (int64_t)mp.pfx[mp.batch] * mp.num_kv_heads;
+    StreamGeom sg;
+    sg.pfx = mp.pfx;
+    sg.Hkv = mp.num_kv_heads;
+    sg.A = mp.seg_cost;
+    sg.TV = sg.request_start(mp.batch);
+    sg.W = mp.num_wg;
+    const int64_t npg = sg.npg(b);
     mr.live = 0;
     if (npg > 0) {
       const int64_t u = (int64_t)b * mp.num_kv_heads + g;
-      const int64_t p_s = (int64_t)mp.pfx[b] * mp.num_kv_heads + g * npg;
-      const int64_t p_e = p_s + npg - 1;
-      const int64_t W = mp.num_wg;
-      const int64_t w_s = ((p_s + 1) * W - 1) / TP;
-      const int64_t w_e = ((p_e + 1) * W - 1) / TP;
+      const int64_t rs = sg.real(b, g);
+      const int64_t w_s = sg.owner(rs);
+      const int64_t w_e = sg.owner(rs + npg - 1);
       mr.live = (int)(w_e - w_s + 1);
       mr.prow0 = (w_s + u) * mp.slot_rows + R;
       mr.step = mp.slot_rows;
       mr.w_first = w_s;
-      mr.TPs = TP;
+      mr.TPs = sg.TV;
     }
   } else if (mp.seq_lens) {
     int b, t0, n;

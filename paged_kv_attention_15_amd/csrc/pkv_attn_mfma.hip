@@ -490,14 +490,13 @@ __global__ __launch_bounds__(C::NTHR) void attn_mfma_kernel(const KParams p) {
 }
 
 // Balanced decode schedule.  The page streams of all (request, KV head) units,
-// laid end to end (unit u = b*Hkv + g owns ceil(L_b/P) pages), are cut into
-// gridDim.x equal page ranges, one per workgroup:  workgroup w owns global
-// pages [w*TP/W, (w+1)*TP/W).  Every maximal piece of one unit inside one
-// workgroup's range is a segment; segment (w, u) writes its partial rows to
-// workspace slot w + u, which is unique because moving from one segment to
-// the next increases w or u.  The reducer recovers a row's segments from the
-// same arithmetic: pages p of unit u belong to workgroups
-// owner(p) = ((p + 1)*W - 1) / TP.
+// laid end to end in the virtual page space of StreamGeom (unit u = b*Hkv + g
+// owns ceil(L_b/P) pages after A placeholder pages), are cut into gridDim.x
+// equal ranges, one per workgroup.  Every maximal piece of one unit's pages
+// inside one workgroup's range is a segment; segment (w, u) writes its
+// partial rows to workspace slot w + u, which is unique because moving from
+// one segment to the next increases w or u.  The reducer recovers a row's
+// segments from the same arithmetic (StreamGeom::owner).
 template <class C>
 __global__ __launch_bounds__(C::NTHR) void attn_mfma_stream_kernel(const KParams p) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -528,29 +527,35 @@ __global__ __launch_bounds__(C::NTHR) void attn_mfma_stream_kernel(const KParams
   }
   __syncthreads();
   const int Hkv = p.num_kv_heads;
-  const int64_t TP = (int64_t)s_pfx[B] * Hkv;
-  const int64_t W = gridDim.x;
+  StreamGeom sg;
+  sg.pfx = s_pfx;
+  sg.Hkv = Hkv;
+  sg.A = p.seg_cost;
+  sg.TV = sg.request_start(B);
+  sg.W = gridDim.x;
+  const int64_t W = sg.W;
   const int64_t w = blockIdx.x;
   if (w == 0)
     for (int i = tid; i <= B; i += C::NTHR) p.ws_pfx[i] = s_pfx[i];
-  int64_t pos = w * TP / W;
-  const int64_t end = (w + 1) * TP / W;
+  int64_t pos = w * sg.TV / W;
+  const int64_t end = (w + 1) * sg.TV / W;
   while (pos < end) {
-    // request b: s_pfx[b]*Hkv <= pos < s_pfx[b+1]*Hkv
-    int lo = 0, hi = B - 1;
+    int lo = 0, hi = B - 1;  // the last request whose units start at or before pos
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
-      if ((int64_t)s_pfx[mid] * Hkv <= pos) lo = mid; else hi = mid - 1;
+      if (sg.request_start(mid) <= pos) lo = mid; else hi = mid - 1;
     }
     const int b = lo;
-    const int64_t npg = s_pfx[b + 1] - s_pfx[b];
-    const int64_t base = (int64_t)s_pfx[b] * Hkv;
-    const int g = (int)((pos - base) / npg);
-    const int64_t u_start = base + g * npg;
-    const int64_t seg_end = min(end, u_start + npg);
-    const int a = (int)(pos - u_start), e = (int)(seg_end - u_start);
-    attend_block<C>(p, smem, s_pages, b, g, 0, a * p.page_size, e * p.page_size, (int)(w + b * Hkv + g), a == 0);
-    pos = seg_end;
+    const int64_t npg = sg.npg(b);
+    const int g = (int)((pos - sg.request_start(b)) / (npg + sg.A));
+    const int64_t rs = sg.real(b, g);
+    const int64_t seg_lo = max(pos, rs), seg_hi = min(end, rs + npg);
+    if (seg_lo < seg_hi) {
+      const int a = (int)(seg_lo - rs), e = (int)(seg_hi - rs);
+      attend_block<C>(p, smem, s_pages, b, g, 0, a * p.page_size, e * p.page_size, (int)(w + b * Hkv + g),
+                      a == 0);
+    }
+    pos = rs + npg;
   }
 }
 

@@ -126,6 +126,29 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// ---------------------------------------------------------------- balanced schedule geometry
+// The page streams of all (request, KV head) units are laid end to end in a
+// virtual page space in which every unit u = b*Hkv + g is preceded by A
+// placeholder pages standing for the fixed cost of starting a segment (page
+// list, query rows, pipeline fill): unit u occupies [start(u), start(u) + A +
+// npg_b) and its real pages begin at real(u) = start(u) + A.  Workgroup w owns
+// the virtual range [w*TV/W, (w+1)*TV/W); the real pages of one unit inside
+// it form a segment, so a workgroup that has to start several segments gets
+// correspondingly fewer pages.  Page v belongs to owner(v) = ((v+1)*W - 1)/TV;
+// the owners of a unit are owner(real(u)) .. owner(real(u) + npg - 1), every
+// one of them holding at least one of its pages when its range is not empty.
+// `pfx` is the page prefix over requests (pfx[b] = pages of requests < b).
+struct StreamGeom {
+  const int32_t* pfx;
+  int32_t Hkv, A;
+  int64_t TV, W;
+  __device__ int64_t request_start(int b) const { return (int64_t)Hkv * (pfx[b] + (int64_t)A * b); }
+  __device__ int64_t npg(int b) const { return pfx[b + 1] - pfx[b]; }
+  __device__ int64_t real(int b, int g) const { return request_start(b) + g * (npg(b) + A) + A; }
+  __device__ int64_t owner(int64_t v) const { return ((v + 1) * W - 1) / TV; }
+  __device__ bool owns_any(int64_t w) const { return (w + 1) * TV / W > w * TV / W; }
+};
+
 // ---------------------------------------------------------------- error word
 __device__ __forceinline__ void flag_error(int32_t* err_word, int32_t bits) {
   if (err_word) atomicOr(err_word, bits);

@@ -79,6 +79,7 @@ struct KParams {
   // indexed [slot][packed row] with slot_rows packed rows per slot, and the
   // per-request page prefix written to ws_pfx for the reducer
   int32_t stream, num_wg, slot_rows, page_list_cap;
+  int32_t seg_cost, pad2;  // placeholder pages charged per segment start
   int32_t* ws_pfx;
   // balanced schedule with the fused reducer: one zero-at-rest counter per
   // (request, KV head); null selects the separate reducer kernel
@@ -109,7 +110,7 @@ struct MergeParams {
   int32_t batch, q_len, causal, is_context;
   int32_t split_tokens, cap_tokens, max_q_len, total_q;
   // balanced decode schedule: row (t, h) of KV head g reads slots w + b*Hkv + g
-  int32_t stream, num_wg, num_kv_heads, group, slot_rows, page_size;
+  int32_t stream, num_wg, num_kv_heads, group, slot_rows, page_size, seg_cost;
   const int32_t* pfx;
   int32_t* err_word;
   // 1: head_dim_v % 4 == 0 and o_part 16-byte aligned (partial rows read 16 bytes at a time)
