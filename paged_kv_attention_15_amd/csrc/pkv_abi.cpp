@@ -201,10 +201,16 @@ bool kernel_supports(int32_t k, const pkv_args* a, bool is_context) {
     case pkv::KERNEL_M32_CTX_R2:
     case pkv::KERNEL_M32_CTX_R2W8:
     case pkv::KERNEL_M32_CTX_PP:
+    case pkv::KERNEL_M32_CTX_IW:
       return d128 && !fp8 && a->page_size >= 4;
     case pkv::KERNEL_M32_MLA_BF16: return mla && !fp8 && a->page_size % 32 == 0;
   }
   return false;
+}
+
+// the 32x32 MFMA family (pkv_attn_m32.hip): page lists held in registers
+bool is_m32(int32_t k) {
+  return (k >= pkv::KERNEL_M32_CTX_BF16 && k <= pkv::KERNEL_M32_CTX_PP) || k == pkv::KERNEL_M32_CTX_IW;
 }
 
 bool is_gqa_family(int32_t k) {
@@ -367,7 +373,7 @@ pkv_status make_plan(const pkv_args* a, bool is_context, int num_cus, pkv_plan_i
     // the partition's page list sits in LDS after the KV stages: keep the total within 160 KiB
     const int64_t lds_room = (int64_t)(160 * 1024 - shp.lds_static) / 4 - 8;
     int64_t cap_pages = std::min<int64_t>(kMaxPagesPerSplit, lds_room);
-    if (kernel >= pkv::KERNEL_M32_CTX_BF16 && kernel <= pkv::KERNEL_M32_CTX_PP)
+    if (is_m32(kernel))
       cap_pages = std::min<int64_t>(cap_pages, pkv::kM32MaxPages);
     if (cap_pages < 1) return fail(PKV_ERR_UNSUPPORTED, "no LDS left for the page list");
     if (pps > cap_pages) pps = cap_pages;
@@ -480,11 +486,10 @@ pkv_status run(const pkv_args* a, bool is_context, void* ws, size_t ws_bytes, vo
     p.ws_lse = p.ws_o + (size_t)plan.num_splits * p.rows_total * a->head_dim_v;
   }
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  hipError_t e = plan.kernel == pkv::KERNEL_GENERIC          ? pkv::launch_generic(p, s)
-                 : plan.kernel >= pkv::KERNEL_DMA_GQA_FP8_N2  ? pkv::launch_dma(plan.kernel, p, s)
-                 : plan.kernel >= pkv::KERNEL_M32_CTX_BF16    ? pkv::launch_m32(plan.kernel, p, s)
-                 : plan.kernel >= pkv::KERNEL_DMA_GQA_BF16    ? pkv::launch_dma(plan.kernel, p, s)
-                                                              : pkv::launch_mfma(plan.kernel, p, s);
+  hipError_t e = plan.kernel == pkv::KERNEL_GENERIC         ? pkv::launch_generic(p, s)
+                 : is_m32(plan.kernel)                       ? pkv::launch_m32(plan.kernel, p, s)
+                 : plan.kernel >= pkv::KERNEL_DMA_GQA_BF16   ? pkv::launch_dma(plan.kernel, p, s)
+                                                             : pkv::launch_mfma(plan.kernel, p, s);
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "attention launch failed: %s", hipGetErrorString(e));
   if (plan.num_splits > 1 && !plan.fused_merge) {
     pkv::MergeParams mp;

@@ -23,6 +23,8 @@
 // Split-KV partials (normalized O and natural-log LSE per partition, merged
 // by the separate reducer) follow the PR #4557 page's Split-KV description.
 
+#include <type_traits>
+
 #include "pkv_device.h"
 #include "pkv_internal.h"
 #include "pkv_ring.h"
@@ -36,8 +38,13 @@ __device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
 }
 
 template <int DQK_, int DV_, bool VSHARE_, int RB_, int NW_, int KB_, int NS_, int OCC_ = 1, bool PREF_ = true,
-          int DVS_ = 1, bool PP_ = false>
+          int DVS_ = 1, bool PP_ = false, bool IW_ = false>
 struct M32Cfg {
+  // IW (interleaved within the wave): the S^T product of block j+1 and the
+  // softmax of block j are one scheduling region, its MFMAs spread among the
+  // softmax's VALU instructions, so each wave overlaps its own matrix and
+  // vector work; the O rescale and the PV product of block j follow
+  static constexpr bool IW = IW_;
   // PP (ping-pong): waves w and w + NW/2 share a SIMD (measured on gfx950);
   // the second half runs one phase behind the first, with a workgroup barrier
   // between phases, so that on every SIMD one wave is in its MFMA phase while
@@ -130,6 +137,26 @@ __device__ __forceinline__ void sched_reads_ahead() {
   static_for<0, (PD < STEPS ? PD : STEPS)>([] { __builtin_amdgcn_sched_group_barrier(0x008, M, 0); });
 }
 
+// Instruction-scheduler hint for a product of M MFMAs fed by M LDS reads that
+// shares its basic block with independent VALU work: PD reads first, then
+// per MFMA step the MFMA, V VALU instructions and the read PD steps ahead.
+template <int PD, int M, int V, int I = 0>
+__device__ __forceinline__ void sched_interleave() {
+  if constexpr (I == 0) static_for<0, PD>([] { __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); });
+  if constexpr (I < M) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x402, V, 0);
+    if constexpr (I + PD < M) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    sched_interleave<PD, M, V, I + 1>();
+  }
+}
+
+// VALU instructions placed after each MFMA of an interleaved S^T product
+#ifndef PKV_IW_VALU
+#define PKV_IW_VALU 4
+#endif
+constexpr int kIwValu = PKV_IW_VALU;
+
 // Registers per wave holding the page list (64 pages each); the planner caps a
 // partition of these kernels at 64 * kPageRegs pages
 constexpr int kPageRegs = kM32MaxPages / 64;
@@ -202,7 +229,11 @@ __device__ __forceinline__ void m32_block(const KParams& p, unsigned char* smem,
 
   const float k_scale = p.k_scale_dev ? *p.k_scale_dev : p.k_scale;
   const float v_scale = p.v_scale_dev ? *p.v_scale_dev : p.v_scale;
-  const float sc2 = p.scale * k_scale * kLog2e;
+  const float sc2_raw = p.scale * k_scale * kLog2e;
+  // a negative logit scale is folded into Q (an exact bf16 sign flip), so the
+  // softmax only ever needs the row max of the raw products
+  const float sc2 = fabsf(sc2_raw);
+  const uint32_t q_sign = sc2_raw < 0.f ? 0x80008000u : 0u;
 
   int row_t[C::RB], row_h[C::RB], row_c[C::RB];
   bool row_ok[C::RB];
@@ -218,7 +249,12 @@ __device__ __forceinline__ void m32_block(const KParams& p, unsigned char* smem,
     row_c[rb] = row_ok[rb] ? min(max(c, 0), kv_hi) : 0;
     const __bf16* qrow = (const __bf16*)p.q + row_t[rb] * p.q_st + row_h[rb] * p.q_sh + 8 * h;
 #pragma unroll
-    for (int ks = 0; ks < C::NKS; ++ks) qB[rb][ks] = row_ok[rb] ? *(const bf16x8*)(qrow + 16 * ks) : bf16x8{};
+    for (int ks = 0; ks < C::NKS; ++ks) {
+      const bf16x8 q = row_ok[rb] ? *(const bf16x8*)(qrow + 16 * ks) : bf16x8{};
+      u32x4 qw = __builtin_bit_cast(u32x4, q);
+      qw ^= u32x4{q_sign, q_sign, q_sign, q_sign};
+      qB[rb][ks] = __builtin_bit_cast(bf16x8, qw);
+    }
   }
 
   // visible-key bounds over this wave's rows: blocks below c_lo need no mask,
@@ -230,8 +266,8 @@ __device__ __forceinline__ void m32_block(const KParams& p, unsigned char* smem,
       c_lo = min(c_lo, row_c[rb]);
       c_hi = max(c_hi, row_c[rb]);
     }
-  c_lo = -wave_max_i(-c_lo);
-  c_hi = wave_max_i(c_hi);
+  c_lo = __builtin_amdgcn_readfirstlane(-wave_max_i(-c_lo));  // wave-uniform: scalar branches below
+  c_hi = __builtin_amdgcn_readfirstlane(wave_max_i(c_hi));
 
   // Row sums come from the matrix core: an all-ones A operand against the P^T
   // operand of the PV product sums the bf16 weights actually used for O (every
@@ -414,18 +450,11 @@ __device__ __forceinline__ void m32_block(const KParams& p, unsigned char* smem,
       float w[16];
       float mx;
       if (full) {
-        // scores are acc * sc2: reduce the raw accumulators, scale once
+        // scores are acc * sc2 with sc2 >= 0: reduce the raw accumulators, scale once
         float mr = acc[rb][0];
-        if (sc2 >= 0.f) {
 #pragma unroll
-          for (int e = 1; e < 16; ++e) mr = fmaxf(mr, acc[rb][e]);
-          mr = half_swap_max(mr);
-        } else {
-#pragma unroll
-          for (int e = 1; e < 16; ++e) mr = fminf(mr, acc[rb][e]);
-          mr = half_swap_min(mr);
-        }
-        mx = mr * sc2;
+        for (int e = 1; e < 16; ++e) mr = fmaxf(mr, acc[rb][e]);
+        mx = half_swap_max(mr) * sc2;
       } else {
         mx = -INFINITY;
 #pragma unroll
@@ -457,6 +486,61 @@ __device__ __forceinline__ void m32_block(const KParams& p, unsigned char* smem,
       for (int st = 0; st < 2; ++st) {
         u32x4 wv{pack_bf16x2(w[8 * st + 0], w[8 * st + 1]), pack_bf16x2(w[8 * st + 2], w[8 * st + 3]),
                  pack_bf16x2(w[8 * st + 4], w[8 * st + 5]), pack_bf16x2(w[8 * st + 6], w[8 * st + 7])};
+        pb[rb][st] = __builtin_bit_cast(bf16x8, wv);
+      }
+    }
+  };
+  // The same online softmax in two parts with the O rescale left to the
+  // caller, so that a scheduling region holding the second part has no branch
+  // and no cross-lane operation (the row max needs one).  FULL: no key of the
+  // block is masked for any row of the wave.  Part 1: the row max, the new
+  // reference, alpha and whether any lane moved; part 2: weights and packing.
+  auto softmax_max = [&](auto full_tag, int j, const f32x16 (&acc)[C::RB], float (&w)[C::RB][16],
+                         float (&m_use)[C::RB], float (&alpha)[C::RB], bool (&mv)[C::RB]) {
+    constexpr bool FULL = decltype(full_tag)::value;
+    const int blk_tok = kv_lo + j * 32;
+#pragma unroll
+    for (int rb = 0; rb < C::RB; ++rb) {
+      float mx;
+      if constexpr (FULL) {
+        float mr = acc[rb][0];
+#pragma unroll
+        for (int e = 1; e < 16; ++e) mr = fmaxf(mr, acc[rb][e]);
+        mx = half_swap_max(mr) * sc2;
+      } else {
+        mx = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int tok = blk_tok + 16 * (e >> 3) + 8 * h + (e & 7);
+          w[rb][e] = tok < row_c[rb] ? acc[rb][e] * sc2 : -INFINITY;
+          mx = fmaxf(mx, w[rb][e]);
+        }
+        mx = half_swap_max(mx);
+      }
+      const bool move = mx > m_run[rb] + kLazyMax;  // also true on a row's first visible key
+      const float m_new = move ? mx : m_run[rb];
+      m_use[rb] = (m_new == -INFINITY) ? 0.f : m_new;
+      alpha[rb] = move ? fast_exp2(m_run[rb] - m_use[rb]) : 1.f;
+      mv[rb] = move;
+      m_run[rb] = m_new;
+    }
+  };
+  auto softmax_exp = [&](auto full_tag, const f32x16 (&acc)[C::RB], float (&w)[C::RB][16],
+                         const float (&m_use)[C::RB], bf16x8 (&pb)[C::RB][2]) {
+    constexpr bool FULL = decltype(full_tag)::value;
+#pragma unroll
+    for (int rb = 0; rb < C::RB; ++rb) {
+      if constexpr (FULL) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) w[rb][e] = fast_exp2(fmaf(acc[rb][e], sc2, -m_use[rb]));
+      } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) w[rb][e] = fast_exp2(w[rb][e] - m_use[rb]);
+      }
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        u32x4 wv{pack_bf16x2(w[rb][8 * st + 0], w[rb][8 * st + 1]), pack_bf16x2(w[rb][8 * st + 2], w[rb][8 * st + 3]),
+                 pack_bf16x2(w[rb][8 * st + 4], w[rb][8 * st + 5]), pack_bf16x2(w[rb][8 * st + 6], w[rb][8 * st + 7])};
         pb[rb][st] = __builtin_bit_cast(bf16x8, wv);
       }
     }
@@ -547,9 +631,11 @@ __device__ __forceinline__ void m32_block(const KParams& p, unsigned char* smem,
     if (issue_now && t + C::NS - 1 < n_tiles) issue(t + C::NS - 1, (t + C::NS - 1) % C::NS);
   };
 
-  // prologue: the first NS-1 tiles in flight
+  // prologue: the first NS-1 tiles in flight (NS-2 for IW, whose PV product
+  // trails the barrier of the next tile by one block)
+  constexpr int PRE = C::IW ? C::NS - 2 : C::NS - 1;
 #pragma unroll
-  for (int t = 0; t < C::NS - 1; ++t)
+  for (int t = 0; t < PRE; ++t)
     if (t < n_tiles) issue(t, t);
 
   // Software pipeline over 32-key blocks j.  Step j first issues the LDS reads
@@ -653,6 +739,77 @@ __device__ __forceinline__ void m32_block(const KParams& p, unsigned char* smem,
             ++issued;
           }
         }
+      }
+    }
+  } else if constexpr (C::IW) {
+    // Step j: [block j+1 starts tile t: wait for it and take the barrier]; one
+    // scheduling region with the S^T product of block j+1 (K operands read a
+    // few MFMA steps ahead) and the softmax of block j; the O rescale; the PV
+    // product of block j.  The PV of a tile's last block runs after the next
+    // tile's barrier, so a stage is refilled one barrier later than in the other
+    // paths: the barrier of tile t frees the stage of tile t-2 (every wave has
+    // finished the PV products of tile t-2 by then), which takes tile t+NS-2;
+    // NS-2 tiles are in flight.  Blocks past this wave's last visible key are
+    // skipped (every later block is too); every wave still takes every barrier.
+    static_assert(C::NS >= 3 && C::RB == 1, "IW ring depth, one row block per wave");
+    auto tile_start_iw = [&](int t) {
+      const int after = min(C::NS - 3, n_tiles - 1 - t);  // tiles issued after t
+      if constexpr (C::NS >= 5) {
+        if (after >= 2) wait_loads<2 * C::KPW>();
+        else if (after == 1) wait_loads<C::KPW>();
+        else wait_loads<0>();
+      } else if constexpr (C::NS == 4) {
+        if (after >= 1) wait_loads<C::KPW>();
+        else wait_loads<0>();
+      } else {
+        wait_loads<0>();
+      }
+      ring_barrier();
+    };
+    auto step_iw = [&](int j, f32x16 (&cur)[C::RB], f32x16 (&nxt)[C::RB]) {
+      const bool act = active(j);
+      if (j + 1 < nblk && (j + 1) % C::KB == 0) tile_start_iw((j + 1) / C::KB);
+      {
+        const int u = (j + 1) / C::KB + C::NS - 2;
+        const int part = (j + 1) % C::KB;
+        if (u < n_tiles) issue(u, u % C::NS, part * C::KPW / C::KB, (part + 1) * C::KPW / C::KB);
+      }
+      if (!act) return;
+      const bool nxt_on = j + 1 < nblk && active(j + 1);
+      const bool full = kv_lo + j * 32 + 32 <= c_lo;
+      bf16x8 pb[C::RB][2];
+      float w[C::RB][16], m_use[C::RB], alpha[C::RB];
+      bool mv[C::RB];
+      if (full && nxt_on) {
+        softmax_max(std::true_type{}, j, cur, w, m_use, alpha, mv);
+        __builtin_amdgcn_sched_barrier(0);
+        s_product_ring(j + 1, nxt);
+        softmax_exp(std::true_type{}, cur, w, m_use, pb);
+        // spread the MFMAs of the S^T product over the exponentials
+        sched_interleave<(C::PDK < C::NKS ? C::PDK : C::NKS), C::NKS, kIwValu>();
+      } else if (full) {
+        softmax_max(std::true_type{}, j, cur, w, m_use, alpha, mv);
+        softmax_exp(std::true_type{}, cur, w, m_use, pb);
+      } else {
+        if (nxt_on) s_product_ring(j + 1, nxt);
+        softmax_max(std::false_type{}, j, cur, w, m_use, alpha, mv);
+        softmax_exp(std::false_type{}, cur, w, m_use, pb);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (__builtin_amdgcn_ballot_w64(mv[0]) != 0) {
+        Lsum[0] *= alpha[0];
+#pragma unroll
+        for (int d = 0; d < C::NDB; ++d) O[0][d] *= alpha[0];
+      }
+      pv_product_ring(j, pb);
+    };
+    if (nblk > 0) {
+      tile_start_iw(0);
+      if (C::NS - 2 < n_tiles) issue(C::NS - 2, C::NS - 2, 0, C::KPW / C::KB);
+      if (active(0)) s_product_ring(0, accA);
+      for (int j = 0; j < nblk; j += 2) {
+        step_iw(j, accA, accB);
+        if (j + 1 < nblk) step_iw(j + 1, accB, accA);
       }
     }
   } else if constexpr (C::PREF) {
@@ -774,6 +931,7 @@ using M32CtxR1S3 = M32Cfg<128, 128, false, 1, 4, 1, 3, 3>;  // 128 rows, 48 KiB:
 using M32CtxR2 = M32Cfg<128, 128, false, 2, 4, 1, 4, 2, false>;   // 256 rows, 64 rows per wave, 64 KiB
 using M32CtxR2W8 = M32Cfg<128, 128, false, 2, 8, 2, 4, 2, false>;  // 512 rows, 64 rows per wave, 128 KiB
 using M32CtxPP = M32Cfg<128, 128, false, 1, 8, 2, 4, 2, false, 1, true>;  // 256 rows, ping-pong halves
+using M32CtxIW = M32Cfg<128, 128, false, 1, 8, 2, 4, 2, false, 1, false, true>;  // W8 with in-wave overlap
 
 template <class C>
 static void fill_m32_shape(MfmaShape* s) {
@@ -793,6 +951,7 @@ bool m32_shape(int32_t kernel, MfmaShape* s) {
     case KERNEL_M32_CTX_R2: fill_m32_shape<M32CtxR2>(s); return true;
     case KERNEL_M32_CTX_R2W8: fill_m32_shape<M32CtxR2W8>(s); return true;
     case KERNEL_M32_CTX_PP: fill_m32_shape<M32CtxPP>(s); return true;
+    case KERNEL_M32_CTX_IW: fill_m32_shape<M32CtxIW>(s); return true;
     default: return false;
   }
 }
@@ -822,6 +981,7 @@ hipError_t launch_m32(int32_t kernel, const KParams& p, hipStream_t s) {
     case KERNEL_M32_CTX_R2: return launch_m32_cfg<M32CtxR2>(p, s);
     case KERNEL_M32_CTX_R2W8: return launch_m32_cfg<M32CtxR2W8>(p, s);
     case KERNEL_M32_CTX_PP: return launch_m32_cfg<M32CtxPP>(p, s);
+    case KERNEL_M32_CTX_IW: return launch_m32_cfg<M32CtxIW>(p, s);
     default: return hipErrorInvalidValue;
   }
 }

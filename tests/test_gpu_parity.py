@@ -368,7 +368,7 @@ def test_gqa_kernel_families_match_oracle(kernel, kv, splits):
                                            ("m32_ctx_bf16", 3), ("m32_ctx_w8", None), ("m32_ctx_r1", None),
                                            ("m32_ctx_r1s3", None), ("m32_ctx_r1", 2), ("m32_ctx_r2", None),
                                            ("m32_ctx_r2w8", None), ("m32_ctx_w8", 2), ("m32_ctx_pp", None),
-                                           ("m32_ctx_pp", 3)])
+                                           ("m32_ctx_pp", 3), ("m32_ctx_iw", None), ("m32_ctx_iw", 3)])
 def test_context_kernel_families_match_oracle(kernel, splits):
     prob = W.make_problem(name="ctx-fam", seed=9, batch=3, seq_lens=[70, 5, 333], q_lens=[64, 5, 130],
                           num_qo_heads=16, num_kv_heads=2, head_dim_qk=128, head_dim_v=128, page_size=16,
@@ -380,7 +380,7 @@ def test_context_kernel_families_match_oracle(kernel, splits):
     compare(prob, dp, label=f"{kernel}/{splits}")
 
 
-@pytest.mark.parametrize("kernel", ["m32_ctx_bf16", "m32_ctx_pp"])
+@pytest.mark.parametrize("kernel", ["m32_ctx_bf16", "m32_ctx_pp", "m32_ctx_iw"])
 def test_context_full_size_m32(kernel):
     prob = W.context_b4_q511_kv2047()
     say(f"case {prob.name} kernel={kernel}")
