@@ -272,6 +272,51 @@ def test_repeated_calls_are_bitwise_deterministic():
     assert torch.equal(first, dp.out)
 
 
+@pytest.mark.parametrize("case", ["gqa_bf16", "fp8_balanced_merge", "fp8_fused_merge", "context"])
+def test_graph_replay_matches_eager(case):
+    # the calls enqueue kernels only (no allocation, no memset, no host sync), so
+    # they can be captured; every replay, with eager work and synchronizations in
+    # between, must reproduce the eager result bitwise
+    if case == "gqa_bf16":
+        prob, kw = _gqa([513, 1000], poison=True), {}
+    elif case == "context":
+        prob = W.make_problem(name="ctx-graph", seed=4, batch=3, seq_lens=[50, 1, 300], q_lens=[20, 1, 70],
+                              num_qo_heads=64, num_kv_heads=8, head_dim_qk=128, head_dim_v=128, page_size=32,
+                              is_decode=False, poison=True, extra_page_frac=0.3, table_slack_pages=1)
+        kw = {}
+    else:
+        prob = _gqa([5, 64, 65, 1500], hq=64, hkv=8, P=64, kv=W.E4M3)
+        kw = {"num_splits": -1, "merge_counters": case == "fp8_fused_merge"}
+    say(f"case graph {case}")
+    dp = pkv.upload(prob, "cuda", **kw)
+    dp.run()
+    torch.cuda.synchronize()
+    eager_out, eager_lse = dp.out.clone(), dp.lse.clone()
+    compare(prob, dp, label=f"graph {case} eager")
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        dp.run()  # warm the side stream once outside capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        dp.run()
+    for r in range(3):
+        dp.tensors["out"].fill_(float("nan"))
+        dp.tensors["lse"].fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(dp.out, eager_out), f"replay {r} differs from the eager output"
+        assert torch.equal(dp.lse, eager_lse), f"replay {r} lse differs from the eager lse"
+        if "counters" in dp.tensors:
+            assert int(dp.tensors["counters"].abs().sum().item()) == 0
+        dp.run()  # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(dp.out, eager_out)
+
+
 def test_nhd_layout_matches_oracle():
     prob = _gqa([40, 129], layout=W.NHD)
     say(f"case {prob.name} NHD")
