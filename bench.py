@@ -116,6 +116,51 @@ def time_graph(dp, steps: int, warmup: int):
     return wall, e0.elapsed_time(e1) / 1e3 / n
 
 
+def single_call_stats(dp, kv_bytes: int, samples: int = 30):
+    """Single calls replayed from a one-call HIP graph, one HIP event pair around
+    each: warm (back to back) and cold (a 1 GiB buffer read before every call,
+    outside the timed span, so L2 and the Infinity Cache hold none of the
+    inputs).  The eviction pass reads rather than writes: dirty lines left by a
+    write pass would be written back during the timed call and be counted as
+    part of it.  Median, p10 and p90 in microseconds."""
+    import numpy as np
+    import torch
+
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        dp.run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        dp.run()
+    scratch = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    sink = torch.empty(1, dtype=torch.float32, device="cuda")
+    torch.sum(scratch, dim=0, out=sink[0])  # the initial writes reach memory before the samples
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    out = {}
+    for mode in ("warm", "cold"):
+        ts = []
+        for i in range(samples):
+            if mode == "cold":
+                torch.sum(scratch, dim=0, out=sink[0])
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3)
+        ts = np.array(ts)
+        med = float(np.median(ts))
+        out[mode] = {"us_median": round(med, 2), "us_p10": round(float(np.percentile(ts, 10)), 2),
+                     "us_p90": round(float(np.percentile(ts, 90)), 2), "gbs_median": round(kv_bytes / med / 1e3, 1)}
+    del scratch, sink
+    return out
+
+
 def measure(prob, steps: int, warmup: int, num_splits=None):
     from paged_kv_attention_15_amd import pkv
 
@@ -146,7 +191,7 @@ def cpu_baseline(prob, max_pairs: int):
                       f"same workload, single-threaded fp64 C oracle, {dt:.1f} s"}
 
 
-def secondary_results(steps: int, warmup: int):
+def secondary_results(steps: int, warmup: int, single_call: bool = True):
     import torch
 
     from paged_kv_attention_15_amd import pkv, workloads as W
@@ -167,7 +212,13 @@ def secondary_results(steps: int, warmup: int):
             pass
         gbs = prob.kv_bytes() / ev_mean / 1e9
         tflops = prob.flops() / ev_mean / 1e12
-        rec = {"us_per_call": round(ev_mean * 1e6, 3),
+        sc = None
+        if single_call:
+            try:
+                sc = single_call_stats(dp, prob.kv_bytes())
+            except Exception as exc:
+                sc = {"error": str(exc)[:200]}
+        rec = {"us_per_call": round(ev_mean * 1e6, 3), "single_call": sc,
                "kernel": pkv.KERNEL_NAMES[info.kernel], "num_splits": info.num_splits,
                "fused_merge": int(info.fused_merge),
                "kv_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
@@ -187,6 +238,8 @@ def main():
     ap.add_argument("--num-splits", type=int, default=None)
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-single-call", action="store_true",
+                    help="skip the warm/cold single-call samples (profiling runs: only the timed calls)")
     ap.add_argument("--cpu-pairs", type=int, default=1024)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device-to-device copy (known bytes) to scale HBM counters")
@@ -245,6 +298,11 @@ def main():
                      "timing": timing},
         "eager": eager,
     }
+    if not args.no_single_call:
+        try:
+            line["single_call"] = single_call_stats(dp, kv)
+        except Exception as exc:
+            line["single_call"] = {"error": str(exc)[:200]}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(prob, args.cpu_pairs)
     del dp
@@ -259,7 +317,8 @@ def main():
         del src, dst
         torch.cuda.empty_cache()
     if not args.no_secondary:
-        line["secondary"] = secondary_results(max(20, args.steps // 4), max(5, args.warmup // 2))
+        line["secondary"] = secondary_results(max(20, args.steps // 4), max(5, args.warmup // 2),
+                                              not args.no_single_call)
     print(json.dumps(line), flush=True)
 
 
