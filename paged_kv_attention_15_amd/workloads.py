@@ -350,3 +350,146 @@ WORKLOADS: Dict[str, callable] = {
     "mla-b512-kv4096": mla_b512_kv4096,
     "ctx-b4-q511-kv2047": context_b4_q511_kv2047,
 }
+
+
+# ---------------------------------------------------------------- paged KV append producer inputs
+#
+# PR #5952 page (fused BF16 QK RMSNorm + NeoX RoPE + paged KV append), summary:
+# a packed BF16 qkv [T, (Hq + 2 Hkv) * 128] (Q heads, then K heads, then V
+# heads), an FP32 cos_sin [max_pos, 128] table, optional per-head RMSNorm
+# weights, NHD caches [num_pages, page_size, Hkv, 128] reached through a dense
+# [B, max_pages] table; PR #5956 "Contract": seq_lens is the total length after
+# the append and K/V may be stored as e4m3 codes of x / scale.
+
+ROPE_DIM = 128
+
+
+@dataclasses.dataclass
+class AppendProblem:
+    """One append call, held in host memory (raw storage arrays).
+
+      qkv          uint16 bf16 bits [T, (Hq + 2 Hkv) * 128]
+      cos_sin      float32 [max_pos, 128]: cos of the 64 frequencies, then their sin
+      q_weight     uint16 bf16 bits [128] (RMSNorm weights of the Q heads)
+      k_weight     uint16 bf16 bits [128]
+      q_indptr     int32 [B + 1]   rows of request b are q_indptr[b] .. q_indptr[b+1]
+      seq_lens     int32 [B]       total length after the append
+      block_tables int32 [B, max_pages]
+      k_cache0     initial NHD K cache [num_pages, P, Hkv, 128] (uint16 bf16 bits or uint8 e4m3)
+      v_cache0     same for V
+    """
+
+    name: str
+    batch: int
+    num_qo_heads: int
+    num_kv_heads: int
+    page_size: int
+    qkv: np.ndarray
+    cos_sin: np.ndarray
+    q_weight: np.ndarray
+    k_weight: np.ndarray
+    q_indptr: np.ndarray
+    seq_lens: np.ndarray
+    block_tables: np.ndarray
+    k_cache0: np.ndarray
+    v_cache0: np.ndarray
+    norm_policy: int = 0
+    eps: float = 1e-6
+    kv_dtype: str = BF16
+    k_scale: float = 1.0
+    v_scale: float = 1.0
+    clear_tail: bool = True
+    head_dim: int = ROPE_DIM
+
+    @property
+    def total_tokens(self) -> int:
+        return int(self.q_indptr[-1])
+
+    @property
+    def num_pages(self) -> int:
+        return int(self.k_cache0.shape[0])
+
+    @property
+    def max_pages(self) -> int:
+        return int(self.block_tables.shape[1])
+
+    @property
+    def max_pos(self) -> int:
+        return int(self.cos_sin.shape[0])
+
+    def bytes_moved(self) -> int:
+        """Algorithmic HBM bytes of one call: qkv read, Q written, K and V rows
+        written, and the cleared tail rows of every nonempty request."""
+        T, Hq, Hkv, D, P = self.total_tokens, self.num_qo_heads, self.num_kv_heads, self.head_dim, self.page_size
+        eb = 1 if self.kv_dtype == E4M3 else 2
+        tail = 0
+        if self.clear_tail:
+            for L in self.seq_lens.tolist():
+                if L > 0:
+                    tail += P - 1 - (L - 1) % P
+        return T * (Hq + 2 * Hkv) * D * 2 + T * Hq * D * 2 + 2 * T * Hkv * D * eb + 2 * tail * Hkv * D * eb
+
+
+def rope_table(max_pos: int, base: float = 10000.0) -> np.ndarray:
+    """A standard NeoX rotary table [max_pos, 128]: frequency i = base^(-2i/128),
+    row p = cos(p * f_0..63) then sin(p * f_0..63), in fp32."""
+    half = ROPE_DIM // 2
+    inv = base ** (-np.arange(half, dtype=np.float64) * 2.0 / ROPE_DIM)
+    ang = np.arange(max_pos, dtype=np.float64)[:, None] * inv[None, :]
+    return np.concatenate([np.cos(ang), np.sin(ang)], axis=1).astype(np.float32)
+
+
+def make_append_problem(*, name: str, seed: int, new_lens, seq_lens, num_qo_heads: int, num_kv_heads: int,
+                        page_size: int, norm_policy: int = 0, kv_dtype: str = BF16, clear_tail: bool = True,
+                        k_scale: float = 1.0, v_scale: float = 1.0, extra_pages: int = 2,
+                        table_slack_pages: int = 1, max_pos: Optional[int] = None) -> AppendProblem:
+    """Draw order: page permutation, qkv, the two weight vectors, the initial
+    cache contents (random non-zero storage so that untouched and cleared rows
+    are told apart).  Unused table slots point at a spare page that no request
+    owns, so any stray write through them shows up."""
+    rng = np.random.default_rng(seed)
+    new_lens = [int(x) for x in new_lens]
+    seq_lens = [int(x) for x in seq_lens]
+    B = len(seq_lens)
+    D, P, Hq, Hkv = ROPE_DIM, int(page_size), int(num_qo_heads), int(num_kv_heads)
+    pages_per = [(L + P - 1) // P for L in seq_lens]
+    used = sum(pages_per)
+    num_pages = used + max(1, extra_pages)
+    perm = rng.permutation(num_pages).astype(np.int32)
+    spare = int(perm[-1])
+    width = max(1, max(pages_per) if pages_per else 1) + table_slack_pages
+    table = np.full((B, width), spare, dtype=np.int32)
+    off = 0
+    for b, n in enumerate(pages_per):
+        table[b, :n] = perm[off:off + n]
+        off += n
+    q_indptr = np.zeros(B + 1, dtype=np.int32)
+    q_indptr[1:] = np.cumsum(new_lens)
+    T = int(q_indptr[-1])
+    qkv = bf16_bits(rng.standard_normal((T, (Hq + 2 * Hkv) * D)).astype(np.float32))
+    q_w = bf16_bits((1.0 + 0.25 * rng.standard_normal(D)).astype(np.float32))
+    k_w = bf16_bits((1.0 + 0.25 * rng.standard_normal(D)).astype(np.float32))
+    shape = (num_pages, P, Hkv, D)
+    if kv_dtype == BF16:
+        k0 = bf16_bits((rng.standard_normal(shape) + 3.0).astype(np.float32))
+        v0 = bf16_bits((rng.standard_normal(shape) + 3.0).astype(np.float32))
+    elif kv_dtype == E4M3:
+        k0 = rng.integers(1, 0x7E, size=shape, dtype=np.uint8)  # finite, non-zero codes
+        v0 = rng.integers(1, 0x7E, size=shape, dtype=np.uint8)
+    else:
+        raise ValueError(kv_dtype)
+    mp = max_pos if max_pos is not None else max(1, max(seq_lens) if seq_lens else 1) + 7
+    return AppendProblem(name=name, batch=B, num_qo_heads=Hq, num_kv_heads=Hkv, page_size=P, qkv=qkv,
+                         cos_sin=rope_table(mp), q_weight=q_w, k_weight=k_w, q_indptr=q_indptr,
+                         seq_lens=np.array(seq_lens, dtype=np.int32), block_tables=table, k_cache0=k0,
+                         v_cache0=v0, norm_policy=norm_policy, kv_dtype=kv_dtype, k_scale=float(k_scale),
+                         v_scale=float(v_scale), clear_tail=clear_tail)
+
+
+def append_h64x8_b32_decode(seed: int = 0, norm_policy: int = 2, kv_dtype: str = BF16) -> AppendProblem:
+    """The pages' H1 row: Hq=64 / Hkv=8, 32 requests appending one row each,
+    here at total lengths 2048 with 64-token pages."""
+    return make_append_problem(name=f"append-h64x8-b32-decode-p{norm_policy}-{kv_dtype}", seed=seed,
+                               new_lens=[1] * 32, seq_lens=[2048] * 32, num_qo_heads=64, num_kv_heads=8,
+                               page_size=64, norm_policy=norm_policy, kv_dtype=kv_dtype,
+                               k_scale=0.05 if kv_dtype == E4M3 else 1.0, v_scale=0.05 if kv_dtype == E4M3 else 1.0)

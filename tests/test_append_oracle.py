@@ -1,0 +1,191 @@
+"""Pins for the append-producer oracle (no GPU).
+
+Each test ties oracle/append.py to something other than itself: the pages'
+placement and tail rules worked by hand (tests/golden/append_contract.json),
+torch's e4m3 decoding, the rotation identities of the NeoX embedding (identity
+at angle 0, norm preservation, composition of positions, the equivalent
+complex product), closed forms of RMSNorm, and order properties of the norm
+policies.
+"""
+from __future__ import annotations
+
+import dataclasses
+import json
+import os
+
+import numpy as np
+import torch
+
+import oracle.append as A
+from paged_kv_attention_15_amd import workloads as W
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _small(policy=0, kv=W.BF16, **kw):
+    base = dict(name="pin", seed=3, new_lens=[2, 0, 5, 1], seq_lens=[9, 6, 5, 17], num_qo_heads=8,
+                num_kv_heads=1, page_size=4, norm_policy=policy, kv_dtype=kv)
+    base.update(kw)
+    return W.make_append_problem(**base)
+
+
+def test_e4m3_decode_matches_torch_on_all_codes():
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = A.e4m3_to_f64(np.arange(256, dtype=np.uint8))
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    fin = ~np.isnan(ref)
+    assert np.array_equal(got[fin], ref[fin])
+    g = json.load(open(os.path.join(GOLD, "e4m3_points.json")))
+    for pt in g["points"]:
+        assert A.e4m3_to_f64(np.array([int(pt["code"], 16)], dtype=np.uint8))[0] == pt["value"]
+
+
+def test_bf16_decode_matches_torch():
+    rng = np.random.default_rng(0)
+    bits = rng.integers(0, 1 << 16, size=4000, dtype=np.uint16)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    got = A.bf16_to_f64(bits)
+    fin = np.isfinite(ref)
+    assert np.array_equal(got[fin], ref[fin])
+
+
+def test_rope_identity_at_angle_zero_and_norm_preserving():
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal(128)
+    tab = W.rope_table(40).astype(np.float64)
+    assert np.array_equal(A.rope(x, tab[0]), x)  # cos 1, sin 0
+    for p in (1, 7, 39):
+        y = A.rope(x, tab[p])
+        pair_x = x[:64] ** 2 + x[64:] ** 2
+        pair_y = y[:64] ** 2 + y[64:] ** 2
+        np.testing.assert_allclose(pair_y, pair_x, rtol=1e-6)  # each (i, i+64) pair is rotated
+
+
+def test_rope_positions_compose():
+    # rotating by position p, then by q, equals rotating by p + q
+    rng = np.random.default_rng(2)
+    x = rng.standard_normal(128)
+    tab = W.rope_table(64).astype(np.float64)
+    for p, q in ((3, 5), (10, 20), (0, 31)):
+        np.testing.assert_allclose(A.rope(A.rope(x, tab[p]), tab[q]), A.rope(x, tab[p + q]), atol=1e-5)
+
+
+def test_rope_is_the_complex_product():
+    # pair (x_i, x_{i+64}) as x_i + j x_{i+64}, multiplied by exp(j p f_i)
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal(128)
+    p = 13
+    f = 10000.0 ** (-np.arange(64) * 2.0 / 128)
+    z = (x[:64] + 1j * x[64:]) * np.exp(1j * p * f)
+    y = A.rope(x, W.rope_table(20).astype(np.float64)[p])
+    np.testing.assert_allclose(y[:64], z.real, atol=1e-6)
+    np.testing.assert_allclose(y[64:], z.imag, atol=1e-6)
+
+
+def test_rms_norm_closed_forms():
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal(128) * 3.0
+    ones = np.ones(128)
+    eps = 1e-6
+    y = A.rms_norm(x, ones, eps)
+    ms = np.mean(x * x)
+    assert abs(np.mean(y * y) - ms / (ms + eps)) < 1e-12
+    np.testing.assert_allclose(A.rms_norm(5.0 * x, ones, 0.0), A.rms_norm(x, ones, 0.0), rtol=1e-12)
+    w = rng.standard_normal(128)
+    np.testing.assert_allclose(A.rms_norm(x, w, eps), y * w, rtol=1e-12)
+    assert np.array_equal(A.rms_norm(np.zeros(128), ones, eps), np.zeros(128))
+
+
+def test_norm_policies_order():
+    # with unit weights RoPE commutes with the (rotation-invariant) norm; with
+    # other weights the two orders differ, and policy 0 applies no norm at all
+    p1 = _small(1)
+    ones = W.bf16_bits(np.ones(128, dtype=np.float32))
+    u1 = A.append(dataclasses.replace(p1, q_weight=ones, k_weight=ones))
+    u2 = A.append(dataclasses.replace(p1, q_weight=ones, k_weight=ones, norm_policy=2))
+    rows = ~np.isnan(u1.out_q[:, 0, 0])
+    # (the fp32 table makes each rotation norm-preserving to ~1e-8 only)
+    np.testing.assert_allclose(u1.out_q[rows], u2.out_q[rows], rtol=1e-6, atol=1e-7)
+    r1, r2 = A.append(p1), A.append(dataclasses.replace(p1, norm_policy=2))
+    assert not np.allclose(r1.out_q[rows], r2.out_q[rows])
+    r0 = A.append(dataclasses.replace(p1, norm_policy=0))
+    # policy 0 keeps each rotated pair's length: the raw row's pair lengths
+    x = A.bf16_to_f64(p1.qkv).reshape(p1.total_tokens, 10, 128)[:, :8]
+    got = r0.out_q[rows]
+    np.testing.assert_allclose(got[..., :64] ** 2 + got[..., 64:] ** 2,
+                               x[rows][..., :64] ** 2 + x[rows][..., 64:] ** 2, rtol=1e-5)
+
+
+def test_placement_and_tail_follow_the_golden_case():
+    g = json.load(open(os.path.join(GOLD, "append_contract.json")))
+    prob = _small(0, new_lens=[2, 1], seq_lens=g["seq_lens"], page_size=g["page_size"])
+    prob = dataclasses.replace(prob, q_indptr=np.array(g["q_indptr"], dtype=np.int32),
+                               block_tables=np.array(g["block_tables"], dtype=np.int32))
+    res = A.append(prob)
+    assert sorted(res.k_rows) == sorted((e["page"], e["slot"], 0) for e in g["rows"])
+    assert sorted(res.v_rows) == sorted(res.k_rows)
+    assert sorted(res.cleared) == sorted((e["page"], e["slot"], 0) for e in g["cleared"])
+    # zero-angle table and policy 0: the appended rows are the raw K and V rows
+    flat = dataclasses.replace(prob, cos_sin=np.concatenate([np.ones((prob.max_pos, 64)), np.zeros((prob.max_pos, 64))],
+                                                               axis=1).astype(np.float32))
+    res = A.append(flat)
+    x = A.bf16_to_f64(prob.qkv).reshape(prob.total_tokens, 10, 128)
+    for e in g["rows"]:
+        np.testing.assert_array_equal(res.k_rows[(e["page"], e["slot"], 0)], x[e["row"], 8])
+        np.testing.assert_array_equal(res.v_rows[(e["page"], e["slot"], 0)], x[e["row"], 9])
+        np.testing.assert_array_equal(res.out_q[e["row"]], x[e["row"], :8])
+
+
+def test_brute_force_positions_and_rotation_angles():
+    # every appended key row equals the raw row rotated by exactly its own
+    # position (checked through the complex product), found by an independent walk
+    prob = _small(0)
+    res = A.append(prob)
+    x = A.bf16_to_f64(prob.qkv).reshape(prob.total_tokens, 10, 128)
+    f = 10000.0 ** (-np.arange(64) * 2.0 / 128)
+    r = 0
+    for b in range(prob.batch):
+        n = int(prob.q_indptr[b + 1] - prob.q_indptr[b])
+        L = int(prob.seq_lens[b])
+        for i in range(n):
+            pos = L - n + i
+            key = (int(prob.block_tables[b, pos // prob.page_size]), pos % prob.page_size, 0)
+            z = (x[r, 8, :64] + 1j * x[r, 8, 64:]) * np.exp(1j * pos * f)
+            np.testing.assert_allclose(res.k_rows[key], np.concatenate([z.real, z.imag]), atol=1e-5)
+            r += 1
+    assert r == prob.total_tokens
+
+
+def test_e4m3_payload_is_scaled_and_tail_clearing_can_be_off():
+    prob = _small(2, kv=W.E4M3, k_scale=0.5, v_scale=0.25)
+    res = A.append(prob)
+    base = A.append(dataclasses.replace(prob, kv_dtype=W.BF16))
+    for key in res.k_rows:
+        np.testing.assert_allclose(res.k_rows[key], base.k_rows[key] / 0.5, rtol=1e-12)
+        np.testing.assert_allclose(res.v_rows[key], base.v_rows[key] / 0.25, rtol=1e-12)
+    assert A.append(dataclasses.replace(prob, clear_tail=False)).cleared == []
+
+
+def test_requests_that_do_not_fit_are_skipped():
+    prob = _small(0, new_lens=[3, 1], seq_lens=[2, 4])  # request 0 appends 3 rows to a length of 2
+    res = A.append(prob)
+    assert res.bad_requests == [0]
+    assert np.isnan(res.out_q[:3]).all() and not np.isnan(res.out_q[3]).any()
+    assert all(k[0] == int(prob.block_tables[1, 0]) for k in res.k_rows)
+
+
+def test_policy_one_normalizes_last_and_policy_two_rotates_last():
+    # policy 1 (RoPE then norm): out / w has unit mean square; policy 2 (norm
+    # then RoPE): the pair lengths of the output are those of norm(x) * w
+    p1 = _small(1)
+    w = A.bf16_to_f64(p1.q_weight)
+    x = A.bf16_to_f64(p1.qkv).reshape(p1.total_tokens, 10, 128)[:, :8]
+    r1 = A.append(p1)
+    rows = ~np.isnan(r1.out_q[:, 0, 0])
+    y = r1.out_q[rows] / w
+    ms = np.mean(y * y, axis=-1)
+    np.testing.assert_allclose(ms, 1.0, atol=1e-5)
+    r2 = A.append(dataclasses.replace(p1, norm_policy=2))
+    z = r2.out_q[rows]
+    n = np.stack([A.rms_norm(v, w, p1.eps) for v in x[rows].reshape(-1, 128)]).reshape(z.shape)
+    np.testing.assert_allclose(z[..., :64] ** 2 + z[..., 64:] ** 2, n[..., :64] ** 2 + n[..., 64:] ** 2, rtol=1e-5)
