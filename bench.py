@@ -230,6 +230,34 @@ def secondary_results(steps: int, warmup: int, single_call: bool = True):
     return out
 
 
+def append_result(steps: int, warmup: int):
+    """The paged-KV append producer on the pages' H1 row (Hq=64 / Hkv=8, 32
+    requests appending one row each, norm then RoPE, bf16 caches of 64-token
+    pages): per-call time as HIP-graph replays, and bytes moved per call."""
+    import torch
+
+    from paged_kv_attention_15_amd import pkv, workloads as W
+
+    prob = W.append_h64x8_b32_decode(norm_policy=2)
+    da = pkv.upload_append(prob, "cuda", with_err=False)
+    for _ in range(warmup):
+        da.run()
+    torch.cuda.synchronize()
+    try:
+        _, ev = time_graph(da, steps, warmup)
+        timing = "graph"
+    except Exception:
+        _, ev = time_calls(da, steps, warmup)
+        timing = "eager"
+    nbytes = prob.bytes_moved()
+    rec = {"us_per_call": round(ev * 1e6, 3), "bytes_per_call": nbytes, "gbs": round(nbytes / ev / 1e9, 1),
+           "hbm_frac": round(nbytes / ev / 1e9 / HBM_PEAK_GBS, 4), "timing": timing,
+           "bound": "latency (1.3 MB per call: one dependent load-compute-store chain per wave)"}
+    del da
+    torch.cuda.empty_cache()
+    return rec
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -319,6 +347,8 @@ def main():
     if not args.no_secondary:
         line["secondary"] = secondary_results(max(20, args.steps // 4), max(5, args.warmup // 2),
                                               not args.no_single_call)
+        line["secondary"]["append-h64x8-b32-decode"] = append_result(max(20, args.steps // 4),
+                                                                     max(5, args.warmup // 2))
     print(json.dumps(line), flush=True)
 
 

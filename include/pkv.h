@@ -73,6 +73,7 @@ typedef enum pkv_layout {
 #define PKV_DEVERR_SEQ_GT_TABLE 0x2   /* seq_lens[b] > max_pages_per_seq * page_size (clamped) */
 #define PKV_DEVERR_PAGE_RANGE 0x4     /* a referenced page index outside [0, num_pages) (clamped) */
 #define PKV_DEVERR_QINDPTR 0x8        /* q_indptr not monotone, or rows exceed max_q_len / total_q */
+#define PKV_DEVERR_POS_RANGE 0x10     /* pkv_append: a row's position is past the rotary table */
 
 /*
  * Arguments of one attention call.  Strides are in ELEMENTS of the tensor's
@@ -214,6 +215,71 @@ pkv_status pkv_lse_merge(int32_t num_splits, int32_t num_rows, int32_t num_qo_he
                          int32_t head_dim_v, const float* o_part, const float* lse_part,
                          void* out, int32_t o_dtype, int64_t o_stride_tok, int64_t o_stride_head,
                          float* lse_out, void* stream);
+
+/* ---------------------------------------------------------------- paged KV append (the producer) */
+
+/*
+ * Fused QK RMSNorm + NeoX rotary embedding + paged K/V append, one launch
+ * (PR #5952 page, summary; the PR #5956 body quoted there, section "Contract").
+ * Packed row r of request b (rows q_indptr[b] .. q_indptr[b+1] of qkv) sits at
+ * position pos = r + seq_lens[b] - q_indptr[b+1] (seq_lens = total length
+ * after the append) and holds Hq query heads, Hkv key heads and Hkv value
+ * heads of 128 channels each, in that order.
+ *   - query and key heads: the norm policy (0 none; 1 rotary then RMSNorm;
+ *     2 RMSNorm then rotary), RMSNorm y = x / sqrt(mean(x^2) + eps) * w in fp32
+ *     with w = q_weight or k_weight, and the NeoX rotary embedding with row pos
+ *     of cos_sin = (cos_0..63, sin_0..63): channel i < 64 pairs with i + 64,
+ *     y_i = x_i cos_i - x_{i+64} sin_i, y_{i+64} = x_{i+64} cos_i + x_i sin_i;
+ *   - the query heads are written to out_q[r] (bf16, round to nearest even);
+ *   - key heads and the unchanged value heads are written to token pos % P of
+ *     page block_tables[b][pos / P] of the NHD caches [num_pages, P, Hkv, 128]:
+ *     bf16, or e4m3 codes of x / k_scale and x / v_scale (round to nearest
+ *     even, saturated to +-448);
+ *   - with clear_tail, tokens [(seq_lens[b] - 1) % P + 1, P) of every nonempty
+ *     request's last page are zeroed in both caches (the caller owns the pages
+ *     exclusively: a page shared with a longer request would lose rows).
+ * A request whose rows do not fit (seq_lens[b] < rows, seq_lens[b] > max_pages_per_seq * P
+ * or > max_pos, q_indptr not monotone or past num_tokens) writes nothing and
+ * sets PKV_DEVERR_* bits; a page index outside [0, num_pages) (num_pages > 0)
+ * skips that row's cache write and sets PKV_DEVERR_PAGE_RANGE.  Device values
+ * are never used for addressing unchecked.  Nothing is allocated, nothing
+ * synchronizes the host; the work is enqueued on `stream` and can be captured
+ * in a graph.  Returns PKV_ERR_INVALID_ARG / PKV_ERR_UNSUPPORTED for
+ * host-checkable problems before anything is enqueued.
+ */
+typedef struct pkv_append_args {
+  int32_t num_tokens;        /* T = q_indptr[B], rows of qkv and out_q (host value) */
+  int32_t batch;             /* B >= 0; T = 0 with clear_tail = 0 (or B = 0) is a no-op */
+  int32_t num_qo_heads;      /* Hq >= 1 */
+  int32_t num_kv_heads;      /* Hkv >= 1 */
+  int32_t head_dim;          /* 128 */
+  int32_t page_size;         /* P >= 1 */
+  int32_t max_pages_per_seq; /* readable width of each block-table row */
+  int32_t max_pos;           /* rows of cos_sin */
+  int32_t num_pages;         /* cache pages, for checking page indices (0 = unchecked) */
+  int32_t norm_policy;       /* 0, 1 or 2 (above) */
+  int32_t clear_tail;        /* 1: zero the tail of each nonempty request's last page */
+  int32_t kv_dtype;          /* PKV_DTYPE_BF16 or PKV_DTYPE_FP8_E4M3 */
+  float eps;                 /* RMSNorm epsilon (the pages use 1e-6), >= 0 */
+  float k_scale;             /* e4m3 caches: stored = x / k_scale (finite, non-zero) */
+  float v_scale;
+  float reserved;
+  const void* qkv;           /* bf16 [T, qkv_stride_tok], the first (Hq + 2 Hkv) * 128 used */
+  int64_t qkv_stride_tok;    /* elements between rows, >= (Hq + 2 Hkv) * 128 */
+  const float* cos_sin;      /* fp32 [max_pos, 128] */
+  const void* q_weight;      /* bf16 [128]; read only when norm_policy != 0 */
+  const void* k_weight;      /* bf16 [128] */
+  const int32_t* q_indptr;   /* [B + 1] */
+  const int32_t* seq_lens;   /* [B] */
+  const int32_t* block_tables; /* [B, table_stride] */
+  int64_t table_stride;      /* >= max_pages_per_seq */
+  void* out_q;               /* bf16 [T, Hq, 128] */
+  void* k_cache;             /* NHD [num_pages, P, Hkv, 128], bf16 or e4m3 */
+  void* v_cache;
+  int32_t* err_word;         /* optional device word, OR-ed with PKV_DEVERR_* bits */
+} pkv_append_args;
+
+pkv_status pkv_append(const pkv_append_args* args, void* stream);
 
 #ifdef __cplusplus
 }

@@ -11,6 +11,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -602,3 +603,47 @@ pkv_status pkv_lse_merge(int32_t num_splits, int32_t num_rows, int32_t num_qo_he
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------- paged KV append
+
+extern "C" pkv_status pkv_append(const pkv_append_args* a, void* stream) {
+  if (!a) return fail(PKV_ERR_INVALID_ARG, "args is NULL");
+  if (a->num_tokens < 0 || a->batch < 0) return fail(PKV_ERR_INVALID_ARG, "num_tokens and batch must be >= 0");
+  if (a->num_qo_heads < 1 || a->num_kv_heads < 1)
+    return fail(PKV_ERR_INVALID_ARG, "num_qo_heads and num_kv_heads must be >= 1");
+  if (a->head_dim != 128) return fail(PKV_ERR_UNSUPPORTED, "head_dim %d: the append route is built for 128", a->head_dim);
+  if (a->page_size < 1) return fail(PKV_ERR_INVALID_ARG, "page_size must be >= 1 (got %d)", a->page_size);
+  if (a->norm_policy < 0 || a->norm_policy > 2) return fail(PKV_ERR_INVALID_ARG, "norm_policy must be 0, 1 or 2");
+  if (a->kv_dtype != PKV_DTYPE_BF16 && a->kv_dtype != PKV_DTYPE_FP8_E4M3)
+    return fail(PKV_ERR_UNSUPPORTED, "kv_dtype %d: caches are bf16 or e4m3", a->kv_dtype);
+  if (a->kv_dtype == PKV_DTYPE_FP8_E4M3 &&
+      (!(std::fabs(a->k_scale) > 0.f) || !(std::fabs(a->v_scale) > 0.f) || !std::isfinite(a->k_scale) ||
+       !std::isfinite(a->v_scale)))
+    return fail(PKV_ERR_INVALID_ARG, "e4m3 caches need finite non-zero k_scale and v_scale");
+  if (!(a->eps >= 0.f)) return fail(PKV_ERR_INVALID_ARG, "eps must be >= 0");
+  if (a->batch == 0 || (a->num_tokens == 0 && !a->clear_tail)) return ok();
+  if (!a->q_indptr || !a->seq_lens || !a->block_tables || !a->k_cache || !a->v_cache)
+    return fail(PKV_ERR_INVALID_ARG, "q_indptr, seq_lens, block_tables and both caches are required");
+  if (a->num_pages < 1)
+    return fail(PKV_ERR_INVALID_ARG, "num_pages must give the cache size: every page index is checked before a write");
+  if (a->max_pages_per_seq < 1 || a->table_stride < a->max_pages_per_seq)
+    return fail(PKV_ERR_INVALID_ARG, "need max_pages_per_seq >= 1 and table_stride >= max_pages_per_seq");
+  if (a->num_tokens > 0) {
+    if (!a->qkv || !a->cos_sin || !a->out_q) return fail(PKV_ERR_INVALID_ARG, "qkv, cos_sin and out_q are required");
+    if (a->norm_policy != 0 && (!a->q_weight || !a->k_weight))
+      return fail(PKV_ERR_INVALID_ARG, "norm_policy %d needs q_weight and k_weight", a->norm_policy);
+    if (a->max_pos < 1) return fail(PKV_ERR_INVALID_ARG, "max_pos must be >= 1");
+    const int64_t row = (int64_t)(a->num_qo_heads + 2 * a->num_kv_heads) * 128;
+    if (a->qkv_stride_tok < row) return fail(PKV_ERR_INVALID_ARG, "qkv_stride_tok smaller than (Hq + 2 Hkv) * 128");
+    const uintptr_t al = reinterpret_cast<uintptr_t>(a->qkv) | reinterpret_cast<uintptr_t>(a->out_q) |
+                         reinterpret_cast<uintptr_t>(a->q_weight) | reinterpret_cast<uintptr_t>(a->k_weight);
+    if ((al & 1u) || (reinterpret_cast<uintptr_t>(a->cos_sin) & 3u))
+      return fail(PKV_ERR_INVALID_ARG, "bf16 arrays must be 2-byte and cos_sin 4-byte aligned");
+  }
+  if (a->kv_dtype == PKV_DTYPE_BF16 &&
+      ((reinterpret_cast<uintptr_t>(a->k_cache) | reinterpret_cast<uintptr_t>(a->v_cache)) & 1u))
+    return fail(PKV_ERR_INVALID_ARG, "bf16 caches must be 2-byte aligned");
+  hipError_t e = pkv::launch_append(a, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "append launch failed: %s", hipGetErrorString(e));
+  return ok();
+}

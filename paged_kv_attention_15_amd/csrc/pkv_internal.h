@@ -119,6 +119,9 @@ struct MergeParams {
 };
 hipError_t launch_merge(const MergeParams& mp, hipStream_t s);
 
+// The paged KV append producer (pkv_append.hip); arguments validated by the caller.
+hipError_t launch_append(const pkv_append_args* a, hipStream_t s);
+
 // Static shape facts of the MFMA kernel families (host-side planner input).
 struct MfmaShape {
   int rows_per_block;    // packed query rows per workgroup

@@ -33,7 +33,8 @@ KERNEL_IDS = {v: k for k, v in KERNEL_NAMES.items()}
 
 DTYPE_CODES = {"f32": PKV_DTYPE_F32, "bf16": PKV_DTYPE_BF16, "e4m3": PKV_DTYPE_FP8_E4M3}
 EXPORTED = ["pkv_abi_version", "pkv_last_error", "pkv_plan", "pkv_workspace_bytes", "pkv_decode",
-            "pkv_context", "pkv_lse_merge"]
+            "pkv_context", "pkv_lse_merge", "pkv_append"]
+PKV_DEVERR_POS_RANGE = 0x10
 
 
 class PkvArgs(C.Structure):
@@ -68,6 +69,21 @@ class PkvPlanInfo(C.Structure):
     ]
 
 
+class PkvAppendArgs(C.Structure):
+    """Mirror of `pkv_append_args` in include/pkv.h (field order and types must match)."""
+    _fields_ = [
+        ("num_tokens", C.c_int32), ("batch", C.c_int32), ("num_qo_heads", C.c_int32),
+        ("num_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("page_size", C.c_int32),
+        ("max_pages_per_seq", C.c_int32), ("max_pos", C.c_int32), ("num_pages", C.c_int32),
+        ("norm_policy", C.c_int32), ("clear_tail", C.c_int32), ("kv_dtype", C.c_int32),
+        ("eps", C.c_float), ("k_scale", C.c_float), ("v_scale", C.c_float), ("reserved", C.c_float),
+        ("qkv", C.c_void_p), ("qkv_stride_tok", C.c_int64), ("cos_sin", C.c_void_p),
+        ("q_weight", C.c_void_p), ("k_weight", C.c_void_p), ("q_indptr", C.c_void_p),
+        ("seq_lens", C.c_void_p), ("block_tables", C.c_void_p), ("table_stride", C.c_int64),
+        ("out_q", C.c_void_p), ("k_cache", C.c_void_p), ("v_cache", C.c_void_p), ("err_word", C.c_void_p),
+    ]
+
+
 class PkvError(RuntimeError):
     def __init__(self, status: int, message: str):
         super().__init__(f"pkv status {status}: {message}")
@@ -89,6 +105,8 @@ def load_library(path: str = LIB_PATH):
         lib.pkv_last_error.restype = C.c_char_p
         lib.pkv_plan.argtypes = [C.POINTER(PkvArgs), C.c_int, C.c_int, C.POINTER(PkvPlanInfo)]
         lib.pkv_plan.restype = C.c_int
+        lib.pkv_append.argtypes = [C.POINTER(PkvAppendArgs), C.c_void_p]
+        lib.pkv_append.restype = C.c_int
         lib.pkv_workspace_bytes.argtypes = [C.POINTER(PkvArgs), C.c_int, C.POINTER(C.c_size_t)]
         lib.pkv_workspace_bytes.restype = C.c_int
         for fn in (lib.pkv_decode, lib.pkv_context):
@@ -155,6 +173,13 @@ def pkv_lse_merge(num_splits: int, num_rows: int, num_qo_heads: int, head_dim_v:
 
 
 # ---------------------------------------------------------------- torch marshalling
+
+def pkv_append(args: PkvAppendArgs, stream: int, check: bool = True) -> int:
+    st = load_library().pkv_append(C.byref(args), C.c_void_p(stream or None))
+    if check:
+        _check(st)
+    return st
+
 
 def _torch():
     import torch
@@ -297,3 +322,69 @@ def fill_args(prob, t: dict, num_splits: Optional[int] = None) -> PkvArgs:
     a.k_scale = prob.k_scale
     a.v_scale = prob.v_scale
     return a
+
+
+@dataclass
+class DeviceAppend:
+    args: PkvAppendArgs
+    tensors: dict
+
+    def run(self, stream=None, check: bool = True) -> int:
+        torch = _torch()
+        s = stream if stream is not None else torch.cuda.current_stream()
+        return pkv_append(self.args, int(s.cuda_stream), check=check)
+
+
+def upload_append(prob, device="cuda", with_err: bool = True) -> DeviceAppend:
+    """Copy a workloads.AppendProblem to `device` (caches from their initial
+    contents, out_q NaN-filled) and fill pkv_append_args for it."""
+    import numpy as np
+    torch = _torch()
+    t = {}
+    t["qkv"] = torch.from_numpy(prob.qkv.view(np.int16)).to(device)
+    t["cos_sin"] = torch.from_numpy(prob.cos_sin).to(device)
+    t["q_w"] = torch.from_numpy(prob.q_weight.view(np.int16)).to(device)
+    t["k_w"] = torch.from_numpy(prob.k_weight.view(np.int16)).to(device)
+    t["q_indptr"] = torch.from_numpy(prob.q_indptr).to(device)
+    t["seq_lens"] = torch.from_numpy(prob.seq_lens).to(device)
+    t["table"] = torch.from_numpy(prob.block_tables).to(device)
+    if prob.kv_dtype == "bf16":
+        t["k_cache"] = torch.from_numpy(prob.k_cache0.view(np.int16)).to(device)
+        t["v_cache"] = torch.from_numpy(prob.v_cache0.view(np.int16)).to(device)
+    else:
+        t["k_cache"] = torch.from_numpy(prob.k_cache0).to(device)
+        t["v_cache"] = torch.from_numpy(prob.v_cache0).to(device)
+    T = prob.total_tokens
+    t["out_q"] = torch.full((max(T, 1), prob.num_qo_heads, 128), -1, dtype=torch.int16, device=device)
+    if with_err:
+        t["err"] = torch.zeros(1, dtype=torch.int32, device=device)
+    a = PkvAppendArgs()
+    a.num_tokens = T
+    a.batch = prob.batch
+    a.num_qo_heads = prob.num_qo_heads
+    a.num_kv_heads = prob.num_kv_heads
+    a.head_dim = 128
+    a.page_size = prob.page_size
+    a.max_pages_per_seq = prob.max_pages
+    a.max_pos = prob.max_pos
+    a.num_pages = prob.num_pages
+    a.norm_policy = prob.norm_policy
+    a.clear_tail = 1 if prob.clear_tail else 0
+    a.kv_dtype = DTYPE_CODES[prob.kv_dtype]
+    a.eps = prob.eps
+    a.k_scale = prob.k_scale
+    a.v_scale = prob.v_scale
+    a.qkv = t["qkv"].data_ptr()
+    a.qkv_stride_tok = prob.qkv.shape[1]
+    a.cos_sin = t["cos_sin"].data_ptr()
+    a.q_weight = t["q_w"].data_ptr()
+    a.k_weight = t["k_w"].data_ptr()
+    a.q_indptr = t["q_indptr"].data_ptr()
+    a.seq_lens = t["seq_lens"].data_ptr()
+    a.block_tables = t["table"].data_ptr()
+    a.table_stride = prob.block_tables.shape[1]
+    a.out_q = t["out_q"].data_ptr()
+    a.k_cache = t["k_cache"].data_ptr()
+    a.v_cache = t["v_cache"].data_ptr()
+    a.err_word = t["err"].data_ptr() if with_err else 0
+    return DeviceAppend(args=a, tensors=t)

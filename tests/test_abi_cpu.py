@@ -224,3 +224,62 @@ def test_balanced_schedule_rejected_for_non_gqa_families():
     a.q = a.k_pages = a.v_pages = a.out = 0x1000
     a.num_splits = -1
     assert pkv.pkv_context(a, 0, 0, 0, check=False) == pkv.PKV_ERR_UNSUPPORTED
+
+
+# ----------------------------------------------------------------- paged KV append (host side)
+
+def test_append_ctypes_mirror_matches_c_layout(tmp_path):
+    fields = [f for f, _ in pkv.PkvAppendArgs._fields_]
+    prog = ["#include <stdio.h>", "#include <stddef.h>", f'#include "{HEADER}"', "int main(void) {",
+            'printf("%zu\\n", sizeof(pkv_append_args));']
+    prog += [f'printf("%zu\\n", offsetof(pkv_append_args, {f}));' for f in fields]
+    prog += ["return 0; }"]
+    src = tmp_path / "layout_append.c"
+    src.write_text("\n".join(prog))
+    exe = tmp_path / "layout_append"
+    subprocess.check_call(["gcc", "-std=c99", "-o", str(exe), str(src)])
+    vals = [int(x) for x in subprocess.check_output([str(exe)]).split()]
+    assert vals[0] == C.sizeof(pkv.PkvAppendArgs)
+    for f, off in zip(fields, vals[1:]):
+        assert getattr(pkv.PkvAppendArgs, f).offset == off, f
+
+
+def _append_args(**kw):
+    a = pkv.PkvAppendArgs()
+    a.num_tokens, a.batch, a.num_qo_heads, a.num_kv_heads, a.head_dim = 4, 2, 8, 1, 128
+    a.page_size, a.max_pages_per_seq, a.max_pos, a.num_pages = 16, 4, 64, 8
+    a.norm_policy, a.clear_tail, a.kv_dtype, a.eps = 2, 1, pkv.PKV_DTYPE_BF16, 1e-6
+    a.k_scale = a.v_scale = 1.0
+    for name in ("qkv", "cos_sin", "q_weight", "k_weight", "q_indptr", "seq_lens", "block_tables", "out_q",
+                 "k_cache", "v_cache"):
+        setattr(a, name, 0x1000)
+    a.qkv_stride_tok = 10 * 128
+    a.table_stride = 4
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("head_dim", 64, pkv.PKV_ERR_UNSUPPORTED),
+    ("page_size", 0, pkv.PKV_ERR_INVALID_ARG),
+    ("norm_policy", 3, pkv.PKV_ERR_INVALID_ARG),
+    ("kv_dtype", pkv.PKV_DTYPE_F32, pkv.PKV_ERR_UNSUPPORTED),
+    ("num_pages", 0, pkv.PKV_ERR_INVALID_ARG),
+    ("qkv_stride_tok", 100, pkv.PKV_ERR_INVALID_ARG),
+    ("table_stride", 2, pkv.PKV_ERR_INVALID_ARG),
+    ("max_pos", 0, pkv.PKV_ERR_INVALID_ARG),
+    ("qkv", 0x1001, pkv.PKV_ERR_INVALID_ARG),
+    ("q_weight", 0, pkv.PKV_ERR_INVALID_ARG),
+    ("num_qo_heads", 0, pkv.PKV_ERR_INVALID_ARG),
+])
+def test_append_rejects_bad_arguments_before_launch(field, value, status):
+    assert pkv.pkv_append(_append_args(**{field: value}), 0, check=False) == status
+    assert pkv.pkv_last_error() != ""
+
+
+def test_append_e4m3_needs_scales_and_empty_calls_are_noops():
+    bad = _append_args(kv_dtype=pkv.PKV_DTYPE_FP8_E4M3, k_scale=0.0)
+    assert pkv.pkv_append(bad, 0, check=False) == pkv.PKV_ERR_INVALID_ARG
+    assert pkv.pkv_append(_append_args(batch=0), 0, check=False) == pkv.PKV_OK
+    assert pkv.pkv_append(_append_args(num_tokens=0, clear_tail=0), 0, check=False) == pkv.PKV_OK
