@@ -40,6 +40,7 @@ class _Problem(C.Structure):
         ("k_page_stride", C.c_int64), ("k_head_stride", C.c_int64), ("k_tok_stride", C.c_int64),
         ("v_page_stride", C.c_int64), ("v_head_stride", C.c_int64), ("v_tok_stride", C.c_int64),
         ("scale", C.c_double), ("k_scale", C.c_double), ("v_scale", C.c_double),
+        ("sinks", C.c_void_p),
     ]
 
 
@@ -66,7 +67,7 @@ def _load():
                                                 C.c_void_p, C.c_void_p]
             lib.orc_attention_split.restype = C.c_int
             lib.orc_merge.argtypes = [C.c_int, C.c_int64, C.c_int, C.c_void_p, C.c_void_p, C.c_void_p,
-                                      C.c_void_p]
+                                      C.c_void_p, C.c_void_p]
             lib.orc_merge.restype = C.c_int
             lib.orc_e4m3_to_double.argtypes = [C.c_uint8]
             lib.orc_e4m3_to_double.restype = C.c_double
@@ -109,8 +110,11 @@ def _make_struct(prob, keep: list):
     s.q_indptr = ptr(np.asarray(prob.q_indptr, dtype=np.int32))
     s.seq_lens = ptr(np.asarray(prob.seq_lens, dtype=np.int32))
     table = np.ascontiguousarray(prob.block_tables, dtype=np.int32)
+    v_table = table if getattr(prob, "v_block_tables", None) is None else \
+        np.ascontiguousarray(prob.v_block_tables, dtype=np.int32)
+    assert v_table.shape == table.shape
     s.k_table = ptr(table)
-    s.v_table = ptr(table)
+    s.v_table = ptr(v_table)
     s.table_stride = table.shape[1]
     s.q = ptr(prob.q)
     s.k = k_pool.ctypes.data
@@ -120,6 +124,8 @@ def _make_struct(prob, keep: list):
     s.scale = prob.scale
     s.k_scale = prob.k_scale
     s.v_scale = prob.v_scale
+    sinks = getattr(prob, "sinks", None)
+    s.sinks = ptr(np.asarray(sinks, dtype=np.float64)) if sinks is not None else None
     return s
 
 
@@ -165,15 +171,18 @@ def attention_split(prob, num_splits: int, pairs: np.ndarray | None = None):
     return o_part, lse_part
 
 
-def merge(o_part: np.ndarray, lse_part: np.ndarray):
-    """Log-sum-exp merge of [S, n, D_v] partial outputs with [S, n] LSEs."""
+def merge(o_part: np.ndarray, lse_part: np.ndarray, row_sinks: np.ndarray | None = None):
+    """Log-sum-exp merge of [S, n, D_v] partial outputs with [S, n] LSEs; row_sinks
+    [n] (optional) folds one sink logit into each merged row."""
     lib = _load()
     o_part = np.ascontiguousarray(o_part, dtype=np.float64)
     lse_part = np.ascontiguousarray(lse_part, dtype=np.float64)
     S, n, dv = o_part.shape
     out = np.zeros((n, dv), dtype=np.float64)
     lse = np.zeros(n, dtype=np.float64)
-    lib.orc_merge(S, n, dv, o_part.ctypes.data, lse_part.ctypes.data, out.ctypes.data, lse.ctypes.data)
+    rs = None if row_sinks is None else np.ascontiguousarray(row_sinks, dtype=np.float64)
+    lib.orc_merge(S, n, dv, o_part.ctypes.data, lse_part.ctypes.data, out.ctypes.data, lse.ctypes.data,
+                  None if rs is None else rs.ctypes.data)
     return out, lse
 
 

@@ -21,6 +21,13 @@
  *       m     = max_j s_j ,  w_j = exp(s_j - m),  l = sum_j w_j
  *       out   = v_scale * sum_j w_j v_j / l ,      lse = m + ln l
  *   Rows with no visible key (c <= 0) give out = 0 and lse = -inf.
+ *   Attention sinks (optional, one logit sigma_h per query head, in the units
+ *   of s_j): the softmax denominator gains exp(sigma_h) and no value, i.e.
+ *       lse' = ln(exp(lse) + exp(sigma_h)),  out' = out * exp(lse - lse')
+ *   (an empty row gets lse' = sigma_h and out' = 0); the Split-KV partials
+ *   carry no sink, the merge applies it once.                              (C)
+ *   Separate K and V page tables (optional): key j is read through k_table,
+ *   value j through v_table.                                               (D)
  *
  * Passages followed:
  *   (A) flashinfer.cake_fmha API page: the paged decode call takes query,
@@ -42,6 +49,12 @@
  *   MLA: PR #4557 page, V is the 512 latent channels of the shared 576-wide
  *       row; expressed here by passing the K pool again as the V pool with a
  *       smaller head_dim_v.
+ *   (C) The pages list `sinks` among the decode call's arguments (PR #4557
+ *       page, MLA dispatcher excerpt and the benchmark row "B1 KV1024 page64
+ *       sink") without defining them; the reading taken is one extra logit
+ *       per query head in the softmax denominator, with no value row.
+ *   (D) flashinfer.cake_fmha API page, BF16 context profiles: a q257/KV1024
+ *       profile with separate K/V page tables.
  *   Split-KV + log-sum-exp merge: PR #4557 page (Split-KV reduction, split8
  *       reducer with 32 statistics slots, two-kernel split-major ABI).  The
  *       oracle's split mode partitions [0, c) at page-aligned boundaries and
@@ -82,6 +95,7 @@ typedef struct {
   int64_t k_page_stride, k_head_stride, k_tok_stride; /* in elements */
   int64_t v_page_stride, v_head_stride, v_tok_stride;
   double scale, k_scale, v_scale;
+  const double* sinks;       /* [num_qo_heads] or NULL: no sink */
 } orc_problem;
 
 double orc_bf16_to_double(uint16_t bits) {
@@ -157,6 +171,15 @@ static void value_row(const orc_problem* p, int b, int h, int64_t j, double* vro
   for (int d = 0; d < p->head_dim_v; ++d) vrow[d] = load_elem(p->v, p->v_dtype, off + d);
 }
 
+/* Fold a sink logit into a finished row: its weight joins the denominator. */
+static void apply_sink(double* out, int dv, double* lse, double sigma) {
+  double a = *lse, hi = a > sigma ? a : sigma;
+  double lse2 = hi + log(exp(a - hi) + exp(sigma - hi));  /* a = -inf gives sigma */
+  double f = exp(a - lse2);
+  for (int d = 0; d < dv; ++d) out[d] *= f;
+  *lse = lse2;
+}
+
 /* softmax-weighted mean over keys [j0, j1) for (row t, head h).
  * Writes the normalized output (times v_scale) and the natural-log LSE;
  * an empty range gives zeros and -inf. */
@@ -217,6 +240,7 @@ int orc_attention(const orc_problem* p, const int64_t* pairs, int64_t n, double*
     }
     double l_out;
     attend_range(p, b, t, h, 0, visible_keys(p, b, t), out + k * p->head_dim_v, &l_out, s, vrow);
+    if (p->sinks) apply_sink(out + k * p->head_dim_v, p->head_dim_v, &l_out, p->sinks[h]);
     if (lse) lse[k] = l_out;
   }
   free(s);
@@ -267,9 +291,11 @@ int orc_attention_split(const orc_problem* p, int num_splits, const int64_t* pai
   return rc;
 }
 
-/* Log-sum-exp merge of num_splits partial results (layouts as above). */
+/* Log-sum-exp merge of num_splits partial results (layouts as above); row k's
+ * sink logit row_sinks[k] is applied once to the merged row when row_sinks is
+ * not NULL. */
 int orc_merge(int num_splits, int64_t n, int head_dim_v, const double* o_part,
-              const double* lse_part, double* out, double* lse) {
+              const double* lse_part, double* out, double* lse, const double* row_sinks) {
   for (int64_t k = 0; k < n; ++k) {
     double mx = -INFINITY;
     for (int sp = 0; sp < num_splits; ++sp)
@@ -277,7 +303,9 @@ int orc_merge(int num_splits, int64_t n, int head_dim_v, const double* o_part,
     double* o = out + k * head_dim_v;
     for (int d = 0; d < head_dim_v; ++d) o[d] = 0.0;
     if (mx == -INFINITY) {
-      if (lse) lse[k] = -INFINITY;
+      double l_empty = -INFINITY;
+      if (row_sinks) apply_sink(o, head_dim_v, &l_empty, row_sinks[k]);
+      if (lse) lse[k] = l_empty;
       continue;
     }
     double wsum = 0.0;
@@ -289,7 +317,9 @@ int orc_merge(int num_splits, int64_t n, int head_dim_v, const double* o_part,
       for (int d = 0; d < head_dim_v; ++d) o[d] += w * os[d];
     }
     for (int d = 0; d < head_dim_v; ++d) o[d] /= wsum;
-    if (lse) lse[k] = mx + log(wsum);
+    double l_row = mx + log(wsum);
+    if (row_sinks) apply_sink(o, head_dim_v, &l_row, row_sinks[k]);
+    if (lse) lse[k] = l_row;
   }
   return 0;
 }

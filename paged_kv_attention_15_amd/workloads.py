@@ -113,6 +113,8 @@ class Problem:
     is_decode: bool = True      # uniform q rows per request (decode / speculative rows)
     mla: bool = False           # V shares the K rows
     num_splits: int = 0         # 0 = let the planner choose
+    sinks: Optional[np.ndarray] = None           # float32 [Hq] sink logits, or None
+    v_block_tables: Optional[np.ndarray] = None  # int32 [B, max_pages] for V, None = shared
 
     @property
     def num_pages(self) -> int:
@@ -180,12 +182,18 @@ def make_problem(
     table_slack_pages: int = 0,
     rng: Optional[np.random.Generator] = None,
     num_splits: int = 0,
+    sinks: bool = False,
+    separate_v_table: bool = False,
 ) -> Problem:
     """Draw one problem.  `seq_lens` / `q_lens` are int sequences of length B.
 
     poison=True fills page tails (tokens >= L in a request's last page), the
     extra pages and the unused block-table slots' target pages with NaN, so a
-    kernel that reads anything it should not turns the output non-finite."""
+    kernel that reads anything it should not turns the output non-finite.
+
+    sinks=True draws one sink logit per query head (N(1, 1)) after everything
+    else; separate_v_table=True then moves every V page to a second random
+    placement with its own table (the key pages stay where they are)."""
     if rng is None:
         rng = np.random.default_rng(seed)
     seq_lens = np.asarray(seq_lens, dtype=np.int32).reshape(batch)
@@ -257,6 +265,25 @@ def make_problem(
                     _nan_fill(pool[perm[cursor + npg - 1], :, L % P:, :], kv_dtype)
                 cursor += npg
 
+    sink_vals = None
+    if sinks:
+        sink_vals = (1.0 + rng.standard_normal(num_qo_heads)).astype(np.float32)
+    v_tables = None
+    if separate_v_table:
+        if v_pool is None:
+            raise ValueError("separate V tables need a separate V pool")
+        perm_v = rng.permutation(num_pages).astype(np.int32)
+        moved = np.empty_like(v_pool)
+        moved[perm_v] = v_pool[perm]  # logical page i: from perm[i] to perm_v[i]
+        v_pool = moved
+        v_tables = np.zeros_like(block_tables)
+        v_poison = int(perm_v[needed]) if extra > 0 else 0
+        cursor = 0
+        for b, npg in enumerate(pages_per_req):
+            v_tables[b, :npg] = perm_v[cursor:cursor + npg]
+            v_tables[b, npg:] = v_poison
+            cursor += npg
+
     if layout == NHD:
         k_pool = np.ascontiguousarray(k_pool.transpose(0, 2, 1, 3))
         if v_pool is not None:
@@ -270,7 +297,7 @@ def make_problem(
         q_dtype=q_dtype, kv_dtype=kv_dtype, o_dtype=o_dtype, q=q, k_pool=k_pool,
         v_pool=v_pool, block_tables=block_tables, seq_lens=seq_lens, q_indptr=q_indptr,
         scale=float(scale), k_scale=k_scale, v_scale=v_scale, causal=causal,
-        is_decode=is_decode, mla=mla, num_splits=num_splits,
+        is_decode=is_decode, mla=mla, num_splits=num_splits, sinks=sink_vals, v_block_tables=v_tables,
     )
 
 

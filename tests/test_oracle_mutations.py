@@ -40,6 +40,9 @@ MUTATIONS = {
     "v-row-from-next-token": ("int64_t off = key_offset(page, g, j % p->page_size, p->v_page_stride",
                               "int64_t off = key_offset(page, g, (j + 1) % p->page_size, p->v_page_stride"),
     "max-not-subtracted-lse": ("*lse = m + log(l);", "*lse = log(l);"),
+    "sink-weight-sign": ("double lse2 = hi + log(exp(a - hi) + exp(sigma - hi));",
+                         "double lse2 = hi + log(exp(a - hi) + exp(hi - sigma));"),
+    "sink-output-not-rescaled": ("for (int d = 0; d < dv; ++d) out[d] *= f;", "for (int d = 0; d < dv; ++d) out[d] *= 1.0;"),
 }
 
 

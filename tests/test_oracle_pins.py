@@ -9,6 +9,7 @@ least one of them (tests/test_oracle_mutations.py checks exactly that).
 """
 from __future__ import annotations
 
+import dataclasses
 import json
 import math
 import os
@@ -321,3 +322,97 @@ def test_merge_with_all_empty_partitions():
     l = np.full((3, 2), -np.inf)
     mo, ml = oracle.merge(o, l)
     assert np.array_equal(mo, np.zeros((2, 4))) and np.isneginf(ml).all()
+
+
+# --------------------------------------------------------------------------
+# attention sinks and separate K/V page tables
+# --------------------------------------------------------------------------
+
+def _sink_problem(**kw):
+    base = dict(name="sinks", seed=31, batch=3, seq_lens=[37, 100, 5], q_lens=[2, 2, 2], num_qo_heads=4,
+                num_kv_heads=2, head_dim_qk=32, head_dim_v=32, page_size=16, q_dtype=W.F32, kv_dtype=W.F32,
+                sinks=True)
+    base.update(kw)
+    return W.make_problem(**base)
+
+
+def test_sinks_match_a_dense_softmax_with_an_extra_logit():
+    # brute force: the sink is one more logit in the row's softmax whose value row is zero
+    prob = _sink_problem()
+    out, lse = oracle.attention(prob)
+    kd = R.decode_storage(prob.k_pool, prob.kv_dtype)
+    vd = R.decode_storage(prob.v_pool, prob.kv_dtype)
+    qd = R.decode_storage(prob.q, prob.q_dtype)
+    G = prob.num_qo_heads // prob.num_kv_heads
+    k = 0
+    for b in range(prob.batch):
+        L = int(prob.seq_lens[b])
+        n = int(prob.q_indptr[b + 1] - prob.q_indptr[b])
+        idx = np.arange(L)
+        pages = prob.block_tables[b, idx // prob.page_size]
+        for i in range(n):
+            t = int(prob.q_indptr[b]) + i
+            c = L - n + i + 1
+            for h in range(prob.num_qo_heads):
+                kk = torch.from_numpy(kd[pages, h // G, idx % prob.page_size, :][:c])
+                vv = torch.from_numpy(vd[pages, h // G, idx % prob.page_size, :][:c])
+                s = prob.scale * (kk @ torch.from_numpy(qd[t, h]))
+                s = torch.cat([s, torch.tensor([float(prob.sinks[h])], dtype=torch.float64)])
+                w = torch.softmax(s, 0)
+                ref = (w[:-1, None] * vv).sum(0).numpy()
+                row = t * prob.num_qo_heads + h
+                np.testing.assert_allclose(out[row], ref, rtol=1e-12, atol=1e-14)
+                assert lse[row] == pytest.approx(float(torch.logsumexp(s, 0)), rel=1e-13)
+                k += 1
+    assert k == prob.total_q * prob.num_qo_heads
+
+
+def test_sink_closed_forms_and_neutral_sink():
+    # one key: out = v * logistic(s - sigma), lse = ln(e^s + e^sigma); sigma = -inf is no sink
+    q = np.array([[[1.0, 2.0]]], np.float32)
+    k = [np.array([[[0.5, -1.0]]], np.float32)]
+    v = [np.array([[[3.0, -2.0]]], np.float32)]
+    prob = R.paged_problem_from_dense(k, v, q, [1], [1], 1, rng=np.random.default_rng(0), scale=0.7)
+    s = 0.7 * (0.5 - 2.0)
+    for sigma in (0.3, -4.0, 6.0):
+        out, lse = oracle.attention(dataclasses.replace(prob, sinks=np.array([sigma], np.float32)))
+        sig = np.float64(np.float32(sigma))
+        w = 1.0 / (1.0 + math.exp(sig - s))
+        np.testing.assert_allclose(out[0], [3.0 * w, -2.0 * w], rtol=1e-14)
+        assert lse[0] == pytest.approx(math.log(math.exp(s) + math.exp(sig)), rel=1e-14)
+    base = oracle.attention(prob)
+    neutral = oracle.attention(dataclasses.replace(prob, sinks=np.array([-np.inf], np.float32)))
+    assert np.array_equal(base[0], neutral[0]) and np.array_equal(base[1], neutral[1])
+
+
+def test_sink_on_a_row_with_no_visible_key():
+    prob = _sink_problem(seq_lens=[1, 3, 5], q_lens=[2, 1, 1])  # request 0: row 0 sees no key
+    out, lse = oracle.attention(prob)
+    rows = [0 * prob.num_qo_heads + h for h in range(prob.num_qo_heads)]
+    assert np.array_equal(out[rows], np.zeros_like(out[rows]))
+    np.testing.assert_array_equal(lse[rows], prob.sinks.astype(np.float64))
+
+
+@pytest.mark.parametrize("S", [2, 7])
+def test_split_merge_with_sinks_equals_unsplit(S):
+    prob = _sink_problem()
+    full_o, full_l = oracle.attention(prob)
+    o_part, l_part = oracle.attention_split(prob, S)
+    pairs = oracle.all_pairs(prob)
+    mo, ml = oracle.merge(o_part, l_part, row_sinks=prob.sinks[pairs[:, 1]].astype(np.float64))
+    np.testing.assert_allclose(mo, full_o, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(ml, full_l, rtol=1e-12, atol=1e-13)
+
+
+def test_separate_value_table_moves_only_the_value_pages():
+    # the same draws with V pages placed through their own table give bitwise the same result
+    shared = _sink_problem(sinks=False, poison=True, extra_page_frac=0.25, table_slack_pages=1)
+    split_tab = _sink_problem(sinks=False, poison=True, extra_page_frac=0.25, table_slack_pages=1,
+                              separate_v_table=True)
+    assert not np.array_equal(shared.block_tables, split_tab.v_block_tables)
+    a = oracle.attention(shared)
+    b = oracle.attention(split_tab)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    # and reading V through the key table instead gives something else
+    wrong = dataclasses.replace(split_tab, v_block_tables=None)
+    assert not np.allclose(oracle.attention(wrong)[0], a[0], equal_nan=True)
