@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 2
+#define PKV_ABI_VERSION 3
 
 typedef enum pkv_status {
   PKV_OK = 0,
@@ -145,6 +145,20 @@ typedef struct pkv_args {
      reducer kernel.  Calls that share one counter buffer must not overlap in
      time (same stream, or otherwise ordered).  Ignored by every other plan. */
   int32_t* merge_counters;
+  /* Optional attention sinks: fp32 [num_qo_heads] device array, one logit per
+     query head in the units of the scaled scores (scale * k_scale * q.k).  Its
+     weight joins each row's softmax denominator and carries no value:
+     lse = ln(sum_j e^{s_j} + e^{sink}) and the output shrinks by the same
+     factor; a row with no visible key reports lse = sink.  The pages list
+     `sinks` among the decode arguments (PR #4557 page, MLA dispatcher excerpt)
+     without defining them: this is the reading taken.  NULL: no sink. */
+  const float* sinks;
+  /* Optional separate V page table [B, table_stride] (flashinfer.cake_fmha API
+     page: a context profile with separate K/V page tables): value j of request
+     b is read from page v_block_tables[b][j / P].  NULL: V shares block_tables.
+     Served by the generic kernel (PKV_ERR_UNSUPPORTED for a kernel_hint of
+     another family). */
+  const int32_t* v_block_tables;
 
   int64_t q_stride_tok, q_stride_head;
   int64_t o_stride_tok, o_stride_head;

@@ -67,6 +67,10 @@ pkv_status validate(const pkv_args* a, bool is_context) {
   if (!a) return fail(PKV_ERR_INVALID_ARG, "args is NULL");
   if ((reinterpret_cast<uintptr_t>(a->merge_counters) & 3u) != 0)
     return fail(PKV_ERR_INVALID_ARG, "merge_counters must be 4-byte aligned");
+  if (a->v_block_tables && a->v_shares_k)
+    return fail(PKV_ERR_INVALID_ARG, "v_block_tables with v_shares_k: V rows are the K rows");
+  if ((reinterpret_cast<uintptr_t>(a->sinks) | reinterpret_cast<uintptr_t>(a->v_block_tables)) & 3u)
+    return fail(PKV_ERR_INVALID_ARG, "sinks and v_block_tables must be 4-byte aligned");
   if (a->batch < 0) return fail(PKV_ERR_INVALID_ARG, "batch must be >= 0 (got %d)", a->batch);
   if (a->num_kv_heads < 1 || a->num_qo_heads < 1 || a->num_qo_heads % a->num_kv_heads != 0)
     return fail(PKV_ERR_INVALID_ARG, "num_qo_heads (%d) must be a positive multiple of num_kv_heads (%d)",
@@ -159,6 +163,7 @@ bool mfma_eligible(const pkv_args* a) {
 bool kernel_supports(int32_t k, const pkv_args* a, bool is_context) {
   if (k == pkv::KERNEL_GENERIC) return a->head_dim_qk <= 1024 && a->head_dim_v <= 512;
   if (k <= pkv::KERNEL_GENERIC || k >= pkv::KERNEL_COUNT || !mfma_eligible(a)) return false;
+  if (a->v_block_tables) return false;  // separate V tables: the generic kernel
   const bool fp8 = a->kv_dtype == PKV_DTYPE_FP8_E4M3;
   const int G = a->num_qo_heads / a->num_kv_heads;
   const bool d128 = a->head_dim_qk == 128 && a->head_dim_v == 128 && !a->v_shares_k;
@@ -258,7 +263,7 @@ int32_t seg_cost_pages(const pkv_args* a) {
 }
 
 int32_t choose_kernel(const pkv_args* a, bool is_context) {
-  if (!mfma_eligible(a)) return pkv::KERNEL_GENERIC;
+  if (!mfma_eligible(a) || a->v_block_tables) return pkv::KERNEL_GENERIC;
   const bool fp8 = a->kv_dtype == PKV_DTYPE_FP8_E4M3;
   const int G = a->num_qo_heads / a->num_kv_heads;
   // Measured on MI355X (bf16 GQA decode B32/L4096, e4m3 ragged decode B16, MLA
@@ -465,6 +470,8 @@ pkv_status run(const pkv_args* a, bool is_context, void* ws, size_t ws_bytes, vo
   p.scale = a->scale;
   p.k_scale = a->k_scale;
   p.v_scale = a->v_scale;
+  p.sinks = a->sinks;
+  p.v_table = a->v_block_tables;
   p.page_list_cap = plan.pages_per_split;
   if (plan.schedule == 1) {
     p.stream = 1;
@@ -517,6 +524,7 @@ pkv_status run(const pkv_args* a, bool is_context, void* ws, size_t ws_bytes, vo
     mp.max_q_len = p.max_q_len;
     mp.total_q = p.total_q;
     mp.err_word = a->err_word;
+    mp.sinks = a->sinks;
     mp.vec4 = a->head_dim_v % 4 == 0;  // the workspace partials are 256-byte aligned
     if (p.stream) {
       mp.stream = 1;

@@ -467,8 +467,9 @@ __device__ __forceinline__ void dma_block(const KParams& p, unsigned char* smem,
   for (int rt = 0; rt < C::RT; ++rt) {
     if (!row_ok[rt]) continue;
     const bool empty = !(l_run[rt] > 0.f);
-    const float inv = empty ? 0.f : v_scale / l_run[rt];
-    const float lse = empty ? -INFINITY : (m_run[rt] * kLn2 + __logf(l_run[rt]));
+    float inv = empty ? 0.f : v_scale / l_run[rt];
+    float lse = empty ? -INFINITY : (m_run[rt] * kLn2 + __logf(l_run[rt]));
+    if (p.sinks && !split_mode) inv *= fold_sink(lse, p.sinks[row_h[rt]]);  // split: the reducer adds it
     const int64_t row_g = (int64_t)row_t[rt] * p.num_qo_heads + row_h[rt];
     if (split_mode) {
       const int64_t prow = p.stream ? (int64_t)slot * p.slot_rows + row_R[rt] : (int64_t)slot * p.rows_total + row_g;
@@ -605,18 +606,19 @@ __device__ __forceinline__ void merge_unit(const KParams& p, const int* s_slot, 
 #pragma unroll
   for (int j = 0; j < J; ++j) {
     if (threadIdx.x + j * C::NTHR >= nitem) continue;
-    const float inv = l[j] > 0.f ? 1.f / l[j] : 0.f;
-    const f32x4 o = acc[j] * inv;
     const int64_t t = (int64_t)su.b * p.q_len + R[j] / G;
     const int h = su.g * G + R[j] % G;
+    float inv = l[j] > 0.f ? 1.f / l[j] : 0.f;
+    float lse_row = (m[j] == -INFINITY) ? -INFINITY : m[j] + __logf(l[j]);
+    if (p.sinks) inv *= fold_sink(lse_row, p.sinks[h]);
+    const f32x4 o = acc[j] * inv;
     if (p.o_dtype == PKV_DTYPE_BF16) {
       __bf16* dst = (__bf16*)p.out + t * p.o_st + h * p.o_sh + 4 * c4[j];
       *(u32x2*)dst = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
     } else {
       *(f32x4*)((float*)p.out + t * p.o_st + h * p.o_sh + 4 * c4[j]) = o;
     }
-    if (c4[j] == 0 && p.lse_out)
-      p.lse_out[t * p.num_qo_heads + h] = (m[j] == -INFINITY) ? -INFINITY : m[j] + __logf(l[j]);
+    if (c4[j] == 0 && p.lse_out) p.lse_out[t * p.num_qo_heads + h] = lse_row;
   }
 }
 
@@ -709,7 +711,7 @@ __global__ __launch_bounds__(C::NTHR) void attn_dma_stream_kernel(const KParams 
         const int h = rr % p.num_qo_heads;
         if (p.o_dtype == PKV_DTYPE_BF16) ((__bf16*)p.out)[t * p.o_st + h * p.o_sh + d] = (__bf16)0.f;
         else ((float*)p.out)[t * p.o_st + h * p.o_sh + d] = 0.f;
-        if (d == 0 && p.lse_out) p.lse_out[t * p.num_qo_heads + h] = -INFINITY;
+        if (d == 0 && p.lse_out) p.lse_out[t * p.num_qo_heads + h] = p.sinks ? p.sinks[h] : -INFINITY;
       }
     }
   }

@@ -102,7 +102,15 @@ __global__ __launch_bounds__(64) void attn_generic_kernel(const KParams p) {
       }
       const int off = tok % p.page_size;
       const int64_t koff = (int64_t)pg * p.k_sp + (int64_t)g * p.k_sh + (int64_t)off * p.k_stok;
-      voff = (int64_t)pg * p.v_sp + (int64_t)g * p.v_sh + (int64_t)off * p.v_stok;
+      int vpg = pg;
+      if (p.v_table) {
+        vpg = p.v_table[(int64_t)b * p.table_stride + tok / p.page_size];
+        if (p.num_pages > 0 && (vpg < 0 || vpg >= p.num_pages)) {
+          flag_error(p.err_word, PKV_DEVERR_PAGE_RANGE);
+          vpg = min(max(vpg, 0), p.num_pages - 1);
+        }
+      }
+      voff = (int64_t)vpg * p.v_sp + (int64_t)g * p.v_sh + (int64_t)off * p.v_stok;
       float dot = 0.f;
       for (int d = 0; d < p.head_dim_qk; ++d) dot += s_q[d] * load_elem(p.k, koff + d, p.kv_dtype);
       s = dot * sc2;
@@ -133,8 +141,9 @@ __global__ __launch_bounds__(64) void attn_generic_kernel(const KParams p) {
   }
 
   const bool empty = !(l_run > 0.f);
-  const float inv = empty ? 0.f : v_scale / l_run;
-  const float lse = empty ? -INFINITY : (m_run * kLn2 + __logf(l_run));
+  float inv = empty ? 0.f : v_scale / l_run;
+  float lse = empty ? -INFINITY : (m_run * kLn2 + __logf(l_run));
+  if (p.sinks && p.ws_o == nullptr) inv *= fold_sink(lse, p.sinks[h]);  // split partials: the reducer adds it
   const int64_t row_g = (int64_t)t * p.num_qo_heads + h;
   if (p.ws_o != nullptr) {
     if (lane == 0) p.ws_lse[(int64_t)split * p.rows_total + row_g] = lse;
@@ -275,7 +284,9 @@ __device__ __forceinline__ void merge_row(const MergeParams& mp, const MergeRow&
       }
       m = M;
     }
-    const float inv = l > 0.f ? 1.f / l : 0.f;
+    float inv = l > 0.f ? 1.f / l : 0.f;
+    float lse_row = (m == -INFINITY) ? -INFINITY : m + __logf(l);
+    if (mp.sinks) inv *= fold_sink(lse_row, mp.sinks[h]);
 #pragma unroll
     for (int c = 0; c < CW; ++c) {
       const int d = q * CW + c;
@@ -287,7 +298,7 @@ __device__ __forceinline__ void merge_row(const MergeParams& mp, const MergeRow&
         ((float*)mp.out)[oi] = acc[c] * inv;
       }
     }
-    if (mp.lse_out && q == 0) mp.lse_out[r] = (m == -INFINITY) ? -INFINITY : m + __logf(l);
+    if (mp.lse_out && q == 0) mp.lse_out[r] = lse_row;
   }
   if (S_sub == 1) __syncthreads();  // matches the idle threads' barrier
 }

@@ -848,8 +848,9 @@ __device__ __forceinline__ void m32_block(const KParams& p, unsigned char* smem,
   for (int rb = 0; rb < C::RB; ++rb) {
     if (!row_ok[rb]) continue;
     const bool empty = !(l_run[rb] > 0.f);
-    const float inv = empty ? 0.f : v_scale / l_run[rb];
-    const float lse = empty ? -INFINITY : (m_run[rb] * kLn2 + __logf(l_run[rb]));
+    float inv = empty ? 0.f : v_scale / l_run[rb];
+    float lse = empty ? -INFINITY : (m_run[rb] * kLn2 + __logf(l_run[rb]));
+    if (p.sinks && !split_mode) inv *= fold_sink(lse, p.sinks[row_h[rb]]);  // split: the reducer adds it
     const int64_t row_g = (int64_t)row_t[rb] * p.num_qo_heads + row_h[rb];
     if (split_mode) {
       const int64_t prow = (int64_t)slot * p.rows_total + row_g;

@@ -440,8 +440,9 @@ __device__ __forceinline__ void attend_block(const KParams& p, unsigned char* sm
   for (int rt = 0; rt < C::RT; ++rt) {
     if (!row_ok[rt]) continue;
     const bool empty = !(l_run[rt] > 0.f);
-    const float inv = empty ? 0.f : v_scale / l_run[rt];
-    const float lse = empty ? -INFINITY : (m_run[rt] * kLn2 + __logf(l_run[rt]));
+    float inv = empty ? 0.f : v_scale / l_run[rt];
+    float lse = empty ? -INFINITY : (m_run[rt] * kLn2 + __logf(l_run[rt]));
+    if (p.sinks && !split_mode) inv *= fold_sink(lse, p.sinks[row_h[rt]]);  // split: the reducer adds it
     const int64_t row_g = (int64_t)row_t[rt] * p.num_qo_heads + row_h[rt];
     if (split_mode) {
       const int64_t prow = p.stream ? (int64_t)slot * p.slot_rows + row_R[rt] : (int64_t)slot * p.rows_total + row_g;

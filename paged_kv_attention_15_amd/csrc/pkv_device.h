@@ -149,6 +149,21 @@ struct StreamGeom {
   __device__ bool owns_any(int64_t w) const { return (w + 1) * TV / W > w * TV / W; }
 };
 
+// ---------------------------------------------------------------- attention sinks
+// A sink logit sigma (natural-log units, the units of the scaled scores) folded
+// into a finished row: its weight joins the softmax denominator and carries no
+// value, so lse becomes ln(e^lse + e^sigma) and the row's output is multiplied
+// by the returned e^(lse_old - lse_new) (0 for a row with no visible key, which
+// then reports lse = sigma).  sigma = -inf leaves the row unchanged.
+__device__ __forceinline__ float fold_sink(float& lse, float sigma) {
+  if (sigma == -INFINITY) return 1.f;
+  const float hi = fmaxf(lse, sigma);
+  const float lse2 = hi + __logf(__expf(lse - hi) + __expf(sigma - hi));
+  const float f = __expf(lse - lse2);
+  lse = lse2;
+  return f;
+}
+
 // ---------------------------------------------------------------- error word
 __device__ __forceinline__ void flag_error(int32_t* err_word, int32_t bits) {
   if (err_word) atomicOr(err_word, bits);

@@ -85,6 +85,8 @@ struct KParams {
   // balanced schedule with the fused reducer: one zero-at-rest counter per
   // (request, KV head); null selects the separate reducer kernel
   int32_t* counters;
+  const float* sinks;      // [num_qo_heads] sink logits, or null
+  const int32_t* v_table;  // separate V page table (generic kernel only), or null
 };
 
 struct LaunchShape {
@@ -116,6 +118,7 @@ struct MergeParams {
   int32_t* err_word;
   // 1: head_dim_v % 4 == 0 and o_part 16-byte aligned (partial rows read 16 bytes at a time)
   int32_t vec4;
+  const float* sinks;  // [num_qo_heads] sink logits folded into each merged row, or null
 };
 hipError_t launch_merge(const MergeParams& mp, hipStream_t s);
 

@@ -51,6 +51,7 @@ class PkvArgs(C.Structure):
         ("block_tables", C.c_void_p), ("seq_lens", C.c_void_p), ("q_indptr", C.c_void_p),
         ("out", C.c_void_p), ("lse_out", C.c_void_p), ("err_word", C.c_void_p),
         ("k_scale_dev", C.c_void_p), ("v_scale_dev", C.c_void_p), ("merge_counters", C.c_void_p),
+        ("sinks", C.c_void_p), ("v_block_tables", C.c_void_p),
         ("q_stride_tok", C.c_int64), ("q_stride_head", C.c_int64),
         ("o_stride_tok", C.c_int64), ("o_stride_head", C.c_int64),
         ("k_stride_page", C.c_int64), ("k_stride_head", C.c_int64), ("k_stride_tok", C.c_int64),
@@ -235,6 +236,7 @@ def upload(prob, device="cuda", with_lse: bool = True, with_err: bool = True, nu
 
     merge_counters: give the balanced decode schedule a zeroed counter buffer
     (the in-kernel reducer); other plans ignore it."""
+    import numpy as np
     torch = _torch()
     t = {}
     t["q"] = _to_device(prob.q, device)
@@ -250,6 +252,10 @@ def upload(prob, device="cuda", with_lse: bool = True, with_err: bool = True, nu
         t["lse"] = torch.full((prob.total_q, prob.num_qo_heads), float("nan"), dtype=torch.float32, device=device)
     if with_err:
         t["err"] = torch.zeros(1, dtype=torch.int32, device=device)
+    if getattr(prob, "sinks", None) is not None:
+        t["sinks"] = torch.from_numpy(np.ascontiguousarray(prob.sinks, dtype=np.float32)).to(device)
+    if getattr(prob, "v_block_tables", None) is not None:
+        t["v_table"] = torch.from_numpy(np.ascontiguousarray(prob.v_block_tables, dtype=np.int32)).to(device)
     if device_scales:
         t["k_scale"] = torch.tensor([prob.k_scale], dtype=torch.float32, device=device)
         t["v_scale"] = torch.tensor([prob.v_scale], dtype=torch.float32, device=device)
@@ -301,6 +307,8 @@ def fill_args(prob, t: dict, num_splits: Optional[int] = None) -> PkvArgs:
     a.err_word = t["err"].data_ptr() if t.get("err") is not None else 0
     a.k_scale_dev = t["k_scale"].data_ptr() if "k_scale" in t else 0
     a.v_scale_dev = t["v_scale"].data_ptr() if "v_scale" in t else 0
+    a.sinks = t["sinks"].data_ptr() if "sinks" in t else 0
+    a.v_block_tables = t["v_table"].data_ptr() if "v_table" in t else 0
     D, Dv = prob.head_dim_qk, prob.head_dim_v
     a.q_stride_tok = prob.num_qo_heads * D
     a.q_stride_head = D

@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
     assert set(declared) == set(pkv.EXPORTED)
     for name in declared:
         assert hasattr(lib, name), name
-    assert pkv.pkv_abi_version() == 2
+    assert pkv.pkv_abi_version() == 3
 
 
 def test_ctypes_mirror_matches_c_layout(tmp_path):
@@ -283,3 +283,18 @@ def test_append_e4m3_needs_scales_and_empty_calls_are_noops():
     assert pkv.pkv_append(bad, 0, check=False) == pkv.PKV_ERR_INVALID_ARG
     assert pkv.pkv_append(_append_args(batch=0), 0, check=False) == pkv.PKV_OK
     assert pkv.pkv_append(_append_args(num_tokens=0, clear_tail=0), 0, check=False) == pkv.PKV_OK
+
+
+def test_separate_value_tables_route_to_the_generic_kernel():
+    a = _args_for(_fake())
+    a.q = a.k_pages = a.v_pages = a.out = 0x1000
+    a.v_block_tables = 0x2000
+    assert pkv.KERNEL_NAMES[pkv.pkv_plan(a).kernel] == "generic"
+    a.kernel_hint = pkv.KERNEL_IDS["gqa_bf16"]
+    assert pkv.pkv_plan(a, check=False).status == pkv.PKV_ERR_UNSUPPORTED
+    a.kernel_hint = 0
+    a.v_shares_k = 1
+    assert pkv.pkv_plan(a, check=False).status == pkv.PKV_ERR_INVALID_ARG
+    a.v_shares_k = 0
+    a.sinks = 0x2002
+    assert pkv.pkv_plan(a, check=False).status == pkv.PKV_ERR_INVALID_ARG

@@ -317,6 +317,64 @@ def test_graph_replay_matches_eager(case):
         assert torch.equal(dp.out, eager_out)
 
 
+# ----------------------------------------------------------------- attention sinks, separate V tables
+
+@pytest.mark.parametrize("kernel,kv,splits,counters", [
+    (None, W.BF16, None, False), ("gqa_bf16", W.BF16, 3, False), ("dma_gqa_bf16", W.BF16, 1, False),
+    ("dma_gqa_fp8_n2", W.E4M3, -1, False), ("dma_gqa_fp8_n2", W.E4M3, -1, True), ("generic", W.BF16, None, False),
+])
+def test_sinks_decode(kernel, kv, splits, counters):
+    P = 64 if kv == W.E4M3 else 32
+    prob = _gqa([1, 31, 64, 65, 700, 1300], hq=64 if kv == W.E4M3 else 32, hkv=8, P=P, kv=kv, sinks=True)
+    say(f"case sinks decode {kernel} splits={splits} counters={counters}")
+    dp = pkv.upload(prob, "cuda", num_splits=splits, kernel=kernel, merge_counters=counters)
+    dp.run()
+    torch.cuda.synchronize()
+    compare(prob, dp, label=f"sinks {kernel}/{splits}/{counters}")
+
+
+def test_sinks_speculative_rows_with_an_empty_row():
+    # request 0 has 3 rows over 2 keys: its first row sees no key and reports lse = sink
+    prob = _gqa([2, 300, 77], q_lens=[3, 3, 3], hq=16, hkv=4, sinks=True)
+    compare(prob, run_gpu(prob, num_splits=-1), expect_err=pkv.PKV_DEVERR_SEQ_LT_QLEN)
+
+
+@pytest.mark.parametrize("kernel,splits", [(None, None), ("m32_ctx_w8", 3), ("dma_wide_bf16", None)])
+def test_sinks_context(kernel, splits):
+    prob = W.make_problem(name="ctx-sinks", seed=9, batch=3, seq_lens=[70, 5, 333], q_lens=[64, 5, 130],
+                          num_qo_heads=16, num_kv_heads=2, head_dim_qk=128, head_dim_v=128, page_size=16,
+                          is_decode=False, poison=True, extra_page_frac=0.3, table_slack_pages=1, sinks=True)
+    dp = pkv.upload(prob, "cuda", kernel=kernel, num_splits=splits)
+    dp.run()
+    torch.cuda.synchronize()
+    compare(prob, dp, label=f"ctx sinks {kernel}/{splits}")
+
+
+@pytest.mark.parametrize("q_len", [1, 2])
+def test_sinks_mla(q_len):
+    prob = W.make_problem(name=f"mla-sinks-q{q_len}", seed=3, batch=3, seq_lens=[2, 70, 300],
+                          q_lens=[q_len] * 3, num_qo_heads=128, num_kv_heads=1, head_dim_qk=576,
+                          head_dim_v=512, page_size=64, mla=True, scale=1 / 24.0, poison=True,
+                          extra_page_frac=0.3, table_slack_pages=1, sinks=True)
+    compare(prob, run_gpu(prob))
+
+
+@pytest.mark.parametrize("decode", [True, False])
+def test_separate_value_tables(decode):
+    if decode:
+        prob = _gqa([1, 31, 64, 65, 700], separate_v_table=True, sinks=True)
+    else:
+        prob = W.make_problem(name="ctx-vtab", seed=12, batch=2, seq_lens=[300, 40], q_lens=[30, 40],
+                              num_qo_heads=16, num_kv_heads=2, head_dim_qk=128, head_dim_v=128, page_size=16,
+                              is_decode=False, poison=True, extra_page_frac=0.3, table_slack_pages=1,
+                              separate_v_table=True)
+    dp = pkv.upload(prob, "cuda")
+    assert pkv.KERNEL_NAMES[pkv.pkv_plan(dp.args, dp.is_context).kernel] == "generic"
+    dp.run()
+    torch.cuda.synchronize()
+    compare(prob, dp, label=f"separate V tables decode={decode}")
+
+
 def test_nhd_layout_matches_oracle():
     prob = _gqa([40, 129], layout=W.NHD)
     say(f"case {prob.name} NHD")
