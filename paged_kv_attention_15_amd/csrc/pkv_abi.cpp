@@ -269,7 +269,9 @@ int32_t choose_kernel(const pkv_args* a, bool is_context) {
   // Measured on MI355X (bf16 GQA decode B32/L4096, e4m3 ragged decode B16, MLA
   // B512/L4096, causal context B4 q511/L2047): register-staged tiles win for
   // bf16 decode, the direct-to-LDS ring for e4m3 decode (two-wave groups, four
-  // per CU) and MLA, the 32x32 MFMA family with two waves per SIMD for bf16 context.
+  // per CU) and MLA, the 32x32 MFMA family with two waves per SIMD for bf16
+  // context (the variant with the next block's S^T interleaved with the softmax
+  // measured within +-3 % of it over five runs on different boxes).
   if (a->head_dim_qk == 128 && a->head_dim_v == 128 && !a->v_shares_k) {
     const int64_t rows = is_context ? (int64_t)a->max_q_len * G : (int64_t)a->q_len * G;
     if (!is_context && rows <= 16) return fp8 ? pkv::KERNEL_DMA_GQA_FP8_N2 : pkv::KERNEL_GQA_BF16;

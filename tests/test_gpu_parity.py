@@ -375,6 +375,28 @@ def test_separate_value_tables(decode):
     compare(prob, dp, label=f"separate V tables decode={decode}")
 
 
+@pytest.mark.parametrize("separate", [False, True])
+def test_context_q257_kv1024_page1024_profile(separate):
+    # the API page's second BF16 context profile: four requests of 257 rows over
+    # 1024 keys, 1024-token pages, separate K/V page tables (and the shared form)
+    prob = W.make_problem(name=f"ctx-q257-kv1024-p1024-sep{int(separate)}", seed=13, batch=4,
+                          seq_lens=[1024] * 4, q_lens=[257] * 4, num_qo_heads=64, num_kv_heads=8,
+                          head_dim_qk=128, head_dim_v=128, page_size=1024, is_decode=False, poison=True,
+                          extra_page_frac=0.25, table_slack_pages=1, separate_v_table=separate)
+    say(f"case {prob.name}")
+    dp = run_gpu(prob)
+    compare(prob, dp, sample_pairs(prob, 192))
+
+
+@pytest.mark.parametrize("P", [1, 2, 1024])
+def test_extreme_page_sizes_decode(P):
+    prob = _gqa([1, 3, 1000, 2049], P=P)
+    say(f"case decode P={P}")
+    dp = run_gpu(prob)
+    say(f"  kernel {pkv.KERNEL_NAMES[pkv.pkv_plan(dp.args).kernel]}")
+    compare(prob, dp)
+
+
 def test_nhd_layout_matches_oracle():
     prob = _gqa([40, 129], layout=W.NHD)
     say(f"case {prob.name} NHD")
@@ -483,7 +505,7 @@ def test_context_kernel_families_match_oracle(kernel, splits):
     compare(prob, dp, label=f"{kernel}/{splits}")
 
 
-@pytest.mark.parametrize("kernel", ["m32_ctx_bf16", "m32_ctx_pp", "m32_ctx_iw"])
+@pytest.mark.parametrize("kernel", ["m32_ctx_bf16", "m32_ctx_pp", "m32_ctx_iw", "m32_ctx_w8"])
 def test_context_full_size_m32(kernel):
     prob = W.context_b4_q511_kv2047()
     say(f"case {prob.name} kernel={kernel}")
