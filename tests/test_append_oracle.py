@@ -16,8 +16,21 @@ import os
 import numpy as np
 import torch
 
-import oracle.append as A
 from paged_kv_attention_15_amd import workloads as W
+
+if os.environ.get("PKV_APPEND_ORACLE"):
+    # tests/test_append_oracle_mutations.py points this at a deliberately broken
+    # copy of oracle/append.py; nothing else sets it
+    import importlib.util
+
+    _spec = importlib.util.spec_from_file_location("append_mut", os.environ["PKV_APPEND_ORACLE"])
+    A = importlib.util.module_from_spec(_spec)
+    import sys
+
+    sys.modules["append_mut"] = A  # dataclasses resolve annotations through sys.modules
+    _spec.loader.exec_module(A)
+else:
+    import oracle.append as A
 
 GOLD = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -152,6 +165,7 @@ def test_brute_force_positions_and_rotation_angles():
             key = (int(prob.block_tables[b, pos // prob.page_size]), pos % prob.page_size, 0)
             z = (x[r, 8, :64] + 1j * x[r, 8, 64:]) * np.exp(1j * pos * f)
             np.testing.assert_allclose(res.k_rows[key], np.concatenate([z.real, z.imag]), atol=1e-5)
+            np.testing.assert_array_equal(res.v_rows[key], x[r, 9])  # values: neither normed nor rotated
             r += 1
     assert r == prob.total_tokens
 
