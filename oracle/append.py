@@ -21,11 +21,20 @@ append", summary paragraph; PR #5956 body quoted on it, section "Contract"):
     to slot pos % P of page block_tables[b][pos / P] of the NHD caches, as bf16
     or as e4m3 codes of x / k_scale and x / v_scale;
   * with tail clearing, rows [last + 1, P) of every nonempty request's last
-    page are zeroed in both caches, last = (seq_lens[b] - 1) % P.
+    page are zeroed in both caches, last = (seq_lens[b] - 1) % P;
+  * optional e4m3 query output (the same Contract section): with the dynamic
+    policy each (row, head) gets its own scale q_scale = max(max_i |y_i|,
+    1e-6) / upper_max and the stored payload is y / q_scale; with the static
+    policy the payload is y * q_scale_inv and no scale is written.  The
+    dynamic scales sit at [T, Hq] (decode) or at [B, Hq, stride], entry
+    (b, h, i) for the request's i-th new row (prefill; the pages size the
+    last axis as max_seqlen rounded up to 128).
 Reading where the pages are silent: a request whose rows do not fit its
 length, the table or the rotary table (seq_lens[b] < rows, a position past
 the table width or past max_pos) is skipped entirely (nothing written, its
-tail not cleared) and reported.
+tail not cleared) and reported; so is a request with more new rows than
+the prefill scale layout's stride.  The static policy multiplies by
+q_scale_inv (the argument's name: the inverse of a scale).
 
 Returns expected *values* (float64), never storage bits: the tests compare the
 HIP path's bf16 rows with the pages' tolerance and its e4m3 codes against the
@@ -70,9 +79,22 @@ def rope(x: np.ndarray, cs_row: np.ndarray) -> np.ndarray:
     return np.concatenate([lo * c - hi * s, hi * c + lo * s])
 
 
+# query output policies
+Q_BF16, Q_DYNAMIC, Q_STATIC = 0, 1, 2
+Q_SCALE_FLOOR = 1e-6
+
+
+def q_scale_index(prob, b: int, h: int, r: int, lo: int) -> int:
+    """Flat position of the dynamic scale of row r (request b starting at row lo), head h."""
+    if prob.q_scale_layout == 0:
+        return r * prob.num_qo_heads + h
+    return (b * prob.num_qo_heads + h) * prob.q_scale_stride + (r - lo)
+
+
 @dataclasses.dataclass
 class AppendResult:
-    out_q: np.ndarray                      # [T, Hq, 128] float64, NaN for rows not written
+    out_q: np.ndarray                      # [T, Hq, 128] float64 payload, NaN for rows not written
+    q_scale: Dict[int, float]              # flat q_scale index -> dynamic scale (dynamic policy only)
     k_rows: Dict[Tuple[int, int, int], np.ndarray]  # (page, slot, kv head) -> value (x / k_scale for e4m3)
     v_rows: Dict[Tuple[int, int, int], np.ndarray]
     cleared: List[Tuple[int, int, int]]    # (page, slot, kv head) zeroed in both caches
@@ -88,6 +110,7 @@ def append(prob) -> AppendResult:
     qw, kw = bf16_to_f64(prob.q_weight), bf16_to_f64(prob.k_weight)
     e4m3 = prob.kv_dtype == "e4m3"
     out_q = np.full((T, Hq, D), np.nan)
+    q_scale: Dict[int, float] = {}
     k_rows, v_rows, cleared, bad = {}, {}, [], []
 
     def qk_transform(x, w, cs_row):
@@ -102,6 +125,8 @@ def append(prob) -> AppendResult:
         L = int(prob.seq_lens[b])
         n = hi - lo
         ok = 0 <= lo <= hi <= T and n <= L and L <= prob.max_pages * P and L <= prob.max_pos
+        if prob.q_quant == Q_DYNAMIC and prob.q_scale_layout == 1 and n > prob.q_scale_stride:
+            ok = False
         if not ok:
             bad.append(b)
             continue
@@ -110,7 +135,14 @@ def append(prob) -> AppendResult:
             page = int(prob.block_tables[b, pos // P])
             slot = pos % P
             for h in range(Hq):
-                out_q[r, h] = qk_transform(qkv[r, h], qw, cs[pos])
+                y = qk_transform(qkv[r, h], qw, cs[pos])
+                if prob.q_quant == Q_DYNAMIC:
+                    sc = max(float(np.max(np.abs(y))), Q_SCALE_FLOOR) / prob.upper_max
+                    q_scale[q_scale_index(prob, b, h, r, lo)] = sc
+                    y = y / sc
+                elif prob.q_quant == Q_STATIC:
+                    y = y * prob.q_scale_inv
+                out_q[r, h] = y
             for g in range(Hkv):
                 k = qk_transform(qkv[r, Hq + g], kw, cs[pos])
                 v = qkv[r, Hq + Hkv + g]
@@ -121,4 +153,5 @@ def append(prob) -> AppendResult:
             for slot in range((L - 1) % P + 1, P):
                 for g in range(Hkv):
                     cleared.append((page, slot, g))
-    return AppendResult(out_q=out_q, k_rows=k_rows, v_rows=v_rows, cleared=cleared, bad_requests=bad)
+    return AppendResult(out_q=out_q, q_scale=q_scale, k_rows=k_rows, v_rows=v_rows, cleared=cleared,
+                        bad_requests=bad)

@@ -427,6 +427,23 @@ class AppendProblem:
     v_scale: float = 1.0
     clear_tail: bool = True
     head_dim: int = ROPE_DIM
+    # query output: 0 bf16; 1 e4m3 with a dynamic scale per (row, head)
+    # (q_scale = max(|q|, 1e-6) / upper_max); 2 e4m3 of q * q_scale_inv
+    q_quant: int = 0
+    upper_max: float = 448.0
+    q_scale_inv: float = 1.0
+    # dynamic scales: 0 -> [T, Hq]; 1 -> [B, Hq, q_scale_stride] indexed by the row inside its request
+    q_scale_layout: int = 0
+    q_scale_stride: int = 0
+
+    @property
+    def q_scale_entries(self) -> int:
+        """Length of the dynamic scale buffer (0 without the dynamic policy)."""
+        if self.q_quant != 1:
+            return 0
+        if self.q_scale_layout == 0:
+            return self.total_tokens * self.num_qo_heads
+        return self.batch * self.num_qo_heads * self.q_scale_stride
 
     @property
     def total_tokens(self) -> int:
@@ -454,7 +471,10 @@ class AppendProblem:
             for L in self.seq_lens.tolist():
                 if L > 0:
                     tail += P - 1 - (L - 1) % P
-        return T * (Hq + 2 * Hkv) * D * 2 + T * Hq * D * 2 + 2 * T * Hkv * D * eb + 2 * tail * Hkv * D * eb
+        qb = 2 if self.q_quant == 0 else 1
+        qs = 4 * T * Hq if self.q_quant == 1 else 0
+        return (T * (Hq + 2 * Hkv) * D * 2 + T * Hq * D * qb + qs + 2 * T * Hkv * D * eb
+                + 2 * tail * Hkv * D * eb)
 
 
 def rope_table(max_pos: int, base: float = 10000.0) -> np.ndarray:
@@ -469,7 +489,9 @@ def rope_table(max_pos: int, base: float = 10000.0) -> np.ndarray:
 def make_append_problem(*, name: str, seed: int, new_lens, seq_lens, num_qo_heads: int, num_kv_heads: int,
                         page_size: int, norm_policy: int = 0, kv_dtype: str = BF16, clear_tail: bool = True,
                         k_scale: float = 1.0, v_scale: float = 1.0, extra_pages: int = 2,
-                        table_slack_pages: int = 1, max_pos: Optional[int] = None) -> AppendProblem:
+                        table_slack_pages: int = 1, max_pos: Optional[int] = None, q_quant: int = 0,
+                        upper_max: float = 448.0, q_scale_inv: float = 1.0, q_scale_layout: int = 0,
+                        q_scale_stride: int = 0) -> AppendProblem:
     """Draw order: page permutation, qkv, the two weight vectors, the initial
     cache contents (random non-zero storage so that untouched and cleared rows
     are told apart).  Unused table slots point at a spare page that no request
@@ -510,7 +532,9 @@ def make_append_problem(*, name: str, seed: int, new_lens, seq_lens, num_qo_head
                          cos_sin=rope_table(mp), q_weight=q_w, k_weight=k_w, q_indptr=q_indptr,
                          seq_lens=np.array(seq_lens, dtype=np.int32), block_tables=table, k_cache0=k0,
                          v_cache0=v0, norm_policy=norm_policy, kv_dtype=kv_dtype, k_scale=float(k_scale),
-                         v_scale=float(v_scale), clear_tail=clear_tail)
+                         v_scale=float(v_scale), clear_tail=clear_tail, q_quant=int(q_quant),
+                         upper_max=float(upper_max), q_scale_inv=float(q_scale_inv),
+                         q_scale_layout=int(q_scale_layout), q_scale_stride=int(q_scale_stride))
 
 
 def append_h64x8_b32_decode(seed: int = 0, norm_policy: int = 2, kv_dtype: str = BF16) -> AppendProblem:

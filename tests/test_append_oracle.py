@@ -203,3 +203,72 @@ def test_policy_one_normalizes_last_and_policy_two_rotates_last():
     z = r2.out_q[rows]
     n = np.stack([A.rms_norm(v, w, p1.eps) for v in x[rows].reshape(-1, 128)]).reshape(z.shape)
     np.testing.assert_allclose(z[..., :64] ** 2 + z[..., 64:] ** 2, n[..., :64] ** 2 + n[..., 64:] ** 2, rtol=1e-5)
+
+
+# ---- e4m3 query output (PR #5956 body, "Contract": a dynamic scale per (row,
+# head) of max(|q|, 1e-6) / upper_max, or a static inverse scale)
+
+def test_dynamic_query_scale_puts_every_head_maximum_at_upper_max():
+    for upper in (448.0, 240.0):
+        res = A.append(_small(policy=2, q_quant=1, upper_max=upper))
+        wrote = ~np.isnan(res.out_q[:, 0, 0])
+        assert wrote.sum() == 8
+        amax = np.max(np.abs(res.out_q[wrote]), axis=2)  # [rows, Hq]: one maximum per (row, head)
+        assert np.allclose(amax, upper, rtol=1e-13, atol=0.0)
+
+
+def test_dynamic_query_payload_times_scale_is_the_bf16_route_value():
+    base = _small(policy=1)
+    ref = A.append(base).out_q
+    prob = dataclasses.replace(base, q_quant=1, upper_max=240.0)
+    res = A.append(prob)
+    assert len(res.q_scale) == 8 * 8  # [T, Hq] layout: T = 8 rows
+    for r in range(8):
+        for h in range(8):
+            sc = res.q_scale[r * 8 + h]
+            assert np.allclose(res.out_q[r, h] * sc, ref[r, h], rtol=1e-13, atol=1e-300)
+            assert np.isclose(sc, max(np.max(np.abs(ref[r, h])), 1e-6) / 240.0, rtol=1e-13)
+
+
+def test_prefill_scale_layout_positions_worked_by_hand():
+    # new rows per request [2, 0, 5, 1] -> rows 0-1 (b0), 2-6 (b2), 7 (b3); Hq = 8; stride 128:
+    # entry (b, h, i) = (b * 8 + h) * 128 + i
+    base = _small(policy=2)
+    ref = A.append(base).out_q
+    res = A.append(dataclasses.replace(base, q_quant=1, upper_max=448.0, q_scale_layout=1, q_scale_stride=128))
+    hand = {  # flat index -> (row, head)
+        0 * 128 + 0: (0, 0), 7 * 128 + 1: (1, 7),            # request 0: rows 0, 1
+        (16 + 5) * 128 + 4: (6, 5), (16 + 0) * 128 + 0: (2, 0),  # request 2: rows 2..6 -> i 0..4
+        (24 + 3) * 128 + 0: (7, 3),                          # request 3: row 7 -> i 0
+    }
+    assert 2692 in hand and 3456 in hand
+    for idx, (r, h) in hand.items():
+        assert np.isclose(res.q_scale[idx], max(np.max(np.abs(ref[r, h])), 1e-6) / 448.0, rtol=1e-13), idx
+    used = sorted(res.q_scale)
+    assert len(used) == 8 * 8 and used[0] == 0 and used[-1] == (24 + 7) * 128 + 0
+    assert not any(8 * 128 <= i < 16 * 128 for i in used)  # request 1 appends nothing
+
+
+def test_dynamic_query_scale_floor_on_an_all_zero_head():
+    prob = _small(policy=0, q_quant=1, upper_max=448.0)
+    qkv = prob.qkv.reshape(prob.total_tokens, -1, 128).copy()
+    qkv[0, 3] = 0  # +0.0 in bf16: the rotation keeps it zero
+    res = A.append(dataclasses.replace(prob, qkv=qkv.reshape(prob.total_tokens, -1)))
+    assert res.q_scale[0 * 8 + 3] == 1e-6 / 448.0
+    assert np.all(res.out_q[0, 3] == 0.0)
+
+
+def test_static_query_payload_is_the_value_times_the_inverse_scale():
+    base = _small(policy=2)
+    ref = A.append(base).out_q
+    res = A.append(dataclasses.replace(base, q_quant=2, q_scale_inv=4.0))
+    assert res.q_scale == {}
+    wrote = ~np.isnan(ref[:, 0, 0])
+    assert np.array_equal(res.out_q[wrote], 4.0 * ref[wrote])  # a power of two: exact
+
+
+def test_prefill_scale_layout_skips_a_request_longer_than_the_stride():
+    res = A.append(_small(policy=2, q_quant=1, q_scale_layout=1, q_scale_stride=4))  # request 2 has 5 rows
+    assert res.bad_requests == [2]
+    assert np.isnan(res.out_q[2:7]).all() and not np.isnan(res.out_q[[0, 1, 7]]).any()
+    assert not any(16 * 4 <= i < 24 * 4 for i in res.q_scale)

@@ -25,11 +25,18 @@ MUTATIONS = {
     "k-scale-multiplied": ("k_rows[(page, slot, g)] = k / prob.k_scale if e4m3 else k",
                            "k_rows[(page, slot, g)] = k * prob.k_scale if e4m3 else k"),
     "values-rotated": ("v = qkv[r, Hq + Hkv + g]", "v = rope(qkv[r, Hq + Hkv + g], cs[pos])"),
-    "query-uses-key-weights": ("out_q[r, h] = qk_transform(qkv[r, h], qw, cs[pos])",
-                               "out_q[r, h] = qk_transform(qkv[r, h], kw, cs[pos])"),
+    "query-uses-key-weights": ("y = qk_transform(qkv[r, h], qw, cs[pos])",
+                               "y = qk_transform(qkv[r, h], kw, cs[pos])"),
     "page-from-next-slot": ("page = int(prob.block_tables[b, pos // P])", "page = int(prob.block_tables[b, (pos + 1) // P])"),
     "bad-request-not-skipped": ("ok = 0 <= lo <= hi <= T and n <= L and", "ok = 0 <= lo <= hi <= T and"),
     "e4m3-bias": ("(1.0 + m / 8.0) * 2.0 ** (e - 7)", "(1.0 + m / 8.0) * 2.0 ** (e - 8)"),
+    "q-scale-no-floor": ("max(float(np.max(np.abs(y))), Q_SCALE_FLOOR)", "float(np.max(np.abs(y)))"),
+    "q-scale-mean-not-max": ("max(float(np.max(np.abs(y))), Q_SCALE_FLOOR)",
+                             "max(float(np.mean(np.abs(y))), Q_SCALE_FLOOR)"),
+    "q-payload-multiplied": ("y = y / sc", "y = y * sc"),
+    "q-static-divides": ("y = y * prob.q_scale_inv", "y = y / prob.q_scale_inv"),
+    "q-scale-index-global-row": ("* prob.q_scale_stride + (r - lo)", "* prob.q_scale_stride + r"),
+    "q-scale-stride-not-checked": ("n > prob.q_scale_stride:", "n > prob.q_scale_stride + 8:"),
 }
 
 
