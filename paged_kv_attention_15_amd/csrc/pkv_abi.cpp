@@ -106,6 +106,10 @@ pkv_status validate(const pkv_args* a, bool is_context) {
     if ((int64_t)a->q_len > (int64_t)a->max_pages_per_seq * a->page_size && a->batch > 0)
       return fail(PKV_ERR_INVALID_ARG, "q_len exceeds the table capacity");
   }
+  // query rows x heads index the reducer's grid and its 32-bit row arithmetic
+  const int64_t q_rows = (is_context ? (int64_t)a->total_q : (int64_t)a->batch * a->q_len) * a->num_qo_heads;
+  if (q_rows > INT32_MAX)
+    return fail(PKV_ERR_INVALID_ARG, "query rows x heads (%lld) exceed 2^31 - 1", (long long)q_rows);
   // layout consistency of the strides (innermost dimension contiguous)
   const int64_t D_qk = a->head_dim_qk, D_v = a->head_dim_v, P = a->page_size, H = a->num_kv_heads;
   auto check_pool = [&](int64_t sp, int64_t sh, int64_t st, int64_t D, const char* name) -> pkv_status {

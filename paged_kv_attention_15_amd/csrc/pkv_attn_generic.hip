@@ -205,7 +205,7 @@ struct MergeRow {
 
 template <int CW>
 __device__ __forceinline__ void merge_row(const MergeParams& mp, const MergeRow& mr, const int64_t r,
-                                          float* s_red) {
+                                          const int64_t t, const int h, float* s_red) {
   const int dv = mp.dv;
   const int NQ = (dv + CW - 1) / CW;  // items
   const int tid = threadIdx.x;
@@ -215,12 +215,15 @@ __device__ __forceinline__ void merge_row(const MergeParams& mp, const MergeRow&
     __syncthreads();  // matches the subsets' LDS exchange below
     return;
   }
-  const int64_t t = r / mp.num_qo_heads;
-  const int h = (int)(r % mp.num_qo_heads);
+  // balanced schedule: an owner range may hold workgroups with an empty range,
+  // but only when there are fewer virtual pages than workgroups (otherwise
+  // every range holds at least one page)
+  const bool check_empty = mr.TPs > 0 && mr.TPs < mr.num_wg;
   auto slot_lse = [&](int s) -> float {
-    if (mr.TPs > 0) {  // balanced schedule: an owner range may hold workgroups with an empty range
+    if (check_empty) {
       const int64_t w = mr.w_first + s;
-      if ((w + 1) * mr.TPs / mr.num_wg == w * mr.TPs / mr.num_wg) return -INFINITY;
+      if (floor_div_nonneg((w + 1) * mr.TPs, mr.num_wg) == floor_div_nonneg(w * mr.TPs, mr.num_wg))
+        return -INFINITY;
     }
     return mp.lse_part[mr.prow0 + s * mr.step];
   };
@@ -305,10 +308,14 @@ __device__ __forceinline__ void merge_row(const MergeParams& mp, const MergeRow&
 
 __global__ __launch_bounds__(kMergeThreads) void lse_merge_kernel(const MergeParams mp) {
   __shared__ float s_red[kMergeThreads * 6];
-  const int64_t r = blockIdx.x;
-  if (r >= mp.num_rows) return;
-  const int64_t t = r / mp.num_qo_heads;
-  const int h = (int)(r % mp.num_qo_heads);
+  // row indices in 32 bits (the grid's x extent): the 64-bit integer division
+  // sequences cost more than the rest of a merged row
+  const uint32_t r32 = blockIdx.x;
+  if (r32 >= mp.num_rows) return;
+  const uint32_t nh = (uint32_t)mp.num_qo_heads;
+  const uint32_t t32 = r32 / nh;
+  const int64_t r = r32, t = t32;
+  const int h = (int)(r32 - t32 * nh);
 
   // partial rows of this output row: `live` slots, slot k at partial row
   // prow0 + k*step (Split-KV layout: [split][row]; stream layout: a row
@@ -321,8 +328,9 @@ __global__ __launch_bounds__(kMergeThreads) void lse_merge_kernel(const MergePar
   mr.TPs = 0;
   mr.num_wg = mp.num_wg;
   if (mp.stream) {
-    const int b = (int)(t / mp.q_len);
-    const int i = (int)(t % mp.q_len);
+    const uint32_t ql = (uint32_t)mp.q_len;
+    const int b = (int)(t32 / ql);
+    const int i = (int)(t32 - (uint32_t)b * ql);
     const int g = h / mp.group;
     const int R = i * mp.group + (h % mp.group);
     if (i == 0 && h == 0 && threadIdx.x == 0) {
@@ -364,7 +372,7 @@ __global__ __launch_bounds__(kMergeThreads) void lse_merge_kernel(const MergePar
       if (bad || t < t0 || t >= a1) return;  // the attention kernel skipped this row too
       n = a1 - t0;
     } else {
-      b = (int)(t / mp.q_len);
+      b = (int)(t32 / (uint32_t)mp.q_len);
       t0 = b * mp.q_len;
       n = mp.q_len;
     }
@@ -373,8 +381,8 @@ __global__ __launch_bounds__(kMergeThreads) void lse_merge_kernel(const MergePar
     const int c = mp.causal ? min(L, max(0, L - n + i + 1)) : L;
     mr.live = min(mp.num_splits, (c + mp.split_tokens - 1) / mp.split_tokens);
   }
-  if (mp.vec4) merge_row<4>(mp, mr, r, s_red);
-  else merge_row<1>(mp, mr, r, s_red);
+  if (mp.vec4) merge_row<4>(mp, mr, r, t, h, s_red);
+  else merge_row<1>(mp, mr, r, t, h, s_red);
 }
 
 hipError_t launch_merge(const MergeParams& mp, hipStream_t s) {

@@ -138,6 +138,16 @@ __device__ __forceinline__ void wait_vmcnt() {
 // the owners of a unit are owner(real(u)) .. owner(real(u) + npg - 1), every
 // one of them holding at least one of its pages when its range is not empty.
 // `pfx` is the page prefix over requests (pfx[b] = pages of requests < b).
+// floor(n / d) for 0 <= n < 2^53 and d > 0 by one correctly rounded fp64
+// division instead of the long 64-bit integer division sequence: n and d
+// convert exactly, and a non-integer quotient lies at least 1/d below the
+// next integer, which exceeds half an ulp of the quotient (at most n/d *
+// 2^-53), so rounding never carries it up to that integer.
+__device__ __forceinline__ int64_t floor_div_nonneg(int64_t n, int64_t d) {
+  if (n < (int64_t(1) << 53)) return (int64_t)((double)n / (double)d);
+  return n / d;
+}
+
 struct StreamGeom {
   const int32_t* pfx;
   int32_t Hkv, A;
@@ -145,8 +155,8 @@ struct StreamGeom {
   __device__ int64_t request_start(int b) const { return (int64_t)Hkv * (pfx[b] + (int64_t)A * b); }
   __device__ int64_t npg(int b) const { return pfx[b + 1] - pfx[b]; }
   __device__ int64_t real(int b, int g) const { return request_start(b) + g * (npg(b) + A) + A; }
-  __device__ int64_t owner(int64_t v) const { return ((v + 1) * W - 1) / TV; }
-  __device__ bool owns_any(int64_t w) const { return (w + 1) * TV / W > w * TV / W; }
+  __device__ int64_t owner(int64_t v) const { return floor_div_nonneg((v + 1) * W - 1, TV); }
+  __device__ bool owns_any(int64_t w) const { return floor_div_nonneg((w + 1) * TV, W) > floor_div_nonneg(w * TV, W); }
 };
 
 // ---------------------------------------------------------------- attention sinks

@@ -132,6 +132,7 @@ def test_split_plan_is_page_aligned_and_sized_to_cus():
     ("table_stride", 0, pkv.PKV_ERR_INVALID_ARG),
     ("k_stride_tok", 64, pkv.PKV_ERR_INVALID_ARG),  # rows shorter than head_dim_qk
     ("scale", 0.0, pkv.PKV_ERR_INVALID_ARG),
+    ("batch", 2 ** 26, pkv.PKV_ERR_INVALID_ARG),  # rows x 32 heads = 2^31: past the reducer's 32-bit row index
 ])
 def test_invalid_arguments_rejected_before_launch(field, value, status):
     a = _args_for(_fake())
