@@ -230,15 +230,18 @@ def secondary_results(steps: int, warmup: int, single_call: bool = True):
     return out
 
 
-def append_result(steps: int, warmup: int):
+def append_result(steps: int, warmup: int, fp8: bool = False):
     """The paged-KV append producer on the pages' H1 row (Hq=64 / Hkv=8, 32
-    requests appending one row each, norm then RoPE, bf16 caches of 64-token
-    pages): per-call time as HIP-graph replays, and bytes moved per call."""
+    requests appending one row each, norm then RoPE, caches of 64-token pages;
+    bf16 throughout, or with `fp8` e4m3 caches and e4m3 queries with a dynamic
+    scale per (row, head)): per-call time as HIP-graph replays, and bytes moved
+    per call."""
     import torch
 
     from paged_kv_attention_15_amd import pkv, workloads as W
 
-    prob = W.append_h64x8_b32_decode(norm_policy=2)
+    prob = (W.append_h64x8_b32_decode(norm_policy=2, kv_dtype=W.E4M3, q_quant=1) if fp8
+            else W.append_h64x8_b32_decode(norm_policy=2))
     da = pkv.upload_append(prob, "cuda", with_err=False)
     for _ in range(warmup):
         da.run()
@@ -349,6 +352,8 @@ def main():
                                               not args.no_single_call)
         line["secondary"]["append-h64x8-b32-decode"] = append_result(max(20, args.steps // 4),
                                                                      max(5, args.warmup // 2))
+        line["secondary"]["append-h64x8-b32-decode-e4m3-dynq"] = append_result(
+            max(20, args.steps // 4), max(5, args.warmup // 2), fp8=True)
     print(json.dumps(line), flush=True)
 
 

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 3
+#define PKV_ABI_VERSION 4
 
 typedef enum pkv_status {
   PKV_OK = 0,
@@ -74,6 +74,7 @@ typedef enum pkv_layout {
 #define PKV_DEVERR_PAGE_RANGE 0x4     /* a referenced page index outside [0, num_pages) (clamped) */
 #define PKV_DEVERR_QINDPTR 0x8        /* q_indptr not monotone, or rows exceed max_q_len / total_q */
 #define PKV_DEVERR_POS_RANGE 0x10     /* pkv_append: a row's position is past the rotary table */
+#define PKV_DEVERR_QSCALE_ROWS 0x20   /* pkv_append: a request has more new rows than q_scale_stride */
 
 /*
  * Arguments of one attention call.  Strides are in ELEMENTS of the tensor's
@@ -244,7 +245,16 @@ pkv_status pkv_lse_merge(int32_t num_splits, int32_t num_rows, int32_t num_qo_he
  *     with w = q_weight or k_weight, and the NeoX rotary embedding with row pos
  *     of cos_sin = (cos_0..63, sin_0..63): channel i < 64 pairs with i + 64,
  *     y_i = x_i cos_i - x_{i+64} sin_i, y_{i+64} = x_{i+64} cos_i + x_i sin_i;
- *   - the query heads are written to out_q[r] (bf16, round to nearest even);
+ *   - the query heads are written to out_q[r]: bf16 (round to nearest even)
+ *     with q_quant = 0, else e4m3 codes (round to nearest even, saturated to
+ *     +-448) of y / s with, for q_quant = 1, a scale of its own per (row,
+ *     head) s = max(max_i |y_i|, 1e-6) / upper_max, written as fp32 to
+ *     q_scale (q_scale_layout 0: [T, Hq], entry r * Hq + h; 1: [B, Hq,
+ *     q_scale_stride], entry (b * Hq + h) * q_scale_stride + i for the i-th
+ *     new row of request b -- the pages round the stride up to a multiple of
+ *     128; entries of rows no request appends are left untouched), or, for
+ *     q_quant = 2, of y * q_scale_inv with no scale written (PR #5956 body,
+ *     "Contract": dynamic per-token/per-head or static query quantization);
  *   - key heads and the unchanged value heads are written to token pos % P of
  *     page block_tables[b][pos / P] of the NHD caches [num_pages, P, Hkv, 128]:
  *     bf16, or e4m3 codes of x / k_scale and x / v_scale (round to nearest
@@ -253,7 +263,8 @@ pkv_status pkv_lse_merge(int32_t num_splits, int32_t num_rows, int32_t num_qo_he
  *     request's last page are zeroed in both caches (the caller owns the pages
  *     exclusively: a page shared with a longer request would lose rows).
  * A request whose rows do not fit (seq_lens[b] < rows, seq_lens[b] > max_pages_per_seq * P
- * or > max_pos, q_indptr not monotone or past num_tokens) writes nothing and
+ * or > max_pos, q_indptr not monotone or past num_tokens, more rows than
+ * q_scale_stride in the dynamic [B, Hq, stride] layout) writes nothing and
  * sets PKV_DEVERR_* bits; a page index outside [0, num_pages) (num_pages > 0)
  * skips that row's cache write and sets PKV_DEVERR_PAGE_RANGE.  Device values
  * are never used for addressing unchecked.  Nothing is allocated, nothing
@@ -287,10 +298,16 @@ typedef struct pkv_append_args {
   const int32_t* seq_lens;   /* [B] */
   const int32_t* block_tables; /* [B, table_stride] */
   int64_t table_stride;      /* >= max_pages_per_seq */
-  void* out_q;               /* bf16 [T, Hq, 128] */
+  void* out_q;               /* [T, Hq, 128]: bf16 (q_quant 0) or e4m3 codes */
   void* k_cache;             /* NHD [num_pages, P, Hkv, 128], bf16 or e4m3 */
   void* v_cache;
   int32_t* err_word;         /* optional device word, OR-ed with PKV_DEVERR_* bits */
+  int32_t q_quant;           /* query output: 0 bf16; 1 e4m3, dynamic scale; 2 e4m3, static scale */
+  float upper_max;           /* q_quant 1: finite, in (0, 448] */
+  float q_scale_inv;         /* q_quant 2: finite, non-zero */
+  int32_t q_scale_layout;    /* q_quant 1: 0 [T, Hq] or 1 [B, Hq, q_scale_stride] */
+  int64_t q_scale_stride;    /* q_scale_layout 1: entries per (request, head), >= 1 */
+  float* q_scale;            /* q_quant 1: fp32 scales (layout above), 4-byte aligned */
 } pkv_append_args;
 
 pkv_status pkv_append(const pkv_append_args* args, void* stream);

@@ -635,6 +635,17 @@ extern "C" pkv_status pkv_append(const pkv_append_args* a, void* stream) {
        !std::isfinite(a->v_scale)))
     return fail(PKV_ERR_INVALID_ARG, "e4m3 caches need finite non-zero k_scale and v_scale");
   if (!(a->eps >= 0.f)) return fail(PKV_ERR_INVALID_ARG, "eps must be >= 0");
+  if (a->q_quant < 0 || a->q_quant > 2) return fail(PKV_ERR_INVALID_ARG, "q_quant must be 0, 1 or 2");
+  if (a->q_quant == 1) {
+    if (!(a->upper_max > 0.f && a->upper_max <= 448.f))
+      return fail(PKV_ERR_INVALID_ARG, "upper_max must be finite and in (0, 448]");
+    if (a->q_scale_layout != 0 && a->q_scale_layout != 1)
+      return fail(PKV_ERR_INVALID_ARG, "q_scale_layout must be 0 ([T, Hq]) or 1 ([B, Hq, stride])");
+    if (a->q_scale_layout == 1 && a->q_scale_stride < 1)
+      return fail(PKV_ERR_INVALID_ARG, "q_scale_stride must be >= 1 for the [B, Hq, stride] layout");
+  }
+  if (a->q_quant == 2 && (!std::isfinite(a->q_scale_inv) || a->q_scale_inv == 0.f))
+    return fail(PKV_ERR_INVALID_ARG, "q_scale_inv must be finite and non-zero");
   if (a->batch == 0 || (a->num_tokens == 0 && !a->clear_tail)) return ok();
   if (!a->q_indptr || !a->seq_lens || !a->block_tables || !a->k_cache || !a->v_cache)
     return fail(PKV_ERR_INVALID_ARG, "q_indptr, seq_lens, block_tables and both caches are required");
@@ -644,12 +655,15 @@ extern "C" pkv_status pkv_append(const pkv_append_args* a, void* stream) {
     return fail(PKV_ERR_INVALID_ARG, "need max_pages_per_seq >= 1 and table_stride >= max_pages_per_seq");
   if (a->num_tokens > 0) {
     if (!a->qkv || !a->cos_sin || !a->out_q) return fail(PKV_ERR_INVALID_ARG, "qkv, cos_sin and out_q are required");
+    if (a->q_quant == 1 && (!a->q_scale || (reinterpret_cast<uintptr_t>(a->q_scale) & 3u)))
+      return fail(PKV_ERR_INVALID_ARG, "q_quant 1 needs a 4-byte aligned q_scale");
     if (a->norm_policy != 0 && (!a->q_weight || !a->k_weight))
       return fail(PKV_ERR_INVALID_ARG, "norm_policy %d needs q_weight and k_weight", a->norm_policy);
     if (a->max_pos < 1) return fail(PKV_ERR_INVALID_ARG, "max_pos must be >= 1");
     const int64_t row = (int64_t)(a->num_qo_heads + 2 * a->num_kv_heads) * 128;
     if (a->qkv_stride_tok < row) return fail(PKV_ERR_INVALID_ARG, "qkv_stride_tok smaller than (Hq + 2 Hkv) * 128");
-    const uintptr_t al = reinterpret_cast<uintptr_t>(a->qkv) | reinterpret_cast<uintptr_t>(a->out_q) |
+    const uintptr_t al = reinterpret_cast<uintptr_t>(a->qkv) |
+                         (a->q_quant == 0 ? reinterpret_cast<uintptr_t>(a->out_q) : 0) |
                          reinterpret_cast<uintptr_t>(a->q_weight) | reinterpret_cast<uintptr_t>(a->k_weight);
     if ((al & 1u) || (reinterpret_cast<uintptr_t>(a->cos_sin) & 3u))
       return fail(PKV_ERR_INVALID_ARG, "bf16 arrays must be 2-byte and cos_sin 4-byte aligned");

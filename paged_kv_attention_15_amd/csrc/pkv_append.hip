@@ -5,11 +5,13 @@
 // One wavefront per (packed row, head): lane l holds channels l and l + 64,
 // which are exactly the pair the NeoX rotation mixes, so the rotation needs
 // no data movement and the RMSNorm's sum of squares is one wavefront sum.
-// Loads and stores of a head are two coalesced 128-byte (bf16) runs.  After
-// the T * (Hq + 2 Hkv) row waves come B * Hkv * 2 waves that zero the tail of
-// each request's last page in the K and the V cache.  Every request is
+// Loads and stores of a head are two coalesced 128-byte (bf16) runs.  Query
+// heads may leave as e4m3 codes instead (PR #5956 body, "Contract"): with a
+// dynamic scale the head's absolute maximum is one more wavefront reduction.
+// After the T * (Hq + 2 Hkv) row waves come B * Hkv * 2 waves that zero the
+// tail of each request's last page in the K and the V cache.  Every request is
 // validated on the device (lengths, q_indptr, table width, rotary table
-// length, page range) before anything of it is written.
+// length, scale layout, page range) before anything of it is written.
 
 #include "pkv_device.h"
 #include "pkv_internal.h"
@@ -19,6 +21,10 @@ namespace pkv {
 struct AppendParams {
   int32_t T, B, Hq, Hkv, P, max_pages, max_pos, num_pages, policy, clear_tail, fp8;
   float eps, inv_k_scale, inv_v_scale;
+  int32_t q_quant, qs_layout;
+  float upper_max, q_scale_inv;
+  int64_t qs_stride;
+  float* q_scale;
   const uint16_t* qkv;
   int64_t qkv_st;
   const float* cos_sin;
@@ -66,6 +72,10 @@ __device__ __forceinline__ bool append_request(const AppendParams& p, int b, int
   }
   if (len > p.max_pos) {
     flag_error(p.err_word, PKV_DEVERR_POS_RANGE);
+    return false;
+  }
+  if (p.q_quant == 1 && p.qs_layout == 1 && a1 - a0 > p.qs_stride) {
+    flag_error(p.err_word, PKV_DEVERR_QSCALE_ROWS);
     return false;
   }
   *lo = a0;
@@ -120,9 +130,28 @@ __global__ __launch_bounds__(256) void append_kernel(const AppendParams p) {
       if (p.policy == 1) norm();
     }
     if (is_q) {
-      uint16_t* dst = p.out_q + ((int64_t)r * p.Hq + hh) * 128;
-      dst[lane] = f32_to_bf16_rne(x0);
-      dst[lane + 64] = f32_to_bf16_rne(x1);
+      const int64_t qrow = ((int64_t)r * p.Hq + hh) * 128;
+      if (p.q_quant == 0) {
+        uint16_t* dst = p.out_q + qrow;
+        dst[lane] = f32_to_bf16_rne(x0);
+        dst[lane + 64] = f32_to_bf16_rne(x1);
+        return;
+      }
+      unsigned char* dst = (unsigned char*)p.out_q + qrow;
+      if (p.q_quant == 1) {
+        const float amax = wave_max(fmaxf(fabsf(x0), fabsf(x1)));
+        const float sc = fmaxf(amax, 1e-6f) / p.upper_max;
+        if (lane == 0) {
+          const int64_t at = p.qs_layout == 0 ? (int64_t)r * p.Hq + hh
+                                              : ((int64_t)lo_b * p.Hq + hh) * p.qs_stride + (r - lo);
+          p.q_scale[at] = sc;
+        }
+        dst[lane] = f32_to_e4m3_sat(x0 / sc);
+        dst[lane + 64] = f32_to_e4m3_sat(x1 / sc);
+      } else {
+        dst[lane] = f32_to_e4m3_sat(x0 * p.q_scale_inv);
+        dst[lane + 64] = f32_to_e4m3_sat(x1 * p.q_scale_inv);
+      }
       return;
     }
     const int g = is_k ? hh - p.Hq : hh - p.Hq - p.Hkv;
@@ -194,6 +223,12 @@ hipError_t launch_append(const pkv_append_args* a, hipStream_t s) {
   p.k_cache = (unsigned char*)a->k_cache;
   p.v_cache = (unsigned char*)a->v_cache;
   p.err_word = a->err_word;
+  p.q_quant = a->q_quant;
+  p.qs_layout = a->q_scale_layout;
+  p.upper_max = a->upper_max;
+  p.q_scale_inv = a->q_scale_inv;
+  p.qs_stride = a->q_scale_stride;
+  p.q_scale = a->q_scale;
   const int64_t waves = (int64_t)p.T * (p.Hq + 2 * p.Hkv) + (p.clear_tail ? (int64_t)p.B * p.Hkv * 2 : 0);
   if (waves == 0 || p.B == 0) return hipSuccess;
   hipLaunchKernelGGL(append_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, p);

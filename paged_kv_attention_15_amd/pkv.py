@@ -35,6 +35,7 @@ DTYPE_CODES = {"f32": PKV_DTYPE_F32, "bf16": PKV_DTYPE_BF16, "e4m3": PKV_DTYPE_F
 EXPORTED = ["pkv_abi_version", "pkv_last_error", "pkv_plan", "pkv_workspace_bytes", "pkv_decode",
             "pkv_context", "pkv_lse_merge", "pkv_append"]
 PKV_DEVERR_POS_RANGE = 0x10
+PKV_DEVERR_QSCALE_ROWS = 0x20
 
 
 class PkvArgs(C.Structure):
@@ -82,6 +83,8 @@ class PkvAppendArgs(C.Structure):
         ("q_weight", C.c_void_p), ("k_weight", C.c_void_p), ("q_indptr", C.c_void_p),
         ("seq_lens", C.c_void_p), ("block_tables", C.c_void_p), ("table_stride", C.c_int64),
         ("out_q", C.c_void_p), ("k_cache", C.c_void_p), ("v_cache", C.c_void_p), ("err_word", C.c_void_p),
+        ("q_quant", C.c_int32), ("upper_max", C.c_float), ("q_scale_inv", C.c_float),
+        ("q_scale_layout", C.c_int32), ("q_scale_stride", C.c_int64), ("q_scale", C.c_void_p),
     ]
 
 
@@ -363,7 +366,12 @@ def upload_append(prob, device="cuda", with_err: bool = True) -> DeviceAppend:
         t["k_cache"] = torch.from_numpy(prob.k_cache0).to(device)
         t["v_cache"] = torch.from_numpy(prob.v_cache0).to(device)
     T = prob.total_tokens
-    t["out_q"] = torch.full((max(T, 1), prob.num_qo_heads, 128), -1, dtype=torch.int16, device=device)
+    if prob.q_quant == 0:
+        t["out_q"] = torch.full((max(T, 1), prob.num_qo_heads, 128), -1, dtype=torch.int16, device=device)
+    else:  # e4m3 codes; 0xFF (a NaN code) marks bytes never written
+        t["out_q"] = torch.full((max(T, 1), prob.num_qo_heads, 128), 0xFF, dtype=torch.uint8, device=device)
+    if prob.q_quant == 1:  # NaN-filled: entries no row writes stay NaN
+        t["q_scale"] = torch.full((max(prob.q_scale_entries, 1),), float("nan"), dtype=torch.float32, device=device)
     if with_err:
         t["err"] = torch.zeros(1, dtype=torch.int32, device=device)
     a = PkvAppendArgs()
@@ -395,4 +403,10 @@ def upload_append(prob, device="cuda", with_err: bool = True) -> DeviceAppend:
     a.k_cache = t["k_cache"].data_ptr()
     a.v_cache = t["v_cache"].data_ptr()
     a.err_word = t["err"].data_ptr() if with_err else 0
+    a.q_quant = prob.q_quant
+    a.upper_max = prob.upper_max
+    a.q_scale_inv = prob.q_scale_inv
+    a.q_scale_layout = prob.q_scale_layout
+    a.q_scale_stride = prob.q_scale_stride
+    a.q_scale = t["q_scale"].data_ptr() if prob.q_quant == 1 else 0
     return DeviceAppend(args=a, tensors=t)

@@ -537,10 +537,13 @@ def make_append_problem(*, name: str, seed: int, new_lens, seq_lens, num_qo_head
                          q_scale_layout=int(q_scale_layout), q_scale_stride=int(q_scale_stride))
 
 
-def append_h64x8_b32_decode(seed: int = 0, norm_policy: int = 2, kv_dtype: str = BF16) -> AppendProblem:
+def append_h64x8_b32_decode(seed: int = 0, norm_policy: int = 2, kv_dtype: str = BF16,
+                            q_quant: int = 0) -> AppendProblem:
     """The pages' H1 row: Hq=64 / Hkv=8, 32 requests appending one row each,
-    here at total lengths 2048 with 64-token pages."""
-    return make_append_problem(name=f"append-h64x8-b32-decode-p{norm_policy}-{kv_dtype}", seed=seed,
+    here at total lengths 2048 with 64-token pages (q_quant 1: e4m3 queries
+    with a dynamic scale per (row, head) in the [T, Hq] layout, upper_max 448)."""
+    return make_append_problem(name=f"append-h64x8-b32-decode-p{norm_policy}-{kv_dtype}-q{q_quant}", seed=seed,
                                new_lens=[1] * 32, seq_lens=[2048] * 32, num_qo_heads=64, num_kv_heads=8,
                                page_size=64, norm_policy=norm_policy, kv_dtype=kv_dtype,
-                               k_scale=0.05 if kv_dtype == E4M3 else 1.0, v_scale=0.05 if kv_dtype == E4M3 else 1.0)
+                               k_scale=0.05 if kv_dtype == E4M3 else 1.0, v_scale=0.05 if kv_dtype == E4M3 else 1.0,
+                               q_quant=q_quant, upper_max=448.0)

@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
     assert set(declared) == set(pkv.EXPORTED)
     for name in declared:
         assert hasattr(lib, name), name
-    assert pkv.pkv_abi_version() == 3
+    assert pkv.pkv_abi_version() == 4
 
 
 def test_ctypes_mirror_matches_c_layout(tmp_path):
@@ -276,6 +276,23 @@ def _append_args(**kw):
 ])
 def test_append_rejects_bad_arguments_before_launch(field, value, status):
     assert pkv.pkv_append(_append_args(**{field: value}), 0, check=False) == status
+    assert pkv.pkv_last_error() != ""
+
+
+@pytest.mark.parametrize("kw", [
+    dict(q_quant=3),
+    dict(q_quant=1, upper_max=0.0, q_scale=0x1000),
+    dict(q_quant=1, upper_max=449.0, q_scale=0x1000),
+    dict(q_quant=1, upper_max=float("inf"), q_scale=0x1000),
+    dict(q_quant=1, upper_max=448.0, q_scale=0),
+    dict(q_quant=1, upper_max=448.0, q_scale=0x1002),
+    dict(q_quant=1, upper_max=448.0, q_scale=0x1000, q_scale_layout=2),
+    dict(q_quant=1, upper_max=448.0, q_scale=0x1000, q_scale_layout=1, q_scale_stride=0),
+    dict(q_quant=2, q_scale_inv=0.0),
+    dict(q_quant=2, q_scale_inv=float("nan")),
+])
+def test_append_query_quantization_arguments_checked_before_launch(kw):
+    assert pkv.pkv_append(_append_args(**kw), 0, check=False) == pkv.PKV_ERR_INVALID_ARG
     assert pkv.pkv_last_error() != ""
 
 

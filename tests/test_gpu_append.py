@@ -41,15 +41,32 @@ def check_append(prob, da, expect_err=0, label=""):
     res = A.append(prob)
     T, Hq = prob.total_tokens, prob.num_qo_heads
     tol = 1e-2 if prob.kv_dtype == W.BF16 else 0.1
-    # query rows
-    q_bits = da.tensors["out_q"].cpu().numpy().view(np.uint16)[:T]
+    # query rows: bf16 at 1e-2 / 1e-2, or e4m3 codes decoded against the
+    # unrounded payload at 0.1 / 0.1 (the PR #5956 tests' tolerance)
     wrote = ~np.isnan(res.out_q[:, 0, 0])
+    if prob.q_quant == 0:
+        q_bits = da.tensors["out_q"].cpu().numpy().view(np.uint16)[:T]
+        got_q, qtol, unwritten = (A.bf16_to_f64(q_bits[wrote]) if wrote.any() else None), 1e-2, 0xFFFF
+    else:
+        q_bits = da.tensors["out_q"].cpu().numpy().view(np.uint8)[:T]
+        got_q, qtol, unwritten = (A.e4m3_to_f64(q_bits[wrote]) if wrote.any() else None), 0.1, 0xFF
     if wrote.any():
-        got = A.bf16_to_f64(q_bits[wrote])
         ref = res.out_q[wrote]
-        bad = np.abs(got - ref) > 1e-2 + 1e-2 * np.abs(ref)
-        assert not bad.any(), f"{bad.sum()} query elements out of tolerance"
-    assert (q_bits[~wrote] == 0xFFFF).all(), "query rows of skipped requests were written"
+        bad = np.abs(got_q - ref) > qtol + qtol * np.abs(ref)
+        assert not bad.any(), f"{bad.sum()} query elements out of tolerance (max err {np.max(np.abs(got_q - ref))})"
+    assert (q_bits[~wrote] == unwritten).all(), "query rows of skipped requests were written"
+    if prob.q_quant == 1:
+        qs = da.tensors["q_scale"].cpu().numpy().astype(np.float64)
+        idx = np.array(sorted(res.q_scale), dtype=np.int64)
+        if idx.size:
+            want = np.array([res.q_scale[i] for i in idx])
+            rel = np.abs(qs[idx] - want) / want
+            assert (rel <= 1e-5).all(), f"q_scale rel err {rel.max():.2e}"
+        rest = np.ones(qs.size, dtype=bool)
+        rest[idx] = False
+        assert np.isnan(qs[rest]).all(), "q_scale entries of rows no request appends were written"
+        say(f"  [{label or prob.name}] q_scale: {idx.size} entries, max rel err "
+            f"{(rel.max() if idx.size else 0.0):.2e}")
     # caches
     for side, rows, init in (("k", res.k_rows, prob.k_cache0), ("v", res.v_rows, prob.v_cache0)):
         got = _storage(da.tensors[f"{side}_cache"], prob.kv_dtype).reshape(init.shape)
@@ -116,9 +133,9 @@ def test_append_rows_past_the_rotary_table_are_flagged():
     check_append(prob, _run(prob), expect_err=pkv.PKV_DEVERR_POS_RANGE)
 
 
-@pytest.mark.parametrize("kv", [W.BF16, W.E4M3])
-def test_append_full_size_h1_row(kv):
-    prob = W.append_h64x8_b32_decode(kv_dtype=kv)
+@pytest.mark.parametrize("kv,q_quant", [(W.BF16, 0), (W.E4M3, 0), (W.E4M3, 1)])
+def test_append_full_size_h1_row(kv, q_quant):
+    prob = W.append_h64x8_b32_decode(kv_dtype=kv, q_quant=q_quant)
     say(f"case {prob.name}")
     check_append(prob, _run(prob))
 
@@ -153,11 +170,14 @@ def test_append_e4m3_codes_round_to_nearest_even_and_saturate():
     assert mism.size == 0, f"{mism.size} codes differ, e.g. value {want[mism[0]]}: got {codes[mism[0]]:#x} want {ref[mism[0]]:#x}"
 
 
-def test_append_graph_replay_matches_eager():
+@pytest.mark.parametrize("q_quant", [0, 1])
+def test_append_graph_replay_matches_eager(q_quant):
     prob = W.make_append_problem(name="app-graph", seed=26, new_lens=[2, 1, 4], seq_lens=[20, 9, 4],
-                                 num_qo_heads=64, num_kv_heads=8, page_size=16, norm_policy=2)
+                                 num_qo_heads=64, num_kv_heads=8, page_size=16, norm_policy=2, q_quant=q_quant,
+                                 q_scale_layout=1, q_scale_stride=128)
     da = _run(prob)
-    ref = {k: da.tensors[k].clone() for k in ("out_q", "k_cache", "v_cache")}
+    keys = ("out_q", "k_cache", "v_cache") + (("q_scale",) if q_quant == 1 else ())
+    ref = {k: da.tensors[k].clone() for k in keys}
     g = torch.cuda.CUDAGraph()
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -168,11 +188,48 @@ def test_append_graph_replay_matches_eager():
     with torch.cuda.graph(g):
         da.run()
     for _ in range(3):
-        da.tensors["out_q"].fill_(-1)
+        da.tensors["out_q"].fill_(-1 if q_quant == 0 else 0xFF)
+        if q_quant == 1:
+            da.tensors["q_scale"].fill_(float("nan"))
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
         for k, v in ref.items():
-            assert torch.equal(da.tensors[k], v), k
+            assert torch.equal(da.tensors[k], v) if k != "q_scale" else torch.equal(
+                torch.nan_to_num(da.tensors[k], nan=-7.0), torch.nan_to_num(v, nan=-7.0)), k
         da.run()
         torch.cuda.synchronize()
+
+
+# ---- e4m3 query output (PR #5956 body, "Contract": quant_policy 1 dynamic per
+# (row, head) scale, quant_policy 2 static inverse scale)
+
+@pytest.mark.parametrize("q_quant,upper", [(1, 448.0), (1, 240.0), (2, 448.0)])
+@pytest.mark.parametrize("kv", [W.BF16, W.E4M3])
+def test_append_query_e4m3_decode_h64x8(q_quant, upper, kv):
+    prob = W.make_append_problem(name="app-q8-dec", seed=30, new_lens=[1] * 5, seq_lens=[1, 16, 17, 100, 333],
+                                 num_qo_heads=64, num_kv_heads=8, page_size=16, norm_policy=2, kv_dtype=kv,
+                                 k_scale=0.05 if kv == W.E4M3 else 1.0, v_scale=0.04 if kv == W.E4M3 else 1.0,
+                                 q_quant=q_quant, upper_max=upper, q_scale_inv=16.0)
+    say(f"case append e4m3 query decode q_quant={q_quant} upper_max={upper} kv={kv}")
+    check_append(prob, _run(prob), label=f"q{q_quant} u{upper:g} {kv}")
+
+
+@pytest.mark.parametrize("rows", [127, 128, 129])
+def test_append_query_e4m3_prefill_scale_padding_edge(rows):
+    # the pages' E rows: prefill, dynamic scales, norm 2, four requests of Q new
+    # rows each, the scale layout's last axis max_seqlen = Q rounded up to 128
+    stride = (rows + 127) // 128 * 128
+    prob = W.make_append_problem(name="app-q8-pre", seed=31 + rows, new_lens=[rows] * 4, seq_lens=[rows] * 4,
+                                 num_qo_heads=8, num_kv_heads=1, page_size=64, norm_policy=2, kv_dtype=W.E4M3,
+                                 k_scale=0.05, v_scale=0.05, q_quant=1, upper_max=448.0, q_scale_layout=1,
+                                 q_scale_stride=stride)
+    say(f"case append e4m3 query prefill rows={rows} stride={stride}")
+    check_append(prob, _run(prob), label=f"prefill Q{rows}")
+
+
+def test_append_query_e4m3_rows_past_the_scale_stride_are_flagged():
+    prob = W.make_append_problem(name="app-q8-stride", seed=35, new_lens=[3, 6, 2], seq_lens=[9, 6, 2],
+                                 num_qo_heads=8, num_kv_heads=1, page_size=4, norm_policy=2, q_quant=1,
+                                 upper_max=448.0, q_scale_layout=1, q_scale_stride=4)
+    check_append(prob, _run(prob), expect_err=pkv.PKV_DEVERR_QSCALE_ROWS)
