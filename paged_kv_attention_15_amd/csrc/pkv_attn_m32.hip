@@ -218,6 +218,9 @@ __device__ __forceinline__ void m32_block(const KParams& p, unsigned char* smem,
 
   const int pg_lo = kv_lo >> p.log2_page;
   const int n_pg = n_tiles > 0 ? ((kv_hi - 1) >> p.log2_page) - pg_lo + 1 : 0;
+  // a separate V table (API page, context profile with separate K/V page
+  // tables) gets its own list right after the K list
+  int32_t* s_vpages = p.v_table ? s_pages + p.page_list_cap : s_pages;
   for (int i = tid; i < n_pg; i += C::NTHR) {
     int pg = p.table[(int64_t)b * p.table_stride + pg_lo + i];
     if (p.num_pages > 0 && (pg < 0 || pg >= p.num_pages)) {
@@ -225,6 +228,14 @@ __device__ __forceinline__ void m32_block(const KParams& p, unsigned char* smem,
       pg = min(max(pg, 0), p.num_pages - 1);
     }
     s_pages[i] = pg;
+    if (p.v_table) {
+      int vpg = p.v_table[(int64_t)b * p.table_stride + pg_lo + i];
+      if (p.num_pages > 0 && (vpg < 0 || vpg >= p.num_pages)) {
+        flag_error(p.err_word, PKV_DEVERR_PAGE_RANGE);
+        vpg = min(max(vpg, 0), p.num_pages - 1);
+      }
+      s_vpages[i] = vpg;
+    }
   }
 
   const float k_scale = p.k_scale_dev ? *p.k_scale_dev : p.k_scale;
@@ -295,14 +306,17 @@ __device__ __forceinline__ void m32_block(const KParams& p, unsigned char* smem,
   // page 64k + l (the planner keeps a partition within 64 * kPageRegs pages): a
   // wave-instruction's page is then one v_readlane, with no memory access whose
   // wait counter would also cover the ring's loads in flight.
-  int pl[kPageRegs];
+  int pl[kPageRegs], plv[kPageRegs];  // K pages, V pages (the same list without a V table)
 #pragma unroll
-  for (int k = 0; k < kPageRegs; ++k) pl[k] = 64 * k + lane < n_pg ? s_pages[64 * k + lane] : 0;
-  auto page_of = [&](int idx) -> uint32_t {
-    int v = __builtin_amdgcn_readlane(pl[0], idx & 63);
+  for (int k = 0; k < kPageRegs; ++k) {
+    pl[k] = 64 * k + lane < n_pg ? s_pages[64 * k + lane] : 0;
+    plv[k] = 64 * k + lane < n_pg ? s_vpages[64 * k + lane] : 0;
+  }
+  auto page_of = [&](int idx, bool is_k) -> uint32_t {
+    int v = __builtin_amdgcn_readlane(is_k ? pl[0] : plv[0], idx & 63);
 #pragma unroll
     for (int k = 1; k < kPageRegs; ++k)
-      if ((idx >> 6) == k) v = __builtin_amdgcn_readlane(pl[k], idx & 63);
+      if ((idx >> 6) == k) v = __builtin_amdgcn_readlane(is_k ? pl[k] : plv[k], idx & 63);
     return (uint32_t)v;
   };
 
@@ -375,7 +389,7 @@ __device__ __forceinline__ void m32_block(const KParams& p, unsigned char* smem,
       const int I = min(wave * C::KPW + q, C::NI - 1);
       const int r0 = I * 64 < C::KCH ? (I * 64) / C::NCK : (I * 64 - C::KCH) / C::NCV;
       const int tokf = __builtin_amdgcn_readfirstlane(min(tok0 + r0, kv_hi - 1));
-      pgv[q] = page_of((tokf >> p.log2_page) - pg_lo);
+      pgv[q] = page_of((tokf >> p.log2_page) - pg_lo, I * 64 < C::KCH);
     }
 #pragma unroll
     for (int q = 0; q < C::KPW; ++q) {
@@ -960,7 +974,8 @@ bool m32_shape(int32_t kernel, MfmaShape* s) {
 template <class C>
 static hipError_t launch_m32_cfg(const KParams& p, hipStream_t s) {
   static bool attr_done = false;  // idempotent; a race only repeats the same call
-  const size_t lds = C::LDS + (((size_t)p.page_list_cap + 3) & ~size_t(3)) * sizeof(int32_t);
+  const size_t list = (size_t)p.page_list_cap * (p.v_table ? 2 : 1);
+  const size_t lds = C::LDS + ((list + 3) & ~size_t(3)) * sizeof(int32_t);
   if (!attr_done) {
     hipError_t e = hipFuncSetAttribute((const void*)attn_m32_kernel<C>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                        160 * 1024);

@@ -149,6 +149,9 @@ __device__ __forceinline__ void attend_block(const KParams& p, unsigned char* sm
   // ---- page list of the partition -> LDS (clamped to the pool)
   const int pg_lo = kv_lo >> p.log2_page;
   const int n_pg = n_tiles > 0 ? ((kv_hi - 1) >> p.log2_page) - pg_lo + 1 : 0;
+  // a separate V table (API page, context profile with separate K/V page
+  // tables) gets its own list right after the K list
+  int32_t* s_vpages = p.v_table ? s_pages + p.page_list_cap : s_pages;
   for (int i = tid; i < n_pg; i += C::NTHR) {
     int pg = p.table[(int64_t)b * p.table_stride + pg_lo + i];
     if (p.num_pages > 0 && (pg < 0 || pg >= p.num_pages)) {
@@ -156,6 +159,14 @@ __device__ __forceinline__ void attend_block(const KParams& p, unsigned char* sm
       pg = min(max(pg, 0), p.num_pages - 1);
     }
     s_pages[i] = pg;
+    if (p.v_table) {
+      int vpg = p.v_table[(int64_t)b * p.table_stride + pg_lo + i];
+      if (p.num_pages > 0 && (vpg < 0 || vpg >= p.num_pages)) {
+        flag_error(p.err_word, PKV_DEVERR_PAGE_RANGE);
+        vpg = min(max(vpg, 0), p.num_pages - 1);
+      }
+      s_vpages[i] = vpg;
+    }
   }
 
   // ---- this lane's query rows: one per row tile
@@ -230,7 +241,7 @@ __device__ __forceinline__ void attend_block(const KParams& p, unsigned char* sm
       const int r = q / C::SCV;
       const int sc = q % C::SCV;
       const int tok = min(tok0 + r, kv_hi - 1);
-      const int pg = s_pages[(tok >> p.log2_page) - pg_lo];
+      const int pg = s_vpages[(tok >> p.log2_page) - pg_lo];
       const int64_t off = (int64_t)pg * p.v_sp + (int64_t)g * p.v_sh + (int64_t)(tok & pmask) * p.v_stok;
       vreg[i] = __builtin_nontemporal_load((const u32x4*)(vbase + off * C::EB + sc * 16));
     }
@@ -601,7 +612,8 @@ bool mfma_shape(int32_t kernel, MfmaShape* s) {
 template <class C>
 static hipError_t launch_cfg(const KParams& p, hipStream_t s) {
   static bool attr_done = false;  // idempotent; a race only repeats the same calls
-  const size_t extra = (size_t)p.page_list_cap + (p.stream ? (size_t)p.batch + 1 : 0);
+  if (p.stream && p.v_table) return hipErrorInvalidValue;  // the balanced schedule keeps one page list
+  const size_t extra = (size_t)p.page_list_cap * (p.v_table ? 2 : 1) + (p.stream ? (size_t)p.batch + 1 : 0);
   const size_t lds = C::LDS + ((extra + 3) & ~size_t(3)) * sizeof(int32_t);
   if (!attr_done) {
     hipError_t e = hipFuncSetAttribute((const void*)attn_mfma_kernel<C>,

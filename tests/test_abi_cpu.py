@@ -303,14 +303,19 @@ def test_append_e4m3_needs_scales_and_empty_calls_are_noops():
     assert pkv.pkv_append(_append_args(num_tokens=0, clear_tail=0), 0, check=False) == pkv.PKV_OK
 
 
-def test_separate_value_tables_route_to_the_generic_kernel():
+def test_separate_value_tables_route_to_families_with_a_second_page_list():
     a = _args_for(_fake())
     a.q = a.k_pages = a.v_pages = a.out = 0x1000
     a.v_block_tables = 0x2000
-    assert pkv.KERNEL_NAMES[pkv.pkv_plan(a).kernel] == "generic"
-    a.kernel_hint = pkv.KERNEL_IDS["gqa_bf16"]
-    assert pkv.pkv_plan(a, check=False).status == pkv.PKV_ERR_UNSUPPORTED
+    plan = pkv.pkv_plan(a)
+    assert pkv.KERNEL_NAMES[plan.kernel] == "gqa_bf16" and plan.schedule == 0  # never the balanced schedule
+    for name in ("dma_gqa_bf16", "dma_gqa_fp8_n2", "dma_wide_bf16"):  # the direct-to-LDS ring keeps one list
+        a.kernel_hint = pkv.KERNEL_IDS[name]
+        assert pkv.pkv_plan(a, check=False).status == pkv.PKV_ERR_UNSUPPORTED
     a.kernel_hint = 0
+    a.num_splits = -1
+    assert pkv.pkv_plan(a, check=False).status == pkv.PKV_ERR_UNSUPPORTED
+    a.num_splits = 0
     a.v_shares_k = 1
     assert pkv.pkv_plan(a, check=False).status == pkv.PKV_ERR_INVALID_ARG
     a.v_shares_k = 0

@@ -359,20 +359,37 @@ def test_sinks_mla(q_len):
     compare(prob, run_gpu(prob))
 
 
-@pytest.mark.parametrize("decode", [True, False])
-def test_separate_value_tables(decode):
+# separate V page tables: the planner's choice per shape (register-staged
+# tiles for decode, the 32x32 kernel for bf16 context, the wide tiles for e4m3
+# context), forced split partitions, and the other families that keep a second
+# page list
+@pytest.mark.parametrize("decode,kv,kernel,splits,expect", [
+    (True, W.BF16, None, None, "gqa_bf16"),
+    (True, W.E4M3, None, None, "gqa_fp8"),
+    (True, W.BF16, None, 3, "gqa_bf16"),
+    (True, W.BF16, "generic", None, "generic"),
+    (True, W.BF16, "gqa_bf16_t256", None, "gqa_bf16_t256"),
+    (False, W.BF16, None, None, "m32_ctx_w8"),
+    (False, W.BF16, "m32_ctx_w8", 3, "m32_ctx_w8"),
+    (False, W.E4M3, None, None, "wide_fp8"),
+    (False, W.BF16, "wide_bf16", None, "wide_bf16"),
+    (False, W.BF16, "generic", None, "generic"),
+])
+def test_separate_value_tables(decode, kv, kernel, splits, expect):
     if decode:
-        prob = _gqa([1, 31, 64, 65, 700], separate_v_table=True, sinks=True)
+        prob = _gqa([1, 31, 64, 65, 700], kv=kv, separate_v_table=True, sinks=True)
     else:
         prob = W.make_problem(name="ctx-vtab", seed=12, batch=2, seq_lens=[300, 40], q_lens=[30, 40],
                               num_qo_heads=16, num_kv_heads=2, head_dim_qk=128, head_dim_v=128, page_size=16,
-                              is_decode=False, poison=True, extra_page_frac=0.3, table_slack_pages=1,
-                              separate_v_table=True)
-    dp = pkv.upload(prob, "cuda")
-    assert pkv.KERNEL_NAMES[pkv.pkv_plan(dp.args, dp.is_context).kernel] == "generic"
+                              kv_dtype=kv, q_dtype=W.BF16, o_dtype=W.BF16, is_decode=False, poison=True,
+                              extra_page_frac=0.3, table_slack_pages=1, separate_v_table=True)
+    dp = pkv.upload(prob, "cuda", kernel=kernel, num_splits=splits)
+    info = pkv.pkv_plan(dp.args, dp.is_context)
+    assert pkv.KERNEL_NAMES[info.kernel] == expect
+    say(f"case separate V tables decode={decode} kv={kv} kernel={expect} splits={info.num_splits}")
     dp.run()
     torch.cuda.synchronize()
-    compare(prob, dp, label=f"separate V tables decode={decode}")
+    compare(prob, dp, label=f"separate V tables decode={decode} {kv} {expect}")
 
 
 @pytest.mark.parametrize("separate", [False, True])
