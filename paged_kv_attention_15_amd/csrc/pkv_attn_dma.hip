@@ -521,14 +521,27 @@ __device__ __forceinline__ void dma_block(const KParams& p, unsigned char* smem,
   }
 }
 
+// Workgroup i runs on XCD i % 8, each XCD with its own L2.  With several row
+// blocks per (request, KV head), which read the same pages, the grid is laid
+// out so that consecutive logical items fall on one XCD and are dispatched one
+// after the other: the row blocks of a request then read its pages once from
+// memory and again from that XCD's L2, not twice from memory (measured on the
+// MLA decode with two speculative rows: 4.98 GB fetched per call before, 2.57
+// GB after, for 2.42 GB of KV).
 template <class C>
 __global__ __launch_bounds__(C::NTHR) void attn_dma_kernel(const KParams p) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   int32_t* s_pages = (int32_t*)(smem + C::LDS);
-  const int split = blockIdx.x;
+  const int nx = gridDim.x, ny = gridDim.y;
+  const int64_t N = (int64_t)nx * ny * gridDim.z;
+  const int64_t P = blockIdx.x + (int64_t)nx * (blockIdx.y + (int64_t)ny * blockIdx.z);
+  const int64_t Lg = (p.row_blocks > 1 && N % 8 == 0) ? (P % 8) * (N / 8) + P / 8 : P;
+  const int split = (int)(Lg % nx);
+  const int y = (int)((Lg / nx) % ny);
+  const int z = (int)(Lg / ((int64_t)nx * ny));
   const int span = p.pages_per_split * p.page_size;
-  dma_block<C>(p, smem, s_pages, blockIdx.z, blockIdx.y / p.row_blocks, blockIdx.y % p.row_blocks, split * span,
-               split * span + span, split, split == 0);
+  dma_block<C>(p, smem, s_pages, z, y / p.row_blocks, y % p.row_blocks, split * span, split * span + span, split,
+               split == 0);
 }
 
 // Fused reducer of the balanced schedule.  Unit u = (request b, KV head g) owns
