@@ -202,6 +202,7 @@ def secondary_results(steps: int, warmup: int, single_call: bool = True):
         ("mla-b512-kv4096-q1", lambda: W.mla_b512_kv4096(q_len=1), "hbm"),
         ("mla-b512-kv4096-q2", lambda: W.mla_b512_kv4096(q_len=2), "mfma"),
         ("ctx-b4-q511-kv2047", lambda: W.context_b4_q511_kv2047(), "mfma"),
+        ("ctx-b4-q257-kv1024-p1024-sepkv", lambda: W.context_b4_q257_kv1024_p1024(separate=True), "mfma"),
     ]
     for name, make, bound in cases:
         prob = make()

@@ -181,17 +181,20 @@ hipError_t launch_generic(const KParams& p, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------- LSE merge
-// One workgroup of kMergeThreads threads per merged row.  The row's value
-// channels are cut into items of CW channels; when there are fewer items than
-// threads, the threads of one item split the partitions between them
-// (partition s goes to subset s mod S_sub).  Each thread walks its partitions
-// with the running-max update of the online softmax (m, l and the channel sums
-// rescaled whenever the max grows), loading a batch of partitions' LSE and
-// partial channels before using any of them, so a row costs about one memory
-// round trip however many partitions it has; the subsets meet in LDS.  An
-// empty partition (lse = -inf, channels never written) is selected out, never
-// multiplied.  With request geometry attached (decode / context calls) a row
-// reads only the partitions that can hold one of its visible keys: the
+// A workgroup of kMergeThreads threads merges rows_per_wg rows; each row gets
+// NQ * subsets threads.  The row's value channels are cut into NQ items of CW
+// channels, and the threads of one item split the partitions between them
+// (partition s goes to subset s mod subsets).  Each thread walks its
+// partitions with the running-max update of the online softmax (m, l and the
+// channel sums rescaled whenever the max grows), loading a batch of
+// partitions' LSE and partial channels before using any of them, so a row
+// costs about one memory round trip per kMergeBatch partitions of a subset;
+// the subsets meet in LDS.  Few partitions per row (a split context or decode
+// plan) need one subset, so a workgroup takes several rows: a call with tens of
+// thousands of rows then launches a few thousand workgroups, not one per row.
+// An empty partition (lse = -inf, channels never written) is selected out,
+// never multiplied.  With request geometry attached (decode / context calls)
+// a row reads only the partitions that can hold one of its visible keys: the
 // attention kernel skips the rest without writing them.
 constexpr int kMergeThreads = 256;
 constexpr int kMergeBatch = 4;
@@ -203,18 +206,16 @@ struct MergeRow {
   int64_t num_wg;
 };
 
+// tl: this thread's index among the NQ * S_sub threads of its row; s_red: the
+// row's LDS scratch (NQ * S_sub entries of CW + 2 floats).  Every thread of the
+// workgroup calls this exactly once and passes exactly one barrier in it.
 template <int CW>
-__device__ __forceinline__ void merge_row(const MergeParams& mp, const MergeRow& mr, const int64_t r,
-                                          const int64_t t, const int h, float* s_red) {
+__device__ __forceinline__ void merge_row(const MergeParams& mp, const MergeRow& mr, const int64_t t, const int h,
+                                          const bool write, float* s_red, const int tl, const int S_sub) {
   const int dv = mp.dv;
   const int NQ = (dv + CW - 1) / CW;  // items
-  const int tid = threadIdx.x;
-  const int S_sub = NQ >= kMergeThreads ? 1 : kMergeThreads / NQ;
-  const int sub = NQ >= kMergeThreads ? 0 : tid / NQ;
-  if (sub >= S_sub) {
-    __syncthreads();  // matches the subsets' LDS exchange below
-    return;
-  }
+  const int TG = NQ * S_sub;           // threads of this row (NQ >= kMergeThreads: S_sub = 1, TG = kMergeThreads)
+  const int sub = NQ >= kMergeThreads ? 0 : tl / NQ;
   // balanced schedule: an owner range may hold workgroups with an empty range,
   // but only when there are fewer virtual pages than workgroups (otherwise
   // every range holds at least one page)
@@ -227,7 +228,9 @@ __device__ __forceinline__ void merge_row(const MergeParams& mp, const MergeRow&
     }
     return mp.lse_part[mr.prow0 + s * mr.step];
   };
-  for (int q = (NQ >= kMergeThreads ? tid : tid % NQ); q < NQ; q += (NQ >= kMergeThreads ? kMergeThreads : NQ)) {
+  const int q0 = NQ >= kMergeThreads ? tl : tl % NQ;
+  const int qstep = NQ >= kMergeThreads ? kMergeThreads : NQ;
+  for (int q = q0; q < NQ; q += qstep) {
     float m = -INFINITY, l = 0.f;
     float acc[CW];
 #pragma unroll
@@ -267,8 +270,6 @@ __device__ __forceinline__ void merge_row(const MergeParams& mp, const MergeRow&
       e[1] = l;
 #pragma unroll
       for (int c = 0; c < CW; ++c) e[2 + c] = acc[c];
-    }
-    if (S_sub > 1) {
       __syncthreads();
       if (sub != 0) return;
       float M = -INFINITY;
@@ -287,6 +288,7 @@ __device__ __forceinline__ void merge_row(const MergeParams& mp, const MergeRow&
       }
       m = M;
     }
+    if (!write) continue;
     float inv = l > 0.f ? 1.f / l : 0.f;
     float lse_row = (m == -INFINITY) ? -INFINITY : m + __logf(l);
     if (mp.sinks) inv *= fold_sink(lse_row, mp.sinks[h]);
@@ -301,39 +303,46 @@ __device__ __forceinline__ void merge_row(const MergeParams& mp, const MergeRow&
         ((float*)mp.out)[oi] = acc[c] * inv;
       }
     }
-    if (mp.lse_out && q == 0) mp.lse_out[r] = lse_row;
+    if (mp.lse_out && q == 0) mp.lse_out[t * mp.num_qo_heads + h] = lse_row;
   }
-  if (S_sub == 1) __syncthreads();  // matches the idle threads' barrier
+  if (S_sub == 1) __syncthreads();  // the one barrier of threads that merge without subsets
 }
 
 __global__ __launch_bounds__(kMergeThreads) void lse_merge_kernel(const MergeParams mp) {
   __shared__ float s_red[kMergeThreads * 6];
-  // row indices in 32 bits (the grid's x extent): the 64-bit integer division
+  const int NQ = (mp.dv + (mp.vec4 ? 4 : 1) - 1) / (mp.vec4 ? 4 : 1);
+  const int TG = NQ >= kMergeThreads ? kMergeThreads : NQ * mp.subsets;
+  const int lr = threadIdx.x / TG;  // row of this thread inside the workgroup
+  const int tl = threadIdx.x - lr * TG;
+  // row indices in 32 bits (the grid's x extent times rows_per_wg stays below
+  // 2^31: the host checks the row count): the 64-bit integer division
   // sequences cost more than the rest of a merged row
-  const uint32_t r32 = blockIdx.x;
-  if (r32 >= mp.num_rows) return;
+  const uint32_t r32 = blockIdx.x * (uint32_t)mp.rows_per_wg + (uint32_t)lr;
+  const bool in_range = lr < mp.rows_per_wg && r32 < (uint32_t)mp.num_rows;
   const uint32_t nh = (uint32_t)mp.num_qo_heads;
-  const uint32_t t32 = r32 / nh;
+  const uint32_t t32 = in_range ? r32 / nh : 0;
   const int64_t r = r32, t = t32;
-  const int h = (int)(r32 - t32 * nh);
+  const int h = in_range ? (int)(r32 - t32 * nh) : 0;
+  float* s_row = s_red + (lr * TG) * (mp.vec4 ? 6 : 3);
 
   // partial rows of this output row: `live` slots, slot k at partial row
   // prow0 + k*step (Split-KV layout: [split][row]; stream layout: a row
   // of slot (w + u) for the consecutive workgroups w that own unit u's pages)
   MergeRow mr;
-  mr.live = mp.num_splits;
+  mr.live = in_range ? mp.num_splits : 0;
   mr.prow0 = r;
   mr.step = mp.num_rows;
   mr.w_first = 0;
   mr.TPs = 0;
   mr.num_wg = mp.num_wg;
-  if (mp.stream) {
+  bool write = in_range;
+  if (in_range && mp.stream) {
     const uint32_t ql = (uint32_t)mp.q_len;
     const int b = (int)(t32 / ql);
     const int i = (int)(t32 - (uint32_t)b * ql);
     const int g = h / mp.group;
     const int R = i * mp.group + (h % mp.group);
-    if (i == 0 && h == 0 && threadIdx.x == 0) {
+    if (i == 0 && h == 0 && tl == 0) {
       const int L0 = mp.seq_lens[b];
       if (L0 > mp.cap_tokens) flag_error(mp.err_word, PKV_DEVERR_SEQ_GT_TABLE);
       if (L0 < mp.q_len) flag_error(mp.err_word, PKV_DEVERR_SEQ_LT_QLEN);
@@ -357,37 +366,53 @@ __global__ __launch_bounds__(kMergeThreads) void lse_merge_kernel(const MergePar
       mr.w_first = w_s;
       mr.TPs = sg.TV;
     }
-  } else if (mp.seq_lens) {
+  } else if (in_range && mp.seq_lens) {
     int b, t0, n;
+    bool skip = false;
     if (mp.is_context) {
       int lo = 0, hi = mp.batch - 1;
       while (lo < hi) {
         int mid = (lo + hi + 1) >> 1;
-        if (mp.q_indptr[mid] <= t) lo = mid; else hi = mid - 1;
+        if (mp.q_indptr[mid] <= (int)t32) lo = mid; else hi = mid - 1;
       }
       b = lo;
       t0 = mp.q_indptr[b];
       const int a1 = mp.q_indptr[b + 1];
       const bool bad = (t0 < 0) || (a1 < t0) || (a1 - t0 > mp.max_q_len) || (a1 > mp.total_q);
-      if (bad || t < t0 || t >= a1) return;  // the attention kernel skipped this row too
+      skip = bad || (int)t32 < t0 || (int)t32 >= a1;  // the attention kernel skipped this row too
       n = a1 - t0;
     } else {
       b = (int)(t32 / (uint32_t)mp.q_len);
       t0 = b * mp.q_len;
       n = mp.q_len;
     }
-    const int i = (int)(t - t0);
-    const int L = max(0, min(mp.seq_lens[b], mp.cap_tokens));
-    const int c = mp.causal ? min(L, max(0, L - n + i + 1)) : L;
-    mr.live = min(mp.num_splits, (c + mp.split_tokens - 1) / mp.split_tokens);
+    if (skip) {
+      mr.live = 0;
+      write = false;
+    } else {
+      const int i = (int)(t32 - t0);
+      const int L = max(0, min(mp.seq_lens[b], mp.cap_tokens));
+      const int c = mp.causal ? min(L, max(0, L - n + i + 1)) : L;
+      mr.live = min(mp.num_splits, (c + mp.split_tokens - 1) / mp.split_tokens);
+    }
   }
-  if (mp.vec4) merge_row<4>(mp, mr, r, t, h, s_red);
-  else merge_row<1>(mp, mr, r, t, h, s_red);
+  if (mp.vec4) merge_row<4>(mp, mr, t, h, write, s_row, tl, mp.subsets);
+  else merge_row<1>(mp, mr, t, h, write, s_row, tl, mp.subsets);
 }
 
-hipError_t launch_merge(const MergeParams& mp, hipStream_t s) {
+hipError_t launch_merge(MergeParams mp, hipStream_t s) {
   if (mp.num_rows == 0) return hipSuccess;
-  hipLaunchKernelGGL(lse_merge_kernel, dim3((unsigned)mp.num_rows), dim3(kMergeThreads), 0, s, mp);
+  // Thread subsets per row: enough that each walks about one batch of
+  // partitions (the balanced schedule's rows may have many owners: all
+  // threads), then as many rows per workgroup as the threads allow.
+  const int NQ = (mp.dv + (mp.vec4 ? 4 : 1) - 1) / (mp.vec4 ? 4 : 1);
+  const int max_sub = NQ >= kMergeThreads ? 1 : kMergeThreads / NQ;
+  const int want = mp.stream ? max_sub : (mp.num_splits + kMergeBatch - 1) / kMergeBatch;
+  mp.subsets = std::max(1, std::min(max_sub, want));
+  const int TG = NQ >= kMergeThreads ? kMergeThreads : NQ * mp.subsets;
+  mp.rows_per_wg = std::max(1, kMergeThreads / TG);
+  const int64_t wgs = (mp.num_rows + mp.rows_per_wg - 1) / mp.rows_per_wg;
+  hipLaunchKernelGGL(lse_merge_kernel, dim3((unsigned)wgs), dim3(kMergeThreads), 0, s, mp);
   return hipGetLastError();
 }
 

@@ -119,8 +119,10 @@ struct MergeParams {
   // 1: head_dim_v % 4 == 0 and o_part 16-byte aligned (partial rows read 16 bytes at a time)
   int32_t vec4;
   const float* sinks;  // [num_qo_heads] sink logits folded into each merged row, or null
+  // set by launch_merge: rows merged per workgroup and thread subsets per row
+  int32_t rows_per_wg, subsets;
 };
-hipError_t launch_merge(const MergeParams& mp, hipStream_t s);
+hipError_t launch_merge(MergeParams mp, hipStream_t s);
 
 // The paged KV append producer (pkv_append.hip); arguments validated by the caller.
 hipError_t launch_append(const pkv_append_args* a, hipStream_t s);

@@ -370,6 +370,18 @@ def context_b4_q511_kv2047(seed: int = 0, poison: bool = False) -> Problem:
     )
 
 
+def context_b4_q257_kv1024_p1024(seed: int = 0, separate: bool = True, poison: bool = False) -> Problem:
+    """The API page's second BF16 context profile: B=4, 257 new rows per
+    request over 1024 keys, Hq=64 / Hkv=8, D=128, 1024-token pages, with
+    separate K/V page tables (or the shared table)."""
+    return make_problem(
+        name=f"ctx-b4-q257-kv1024-p1024-sep{int(separate)}", seed=seed, batch=4, seq_lens=[1024] * 4,
+        q_lens=[257] * 4, num_qo_heads=64, num_kv_heads=8, head_dim_qk=128, head_dim_v=128,
+        page_size=1024, q_dtype=BF16, kv_dtype=BF16, is_decode=False, poison=poison,
+        extra_page_frac=0.25 if poison else 0.0, separate_v_table=separate,
+    )
+
+
 WORKLOADS: Dict[str, callable] = {
     "tiny-gqa-fp32": tiny_gqa_fp32,
     "bf16-gqa-b32-kv4096": gqa_bf16_b32_kv4096,

@@ -118,6 +118,18 @@ def test_split_plan_is_page_aligned_and_sized_to_cus():
     assert info7.num_splits == 7 and info7.workspace_bytes >= 7 * rows * 129 * 4
 
 
+def test_context_split_plan_only_fills_the_cus_once():
+    # one request of 511 rows over 2047 keys, Hq 64 / Hkv 8: 16 row blocks x 8 KV
+    # heads = 128 units on 256 CUs -> two partitions (a decode-sized plan of four
+    # partitions per CU would write eight times the rows' fp32 partials)
+    prob = W.make_problem(name="ctx1", seed=0, batch=1, seq_lens=[2047], q_lens=[511], num_qo_heads=64,
+                          num_kv_heads=8, head_dim_qk=128, head_dim_v=128, page_size=32, is_decode=False)
+    info = pkv.pkv_plan(_args_for(prob), True, 256)
+    assert pkv.KERNEL_NAMES[info.kernel] == "m32_ctx_w8" and info.num_splits == 2
+    # four such requests fill the CUs: no split
+    assert pkv.pkv_plan(_args_for(W.context_b4_q511_kv2047()), True, 256).num_splits == 1
+
+
 @pytest.mark.parametrize("field,value,status", [
     ("page_size", 0, pkv.PKV_ERR_INVALID_ARG),
     ("batch", -1, pkv.PKV_ERR_INVALID_ARG),

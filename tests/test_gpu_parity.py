@@ -402,7 +402,12 @@ def test_context_q257_kv1024_page1024_profile(separate):
                           extra_page_frac=0.25, table_slack_pages=1, separate_v_table=separate)
     say(f"case {prob.name}")
     dp = run_gpu(prob)
+    assert pkv.KERNEL_NAMES[pkv.pkv_plan(dp.args, dp.is_context).kernel] == "m32_ctx_w8"
     compare(prob, dp, sample_pairs(prob, 192))
+    # the benchmark's configuration of this profile (no poison, the planner's plan)
+    bprob = W.context_b4_q257_kv1024_p1024(separate=separate)
+    bdp = run_gpu(bprob)
+    compare(bprob, bdp, sample_pairs(bprob, 192), label=f"{bprob.name} (bench configuration)")
 
 
 @pytest.mark.parametrize("P", [1, 2, 1024])
