@@ -377,19 +377,21 @@ pkv_status make_plan(const pkv_args* a, bool is_context, int num_cus, pkv_plan_i
   // needs no reducer.  Otherwise cut every unit into page-aligned partitions so
   // the longest request yields about four partitions per CU: the planner only
   // knows max_kv_len, so shorter requests simply own fewer live partitions
-  // (the rest exit at once and are never merged).  Context rows are many, and
-  // each partition writes and the reducer reads back fp32 partial rows for all
-  // of them, so a context plan takes only the partitions that fill the CUs
-  // once (measured on MI355X for one request of 511 rows over 2047 keys, Hq 64
-  // / Hkv 8: 80.7 us unsplit, 71.1 us with 2 partitions, 85.4 with 4, 122.6
-  // with 8).
+  // (the rest exit at once and are never merged).  When a unit has more than
+  // 16 packed rows (context, MLA), each partition writes and the reducer reads
+  // back fp32 partial rows for all of them, so such plans take only the
+  // partitions that fill the CUs once.  Measured on MI355X: one request of 511
+  // rows over 2047 keys (Hq 64 / Hkv 8): 80.7 us unsplit, 71.1 us with 2
+  // partitions, 85.4 with 4, 122.6 with 8; MLA decode of 64 requests over
+  // 4096 keys: 537 / 298 / 206 / 240 / 300 us with 1 / 2 / 4 / 8 / 16; of 16
+  // requests over 16384 keys: 200 us with 16 partitions, 294 with 64.
   int S = std::max(a->num_splits, 0);
   int64_t pps;
   if (S == 0) {
     if (units >= num_cus) {
       S = 1;
     } else {
-      const int64_t per_cu = is_context ? 1 : 4;
+      const int64_t per_cu = (is_context || rows_per_kv > 16) ? 1 : 4;
       const int64_t want = (per_cu * (int64_t)num_cus + units - 1) / std::max<int64_t>(units, 1);
       const int64_t min_pages = std::max<int64_t>(1, (tile_tokens + a->page_size - 1) / a->page_size);
       const int64_t s_cap = std::max<int64_t>(1, max_pages / min_pages);

@@ -128,6 +128,12 @@ def test_context_split_plan_only_fills_the_cus_once():
     assert pkv.KERNEL_NAMES[info.kernel] == "m32_ctx_w8" and info.num_splits == 2
     # four such requests fill the CUs: no split
     assert pkv.pkv_plan(_args_for(W.context_b4_q511_kv2047()), True, 256).num_splits == 1
+    # MLA decode (128 packed rows per unit) likewise: 64 requests over 4096 keys -> 4 partitions
+    # (arrays drawn for one page per request, the plan's host scalars then set to 4096 keys)
+    a = _args_for(W.mla_b512_kv4096(batch=64, seq_len=64))
+    a.max_kv_len, a.max_pages_per_seq, a.table_stride = 4096, 64, 64
+    info = pkv.pkv_plan(a, False, 256)
+    assert pkv.KERNEL_NAMES[info.kernel] == "dma_mla_bf16" and info.num_splits == 4
 
 
 @pytest.mark.parametrize("field,value,status", [
