@@ -161,6 +161,40 @@ def single_call_stats(dp, kv_bytes: int, samples: int = 30):
     return out
 
 
+def gpu_clocks():
+    """Current and highest shader (sclk) and memory (mclk) clock levels of
+    device 0 from its sysfs DPM tables (the entry marked '*' is the current
+    one), read right after a timed region; None where the files are absent."""
+    import glob
+    import re
+
+    import torch
+
+    props = torch.cuda.get_device_properties(0)
+    bdf = f"{props.pci_domain_id:04x}:{props.pci_bus_id:02x}:{props.pci_device_id:02x}.0"
+    paths = [f"/sys/bus/pci/devices/{bdf}"]
+    cards = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+    if not os.path.exists(os.path.join(paths[0], "pp_dpm_sclk")) and len(cards) == 1:
+        paths.append(os.path.dirname(cards[0]))  # the only card visible: it is device 0
+    out = {"pci": bdf}
+    for name in ("sclk", "mclk"):
+        for base in paths:
+            try:
+                lines = open(os.path.join(base, f"pp_dpm_{name}")).read().splitlines()
+            except OSError:
+                continue
+            levels = [(int(m.group(1)), line.strip().endswith("*"))
+                      for line in lines for m in [re.search(r"(\d+)\s*[Mm]hz", line)] if m]
+            if levels:
+                out[f"{name}_mhz"] = next((v for v, cur in levels if cur), None)
+                out[f"{name}_max_mhz"] = max(v for v, _ in levels)
+                out[f"{name}_source"] = base
+                break
+    if out.get("sclk_mhz") and out.get("sclk_max_mhz"):
+        out["sclk_below_70pct_of_max"] = out["sclk_mhz"] < 0.7 * out["sclk_max_mhz"]
+    return out
+
+
 def measure(prob, steps: int, warmup: int, num_splits=None):
     from paged_kv_attention_15_amd import pkv
 
@@ -304,6 +338,10 @@ def main():
         timing = f"back-to-back eager calls (graph capture failed: {str(exc)[:120]}); one HIP event pair"
     value = kv / wall / 1e9
     achieved = kv / ev_mean / 1e9
+    try:
+        clocks = gpu_clocks()
+    except Exception as exc:  # no sysfs view of the device: report why
+        clocks = {"error": str(exc)[:120]}
     single_kernel = info.num_splits == 1
     line = {
         "metric": METRIC,
@@ -329,6 +367,7 @@ def main():
                      "kernel": f"{pkv.KERNEL_NAMES[info.kernel]} attention kernel" + ("" if single_kernel else " + lse_merge_kernel"),
                      "timing": timing},
         "eager": eager,
+        "clocks": clocks,
     }
     if not args.no_single_call:
         try:
