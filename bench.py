@@ -164,7 +164,8 @@ def single_call_stats(dp, kv_bytes: int, samples: int = 30):
 def gpu_clocks():
     """Current and highest shader (sclk) and memory (mclk) clock levels of
     device 0 from its sysfs DPM tables (the entry marked '*' is the current
-    one), read right after a timed region; None where the files are absent."""
+    one), read before the timed region (ClockSampler follows sclk during it);
+    absent keys where the files are missing."""
     import glob
     import re
 
@@ -195,6 +196,67 @@ def gpu_clocks():
     return out
 
 
+class ClockSampler:
+    """Reads device 0's current sclk level from sysfs every millisecond on a
+    host thread while a timed region runs (the level read after the region
+    shows the idle clock, not the clock the kernels ran at)."""
+
+    def __init__(self, source):
+        import threading
+
+        self.path = os.path.join(source, "pp_dpm_sclk") if source else None
+        self.samples = []
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    def _run(self):
+        import re
+
+        while not self._stop.is_set():
+            try:
+                for line in open(self.path).read().splitlines():
+                    m = re.search(r"(\d+)\s*[Mm]hz", line)
+                    if m and line.strip().endswith("*"):
+                        self.samples.append(int(m.group(1)))
+            except OSError:
+                return
+            self._stop.wait(0.001)
+
+    def __enter__(self):
+        if self.path:
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        if self.path:
+            self._stop.set()
+            self._thread.join()
+
+    def summary(self):
+        if not self.samples:
+            return None
+        v = sorted(self.samples)
+        return {"samples": len(v), "sclk_mhz_median": v[len(v) // 2], "sclk_mhz_min": v[0], "sclk_mhz_max": v[-1]}
+
+
+# MI355X's shader clock climbs from about 1 GHz to 2.2-2.4 GHz over the first
+# 100-200 ms of sustained load (measured with ClockSampler: bf16 decode calls
+# took 87.0 us at a median 1.1 GHz, 83.8 us from 1.5 GHz on), so every workload
+# first runs untimed for this long before its W warm-up calls
+CLOCK_SETTLE_S = 0.3
+
+
+def settle_clocks(dp, seconds: float = CLOCK_SETTLE_S):
+    """Untimed calls for `seconds` of wall time (synchronizing every 20 calls)."""
+    import torch
+
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(20):
+            dp.run()
+        torch.cuda.synchronize()
+
+
 def measure(prob, steps: int, warmup: int, num_splits=None):
     from paged_kv_attention_15_amd import pkv
 
@@ -202,6 +264,7 @@ def measure(prob, steps: int, warmup: int, num_splits=None):
     # (merge_counters) on the ragged e4m3 workload
     dp = pkv.upload(prob, "cuda", with_lse=False, with_err=False, num_splits=num_splits)
     info = pkv.pkv_plan(dp.args, dp.is_context)
+    settle_clocks(dp)
     wall, ev_mean = time_calls(dp, steps, warmup)
     return dp, info, wall, ev_mean
 
@@ -225,7 +288,7 @@ def cpu_baseline(prob, max_pairs: int):
                       f"same workload, single-threaded fp64 C oracle, {dt:.1f} s"}
 
 
-def secondary_results(steps: int, warmup: int, single_call: bool = True):
+def secondary_results(steps: int, warmup: int, single_call: bool = True, clock_source=None):
     import torch
 
     from paged_kv_attention_15_amd import pkv, workloads as W
@@ -241,10 +304,11 @@ def secondary_results(steps: int, warmup: int, single_call: bool = True):
     for name, make, bound in cases:
         prob = make()
         dp, info, wall, ev_mean = measure(prob, steps, warmup)
-        try:
-            wall, ev_mean = time_graph(dp, steps, warmup)
-        except Exception:  # capture unavailable: keep the eager figures
-            pass
+        with ClockSampler(clock_source) as sampler:
+            try:
+                wall, ev_mean = time_graph(dp, steps, warmup)
+            except Exception:  # capture unavailable: keep the eager figures
+                pass
         gbs = prob.kv_bytes() / ev_mean / 1e9
         tflops = prob.flops() / ev_mean / 1e12
         sc = None
@@ -258,7 +322,8 @@ def secondary_results(steps: int, warmup: int, single_call: bool = True):
                "fused_merge": int(info.fused_merge),
                "kv_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
                "tflops": round(tflops, 2), "mfma_frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
-               "bound": bound, "kv_bytes": prob.kv_bytes(), "flops": prob.flops()}
+               "bound": bound, "kv_bytes": prob.kv_bytes(), "flops": prob.flops(),
+               "sclk_during": sampler.summary()}
         out[name] = rec
         del dp
         torch.cuda.empty_cache()
@@ -278,6 +343,7 @@ def append_result(steps: int, warmup: int, fp8: bool = False):
     prob = (W.append_h64x8_b32_decode(norm_policy=2, kv_dtype=W.E4M3, q_quant=1) if fp8
             else W.append_h64x8_b32_decode(norm_policy=2))
     da = pkv.upload_append(prob, "cuda", with_err=False)
+    settle_clocks(da)
     for _ in range(warmup):
         da.run()
     torch.cuda.synchronize()
@@ -333,15 +399,21 @@ def main():
     # headline is the same K calls replayed from HIP graphs, eager kept beside it.
     timing = "HIP graphs of 10 back-to-back calls, replayed; one HIP event pair on the launch stream"
     try:
-        wall, ev_mean = time_graph(dp, args.steps, args.warmup)
-    except Exception as exc:  # capture unavailable: the eager figures are the headline
-        timing = f"back-to-back eager calls (graph capture failed: {str(exc)[:120]}); one HIP event pair"
-    value = kv / wall / 1e9
-    achieved = kv / ev_mean / 1e9
-    try:
         clocks = gpu_clocks()
     except Exception as exc:  # no sysfs view of the device: report why
         clocks = {"error": str(exc)[:120]}
+    with ClockSampler(clocks.get("sclk_source")) as sampler:
+        try:
+            wall, ev_mean = time_graph(dp, args.steps, args.warmup)
+        except Exception as exc:  # capture unavailable: the eager figures are the headline
+            timing = f"back-to-back eager calls (graph capture failed: {str(exc)[:120]}); one HIP event pair"
+    value = kv / wall / 1e9
+    achieved = kv / ev_mean / 1e9
+    during = sampler.summary()
+    if during is not None:
+        clocks["during_timed_calls"] = during
+        if clocks.get("sclk_max_mhz"):
+            clocks["sclk_below_70pct_of_max"] = during["sclk_mhz_median"] < 0.7 * clocks["sclk_max_mhz"]
     single_kernel = info.num_splits == 1
     line = {
         "metric": METRIC,
@@ -368,6 +440,7 @@ def main():
                      "timing": timing},
         "eager": eager,
         "clocks": clocks,
+        "clock_settle_s": CLOCK_SETTLE_S,
     }
     if not args.no_single_call:
         try:
@@ -389,7 +462,7 @@ def main():
         torch.cuda.empty_cache()
     if not args.no_secondary:
         line["secondary"] = secondary_results(max(20, args.steps // 4), max(5, args.warmup // 2),
-                                              not args.no_single_call)
+                                              not args.no_single_call, clocks.get("sclk_source"))
         line["secondary"]["append-h64x8-b32-decode"] = append_result(max(20, args.steps // 4),
                                                                      max(5, args.warmup // 2))
         line["secondary"]["append-h64x8-b32-decode-e4m3-dynq"] = append_result(
