@@ -21,6 +21,7 @@ import json
 import os
 import sys
 import time
+from typing import Optional
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
@@ -246,10 +247,11 @@ class ClockSampler:
 CLOCK_SETTLE_S = 0.3
 
 
-def settle_clocks(dp, seconds: float = CLOCK_SETTLE_S):
+def settle_clocks(dp, seconds: Optional[float] = None):
     """Untimed calls for `seconds` of wall time (synchronizing every 20 calls)."""
     import torch
 
+    seconds = CLOCK_SETTLE_S if seconds is None else seconds
     t0 = time.perf_counter()
     while time.perf_counter() - t0 < seconds:
         for _ in range(20):
@@ -363,6 +365,7 @@ def append_result(steps: int, warmup: int, fp8: bool = False):
 
 
 def main():
+    global CLOCK_SETTLE_S
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
@@ -373,9 +376,12 @@ def main():
     ap.add_argument("--no-single-call", action="store_true",
                     help="skip the warm/cold single-call samples (profiling runs: only the timed calls)")
     ap.add_argument("--cpu-pairs", type=int, default=1024)
+    ap.add_argument("--settle", type=float, default=CLOCK_SETTLE_S,
+                    help="seconds of untimed calls before each workload's warm-up (0: none, as in profiling runs)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device-to-device copy (known bytes) to scale HBM counters")
     args = ap.parse_args()
+    CLOCK_SETTLE_S = max(0.0, args.settle)
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}). "
