@@ -1,0 +1,111 @@
+"""Host-side planner invariants over seeded random argument sets (no GPU).
+
+pkv_plan either rejects a call with a status of its own or returns a plan the
+kernels can run: partitions that cover the longest request with page-aligned
+boundaries, a workspace large enough for every partial row, grid and block
+sizes within the launch limits, page lists within what the kernel families
+hold, separate V tables only on the families that keep a second page list,
+and a kernel_hint honoured or refused, never silently replaced."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+from paged_kv_attention_15_amd import pkv
+
+OK, INVALID, UNSUPPORTED = pkv.PKV_OK, pkv.PKV_ERR_INVALID_ARG, pkv.PKV_ERR_UNSUPPORTED
+DT = {"f32": pkv.PKV_DTYPE_F32, "bf16": pkv.PKV_DTYPE_BF16, "e4m3": pkv.PKV_DTYPE_FP8_E4M3}
+
+
+def _random_args(rng):
+    a = pkv.PkvArgs()
+    context = bool(rng.integers(0, 2))
+    shape = rng.choice(["gqa", "gqa", "mla", "d64", "d96"])
+    if shape == "mla":
+        hkv, G, dqk, dv, mla = 1, int(rng.choice([16, 64, 128])), 576, 512, True
+    else:
+        hkv = int(rng.choice([1, 2, 4, 8, 16]))
+        G = int(rng.choice([1, 2, 4, 8, 16]))
+        dqk = dv = {"gqa": 128, "d64": 64, "d96": 96}[shape]
+        mla = False
+    P = int(rng.choice([1, 2, 4, 5, 8, 16, 24, 32, 64, 128, 1024]))
+    B = int(rng.integers(0, 600))
+    max_kv = int(rng.integers(0, 40000))
+    max_pages = max(1, (max_kv + P - 1) // P + int(rng.integers(0, 3)))
+    a.batch, a.num_kv_heads, a.num_qo_heads = B, hkv, hkv * G
+    a.head_dim_qk, a.head_dim_v, a.v_shares_k = dqk, dv, int(mla)
+    a.page_size, a.max_pages_per_seq, a.max_kv_len = P, max_pages, max_kv
+    a.num_pages = int(rng.integers(0, 2)) * (B * max_pages + 1)
+    if context:
+        a.max_q_len = int(rng.integers(0, 600))
+        a.total_q = int(rng.integers(0, B * max(a.max_q_len, 1) + 1))
+        a.q_len = 1
+    else:
+        a.q_len = int(rng.integers(1, 9))
+    a.q_dtype = DT["f32"] if rng.random() < 0.1 else DT["bf16"]
+    a.kv_dtype = DT[str(rng.choice(["bf16", "bf16", "e4m3", "f32"]))]
+    a.o_dtype = DT["bf16"]
+    a.layout = pkv.PKV_LAYOUT_HND if rng.random() < 0.8 else pkv.PKV_LAYOUT_NHD
+    a.causal = 1
+    a.num_splits = int(rng.choice([0, 0, 0, -1, 1, 2, 3, 16, 255, 256, 300]))
+    for f in ("q", "k_pages", "v_pages", "block_tables", "seq_lens", "q_indptr", "out"):
+        setattr(a, f, 0x10000)
+    if rng.random() < 0.2:
+        a.v_block_tables = 0x20000
+    if rng.random() < 0.2:
+        a.sinks = 0x30000
+    if rng.random() < 0.3:
+        a.kernel_hint = int(rng.choice(sorted(k for k in pkv.KERNEL_NAMES if k > 0)))
+    H = hkv
+    a.q_stride_head, a.q_stride_tok = dqk, a.num_qo_heads * dqk
+    a.o_stride_head, a.o_stride_tok = dv, a.num_qo_heads * dv
+    if a.layout == pkv.PKV_LAYOUT_HND:
+        a.k_stride_tok, a.k_stride_head, a.k_stride_page = dqk, P * dqk, H * P * dqk
+        a.v_stride_tok, a.v_stride_head, a.v_stride_page = dv, P * dv, H * P * dv
+    else:
+        a.k_stride_tok, a.k_stride_head, a.k_stride_page = H * dqk, dqk, P * H * dqk
+        a.v_stride_tok, a.v_stride_head, a.v_stride_page = H * dv, dv, P * H * dv
+    if mla:
+        a.v_stride_tok, a.v_stride_head, a.v_stride_page = a.k_stride_tok, a.k_stride_head, a.k_stride_page
+    a.table_stride = max_pages
+    a.scale, a.k_scale, a.v_scale = 0.088, 1.0, 1.0
+    return a, context
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_plans_are_runnable_or_refused(seed):
+    rng = np.random.default_rng(1000 + seed)
+    n_ok = 0
+    for _ in range(400):
+        a, context = _random_args(rng)
+        info = pkv.pkv_plan(a, context, 256, check=False)
+        st = info.status
+        assert st in (OK, INVALID, UNSUPPORTED), st
+        if st != OK or a.batch == 0:
+            continue
+        n_ok += 1
+        name = pkv.KERNEL_NAMES[info.kernel]
+        what = f"{name} B={a.batch} P={a.page_size} L={a.max_kv_len} S={a.num_splits} ctx={context}"
+        if a.kernel_hint:
+            assert info.kernel == a.kernel_hint, what
+        assert info.block_threads in (64, 128, 256, 512, 1024), what
+        for g in (info.grid_x, info.grid_y, info.grid_z):
+            assert 1 <= g < 2 ** 31, what
+        if a.v_block_tables:
+            assert not name.startswith("dma_") and "mla" not in name and info.schedule == 0, what
+        rows = (a.total_q if context else a.batch * a.q_len) * a.num_qo_heads
+        if info.schedule == 1:  # balanced schedule: one slot of partial rows per workgroup and unit
+            assert not context and info.num_splits == info.grid_x + info.counter_words, what
+            slot_rows = a.q_len * (a.num_qo_heads // a.num_kv_heads)
+            assert info.workspace_bytes >= info.num_splits * slot_rows * (a.head_dim_v + 1) * 4, what
+            continue
+        S, pps = info.num_splits, info.pages_per_split
+        assert 1 <= S <= 256 and pps >= 1, what
+        assert S * pps * a.page_size >= a.max_kv_len, what  # the partitions cover the longest request
+        if a.num_splits <= 0:
+            assert (S - 1) * pps * a.page_size < max(a.max_kv_len, 1), what  # no partition starts past it
+        if S > 1:
+            assert info.workspace_bytes >= S * rows * (a.head_dim_v + 1) * 4, what
+        if name.startswith("m32_"):
+            assert pps <= 128, what  # the 32x32 kernels hold the page list in two registers per lane
+    assert n_ok > 50
