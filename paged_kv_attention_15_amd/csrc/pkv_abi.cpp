@@ -217,6 +217,7 @@ bool kernel_supports(int32_t k, const pkv_args* a, bool is_context) {
     case pkv::KERNEL_M32_CTX_R2W8:
     case pkv::KERNEL_M32_CTX_PP:
     case pkv::KERNEL_M32_CTX_IW:
+    case pkv::KERNEL_M32_CTX_W8T128:
       return d128 && !fp8 && a->page_size >= 4;
     case pkv::KERNEL_M32_MLA_BF16: return mla && !fp8 && a->page_size % 32 == 0;
   }
@@ -225,7 +226,8 @@ bool kernel_supports(int32_t k, const pkv_args* a, bool is_context) {
 
 // the 32x32 MFMA family (pkv_attn_m32.hip): page lists held in registers
 bool is_m32(int32_t k) {
-  return (k >= pkv::KERNEL_M32_CTX_BF16 && k <= pkv::KERNEL_M32_CTX_PP) || k == pkv::KERNEL_M32_CTX_IW;
+  return (k >= pkv::KERNEL_M32_CTX_BF16 && k <= pkv::KERNEL_M32_CTX_PP) || k == pkv::KERNEL_M32_CTX_IW ||
+         k == pkv::KERNEL_M32_CTX_W8T128;
 }
 
 bool is_gqa_family(int32_t k) {
@@ -280,19 +282,21 @@ int32_t choose_kernel(const pkv_args* a, bool is_context) {
     if (a->head_dim_qk != 128 || a->head_dim_v != 128 || a->v_shares_k) return pkv::KERNEL_GENERIC;
     const int64_t rows = is_context ? (int64_t)a->max_q_len * G : (int64_t)a->q_len * G;
     if (!is_context && rows <= 16) return fp8 ? pkv::KERNEL_GQA_FP8 : pkv::KERNEL_GQA_BF16;
-    if (is_context && !fp8) return pkv::KERNEL_M32_CTX_W8;
+    if (is_context && !fp8) return pkv::KERNEL_M32_CTX_W8T128;
     return fp8 ? pkv::KERNEL_WIDE_FP8 : pkv::KERNEL_WIDE_BF16;
   }
   // Measured on MI355X (bf16 GQA decode B32/L4096, e4m3 ragged decode B16, MLA
   // B512/L4096, causal context B4 q511/L2047): register-staged tiles win for
   // bf16 decode, the direct-to-LDS ring for e4m3 decode (two-wave groups, four
   // per CU) and MLA, the 32x32 MFMA family with two waves per SIMD for bf16
-  // context (the variant with the next block's S^T interleaved with the softmax
-  // measured within +-3 % of it over five runs on different boxes).
+  // context, in the form with two 128-key stages (2-3 % faster than four 64-key
+  // stages in five back-to-back pairs: half the workgroup barriers; 96-key
+  // stages were 2-4 % slower; the variant with the next block's S^T interleaved
+  // with the softmax measured within +-3 % of the 64-key form).
   if (a->head_dim_qk == 128 && a->head_dim_v == 128 && !a->v_shares_k) {
     const int64_t rows = is_context ? (int64_t)a->max_q_len * G : (int64_t)a->q_len * G;
     if (!is_context && rows <= 16) return fp8 ? pkv::KERNEL_DMA_GQA_FP8_N2 : pkv::KERNEL_GQA_BF16;
-    if (is_context && !fp8) return pkv::KERNEL_M32_CTX_W8;
+    if (is_context && !fp8) return pkv::KERNEL_M32_CTX_W8T128;
     return fp8 ? pkv::KERNEL_DMA_WIDE_FP8 : pkv::KERNEL_DMA_WIDE_BF16;
   }
   if (a->head_dim_qk == 576 && a->head_dim_v == 512 && a->v_shares_k)

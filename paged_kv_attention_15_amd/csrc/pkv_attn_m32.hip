@@ -947,6 +947,7 @@ using M32CtxR2 = M32Cfg<128, 128, false, 2, 4, 1, 4, 2, false>;   // 256 rows, 6
 using M32CtxR2W8 = M32Cfg<128, 128, false, 2, 8, 2, 4, 2, false>;  // 512 rows, 64 rows per wave, 128 KiB
 using M32CtxPP = M32Cfg<128, 128, false, 1, 8, 2, 4, 2, false, 1, true>;  // 256 rows, ping-pong halves
 using M32CtxIW = M32Cfg<128, 128, false, 1, 8, 2, 4, 2, false, 1, false, true>;  // W8 with in-wave overlap
+using M32CtxW8T128 = M32Cfg<128, 128, false, 1, 8, 4, 2, 2, false>;  // W8 with 128-key stages, two of them
 
 template <class C>
 static void fill_m32_shape(MfmaShape* s) {
@@ -967,6 +968,7 @@ bool m32_shape(int32_t kernel, MfmaShape* s) {
     case KERNEL_M32_CTX_R2W8: fill_m32_shape<M32CtxR2W8>(s); return true;
     case KERNEL_M32_CTX_PP: fill_m32_shape<M32CtxPP>(s); return true;
     case KERNEL_M32_CTX_IW: fill_m32_shape<M32CtxIW>(s); return true;
+    case KERNEL_M32_CTX_W8T128: fill_m32_shape<M32CtxW8T128>(s); return true;
     default: return false;
   }
 }
@@ -998,6 +1000,7 @@ hipError_t launch_m32(int32_t kernel, const KParams& p, hipStream_t s) {
     case KERNEL_M32_CTX_R2W8: return launch_m32_cfg<M32CtxR2W8>(p, s);
     case KERNEL_M32_CTX_PP: return launch_m32_cfg<M32CtxPP>(p, s);
     case KERNEL_M32_CTX_IW: return launch_m32_cfg<M32CtxIW>(p, s);
+    case KERNEL_M32_CTX_W8T128: return launch_m32_cfg<M32CtxW8T128>(p, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -49,7 +49,8 @@ enum KernelId : int32_t {
   KERNEL_DMA_GQA_FP8_N1 = 33,   // 1 token wave, 32-key tiles, 3 stages (24 KiB: six groups per CU)
   KERNEL_DMA_GQA_FP8_N2S3 = 34, // 2 token waves, 64-key tiles, 3 stages (48 KiB)
   KERNEL_M32_CTX_IW = 35,       // D = 128, 8 waves x 32 rows, S^T of the next block interleaved with the softmax
-  KERNEL_COUNT = 36,
+  KERNEL_M32_CTX_W8T128 = 36,   // D = 128, 8 waves x 32 rows, 2 x 64 KiB stages of 128 keys (half the barriers of W8)
+  KERNEL_COUNT = 37,
 };
 
 // Everything a kernel reads, by value.  Element strides as in pkv_args.

@@ -93,7 +93,7 @@ def test_kernel_choice_by_shape():
     c = _args_for(_fake(q_lens=[20, 30], seq_lens=[40, 70], is_decode=False))
     c.q = c.k_pages = c.v_pages = c.out = 0x1000
     info = pkv.pkv_plan(c, True)
-    assert pkv.KERNEL_NAMES[info.kernel] == "m32_ctx_w8"
+    assert pkv.KERNEL_NAMES[info.kernel] == "m32_ctx_w8t128"
     # MLA shape
     m = _args_for(_fake(num_qo_heads=16, num_kv_heads=1, head_dim_qk=576, head_dim_v=512, page_size=64,
                         mla=True))
@@ -125,7 +125,7 @@ def test_context_split_plan_only_fills_the_cus_once():
     prob = W.make_problem(name="ctx1", seed=0, batch=1, seq_lens=[2047], q_lens=[511], num_qo_heads=64,
                           num_kv_heads=8, head_dim_qk=128, head_dim_v=128, page_size=32, is_decode=False)
     info = pkv.pkv_plan(_args_for(prob), True, 256)
-    assert pkv.KERNEL_NAMES[info.kernel] == "m32_ctx_w8" and info.num_splits == 2
+    assert pkv.KERNEL_NAMES[info.kernel] == "m32_ctx_w8t128" and info.num_splits == 2
     # four such requests fill the CUs: no split
     assert pkv.pkv_plan(_args_for(W.context_b4_q511_kv2047()), True, 256).num_splits == 1
     # MLA decode (128 packed rows per unit) likewise: 64 requests over 4096 keys -> 4 partitions

@@ -369,7 +369,7 @@ def test_sinks_mla(q_len):
     (True, W.BF16, None, 3, "gqa_bf16"),
     (True, W.BF16, "generic", None, "generic"),
     (True, W.BF16, "gqa_bf16_t256", None, "gqa_bf16_t256"),
-    (False, W.BF16, None, None, "m32_ctx_w8"),
+    (False, W.BF16, None, None, "m32_ctx_w8t128"),
     (False, W.BF16, "m32_ctx_w8", 3, "m32_ctx_w8"),
     (False, W.E4M3, None, None, "wide_fp8"),
     (False, W.BF16, "wide_bf16", None, "wide_bf16"),
@@ -402,7 +402,7 @@ def test_context_q257_kv1024_page1024_profile(separate):
                           extra_page_frac=0.25, table_slack_pages=1, separate_v_table=separate)
     say(f"case {prob.name}")
     dp = run_gpu(prob)
-    assert pkv.KERNEL_NAMES[pkv.pkv_plan(dp.args, dp.is_context).kernel] == "m32_ctx_w8"
+    assert pkv.KERNEL_NAMES[pkv.pkv_plan(dp.args, dp.is_context).kernel] == "m32_ctx_w8t128"
     compare(prob, dp, sample_pairs(prob, 192))
     # the benchmark's configuration of this profile (no poison, the planner's plan)
     bprob = W.context_b4_q257_kv1024_p1024(separate=separate)
@@ -515,7 +515,8 @@ def test_gqa_kernel_families_match_oracle(kernel, kv, splits):
                                            ("m32_ctx_bf16", 3), ("m32_ctx_w8", None), ("m32_ctx_r1", None),
                                            ("m32_ctx_r1s3", None), ("m32_ctx_r1", 2), ("m32_ctx_r2", None),
                                            ("m32_ctx_r2w8", None), ("m32_ctx_w8", 2), ("m32_ctx_pp", None),
-                                           ("m32_ctx_pp", 3), ("m32_ctx_iw", None), ("m32_ctx_iw", 3)])
+                                           ("m32_ctx_pp", 3), ("m32_ctx_iw", None), ("m32_ctx_iw", 3),
+                                           ("m32_ctx_w8t128", None), ("m32_ctx_w8t128", 3)])
 def test_context_kernel_families_match_oracle(kernel, splits):
     prob = W.make_problem(name="ctx-fam", seed=9, batch=3, seq_lens=[70, 5, 333], q_lens=[64, 5, 130],
                           num_qo_heads=16, num_kv_heads=2, head_dim_qk=128, head_dim_v=128, page_size=16,
@@ -527,7 +528,7 @@ def test_context_kernel_families_match_oracle(kernel, splits):
     compare(prob, dp, label=f"{kernel}/{splits}")
 
 
-@pytest.mark.parametrize("kernel", ["m32_ctx_bf16", "m32_ctx_pp", "m32_ctx_iw", "m32_ctx_w8"])
+@pytest.mark.parametrize("kernel", ["m32_ctx_bf16", "m32_ctx_pp", "m32_ctx_iw", "m32_ctx_w8", "m32_ctx_w8t128"])
 def test_context_full_size_m32(kernel):
     prob = W.context_b4_q511_kv2047()
     say(f"case {prob.name} kernel={kernel}")
