@@ -84,6 +84,18 @@ def test_balanced_schedule_one_long_request():
     compare(prob, dp)
 
 
+@pytest.mark.parametrize("kv", [W.BF16, W.E4M3])
+def test_decode_one_128k_token_request(kv):
+    # the longest context here: one request of 131,072 keys (537 MB of bf16 K/V in 8 KV heads),
+    # spread by the balanced schedule over every workgroup: ~128 partial slots per row
+    prob = _gqa([131072], hq=32 if kv == W.BF16 else 64, hkv=8, P=32 if kv == W.BF16 else 64, kv=kv, poison=False)
+    say(f"case decode one 128k-token request kv={kv}")
+    dp = run_gpu(prob)
+    info = pkv.pkv_plan(dp.args)
+    assert info.schedule == 1
+    compare(prob, dp, sample_pairs(prob, 16), label=f"128k {kv} kernel={pkv.KERNEL_NAMES[info.kernel]}")
+
+
 def test_balanced_schedule_fewer_pages_than_workgroups():
     prob = _gqa([1, 2, 40], hq=16, hkv=2, P=16, q_lens=[1, 1, 1])
     dp = run_gpu(prob, num_splits=-1)
