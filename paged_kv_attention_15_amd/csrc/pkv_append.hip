@@ -54,10 +54,10 @@ __device__ __forceinline__ uint8_t f32_to_e4m3_sat(float x) {
   return (uint8_t)(w & 0xFF);
 }
 
-// Validated geometry of request b, or false (nothing of it is written).
-__device__ __forceinline__ bool append_request(const AppendParams& p, int b, int* lo, int* hi, int* L) {
-  const int a0 = p.q_indptr[b], a1 = p.q_indptr[b + 1];
-  const int len = p.seq_lens[b];
+// Validated geometry of a request given its q_indptr pair and length, or
+// false (nothing of it is written).
+__device__ __forceinline__ bool request_fits(const AppendParams& p, int a0, int a1, int len, int* lo, int* hi,
+                                             int* L) {
   if (a0 < 0 || a1 < a0 || a1 > p.T) {
     flag_error(p.err_word, PKV_DEVERR_QINDPTR);
     return false;
@@ -84,6 +84,10 @@ __device__ __forceinline__ bool append_request(const AppendParams& p, int b, int
   return true;
 }
 
+__device__ __forceinline__ bool append_request(const AppendParams& p, int b, int* lo, int* hi, int* L) {
+  return request_fits(p, p.q_indptr[b], p.q_indptr[b + 1], p.seq_lens[b], lo, hi, L);
+}
+
 __device__ __forceinline__ bool page_ok(const AppendParams& p, int pg) {
   if (p.num_pages > 0 && (pg < 0 || pg >= p.num_pages)) {
     flag_error(p.err_word, PKV_DEVERR_PAGE_RANGE);
@@ -100,17 +104,33 @@ __global__ __launch_bounds__(256) void append_kernel(const AppendParams p) {
   if (wid < n_rows) {
     const int r = (int)(wid / H);
     const int hh = (int)(wid % H);
-    int lo_b = 0, hi_b = p.B - 1;  // the last request whose rows start at or before r
-    while (lo_b < hi_b) {
-      const int mid = (lo_b + hi_b + 1) >> 1;
-      if (p.q_indptr[mid] <= r) lo_b = mid; else hi_b = mid - 1;
-    }
-    int lo, hi, L;
-    if (!append_request(p, lo_b, &lo, &hi, &L)) return;
-    if (r < lo || r >= hi) return;  // a row no well-formed request owns
-    const int pos = r + L - hi;
+    // the row's own channels first: they do not depend on which request owns it
     const uint16_t* src = p.qkv + (int64_t)r * p.qkv_st + hh * 128;
     float x0 = bf16_to_f32(src[lane]), x1 = bf16_to_f32(src[lane + 64]);
+    int lo_b;  // the last request whose rows start at or before r
+    int lo, hi, L;
+    if (p.B < 64) {
+      // one pass over the whole (q_indptr, seq_lens) table: lane k holds entry k,
+      // the owner is the number of requests b >= 1 starting at or before r (the
+      // table is monotone in every well-formed call; request_fits catches the
+      // rest), and its entries come from lanes b and b + 1 -- one memory round
+      // trip instead of a chain of dependent loads
+      const int qi = lane <= p.B ? p.q_indptr[lane] : 0;
+      const int sl = lane < p.B ? p.seq_lens[lane] : 0;
+      lo_b = __popcll(__builtin_amdgcn_ballot_w64(lane >= 1 && lane < p.B && qi <= r));
+      const int a0 = __shfl(qi, lo_b, 64), a1 = __shfl(qi, lo_b + 1, 64), len = __shfl(sl, lo_b, 64);
+      if (!request_fits(p, a0, a1, len, &lo, &hi, &L)) return;
+    } else {
+      int lo_s = 0, hi_s = p.B - 1;
+      while (lo_s < hi_s) {
+        const int mid = (lo_s + hi_s + 1) >> 1;
+        if (p.q_indptr[mid] <= r) lo_s = mid; else hi_s = mid - 1;
+      }
+      lo_b = lo_s;
+      if (!append_request(p, lo_b, &lo, &hi, &L)) return;
+    }
+    if (r < lo || r >= hi) return;  // a row no well-formed request owns
+    const int pos = r + L - hi;
     const bool is_q = hh < p.Hq, is_k = !is_q && hh < p.Hq + p.Hkv;
     if (is_q || is_k) {
       const uint16_t* wv = is_q ? p.q_w : p.k_w;
