@@ -290,7 +290,7 @@ def cpu_baseline(prob, max_pairs: int):
                       f"same workload, single-threaded fp64 C oracle, {dt:.1f} s"}
 
 
-def secondary_results(steps: int, warmup: int, single_call: bool = True, clock_source=None):
+def secondary_results(steps: int, warmup: int, single_call: bool = True, clock_source=None, only=None):
     import torch
 
     from paged_kv_attention_15_amd import pkv, workloads as W
@@ -304,6 +304,8 @@ def secondary_results(steps: int, warmup: int, single_call: bool = True, clock_s
         ("ctx-b4-q257-kv1024-p1024-sepkv", lambda: W.context_b4_q257_kv1024_p1024(separate=True), "mfma"),
     ]
     for name, make, bound in cases:
+        if only and name != only:
+            continue
         prob = make()
         dp, info, wall, ev_mean = measure(prob, steps, warmup)
         with ClockSampler(clock_source) as sampler:
@@ -376,6 +378,8 @@ def main():
     ap.add_argument("--no-single-call", action="store_true",
                     help="skip the warm/cold single-call samples (profiling runs: only the timed calls)")
     ap.add_argument("--cpu-pairs", type=int, default=1024)
+    ap.add_argument("--only", default=None,
+                    help="run only this secondary workload after the headline (profiling runs)")
     ap.add_argument("--settle", type=float, default=CLOCK_SETTLE_S,
                     help="seconds of untimed calls before each workload's warm-up (0: none, as in profiling runs)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -468,11 +472,13 @@ def main():
         torch.cuda.empty_cache()
     if not args.no_secondary:
         line["secondary"] = secondary_results(max(20, args.steps // 4), max(5, args.warmup // 2),
-                                              not args.no_single_call, clocks.get("sclk_source"))
-        line["secondary"]["append-h64x8-b32-decode"] = append_result(max(20, args.steps // 4),
-                                                                     max(5, args.warmup // 2))
-        line["secondary"]["append-h64x8-b32-decode-e4m3-dynq"] = append_result(
-            max(20, args.steps // 4), max(5, args.warmup // 2), fp8=True)
+                                              not args.no_single_call, clocks.get("sclk_source"), args.only)
+        if not args.only or args.only == "append-h64x8-b32-decode":
+            line["secondary"]["append-h64x8-b32-decode"] = append_result(max(20, args.steps // 4),
+                                                                         max(5, args.warmup // 2))
+        if not args.only or args.only == "append-h64x8-b32-decode-e4m3-dynq":
+            line["secondary"]["append-h64x8-b32-decode-e4m3-dynq"] = append_result(
+                max(20, args.steps // 4), max(5, args.warmup // 2), fp8=True)
     print(json.dumps(line), flush=True)
 
 
