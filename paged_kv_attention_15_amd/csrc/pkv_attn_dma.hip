@@ -294,7 +294,17 @@ __device__ __forceinline__ void dma_block(const KParams& p, unsigned char* smem,
     // (1-2 instructions each) beats keeping ~100 hoisted copies live across the
     // loop, so the lane index is made opaque to loop-invariant code motion here.
     int l16 = l16_in, G4 = G4_in;
-    if constexpr (C::LEAN) asm volatile("" : "+v"(l16), "+v"(G4));
+    if constexpr (C::LEAN) {
+      asm volatile("" : "+v"(l16), "+v"(G4));
+      // re-state the ranges the barrier hid (one AND each): with them the
+      // swizzle-group mask of every chunk index folds to a constant
+      if constexpr (C::FP8) {
+        G4 &= 3;
+      } else {
+        l16 &= 15;
+        G4 &= 3;
+      }
+    }
 
     // ---- S^T = K Q^T, K rows permuted inside every 32-key chunk
     f32x4 acc[C::RT][C::NNB];
