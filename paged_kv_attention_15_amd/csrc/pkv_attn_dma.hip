@@ -75,6 +75,11 @@ struct DmaCfg {
 // rows 16 distinct keys.  Separate V buffers are read as runs of consecutive
 // rows by the transpose reads: key r & 15.
 __device__ __forceinline__ int key_k(int r) { return (r & 3) | ((r >> 1) & 12); }
+
+// Largest rise of a row's running max (log2 units) absorbed without rescaling
+// O: below it the stale max keeps every weight under 2^kRingLazyMax, and since
+// the row sum and O share that reference the result is the same up to rounding.
+constexpr float kRingLazyMax = 8.f;
 __device__ __forceinline__ int key_v(int r) { return r & 15; }
 
 template <int NC>
@@ -358,9 +363,10 @@ __device__ __forceinline__ void dma_block(const KParams& p, unsigned char* smem,
         }
       mx = xor_max(mx, 16);
       mx = xor_max(mx, 32);
-      const float m_new = fmaxf(m_run[rt], mx);
+      const bool move = mx > m_run[rt] + kRingLazyMax;  // also true on a row's first visible key
+      const float m_new = move ? mx : m_run[rt];
       const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run[rt] - m_use);
+      const float alpha = move ? fast_exp2(m_run[rt] - m_use) : 1.f;
       float ps = 0.f;
 #pragma unroll
       for (int nb = 0; nb < C::NNB; ++nb)
@@ -372,7 +378,7 @@ __device__ __forceinline__ void dma_block(const KParams& p, unsigned char* smem,
       l_run[rt] = l_run[rt] * alpha + ps;
       m_run[rt] = m_new;
       // alpha is exactly 1 wherever the running max did not move: rescale only if some lane's did
-      if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
+      if (__builtin_amdgcn_ballot_w64(move) != 0) {
 #pragma unroll
         for (int d = 0; d < C::NDB; ++d) O[rt][d] *= alpha;
       }
