@@ -68,6 +68,9 @@ struct DmaCfg {
   // recomputed every tile instead of being kept live (cheap VALU vs. spills)
   static constexpr bool LEAN = DQK > 256;
   static_assert(!VSHARE || DV <= DQK, "shared V rows");
+  // bf16 operand reads split the swizzle per step group (phys_chunk_split): K rows
+  // hold exactly the chunks the S^T loop walks, V rows at least those of the PV loop
+  static_assert(FP8 || (NCK == 4 * NKS && NCV >= 2 * NDB), "operand chunk walk");
 };
 
 // Swizzle keys.  K rows are read 16 at a time in the permuted order
@@ -85,6 +88,18 @@ __device__ __forceinline__ int key_v(int r) { return r & 15; }
 template <int NC>
 __device__ __forceinline__ int phys_chunk(int c, int key) {
   return c ^ (key & swz_mask<NC>(c));
+}
+
+// The same chunk for c = base + sub, base a multiple of STEP (4 or 2), sub < STEP
+// and base + STEP - 1 < NC.  Then the group mask m of c is that of base and is
+// at least STEP - 1, so the XOR only touches the low bits of base:
+//   c ^ (key & m) = (base & ~m) + ((base & m) ^ ((sub ^ key) & m)).
+// With base an unrolled constant the first term is an immediate, and the
+// second takes only a few values per lane (shared between loop steps).
+template <int NC, int STEP>
+__device__ __forceinline__ int phys_chunk_split(int base, int sub, int key) {
+  const int m = swz_mask<NC>(base);
+  return (base & ~m) + ((base & m) ^ ((sub ^ key) & m));
 }
 
 // Device-coherent word access (agent scope, relaxed): the value goes to or
@@ -333,8 +348,8 @@ __device__ __forceinline__ void dma_block(const KParams& p, unsigned char* smem,
           const u32x2 w = *(const u32x2*)(kst + r * C::KROWB + phys_chunk<C::NCK>(ch, key_k(r)) * 16 + (cb & 15));
           a = e4m3x8_to_bf16x8(w);
         } else {
-          const int ch = 4 * ks + G4;
-          a = *(const bf16x8*)(kst + r * C::KROWB + phys_chunk<C::NCK>(ch, key_k(r)) * 16);
+          // chunk 4 ks + G4 (a row holds 4 NKS chunks)
+          a = *(const bf16x8*)(kst + r * C::KROWB + phys_chunk_split<C::NCK, 4>(4 * ks, G4, key_k(r)) * 16);
         }
 #pragma unroll
         for (int rt = 0; rt < C::RT; ++rt) acc[rt][nb] = mfma16x16x32(a, qB[rt][ks], acc[rt][nb]);
@@ -411,12 +426,19 @@ __device__ __forceinline__ void dma_block(const KParams& p, unsigned char* smem,
           a = e4m3x8_to_bf16x8(w);
         } else {
           // source lane l16 -> key rows vbase_row + l16/4 (+4), channels 16*db + 4*(l16&3) .. +4
-          const int ch = 2 * db + ((l16 & 3) >> 1);
+          // chunk 2 db + (l16 % 4) / 2 (a row holds at least 2 NDB chunks)
+          const int hb = (l16 & 3) >> 1;
           const int half = (l16 & 1) * 8;
           const int r1 = vbase_row + (l16 >> 2);
           const int r2 = r1 + 4;
-          const s16x4 lo = lds_read_tr16(vst + r1 * C::VROWB + phys_chunk<C::NCV>(ch, vkey(r1)) * 16 + half);
-          const s16x4 hi = lds_read_tr16(vst + r2 * C::VROWB + phys_chunk<C::NCV>(ch, vkey(r2)) * 16 + half);
+          const unsigned char* p1 = vst + r1 * C::VROWB + phys_chunk_split<C::NCV, 2>(2 * db, hb, vkey(r1)) * 16 + half;
+          // vbase_row is a multiple of 8, so r1 has bit 2 clear and key_k(r2) == key_k(r1):
+          // with shared rows the second read is the first one 4 rows down
+          const unsigned char* p2 =
+              C::VSHARE ? p1 + 4 * C::VROWB
+                        : vst + r2 * C::VROWB + phys_chunk_split<C::NCV, 2>(2 * db, hb, vkey(r2)) * 16 + half;
+          const s16x4 lo = lds_read_tr16(p1);
+          const s16x4 hi = lds_read_tr16(p2);
           typedef short s16x8 __attribute__((ext_vector_type(8)));
           const s16x8 a8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
           a = __builtin_bit_cast(bf16x8, a8);
