@@ -228,14 +228,15 @@ __device__ __forceinline__ void dma_block(const KParams& p, unsigned char* smem,
 #pragma unroll
     for (int q = 0; q < C::KPW; ++q) {
       const int I = min(wave * C::KPW + q, C::NI - 1);
-      const int P = I * 64 + ln;
+      // non-negative: unsigned division by the (not power-of-two) chunk count
+      const uint32_t P = (uint32_t)I * 64u + (uint32_t)ln;
       if (I * 64 < C::KCH) {
-        const int r = P / C::NCK, ph = P % C::NCK;
+        const int r = (int)(P / C::NCK), ph = (int)(P % C::NCK);
         q_row[q] = r;
         q_chunk[q] = (uint32_t)((ph ^ (key_k(r) & swz_mask<C::NCK>(ph))) * 16);
       } else {
-        const int Pv = P - C::KCH;
-        const int r = Pv / C::NCV, ph = Pv % C::NCV;
+        const uint32_t Pv = P - C::KCH;
+        const int r = (int)(Pv / C::NCV), ph = (int)(Pv % C::NCV);
         q_row[q] = r;
         q_chunk[q] = (uint32_t)((ph ^ (key_v(r) & swz_mask<C::NCV>(ph))) * 16);
       }
@@ -254,6 +255,7 @@ __device__ __forceinline__ void dma_block(const KParams& p, unsigned char* smem,
     if constexpr (C::LEAN) {
       int ln = lane;
       asm volatile("" : "+v"(ln));
+      ln &= 63;  // the lane range, hidden by the asm statement
       geometry(ln, q_row_l, q_chunk_l);
     } else {
       q_row = g_row;
