@@ -815,7 +815,9 @@ using DGqaFp8N1 = DmaCfg<128, 128, true, false, 1, 1, 1, 32, 3>;
 using DGqaFp8N2S3 = DmaCfg<128, 128, true, false, 1, 1, 2, 32, 3>;
 using DWideBf16 = DmaCfg<128, 128, false, false, 2, 4, 1, 64, 4>;
 using DWideFp8 = DmaCfg<128, 128, true, false, 2, 4, 1, 64, 4>;
-using DMlaBf16 = DmaCfg<576, 512, false, true, 1, 8, 1, 32, 4>;
+// MLA: two 72 KiB stages of 64 keys (one workgroup barrier per 64 keys) fit 252
+// VGPRs once the operand addresses are cheap; they beat four 32-key stages
+using DMlaBf16 = DmaCfg<576, 512, false, true, 1, 8, 1, 64, 2>;
 using DMlaFp8 = DmaCfg<576, 512, true, true, 1, 8, 1, 64, 4>;
 
 template <class C>
