@@ -30,12 +30,18 @@
  *   Host-checkable argument problems return PKV_ERR_INVALID_ARG before anything
  *   is enqueued.  Shapes or dtypes with no kernel return PKV_ERR_UNSUPPORTED
  *   (fail closed).  Device values are never trusted for addressing: a request
- *   uses L = min(seq_lens[b], max_pages_per_seq * page_size) keys, and page
- *   indices are clamped to [0, num_pages) when num_pages > 0.  A request with
- *   seq_lens[b] < its query rows, seq_lens[b] > max_pages_per_seq * page_size,
- *   or a referenced table entry outside [0, num_pages) sets the optional device
- *   error word (bit flags PKV_DEVERR_*); rows with no visible key produce zeros
- *   and lse = -inf.
+ *   uses L = min(seq_lens[b], span) keys, where span is the table capacity
+ *   max_pages_per_seq * page_size or, for a Split-KV plan sized from max_kv_len
+ *   (num_splits partitions of pages_per_split pages, pkv_plan_info), the
+ *   num_splits * pages_per_split * page_size keys those partitions cover when
+ *   that is smaller; page indices are clamped to [0, num_pages) when
+ *   num_pages > 0.  A request with seq_lens[b] < its query rows, seq_lens[b] >
+ *   max_pages_per_seq * page_size, seq_lens[b] > max_kv_len, or a referenced
+ *   table entry outside [0, num_pages) sets the optional device error word
+ *   (bit flags PKV_DEVERR_*) -- the PR #4557 page's review insists that the
+ *   lengths a plan was made for stay tied to the call, so a stale host bound
+ *   is reported rather than silently truncating; rows with no visible key
+ *   produce zeros and lse = -inf.
  */
 #ifndef PKV_H
 #define PKV_H
@@ -75,6 +81,8 @@ typedef enum pkv_layout {
 #define PKV_DEVERR_QINDPTR 0x8        /* q_indptr not monotone, or rows exceed max_q_len / total_q */
 #define PKV_DEVERR_POS_RANGE 0x10     /* pkv_append: a row's position is past the rotary table */
 #define PKV_DEVERR_QSCALE_ROWS 0x20   /* pkv_append: a request has more new rows than q_scale_stride */
+#define PKV_DEVERR_SEQ_GT_MAXLEN 0x40 /* seq_lens[b] > max_kv_len, the host bound the plan was sized from:
+                                         keys past the planned span are not read (clamped) */
 
 /*
  * Arguments of one attention call.  Strides are in ELEMENTS of the tensor's
@@ -110,7 +118,9 @@ typedef struct pkv_args {
   int32_t head_dim_v;        /* D_v, multiple of 8, <= head_dim_qk when v_shares_k */
   int32_t page_size;         /* P >= 1 */
   int32_t max_pages_per_seq; /* readable width of each block-table row */
-  int32_t max_kv_len;        /* host upper bound on seq_lens (sizes the Split-KV plan) */
+  int32_t max_kv_len;        /* host upper bound on seq_lens (sizes the Split-KV plan); a device
+                                length above it is flagged (PKV_DEVERR_SEQ_GT_MAXLEN) and cut
+                                to the planned span */
   int32_t max_q_len;         /* context: host upper bound on rows per request */
   int32_t total_q;           /* context: rows of q / out (= q_indptr[B]); decode: ignored */
   int32_t num_pages;         /* pool size in pages for clamping, 0 = unchecked */

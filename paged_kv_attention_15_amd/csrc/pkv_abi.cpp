@@ -86,6 +86,8 @@ pkv_status validate(const pkv_args* a, bool is_context) {
   if ((int64_t)a->max_kv_len > (int64_t)a->max_pages_per_seq * a->page_size)
     return fail(PKV_ERR_INVALID_ARG, "max_kv_len %d exceeds the table capacity %lld", a->max_kv_len,
                 (long long)a->max_pages_per_seq * a->page_size);
+  if ((int64_t)a->max_pages_per_seq * a->page_size > INT32_MAX)
+    return fail(PKV_ERR_INVALID_ARG, "max_pages_per_seq * page_size exceeds 2^31 - 1 keys");
   if (a->num_pages < 0) return fail(PKV_ERR_INVALID_ARG, "num_pages must be >= 0");
   if (a->q_dtype != PKV_DTYPE_F32 && a->q_dtype != PKV_DTYPE_BF16)
     return fail(PKV_ERR_UNSUPPORTED, "q_dtype %d not supported (F32 or BF16)", a->q_dtype);
@@ -506,6 +508,14 @@ pkv_status run(const pkv_args* a, bool is_context, void* ws, size_t ws_bytes, vo
   p.sinks = a->sinks;
   p.v_table = a->v_block_tables;
   p.page_list_cap = plan.pages_per_split;
+  p.max_kv_len = a->max_kv_len;
+  {
+    // a split plan streams S partitions of pages_per_split pages; keys past
+    // them are never read, so a longer request is cut there (and flagged)
+    const int64_t cap = (int64_t)a->max_pages_per_seq * a->page_size;
+    const int64_t span = plan.schedule == 1 ? cap : (int64_t)plan.num_splits * plan.pages_per_split * a->page_size;
+    p.kv_span = (int32_t)std::min<int64_t>(cap, span);
+  }
   if (plan.schedule == 1) {
     p.stream = 1;
     p.seg_cost = seg_cost_pages(a);
@@ -553,7 +563,8 @@ pkv_status run(const pkv_args* a, bool is_context, void* ws, size_t ws_bytes, vo
     mp.causal = p.causal;
     mp.is_context = p.is_context;
     mp.split_tokens = plan.pages_per_split * a->page_size;
-    mp.cap_tokens = a->max_pages_per_seq * a->page_size;
+    mp.cap_tokens = p.kv_span;
+    mp.max_kv_len = a->max_kv_len;
     mp.max_q_len = p.max_q_len;
     mp.total_q = p.total_q;
     mp.err_word = a->err_word;

@@ -148,9 +148,10 @@ __device__ __forceinline__ void dma_block(const KParams& p, unsigned char* smem,
   const int cap = p.max_pages_per_seq * p.page_size;
   if (lead && g == 0 && rb == 0 && tid == 0) {
     if (L > cap) flag_error(p.err_word, PKV_DEVERR_SEQ_GT_TABLE);
+    if (L > p.max_kv_len) flag_error(p.err_word, PKV_DEVERR_SEQ_GT_MAXLEN);
     if (L < n_b) flag_error(p.err_word, PKV_DEVERR_SEQ_LT_QLEN);
   }
-  L = max(0, min(L, cap));
+  L = max(0, min(L, p.kv_span));
 
   const int last_row = min(row0 + C::ROWS, row_space) - 1;
   const int i_max = last_row / G;
@@ -723,7 +724,7 @@ __global__ __launch_bounds__(C::NTHR) void attn_dma_stream_kernel(const KParams 
       const int bb = c0 + lane;
       int v = 0;
       if (bb < B) {
-        const int L = max(0, min(p.seq_lens[bb], cap));
+        const int L = max(0, min(p.seq_lens[bb], p.kv_span));
         v = (L + p.page_size - 1) >> p.log2_page;
       }
 #pragma unroll
@@ -755,6 +756,7 @@ __global__ __launch_bounds__(C::NTHR) void attn_dma_stream_kernel(const KParams 
       if (tid == 0) {
         const int L0 = p.seq_lens[bb];
         if (L0 > cap) flag_error(p.err_word, PKV_DEVERR_SEQ_GT_TABLE);
+        if (L0 > p.max_kv_len) flag_error(p.err_word, PKV_DEVERR_SEQ_GT_MAXLEN);
         if (L0 < p.q_len) flag_error(p.err_word, PKV_DEVERR_SEQ_LT_QLEN);
       }
       const int nrow = p.q_len * p.num_qo_heads;

@@ -67,9 +67,10 @@ __global__ __launch_bounds__(64) void attn_generic_kernel(const KParams p) {
   const int cap = p.max_pages_per_seq * p.page_size;
   if (split == 0 && h == 0 && i == 0 && lane == 0) {
     if (L > cap) flag_error(p.err_word, PKV_DEVERR_SEQ_GT_TABLE);
+    if (L > p.max_kv_len) flag_error(p.err_word, PKV_DEVERR_SEQ_GT_MAXLEN);
     if (L < n_b) flag_error(p.err_word, PKV_DEVERR_SEQ_LT_QLEN);
   }
-  L = max(0, min(L, cap));
+  L = max(0, min(L, p.kv_span));
   const int c = p.causal ? min(L, max(0, L - n_b + i + 1)) : L;
   const int kv_lo = split * p.pages_per_split * p.page_size;
   const int kv_hi = min(kv_lo + p.pages_per_split * p.page_size, c);
@@ -345,6 +346,7 @@ __global__ __launch_bounds__(kMergeThreads) void lse_merge_kernel(const MergePar
     if (i == 0 && h == 0 && tl == 0) {
       const int L0 = mp.seq_lens[b];
       if (L0 > mp.cap_tokens) flag_error(mp.err_word, PKV_DEVERR_SEQ_GT_TABLE);
+      if (L0 > mp.max_kv_len) flag_error(mp.err_word, PKV_DEVERR_SEQ_GT_MAXLEN);
       if (L0 < mp.q_len) flag_error(mp.err_word, PKV_DEVERR_SEQ_LT_QLEN);
     }
     StreamGeom sg;

@@ -204,9 +204,10 @@ __device__ __forceinline__ void m32_block(const KParams& p, unsigned char* smem,
   const int cap = p.max_pages_per_seq * p.page_size;
   if (lead && g == 0 && rblk == 0 && tid == 0) {
     if (L > cap) flag_error(p.err_word, PKV_DEVERR_SEQ_GT_TABLE);
+    if (L > p.max_kv_len) flag_error(p.err_word, PKV_DEVERR_SEQ_GT_MAXLEN);
     if (L < n_b) flag_error(p.err_word, PKV_DEVERR_SEQ_LT_QLEN);
   }
-  L = max(0, min(L, cap));
+  L = max(0, min(L, p.kv_span));
 
   const int last_row = min(row0 + C::ROWS, row_space) - 1;
   const int i_max = last_row / G;

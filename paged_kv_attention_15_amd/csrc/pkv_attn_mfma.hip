@@ -132,9 +132,10 @@ __device__ __forceinline__ void attend_block(const KParams& p, unsigned char* sm
   const int cap = p.max_pages_per_seq * p.page_size;
   if (lead && g == 0 && rb == 0 && tid == 0) {
     if (L > cap) flag_error(p.err_word, PKV_DEVERR_SEQ_GT_TABLE);
+    if (L > p.max_kv_len) flag_error(p.err_word, PKV_DEVERR_SEQ_GT_MAXLEN);
     if (L < n_b) flag_error(p.err_word, PKV_DEVERR_SEQ_LT_QLEN);
   }
-  L = max(0, min(L, cap));
+  L = max(0, min(L, p.kv_span));
 
   // keys this workgroup may need: its partition, cut at the last key any of its rows sees
   const int last_row = min(row0 + C::ROWS, row_space) - 1;
@@ -517,7 +518,6 @@ __global__ __launch_bounds__(C::NTHR) void attn_mfma_stream_kernel(const KParams
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int B = p.batch;
-  const int cap = p.max_pages_per_seq * p.page_size;
   if (tid < 64) {
     int carry = 0;
     if (lane == 0) s_pfx[0] = 0;
@@ -525,7 +525,7 @@ __global__ __launch_bounds__(C::NTHR) void attn_mfma_stream_kernel(const KParams
       const int bb = c0 + lane;
       int v = 0;
       if (bb < B) {
-        const int L = max(0, min(p.seq_lens[bb], cap));
+        const int L = max(0, min(p.seq_lens[bb], p.kv_span));
         v = (L + p.page_size - 1) >> p.log2_page;
       }
 #pragma unroll

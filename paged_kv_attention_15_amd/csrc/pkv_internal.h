@@ -82,6 +82,11 @@ struct KParams {
   // per-request page prefix written to ws_pfx for the reducer
   int32_t stream, num_wg, slot_rows, page_list_cap;
   int32_t seg_cost, pad2;  // placeholder pages charged per segment start
+  // keys a request may use: seq_lens[b] is clamped to kv_span, the table
+  // capacity or, for a plan of S partitions of pages_per_split pages each,
+  // S * pages_per_split * page_size when that is smaller; a length above the
+  // host bound max_kv_len sets PKV_DEVERR_SEQ_GT_MAXLEN
+  int32_t kv_span, max_kv_len;
   int32_t* ws_pfx;
   // balanced schedule with the fused reducer: one zero-at-rest counter per
   // (request, KV head); null selects the separate reducer kernel
@@ -112,7 +117,8 @@ struct MergeParams {
   const int32_t* seq_lens;
   const int32_t* q_indptr;
   int32_t batch, q_len, causal, is_context;
-  int32_t split_tokens, cap_tokens, max_q_len, total_q;
+  int32_t split_tokens, cap_tokens, max_q_len, total_q;  // cap_tokens = KParams::kv_span
+  int32_t max_kv_len, pad_m;
   // balanced decode schedule: row (t, h) of KV head g reads slots w + b*Hkv + g
   int32_t stream, num_wg, num_kv_heads, group, slot_rows, page_size, seg_cost;
   const int32_t* pfx;

@@ -36,6 +36,7 @@ EXPORTED = ["pkv_abi_version", "pkv_last_error", "pkv_plan", "pkv_workspace_byte
             "pkv_context", "pkv_lse_merge", "pkv_append"]
 PKV_DEVERR_POS_RANGE = 0x10
 PKV_DEVERR_QSCALE_ROWS = 0x20
+PKV_DEVERR_SEQ_GT_MAXLEN = 0x40
 
 
 class PkvArgs(C.Structure):

@@ -76,6 +76,35 @@ def _np_storage(dtype: str):
 
 
 @dataclasses.dataclass
+class LogitProfile:
+    """Shapes the scaled logits of a drawn problem (inputs that move a row's
+    running maximum where a test wants it, or hold every logit equal or far
+    below zero).
+
+    Every KV head g gets a random unit direction u_g (its own generator, so the
+    main draws are unchanged).  Every query row of a head of group g is shifted
+    by q_shift * u_g.  A key listed in `levels` as (request b, first key j0,
+    end key j1, rise) has its K row replaced by c * u_g in every KV head g,
+    with c = rise / (scale * q_shift): its logit against a query row of the
+    group is then rise * (1 + <z, u_g> / q_shift) in natural-log units, z the
+    row's own standard-normal part (about 5 % of spread per sigma for the
+    default shift), while the other keys' logits stay near N(0, 2).  `tail_rise`
+    does the same to the keys past each request's length in its last page
+    (they must stay invisible; V keeps its poison there).  `equal_keys` makes
+    every key row of a (request, KV head) one shared random vector, so all of
+    a row's logits are equal; `negative` (> 0) shifts Q by +a u_g and every K
+    row by -a u_g with a = sqrt(negative / scale), putting every logit near
+    -negative."""
+
+    q_shift: float = 20.0
+    levels: tuple = ()
+    tail_rise: Optional[float] = None
+    equal_keys: bool = False
+    negative: float = 0.0
+    seed: int = 7919
+
+
+@dataclasses.dataclass
 class Problem:
     """One paged attention call, held in host memory.
 
@@ -184,6 +213,7 @@ def make_problem(
     num_splits: int = 0,
     sinks: bool = False,
     separate_v_table: bool = False,
+    logits: Optional[LogitProfile] = None,
 ) -> Problem:
     """Draw one problem.  `seq_lens` / `q_lens` are int sequences of length B.
 
@@ -218,7 +248,30 @@ def make_problem(
         scale = 1.0 / math.sqrt(head_dim_qk)
 
     T_q = int(q_indptr[-1])
-    q = _store(rng.standard_normal((T_q, num_qo_heads, head_dim_qk), dtype=np.float32), q_dtype)
+    q32 = rng.standard_normal((T_q, num_qo_heads, head_dim_qk), dtype=np.float32)
+    G = num_qo_heads // Hkv
+    page_start = np.concatenate([[0], np.cumsum(pages_per_req)]).astype(np.int64)
+    if logits is not None:
+        prng = np.random.default_rng(logits.seed)
+        u = prng.standard_normal((Hkv, head_dim_qk))
+        u = (u / np.linalg.norm(u, axis=1, keepdims=True)).astype(np.float32)  # [Hkv, D]
+        a_q = math.sqrt(logits.negative / scale) if logits.negative > 0 else logits.q_shift
+        q32 += a_q * np.repeat(u, G, axis=0)[None, :, :]
+        k_equal = prng.standard_normal((Hkv, head_dim_qk)).astype(np.float32)
+        # (logical page, token, rise) of every planted key
+        plants = []
+        for (b, j0, j1, rise) in logits.levels:
+            for j in range(int(j0), int(j1)):
+                if 0 <= j < int(seq_lens[b]):
+                    plants.append((int(page_start[b]) + j // P, j % P, float(rise)))
+        if logits.tail_rise is not None:
+            for b in range(batch):
+                L = int(seq_lens[b])
+                if L % P:
+                    lp = int(page_start[b]) + L // P
+                    plants += [(lp, t, float(logits.tail_rise)) for t in range(L % P, P)]
+    q = _store(q32, q_dtype)
+    del q32
 
     # logical page i of the concatenated requests lives at physical page perm[i]
     def draw_pool(dim: int, dtype_tag: str):
@@ -228,10 +281,20 @@ def make_problem(
         for start in range(0, needed, chunk):
             stop = min(needed, start + chunk)
             vals = rng.standard_normal((stop - start, Hkv, P, dim), dtype=np.float32)
+            if is_k and logits is not None:
+                if logits.equal_keys:
+                    vals[...] = k_equal[None, :, None, :]
+                if logits.negative > 0:
+                    vals -= math.sqrt(logits.negative / scale) * u[None, :, None, :]
+                for (lp, t, rise) in plants:
+                    if start <= lp < stop:
+                        vals[lp - start, :, t, :] = (rise / (scale * logits.q_shift)) * u
             pool[perm[start:stop]] = _store(vals, store_dtype)
         return pool
 
+    is_k = True
     k_pool = draw_pool(head_dim_qk, kv_dtype)
+    is_k = False
     v_pool = None if mla else draw_pool(head_dim_v, kv_dtype)
 
     k_scale = v_scale = 1.0
@@ -258,6 +321,8 @@ def make_problem(
                 continue
             for phys in perm[needed:]:
                 _nan_fill(pool[phys], kv_dtype)
+            if pool is k_pool and logits is not None and logits.tail_rise is not None:
+                continue  # the K tails hold the planted keys instead
             cursor = 0
             for b, npg in enumerate(pages_per_req):
                 L = int(seq_lens[b])

@@ -127,6 +127,29 @@ def paged_problem_from_dense(dense_k, dense_v, q, seq_lens, q_lens, page_size, *
     )
 
 
+def row_norm_report(got, ref, rtol, floor):
+    """Per row: ||got - ref||_2 <= rtol * ||ref||_2 + floor (rows of [n, D]).
+    Returns (ok, worst ratio ||got - ref|| / max(||ref||, tiny), n_bad rows)."""
+    got = np.asarray(got, dtype=np.float64).reshape(len(ref), -1)
+    ref = np.asarray(ref, dtype=np.float64).reshape(len(ref), -1)
+    dn = np.linalg.norm(got - ref, axis=1)
+    rn = np.linalg.norm(ref, axis=1)
+    bad = ~(dn <= rtol * rn + floor)
+    worst = float(np.nanmax(dn / np.maximum(rn, 1e-30))) if len(rn) else 0.0
+    return (not bad.any()), worst, int(bad.sum())
+
+
+def check_output(got, ref, atol, rtol, norm_rtol, norm_floor):
+    """The output comparison of the GPU parity tests: the pages' elementwise
+    bound AND the per-row relative 2-norm bound.  Returns (ok, report dict)."""
+    ok_e, max_abs, max_rel, nbad = allclose_report(got, ref, atol, rtol)
+    ok_n, worst, nbad_rows = row_norm_report(got, ref, norm_rtol, norm_floor)
+    finite = bool(np.isfinite(np.asarray(got, dtype=np.float64)).all())
+    rep = {"max_abs": max_abs, "max_rel": max_rel, "bad_elems": nbad, "max_row_norm_rel": worst,
+           "bad_rows": nbad_rows, "finite": finite}
+    return ok_e and ok_n and finite, rep
+
+
 def allclose_report(got, ref, atol, rtol):
     """Elementwise |got - ref| <= atol + rtol*|ref|; returns (ok, max_abs, max_rel, n_bad)."""
     got = np.asarray(got, dtype=np.float64)

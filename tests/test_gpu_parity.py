@@ -559,3 +559,42 @@ def test_context_fp8_kv_families_match_oracle():
         dp.run()
         torch.cuda.synchronize()
         compare(prob, dp, label=kernel)
+
+
+# ----------------------------------------------------------------- lengths above the host bound
+
+@pytest.mark.parametrize("kernel,splits,kv,ctx", [
+    ("gqa_bf16", 1, W.BF16, False), ("gqa_bf16", 3, W.BF16, False), ("dma_gqa_fp8_n2", 4, W.E4M3, False),
+    ("generic", 2, W.BF16, False), ("gqa_bf16", -1, W.BF16, False), ("dma_mla_bf16", None, W.BF16, False),
+    ("m32_ctx_w8t128", None, W.BF16, True), ("m32_ctx_w8t128", 2, W.BF16, True),
+])
+def test_seq_len_above_max_kv_len_is_flagged_and_cut_to_the_plan(kernel, splits, kv, ctx):
+    # the plan is sized from max_kv_len = 700 while the device says 1000: the
+    # request is cut to the keys the plan's partitions cover (the balanced
+    # schedule covers the whole table) and PKV_DEVERR_SEQ_GT_MAXLEN is set
+    mla = kernel == "dma_mla_bf16"
+    if ctx:
+        prob = W.make_problem(name="ctx-gt-maxlen", seed=14, batch=2, seq_lens=[300, 1000], q_lens=[40, 90],
+                              num_qo_heads=16, num_kv_heads=2, head_dim_qk=128, head_dim_v=128, page_size=32,
+                              is_decode=False, poison=True, extra_page_frac=0.3, table_slack_pages=12)
+    elif mla:
+        prob = W.make_problem(name="mla-gt-maxlen", seed=14, batch=2, seq_lens=[300, 1000], q_lens=[1, 1],
+                              num_qo_heads=128, num_kv_heads=1, head_dim_qk=576, head_dim_v=512, page_size=64,
+                              mla=True, scale=1 / 24.0, poison=True, extra_page_frac=0.3, table_slack_pages=6)
+    else:
+        P = 64 if kv == W.E4M3 else 32
+        prob = _gqa([300, 1000], hq=64 if kv == W.E4M3 else 32, hkv=8, P=P, kv=kv)
+        prob = dataclasses.replace(prob, block_tables=np.pad(prob.block_tables, ((0, 0), (0, 12)), mode="edge"))
+    short = dataclasses.replace(prob, seq_lens=np.array([300, 700], dtype=np.int32))
+    dp = pkv.upload(short, "cuda", num_splits=splits, kernel=kernel)
+    info = pkv.pkv_plan(dp.args, dp.is_context)
+    cap = prob.max_pages * prob.page_size
+    span = cap if info.schedule == 1 else min(cap, info.num_splits * info.pages_per_split * prob.page_size)
+    assert 700 <= span < 1000 or info.schedule == 1
+    dp.tensors["seq_lens"][1] = 1000
+    say(f"case seq_len 1000 > max_kv_len 700: {kernel} splits={info.num_splits} schedule={info.schedule} "
+        f"span={span}")
+    dp.run()
+    torch.cuda.synchronize()
+    cut = dataclasses.replace(prob, seq_lens=np.array([300, min(1000, span)], dtype=np.int32))
+    compare(cut, dp, label=f"gt-maxlen {kernel}/{splits}", expect_err=pkv.PKV_DEVERR_SEQ_GT_MAXLEN)
