@@ -9,7 +9,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libpkv.so")
 SOURCES = ["pkv_abi.cpp", "pkv_attn_generic.hip", "pkv_attn_mfma.hip", "pkv_attn_dma.hip", "pkv_attn_m32.hip",
-           "pkv_append.hip"]
+           "pkv_attn_mla.hip", "pkv_append.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

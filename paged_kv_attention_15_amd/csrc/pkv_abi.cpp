@@ -173,7 +173,8 @@ bool kernel_supports(int32_t k, const pkv_args* a, bool is_context) {
   // page list; the direct-to-LDS ring families do not
   if (a->v_block_tables && (k >= pkv::KERNEL_DMA_GQA_BF16 && k <= pkv::KERNEL_DMA_GQA_BF16_S2)) return false;
   if (a->v_block_tables && (k >= pkv::KERNEL_DMA_GQA_FP8_N2 && k <= pkv::KERNEL_DMA_GQA_FP8_N2S3)) return false;
-  if (a->v_block_tables && (k == pkv::KERNEL_M32_MLA_BF16 || k == pkv::KERNEL_MLA_BF16 || k == pkv::KERNEL_MLA_FP8))
+  if (a->v_block_tables && (k == pkv::KERNEL_M32_MLA_BF16 || k == pkv::KERNEL_MLA_BF16 || k == pkv::KERNEL_MLA_FP8 ||
+                            k == pkv::KERNEL_MLA32_BF16 || k == pkv::KERNEL_MLA32_SEQ_BF16))
     return false;
   const bool fp8 = a->kv_dtype == PKV_DTYPE_FP8_E4M3;
   const int G = a->num_qo_heads / a->num_kv_heads;
@@ -222,6 +223,9 @@ bool kernel_supports(int32_t k, const pkv_args* a, bool is_context) {
     case pkv::KERNEL_M32_CTX_W8T128:
       return d128 && !fp8 && a->page_size >= 4;
     case pkv::KERNEL_M32_MLA_BF16: return mla && !fp8 && a->page_size % 32 == 0;
+    // 32-key blocks inside one page: pages of a multiple of 32 tokens
+    case pkv::KERNEL_MLA32_BF16:
+    case pkv::KERNEL_MLA32_SEQ_BF16: return mla && !fp8 && a->page_size % 32 == 0;
   }
   return false;
 }
@@ -231,6 +235,13 @@ bool is_m32(int32_t k) {
   return (k >= pkv::KERNEL_M32_CTX_BF16 && k <= pkv::KERNEL_M32_CTX_PP) || k == pkv::KERNEL_M32_CTX_IW ||
          k == pkv::KERNEL_M32_CTX_W8T128;
 }
+
+// families that hold a partition's page list in registers (kM32MaxPages pages at most)
+bool page_list_in_registers(int32_t k) {
+  return is_m32(k) || k == pkv::KERNEL_MLA32_BF16 || k == pkv::KERNEL_MLA32_SEQ_BF16;
+}
+
+bool is_mla32(int32_t k) { return k == pkv::KERNEL_MLA32_BF16 || k == pkv::KERNEL_MLA32_SEQ_BF16; }
 
 bool is_gqa_family(int32_t k) {
   switch (k) {
@@ -257,7 +268,7 @@ bool is_gqa_family(int32_t k) {
 }
 
 bool kernel_shape(int32_t k, pkv::MfmaShape* s) {
-  return pkv::mfma_shape(k, s) || pkv::dma_shape(k, s) || pkv::m32_shape(k, s);
+  return pkv::mfma_shape(k, s) || pkv::dma_shape(k, s) || pkv::m32_shape(k, s) || pkv::mla32_shape(k, s);
 }
 
 // Balanced schedule: the fixed cost of starting a segment (page list and
@@ -301,8 +312,13 @@ int32_t choose_kernel(const pkv_args* a, bool is_context) {
     if (is_context && !fp8) return pkv::KERNEL_M32_CTX_W8T128;
     return fp8 ? pkv::KERNEL_DMA_WIDE_FP8 : pkv::KERNEL_DMA_WIDE_BF16;
   }
-  if (a->head_dim_qk == 576 && a->head_dim_v == 512 && a->v_shares_k)
+  // MLA: bf16 latents on the 32x32 kernel with 32 heads per wave when the
+  // pages hold whole 32-key blocks (B512 L4096: 686 us for one query row and
+  // 1,199 us for two, against 746 / 1,381 us for the 16-head ring kernel)
+  if (a->head_dim_qk == 576 && a->head_dim_v == 512 && a->v_shares_k) {
+    if (!fp8 && a->page_size % 32 == 0) return pkv::KERNEL_MLA32_BF16;
     return fp8 ? pkv::KERNEL_DMA_MLA_FP8 : pkv::KERNEL_DMA_MLA_BF16;
+  }
   return pkv::KERNEL_GENERIC;
 }
 
@@ -414,7 +430,7 @@ pkv_status make_plan(const pkv_args* a, bool is_context, int num_cus, pkv_plan_i
     // the partition's page list sits in LDS after the KV stages: keep the total within 160 KiB
     const int64_t lds_room = ((int64_t)(160 * 1024 - shp.lds_static) / 4 - 8) / (a->v_block_tables ? 2 : 1);
     int64_t cap_pages = std::min<int64_t>(kMaxPagesPerSplit, lds_room);
-    if (is_m32(kernel))
+    if (page_list_in_registers(kernel))
       cap_pages = std::min<int64_t>(cap_pages, pkv::kM32MaxPages);
     if (cap_pages < 1) return fail(PKV_ERR_UNSUPPORTED, "no LDS left for the page list");
     if (pps > cap_pages) pps = cap_pages;
@@ -539,6 +555,7 @@ pkv_status run(const pkv_args* a, bool is_context, void* ws, size_t ws_bytes, vo
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e = plan.kernel == pkv::KERNEL_GENERIC         ? pkv::launch_generic(p, s)
                  : is_m32(plan.kernel)                       ? pkv::launch_m32(plan.kernel, p, s)
+                 : is_mla32(plan.kernel)                     ? pkv::launch_mla32(plan.kernel, p, s)
                  : plan.kernel >= pkv::KERNEL_DMA_GQA_BF16   ? pkv::launch_dma(plan.kernel, p, s)
                                                              : pkv::launch_mfma(plan.kernel, p, s);
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "attention launch failed: %s", hipGetErrorString(e));

@@ -50,7 +50,10 @@ enum KernelId : int32_t {
   KERNEL_DMA_GQA_FP8_N2S3 = 34, // 2 token waves, 64-key tiles, 3 stages (48 KiB)
   KERNEL_M32_CTX_IW = 35,       // D = 128, 8 waves x 32 rows, S^T of the next block interleaved with the softmax
   KERNEL_M32_CTX_W8T128 = 36,   // D = 128, 8 waves x 32 rows, 2 x 64 KiB stages of 128 keys (half the barriers of W8)
-  KERNEL_COUNT = 37,
+  // MLA latent decode on 32x32x16 MFMA, 32 heads per wave, one wave per SIMD (pkv_attn_mla.hip)
+  KERNEL_MLA32_BF16 = 37,       // PV of block j-1 overlapped with the softmax of block j
+  KERNEL_MLA32_SEQ_BF16 = 38,   // one block at a time
+  KERNEL_COUNT = 39,
 };
 
 // Everything a kernel reads, by value.  Element strides as in pkv_args.
@@ -149,5 +152,7 @@ bool m32_shape(int32_t kernel, MfmaShape* out);
 // the 32x32 family keeps a partition's page list in registers: at most this many pages
 constexpr int kM32MaxPages = 128;
 hipError_t launch_m32(int32_t kernel, const KParams& p, hipStream_t s);
+bool mla32_shape(int32_t kernel, MfmaShape* out);
+hipError_t launch_mla32(int32_t kernel, const KParams& p, hipStream_t s);
 
 }  // namespace pkv

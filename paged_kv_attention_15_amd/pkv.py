@@ -28,7 +28,8 @@ KERNEL_NAMES = {0: "none", 1: "generic", 2: "gqa_bf16", 3: "gqa_fp8", 4: "wide_b
                 24: "m32_mla_bf16", 25: "m32_ctx_w8", 26: "m32_ctx_r1", 27: "m32_ctx_r1s3",
                 28: "m32_ctx_r2", 29: "m32_ctx_r2w8", 30: "m32_ctx_pp",
                 31: "dma_gqa_fp8_n2", 32: "dma_gqa_bf16_n2",
-                33: "dma_gqa_fp8_n1", 34: "dma_gqa_fp8_n2s3", 35: "m32_ctx_iw", 36: "m32_ctx_w8t128"}
+                33: "dma_gqa_fp8_n1", 34: "dma_gqa_fp8_n2s3", 35: "m32_ctx_iw", 36: "m32_ctx_w8t128",
+                37: "mla32_bf16", 38: "mla32_seq_bf16"}
 KERNEL_IDS = {v: k for k, v in KERNEL_NAMES.items()}
 
 DTYPE_CODES = {"f32": PKV_DTYPE_F32, "bf16": PKV_DTYPE_BF16, "e4m3": PKV_DTYPE_FP8_E4M3}

@@ -161,7 +161,9 @@ def test_fused_merge_full_size_fp8():
 
 
 @pytest.mark.parametrize("q_len,kernel", [(1, None), (2, None), (1, "dma_mla_bf16"), (2, "dma_mla_bf16"),
-                                          (1, "mla_bf16"), (1, "m32_mla_bf16"), (2, "m32_mla_bf16")])
+                                          (1, "mla_bf16"), (1, "m32_mla_bf16"), (2, "m32_mla_bf16"),
+                                          (1, "mla32_bf16"), (2, "mla32_bf16"), (1, "mla32_seq_bf16"),
+                                          (2, "mla32_seq_bf16"), (3, "mla32_bf16")])
 def test_mla_small(q_len, kernel):
     prob = W.make_problem(name=f"mla-small-q{q_len}", seed=3, batch=3, seq_lens=[2, 70, 300],
                           q_lens=[q_len] * 3, num_qo_heads=128, num_kv_heads=1, head_dim_qk=576,
@@ -171,7 +173,8 @@ def test_mla_small(q_len, kernel):
     dp = pkv.upload(prob, "cuda", kernel=kernel)
     dp.run()
     torch.cuda.synchronize()
-    compare(prob, dp)
+    # with three draft rows the 2-key request has a row that sees no key (flagged)
+    compare(prob, dp, expect_err=pkv.PKV_DEVERR_SEQ_LT_QLEN if q_len > 2 else 0)
 
 
 def test_mla_fp8_latent_small():
@@ -183,6 +186,29 @@ def test_mla_fp8_latent_small():
         dp.run()
         torch.cuda.synchronize()
         compare(prob, dp, label=kernel)
+
+
+@pytest.mark.parametrize("q_len,kernel", [(1, "mla32_bf16"), (2, "mla32_bf16"), (1, "mla32_seq_bf16")])
+def test_mla_full_size_mla32(q_len, kernel):
+    prob = W.mla_b512_kv4096(q_len=q_len)
+    say(f"case {prob.name} kernel={kernel}")
+    dp = pkv.upload(prob, "cuda", kernel=kernel)
+    dp.run()
+    torch.cuda.synchronize()
+    compare(prob, dp, pairs=sample_pairs(prob, 256), label=kernel)
+
+
+@pytest.mark.parametrize("kernel,splits", [("mla32_bf16", 3), ("mla32_bf16", 7), ("mla32_seq_bf16", 2)])
+def test_mla32_split_partitions(kernel, splits):
+    prob = W.make_problem(name="mla32-split", seed=15, batch=3, seq_lens=[1000, 64, 2050], q_lens=[2] * 3,
+                          num_qo_heads=128, num_kv_heads=1, head_dim_qk=576, head_dim_v=512, page_size=64,
+                          mla=True, scale=1 / 24.0, poison=True, extra_page_frac=0.3, table_slack_pages=1,
+                          sinks=True)
+    say(f"case mla32 split {kernel} {splits}")
+    dp = pkv.upload(prob, "cuda", kernel=kernel, num_splits=splits)
+    dp.run()
+    torch.cuda.synchronize()
+    compare(prob, dp, label=f"{kernel}/{splits}")
 
 
 @pytest.mark.parametrize("q_len", [1, 2])
@@ -566,13 +592,14 @@ def test_context_fp8_kv_families_match_oracle():
 @pytest.mark.parametrize("kernel,splits,kv,ctx", [
     ("gqa_bf16", 1, W.BF16, False), ("gqa_bf16", 3, W.BF16, False), ("dma_gqa_fp8_n2", 4, W.E4M3, False),
     ("generic", 2, W.BF16, False), ("gqa_bf16", -1, W.BF16, False), ("dma_mla_bf16", None, W.BF16, False),
+    ("mla32_bf16", None, W.BF16, False),
     ("m32_ctx_w8t128", None, W.BF16, True), ("m32_ctx_w8t128", 2, W.BF16, True),
 ])
 def test_seq_len_above_max_kv_len_is_flagged_and_cut_to_the_plan(kernel, splits, kv, ctx):
     # the plan is sized from max_kv_len = 700 while the device says 1000: the
     # request is cut to the keys the plan's partitions cover (the balanced
     # schedule covers the whole table) and PKV_DEVERR_SEQ_GT_MAXLEN is set
-    mla = kernel == "dma_mla_bf16"
+    mla = kernel in ("dma_mla_bf16", "mla32_bf16")
     if ctx:
         prob = W.make_problem(name="ctx-gt-maxlen", seed=14, batch=2, seq_lens=[300, 1000], q_lens=[40, 90],
                               num_qo_heads=16, num_kv_heads=2, head_dim_qk=128, head_dim_v=128, page_size=32,
