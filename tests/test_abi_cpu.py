@@ -98,7 +98,12 @@ def test_kernel_choice_by_shape():
     m = _args_for(_fake(num_qo_heads=16, num_kv_heads=1, head_dim_qk=576, head_dim_v=512, page_size=64,
                         mla=True))
     m.q = m.k_pages = m.v_pages = m.out = 0x1000
-    assert pkv.KERNEL_NAMES[pkv.pkv_plan(m).kernel] == "dma_mla_bf16"
+    assert pkv.KERNEL_NAMES[pkv.pkv_plan(m).kernel] == "mla32_bf16"
+    # pages of 16 keys do not hold whole 32-key blocks: the ring kernel
+    m16 = _args_for(_fake(num_qo_heads=16, num_kv_heads=1, head_dim_qk=576, head_dim_v=512, page_size=16,
+                          mla=True))
+    m16.q = m16.k_pages = m16.v_pages = m16.out = 0x1000
+    assert pkv.KERNEL_NAMES[pkv.pkv_plan(m16).kernel] == "dma_mla_bf16"
 
 
 def test_split_plan_is_page_aligned_and_sized_to_cus():
