@@ -138,7 +138,7 @@ def test_context_split_plan_only_fills_the_cus_once():
     a = _args_for(W.mla_b512_kv4096(batch=64, seq_len=64))
     a.max_kv_len, a.max_pages_per_seq, a.table_stride = 4096, 64, 64
     info = pkv.pkv_plan(a, False, 256)
-    assert pkv.KERNEL_NAMES[info.kernel] == "dma_mla_bf16" and info.num_splits == 4
+    assert pkv.KERNEL_NAMES[info.kernel] == "mla32_bf16" and info.num_splits == 4
 
 
 @pytest.mark.parametrize("field,value,status", [
