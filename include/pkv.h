@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 4
+#define PKV_ABI_VERSION 5
 
 typedef enum pkv_status {
   PKV_OK = 0,
@@ -228,6 +228,22 @@ pkv_status pkv_decode(const pkv_args* args, void* workspace, size_t workspace_by
 
 /* Paged causal context (prefill): variable rows per request through args->q_indptr. */
 pkv_status pkv_context(const pkv_args* args, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pkv_decode without a workspace argument, for callers that cannot allocate
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  The same plan and kernels as pkv_decode; the Split-KV partials
+ * live in a static device array of PKV_NOALLOC_SCRATCH_BYTES inside the
+ * library, one per GPU, held until the process ends (its device address is
+ * looked up once per device).  The call allocates nothing and frees nothing.
+ * A call whose plan needs more scratch returns PKV_ERR_WORKSPACE before
+ * anything is enqueued.  Every call on one GPU shares that GPU's array, which
+ * keeps the last call's contents (no call relies on it starting at zero):
+ * calls that may overlap on one GPU (different streams, or several host
+ * threads) race and must not be issued.
+ */
+#define PKV_NOALLOC_SCRATCH_BYTES (32u << 20)
+pkv_status pkv_decode_noalloc(const pkv_args* args, void* stream);
 
 /*
  * The log-sum-exp reducer on its own (Split-KV merge, PR #4557 page: split

@@ -15,6 +15,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "../../include/pkv.h"
@@ -605,6 +606,39 @@ pkv_status run(const pkv_args* a, bool is_context, void* ws, size_t ws_bytes, vo
 
 }  // namespace
 
+// ---------------------------------------------------------------- the allocation-free decode
+// Scratch for pkv_decode_noalloc: the Split-KV partials, LSE slots and the
+// balanced schedule's page prefix live in this array instead of a caller
+// workspace.  Each GPU the library runs on holds its own copy until the
+// process ends; host code never uses the array's name as an address (on the
+// host it is only a stand-in), only the device address that
+// hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[PKV_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// device address of `scratch` on the current device, looked up once per device
+pkv_status scratch_for_current_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(PKV_ERR_UNSUPPORTED, "device %d beyond the scratch table", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(PKV_ERR_HIP, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return PKV_OK;
+}
+}  // namespace
+
 extern "C" {
 
 int pkv_abi_version(void) { return PKV_ABI_VERSION; }
@@ -637,6 +671,31 @@ pkv_status pkv_decode(const pkv_args* args, void* workspace, size_t workspace_by
 
 pkv_status pkv_context(const pkv_args* args, void* workspace, size_t workspace_bytes, void* stream) {
   return run(args, true, workspace, workspace_bytes, stream);
+}
+
+pkv_status pkv_decode_noalloc(const pkv_args* args, void* stream) {
+  // plan first (host only): a call whose partials do not fit is refused
+  // before anything touches the device
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
+  }
+  pkv_plan_info plan;
+  pkv_status st = make_plan(args, false, cus, &plan);
+  if (st != PKV_OK) return st;
+  if (plan.workspace_bytes > (size_t)PKV_NOALLOC_SCRATCH_BYTES)
+    return fail(PKV_ERR_WORKSPACE,
+                "pkv_decode_noalloc: this call needs %zu bytes of scratch; the library's static scratch holds %zu "
+                "(use pkv_decode with a caller workspace)",
+                plan.workspace_bytes, (size_t)PKV_NOALLOC_SCRATCH_BYTES);
+  if (args->batch == 0) return ok();
+  void* ws = nullptr;
+  if (plan.workspace_bytes > 0) {
+    st = scratch_for_current_device(&ws);
+    if (st != PKV_OK) return st;
+  }
+  return run(args, false, ws, plan.workspace_bytes > 0 ? (size_t)PKV_NOALLOC_SCRATCH_BYTES : 0, stream);
 }
 
 pkv_status pkv_lse_merge(int32_t num_splits, int32_t num_rows, int32_t num_qo_heads, int32_t head_dim_v,

@@ -33,7 +33,7 @@ KERNEL_NAMES = {0: "none", 1: "generic", 2: "gqa_bf16", 3: "gqa_fp8", 4: "wide_b
 KERNEL_IDS = {v: k for k, v in KERNEL_NAMES.items()}
 
 DTYPE_CODES = {"f32": PKV_DTYPE_F32, "bf16": PKV_DTYPE_BF16, "e4m3": PKV_DTYPE_FP8_E4M3}
-EXPORTED = ["pkv_abi_version", "pkv_last_error", "pkv_plan", "pkv_workspace_bytes", "pkv_decode",
+EXPORTED = ["pkv_abi_version", "pkv_last_error", "pkv_plan", "pkv_workspace_bytes", "pkv_decode", "pkv_decode_noalloc",
             "pkv_context", "pkv_lse_merge", "pkv_append"]
 PKV_DEVERR_POS_RANGE = 0x10
 PKV_DEVERR_QSCALE_ROWS = 0x20
@@ -115,6 +115,8 @@ def load_library(path: str = LIB_PATH):
         lib.pkv_append.restype = C.c_int
         lib.pkv_workspace_bytes.argtypes = [C.POINTER(PkvArgs), C.c_int, C.POINTER(C.c_size_t)]
         lib.pkv_workspace_bytes.restype = C.c_int
+        lib.pkv_decode_noalloc.argtypes = [C.POINTER(PkvArgs), C.c_void_p]
+        lib.pkv_decode_noalloc.restype = C.c_int
         for fn in (lib.pkv_decode, lib.pkv_context):
             fn.argtypes = [C.POINTER(PkvArgs), C.c_void_p, C.c_size_t, C.c_void_p]
             fn.restype = C.c_int
@@ -154,6 +156,14 @@ def pkv_workspace_bytes(args: PkvArgs, is_context: bool = False) -> int:
     n = C.c_size_t(0)
     _check(load_library().pkv_workspace_bytes(C.byref(args), int(is_context), C.byref(n)))
     return int(n.value)
+
+
+PKV_NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def pkv_decode_noalloc(args: PkvArgs, stream: int, check: bool = True) -> int:
+    st = load_library().pkv_decode_noalloc(C.byref(args), C.c_void_p(stream))
+    return _check(st) if check else st
 
 
 def pkv_decode(args: PkvArgs, workspace: int, workspace_bytes: int, stream: int, check: bool = True) -> int:

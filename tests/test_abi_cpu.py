@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
     assert set(declared) == set(pkv.EXPORTED)
     for name in declared:
         assert hasattr(lib, name), name
-    assert pkv.pkv_abi_version() == 4
+    assert pkv.pkv_abi_version() == 5
 
 
 def test_ctypes_mirror_matches_c_layout(tmp_path):
@@ -344,3 +344,16 @@ def test_separate_value_tables_route_to_families_with_a_second_page_list():
     a.v_shares_k = 0
     a.sinks = 0x2002
     assert pkv.pkv_plan(a, check=False).status == pkv.PKV_ERR_INVALID_ARG
+
+
+def test_noalloc_refuses_a_plan_beyond_its_static_scratch():
+    # MLA decode of 64 requests over 4096 keys in 8 partitions needs about 134 MB
+    # of fp32 partials: refused before anything touches a device
+    a = _args_for(W.mla_b512_kv4096(batch=64, seq_len=64))
+    a.max_kv_len, a.max_pages_per_seq, a.table_stride = 4096, 64, 64
+    a.num_splits = 8
+    a.q = a.k_pages = a.out = 0x1000
+    assert pkv.pkv_plan(a, False, 256).workspace_bytes > pkv.PKV_NOALLOC_SCRATCH_BYTES
+    st = pkv.pkv_decode_noalloc(a, 0, check=False)
+    assert st == pkv.PKV_ERR_WORKSPACE
+    assert "static scratch" in pkv.pkv_last_error()
