@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 5
+#define PKV_ABI_VERSION 6
 
 typedef enum pkv_status {
   PKV_OK = 0,
@@ -285,9 +285,14 @@ pkv_status pkv_lse_merge(int32_t num_splits, int32_t num_rows, int32_t num_qo_he
  *     q_quant = 2, of y * q_scale_inv with no scale written (PR #5956 body,
  *     "Contract": dynamic per-token/per-head or static query quantization);
  *   - key heads and the unchanged value heads are written to token pos % P of
- *     page block_tables[b][pos / P] of the NHD caches [num_pages, P, Hkv, 128]:
- *     bf16, or e4m3 codes of x / k_scale and x / v_scale (round to nearest
- *     even, saturated to +-448);
+ *     page block_tables[b][pos / P] of the caches: bf16, or e4m3 codes of
+ *     x / k_scale and x / v_scale (round to nearest even, saturated to
+ *     +-448).  The pages' caches are NHD [num_pages, P, Hkv, 128]; `layout`
+ *     and the element strides also take the HND pools [num_pages, Hkv, P,
+ *     128] the attention entry points read, so the row of slot s, KV head g
+ *     of page pg starts at k_cache + pg*k_stride_page + g*k_stride_head +
+ *     s*k_stride_tok (likewise V), with the same consistency rules as
+ *     pkv_args' pools;
  *   - with clear_tail, tokens [(seq_lens[b] - 1) % P + 1, P) of every nonempty
  *     request's last page are zeroed in both caches (the caller owns the pages
  *     exclusively: a page shared with a longer request would lose rows).
@@ -328,7 +333,7 @@ typedef struct pkv_append_args {
   const int32_t* block_tables; /* [B, table_stride] */
   int64_t table_stride;      /* >= max_pages_per_seq */
   void* out_q;               /* [T, Hq, 128]: bf16 (q_quant 0) or e4m3 codes */
-  void* k_cache;             /* NHD [num_pages, P, Hkv, 128], bf16 or e4m3 */
+  void* k_cache;             /* [num_pages, P, Hkv, 128] (NHD) or [num_pages, Hkv, P, 128] (HND), bf16 or e4m3 */
   void* v_cache;
   int32_t* err_word;         /* optional device word, OR-ed with PKV_DEVERR_* bits */
   int32_t q_quant;           /* query output: 0 bf16; 1 e4m3, dynamic scale; 2 e4m3, static scale */
@@ -337,6 +342,10 @@ typedef struct pkv_append_args {
   int32_t q_scale_layout;    /* q_quant 1: 0 [T, Hq] or 1 [B, Hq, q_scale_stride] */
   int64_t q_scale_stride;    /* q_scale_layout 1: entries per (request, head), >= 1 */
   float* q_scale;            /* q_quant 1: fp32 scales (layout above), 4-byte aligned */
+  int32_t layout;            /* pkv_layout of both caches (validates the strides) */
+  int32_t reserved2;
+  int64_t k_stride_page, k_stride_head, k_stride_tok; /* K cache strides in elements of kv_dtype */
+  int64_t v_stride_page, v_stride_head, v_stride_tok; /* V cache strides */
 } pkv_append_args;
 
 pkv_status pkv_append(const pkv_append_args* args, void* stream);

@@ -63,6 +63,22 @@ bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u
 constexpr int kMaxSplits = 256;
 constexpr int kMaxPagesPerSplit = 4096;  // bounds the LDS page list of the MFMA kernels
 
+// Strides (elements) of a paged pool [pages, Hkv, P, D] (HND) or [pages, P,
+// Hkv, D] (NHD), innermost contiguous: rows of one page never overlap and
+// every page holds all of its rows.
+pkv_status check_pool_strides(int32_t layout, int64_t H, int64_t P, int64_t D, int64_t sp, int64_t sh, int64_t st,
+                              const char* name) {
+  if (sp <= 0 || sh < 0 || st <= 0) return fail(PKV_ERR_INVALID_ARG, "%s strides must be positive", name);
+  if (layout == PKV_LAYOUT_HND) {
+    if (st < D || (H > 1 && sh < P * st) || sp < H * std::max<int64_t>(sh, P * st))
+      return fail(PKV_ERR_INVALID_ARG, "%s strides do not describe an HND [pages, Hkv, P, D] pool", name);
+  } else {
+    if ((H > 1 && sh < D) || st < H * std::max<int64_t>(sh, D) || sp < P * st)
+      return fail(PKV_ERR_INVALID_ARG, "%s strides do not describe an NHD [pages, P, Hkv, D] pool", name);
+  }
+  return PKV_OK;
+}
+
 // Host-visible argument checks shared by plan / decode / context.
 pkv_status validate(const pkv_args* a, bool is_context) {
   if (!a) return fail(PKV_ERR_INVALID_ARG, "args is NULL");
@@ -114,23 +130,13 @@ pkv_status validate(const pkv_args* a, bool is_context) {
   if (q_rows > INT32_MAX)
     return fail(PKV_ERR_INVALID_ARG, "query rows x heads (%lld) exceed 2^31 - 1", (long long)q_rows);
   // layout consistency of the strides (innermost dimension contiguous)
-  const int64_t D_qk = a->head_dim_qk, D_v = a->head_dim_v, P = a->page_size, H = a->num_kv_heads;
-  auto check_pool = [&](int64_t sp, int64_t sh, int64_t st, int64_t D, const char* name) -> pkv_status {
-    if (sp <= 0 || sh < 0 || st <= 0)
-      return fail(PKV_ERR_INVALID_ARG, "%s strides must be positive", name);
-    if (a->layout == PKV_LAYOUT_HND) {
-      if (st < D || (H > 1 && sh < P * st) || sp < H * std::max<int64_t>(sh, P * st))
-        return fail(PKV_ERR_INVALID_ARG, "%s strides do not describe an HND [pages, Hkv, P, D] pool", name);
-    } else {
-      if ((H > 1 && sh < D) || st < H * std::max<int64_t>(sh, D) || sp < P * st)
-        return fail(PKV_ERR_INVALID_ARG, "%s strides do not describe an NHD [pages, P, Hkv, D] pool", name);
-    }
-    return PKV_OK;
-  };
-  pkv_status st = check_pool(a->k_stride_page, a->k_stride_head, a->k_stride_tok, D_qk, "k");
+  const int64_t D_qk = a->head_dim_qk, D_v = a->head_dim_v;
+  pkv_status st = check_pool_strides(a->layout, a->num_kv_heads, a->page_size, D_qk, a->k_stride_page,
+                                     a->k_stride_head, a->k_stride_tok, "k");
   if (st != PKV_OK) return st;
   if (!a->v_shares_k) {
-    st = check_pool(a->v_stride_page, a->v_stride_head, a->v_stride_tok, D_v, "v");
+    st = check_pool_strides(a->layout, a->num_kv_heads, a->page_size, D_v, a->v_stride_page, a->v_stride_head,
+                            a->v_stride_tok, "v");
     if (st != PKV_OK) return st;
   }
   if (a->table_stride < a->max_pages_per_seq)
@@ -176,6 +182,13 @@ bool kernel_supports(int32_t k, const pkv_args* a, bool is_context) {
   if (a->v_block_tables && (k >= pkv::KERNEL_DMA_GQA_FP8_N2 && k <= pkv::KERNEL_DMA_GQA_FP8_N2S3)) return false;
   if (a->v_block_tables && (k == pkv::KERNEL_M32_MLA_BF16 || k == pkv::KERNEL_MLA_BF16 || k == pkv::KERNEL_MLA_FP8 ||
                             k == pkv::KERNEL_MLA32_BF16 || k == pkv::KERNEL_MLA32_SEQ_BF16))
+    return false;
+  // the direct-to-LDS ring loaders form a page's address as a 64-bit base
+  // plus a 32-bit product and offset: pages of 4 GiB or more go elsewhere
+  pkv::MfmaShape ring;
+  const int64_t eb = elem_bytes(a->kv_dtype);
+  if (pkv::dma_shape(k, &ring) &&
+      (a->k_stride_page * eb > (int64_t)UINT32_MAX || (!a->v_shares_k && a->v_stride_page * eb > (int64_t)UINT32_MAX)))
     return false;
   const bool fp8 = a->kv_dtype == PKV_DTYPE_FP8_E4M3;
   const int G = a->num_qo_heads / a->num_kv_heads;
@@ -287,7 +300,7 @@ int32_t seg_cost_pages(const pkv_args* a) {
   return (int32_t)std::min<int64_t>(64, (PKV_SEG_COST_BYTES + page_bytes / 2) / std::max<int64_t>(page_bytes, 1));
 }
 
-int32_t choose_kernel(const pkv_args* a, bool is_context) {
+int32_t preferred_kernel(const pkv_args* a, bool is_context) {
   if (!mfma_eligible(a)) return pkv::KERNEL_GENERIC;
   const bool fp8 = a->kv_dtype == PKV_DTYPE_FP8_E4M3;
   const int G = a->num_qo_heads / a->num_kv_heads;
@@ -321,6 +334,22 @@ int32_t choose_kernel(const pkv_args* a, bool is_context) {
     return fp8 ? pkv::KERNEL_DMA_MLA_FP8 : pkv::KERNEL_DMA_MLA_BF16;
   }
   return pkv::KERNEL_GENERIC;
+}
+
+// The preferred family, else (a direct-to-LDS ring family on pages it cannot
+// address) its register-staged twin, else the generic kernel.
+int32_t choose_kernel(const pkv_args* a, bool is_context) {
+  const int32_t k = preferred_kernel(a, is_context);
+  if (kernel_supports(k, a, is_context)) return k;
+  int32_t twin = pkv::KERNEL_GENERIC;
+  switch (k) {
+    case pkv::KERNEL_DMA_GQA_FP8_N2: twin = pkv::KERNEL_GQA_FP8; break;
+    case pkv::KERNEL_DMA_WIDE_FP8: twin = pkv::KERNEL_WIDE_FP8; break;
+    case pkv::KERNEL_DMA_WIDE_BF16: twin = pkv::KERNEL_WIDE_BF16; break;
+    case pkv::KERNEL_DMA_MLA_FP8: twin = pkv::KERNEL_MLA_FP8; break;
+    case pkv::KERNEL_DMA_MLA_BF16: twin = pkv::KERNEL_MLA_BF16; break;
+  }
+  return kernel_supports(twin, a, is_context) ? twin : pkv::KERNEL_GENERIC;
 }
 
 pkv_status make_plan(const pkv_args* a, bool is_context, int num_cus, pkv_plan_info* info) {
@@ -760,6 +789,14 @@ extern "C" pkv_status pkv_append(const pkv_append_args* a, void* stream) {
   }
   if (a->q_quant == 2 && (!std::isfinite(a->q_scale_inv) || a->q_scale_inv == 0.f))
     return fail(PKV_ERR_INVALID_ARG, "q_scale_inv must be finite and non-zero");
+  if (a->layout != PKV_LAYOUT_HND && a->layout != PKV_LAYOUT_NHD)
+    return fail(PKV_ERR_INVALID_ARG, "layout %d unknown", a->layout);
+  pkv_status st = check_pool_strides(a->layout, a->num_kv_heads, a->page_size, 128, a->k_stride_page,
+                                     a->k_stride_head, a->k_stride_tok, "k cache");
+  if (st != PKV_OK) return st;
+  st = check_pool_strides(a->layout, a->num_kv_heads, a->page_size, 128, a->v_stride_page, a->v_stride_head,
+                          a->v_stride_tok, "v cache");
+  if (st != PKV_OK) return st;
   if (a->batch == 0 || (a->num_tokens == 0 && !a->clear_tail)) return ok();
   if (!a->q_indptr || !a->seq_lens || !a->block_tables || !a->k_cache || !a->v_cache)
     return fail(PKV_ERR_INVALID_ARG, "q_indptr, seq_lens, block_tables and both caches are required");

@@ -34,6 +34,7 @@ struct AppendParams {
   const int32_t* seq_lens;
   const int32_t* table;
   int64_t table_stride;
+  int64_t k_sp, k_sh, k_st, v_sp, v_sh, v_st;  // cache strides (elements)
   uint16_t* out_q;
   unsigned char* k_cache;
   unsigned char* v_cache;
@@ -177,7 +178,8 @@ __global__ __launch_bounds__(256) void append_kernel(const AppendParams p) {
     const int g = is_k ? hh - p.Hq : hh - p.Hq - p.Hkv;
     const int pg = p.table[(int64_t)lo_b * p.table_stride + pos / p.P];
     if (!page_ok(p, pg)) return;
-    const int64_t row = (((int64_t)pg * p.P + pos % p.P) * p.Hkv + g) * 128;
+    const int64_t row = is_k ? pg * p.k_sp + g * p.k_sh + (pos % p.P) * p.k_st
+                             : pg * p.v_sp + g * p.v_sh + (pos % p.P) * p.v_st;
     unsigned char* cache = is_k ? p.k_cache : p.v_cache;
     if (p.fp8) {
       const float inv = is_k ? p.inv_k_scale : p.inv_v_scale;
@@ -201,8 +203,10 @@ __global__ __launch_bounds__(256) void append_kernel(const AppendParams p) {
   const int pg = p.table[(int64_t)b * p.table_stride + (L - 1) / p.P];
   if (!page_ok(p, pg)) return;
   unsigned char* cache = k_side ? p.k_cache : p.v_cache;
+  const int64_t base = k_side ? pg * p.k_sp + g * p.k_sh : pg * p.v_sp + g * p.v_sh;
+  const int64_t st = k_side ? p.k_st : p.v_st;
   for (int slot = (L - 1) % p.P + 1; slot < p.P; ++slot) {
-    const int64_t row = (((int64_t)pg * p.P + slot) * p.Hkv + g) * 128;
+    const int64_t row = base + slot * st;
     if (p.fp8) {
       cache[row + lane] = 0;
       cache[row + lane + 64] = 0;
@@ -239,6 +243,12 @@ hipError_t launch_append(const pkv_append_args* a, hipStream_t s) {
   p.seq_lens = a->seq_lens;
   p.table = a->block_tables;
   p.table_stride = a->table_stride;
+  p.k_sp = a->k_stride_page;
+  p.k_sh = a->k_stride_head;
+  p.k_st = a->k_stride_tok;
+  p.v_sp = a->v_stride_page;
+  p.v_sh = a->v_stride_head;
+  p.v_st = a->v_stride_tok;
   p.out_q = (uint16_t*)a->out_q;
   p.k_cache = (unsigned char*)a->k_cache;
   p.v_cache = (unsigned char*)a->v_cache;

@@ -87,6 +87,9 @@ class PkvAppendArgs(C.Structure):
         ("out_q", C.c_void_p), ("k_cache", C.c_void_p), ("v_cache", C.c_void_p), ("err_word", C.c_void_p),
         ("q_quant", C.c_int32), ("upper_max", C.c_float), ("q_scale_inv", C.c_float),
         ("q_scale_layout", C.c_int32), ("q_scale_stride", C.c_int64), ("q_scale", C.c_void_p),
+        ("layout", C.c_int32), ("reserved2", C.c_int32),
+        ("k_stride_page", C.c_int64), ("k_stride_head", C.c_int64), ("k_stride_tok", C.c_int64),
+        ("v_stride_page", C.c_int64), ("v_stride_head", C.c_int64), ("v_stride_tok", C.c_int64),
     ]
 
 
@@ -421,4 +424,9 @@ def upload_append(prob, device="cuda", with_err: bool = True) -> DeviceAppend:
     a.q_scale_layout = prob.q_scale_layout
     a.q_scale_stride = prob.q_scale_stride
     a.q_scale = t["q_scale"].data_ptr() if prob.q_quant == 1 else 0
+    a.layout = PKV_LAYOUT_HND if prob.layout == "HND" else PKV_LAYOUT_NHD
+    sp, sh, st = prob.cache_strides()
+    a.k_stride_page = a.v_stride_page = sp
+    a.k_stride_head = a.v_stride_head = sh
+    a.k_stride_tok = a.v_stride_tok = st
     return DeviceAppend(args=a, tensors=t)

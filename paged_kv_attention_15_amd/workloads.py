@@ -479,7 +479,9 @@ class AppendProblem:
       q_indptr     int32 [B + 1]   rows of request b are q_indptr[b] .. q_indptr[b+1]
       seq_lens     int32 [B]       total length after the append
       block_tables int32 [B, max_pages]
-      k_cache0     initial NHD K cache [num_pages, P, Hkv, 128] (uint16 bf16 bits or uint8 e4m3)
+      k_cache0     initial K cache (uint16 bf16 bits or uint8 e4m3), NHD [num_pages, P, Hkv, 128 + pad]
+                   or HND [num_pages, Hkv, P, 128 + pad]; the last `cache_pad` elements of each
+                   row are padding no call may write
       v_cache0     same for V
     """
 
@@ -512,6 +514,19 @@ class AppendProblem:
     # dynamic scales: 0 -> [T, Hq]; 1 -> [B, Hq, q_scale_stride] indexed by the row inside its request
     q_scale_layout: int = 0
     q_scale_stride: int = 0
+    layout: str = "NHD"
+    cache_pad: int = 0
+
+    def cache_rows(self, cache: np.ndarray) -> np.ndarray:
+        """View [num_pages, P, Hkv, 128] of a cache array of this problem's
+        layout (writes through the view reach the array)."""
+        rows = cache[..., :self.head_dim]
+        return rows if self.layout == "NHD" else rows.transpose(0, 2, 1, 3)
+
+    def cache_strides(self):
+        """(page, head, token) strides of the caches in elements."""
+        H, P, W = self.num_kv_heads, self.page_size, self.head_dim + self.cache_pad
+        return (P * H * W, W, H * W) if self.layout == "NHD" else (H * P * W, P * W, W)
 
     @property
     def q_scale_entries(self) -> int:
@@ -568,11 +583,11 @@ def make_append_problem(*, name: str, seed: int, new_lens, seq_lens, num_qo_head
                         k_scale: float = 1.0, v_scale: float = 1.0, extra_pages: int = 2,
                         table_slack_pages: int = 1, max_pos: Optional[int] = None, q_quant: int = 0,
                         upper_max: float = 448.0, q_scale_inv: float = 1.0, q_scale_layout: int = 0,
-                        q_scale_stride: int = 0) -> AppendProblem:
+                        q_scale_stride: int = 0, layout: str = "NHD", cache_pad: int = 0) -> AppendProblem:
     """Draw order: page permutation, qkv, the two weight vectors, the initial
     cache contents (random non-zero storage so that untouched and cleared rows
-    are told apart).  Unused table slots point at a spare page that no request
-    owns, so any stray write through them shows up."""
+    are told apart, padding included).  Unused table slots point at a spare
+    page that no request owns, so any stray write through them shows up."""
     rng = np.random.default_rng(seed)
     new_lens = [int(x) for x in new_lens]
     seq_lens = [int(x) for x in seq_lens]
@@ -595,7 +610,9 @@ def make_append_problem(*, name: str, seed: int, new_lens, seq_lens, num_qo_head
     qkv = bf16_bits(rng.standard_normal((T, (Hq + 2 * Hkv) * D)).astype(np.float32))
     q_w = bf16_bits((1.0 + 0.25 * rng.standard_normal(D)).astype(np.float32))
     k_w = bf16_bits((1.0 + 0.25 * rng.standard_normal(D)).astype(np.float32))
-    shape = (num_pages, P, Hkv, D)
+    if layout not in ("NHD", "HND"):
+        raise ValueError(layout)
+    shape = (num_pages, P, Hkv, D + cache_pad) if layout == "NHD" else (num_pages, Hkv, P, D + cache_pad)
     if kv_dtype == BF16:
         k0 = bf16_bits((rng.standard_normal(shape) + 3.0).astype(np.float32))
         v0 = bf16_bits((rng.standard_normal(shape) + 3.0).astype(np.float32))
@@ -611,15 +628,19 @@ def make_append_problem(*, name: str, seed: int, new_lens, seq_lens, num_qo_head
                          v_cache0=v0, norm_policy=norm_policy, kv_dtype=kv_dtype, k_scale=float(k_scale),
                          v_scale=float(v_scale), clear_tail=clear_tail, q_quant=int(q_quant),
                          upper_max=float(upper_max), q_scale_inv=float(q_scale_inv),
-                         q_scale_layout=int(q_scale_layout), q_scale_stride=int(q_scale_stride))
+                         q_scale_layout=int(q_scale_layout), q_scale_stride=int(q_scale_stride),
+                         layout=layout, cache_pad=int(cache_pad))
 
 
 def append_h64x8_b32_decode(seed: int = 0, norm_policy: int = 2, kv_dtype: str = BF16,
-                            q_quant: int = 0) -> AppendProblem:
+                            q_quant: int = 0, layout: str = "NHD") -> AppendProblem:
     """The pages' H1 row: Hq=64 / Hkv=8, 32 requests appending one row each,
     here at total lengths 2048 with 64-token pages (q_quant 1: e4m3 queries
-    with a dynamic scale per (row, head) in the [T, Hq] layout, upper_max 448)."""
-    return make_append_problem(name=f"append-h64x8-b32-decode-p{norm_policy}-{kv_dtype}-q{q_quant}", seed=seed,
+    with a dynamic scale per (row, head) in the [T, Hq] layout, upper_max 448).
+    The pages' caches are NHD; layout "HND" writes the attention pools' layout."""
+    tag = "" if layout == "NHD" else f"-{layout.lower()}"
+    return make_append_problem(name=f"append-h64x8-b32-decode-p{norm_policy}-{kv_dtype}-q{q_quant}{tag}", seed=seed,
+                               layout=layout,
                                new_lens=[1] * 32, seq_lens=[2048] * 32, num_qo_heads=64, num_kv_heads=8,
                                page_size=64, norm_policy=norm_policy, kv_dtype=kv_dtype,
                                k_scale=0.05 if kv_dtype == E4M3 else 1.0, v_scale=0.05 if kv_dtype == E4M3 else 1.0,

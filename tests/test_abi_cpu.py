@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
     assert set(declared) == set(pkv.EXPORTED)
     for name in declared:
         assert hasattr(lib, name), name
-    assert pkv.pkv_abi_version() == 5
+    assert pkv.pkv_abi_version() == 6
 
 
 def test_ctypes_mirror_matches_c_layout(tmp_path):
@@ -279,6 +279,10 @@ def _append_args(**kw):
         setattr(a, name, 0x1000)
     a.qkv_stride_tok = 10 * 128
     a.table_stride = 4
+    a.layout = pkv.PKV_LAYOUT_NHD  # dense [pages, P, Hkv, 128]
+    a.k_stride_page = a.v_stride_page = 16 * 128
+    a.k_stride_head = a.v_stride_head = 128
+    a.k_stride_tok = a.v_stride_tok = 128
     for k, v in kw.items():
         setattr(a, k, v)
     return a
@@ -296,6 +300,10 @@ def _append_args(**kw):
     ("qkv", 0x1001, pkv.PKV_ERR_INVALID_ARG),
     ("q_weight", 0, pkv.PKV_ERR_INVALID_ARG),
     ("num_qo_heads", 0, pkv.PKV_ERR_INVALID_ARG),
+    ("layout", 2, pkv.PKV_ERR_INVALID_ARG),
+    ("k_stride_tok", 64, pkv.PKV_ERR_INVALID_ARG),
+    ("v_stride_page", 1024, pkv.PKV_ERR_INVALID_ARG),
+    ("k_stride_page", 0, pkv.PKV_ERR_INVALID_ARG),
 ])
 def test_append_rejects_bad_arguments_before_launch(field, value, status):
     assert pkv.pkv_append(_append_args(**{field: value}), 0, check=False) == status
@@ -317,6 +325,21 @@ def test_append_rejects_bad_arguments_before_launch(field, value, status):
 def test_append_query_quantization_arguments_checked_before_launch(kw):
     assert pkv.pkv_append(_append_args(**kw), 0, check=False) == pkv.PKV_ERR_INVALID_ARG
     assert pkv.pkv_last_error() != ""
+
+
+def test_append_cache_strides_follow_the_layout():
+    # two KV heads: the NHD and HND dense strides differ, and each layout
+    # accepts only its own (and padded versions of it)
+    nhd = dict(num_kv_heads=2, qkv_stride_tok=12 * 128, k_stride_page=16 * 256, k_stride_head=128,
+               k_stride_tok=256, v_stride_page=16 * 256, v_stride_head=128, v_stride_tok=256)
+    hnd = dict(num_kv_heads=2, qkv_stride_tok=12 * 128, k_stride_page=2 * 16 * 128, k_stride_head=16 * 128,
+               k_stride_tok=128, v_stride_page=2 * 16 * 160, v_stride_head=16 * 160, v_stride_tok=160)
+    for layout, good, bad in ((pkv.PKV_LAYOUT_NHD, nhd, hnd), (pkv.PKV_LAYOUT_HND, hnd, nhd)):
+        # strides are checked before the empty-batch no-op, so nothing launches
+        assert pkv.pkv_append(_append_args(layout=layout, batch=0, **good), 0, check=False) == pkv.PKV_OK
+        assert pkv.pkv_append(_append_args(layout=layout, batch=0, **bad), 0, check=False) == \
+            pkv.PKV_ERR_INVALID_ARG, layout
+        assert "strides" in pkv.pkv_last_error()
 
 
 def test_append_e4m3_needs_scales_and_empty_calls_are_noops():
@@ -357,3 +380,46 @@ def test_noalloc_refuses_a_plan_beyond_its_static_scratch():
     st = pkv.pkv_decode_noalloc(a, 0, check=False)
     assert st == pkv.PKV_ERR_WORKSPACE
     assert "static scratch" in pkv.pkv_last_error()
+
+
+@pytest.mark.parametrize("layout,pad", [("NHD", 0), ("HND", 0), ("NHD", 8), ("HND", 64)])
+def test_append_cache_view_follows_the_header_addressing(layout, pad):
+    # the GPU tests read caches through AppendProblem.cache_rows and hand the
+    # library AppendProblem.cache_strides: both must agree with the header's
+    # rule (row of slot s, KV head g, page pg at pg*sp + g*sh + s*st)
+    prob = W.make_append_problem(name="view", seed=1, new_lens=[2, 1], seq_lens=[5, 9], num_qo_heads=6,
+                                 num_kv_heads=3, page_size=4, layout=layout, cache_pad=pad)
+    flat = np.arange(prob.k_cache0.size, dtype=np.int64).reshape(prob.k_cache0.shape)
+    view = prob.cache_rows(flat)
+    sp, sh, st = prob.cache_strides()
+    assert view.shape == (prob.num_pages, 4, 3, 128)
+    pg, s, g, c = np.meshgrid(*[np.arange(n) for n in view.shape], indexing="ij")
+    assert np.array_equal(view, pg * sp + g * sh + s * st + c)
+    assert prob.v_cache0.shape == prob.k_cache0.shape
+
+
+@pytest.mark.parametrize("kv,mla", [(pkv.PKV_DTYPE_FP8_E4M3, False), (pkv.PKV_DTYPE_BF16, False),
+                                    (pkv.PKV_DTYPE_BF16, True)])
+def test_pages_of_4gib_or_more_avoid_the_ring_loaders(kv, mla):
+    # the direct-to-LDS ring loaders address a page with a 32-bit byte product:
+    # a page stride of 2^32 bytes or more must be planned on another family,
+    # and forcing a ring kernel on it is refused
+    # e4m3 GQA decode, bf16 speculative decode (32 rows per KV head), MLA on 16-token pages
+    kw = dict(num_qo_heads=16, num_kv_heads=1, head_dim_qk=576, head_dim_v=512, page_size=16, mla=True) \
+        if mla else ({} if kv == pkv.PKV_DTYPE_FP8_E4M3 else dict(q_lens=[8, 8]))
+    a = _args_for(_fake(**kw))
+    a.q = a.k_pages = a.v_pages = a.out = 0x1000
+    a.kv_dtype = kv
+    eb = 1 if kv == pkv.PKV_DTYPE_FP8_E4M3 else 2
+    small = pkv.KERNEL_NAMES[pkv.pkv_plan(a).kernel]
+    assert small.startswith("dma_"), small
+    a.k_stride_page = (1 << 32) // eb
+    a.v_stride_page = (1 << 32) // eb
+    big = pkv.KERNEL_NAMES[pkv.pkv_plan(a).kernel]
+    assert not big.startswith("dma_"), big
+    a.kernel_hint = pkv.KERNEL_IDS[small]
+    st = pkv.load_library().pkv_plan(C.byref(a), 0, 0, C.byref(pkv.PkvPlanInfo()))
+    assert st == pkv.PKV_ERR_UNSUPPORTED, st
+    a.k_stride_page = a.v_stride_page = (1 << 32) // eb - 16 // eb  # just under: the ring kernel again
+    a.kernel_hint = 0
+    assert pkv.KERNEL_NAMES[pkv.pkv_plan(a).kernel] == small
