@@ -1,17 +1,20 @@
 """Benchmark: paged decode latency and achieved HBM bandwidth on KV bytes.
 
 One step is one pkv_decode call (attention kernel plus, when the planner
-splits the KV range, the log-sum-exp reducer) over the headline workload:
-bf16 paged GQA decode, B=32, one query row, Hq=32 / Hkv=8, D=128, HND pages of
-32 tokens, 4096 keys per request, pages shuffled across the pool.  Inputs are
-seeded synthetic draws already resident in HBM when timing starts.
+splits the KV range, the log-sum-exp reducer) over the headline workload, the
+largest of the five on one GPU: MLA decode, B=512, one query row, Hq=128 on
+one shared latent head (D_qk = 576 = 512 latent + 64 rope, D_v = 512, V = the
+latent rows), pages of 64 tokens, 4096 keys per request (2.42 GB of KV per
+call), pages shuffled across the pool.  Inputs are seeded synthetic draws
+already resident in HBM when timing starts.
 
 Prints ONE JSON line.  `value` is KV GB/s (algorithmic KV bytes of the call /
 wall time per call).  `roofline` reports the dominant kernel against the
 MI355X HBM peak (8 TB/s); `cpu_baseline` is the fp64 CPU oracle timed on a
 bounded sample of the same workload on the host.  `secondary` holds the same
-measurements for the other four workloads (FP8 ragged split decode, MLA decode
-q=1 / q=2, causal context) unless --no-secondary is given.
+measurements, each with its own roofline, for the other workloads (bf16 GQA
+decode, FP8 ragged split decode, MLA decode q=2, causal context, the append
+producer) unless --no-secondary is given; --only NAME measures one workload.
 """
 from __future__ import annotations
 
@@ -31,27 +34,41 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0
 METRIC = "paged decode µs/call + achieved HBM GB/s (KV bytes) as % of MI355X peak"
 
 
-# Sources the headline kernel (register-staged bf16 GQA decode) is built from;
-# a stored HBM-counter reading is used only while these are unchanged.
-HEADLINE_SOURCES = ("pkv_attn_mfma.hip", "pkv_device.h", "pkv_internal.h")
+# The kernel sources each family is built from: a stored HBM-counter reading
+# is used only while these are unchanged.
+COMMON_SOURCES = ("pkv_device.h", "pkv_internal.h")
+FAMILY_SOURCES = {
+    "mla32": ("pkv_attn_mla.hip", "pkv_ring.h"),
+    "m32": ("pkv_attn_m32.hip", "pkv_ring.h"),
+    "dma": ("pkv_attn_dma.hip", "pkv_ring.h"),
+    "generic": ("pkv_attn_generic.hip",),
+    "mfma": ("pkv_attn_mfma.hip",),
+}
 
 
-def _src_hash() -> str:
+def kernel_sources(kernel: str):
+    fam = ("mla32" if kernel.startswith("mla32") else "m32" if kernel.startswith("m32_") else
+           "dma" if kernel.startswith("dma_") else "generic" if kernel == "generic" else "mfma")
+    return FAMILY_SOURCES[fam] + COMMON_SOURCES
+
+
+def _src_hash(kernel: str) -> str:
     h = hashlib.sha256()
-    for name in HEADLINE_SOURCES:
+    for name in kernel_sources(kernel):
         with open(os.path.join(ROOT, "paged_kv_attention_15_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
 def _traffic(workload: str, kernel: str, num_splits: int):
-    """HBM bytes per launch from committed rocprofv3 counter runs, or None when
-    they are missing, were taken on other kernel sources or on another plan."""
+    """HBM bytes per launch of the attention kernel from committed rocprofv3
+    counter runs, or None when they are missing, were taken on other kernel
+    sources or on another plan."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if rec.get("src_hash") != _src_hash() or rec.get("plan") != [kernel, num_splits]:
+    if rec.get("src_hash") != _src_hash(kernel) or rec.get("plan") != [kernel, num_splits]:
         return None
     return rec.get("bytes_per_launch")
 
@@ -271,67 +288,146 @@ def measure(prob, steps: int, warmup: int, num_splits=None):
     return dp, info, wall, ev_mean
 
 
-def cpu_baseline(prob, max_pairs: int):
+def progress(msg: str) -> None:
+    """A progress line on stderr (the JSON result is the only stdout line)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def host_cpu():
+    """The host's CPU model (lscpu, else /proc/cpuinfo) and the cores this
+    process may run on."""
+    import subprocess
+
+    model = None
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        model = next((ln.split(":", 1)[1].strip() for ln in out.splitlines() if ln.startswith("Model name")), None)
+    except Exception:
+        pass
+    if model is None:
+        try:
+            model = next((ln.split(":", 1)[1].strip() for ln in open("/proc/cpuinfo")
+                          if ln.startswith("model name")), None)
+        except OSError:
+            pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count()
+    return {"cpu_model": model, "nproc": usable, "os_cpu_count": os.cpu_count()}
+
+
+def cpu_baseline(prob, target_s: float):
+    """The single-threaded fp64 C oracle on an evenly spaced sample of the
+    workload's (query row, head) pairs, sized from a 16-pair probe to take
+    about `target_s` seconds; reported in the metric's unit (KV GB/s, the
+    sample's share of the KV bytes over its time)."""
     import numpy as np
 
     import oracle
 
     pairs = oracle.all_pairs(prob)
-    if len(pairs) > max_pairs:
-        idx = np.linspace(0, len(pairs) - 1, max_pairs).astype(np.int64)
-        pairs = pairs[idx]
     t0 = time.perf_counter()
-    oracle.attention(prob, pairs)
+    oracle.attention(prob, pairs[np.linspace(0, len(pairs) - 1, 16).astype(np.int64)])
+    per_pair = (time.perf_counter() - t0) / 16
+    n = int(min(len(pairs), max(16, target_s / max(per_pair, 1e-9))))
+    sample = pairs[np.linspace(0, len(pairs) - 1, n).astype(np.int64)]
+    t0 = time.perf_counter()
+    oracle.attention(prob, sample)
     dt = time.perf_counter() - t0
-    frac = len(pairs) / (prob.total_q * prob.num_qo_heads)
+    frac = n / (prob.total_q * prob.num_qo_heads)
     kv_bytes = prob.kv_bytes() * frac  # bytes the sample's rows read, counted like the GPU metric
     return {"value": round(kv_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{len(pairs)} of {prob.total_q * prob.num_qo_heads} (query row, head) pairs of the "
-                      f"same workload, single-threaded fp64 C oracle, {dt:.1f} s"}
+            "sample": f"{n} of {prob.total_q * prob.num_qo_heads} evenly spaced (query row, head) pairs of the "
+                      f"same workload ({prob.name}), single-threaded fp64 C oracle, {dt:.1f} s",
+            **host_cpu()}
 
 
-def secondary_results(steps: int, warmup: int, single_call: bool = True, clock_source=None, only=None):
+# name -> (builder, the roofline that bounds it)
+WORKLOADS = {
+    "mla-b512-kv4096-q1": (lambda W: W.mla_b512_kv4096(q_len=1), "hbm"),
+    "bf16-gqa-b32-kv4096": (lambda W: W.gqa_bf16_b32_kv4096(), "hbm"),
+    "fp8-gqa-b16-ragged": (lambda W: W.gqa_fp8_b16_ragged(), "hbm"),
+    "mla-b512-kv4096-q2": (lambda W: W.mla_b512_kv4096(q_len=2), "mfma"),
+    "ctx-b4-q511-kv2047": (lambda W: W.context_b4_q511_kv2047(), "mfma"),
+    "ctx-b4-q257-kv1024-p1024-sepkv": (lambda W: W.context_b4_q257_kv1024_p1024(separate=True), "mfma"),
+}
+HEADLINE = "mla-b512-kv4096-q1"
+
+
+def roofline(name, prob, info, sec_per_call, bound, timing):
+    """Roofline object of one workload: algorithmic KV bytes (hbm) or flops
+    (mfma) per call over the measured device time per call."""
+    from paged_kv_attention_15_amd import pkv
+
+    kernel = pkv.KERNEL_NAMES[info.kernel]
+    merged = info.num_splits > 1 and not info.fused_merge
+    rec = {"bound": bound}
+    if bound == "hbm":
+        ach = prob.kv_bytes() / sec_per_call / 1e9
+        rec.update(achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s", frac=round(ach / HBM_PEAK_GBS, 4))
+    else:
+        ach = prob.flops() / sec_per_call / 1e12
+        rec.update(achieved=round(ach, 1), peak=BF16_MFMA_PEAK_TFLOPS, unit="TFLOP/s",
+                   frac=round(ach / BF16_MFMA_PEAK_TFLOPS, 4))
+    rec.update(traffic=_traffic(name, kernel, info.num_splits),
+               kernel=f"{kernel} attention kernel" + (" + lse_merge_kernel" if merged else ""), timing=timing)
+    return rec
+
+
+def config_of(name, prob, info):
+    from paged_kv_attention_15_amd import pkv
+
+    q_lens = sorted(set(int(x) for x in (prob.q_indptr[1:] - prob.q_indptr[:-1])))
+    lens = prob.seq_lens
+    return {"workload": name, "batch": prob.batch, "q_len": q_lens[0] if len(q_lens) == 1 else q_lens,
+            "num_qo_heads": prob.num_qo_heads, "num_kv_heads": prob.num_kv_heads, "head_dim_qk": prob.head_dim_qk,
+            "head_dim_v": prob.head_dim_v, "page_size": prob.page_size, "layout": prob.layout,
+            "kv_len": int(lens[0]) if (lens == lens[0]).all() else [int(lens.min()), int(lens.max())],
+            "kv_dtype": prob.kv_dtype, "causal": bool(prob.causal), "mla": bool(prob.mla),
+            "kernel": pkv.KERNEL_NAMES[info.kernel], "num_splits": info.num_splits,
+            "kv_bytes_per_call": prob.kv_bytes(), "flops_per_call": prob.flops()}
+
+
+def run_workload(name, steps: int, warmup: int, single_call: bool = True, clock_source=None, num_splits=None):
+    """Measure one workload: eager back-to-back calls, then the same number of
+    calls replayed from HIP graphs (the reported figure), optional warm/cold
+    single calls.  Returns (record, problem, wall seconds per graph-replayed call)."""
     import torch
 
     from paged_kv_attention_15_amd import pkv, workloads as W
 
-    out = {}
-    cases = [
-        ("fp8-gqa-b16-ragged", lambda: W.gqa_fp8_b16_ragged(), "hbm"),
-        ("mla-b512-kv4096-q1", lambda: W.mla_b512_kv4096(q_len=1), "hbm"),
-        ("mla-b512-kv4096-q2", lambda: W.mla_b512_kv4096(q_len=2), "mfma"),
-        ("ctx-b4-q511-kv2047", lambda: W.context_b4_q511_kv2047(), "mfma"),
-        ("ctx-b4-q257-kv1024-p1024-sepkv", lambda: W.context_b4_q257_kv1024_p1024(separate=True), "mfma"),
-    ]
-    for name, make, bound in cases:
-        if only and name != only:
-            continue
-        prob = make()
-        dp, info, wall, ev_mean = measure(prob, steps, warmup)
-        with ClockSampler(clock_source) as sampler:
-            try:
-                wall, ev_mean = time_graph(dp, steps, warmup)
-            except Exception:  # capture unavailable: keep the eager figures
-                pass
-        gbs = prob.kv_bytes() / ev_mean / 1e9
-        tflops = prob.flops() / ev_mean / 1e12
-        sc = None
-        if single_call:
-            try:
-                sc = single_call_stats(dp, prob.kv_bytes())
-            except Exception as exc:
-                sc = {"error": str(exc)[:200]}
-        rec = {"us_per_call": round(ev_mean * 1e6, 3), "single_call": sc,
-               "kernel": pkv.KERNEL_NAMES[info.kernel], "num_splits": info.num_splits,
-               "fused_merge": int(info.fused_merge),
-               "kv_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
-               "tflops": round(tflops, 2), "mfma_frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
-               "bound": bound, "kv_bytes": prob.kv_bytes(), "flops": prob.flops(),
-               "sclk_during": sampler.summary()}
-        out[name] = rec
-        del dp
-        torch.cuda.empty_cache()
-    return out
+    make, bound = WORKLOADS[name]
+    progress(f"{name}: drawing inputs")
+    prob = make(W)
+    progress(f"{name}: timing")
+    dp, info, wall_e, ev_e = measure(prob, steps, warmup, num_splits)
+    timing = "HIP graphs of 10 back-to-back calls, replayed; one HIP event pair on the launch stream"
+    with ClockSampler(clock_source) as sampler:
+        try:
+            wall, ev = time_graph(dp, steps, warmup)
+        except Exception as exc:  # capture unavailable: the eager figures stand
+            wall, ev = wall_e, ev_e
+            timing = f"back-to-back eager calls (graph capture failed: {str(exc)[:120]}); one HIP event pair"
+    kv = prob.kv_bytes()
+    rec = {"us_per_call": round(ev * 1e6, 3), "config": config_of(name, prob, info),
+           "kv_gbs": round(kv / ev / 1e9, 1), "hbm_frac": round(kv / ev / 1e9 / HBM_PEAK_GBS, 4),
+           "tflops": round(prob.flops() / ev / 1e12, 2),
+           "mfma_frac": round(prob.flops() / ev / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
+           "fused_merge": int(info.fused_merge),
+           "roofline": roofline(name, prob, info, ev, bound, timing),
+           "eager": {"us_per_call": round(ev_e * 1e6, 3), "wall_us_per_call": round(wall_e * 1e6, 3),
+                     "note": "back-to-back calls from the host, no graph"},
+           "sclk_during": sampler.summary()}
+    if single_call:
+        try:
+            rec["single_call"] = single_call_stats(dp, kv)
+        except Exception as exc:
+            rec["single_call"] = {"error": str(exc)[:200]}
+    del dp
+    torch.cuda.empty_cache()
+    progress(f"{name}: {rec['us_per_call']} us per call ({rec['config']['kernel']})")
+    return rec, prob, wall
 
 
 def append_result(steps: int, warmup: int, fp8: bool = False):
@@ -358,9 +454,13 @@ def append_result(steps: int, warmup: int, fp8: bool = False):
         _, ev = time_calls(da, steps, warmup)
         timing = "eager"
     nbytes = prob.bytes_moved()
-    rec = {"us_per_call": round(ev * 1e6, 3), "bytes_per_call": nbytes, "gbs": round(nbytes / ev / 1e9, 1),
-           "hbm_frac": round(nbytes / ev / 1e9 / HBM_PEAK_GBS, 4), "timing": timing,
-           "bound": "latency (1.3 MB per call: one dependent load-compute-store chain per wave)"}
+    gbs = nbytes / ev / 1e9
+    rec = {"us_per_call": round(ev * 1e6, 3), "bytes_per_call": nbytes, "gbs": round(gbs, 1),
+           "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "timing": timing,
+           "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "append_kernel",
+                        "note": "latency-bound, not bandwidth-bound: about 1 MB per call, one dependent "
+                                "load-compute-store chain per wave plus the launch"}}
     del da
     torch.cuda.empty_cache()
     return rec
@@ -377,11 +477,13 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-single-call", action="store_true",
                     help="skip the warm/cold single-call samples (profiling runs: only the timed calls)")
-    ap.add_argument("--cpu-pairs", type=int, default=1024)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target duration of the CPU oracle's bounded sample")
     ap.add_argument("--only", default=None,
-                    help="run only this secondary workload after the headline (profiling runs)")
+                    help="measure only this workload (profiling runs): " + ", ".join(
+                        list(WORKLOADS) + ["append-h64x8-b32-decode", "append-h64x8-b32-decode-e4m3-dynq"]))
     ap.add_argument("--settle", type=float, default=CLOCK_SETTLE_S,
-                    help="seconds of untimed calls before each workload's warm-up (0: none, as in profiling runs)")
+                    help="seconds of untimed calls before each workload's warm-up (0: none)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device-to-device copy (known bytes) to scale HBM counters")
     args = ap.parse_args()
@@ -395,90 +497,67 @@ def main():
 
     import torch
 
-    from paged_kv_attention_15_amd import pkv, workloads as W
+    from paged_kv_attention_15_amd import pkv
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     pkv.load_library()
-    prob = W.gqa_bf16_b32_kv4096()
-    dp, info, wall, ev_mean = measure(prob, args.steps, args.warmup, args.num_splits)
-    kv = prob.kv_bytes()
-    eager = {"us_per_call": round(ev_mean * 1e6, 3), "gbs": round(kv / ev_mean / 1e9, 1),
-             "wall_gbs": round(kv / wall / 1e9, 1), "note": "back-to-back calls from the host, no graph"}
-    # The pages time their kernels as CUDA-graph replays; the calls here are
-    # capturable (kernels only: no allocation, memset or host sync), so the
-    # headline is the same K calls replayed from HIP graphs, eager kept beside it.
-    timing = "HIP graphs of 10 back-to-back calls, replayed; one HIP event pair on the launch stream"
     try:
         clocks = gpu_clocks()
     except Exception as exc:  # no sysfs view of the device: report why
         clocks = {"error": str(exc)[:120]}
-    with ClockSampler(clocks.get("sclk_source")) as sampler:
-        try:
-            wall, ev_mean = time_graph(dp, args.steps, args.warmup)
-        except Exception as exc:  # capture unavailable: the eager figures are the headline
-            timing = f"back-to-back eager calls (graph capture failed: {str(exc)[:120]}); one HIP event pair"
-    value = kv / wall / 1e9
-    achieved = kv / ev_mean / 1e9
-    during = sampler.summary()
-    if during is not None:
-        clocks["during_timed_calls"] = during
-        if clocks.get("sclk_max_mhz"):
-            clocks["sclk_below_70pct_of_max"] = during["sclk_mhz_median"] < 0.7 * clocks["sclk_max_mhz"]
-    single_kernel = info.num_splits == 1
-    line = {
-        "metric": METRIC,
-        "value": round(value, 1),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(wall * 1e3, 5),
-        "us_per_call": round(ev_mean * 1e6, 3),
-        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": "bf16-gqa-b32-kv4096", "batch": 32, "q_len": 1, "num_qo_heads": 32,
-                   "num_kv_heads": 8, "head_dim": 128, "page_size": 32, "kv_len": 4096, "layout": "HND",
-                   "kv_dtype": "bf16", "kernel": pkv.KERNEL_NAMES[info.kernel], "num_splits": info.num_splits,
-                   "kv_bytes_per_call": kv},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": _traffic("bf16-gqa-b32-kv4096", pkv.KERNEL_NAMES[info.kernel], info.num_splits),
-                     "kernel": f"{pkv.KERNEL_NAMES[info.kernel]} attention kernel" + ("" if single_kernel else " + lse_merge_kernel"),
-                     "timing": timing},
-        "eager": eager,
-        "clocks": clocks,
-        "clock_settle_s": CLOCK_SETTLE_S,
-    }
-    if not args.no_single_call:
-        try:
-            line["single_call"] = single_call_stats(dp, kv)
-        except Exception as exc:
-            line["single_call"] = {"error": str(exc)[:200]}
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(prob, args.cpu_pairs)
-    del dp
-    torch.cuda.empty_cache()
+    src = clocks.get("sclk_source")
+    sec_steps, sec_warm = max(20, args.steps // 4), max(5, args.warmup // 2)
+    line = {"metric": METRIC, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "data": "synthetic"}
+    if args.only is None or args.only == HEADLINE:
+        rec, prob, wall = run_workload(HEADLINE, args.steps, args.warmup, not args.no_single_call, src,
+                                       args.num_splits)
+        kv = prob.kv_bytes()
+        value = kv / wall / 1e9
+        if rec["sclk_during"] is not None:
+            clocks["during_timed_calls"] = rec["sclk_during"]
+            if clocks.get("sclk_max_mhz"):
+                clocks["sclk_below_70pct_of_max"] = rec["sclk_during"]["sclk_mhz_median"] < 0.7 * clocks["sclk_max_mhz"]
+        line.update({
+            "value": round(value, 1),
+            "unit": "GB/s",
+            "ms_per_step": round(wall * 1e3, 5),
+            "us_per_call": rec["us_per_call"],
+            "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+            "dtype": "bf16",
+            "config": rec["config"],
+            "roofline": rec["roofline"],
+            "tflops": rec["tflops"],
+            "mfma_frac": rec["mfma_frac"],
+            "eager": rec["eager"],
+        })
+        if "single_call" in rec:
+            line["single_call"] = rec["single_call"]
+        if not args.no_cpu_baseline:
+            progress("CPU oracle baseline")
+            line["cpu_baseline"] = cpu_baseline(prob, args.cpu_seconds)
+        del prob
+    line["clocks"] = clocks
+    line["clock_settle_s"] = CLOCK_SETTLE_S
     if args.calibrate_copy:
-        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
-        dst = torch.empty_like(src)
+        src_t = torch.ones(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
+        dst_t = torch.empty_like(src_t)
         for _ in range(3):
-            dst.copy_(src)
+            dst_t.copy_(src_t)
         torch.cuda.synchronize()
-        line["calibration_copy_bytes"] = src.numel() * 4
-        del src, dst
+        line["calibration_copy_bytes"] = src_t.numel() * 4
+        del src_t, dst_t
         torch.cuda.empty_cache()
     if not args.no_secondary:
-        line["secondary"] = secondary_results(max(20, args.steps // 4), max(5, args.warmup // 2),
-                                              not args.no_single_call, clocks.get("sclk_source"), args.only)
-        if not args.only or args.only == "append-h64x8-b32-decode":
-            line["secondary"]["append-h64x8-b32-decode"] = append_result(max(20, args.steps // 4),
-                                                                         max(5, args.warmup // 2))
-        if not args.only or args.only == "append-h64x8-b32-decode-e4m3-dynq":
-            line["secondary"]["append-h64x8-b32-decode-e4m3-dynq"] = append_result(
-                max(20, args.steps // 4), max(5, args.warmup // 2), fp8=True)
+        sec = {}
+        for name in WORKLOADS:
+            if name == HEADLINE or (args.only and name != args.only):
+                continue
+            sec[name], _, _ = run_workload(name, sec_steps, sec_warm, not args.no_single_call, src)
+        for name, fp8 in (("append-h64x8-b32-decode", False), ("append-h64x8-b32-decode-e4m3-dynq", True)):
+            if not args.only or args.only == name:
+                sec[name] = append_result(sec_steps, sec_warm, fp8=fp8)
+        line["secondary"] = sec
     print(json.dumps(line), flush=True)
 
 
