@@ -215,7 +215,16 @@ const char* pkv_last_error(void);
  */
 pkv_status pkv_plan(const pkv_args* args, int is_context, int num_cus, pkv_plan_info* info);
 
-/* Workspace bytes pkv_decode / pkv_context need for these arguments (0 if unsplit). */
+/*
+ * Workspace bytes pkv_decode / pkv_context need for these arguments (0 if
+ * unsplit).  The caller owns the workspace and sizes it with this query, and
+ * no call path allocates device memory: the caller-owned-workspace item of
+ * the DeepSeek-V4 hardening summary (#5591) on the PR #4557 page.  The plan
+ * behind the size is made for the compute-unit count of the CURRENT device
+ * (hipGetDevice at the time of the call), the same count pkv_decode and
+ * pkv_context plan with, so query and call on the same device.  pkv_plan's
+ * num_cus argument serves host-side inspection of other counts.
+ */
 pkv_status pkv_workspace_bytes(const pkv_args* args, int is_context, size_t* bytes);
 
 /*

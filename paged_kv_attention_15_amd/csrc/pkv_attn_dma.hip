@@ -679,20 +679,21 @@ __device__ __forceinline__ void merge_unit(const KParams& p, const int* s_slot, 
 template <class C>
 __device__ __forceinline__ void stream_arrive(const KParams& p, unsigned char* smem, int* s_flag,
                                               const StreamUnit& su) {
-  // The partial rows were written with device-coherent stores; once every
-  // thread has waited for its stores to complete they are visible device-wide,
-  // without writing back or invalidating any L2 (which would stall every
-  // workgroup of the XCD).  The counter update and the reads below are
-  // device-coherent too.
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  // Arrival: every thread releases its partial-row stores at agent scope,
+  // the workgroup barrier orders them before thread 0's counter increment
+  // (acquire-release at agent scope), and the last arriver's threads acquire
+  // at agent scope before reading the other owners' rows.  The rows are
+  // written and read with device-coherent accesses as well.
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
   __syncthreads();
   const int n = su.count();
   if (threadIdx.x == 0) {
-    const int old = __hip_atomic_fetch_add(p.counters + su.u, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int old = __hip_atomic_fetch_add(p.counters + su.u, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
     *s_flag = (old + 1 == n);
   }
   __syncthreads();
   if (!*s_flag) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 
   // owner slots into LDS (the ring is idle here; the planner keeps n words within it)
   int* s_slot = (int*)smem;

@@ -24,9 +24,10 @@
 //     sixteen rows one ds_read_b128 serves, and the four rows of each half of a
 //     transposed V read, over all 64 banks (odd rows of 1152 bytes start half
 //     a bank row later), the rope chunks a 3-bit key;
-//   * the PV product of block j-1 runs on the matrix core while the softmax of
-//     block j runs on the vector unit (one scheduling region), then the S^T
-//     product of block j+1; the running maximum moves only on jumps of more
+//   * one MFMA sequence per block carries two independent products, the S^T
+//     product of block j+1 and the PV product of block j, step by step, so
+//     each one's LDS operand reads have twice as long to arrive; the softmax
+//     of block j+1 follows; the running maximum moves only on jumps of more
 //     than 8 (log2 units), so O is rescaled rarely.
 // Paging follows the flashinfer.cake_fmha API page's contract (key j of
 // request b is token j % P of page block_tables[b][j / P]); Split-KV partials
@@ -72,6 +73,9 @@ constexpr int LDS = NS * STAGE;   // 144 KiB
 #endif
 #ifndef PKV_MLA_SACC
 #define PKV_MLA_SACC 1
+#endif
+#ifndef PKV_MLA_ORDER
+#define PKV_MLA_ORDER 2  // 2: S^T and PV streams interleaved; 0: PV with the softmax interleaved
 #endif
 constexpr int PDK = PKV_MLA_PD;   // K operand reads issued this many MFMAs ahead
 constexpr int PDV = PKV_MLA_PDV;  // V^T operand reads issued this many MFMAs ahead
@@ -650,10 +654,77 @@ __global__ __launch_bounds__(mla::NTHR, 1) void attn_mla32_kernel(const KParams 
       pb_prev[1] = pb_cur[1];
     };
     const int j_full = max(1, min(nblk, (c_lo - kv_lo) / BK));  // blocks below j_full need no mask
+    if (PKV_MLA_ORDER == 2) {
+      // Two streams on the matrix core: step j runs the S^T product of block
+      // j+1 and the PV product of block j in one sequence, MFMA by MFMA, so
+      // each stream's LDS operand reads get twice as long to arrive; then the
+      // softmax of block j+1 and the rescale.  S^T steps come at slots
+      // 17 i / 9 (36 of 68), so the product ends on PV steps.
+      auto dual_product = [&](int jS, int jP, const bf16x8 (&pb)[2]) {
+        const KGeo kg = k_geo(jS);
+        const VGeo vg = v_geo(jP);
+        constexpr int NV = 2 * NDB;
+        bf16x8 kr[PDK], vr[PDV];
+#pragma unroll
+        for (int q = 0; q < PDK; ++q) kr[q] = k_read(kg, q);
+#pragma unroll
+        for (int q = 0; q < PDV; ++q) vr[q] = v_read(vg, 2 * (q % NDB) + q / NDB);
+        static_for<0, NKS + NV>([&](auto slot) {
+          constexpr int t = decltype(slot)::value;
+          // S^T step ks sits at slot floor(17 ks / 9); the others are PV steps
+          constexpr int ks_here = (9 * t + 16) / 17;  // first ks with slot(ks) >= t
+          constexpr bool is_s = ks_here < NKS && (17 * ks_here) / 9 == t;
+          constexpr int n_s_before = ks_here < NKS ? ks_here : NKS;  // S steps at slots < t
+          if constexpr (is_s) {
+            constexpr int ks = ks_here;
+            const bf16x8 a = kr[ks % PDK];
+            if (ks + PDK < NKS) kr[ks % PDK] = k_read(kg, ks + PDK);
+            if (ks == 0) mfma_s_first(acc, a, qB[ks]);
+            else if (ks == NKS - 1) mfma_s_last(acc, a, qB[ks]);
+            else mfma_s(acc, a, qB[ks]);
+          } else {
+            constexpr int i = t - n_s_before;
+            constexpr int st = i / NDB, db = i % NDB;
+            const bf16x8 a = vr[i % PDV];
+            if (i + PDV < NV) vr[i % PDV] = v_read(vg, 2 * ((i + PDV) % NDB) + (i + PDV) / NDB);
+            if (i == 0 || i == NDB) mfma_o<true>(O[db], a, pb[st]);
+            else mfma_o<false>(O[db], a, pb[st]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        });
+      };
+      auto softmax_block = [&](int j) {
+        float m_use = 0.f, alpha = 1.f;
+        bool moved = false;
+        if (full_block(j)) {
+          softmax_max(std::true_type{}, j, acc, m_use, alpha, moved);
+          softmax_exp(std::true_type{}, acc, m_use, alpha, pb_cur);
+        } else {
+          softmax_max(std::false_type{}, j, acc, m_use, alpha, moved);
+          softmax_exp(std::false_type{}, acc, m_use, alpha, pb_cur);
+        }
+        rescale(moved, alpha);
+      };
+      // block 0: its S^T ran above; every later block is computed even where
+      // it holds no key a row of this wave sees (the masked softmax then
+      // weighs it zero), so the loop has one product call site
+      if (nblk > 0) softmax_block(0);
+      for (int j = 0; j + 1 < nblk; ++j) {
+        pb_prev[0] = pb_cur[0];
+        pb_prev[1] = pb_cur[1];
+        wait_block(min(1, nblk - 2 - j));
+        ring_barrier();  // block j+1 landed; every wave finished reading block j-1's stage
+        if (j + NS - 1 < nblk) issue(j + NS - 1, (j + NS - 1) % NS);  // into block j-1's stage
+        dual_product(j + 1, j, pb_prev);
+        softmax_block(j + 1);
+      }
+      if (nblk > 0) pv_product(nblk - 1, pb_cur, true, no_work);
+    } else {
     if (nblk > 0) step_plain(0);
     for (int j = 1; j < j_full; ++j) step_fused(j);
     for (int j = j_full; j < nblk; ++j) step_plain(j);
     if (nblk > 0 && active(nblk - 1)) pv_product(nblk - 1, pb_prev, true, no_work);
+    }
   }
   o_fence<16>(O);  // the last MFMAs' outputs before the epilogue reads them
 

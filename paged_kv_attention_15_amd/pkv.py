@@ -13,7 +13,8 @@ from dataclasses import dataclass
 from typing import Optional
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libpkv.so")
+# the in-tree build, unless PKV_LIBRARY_PATH names another build of the same sources
+LIB_PATH = os.environ.get("PKV_LIBRARY_PATH") or os.path.join(HERE, "libpkv.so")
 
 PKV_OK, PKV_ERR_INVALID_ARG, PKV_ERR_UNSUPPORTED, PKV_ERR_WORKSPACE, PKV_ERR_HIP = range(5)
 PKV_DTYPE_F32, PKV_DTYPE_BF16, PKV_DTYPE_FP8_E4M3 = range(3)
