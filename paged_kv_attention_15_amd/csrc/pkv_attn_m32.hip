@@ -164,6 +164,14 @@ constexpr int kPageRegs = kM32MaxPages / 64;
 // Largest rise of a row's max (log2 units) absorbed without rescaling O
 constexpr float kLazyMax = 8.f;
 
+// Row sums: 1 = fp32 sums of the weights on the vector unit (each lane sums
+// its 16 weights of a block; the two lanes of a row are added at the end);
+// 0 = an all-ones A operand on the matrix core against the P^T operand
+#ifndef PKV_M32_VALU_SUMS
+#define PKV_M32_VALU_SUMS 1
+#endif
+constexpr bool kValuSums = PKV_M32_VALU_SUMS != 0;
+
 // A row r of S^T reads key r with bits 2 and 3 exchanged
 __device__ __forceinline__ int m32_perm(int r) { return (r & 0x13) | ((r & 4) << 1) | ((r & 8) >> 1); }
 
@@ -281,9 +289,10 @@ __device__ __forceinline__ void m32_block(const KParams& p, unsigned char* smem,
   c_lo = __builtin_amdgcn_readfirstlane(-wave_max_i(-c_lo));  // wave-uniform: scalar branches below
   c_hi = __builtin_amdgcn_readfirstlane(wave_max_i(c_hi));
 
-  // Row sums come from the matrix core: an all-ones A operand against the P^T
-  // operand of the PV product sums the bf16 weights actually used for O (every
-  // element of Lsum[rb] in a lane holds the sum of that lane's query row).
+  // Row sums: lane-partial fp32 sums of the weights in l_run (kValuSums), or
+  // from the matrix core, where an all-ones A operand against the P^T operand
+  // of the PV product sums the bf16 weights used for O (every element of
+  // Lsum[rb] in a lane then holds the sum of that lane's query row).
   float m_run[C::RB], l_run[C::RB];
   f32x16 O[C::RB][C::NDB];
   f32x16 Lsum[C::RB];
@@ -483,9 +492,9 @@ __device__ __forceinline__ void m32_block(const KParams& p, unsigned char* smem,
       const bool move = mx > m_run[rb] + kLazyMax;  // also true on a row's first visible key
       const float m_new = move ? mx : m_run[rb];
       const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = move ? fast_exp2(m_run[rb] - m_use) : 1.f;
       if (__builtin_amdgcn_ballot_w64(move) != 0) {
-        const float alpha = move ? fast_exp2(m_run[rb] - m_use) : 1.f;
-        Lsum[rb] *= alpha;
+        if constexpr (!kValuSums) Lsum[rb] *= alpha;
 #pragma unroll
         for (int d = 0; d < C::NDB; ++d) O[rb][d] *= alpha;
       }
@@ -496,6 +505,12 @@ __device__ __forceinline__ void m32_block(const KParams& p, unsigned char* smem,
       } else {
 #pragma unroll
         for (int e = 0; e < 16; ++e) w[e] = fast_exp2(w[e] - m_use);
+      }
+      if constexpr (kValuSums) {
+        float ls = w[0];
+#pragma unroll
+        for (int e = 1; e < 16; ++e) ls += w[e];
+        l_run[rb] = fmaf(l_run[rb], alpha, ls);
       }
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
@@ -561,6 +576,7 @@ __device__ __forceinline__ void m32_block(const KParams& p, unsigned char* smem,
     }
   };
   auto row_sums = [&](const bf16x8 (&pb)[C::RB][2]) {
+    if constexpr (kValuSums) return;
 #pragma unroll
     for (int st = 0; st < 2; ++st)
 #pragma unroll
@@ -812,9 +828,15 @@ __device__ __forceinline__ void m32_block(const KParams& p, unsigned char* smem,
       }
       __builtin_amdgcn_sched_barrier(0);
       if (__builtin_amdgcn_ballot_w64(mv[0]) != 0) {
-        Lsum[0] *= alpha[0];
+        if constexpr (!kValuSums) Lsum[0] *= alpha[0];
 #pragma unroll
         for (int d = 0; d < C::NDB; ++d) O[0][d] *= alpha[0];
+      }
+      if constexpr (kValuSums) {
+        float ls = w[0][0];
+#pragma unroll
+        for (int e = 1; e < 16; ++e) ls += w[0][e];
+        l_run[0] = fmaf(l_run[0], alpha[0], ls);
       }
       pv_product_ring(j, pb);
     };
@@ -855,7 +877,7 @@ __device__ __forceinline__ void m32_block(const KParams& p, unsigned char* smem,
 
   // ---- full row sums
 #pragma unroll
-  for (int rb = 0; rb < C::RB; ++rb) l_run[rb] = Lsum[rb][0];
+  for (int rb = 0; rb < C::RB; ++rb) l_run[rb] = kValuSums ? half_swap_sum(l_run[rb]) : Lsum[rb][0];
 
   // ---- epilogue: element e of O[rb][db] is value 32db + 8(e/4) + 4h + e%4 of row c32
   const bool split_mode = p.ws_o != nullptr;
