@@ -176,18 +176,18 @@ bool mfma_eligible(const pkv_args* a) {
 bool kernel_supports(int32_t k, const pkv_args* a, bool is_context) {
   if (k == pkv::KERNEL_GENERIC) return a->head_dim_qk <= 1024 && a->head_dim_v <= 512;
   if (k <= pkv::KERNEL_GENERIC || k >= pkv::KERNEL_COUNT || !mfma_eligible(a)) return false;
-  // separate V tables: the register-staged and 32x32 families keep a second
-  // page list; the direct-to-LDS ring families do not
-  if (a->v_block_tables && (k >= pkv::KERNEL_DMA_GQA_BF16 && k <= pkv::KERNEL_DMA_GQA_BF16_S2)) return false;
-  if (a->v_block_tables && (k >= pkv::KERNEL_DMA_GQA_FP8_N2 && k <= pkv::KERNEL_DMA_GQA_FP8_N2S3)) return false;
-  if (a->v_block_tables && (k == pkv::KERNEL_M32_MLA_BF16 || k == pkv::KERNEL_MLA_BF16 || k == pkv::KERNEL_MLA_FP8 ||
-                            k == pkv::KERNEL_MLA32_BF16 || k == pkv::KERNEL_MLA32_SEQ_BF16))
+  // separate V tables: the register-staged families and the 32x32 context
+  // kernel keep a second page list; the direct-to-LDS ring families and the
+  // MLA kernels (whose V rows are the K rows) do not
+  pkv::MfmaShape ring;
+  const bool ring_family = pkv::dma_shape(k, &ring);
+  if (a->v_block_tables &&
+      (ring_family || k == pkv::KERNEL_MLA_BF16 || k == pkv::KERNEL_MLA_FP8 || k == pkv::KERNEL_MLA32_BF16))
     return false;
   // the direct-to-LDS ring loaders form a page's address as a 64-bit base
   // plus a 32-bit product and offset: pages of 4 GiB or more go elsewhere
-  pkv::MfmaShape ring;
   const int64_t eb = elem_bytes(a->kv_dtype);
-  if (pkv::dma_shape(k, &ring) &&
+  if (ring_family &&
       (a->k_stride_page * eb > (int64_t)UINT32_MAX || (!a->v_shares_k && a->v_stride_page * eb > (int64_t)UINT32_MAX)))
     return false;
   const bool fp8 = a->kv_dtype == PKV_DTYPE_FP8_E4M3;
@@ -195,90 +195,39 @@ bool kernel_supports(int32_t k, const pkv_args* a, bool is_context) {
   const bool d128 = a->head_dim_qk == 128 && a->head_dim_v == 128 && !a->v_shares_k;
   const bool mla = a->head_dim_qk == 576 && a->head_dim_v == 512 && a->v_shares_k;
   switch (k) {
-    case pkv::KERNEL_GQA_BF16:
-    case pkv::KERNEL_GQA_BF16_T256:
-    case pkv::KERNEL_GQA_BF16_S1:
-    case pkv::KERNEL_GQA_BF16_W2:
-      return d128 && !fp8 && !is_context && (int64_t)a->q_len * G <= 16;
+    case pkv::KERNEL_GQA_BF16: return d128 && !fp8 && !is_context && (int64_t)a->q_len * G <= 16;
     case pkv::KERNEL_GQA_FP8:
-    case pkv::KERNEL_GQA_FP8_T128:
-    case pkv::KERNEL_GQA_FP8_S2:
-      return d128 && fp8 && !is_context && (int64_t)a->q_len * G <= 16;
+    case pkv::KERNEL_DMA_GQA_FP8_N2: return d128 && fp8 && !is_context && (int64_t)a->q_len * G <= 16;
     case pkv::KERNEL_WIDE_BF16: return d128 && !fp8;
     case pkv::KERNEL_WIDE_FP8: return d128 && fp8;
     case pkv::KERNEL_MLA_BF16: return mla && !fp8;
     case pkv::KERNEL_MLA_FP8: return mla && fp8;
-    case pkv::KERNEL_DMA_GQA_BF16:
-    case pkv::KERNEL_DMA_GQA_BF16_W4:
-    case pkv::KERNEL_DMA_GQA_BF16_S2:
-    case pkv::KERNEL_DMA_GQA_BF16_N2:
-      return d128 && !fp8 && !is_context && (int64_t)a->q_len * G <= 16;
-    case pkv::KERNEL_DMA_GQA_FP8:
-    case pkv::KERNEL_DMA_GQA_FP8_W8:
-    case pkv::KERNEL_DMA_GQA_FP8_S2:
-    case pkv::KERNEL_DMA_GQA_FP8_N2:
-    case pkv::KERNEL_DMA_GQA_FP8_N1:
-    case pkv::KERNEL_DMA_GQA_FP8_N2S3:
-      return d128 && fp8 && !is_context && (int64_t)a->q_len * G <= 16;
     case pkv::KERNEL_DMA_WIDE_BF16: return d128 && !fp8;
     case pkv::KERNEL_DMA_WIDE_FP8: return d128 && fp8;
     case pkv::KERNEL_DMA_MLA_BF16: return mla && !fp8;
     case pkv::KERNEL_DMA_MLA_FP8: return mla && fp8;
-    // the 32x32 family loads each wave-instruction from one page: four rows
-    // per instruction for D = 128, a whole 32-key tile for the latent rows
-    case pkv::KERNEL_M32_CTX_BF16:
-    case pkv::KERNEL_M32_CTX_W8:
-    case pkv::KERNEL_M32_CTX_R1:
-    case pkv::KERNEL_M32_CTX_R1S3:
-    case pkv::KERNEL_M32_CTX_R2:
-    case pkv::KERNEL_M32_CTX_R2W8:
-    case pkv::KERNEL_M32_CTX_PP:
-    case pkv::KERNEL_M32_CTX_IW:
-    case pkv::KERNEL_M32_CTX_W8T128:
-      return d128 && !fp8 && a->page_size >= 4;
-    case pkv::KERNEL_M32_MLA_BF16: return mla && !fp8 && a->page_size % 32 == 0;
+    // the 32x32 context kernel loads four rows per wave-instruction from one page
+    case pkv::KERNEL_M32_CTX_W8T128: return d128 && !fp8 && a->page_size >= 4;
     // 32-key blocks inside one page: pages of a multiple of 32 tokens
-    case pkv::KERNEL_MLA32_BF16:
-    case pkv::KERNEL_MLA32_SEQ_BF16: return mla && !fp8 && a->page_size % 32 == 0;
+    case pkv::KERNEL_MLA32_BF16: return mla && !fp8 && a->page_size % 32 == 0;
   }
   return false;
-}
-
-// the 32x32 MFMA family (pkv_attn_m32.hip): page lists held in registers
-bool is_m32(int32_t k) {
-  return (k >= pkv::KERNEL_M32_CTX_BF16 && k <= pkv::KERNEL_M32_CTX_PP) || k == pkv::KERNEL_M32_CTX_IW ||
-         k == pkv::KERNEL_M32_CTX_W8T128;
 }
 
 // families that hold a partition's page list in registers (kM32MaxPages pages at most)
-bool page_list_in_registers(int32_t k) {
-  return is_m32(k) || k == pkv::KERNEL_MLA32_BF16 || k == pkv::KERNEL_MLA32_SEQ_BF16;
+bool page_list_in_registers(int32_t k) { return k == pkv::KERNEL_M32_CTX_W8T128 || k == pkv::KERNEL_MLA32_BF16; }
+
+bool is_m32(int32_t k) { return k == pkv::KERNEL_M32_CTX_W8T128; }
+// the direct-to-LDS ring families (pkv_attn_dma.hip)
+bool is_ring(int32_t k) {
+  pkv::MfmaShape sh;
+  return pkv::dma_shape(k, &sh);
 }
+bool is_mla32(int32_t k) { return k == pkv::KERNEL_MLA32_BF16; }
 
-bool is_mla32(int32_t k) { return k == pkv::KERNEL_MLA32_BF16 || k == pkv::KERNEL_MLA32_SEQ_BF16; }
-
+// families with a balanced decode schedule (rows of a KV head in one block)
 bool is_gqa_family(int32_t k) {
-  switch (k) {
-    case pkv::KERNEL_GQA_BF16:
-    case pkv::KERNEL_GQA_FP8:
-    case pkv::KERNEL_GQA_BF16_T256:
-    case pkv::KERNEL_GQA_BF16_S1:
-    case pkv::KERNEL_GQA_FP8_T128:
-    case pkv::KERNEL_GQA_BF16_W2:
-    case pkv::KERNEL_GQA_FP8_S2:
-    case pkv::KERNEL_DMA_GQA_BF16:
-    case pkv::KERNEL_DMA_GQA_FP8:
-    case pkv::KERNEL_DMA_GQA_FP8_W8:
-    case pkv::KERNEL_DMA_GQA_FP8_S2:
-    case pkv::KERNEL_DMA_GQA_BF16_W4:
-    case pkv::KERNEL_DMA_GQA_BF16_S2:
-    case pkv::KERNEL_DMA_GQA_FP8_N2:
-    case pkv::KERNEL_DMA_GQA_BF16_N2:
-    case pkv::KERNEL_DMA_GQA_FP8_N1:
-    case pkv::KERNEL_DMA_GQA_FP8_N2S3:
-      return true;
-  }
-  return false;
+  return k == pkv::KERNEL_GQA_BF16 || k == pkv::KERNEL_GQA_FP8 || k == pkv::KERNEL_DMA_GQA_FP8_N2;
 }
 
 bool kernel_shape(int32_t k, pkv::MfmaShape* s) {
@@ -412,7 +361,7 @@ pkv_status make_plan(const pkv_args* a, bool is_context, int num_cus, pkv_plan_i
       // a unit has at most min(W, max_pages_per_seq) owners.
       const int64_t owners = std::min<int64_t>(W, std::max<int64_t>(a->max_pages_per_seq, 1));
       const bool fits = owners <= (int64_t)shp.lds_static / 4;
-      info->fused_merge = a->merge_counters != nullptr && kernel >= pkv::KERNEL_DMA_GQA_BF16 && fits;
+      info->fused_merge = a->merge_counters != nullptr && is_ring(kernel) && fits;
       info->num_splits = (int32_t)(W + U);
       info->pages_per_split = 0;
       info->grid_x = (int32_t)W;
@@ -586,7 +535,7 @@ pkv_status run(const pkv_args* a, bool is_context, void* ws, size_t ws_bytes, vo
   hipError_t e = plan.kernel == pkv::KERNEL_GENERIC         ? pkv::launch_generic(p, s)
                  : is_m32(plan.kernel)                       ? pkv::launch_m32(plan.kernel, p, s)
                  : is_mla32(plan.kernel)                     ? pkv::launch_mla32(plan.kernel, p, s)
-                 : plan.kernel >= pkv::KERNEL_DMA_GQA_BF16   ? pkv::launch_dma(plan.kernel, p, s)
+                 : is_ring(plan.kernel)                      ? pkv::launch_dma(plan.kernel, p, s)
                                                              : pkv::launch_mfma(plan.kernel, p, s);
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "attention launch failed: %s", hipGetErrorString(e));
   if (plan.num_splits > 1 && !plan.fused_merge) {

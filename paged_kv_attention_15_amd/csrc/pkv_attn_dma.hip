@@ -807,15 +807,7 @@ __global__ __launch_bounds__(C::NTHR) void attn_dma_stream_kernel(const KParams 
 
 // ---------------------------------------------------------------- instances
 //                           DQK  DV   FP8    VSH    RT NWR NWT TT  NS
-using DGqaBf16 = DmaCfg<128, 128, false, false, 1, 1, 2, 32, 4>;  // 64-key tiles, 32 KiB stages
-using DGqaFp8 = DmaCfg<128, 128, true, false, 1, 1, 4, 32, 4>;    // 128-key tiles, 32 KiB stages
-using DGqaFp8W8 = DmaCfg<128, 128, true, false, 1, 1, 8, 32, 2>;
-using DGqaFp8S2 = DmaCfg<128, 128, true, false, 1, 1, 4, 32, 2>;
-using DGqaBf16W4 = DmaCfg<128, 128, false, false, 1, 1, 4, 32, 2>;
-using DGqaBf16S2 = DmaCfg<128, 128, false, false, 1, 1, 2, 32, 2>;
 using DGqaFp8N2 = DmaCfg<128, 128, true, false, 1, 1, 2, 32, 2>;
-using DGqaFp8N1 = DmaCfg<128, 128, true, false, 1, 1, 1, 32, 3>;
-using DGqaFp8N2S3 = DmaCfg<128, 128, true, false, 1, 1, 2, 32, 3>;
 using DWideBf16 = DmaCfg<128, 128, false, false, 2, 4, 1, 64, 4>;
 using DWideFp8 = DmaCfg<128, 128, true, false, 2, 4, 1, 64, 4>;
 // MLA: two 72 KiB stages of 64 keys (one workgroup barrier per 64 keys) fit 252
@@ -834,17 +826,8 @@ static void fill_dma_shape(MfmaShape* s, int waves_per_cu = 8) {
 
 bool dma_shape(int32_t kernel, MfmaShape* s) {
   switch (kernel) {
-    case KERNEL_DMA_GQA_BF16: fill_dma_shape<DGqaBf16>(s); return true;
-    case KERNEL_DMA_GQA_FP8: fill_dma_shape<DGqaFp8>(s); return true;
-    case KERNEL_DMA_GQA_FP8_W8: fill_dma_shape<DGqaFp8W8>(s); return true;
-    case KERNEL_DMA_GQA_FP8_S2: fill_dma_shape<DGqaFp8S2>(s); return true;
     // 128-thread groups whose LDS, not registers, limits residency (four per CU)
     case KERNEL_DMA_GQA_FP8_N2: fill_dma_shape<DGqaFp8N2>(s, 16); return true;
-    case KERNEL_DMA_GQA_BF16_N2: fill_dma_shape<DGqaBf16S2>(s, 16); return true;
-    case KERNEL_DMA_GQA_FP8_N1: fill_dma_shape<DGqaFp8N1>(s, 16); return true;
-    case KERNEL_DMA_GQA_FP8_N2S3: fill_dma_shape<DGqaFp8N2S3>(s, 16); return true;
-    case KERNEL_DMA_GQA_BF16_W4: fill_dma_shape<DGqaBf16W4>(s); return true;
-    case KERNEL_DMA_GQA_BF16_S2: fill_dma_shape<DGqaBf16S2>(s); return true;
     case KERNEL_DMA_WIDE_BF16: fill_dma_shape<DWideBf16>(s); return true;
     case KERNEL_DMA_WIDE_FP8: fill_dma_shape<DWideFp8>(s); return true;
     case KERNEL_DMA_MLA_BF16: fill_dma_shape<DMlaBf16>(s); return true;
@@ -878,16 +861,7 @@ static hipError_t launch_dma_cfg(const KParams& p, hipStream_t s) {
 
 hipError_t launch_dma(int32_t kernel, const KParams& p, hipStream_t s) {
   switch (kernel) {
-    case KERNEL_DMA_GQA_BF16: return launch_dma_cfg<DGqaBf16>(p, s);
-    case KERNEL_DMA_GQA_FP8: return launch_dma_cfg<DGqaFp8>(p, s);
-    case KERNEL_DMA_GQA_FP8_W8: return launch_dma_cfg<DGqaFp8W8>(p, s);
-    case KERNEL_DMA_GQA_FP8_S2: return launch_dma_cfg<DGqaFp8S2>(p, s);
     case KERNEL_DMA_GQA_FP8_N2: return launch_dma_cfg<DGqaFp8N2>(p, s);
-    case KERNEL_DMA_GQA_BF16_N2: return launch_dma_cfg<DGqaBf16S2>(p, s);
-    case KERNEL_DMA_GQA_FP8_N1: return launch_dma_cfg<DGqaFp8N1>(p, s);
-    case KERNEL_DMA_GQA_FP8_N2S3: return launch_dma_cfg<DGqaFp8N2S3>(p, s);
-    case KERNEL_DMA_GQA_BF16_W4: return launch_dma_cfg<DGqaBf16W4>(p, s);
-    case KERNEL_DMA_GQA_BF16_S2: return launch_dma_cfg<DGqaBf16S2>(p, s);
     case KERNEL_DMA_WIDE_BF16: return launch_dma_cfg<DWideBf16>(p, s);
     case KERNEL_DMA_WIDE_FP8: return launch_dma_cfg<DWideFp8>(p, s);
     case KERNEL_DMA_MLA_BF16: return launch_dma_cfg<DMlaBf16>(p, s);

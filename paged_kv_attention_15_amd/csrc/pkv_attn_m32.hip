@@ -1,10 +1,11 @@
 // pkv_attn_m32.hip -- paged attention on v_mfma_f32_32x32x16_bf16 for the
-// compute-heavy shapes: causal context over a GQA group and MLA latent decode.
+// compute-heavy context shape: causal context over a GQA group (the MLA
+// latent decode on the same instruction lives in pkv_attn_mla.hip).
 //
 // Measured on gfx950, the 32x32x16 bf16 MFMA sustains one instruction per 32
 // cycles per SIMD from a single wave (the full bf16 matrix rate), while
 // back-to-back 16x16x32 instructions reach about half of it; so the products
-// that dominate these shapes use the 32x32 form.  Both are transposed, putting
+// that dominate this shape use the 32x32 form.  Both are transposed, putting
 // the query rows on the column axis of the MFMA:
 //   S^T[keys x rows] = K[keys x d] Q^T[d x rows]          A = K rows (LDS), B = Q (registers)
 //   O^T[dv x rows]  += V^T[dv x keys] P^T[keys x rows]    A = V^T (LDS transpose reads), B = P
@@ -37,36 +38,17 @@ __device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-template <int DQK_, int DV_, bool VSHARE_, int RB_, int NW_, int KB_, int NS_, int OCC_ = 1, bool PREF_ = true,
-          int DVS_ = 1, bool PP_ = false, bool IW_ = false>
+template <int DQK_, int DV_, bool VSHARE_, int RB_, int NW_, int KB_, int NS_, int OCC_ = 1>
 struct M32Cfg {
-  // IW (interleaved within the wave): the S^T product of block j+1 and the
-  // softmax of block j are one scheduling region, its MFMAs spread among the
-  // softmax's VALU instructions, so each wave overlaps its own matrix and
-  // vector work; the O rescale and the PV product of block j follow
-  static constexpr bool IW = IW_;
-  // PP (ping-pong): waves w and w + NW/2 share a SIMD (measured on gfx950);
-  // the second half runs one phase behind the first, with a workgroup barrier
-  // between phases, so that on every SIMD one wave is in its MFMA phase while
-  // the other is in its LDS-read and softmax phase
-  static constexpr bool PP = PP_;
-  // DVS waves share each group of rows, each accumulating its own 1/DVS of the
-  // value columns (and each computing the whole S^T of those rows): for long
-  // value rows this trades duplicated QK^T work for a smaller O per wave
-  static constexpr int DVS = DVS_;
   static constexpr int DQK = DQK_, DV = DV_, RB = RB_, NW = NW_, KB = KB_, NS = NS_;
   static constexpr int OCC = OCC_;  // waves per SIMD the register budget is sized for
-  // PREF: software-pipeline the blocks, holding the next block's K operands and
-  // this block's V^T operands in registers; otherwise each block reads its
-  // operands as it goes and other waves of the SIMD cover the latency
-  static constexpr bool PREF = PREF_;
-  // read-ahead distance (in MFMA steps) of the K and V^T operand reads when not prefetching;
+  // read-ahead distance (in MFMA steps) of the K and V^T operand reads;
   // shorter for long rows, whose Q and O already fill the register file
   static constexpr int PDK = DQK > 256 ? 3 : 4;
   static constexpr int PDV = DQK > 256 ? 3 : 4;
   static constexpr bool VSHARE = VSHARE_;
   static constexpr int NTHR = 64 * NW;
-  static constexpr int ROWS = NW / DVS * RB * 32;  // packed query rows per workgroup
+  static constexpr int ROWS = NW * RB * 32;  // packed query rows per workgroup
   static constexpr int T = KB * 32;          // keys per ring stage
   static constexpr int KROWB = DQK * 2;
   static constexpr int VROWB = VSHARE ? KROWB : DV * 2;
@@ -80,7 +62,7 @@ struct M32Cfg {
   static constexpr int NI = (KCH + VCH) / 64;  // wave-instructions per stage
   static constexpr int KPW = (NI + NW - 1) / NW;
   static constexpr int NKS = DQK / 16;  // 16-wide k steps of S^T
-  static constexpr int NDB = DV / 32 / DVS;  // 32-wide value blocks of O^T per wave
+  static constexpr int NDB = DV / 32;  // 32-wide value blocks of O^T per wave
   static constexpr int LDS = NS * STAGE;
   // recompute the loader's per-lane geometry every stage instead of keeping it
   // live: long rows, or more than one wave per SIMD (registers are the limit)
@@ -90,11 +72,7 @@ struct M32Cfg {
   static_assert(KPW * (NS - 1) < 64, "vmcnt holds at most 63 outstanding loads");
   static_assert(DQK % 16 == 0 && DV % 32 == 0 && NCK % 4 == 0 && NCV % 4 == 0, "tiling");
   static_assert(NS >= 2 && NS <= 6, "ring depth");
-  static_assert(!PREF || KPW % KB == 0, "ring refill split over the blocks of a tile");
   static_assert(!VSHARE || DV <= DQK, "shared V rows");
-  // a wave's value slice starts on a 16-chunk swizzle group: its reads are the
-  // first slice's shifted by a whole number of groups
-  static_assert(NW % DVS == 0 && (DVS == 1 || (NDB % 4 == 0 && DV * 2 <= (NCV & ~15) * 16)), "value slices");
 };
 
 // Swizzle key of LDS row r (K and V rows alike): 16-byte chunk c of the row is
@@ -123,40 +101,6 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
-// Instruction-scheduler hint for a product whose LDS operand reads and MFMAs
-// sit in one basic block: the reads run PD steps ahead of the MFMAs that use
-// them (R reads and M MFMAs per step), so each MFMA waits for a read issued
-// PD steps earlier instead of one issued just before it.
-template <int PD, int STEPS, int R, int M>
-__device__ __forceinline__ void sched_reads_ahead() {
-  static_for<0, (PD < STEPS ? PD : STEPS)>([] { __builtin_amdgcn_sched_group_barrier(0x100, R, 0); });
-  static_for<0, (PD < STEPS ? STEPS - PD : 0)>([] {
-    __builtin_amdgcn_sched_group_barrier(0x008, M, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
-  });
-  static_for<0, (PD < STEPS ? PD : STEPS)>([] { __builtin_amdgcn_sched_group_barrier(0x008, M, 0); });
-}
-
-// Instruction-scheduler hint for a product of M MFMAs fed by M LDS reads that
-// shares its basic block with independent VALU work: PD reads first, then
-// per MFMA step the MFMA, V VALU instructions and the read PD steps ahead.
-template <int PD, int M, int V, int I = 0>
-__device__ __forceinline__ void sched_interleave() {
-  if constexpr (I == 0) static_for<0, PD>([] { __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); });
-  if constexpr (I < M) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x402, V, 0);
-    if constexpr (I + PD < M) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    sched_interleave<PD, M, V, I + 1>();
-  }
-}
-
-// VALU instructions placed after each MFMA of an interleaved S^T product
-#ifndef PKV_IW_VALU
-#define PKV_IW_VALU 4
-#endif
-constexpr int kIwValu = PKV_IW_VALU;
-
 // Registers per wave holding the page list (64 pages each); the planner caps a
 // partition of these kernels at 64 * kPageRegs pages
 constexpr int kPageRegs = kM32MaxPages / 64;
@@ -164,13 +108,6 @@ constexpr int kPageRegs = kM32MaxPages / 64;
 // Largest rise of a row's max (log2 units) absorbed without rescaling O
 constexpr float kLazyMax = 8.f;
 
-// Row sums: 1 = fp32 sums of the weights on the vector unit (each lane sums
-// its 16 weights of a block; the two lanes of a row are added at the end);
-// 0 = an all-ones A operand on the matrix core against the P^T operand
-#ifndef PKV_M32_VALU_SUMS
-#define PKV_M32_VALU_SUMS 1
-#endif
-constexpr bool kValuSums = PKV_M32_VALU_SUMS != 0;
 
 // A row r of S^T reads key r with bits 2 and 3 exchanged
 __device__ __forceinline__ int m32_perm(int r) { return (r & 0x13) | ((r & 4) << 1) | ((r & 8) >> 1); }
@@ -185,8 +122,7 @@ __device__ __forceinline__ void m32_block(const KParams& p, unsigned char* smem,
   const int h = lane >> 5;   // k half of the operands, row quad of the results
   const int c32 = lane & 31;  // query row inside a 32-row block
   const int G = p.group;
-  const int wr = wave / C::DVS;         // row group of this wave
-  const int dvb0 = (wave % C::DVS) * C::NDB;  // first 32-wide value block of this wave
+  const int wr = wave;  // row group of this wave
 
   __syncthreads();  // LDS of a previous piece is free again (no loads are in flight here)
 
@@ -289,15 +225,10 @@ __device__ __forceinline__ void m32_block(const KParams& p, unsigned char* smem,
   c_lo = __builtin_amdgcn_readfirstlane(-wave_max_i(-c_lo));  // wave-uniform: scalar branches below
   c_hi = __builtin_amdgcn_readfirstlane(wave_max_i(c_hi));
 
-  // Row sums: lane-partial fp32 sums of the weights in l_run (kValuSums), or
-  // from the matrix core, where an all-ones A operand against the P^T operand
-  // of the PV product sums the bf16 weights used for O (every element of
-  // Lsum[rb] in a lane then holds the sum of that lane's query row).
+  // Row sums: each lane sums its weights of a block in fp32 (l_run); the two
+  // lanes of a row are added at the end.
   float m_run[C::RB], l_run[C::RB];
   f32x16 O[C::RB][C::NDB];
-  f32x16 Lsum[C::RB];
-  const bf16x8 ones = {(__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f,
-                       (__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f};
 #pragma unroll
   for (int rb = 0; rb < C::RB; ++rb) {
     m_run[rb] = -INFINITY;
@@ -306,8 +237,6 @@ __device__ __forceinline__ void m32_block(const KParams& p, unsigned char* smem,
     for (int d = 0; d < C::NDB; ++d)
 #pragma unroll
       for (int e = 0; e < 16; ++e) O[rb][d][e] = 0.f;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) Lsum[rb][e] = 0.f;
   }
 
   __syncthreads();  // page list visible
@@ -426,41 +355,9 @@ __device__ __forceinline__ void m32_block(const KParams& p, unsigned char* smem,
   const int vrow = 8 * (vq >> 1) + (vj >> 2);
   const int vfk = m32_key(vrow);
   const int vc_lane = 2 * (vq & 1) + ((vj & 3) >> 1);
-  const int vl_row = vrow * C::VROWB + 8 * (vj & 1) + 64 * dvb0;
+  const int vl_row = vrow * C::VROWB + 8 * (vj & 1);
 
   // ---- the pieces of one 32-key block
-  auto k_operands = [&](int j, bf16x8 (&ka)[C::NKS]) {
-    const unsigned char* kblk = smem + ((j / C::KB) % C::NS) * C::STAGE + (j % C::KB) * 32 * C::KROWB + kl_row;
-#pragma unroll
-    for (int ks = 0; ks < C::NKS; ++ks) ka[ks] = *(const bf16x8*)(kblk + chunk_phys<C::NCK>(2 * ks, h, kfk) * 16);
-  };
-  auto s_product = [&](const bf16x8 (&ka)[C::NKS], f32x16 (&acc)[C::RB]) {
-#pragma unroll
-    for (int rb = 0; rb < C::RB; ++rb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[rb][e] = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < C::NKS; ++ks)
-#pragma unroll
-      for (int rb = 0; rb < C::RB; ++rb) acc[rb] = mfma32x32x16(ka[ks], qB[rb][ks], acc[rb]);
-  };
-  // V^T operand of value block db, 16-key step st: two transpose reads of four keys each
-  auto v_operands = [&](int j, bf16x8 (&va)[C::NDB][2]) {
-    const unsigned char* vst = smem + ((j / C::KB) % C::NS) * C::STAGE + (C::VSHARE ? 0 : C::KTILE);
-    const unsigned char* vblk = vst + (j % C::KB) * 32 * C::VROWB + vl_row;
-#pragma unroll
-    for (int db = 0; db < C::NDB; ++db) {
-      const int voff = chunk_phys<C::NCV>(4 * db, vc_lane, vfk) * 16;
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        const unsigned char* src = vblk + 16 * st * C::VROWB + voff;
-        const s16x4 lo = lds_read_tr16(src);
-        const s16x4 hi = lds_read_tr16(src + 4 * C::VROWB);
-        typedef short s16x8 __attribute__((ext_vector_type(8)));
-        va[db][st] = __builtin_bit_cast(bf16x8, s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
-      }
-    }
-  };
   // Online softmax (exp2 domain); element e of acc holds key 16(e/8) + 8h + e%8.
   // The running max only moves when a score exceeds it by more than kLazyMax
   // (log2 units): below that the stale max keeps every weight within
@@ -494,7 +391,6 @@ __device__ __forceinline__ void m32_block(const KParams& p, unsigned char* smem,
       const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
       const float alpha = move ? fast_exp2(m_run[rb] - m_use) : 1.f;
       if (__builtin_amdgcn_ballot_w64(move) != 0) {
-        if constexpr (!kValuSums) Lsum[rb] *= alpha;
 #pragma unroll
         for (int d = 0; d < C::NDB; ++d) O[rb][d] *= alpha;
       }
@@ -506,12 +402,10 @@ __device__ __forceinline__ void m32_block(const KParams& p, unsigned char* smem,
 #pragma unroll
         for (int e = 0; e < 16; ++e) w[e] = fast_exp2(w[e] - m_use);
       }
-      if constexpr (kValuSums) {
-        float ls = w[0];
+      float ls = w[0];
 #pragma unroll
-        for (int e = 1; e < 16; ++e) ls += w[e];
-        l_run[rb] = fmaf(l_run[rb], alpha, ls);
-      }
+      for (int e = 1; e < 16; ++e) ls += w[e];
+      l_run[rb] = fmaf(l_run[rb], alpha, ls);
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
         u32x4 wv{pack_bf16x2(w[8 * st + 0], w[8 * st + 1]), pack_bf16x2(w[8 * st + 2], w[8 * st + 3]),
@@ -519,77 +413,6 @@ __device__ __forceinline__ void m32_block(const KParams& p, unsigned char* smem,
         pb[rb][st] = __builtin_bit_cast(bf16x8, wv);
       }
     }
-  };
-  // The same online softmax in two parts with the O rescale left to the
-  // caller, so that a scheduling region holding the second part has no branch
-  // and no cross-lane operation (the row max needs one).  FULL: no key of the
-  // block is masked for any row of the wave.  Part 1: the row max, the new
-  // reference, alpha and whether any lane moved; part 2: weights and packing.
-  auto softmax_max = [&](auto full_tag, int j, const f32x16 (&acc)[C::RB], float (&w)[C::RB][16],
-                         float (&m_use)[C::RB], float (&alpha)[C::RB], bool (&mv)[C::RB]) {
-    constexpr bool FULL = decltype(full_tag)::value;
-    const int blk_tok = kv_lo + j * 32;
-#pragma unroll
-    for (int rb = 0; rb < C::RB; ++rb) {
-      float mx;
-      if constexpr (FULL) {
-        float mr = acc[rb][0];
-#pragma unroll
-        for (int e = 1; e < 16; ++e) mr = fmaxf(mr, acc[rb][e]);
-        mx = half_swap_max(mr) * sc2;
-      } else {
-        mx = -INFINITY;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int tok = blk_tok + 16 * (e >> 3) + 8 * h + (e & 7);
-          w[rb][e] = tok < row_c[rb] ? acc[rb][e] * sc2 : -INFINITY;
-          mx = fmaxf(mx, w[rb][e]);
-        }
-        mx = half_swap_max(mx);
-      }
-      const bool move = mx > m_run[rb] + kLazyMax;  // also true on a row's first visible key
-      const float m_new = move ? mx : m_run[rb];
-      m_use[rb] = (m_new == -INFINITY) ? 0.f : m_new;
-      alpha[rb] = move ? fast_exp2(m_run[rb] - m_use[rb]) : 1.f;
-      mv[rb] = move;
-      m_run[rb] = m_new;
-    }
-  };
-  auto softmax_exp = [&](auto full_tag, const f32x16 (&acc)[C::RB], float (&w)[C::RB][16],
-                         const float (&m_use)[C::RB], bf16x8 (&pb)[C::RB][2]) {
-    constexpr bool FULL = decltype(full_tag)::value;
-#pragma unroll
-    for (int rb = 0; rb < C::RB; ++rb) {
-      if constexpr (FULL) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) w[rb][e] = fast_exp2(fmaf(acc[rb][e], sc2, -m_use[rb]));
-      } else {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) w[rb][e] = fast_exp2(w[rb][e] - m_use[rb]);
-      }
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        u32x4 wv{pack_bf16x2(w[rb][8 * st + 0], w[rb][8 * st + 1]), pack_bf16x2(w[rb][8 * st + 2], w[rb][8 * st + 3]),
-                 pack_bf16x2(w[rb][8 * st + 4], w[rb][8 * st + 5]), pack_bf16x2(w[rb][8 * st + 6], w[rb][8 * st + 7])};
-        pb[rb][st] = __builtin_bit_cast(bf16x8, wv);
-      }
-    }
-  };
-  auto row_sums = [&](const bf16x8 (&pb)[C::RB][2]) {
-    if constexpr (kValuSums) return;
-#pragma unroll
-    for (int st = 0; st < 2; ++st)
-#pragma unroll
-      for (int rb = 0; rb < C::RB; ++rb) Lsum[rb] = mfma32x32x16(ones, pb[rb][st], Lsum[rb]);
-  };
-  auto pv_product = [&](const bf16x8 (&va)[C::NDB][2], const bf16x8 (&pb)[C::RB][2]) {
-    row_sums(pb);
-#pragma unroll
-    for (int db = 0; db < C::NDB; ++db)
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int rb = 0; rb < C::RB; ++rb) O[rb][db] = mfma32x32x16(va[db][st], pb[rb][st], O[rb][db]);
   };
   // Products with their LDS operand reads interleaved: a ring of PD operands
   // in registers, each read issued PD MFMA steps before the MFMA that uses it
@@ -626,7 +449,6 @@ __device__ __forceinline__ void m32_block(const KParams& p, unsigned char* smem,
     };
     constexpr int N = 2 * C::NDB;
     constexpr int PD = C::PDV < N ? C::PDV : N;
-    row_sums(pb);
     bf16x8 ring[PD];
 #pragma unroll
     for (int q = 0; q < PD; ++q) ring[q] = rd(q);
@@ -662,208 +484,20 @@ __device__ __forceinline__ void m32_block(const KParams& p, unsigned char* smem,
     if (issue_now && t + C::NS - 1 < n_tiles) issue(t + C::NS - 1, (t + C::NS - 1) % C::NS);
   };
 
-  // prologue: the first NS-1 tiles in flight (NS-2 for IW, whose PV product
-  // trails the barrier of the next tile by one block)
-  constexpr int PRE = C::IW ? C::NS - 2 : C::NS - 1;
+  // prologue: the first NS-1 tiles in flight
 #pragma unroll
-  for (int t = 0; t < PRE; ++t)
+  for (int t = 0; t < C::NS - 1; ++t)
     if (t < n_tiles) issue(t, t);
 
-  // Software pipeline over 32-key blocks j.  Step j first issues the LDS reads
-  // of the K operands of block j+1 and the V^T operands of block j, runs the
-  // softmax of block j on the VALU while those reads land, and then issues the
-  // S^T product of block j+1 and the PV product of block j back to back on
-  // the matrix core (the other wave of the SIMD fills its VALU meanwhile).  At a
-  // tile boundary the V^T reads of block j come first, so the barrier that
-  // frees block j's stage can be taken before the next tile's K reads.  Blocks
-  // past this wave's last visible key are skipped; every wave still takes
-  // every tile's barrier.
+  // One 32-key block at a time: S^T product (K operands read a few MFMA
+  // steps ahead), softmax, PV product.  The two waves of a SIMD run
+  // independently between the tile barriers, so one's matrix work covers the
+  // other's softmax.  Blocks past this wave's last visible key are skipped;
+  // every wave still takes every tile's barrier.
   const int nblk = n_tiles * C::KB;
-  f32x16 accA[C::RB], accB[C::RB];
+  f32x16 accA[C::RB];
   auto active = [&](int j) { return kv_lo + j * 32 < c_hi; };
-  auto step = [&](int j, f32x16 (&cur)[C::RB], f32x16 (&nxt)[C::RB]) {
-    bf16x8 va[C::NDB][2];
-    bf16x8 ka[C::NKS];
-    const bool act = active(j);
-    const bool act1 = j + 1 < nblk && active(j + 1);
-    if (j + 1 < nblk && (j + 1) % C::KB == 0) {
-      if (act) v_operands(j, va);
-      tile_start((j + 1) / C::KB, false);
-      if (act1) k_operands(j + 1, ka);
-    } else {
-      if (act1) k_operands(j + 1, ka);
-      if (act) v_operands(j, va);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    bf16x8 pb[C::RB][2];
-    if (act) softmax(j, cur, pb);
-    __builtin_amdgcn_sched_barrier(0);
-    // part (j+1) % KB of the ring refill that follows the barrier of tile (j+1) / KB:
-    // the next tile's loads go out a slice per block instead of all at once
-    // after the barrier, when every wave would queue them at the same moment
-    {
-      const int u = (j + 1) / C::KB + C::NS - 1;
-      const int part = (j + 1) % C::KB;
-      if (u < n_tiles) issue(u, u % C::NS, part * C::KPW / C::KB, (part + 1) * C::KPW / C::KB);
-    }
-    if (act1) s_product(ka, nxt);
-    if (act) pv_product(va, pb);
-  };
-  if constexpr (C::PP) {
-    // Slots of the ping-pong.  Phase 2j of a wave (its softmax phase) runs the
-    // softmax of block j on the VALU; phase 2j+1 (its matrix phase) runs the S^T
-    // product of block j+1 and the PV product of block j, their LDS operands
-    // read a few MFMA steps ahead.  The first half of the waves runs phase s in
-    // slot s, the second half in slot s+1; a barrier ends every slot.
-    // Ring: tile t is read from phase 2(t KB - 1) + 1 (the K reads of its first
-    // block; the prologue for t = 0) to phase 2(t KB + KB - 1) + 1 (the V^T reads
-    // of its last block), i.e. up to slot 2(t+1)KB for the lagging half.  So
-    // tile t+NS refills its stage after the barrier ending that slot, and tile t
-    // is waited for before the barrier ending slot 2 t KB - 3.  (The refill of
-    // tile u = t+NS happens after the barrier ending slot 2(t+1)KB.)
-    static_assert(C::NW % 2 == 0 && C::DVS == 1, "ping-pong halves");
-    const int lag = wave >= C::NW / 2 ? 1 : 0;
-    int issued = 0;
-#pragma unroll
-    for (int t = 0; t < C::NS; ++t)
-      if (t < n_tiles) {
-        issue(t, t);
-        ++issued;
-      }
-    auto wait_tile = [&](int t) {
-      const int after = issued - 1 - t;
-      if (after >= 5) wait_loads<5 * C::KPW < 63 ? 5 * C::KPW : 63>();
-      else if (after == 4) wait_loads<4 * C::KPW < 63 ? 4 * C::KPW : 63>();
-      else if (after == 3) wait_loads<3 * C::KPW < 63 ? 3 * C::KPW : 63>();
-      else if (after == 2) wait_loads<2 * C::KPW>();
-      else if (after == 1) wait_loads<C::KPW>();
-      else wait_loads<0>();
-    };
-    if (nblk > 0) {
-      wait_tile(0);
-      ring_barrier();
-      if (active(0)) s_product_ring(0, accA);
-      bf16x8 pb[C::RB][2];
-      const int nslot = 2 * nblk + 1;
-      for (int slot = 0; slot < nslot; ++slot) {
-        const int ph = slot - lag;
-        if (ph >= 0 && ph < 2 * nblk) {
-          const int j = ph >> 1;
-          const bool act = active(j);
-          const bool act1 = j + 1 < nblk && active(j + 1);
-          if ((ph & 1) == 0) {
-            if (act) softmax(j, accA, pb);
-          } else {
-            if (act1) s_product_ring(j + 1, accA);  // block j's scores are consumed: reuse the registers
-            if (act) pv_product_ring(j, pb);
-          }
-        }
-        if ((slot + 3) % (2 * C::KB) == 0) {
-          const int t = (slot + 3) / (2 * C::KB);
-          if (t < n_tiles) wait_tile(t);
-        }
-        ring_barrier();
-        if (slot % (2 * C::KB) == 0 && slot > 0) {
-          const int u = slot / (2 * C::KB) - 1 + C::NS;
-          if (u < n_tiles) {
-            issue(u, u % C::NS);
-            ++issued;
-          }
-        }
-      }
-    }
-  } else if constexpr (C::IW) {
-    // Step j: [block j+1 starts tile t: wait for it and take the barrier]; one
-    // scheduling region with the S^T product of block j+1 (K operands read a
-    // few MFMA steps ahead) and the softmax of block j; the O rescale; the PV
-    // product of block j.  The PV of a tile's last block runs after the next
-    // tile's barrier, so a stage is refilled one barrier later than in the other
-    // paths: the barrier of tile t frees the stage of tile t-2 (every wave has
-    // finished the PV products of tile t-2 by then), which takes tile t+NS-2;
-    // NS-2 tiles are in flight.  Blocks past this wave's last visible key are
-    // skipped (every later block is too); every wave still takes every barrier.
-    static_assert(C::NS >= 3 && C::RB == 1, "IW ring depth, one row block per wave");
-    auto tile_start_iw = [&](int t) {
-      const int after = min(C::NS - 3, n_tiles - 1 - t);  // tiles issued after t
-      if constexpr (C::NS >= 5) {
-        if (after >= 2) wait_loads<2 * C::KPW>();
-        else if (after == 1) wait_loads<C::KPW>();
-        else wait_loads<0>();
-      } else if constexpr (C::NS == 4) {
-        if (after >= 1) wait_loads<C::KPW>();
-        else wait_loads<0>();
-      } else {
-        wait_loads<0>();
-      }
-      ring_barrier();
-    };
-    auto step_iw = [&](int j, f32x16 (&cur)[C::RB], f32x16 (&nxt)[C::RB]) {
-      const bool act = active(j);
-      if (j + 1 < nblk && (j + 1) % C::KB == 0) tile_start_iw((j + 1) / C::KB);
-      {
-        const int u = (j + 1) / C::KB + C::NS - 2;
-        const int part = (j + 1) % C::KB;
-        if (u < n_tiles) issue(u, u % C::NS, part * C::KPW / C::KB, (part + 1) * C::KPW / C::KB);
-      }
-      if (!act) return;
-      const bool nxt_on = j + 1 < nblk && active(j + 1);
-      const bool full = kv_lo + j * 32 + 32 <= c_lo;
-      bf16x8 pb[C::RB][2];
-      float w[C::RB][16], m_use[C::RB], alpha[C::RB];
-      bool mv[C::RB];
-      if (full && nxt_on) {
-        softmax_max(std::true_type{}, j, cur, w, m_use, alpha, mv);
-        __builtin_amdgcn_sched_barrier(0);
-        s_product_ring(j + 1, nxt);
-        softmax_exp(std::true_type{}, cur, w, m_use, pb);
-        // spread the MFMAs of the S^T product over the exponentials
-        sched_interleave<(C::PDK < C::NKS ? C::PDK : C::NKS), C::NKS, kIwValu>();
-      } else if (full) {
-        softmax_max(std::true_type{}, j, cur, w, m_use, alpha, mv);
-        softmax_exp(std::true_type{}, cur, w, m_use, pb);
-      } else {
-        if (nxt_on) s_product_ring(j + 1, nxt);
-        softmax_max(std::false_type{}, j, cur, w, m_use, alpha, mv);
-        softmax_exp(std::false_type{}, cur, w, m_use, pb);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      if (__builtin_amdgcn_ballot_w64(mv[0]) != 0) {
-        if constexpr (!kValuSums) Lsum[0] *= alpha[0];
-#pragma unroll
-        for (int d = 0; d < C::NDB; ++d) O[0][d] *= alpha[0];
-      }
-      if constexpr (kValuSums) {
-        float ls = w[0][0];
-#pragma unroll
-        for (int e = 1; e < 16; ++e) ls += w[0][e];
-        l_run[0] = fmaf(l_run[0], alpha[0], ls);
-      }
-      pv_product_ring(j, pb);
-    };
-    if (nblk > 0) {
-      tile_start_iw(0);
-      if (C::NS - 2 < n_tiles) issue(C::NS - 2, C::NS - 2, 0, C::KPW / C::KB);
-      if (active(0)) s_product_ring(0, accA);
-      for (int j = 0; j < nblk; j += 2) {
-        step_iw(j, accA, accB);
-        if (j + 1 < nblk) step_iw(j + 1, accB, accA);
-      }
-    }
-  } else if constexpr (C::PREF) {
-    if (nblk > 0) {
-      tile_start(0, false);
-      if (C::NS - 1 < n_tiles) issue(C::NS - 1, C::NS - 1, 0, C::KPW / C::KB);
-      if (active(0)) {
-        bf16x8 ka[C::NKS];
-        k_operands(0, ka);
-        s_product(ka, accA);
-      }
-      for (int j = 0; j < nblk; j += 2) {
-        step(j, accA, accB);
-        if (j + 1 < nblk) step(j + 1, accB, accA);
-      }
-    }
-  } else {
+  {
     for (int j = 0; j < nblk; ++j) {
       if (j % C::KB == 0) tile_start(j / C::KB);
       if (active(j)) {
@@ -877,7 +511,7 @@ __device__ __forceinline__ void m32_block(const KParams& p, unsigned char* smem,
 
   // ---- full row sums
 #pragma unroll
-  for (int rb = 0; rb < C::RB; ++rb) l_run[rb] = kValuSums ? half_swap_sum(l_run[rb]) : Lsum[rb][0];
+  for (int rb = 0; rb < C::RB; ++rb) l_run[rb] = half_swap_sum(l_run[rb]);
 
   // ---- epilogue: element e of O[rb][db] is value 32db + 8(e/4) + 4h + e%4 of row c32
   const bool split_mode = p.ws_o != nullptr;
@@ -891,9 +525,9 @@ __device__ __forceinline__ void m32_block(const KParams& p, unsigned char* smem,
     const int64_t row_g = (int64_t)row_t[rb] * p.num_qo_heads + row_h[rb];
     if (split_mode) {
       const int64_t prow = (int64_t)slot * p.rows_total + row_g;
-      if (h == 0 && dvb0 == 0) p.ws_lse[prow] = lse;
+      if (h == 0) p.ws_lse[prow] = lse;
       if (!empty) {
-        float* dst = p.ws_o + prow * C::DV + 4 * h + 32 * dvb0;
+        float* dst = p.ws_o + prow * C::DV + 4 * h;
 #pragma unroll
         for (int d = 0; d < C::NDB; ++d)
 #pragma unroll
@@ -902,9 +536,9 @@ __device__ __forceinline__ void m32_block(const KParams& p, unsigned char* smem,
                 f32x4{O[rb][d][4 * q], O[rb][d][4 * q + 1], O[rb][d][4 * q + 2], O[rb][d][4 * q + 3]} * inv;
       }
     } else {
-      if (p.lse_out && h == 0 && dvb0 == 0) p.lse_out[row_g] = lse;
+      if (p.lse_out && h == 0) p.lse_out[row_g] = lse;
       if (p.o_dtype == PKV_DTYPE_BF16) {
-        __bf16* dst = (__bf16*)p.out + row_t[rb] * p.o_st + row_h[rb] * p.o_sh + 4 * h + 32 * dvb0;
+        __bf16* dst = (__bf16*)p.out + row_t[rb] * p.o_st + row_h[rb] * p.o_sh + 4 * h;
 #pragma unroll
         for (int d = 0; d < C::NDB; ++d)
 #pragma unroll
@@ -914,7 +548,7 @@ __device__ __forceinline__ void m32_block(const KParams& p, unsigned char* smem,
             *(u32x2*)(dst + 32 * d + 8 * q) = w;
           }
       } else {
-        float* dst = (float*)p.out + row_t[rb] * p.o_st + row_h[rb] * p.o_sh + 4 * h + 32 * dvb0;
+        float* dst = (float*)p.out + row_t[rb] * p.o_st + row_h[rb] * p.o_sh + 4 * h;
 #pragma unroll
         for (int d = 0; d < C::NDB; ++d)
 #pragma unroll
@@ -961,16 +595,8 @@ __global__ __launch_bounds__(C::NTHR, C::OCC) void attn_m32_kernel(const KParams
 
 // ---------------------------------------------------------------- instances
 //                          DQK  DV   VSH    RB NW KB NS OCC
-using M32Ctx = M32Cfg<128, 128, false, 2, 4, 2, 4, 1, false>;  // 256 rows, 64-key stages of 32 KiB
-using M32Mla = M32Cfg<576, 512, true, 1, 4, 1, 4, 1, false, 2>;  // 64 heads, two value halves, 36 KiB stages
-using M32CtxW8 = M32Cfg<128, 128, false, 1, 8, 2, 4, 2, false>;  // 256 rows on 8 waves (two per SIMD)
-using M32CtxR1 = M32Cfg<128, 128, false, 1, 4, 1, 4, 2, false>;  // 128 rows, 16 KiB stages: two workgroups per CU
-using M32CtxR1S3 = M32Cfg<128, 128, false, 1, 4, 1, 3, 3>;  // 128 rows, 48 KiB: three workgroups per CU
-using M32CtxR2 = M32Cfg<128, 128, false, 2, 4, 1, 4, 2, false>;   // 256 rows, 64 rows per wave, 64 KiB
-using M32CtxR2W8 = M32Cfg<128, 128, false, 2, 8, 2, 4, 2, false>;  // 512 rows, 64 rows per wave, 128 KiB
-using M32CtxPP = M32Cfg<128, 128, false, 1, 8, 2, 4, 2, false, 1, true>;  // 256 rows, ping-pong halves
-using M32CtxIW = M32Cfg<128, 128, false, 1, 8, 2, 4, 2, false, 1, false, true>;  // W8 with in-wave overlap
-using M32CtxW8T128 = M32Cfg<128, 128, false, 1, 8, 4, 2, 2, false>;  // W8 with 128-key stages, two of them
+// 256 rows on 8 waves (two per SIMD), two 64 KiB stages of 128 keys
+using M32CtxW8T128 = M32Cfg<128, 128, false, 1, 8, 4, 2, 2>;
 
 template <class C>
 static void fill_m32_shape(MfmaShape* s) {
@@ -981,19 +607,9 @@ static void fill_m32_shape(MfmaShape* s) {
 }
 
 bool m32_shape(int32_t kernel, MfmaShape* s) {
-  switch (kernel) {
-    case KERNEL_M32_CTX_BF16: fill_m32_shape<M32Ctx>(s); return true;
-    case KERNEL_M32_MLA_BF16: fill_m32_shape<M32Mla>(s); return true;
-    case KERNEL_M32_CTX_W8: fill_m32_shape<M32CtxW8>(s); return true;
-    case KERNEL_M32_CTX_R1: fill_m32_shape<M32CtxR1>(s); return true;
-    case KERNEL_M32_CTX_R1S3: fill_m32_shape<M32CtxR1S3>(s); return true;
-    case KERNEL_M32_CTX_R2: fill_m32_shape<M32CtxR2>(s); return true;
-    case KERNEL_M32_CTX_R2W8: fill_m32_shape<M32CtxR2W8>(s); return true;
-    case KERNEL_M32_CTX_PP: fill_m32_shape<M32CtxPP>(s); return true;
-    case KERNEL_M32_CTX_IW: fill_m32_shape<M32CtxIW>(s); return true;
-    case KERNEL_M32_CTX_W8T128: fill_m32_shape<M32CtxW8T128>(s); return true;
-    default: return false;
-  }
+  if (kernel != KERNEL_M32_CTX_W8T128) return false;
+  fill_m32_shape<M32CtxW8T128>(s);
+  return true;
 }
 
 template <class C>
@@ -1013,19 +629,8 @@ static hipError_t launch_m32_cfg(const KParams& p, hipStream_t s) {
 }
 
 hipError_t launch_m32(int32_t kernel, const KParams& p, hipStream_t s) {
-  switch (kernel) {
-    case KERNEL_M32_CTX_BF16: return launch_m32_cfg<M32Ctx>(p, s);
-    case KERNEL_M32_MLA_BF16: return launch_m32_cfg<M32Mla>(p, s);
-    case KERNEL_M32_CTX_W8: return launch_m32_cfg<M32CtxW8>(p, s);
-    case KERNEL_M32_CTX_R1: return launch_m32_cfg<M32CtxR1>(p, s);
-    case KERNEL_M32_CTX_R1S3: return launch_m32_cfg<M32CtxR1S3>(p, s);
-    case KERNEL_M32_CTX_R2: return launch_m32_cfg<M32CtxR2>(p, s);
-    case KERNEL_M32_CTX_R2W8: return launch_m32_cfg<M32CtxR2W8>(p, s);
-    case KERNEL_M32_CTX_PP: return launch_m32_cfg<M32CtxPP>(p, s);
-    case KERNEL_M32_CTX_IW: return launch_m32_cfg<M32CtxIW>(p, s);
-    case KERNEL_M32_CTX_W8T128: return launch_m32_cfg<M32CtxW8T128>(p, s);
-    default: return hipErrorInvalidValue;
-  }
+  if (kernel == KERNEL_M32_CTX_W8T128) return launch_m32_cfg<M32CtxW8T128>(p, s);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace pkv

@@ -574,11 +574,6 @@ __global__ __launch_bounds__(C::NTHR) void attn_mfma_stream_kernel(const KParams
 // ---------------------------------------------------------------- instances
 using CfgGqaBf16 = TileCfg<128, 128, false, false, 1, 1, 4, 32>;
 using CfgGqaFp8 = TileCfg<128, 128, true, false, 1, 1, 4, 64, 1>;
-using CfgGqaBf16T256 = TileCfg<128, 128, false, false, 1, 1, 4, 64, 1>;
-using CfgGqaBf16S1 = TileCfg<128, 128, false, false, 1, 1, 4, 32, 1>;
-using CfgGqaFp8T128 = TileCfg<128, 128, true, false, 1, 1, 4, 32, 1>;
-using CfgGqaBf16W2 = TileCfg<128, 128, false, false, 1, 1, 2, 32, 2>;
-using CfgGqaFp8S2 = TileCfg<128, 128, true, false, 1, 1, 4, 32, 2>;
 using CfgWideBf16 = TileCfg<128, 128, false, false, 2, 4, 1, 64>;
 using CfgWideFp8 = TileCfg<128, 128, true, false, 2, 4, 1, 64>;
 using CfgMlaBf16 = TileCfg<576, 512, false, true, 2, 4, 1, 32>;
@@ -596,11 +591,6 @@ bool mfma_shape(int32_t kernel, MfmaShape* s) {
   switch (kernel) {
     case KERNEL_GQA_BF16: fill_shape<CfgGqaBf16>(s); return true;
     case KERNEL_GQA_FP8: fill_shape<CfgGqaFp8>(s); return true;
-    case KERNEL_GQA_BF16_T256: fill_shape<CfgGqaBf16T256>(s); return true;
-    case KERNEL_GQA_BF16_S1: fill_shape<CfgGqaBf16S1>(s); return true;
-    case KERNEL_GQA_FP8_T128: fill_shape<CfgGqaFp8T128>(s); return true;
-    case KERNEL_GQA_BF16_W2: fill_shape<CfgGqaBf16W2>(s); return true;
-    case KERNEL_GQA_FP8_S2: fill_shape<CfgGqaFp8S2>(s); return true;
     case KERNEL_WIDE_BF16: fill_shape<CfgWideBf16>(s); return true;
     case KERNEL_WIDE_FP8: fill_shape<CfgWideFp8>(s); return true;
     case KERNEL_MLA_BF16: fill_shape<CfgMlaBf16>(s); return true;
@@ -637,11 +627,6 @@ hipError_t launch_mfma(int32_t kernel, const KParams& p, hipStream_t s) {
   switch (kernel) {
     case KERNEL_GQA_BF16: return launch_cfg<CfgGqaBf16>(p, s);
     case KERNEL_GQA_FP8: return launch_cfg<CfgGqaFp8>(p, s);
-    case KERNEL_GQA_BF16_T256: return launch_cfg<CfgGqaBf16T256>(p, s);
-    case KERNEL_GQA_BF16_S1: return launch_cfg<CfgGqaBf16S1>(p, s);
-    case KERNEL_GQA_FP8_T128: return launch_cfg<CfgGqaFp8T128>(p, s);
-    case KERNEL_GQA_BF16_W2: return launch_cfg<CfgGqaBf16W2>(p, s);
-    case KERNEL_GQA_FP8_S2: return launch_cfg<CfgGqaFp8S2>(p, s);
     case KERNEL_WIDE_BF16: return launch_cfg<CfgWideBf16>(p, s);
     case KERNEL_WIDE_FP8: return launch_cfg<CfgWideFp8>(p, s);
     case KERNEL_MLA_BF16: return launch_cfg<CfgMlaBf16>(p, s);

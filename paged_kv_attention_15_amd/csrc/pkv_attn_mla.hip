@@ -65,21 +65,11 @@ constexpr int LDS = NS * STAGE;   // 144 KiB
 #ifndef PKV_MLA_PD
 #define PKV_MLA_PD 4
 #endif
-#ifndef PKV_MLA_SPREAD
-#define PKV_MLA_SPREAD 0
-#endif
 #ifndef PKV_MLA_PDV
 #define PKV_MLA_PDV PKV_MLA_PD
 #endif
-#ifndef PKV_MLA_SACC
-#define PKV_MLA_SACC 1
-#endif
-#ifndef PKV_MLA_ORDER
-#define PKV_MLA_ORDER 2  // 2: S^T and PV streams interleaved; 0: PV with the softmax interleaved
-#endif
 constexpr int PDK = PKV_MLA_PD;   // K operand reads issued this many MFMAs ahead
 constexpr int PDV = PKV_MLA_PDV;  // V^T operand reads issued this many MFMAs ahead
-constexpr int SACC = PKV_MLA_SACC;  // independent S^T accumulator chains (summed at the end)
 constexpr float kLazy = 8.f;  // largest rise of a row max (log2 units) absorbed without rescaling O
 static_assert(NI % NW == 0 && KPW * (NS - 1) < 64 && LATB == 1024 && BK * ROPEB == NW * 1024, "ring geometry");
 
@@ -152,7 +142,6 @@ __device__ __forceinline__ void o_touch(f32x16& o) { asm volatile("" : "+a"(o));
 
 }  // namespace mla
 
-template <bool PIPE>
 __global__ __launch_bounds__(mla::NTHR, 1) void attn_mla32_kernel(const KParams p) {
   using namespace mla;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -289,17 +278,17 @@ __global__ __launch_bounds__(mla::NTHR, 1) void attn_mla32_kernel(const KParams 
   const uint64_t k_base = (uint64_t)p.k + (uint64_t)g * (uint64_t)p.k_sh * 2;
   const uint64_t k_pg_b = (uint64_t)p.k_sp * 2;
   const int pmask = p.page_size - 1;
-  // Measured on gfx950: issued as one burst of KPW instructions per block the
-  // loads stall the issuing wave for about 0.7 us per block (the CU accepts
-  // few direct-to-LDS loads at a time, and its queue drains while the wave
-  // computes), so a block's loads are issued one instruction at a time between
-  // the MFMAs of the previous block's products: `issue(blk, stage, q_lo, q_hi)`
-  // issues this wave's instructions q_lo .. q_hi-1 of the block.
+  // A block's KPW instructions per wave go out as one burst right after the
+  // barrier that frees their stage.  Measured on gfx950 (shader-clock stamps
+  // per block): the burst stalls the issuing wave about 63 ticks per
+  // instruction, the rate at which the CU accepts them from four waves at
+  // once; the same instructions placed one at a time between the MFMAs of the
+  // next S^T product cost about 160 ticks each.
   // Instruction q < KPW - 1 of wave w fills latent row r = (KPW - 1) w + q
   // (lane l fetches logical chunk l ^ key_lat(r), so the row's offset is
   // uniform and a lane adds one XOR); instruction KPW - 1 fills the rope
   // rows 8 w .. 8 w + 7 (lane l: row 8 w + l / 8, chunk 64 + (l % 8) ^ key).
-  auto issue = [&](int blk, int stage, int q_lo = 0, int q_hi = KPW) {
+  auto issue = [&](int blk, int stage) {
     const int tok0 = kv_lo + blk * BK;
     const uint64_t sbase = k_base + (uint64_t)page_of((tok0 >> p.log2_page) - pg_lo) * k_pg_b;
     unsigned char* st = smem + stage * STAGE;
@@ -308,7 +297,6 @@ __global__ __launch_bounds__(mla::NTHR, 1) void attn_mla32_kernel(const KParams 
     ln &= 63;
 #pragma unroll
     for (int q = 0; q < KPW; ++q) {
-      if (q < q_lo || q >= q_hi) continue;
       if (q < KPW - 1) {
         const int r = wave * (KPW - 1) + q;  // wave-uniform
         const int tok = min(tok0 + r, kv_hi - 1);
@@ -398,31 +386,14 @@ __global__ __launch_bounds__(mla::NTHR, 1) void attn_mla32_kernel(const KParams 
     bf16x8 ring[PDK];
 #pragma unroll
     for (int q = 0; q < PDK; ++q) ring[q] = k_read(blk, q);
-    if constexpr (SACC == 1) {
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        const bf16x8 a = ring[ks % PDK];
-        if (ks + PDK < NKS) ring[ks % PDK] = k_read(blk, ks + PDK);
-        if (ks == 0) mfma_s_first(acc, a, qB[ks]);
-        else if (ks == NKS - 1) mfma_s_last(acc, a, qB[ks]);
-        else mfma_s(acc, a, qB[ks]);
-        step_work(ks);
-      }
-    } else {
-      // two chains (even and odd k-steps): consecutive MFMAs never wait on
-      // each other's results
-      f32x16 acc2;
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        const bf16x8 a = ring[ks % PDK];
-        if (ks + PDK < NKS) ring[ks % PDK] = k_read(blk, ks + PDK);
-        f32x16& c = (ks & 1) ? acc2 : acc;
-        if (ks < 2) mfma_s_first(c, a, qB[ks]);
-        else if (ks >= NKS - 2) mfma_s_last(c, a, qB[ks]);
-        else mfma_s(c, a, qB[ks]);
-        step_work(ks);
-      }
-      acc += acc2;
+    for (int ks = 0; ks < NKS; ++ks) {
+      const bf16x8 a = ring[ks % PDK];
+      if (ks + PDK < NKS) ring[ks % PDK] = k_read(blk, ks + PDK);
+      if (ks == 0) mfma_s_first(acc, a, qB[ks]);
+      else if (ks == NKS - 1) mfma_s_last(acc, a, qB[ks]);
+      else mfma_s(acc, a, qB[ks]);
+      step_work(ks);
     }
   };
   // O^T += V^T P^T of block j, the 16-key steps outermost (an output block is
@@ -446,24 +417,6 @@ __global__ __launch_bounds__(mla::NTHR, 1) void attn_mla32_kernel(const KParams 
     }
   };
   auto no_work = [](int) {};
-  static_assert(NKS >= 4 * KPW && KPW == 9 && NDB == 16, "load spreading");
-  // this wave's loads of block `blk`, spread over an S^T product (one every
-  // four MFMAs) or over an S^T and the following PV product (five and four)
-  auto spread_issue = [&](int blk) {
-    return [&, blk](int ks) {
-      if (blk < nblk && (ks & 3) == 3) issue(blk, blk % NS, ks >> 2, (ks >> 2) + 1);
-    };
-  };
-  auto spread_issue_s = [&](int blk) {
-    return [&, blk](int ks) {
-      if (blk < nblk && ks % 7 == 3) issue(blk, blk % NS, ks / 7, ks / 7 + 1);  // 0..4
-    };
-  };
-  auto spread_issue_pv = [&](int blk) {
-    return [&, blk](int i) {
-      if (blk < nblk && (i & 7) == 4) issue(blk, blk % NS, 5 + (i >> 3), 6 + (i >> 3));  // 5..8
-    };
-  };
   // Online softmax of block j (exp2 domain).  Element e of acc holds key
   // 16 (e / 8) + 8 h + e % 8 of the block for this lane's query row; the
   // other 16 keys of the row sit in lane l ^ 32.  Part 1: the row max, the new
@@ -538,194 +491,80 @@ __global__ __launch_bounds__(mla::NTHR, 1) void attn_mla32_kernel(const KParams 
     else wait_loads<0>();
   };
 
-  if constexpr (!PIPE) {
-    // one block at a time: barrier, S^T, softmax, PV; three blocks in flight
 #pragma unroll
-    for (int t = 0; t < NS - 1; ++t)
-      if (t < nblk) issue(t, t);
-    for (int j = 0; j < nblk; ++j) {
-      wait_block(min(NS - 2, nblk - 1 - j));
-      ring_barrier();  // block j landed for every wave; every wave left block j-1's stage
-      if (!active(j) || !PKV_MLA_SPREAD) {
-        if (j + NS - 1 < nblk) issue(j + NS - 1, (j + NS - 1) % NS);
-        if (!active(j)) continue;
-      }
-      f32x16 acc;
-      if (PKV_MLA_SPREAD) s_product(j, acc, spread_issue_s(j + NS - 1));  // block j+3 into block j-1's stage
-      else s_product(j, acc, no_work);
-      bf16x8 pb[2];
-      float m_use, alpha;
-      bool moved;
-      if (full_block(j)) {
-        softmax_max(std::true_type{}, j, acc, m_use, alpha, moved);
-        softmax_exp(std::true_type{}, acc, m_use, alpha, pb);
-      } else {
-        softmax_max(std::false_type{}, j, acc, m_use, alpha, moved);
-        softmax_exp(std::false_type{}, acc, m_use, alpha, pb);
-      }
-      rescale(moved, alpha);
-      if (PKV_MLA_SPREAD) pv_product(j, pb, true, spread_issue_pv(j + NS - 1));
-      else pv_product(j, pb, true, no_work);
-    }
-  } else {
-    // Software pipeline: step j runs the PV product of block j-1 on the matrix
-    // core with the softmax of block j on the vector unit interleaved between
-    // its MFMAs, rescales O if a row's reference moved, then takes the barrier
-    // for block j+1 and runs its S^T product.  Block j-1's stage is free after
-    // that barrier and takes block j+3: blocks j+2 and j+3 stay in flight.
-    // Blocks 1 .. j_full-1 need no mask for any row and always have a
-    // predecessor: they run the fused step in a loop of their own (no branch
-    // inside the MFMA sequence); block 0 and the masked tail run the plain
-    // step.  Each loop has one PV call site, so the output accumulators flow
-    // through one chain of MFMAs.
-#pragma unroll
-    for (int t = 0; t < NS - 1; ++t)
-      if (t < nblk) issue(t, t);
-    f32x16 acc;
-    bf16x8 pb_prev[2], pb_cur[2];
-    if (nblk > 0) {
-      wait_block(min(NS - 2, nblk - 1));
-      ring_barrier();
-      if (active(0)) s_product(0, acc, no_work);
-    }
-    auto next_block = [&](int j) {  // barrier for block j+1, loads of block j+3, S^T of block j+1
-      if (j + 1 < nblk) {
-        wait_block(min(1, nblk - 2 - j));
-        ring_barrier();  // block j+1 landed; every wave finished the PV product of block j-1
-        if (!active(j + 1) || !PKV_MLA_SPREAD) {
-          if (j + NS - 1 < nblk) issue(j + NS - 1, (j + NS - 1) % NS);  // into block j-1's stage
-        }
-        if (active(j + 1)) {
-          if (PKV_MLA_SPREAD) s_product(j + 1, acc, spread_issue(j + NS - 1));  // spread over its S^T
-          else s_product(j + 1, acc, no_work);
-        }
-      }
-    };
-    auto step_plain = [&](int j) {
-      const bool act = active(j), act_prev = j > 0 && active(j - 1);
-      float m_use = 0.f, alpha = 1.f;
-      bool moved = false;
-      if (act_prev) pv_product(j - 1, pb_prev, false, no_work);
-      if (act) {
-        if (full_block(j)) {
-          softmax_max(std::true_type{}, j, acc, m_use, alpha, moved);
-          softmax_exp(std::true_type{}, acc, m_use, alpha, pb_cur);
-        } else {
-          softmax_max(std::false_type{}, j, acc, m_use, alpha, moved);
-          softmax_exp(std::false_type{}, acc, m_use, alpha, pb_cur);
-        }
-        rescale(moved, alpha);
-      }
-      next_block(j);
-      pb_prev[0] = pb_cur[0];
-      pb_prev[1] = pb_cur[1];
-    };
-    auto step_fused = [&](int j) {
-      float m_use = 0.f, alpha = 1.f;
-      bool moved = false;
-      float mr = -INFINITY, ls = 0.f;
-      // the first 8 MFMAs carry the row max, the next 16 one weight each
-      auto work = [&](int i) {
-        if (i < 8) {
-          mr = fmaxf(mr, fmaxf(acc[2 * i], acc[2 * i + 1]));
-        } else if (i == 8) {
-          const float mx = half_swap_max(mr) * sc2;
-          moved = mx > m_run + kLazy;
-          const float m_new = moved ? mx : m_run;
-          m_use = (m_new == -INFINITY) ? 0.f : m_new;
-          alpha = moved ? fast_exp2(m_run - m_use) : 1.f;
-          m_run = m_new;
-          weight(std::true_type{}, acc, 0, m_use);
-          ls = acc[0];
-        } else if (i < 24) {
-          weight(std::true_type{}, acc, i - 8, m_use);
-          ls += acc[i - 8];
-        } else if (i == 24) {
-          l_run = fmaf(l_run, alpha, ls);
-        } else if (i == 25) {
-          pack(acc, pb_cur);
-        }
-      };
-      pv_product(j - 1, pb_prev, false, work);
-      __builtin_amdgcn_sched_barrier(0);
-      rescale(moved, alpha);
-      next_block(j);
-      pb_prev[0] = pb_cur[0];
-      pb_prev[1] = pb_cur[1];
-    };
-    const int j_full = max(1, min(nblk, (c_lo - kv_lo) / BK));  // blocks below j_full need no mask
-    if (PKV_MLA_ORDER == 2) {
-      // Two streams on the matrix core: step j runs the S^T product of block
-      // j+1 and the PV product of block j in one sequence, MFMA by MFMA, so
-      // each stream's LDS operand reads get twice as long to arrive; then the
-      // softmax of block j+1 and the rescale.  S^T steps come at slots
-      // 17 i / 9 (36 of 68), so the product ends on PV steps.
-      auto dual_product = [&](int jS, int jP, const bf16x8 (&pb)[2]) {
-        const KGeo kg = k_geo(jS);
-        const VGeo vg = v_geo(jP);
-        constexpr int NV = 2 * NDB;
-        bf16x8 kr[PDK], vr[PDV];
-#pragma unroll
-        for (int q = 0; q < PDK; ++q) kr[q] = k_read(kg, q);
-#pragma unroll
-        for (int q = 0; q < PDV; ++q) vr[q] = v_read(vg, 2 * (q % NDB) + q / NDB);
-        static_for<0, NKS + NV>([&](auto slot) {
-          constexpr int t = decltype(slot)::value;
-          // S^T step ks sits at slot floor(17 ks / 9); the others are PV steps
-          constexpr int ks_here = (9 * t + 16) / 17;  // first ks with slot(ks) >= t
-          constexpr bool is_s = ks_here < NKS && (17 * ks_here) / 9 == t;
-          constexpr int n_s_before = ks_here < NKS ? ks_here : NKS;  // S steps at slots < t
-          if constexpr (is_s) {
-            constexpr int ks = ks_here;
-            const bf16x8 a = kr[ks % PDK];
-            if (ks + PDK < NKS) kr[ks % PDK] = k_read(kg, ks + PDK);
-            if (ks == 0) mfma_s_first(acc, a, qB[ks]);
-            else if (ks == NKS - 1) mfma_s_last(acc, a, qB[ks]);
-            else mfma_s(acc, a, qB[ks]);
-          } else {
-            constexpr int i = t - n_s_before;
-            constexpr int st = i / NDB, db = i % NDB;
-            const bf16x8 a = vr[i % PDV];
-            if (i + PDV < NV) vr[i % PDV] = v_read(vg, 2 * ((i + PDV) % NDB) + (i + PDV) / NDB);
-            if (i == 0 || i == NDB) mfma_o<true>(O[db], a, pb[st]);
-            else mfma_o<false>(O[db], a, pb[st]);
-          }
-          __builtin_amdgcn_sched_barrier(0);
-        });
-      };
-      auto softmax_block = [&](int j) {
-        float m_use = 0.f, alpha = 1.f;
-        bool moved = false;
-        if (full_block(j)) {
-          softmax_max(std::true_type{}, j, acc, m_use, alpha, moved);
-          softmax_exp(std::true_type{}, acc, m_use, alpha, pb_cur);
-        } else {
-          softmax_max(std::false_type{}, j, acc, m_use, alpha, moved);
-          softmax_exp(std::false_type{}, acc, m_use, alpha, pb_cur);
-        }
-        rescale(moved, alpha);
-      };
-      // block 0: its S^T ran above; every later block is computed even where
-      // it holds no key a row of this wave sees (the masked softmax then
-      // weighs it zero), so the loop has one product call site
-      if (nblk > 0) softmax_block(0);
-      for (int j = 0; j + 1 < nblk; ++j) {
-        pb_prev[0] = pb_cur[0];
-        pb_prev[1] = pb_cur[1];
-        wait_block(min(1, nblk - 2 - j));
-        ring_barrier();  // block j+1 landed; every wave finished reading block j-1's stage
-        if (j + NS - 1 < nblk) issue(j + NS - 1, (j + NS - 1) % NS);  // into block j-1's stage
-        dual_product(j + 1, j, pb_prev);
-        softmax_block(j + 1);
-      }
-      if (nblk > 0) pv_product(nblk - 1, pb_cur, true, no_work);
-    } else {
-    if (nblk > 0) step_plain(0);
-    for (int j = 1; j < j_full; ++j) step_fused(j);
-    for (int j = j_full; j < nblk; ++j) step_plain(j);
-    if (nblk > 0 && active(nblk - 1)) pv_product(nblk - 1, pb_prev, true, no_work);
-    }
+  for (int t = 0; t < NS - 1; ++t)
+    if (t < nblk) issue(t, t);
+  f32x16 acc;
+  bf16x8 pb_prev[2], pb_cur[2];
+  if (nblk > 0) {
+    wait_block(min(NS - 2, nblk - 1));
+    ring_barrier();
+    if (active(0)) s_product(0, acc, no_work);
   }
+  // Two streams on the matrix core: step j runs the S^T product of block
+  // j+1 and the PV product of block j in one sequence, MFMA by MFMA, so
+  // each stream's LDS operand reads get twice as long to arrive; then the
+  // softmax of block j+1 and the rescale.  S^T steps come at slots
+  // 17 i / 9 (36 of 68), so the product ends on PV steps.
+  auto dual_product = [&](int jS, int jP, const bf16x8 (&pb)[2]) {
+    const KGeo kg = k_geo(jS);
+    const VGeo vg = v_geo(jP);
+    constexpr int NV = 2 * NDB;
+    bf16x8 kr[PDK], vr[PDV];
+#pragma unroll
+    for (int q = 0; q < PDK; ++q) kr[q] = k_read(kg, q);
+#pragma unroll
+    for (int q = 0; q < PDV; ++q) vr[q] = v_read(vg, 2 * (q % NDB) + q / NDB);
+    static_for<0, NKS + NV>([&](auto slot) {
+      constexpr int t = decltype(slot)::value;
+      // S^T step ks sits at slot floor(17 ks / 9); the others are PV steps
+      constexpr int ks_here = (9 * t + 16) / 17;  // first ks with slot(ks) >= t
+      constexpr bool is_s = ks_here < NKS && (17 * ks_here) / 9 == t;
+      constexpr int n_s_before = ks_here < NKS ? ks_here : NKS;  // S steps at slots < t
+      if constexpr (is_s) {
+        constexpr int ks = ks_here;
+        const bf16x8 a = kr[ks % PDK];
+        if (ks + PDK < NKS) kr[ks % PDK] = k_read(kg, ks + PDK);
+        if (ks == 0) mfma_s_first(acc, a, qB[ks]);
+        else if (ks == NKS - 1) mfma_s_last(acc, a, qB[ks]);
+        else mfma_s(acc, a, qB[ks]);
+      } else {
+        constexpr int i = t - n_s_before;
+        constexpr int st = i / NDB, db = i % NDB;
+        const bf16x8 a = vr[i % PDV];
+        if (i + PDV < NV) vr[i % PDV] = v_read(vg, 2 * ((i + PDV) % NDB) + (i + PDV) / NDB);
+        if (i == 0 || i == NDB) mfma_o<true>(O[db], a, pb[st]);
+        else mfma_o<false>(O[db], a, pb[st]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+  auto softmax_block = [&](int j) {
+    float m_use = 0.f, alpha = 1.f;
+    bool moved = false;
+    if (full_block(j)) {
+      softmax_max(std::true_type{}, j, acc, m_use, alpha, moved);
+      softmax_exp(std::true_type{}, acc, m_use, alpha, pb_cur);
+    } else {
+      softmax_max(std::false_type{}, j, acc, m_use, alpha, moved);
+      softmax_exp(std::false_type{}, acc, m_use, alpha, pb_cur);
+    }
+    rescale(moved, alpha);
+  };
+  // block 0: its S^T ran above; every later block is computed even where
+  // it holds no key a row of this wave sees (the masked softmax then
+  // weighs it zero), so the loop has one product call site
+  if (nblk > 0) softmax_block(0);
+  for (int j = 0; j + 1 < nblk; ++j) {
+    pb_prev[0] = pb_cur[0];
+    pb_prev[1] = pb_cur[1];
+    wait_block(min(1, nblk - 2 - j));
+    ring_barrier();  // block j+1 landed; every wave finished reading block j-1's stage
+    if (j + NS - 1 < nblk) issue(j + NS - 1, (j + NS - 1) % NS);  // into block j-1's stage
+    dual_product(j + 1, j, pb_prev);
+    softmax_block(j + 1);
+  }
+  if (nblk > 0) pv_product(nblk - 1, pb_cur, true, no_work);
   o_fence<16>(O);  // the last MFMAs' outputs before the epilogue reads them
 
   // ---- epilogue: element e of O[db] is value 32 db + 8 (e / 4) + 4 h + e % 4 of row c32
@@ -773,7 +612,7 @@ __global__ __launch_bounds__(mla::NTHR, 1) void attn_mla32_kernel(const KParams 
 }
 
 bool mla32_shape(int32_t kernel, MfmaShape* s) {
-  if (kernel != KERNEL_MLA32_BF16 && kernel != KERNEL_MLA32_SEQ_BF16) return false;
+  if (kernel != KERNEL_MLA32_BF16) return false;
   s->rows_per_block = mla::ROWS;
   s->tile_tokens = mla::BK;
   s->threads = mla::NTHR;
@@ -782,25 +621,19 @@ bool mla32_shape(int32_t kernel, MfmaShape* s) {
   return true;
 }
 
-template <bool PIPE>
-static hipError_t launch_mla32_cfg(const KParams& p, hipStream_t s) {
+hipError_t launch_mla32(int32_t kernel, const KParams& p, hipStream_t s) {
+  if (kernel != KERNEL_MLA32_BF16) return hipErrorInvalidValue;
   static bool attr_done = false;  // idempotent; a race only repeats the same call
   const size_t lds = mla::LDS + (((size_t)p.page_list_cap + 3) & ~size_t(3)) * sizeof(int32_t);
   if (!attr_done) {
-    hipError_t e = hipFuncSetAttribute((const void*)attn_mla32_kernel<PIPE>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    hipError_t e = hipFuncSetAttribute((const void*)attn_mla32_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       160 * 1024);
     if (e != hipSuccess) return e;
     attr_done = true;
   }
   dim3 grid(p.num_splits, p.num_kv_heads * p.row_blocks, p.batch);
-  hipLaunchKernelGGL(attn_mla32_kernel<PIPE>, grid, dim3(mla::NTHR), lds, s, p);
+  hipLaunchKernelGGL(attn_mla32_kernel, grid, dim3(mla::NTHR), lds, s, p);
   return hipGetLastError();
-}
-
-hipError_t launch_mla32(int32_t kernel, const KParams& p, hipStream_t s) {
-  if (kernel == KERNEL_MLA32_BF16) return launch_mla32_cfg<true>(p, s);
-  if (kernel == KERNEL_MLA32_SEQ_BF16) return launch_mla32_cfg<false>(p, s);
-  return hipErrorInvalidValue;
 }
 
 }  // namespace pkv

@@ -10,49 +10,27 @@
 namespace pkv {
 
 // Kernel families picked by the planner (reported through pkv_plan_info.kernel).
+// Ids are stable: the numbers missing below belonged to tile-shape variants
+// that lost to the kept families on every workload and were removed.
 enum KernelId : int32_t {
   KERNEL_NONE = 0,
   KERNEL_GENERIC = 1,     // VALU, one wavefront per (query row, head, split); any dtype / head dim
-  KERNEL_GQA_BF16 = 2,    // MFMA, <= 16 packed rows per KV head, D = 128, bf16 KV
+  KERNEL_GQA_BF16 = 2,    // MFMA, <= 16 packed rows per KV head, D = 128, bf16 KV, register-staged tiles
   KERNEL_GQA_FP8 = 3,     // same with e4m3 KV
   KERNEL_WIDE_BF16 = 4,   // MFMA, 128 packed rows per workgroup (context / large groups), D = 128
   KERNEL_WIDE_FP8 = 5,
   KERNEL_MLA_BF16 = 6,    // MFMA, 128 heads on one latent KV head, D_qk = 576, D_v = 512
   KERNEL_MLA_FP8 = 7,
-  KERNEL_GQA_BF16_T256 = 8,  // GQA bf16 with 256-token tiles in one LDS stage
-  KERNEL_GQA_BF16_S1 = 9,    // GQA bf16, 128-token tiles, one LDS stage (64 KiB: two workgroups per CU)
-  KERNEL_GQA_FP8_T128 = 10,  // GQA e4m3, 128-token tiles, one LDS stage (64 KiB)
-  KERNEL_GQA_BF16_W2 = 11,   // GQA bf16, two token waves, 64-token tiles, two stages (64 KiB)
-  KERNEL_GQA_FP8_S2 = 12,    // GQA e4m3, 128-token tiles, two LDS stages (128 KiB)
-  // direct-to-LDS ring variants (pkv_attn_dma.hip); KV stays in its stored dtype in LDS
-  KERNEL_DMA_GQA_BF16 = 13,
-  KERNEL_DMA_GQA_FP8 = 14,
+  // direct-to-LDS ring families (pkv_attn_dma.hip); KV stays in its stored dtype in LDS
   KERNEL_DMA_WIDE_BF16 = 15,
   KERNEL_DMA_WIDE_FP8 = 16,
   KERNEL_DMA_MLA_BF16 = 17,
   KERNEL_DMA_MLA_FP8 = 18,
-  KERNEL_DMA_GQA_FP8_W8 = 19,   // 8 token waves, 256-key tiles, 2 stages (128 KiB)
-  KERNEL_DMA_GQA_FP8_S2 = 20,   // 4 token waves, 128-key tiles, 2 stages (64 KiB: two groups per CU)
-  KERNEL_DMA_GQA_BF16_W4 = 21,  // 4 token waves, 128-key tiles, 2 stages (128 KiB)
-  KERNEL_DMA_GQA_BF16_S2 = 22,  // 2 token waves, 64-key tiles, 2 stages (64 KiB)
-  // 32x32x16 MFMA families (pkv_attn_m32.hip), bf16 KV
-  KERNEL_M32_CTX_BF16 = 23,  // D = 128, 4 waves x 64 packed rows, 64-key stages
-  KERNEL_M32_MLA_BF16 = 24,  // D_qk = 576 / D_v = 512 latent, 4 waves x 32 heads, 32-key stages
-  KERNEL_M32_CTX_W8 = 25,    // D = 128, 8 waves x 32 rows (two waves per SIMD)
-  KERNEL_M32_CTX_R1 = 26,    // D = 128, 4 waves x 32 rows, 4 x 16 KiB stages (two workgroups per CU)
-  KERNEL_M32_CTX_R1S3 = 27,  // D = 128, 4 waves x 32 rows, 3 x 16 KiB stages (three workgroups per CU)
-  KERNEL_M32_CTX_R2 = 28,    // D = 128, 4 waves x 64 rows, 4 x 16 KiB stages (two workgroups per CU)
-  KERNEL_M32_CTX_R2W8 = 29,  // D = 128, 8 waves x 64 rows, 4 x 32 KiB stages
-  KERNEL_M32_CTX_PP = 30,    // D = 128, 8 waves x 32 rows in two ping-pong halves
-  KERNEL_DMA_GQA_FP8_N2 = 31,   // 2 token waves, 64-key tiles, 2 stages (32 KiB: four groups per CU)
-  KERNEL_DMA_GQA_BF16_N2 = 32,  // 2 token waves, 64-key tiles, 2 stages (64 KiB)
-  KERNEL_DMA_GQA_FP8_N1 = 33,   // 1 token wave, 32-key tiles, 3 stages (24 KiB: six groups per CU)
-  KERNEL_DMA_GQA_FP8_N2S3 = 34, // 2 token waves, 64-key tiles, 3 stages (48 KiB)
-  KERNEL_M32_CTX_IW = 35,       // D = 128, 8 waves x 32 rows, S^T of the next block interleaved with the softmax
-  KERNEL_M32_CTX_W8T128 = 36,   // D = 128, 8 waves x 32 rows, 2 x 64 KiB stages of 128 keys (half the barriers of W8)
+  KERNEL_DMA_GQA_FP8_N2 = 31,   // e4m3 GQA decode: 2 token waves, 64-key tiles, 2 stages (four groups per CU)
+  // 32x32x16 MFMA context (pkv_attn_m32.hip): D = 128, 8 waves x 32 rows, 2 x 64 KiB stages of 128 keys
+  KERNEL_M32_CTX_W8T128 = 36,
   // MLA latent decode on 32x32x16 MFMA, 32 heads per wave, one wave per SIMD (pkv_attn_mla.hip)
-  KERNEL_MLA32_BF16 = 37,       // PV of block j-1 overlapped with the softmax of block j
-  KERNEL_MLA32_SEQ_BF16 = 38,   // one block at a time
+  KERNEL_MLA32_BF16 = 37,
   KERNEL_COUNT = 39,
 };
 

@@ -21,16 +21,10 @@ PKV_DTYPE_F32, PKV_DTYPE_BF16, PKV_DTYPE_FP8_E4M3 = range(3)
 PKV_LAYOUT_HND, PKV_LAYOUT_NHD = range(2)
 PKV_DEVERR_SEQ_LT_QLEN, PKV_DEVERR_SEQ_GT_TABLE, PKV_DEVERR_PAGE_RANGE, PKV_DEVERR_QINDPTR = 1, 2, 4, 8
 
+# kernel ids of pkv_plan_info.kernel (stable; ids not listed are retired variants)
 KERNEL_NAMES = {0: "none", 1: "generic", 2: "gqa_bf16", 3: "gqa_fp8", 4: "wide_bf16", 5: "wide_fp8",
-                6: "mla_bf16", 7: "mla_fp8", 8: "gqa_bf16_t256", 9: "gqa_bf16_s1", 10: "gqa_fp8_t128",
-                11: "gqa_bf16_w2", 12: "gqa_fp8_s2", 13: "dma_gqa_bf16", 14: "dma_gqa_fp8", 15: "dma_wide_bf16",
-                16: "dma_wide_fp8", 17: "dma_mla_bf16", 18: "dma_mla_fp8", 19: "dma_gqa_fp8_w8",
-                20: "dma_gqa_fp8_s2", 21: "dma_gqa_bf16_w4", 22: "dma_gqa_bf16_s2", 23: "m32_ctx_bf16",
-                24: "m32_mla_bf16", 25: "m32_ctx_w8", 26: "m32_ctx_r1", 27: "m32_ctx_r1s3",
-                28: "m32_ctx_r2", 29: "m32_ctx_r2w8", 30: "m32_ctx_pp",
-                31: "dma_gqa_fp8_n2", 32: "dma_gqa_bf16_n2",
-                33: "dma_gqa_fp8_n1", 34: "dma_gqa_fp8_n2s3", 35: "m32_ctx_iw", 36: "m32_ctx_w8t128",
-                37: "mla32_bf16", 38: "mla32_seq_bf16"}
+                6: "mla_bf16", 7: "mla_fp8", 15: "dma_wide_bf16", 16: "dma_wide_fp8", 17: "dma_mla_bf16",
+                18: "dma_mla_fp8", 31: "dma_gqa_fp8_n2", 36: "m32_ctx_w8t128", 37: "mla32_bf16"}
 KERNEL_IDS = {v: k for k, v in KERNEL_NAMES.items()}
 
 DTYPE_CODES = {"f32": PKV_DTYPE_F32, "bf16": PKV_DTYPE_BF16, "e4m3": PKV_DTYPE_FP8_E4M3}

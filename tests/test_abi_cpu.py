@@ -214,13 +214,14 @@ def test_fused_merge_plan_needs_counters_and_a_ring_kernel():
     assert info.schedule == 1 and info.counter_words == 2 * 8 and info.fused_merge == 0
     a.merge_counters = 0x2000
     info = pkv.pkv_plan(a, False, 256)
-    assert info.fused_merge == (1 if info.kernel >= pkv.KERNEL_IDS["dma_gqa_bf16"] else 0)
-    a.kernel_hint = pkv.KERNEL_IDS["dma_gqa_fp8_n2"] if a.kv_dtype == pkv.PKV_DTYPE_FP8_E4M3 \
-        else pkv.KERNEL_IDS["dma_gqa_bf16_n2"]
-    assert pkv.pkv_plan(a, False, 256).fused_merge == 1
-    a.kernel_hint = pkv.KERNEL_IDS["gqa_bf16"] if a.kv_dtype == pkv.PKV_DTYPE_BF16 else pkv.KERNEL_IDS["gqa_fp8"]
+    assert pkv.KERNEL_NAMES[info.kernel] == "gqa_bf16" and info.fused_merge == 0  # bf16: register-staged
+    a.kv_dtype = pkv.PKV_DTYPE_FP8_E4M3
+    info = pkv.pkv_plan(a, False, 256)
+    assert pkv.KERNEL_NAMES[info.kernel] == "dma_gqa_fp8_n2" and info.fused_merge == 1  # the ring kernel
+    a.kernel_hint = pkv.KERNEL_IDS["gqa_fp8"]
     assert pkv.pkv_plan(a, False, 256).fused_merge == 0  # register-staged kernels keep the separate reducer
     a.kernel_hint = 0
+    a.kv_dtype = pkv.PKV_DTYPE_BF16
     a.num_splits = 5  # per-unit partitions: counters are not used
     info = pkv.pkv_plan(a, False, 256)
     assert info.schedule == 0 and info.fused_merge == 0 and info.counter_words == 0
@@ -355,7 +356,7 @@ def test_separate_value_tables_route_to_families_with_a_second_page_list():
     a.v_block_tables = 0x2000
     plan = pkv.pkv_plan(a)
     assert pkv.KERNEL_NAMES[plan.kernel] == "gqa_bf16" and plan.schedule == 0  # never the balanced schedule
-    for name in ("dma_gqa_bf16", "dma_gqa_fp8_n2", "dma_wide_bf16"):  # the direct-to-LDS ring keeps one list
+    for name in ("dma_wide_bf16", "dma_wide_fp8"):  # the direct-to-LDS ring keeps one list
         a.kernel_hint = pkv.KERNEL_IDS[name]
         assert pkv.pkv_plan(a, check=False).status == pkv.PKV_ERR_UNSUPPORTED
     a.kernel_hint = 0

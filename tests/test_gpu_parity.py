@@ -126,9 +126,7 @@ def _fused_runs(prob, kernel=None, runs=3, expect_err=0, pairs=None):
     return dp
 
 
-@pytest.mark.parametrize("kernel,kv", [("dma_gqa_fp8_n2", W.E4M3), ("dma_gqa_bf16_n2", W.BF16),
-                                       ("dma_gqa_fp8_n1", W.E4M3), ("dma_gqa_fp8", W.E4M3),
-                                       ("dma_gqa_bf16", W.BF16)])
+@pytest.mark.parametrize("kernel,kv", [("dma_gqa_fp8_n2", W.E4M3)])
 def test_fused_merge_kernel_families(kernel, kv):
     P = 64 if kv == W.E4M3 else 32
     prob = _gqa([1, 31, 64, 65, 700, 1300], hq=64 if kv == W.E4M3 else 32, hkv=8, P=P, kv=kv)
@@ -161,9 +159,8 @@ def test_fused_merge_full_size_fp8():
 
 
 @pytest.mark.parametrize("q_len,kernel", [(1, None), (2, None), (1, "dma_mla_bf16"), (2, "dma_mla_bf16"),
-                                          (1, "mla_bf16"), (1, "m32_mla_bf16"), (2, "m32_mla_bf16"),
-                                          (1, "mla32_bf16"), (2, "mla32_bf16"), (1, "mla32_seq_bf16"),
-                                          (2, "mla32_seq_bf16"), (3, "mla32_bf16")])
+                                          (1, "mla_bf16"), (1, "mla32_bf16"), (2, "mla32_bf16"),
+                                          (3, "mla32_bf16")])
 def test_mla_small(q_len, kernel):
     prob = W.make_problem(name=f"mla-small-q{q_len}", seed=3, batch=3, seq_lens=[2, 70, 300],
                           q_lens=[q_len] * 3, num_qo_heads=128, num_kv_heads=1, head_dim_qk=576,
@@ -188,7 +185,7 @@ def test_mla_fp8_latent_small():
         compare(prob, dp, label=kernel)
 
 
-@pytest.mark.parametrize("q_len,kernel", [(1, "mla32_bf16"), (2, "mla32_bf16"), (1, "mla32_seq_bf16")])
+@pytest.mark.parametrize("q_len,kernel", [(1, "mla32_bf16"), (2, "mla32_bf16")])
 def test_mla_full_size_mla32(q_len, kernel):
     prob = W.mla_b512_kv4096(q_len=q_len)
     say(f"case {prob.name} kernel={kernel}")
@@ -198,7 +195,7 @@ def test_mla_full_size_mla32(q_len, kernel):
     compare(prob, dp, pairs=sample_pairs(prob, 256), label=kernel)
 
 
-@pytest.mark.parametrize("kernel,splits", [("mla32_bf16", 3), ("mla32_bf16", 7), ("mla32_seq_bf16", 2)])
+@pytest.mark.parametrize("kernel,splits", [("mla32_bf16", 3), ("mla32_bf16", 7), ("mla32_bf16", 2)])
 def test_mla32_split_partitions(kernel, splits):
     prob = W.make_problem(name="mla32-split", seed=15, batch=3, seq_lens=[1000, 64, 2050], q_lens=[2] * 3,
                           num_qo_heads=128, num_kv_heads=1, head_dim_qk=576, head_dim_v=512, page_size=64,
@@ -209,16 +206,6 @@ def test_mla32_split_partitions(kernel, splits):
     dp.run()
     torch.cuda.synchronize()
     compare(prob, dp, label=f"{kernel}/{splits}")
-
-
-@pytest.mark.parametrize("q_len", [1, 2])
-def test_mla_full_size_m32(q_len):
-    prob = W.mla_b512_kv4096(q_len=q_len)
-    say(f"case {prob.name} kernel=m32_mla_bf16")
-    dp = pkv.upload(prob, "cuda", kernel="m32_mla_bf16")
-    dp.run()
-    torch.cuda.synchronize()
-    compare(prob, dp, pairs=sample_pairs(prob, 256), label="m32_mla_bf16")
 
 
 @pytest.mark.parametrize("q_len", [1, 2])
@@ -358,7 +345,7 @@ def test_graph_replay_matches_eager(case):
 # ----------------------------------------------------------------- attention sinks, separate V tables
 
 @pytest.mark.parametrize("kernel,kv,splits,counters", [
-    (None, W.BF16, None, False), ("gqa_bf16", W.BF16, 3, False), ("dma_gqa_bf16", W.BF16, 1, False),
+    (None, W.BF16, None, False), ("gqa_bf16", W.BF16, 3, False), ("gqa_fp8", W.E4M3, 1, False),
     ("dma_gqa_fp8_n2", W.E4M3, -1, False), ("dma_gqa_fp8_n2", W.E4M3, -1, True), ("generic", W.BF16, None, False),
 ])
 def test_sinks_decode(kernel, kv, splits, counters):
@@ -377,7 +364,7 @@ def test_sinks_speculative_rows_with_an_empty_row():
     compare(prob, run_gpu(prob, num_splits=-1), expect_err=pkv.PKV_DEVERR_SEQ_LT_QLEN)
 
 
-@pytest.mark.parametrize("kernel,splits", [(None, None), ("m32_ctx_w8", 3), ("dma_wide_bf16", None)])
+@pytest.mark.parametrize("kernel,splits", [(None, None), ("m32_ctx_w8t128", 3), ("dma_wide_bf16", None)])
 def test_sinks_context(kernel, splits):
     prob = W.make_problem(name="ctx-sinks", seed=9, batch=3, seq_lens=[70, 5, 333], q_lens=[64, 5, 130],
                           num_qo_heads=16, num_kv_heads=2, head_dim_qk=128, head_dim_v=128, page_size=16,
@@ -406,9 +393,9 @@ def test_sinks_mla(q_len):
     (True, W.E4M3, None, None, "gqa_fp8"),
     (True, W.BF16, None, 3, "gqa_bf16"),
     (True, W.BF16, "generic", None, "generic"),
-    (True, W.BF16, "gqa_bf16_t256", None, "gqa_bf16_t256"),
+    (True, W.E4M3, "gqa_fp8", 2, "gqa_fp8"),
     (False, W.BF16, None, None, "m32_ctx_w8t128"),
-    (False, W.BF16, "m32_ctx_w8", 3, "m32_ctx_w8"),
+    (False, W.BF16, "m32_ctx_w8t128", 3, "m32_ctx_w8t128"),
     (False, W.E4M3, None, None, "wide_fp8"),
     (False, W.BF16, "wide_bf16", None, "wide_bf16"),
     (False, W.BF16, "generic", None, "generic"),
@@ -530,14 +517,10 @@ def test_malformed_q_indptr_flagged_without_writes():
 # ----------------------------------------------------------------- every kernel family on the same inputs
 
 @pytest.mark.parametrize("kernel,kv,splits", [
-    ("dma_gqa_bf16", W.BF16, None), ("dma_gqa_bf16", W.BF16, 1), ("dma_gqa_bf16", W.BF16, 3),
-    ("dma_gqa_fp8", W.E4M3, None), ("dma_gqa_fp8", W.E4M3, 1), ("dma_gqa_fp8", W.E4M3, 5),
-    ("gqa_bf16_s1", W.BF16, None), ("gqa_fp8_t128", W.E4M3, None), ("gqa_bf16_w2", W.BF16, None),
-    ("gqa_fp8_s2", W.E4M3, 2), ("gqa_bf16_t256", W.BF16, 2),
-    ("dma_gqa_fp8_w8", W.E4M3, None), ("dma_gqa_fp8_s2", W.E4M3, None), ("dma_gqa_bf16_w4", W.BF16, None),
-    ("dma_gqa_bf16_s2", W.BF16, None), ("dma_gqa_bf16_w4", W.BF16, 2),
-    ("dma_gqa_fp8_n2", W.E4M3, None), ("dma_gqa_fp8_n2", W.E4M3, -1), ("dma_gqa_bf16_n2", W.BF16, -1),
-    ("dma_gqa_fp8_n1", W.E4M3, -1), ("dma_gqa_fp8_n2s3", W.E4M3, -1),
+    ("gqa_bf16", W.BF16, None), ("gqa_bf16", W.BF16, 1), ("gqa_bf16", W.BF16, 3), ("gqa_bf16", W.BF16, -1),
+    ("gqa_fp8", W.E4M3, None), ("gqa_fp8", W.E4M3, 1), ("gqa_fp8", W.E4M3, 5), ("gqa_fp8", W.E4M3, -1),
+    ("dma_gqa_fp8_n2", W.E4M3, None), ("dma_gqa_fp8_n2", W.E4M3, 1), ("dma_gqa_fp8_n2", W.E4M3, 5),
+    ("dma_gqa_fp8_n2", W.E4M3, -1),
 ])
 def test_gqa_kernel_families_match_oracle(kernel, kv, splits):
     P = 64 if kv == W.E4M3 else 32
@@ -549,12 +532,9 @@ def test_gqa_kernel_families_match_oracle(kernel, kv, splits):
     compare(prob, dp, label=f"{kernel}/{splits}")
 
 
-@pytest.mark.parametrize("kernel,splits", [("dma_wide_bf16", None), ("wide_bf16", None), ("m32_ctx_bf16", None),
-                                           ("m32_ctx_bf16", 3), ("m32_ctx_w8", None), ("m32_ctx_r1", None),
-                                           ("m32_ctx_r1s3", None), ("m32_ctx_r1", 2), ("m32_ctx_r2", None),
-                                           ("m32_ctx_r2w8", None), ("m32_ctx_w8", 2), ("m32_ctx_pp", None),
-                                           ("m32_ctx_pp", 3), ("m32_ctx_iw", None), ("m32_ctx_iw", 3),
-                                           ("m32_ctx_w8t128", None), ("m32_ctx_w8t128", 3)])
+@pytest.mark.parametrize("kernel,splits", [("dma_wide_bf16", None), ("wide_bf16", None), ("wide_bf16", 2),
+                                           ("m32_ctx_w8t128", None), ("m32_ctx_w8t128", 2),
+                                           ("m32_ctx_w8t128", 3)])
 def test_context_kernel_families_match_oracle(kernel, splits):
     prob = W.make_problem(name="ctx-fam", seed=9, batch=3, seq_lens=[70, 5, 333], q_lens=[64, 5, 130],
                           num_qo_heads=16, num_kv_heads=2, head_dim_qk=128, head_dim_v=128, page_size=16,
@@ -566,7 +546,7 @@ def test_context_kernel_families_match_oracle(kernel, splits):
     compare(prob, dp, label=f"{kernel}/{splits}")
 
 
-@pytest.mark.parametrize("kernel", ["m32_ctx_bf16", "m32_ctx_pp", "m32_ctx_iw", "m32_ctx_w8", "m32_ctx_w8t128"])
+@pytest.mark.parametrize("kernel", ["m32_ctx_w8t128", "dma_wide_bf16"])
 def test_context_full_size_m32(kernel):
     prob = W.context_b4_q511_kv2047()
     say(f"case {prob.name} kernel={kernel}")

@@ -85,7 +85,7 @@ def test_peaked_fp8_default_plan(kind):
 
 @pytest.mark.parametrize("kind", ["peaked", "equal", "negative"])
 @pytest.mark.parametrize("q_len", [1, 2])
-@pytest.mark.parametrize("kernel", [None, "dma_mla_bf16", "m32_mla_bf16", "mla32_bf16", "mla32_seq_bf16"])
+@pytest.mark.parametrize("kernel", [None, "dma_mla_bf16", "mla_bf16", "mla32_bf16"])
 def test_peaked_mla_decode(kind, q_len, kernel):
     # with two speculative rows the planted last key of requests 2 and 5 is
     # masked for row 0 and visible to row 1
@@ -94,6 +94,6 @@ def test_peaked_mla_decode(kind, q_len, kernel):
 
 @pytest.mark.parametrize("kind", ["peaked", "equal", "negative"])
 @pytest.mark.parametrize("kernel,splits", [("m32_ctx_w8t128", None), ("m32_ctx_w8t128", 1),
-                                           ("m32_ctx_w8t128", 3), ("m32_ctx_w8", 2), ("dma_wide_bf16", None)])
+                                           ("m32_ctx_w8t128", 3), ("wide_bf16", 2), ("dma_wide_bf16", None)])
 def test_peaked_context(kind, kernel, splits):
     _run(_case("ctx", kind), f"context {kind} splits={splits}", kernel=kernel, num_splits=splits)
