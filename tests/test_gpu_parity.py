@@ -195,6 +195,22 @@ def test_mla_full_size_mla32(q_len, kernel):
     compare(prob, dp, pairs=sample_pairs(prob, 256), label=kernel)
 
 
+@pytest.mark.parametrize("P,hq,q_len", [(32, 128, 1), (128, 128, 2), (256, 64, 1), (64, 16, 2), (32, 48, 1)])
+def test_mla32_page_sizes_and_head_counts(P, hq, q_len):
+    # pages of 32 .. 256 tokens (a 32-key block never crosses a page), head
+    # counts that leave whole waves of a workgroup without a valid row, and
+    # lengths around the block and page boundaries
+    prob = W.make_problem(name=f"mla32-p{P}-h{hq}-q{q_len}", seed=16, batch=6,
+                          seq_lens=[2, 31, 32, 33, 257, 700], q_lens=[q_len] * 6, num_qo_heads=hq,
+                          num_kv_heads=1, head_dim_qk=576, head_dim_v=512, page_size=P, mla=True,
+                          scale=1 / 24.0, poison=True, extra_page_frac=0.3, table_slack_pages=1)
+    say(f"case {prob.name}")
+    dp = pkv.upload(prob, "cuda", kernel="mla32_bf16")
+    dp.run()
+    torch.cuda.synchronize()
+    compare(prob, dp, label=prob.name)
+
+
 @pytest.mark.parametrize("kernel,splits", [("mla32_bf16", 3), ("mla32_bf16", 7), ("mla32_bf16", 2)])
 def test_mla32_split_partitions(kernel, splits):
     prob = W.make_problem(name="mla32-split", seed=15, batch=3, seq_lens=[1000, 64, 2050], q_lens=[2] * 3,
