@@ -34,6 +34,7 @@
 // (normalized O and natural-log LSE) go to the caller's workspace for the
 // separate reducer as the PR #4557 page describes.
 
+#include <cfloat>
 #include <type_traits>
 
 #include "pkv_device.h"
@@ -137,6 +138,22 @@ __device__ __forceinline__ void o_fence(f32x16 (&O)[NDB]) {
                    "+a"(O[15]));
 }
 
+// Slot of S^T step ks in the two-stream MFMA sequence of a block (68 slots:
+// 36 S^T steps, 32 PV steps): seven S^T steps, then one PV step, so the S^T
+// product ends at slot 40 and the softmax runs beside the remaining PV steps.
+constexpr int s_slot(int ks) { return ks + ks / 7; }
+constexpr int s_step_at(int t) {
+  for (int ks = 0; ks < NKS; ++ks)
+    if (s_slot(ks) == t) return ks;
+  return -1;
+}
+constexpr int s_steps_before(int t) {
+  int n = 0;
+  for (int ks = 0; ks < NKS; ++ks) n += s_slot(ks) < t;
+  return n;
+}
+static_assert(s_slot(NKS - 1) == 40 && s_steps_before(68) == NKS, "slot map");
+
 // orders vector access to one block of AGPR outputs (no instructions)
 __device__ __forceinline__ void o_touch(f32x16& o) { asm volatile("" : "+a"(o)); }
 
@@ -221,7 +238,7 @@ __global__ __launch_bounds__(mla::NTHR, 1) void attn_mla32_kernel(const KParams 
   const float sc2_raw = p.scale * k_scale * kLog2e;
   // a negative logit scale is folded into Q (an exact bf16 sign flip), so the
   // softmax only ever needs the row max of the raw products
-  const float sc2 = fabsf(sc2_raw);
+  const float sc2 = fmaxf(fabsf(sc2_raw), FLT_MIN);  // > 0: a masked key's -inf score stays -inf
   const uint32_t q_sign = sc2_raw < 0.f ? 0x80008000u : 0u;
 
   // ---- this lane's query row and its Q operands (B of S^T: row c32, channels 16 ks + 8 h .. +7)
@@ -503,25 +520,68 @@ __global__ __launch_bounds__(mla::NTHR, 1) void attn_mla32_kernel(const KParams 
   }
   // Two streams on the matrix core: step j runs the S^T product of block
   // j+1 and the PV product of block j in one sequence, MFMA by MFMA, so
-  // each stream's LDS operand reads get twice as long to arrive; then the
-  // softmax of block j+1 and the rescale.  S^T steps come at slots
-  // 17 i / 9 (36 of 68), so the product ends on PV steps.
+  // each stream's LDS operand reads get longer to arrive.  The S^T steps
+  // come first (ks + ks / 7: seven S^T steps, then one PV step), and the
+  // softmax of block j+1 runs in pieces between the PV steps that follow,
+  // in the shadow of their MFMAs; the rare O rescale comes after the last.
+  // Each piece ties its results to an empty asm statement, which keeps it
+  // between the MFMA statements around it (the compiler would otherwise
+  // sink the arithmetic to its first use after the sequence).
+  float sm_mx = 0.f, sm_use = 0.f, sm_alpha = 1.f, sm_ls = 0.f;
+  bool sm_moved = false;
+  auto softmax_piece = [&](auto piece, int jS, bool full) {
+    constexpr int c = decltype(piece)::value;
+    if constexpr (c == 0) {
+      if (!full) {  // keys at or past a row's causal limit weigh zero (sc2 > 0)
+        const int blk_tok = kv_lo + jS * BK;
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (blk_tok + 16 * (e >> 3) + 8 * h + (e & 7) >= row_c) acc[e] = -INFINITY;
+      }
+      sm_mx = acc[0];
+#pragma unroll
+      for (int e = 1; e < 8; ++e) sm_mx = fmaxf(sm_mx, acc[e]);
+      asm volatile("" : "+v"(sm_mx));
+    } else if constexpr (c == 1) {
+#pragma unroll
+      for (int e = 8; e < 16; ++e) sm_mx = fmaxf(sm_mx, acc[e]);
+      asm volatile("" : "+v"(sm_mx));
+    } else if constexpr (c == 2) {
+      const float mx = half_swap_max(sm_mx) * sc2;
+      sm_moved = mx > m_run + kLazy;  // also true on a row's first visible key
+      const float m_new = sm_moved ? mx : m_run;
+      sm_use = (m_new == -INFINITY) ? 0.f : m_new;
+      sm_alpha = sm_moved ? fast_exp2(m_run - sm_use) : 1.f;
+      m_run = m_new;
+      sm_ls = 0.f;
+      asm volatile("" : "+v"(sm_use), "+v"(sm_alpha), "+v"(m_run));
+    } else if constexpr (c < 19) {
+      constexpr int e = c - 3;
+      acc[e] = fast_exp2(fmaf(acc[e], sc2, -sm_use));
+      sm_ls += acc[e];
+      asm volatile("" : "+v"(acc[e]), "+v"(sm_ls));
+    } else {
+      l_run = fmaf(l_run, sm_alpha, sm_ls);
+      pack(acc, pb_cur);
+      asm volatile("" : "+v"(pb_cur[0]), "+v"(pb_cur[1]), "+v"(l_run));
+    }
+  };
+  constexpr int kPieces = 20;
   auto dual_product = [&](int jS, int jP, const bf16x8 (&pb)[2]) {
+    const bool full = full_block(jS);
     const KGeo kg = k_geo(jS);
     const VGeo vg = v_geo(jP);
     constexpr int NV = 2 * NDB;
+    constexpr int NSLOT = NKS + NV;
     bf16x8 kr[PDK], vr[PDV];
 #pragma unroll
     for (int q = 0; q < PDK; ++q) kr[q] = k_read(kg, q);
 #pragma unroll
     for (int q = 0; q < PDV; ++q) vr[q] = v_read(vg, 2 * (q % NDB) + q / NDB);
-    static_for<0, NKS + NV>([&](auto slot) {
+    static_for<0, NSLOT>([&](auto slot) {
       constexpr int t = decltype(slot)::value;
-      // S^T step ks sits at slot floor(17 ks / 9); the others are PV steps
-      constexpr int ks_here = (9 * t + 16) / 17;  // first ks with slot(ks) >= t
-      constexpr bool is_s = ks_here < NKS && (17 * ks_here) / 9 == t;
-      constexpr int n_s_before = ks_here < NKS ? ks_here : NKS;  // S steps at slots < t
-      if constexpr (is_s) {
+      constexpr int ks_here = s_step_at(t);
+      if constexpr (ks_here >= 0) {
         constexpr int ks = ks_here;
         const bf16x8 a = kr[ks % PDK];
         if (ks + PDK < NKS) kr[ks % PDK] = k_read(kg, ks + PDK);
@@ -529,12 +589,21 @@ __global__ __launch_bounds__(mla::NTHR, 1) void attn_mla32_kernel(const KParams 
         else if (ks == NKS - 1) mfma_s_last(acc, a, qB[ks]);
         else mfma_s(acc, a, qB[ks]);
       } else {
-        constexpr int i = t - n_s_before;
+        constexpr int i = t - s_steps_before(t);
         constexpr int st = i / NDB, db = i % NDB;
         const bf16x8 a = vr[i % PDV];
         if (i + PDV < NV) vr[i % PDV] = v_read(vg, 2 * ((i + PDV) % NDB) + (i + PDV) / NDB);
         if (i == 0 || i == NDB) mfma_o<true>(O[db], a, pb[st]);
         else mfma_o<false>(O[db], a, pb[st]);
+        // softmax piece c at slot first + c (NSLOT - 2 - first) / (kPieces - 1):
+        // the last piece writes P^T of block j+1 before the last MFMA reads
+        // P^T of block j, so the two never share registers
+        constexpr int first = s_slot(NKS - 1) + 1;
+        constexpr int span = NSLOT - 2 - first;
+        static_for<0, kPieces>([&](auto piece) {
+          constexpr int c = decltype(piece)::value;
+          if constexpr (first + (c * span) / (kPieces - 1) == t) softmax_piece(piece, jS, full);
+        });
       }
       __builtin_amdgcn_sched_barrier(0);
     });
@@ -562,7 +631,7 @@ __global__ __launch_bounds__(mla::NTHR, 1) void attn_mla32_kernel(const KParams 
     ring_barrier();  // block j+1 landed; every wave finished reading block j-1's stage
     if (j + NS - 1 < nblk) issue(j + NS - 1, (j + NS - 1) % NS);  // into block j-1's stage
     dual_product(j + 1, j, pb_prev);
-    softmax_block(j + 1);
+    rescale(sm_moved, sm_alpha);
   }
   if (nblk > 0) pv_product(nblk - 1, pb_cur, true, no_work);
   o_fence<16>(O);  // the last MFMAs' outputs before the epilogue reads them
