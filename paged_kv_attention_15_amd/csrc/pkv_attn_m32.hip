@@ -24,6 +24,7 @@
 // Split-KV partials (normalized O and natural-log LSE per partition, merged
 // by the separate reducer) follow the PR #4557 page's Split-KV description.
 
+#include <cfloat>
 #include <type_traits>
 
 #include "pkv_device.h"
@@ -92,11 +93,11 @@ __device__ __forceinline__ int chunk_phys(int c_const, int c_lane, int key) {
   return (c_const & ~m) + (((c_const & m) + c_lane) ^ (key & m));
 }
 
-// Compile-time loop (the scheduling builtins below need literal arguments)
+// Compile-time loop: f receives the index as a std::integral_constant
 template <int I, int N, class F>
 __device__ __forceinline__ void static_for(F&& f) {
   if constexpr (I < N) {
-    f();
+    f(std::integral_constant<int, I>{});
     static_for<I + 1, N>(f);
   }
 }
@@ -188,7 +189,7 @@ __device__ __forceinline__ void m32_block(const KParams& p, unsigned char* smem,
   const float sc2_raw = p.scale * k_scale * kLog2e;
   // a negative logit scale is folded into Q (an exact bf16 sign flip), so the
   // softmax only ever needs the row max of the raw products
-  const float sc2 = fabsf(sc2_raw);
+  const float sc2 = fmaxf(fabsf(sc2_raw), FLT_MIN);  // > 0: a masked key's -inf score stays -inf
   const uint32_t q_sign = sc2_raw < 0.f ? 0x80008000u : 0u;
 
   int row_t[C::RB], row_h[C::RB], row_c[C::RB];
@@ -460,6 +461,101 @@ __device__ __forceinline__ void m32_block(const KParams& p, unsigned char* smem,
       for (int rb = 0; rb < C::RB; ++rb) O[rb][i >> 1] = mfma32x32x16(a, pb[rb][i & 1], O[rb][i >> 1]);
     }
   };
+  // PV product of block jP with the softmax of block jS (whose S^T product
+  // just ended) in pieces between its MFMAs: the wave's own vector work then
+  // runs in the shadow of its matrix work instead of only beside the other
+  // wave of the SIMD.  Each piece ties its results to an empty asm statement
+  // so that it stays between the MFMAs around it.  The rescale of O for block
+  // jS (rare) follows the last MFMA of block jP.
+  float sm_mx[C::RB], sm_use[C::RB], sm_alpha[C::RB], sm_ls[C::RB];
+  bool sm_move[C::RB];
+  auto softmax_piece = [&](auto piece, int jS, f32x16 (&acc)[C::RB], bf16x8 (&pb)[C::RB][2]) {
+    constexpr int c = decltype(piece)::value;
+    const int blk_tok = kv_lo + jS * 32;
+    const bool full = blk_tok + 32 <= c_lo;
+#pragma unroll
+    for (int rb = 0; rb < C::RB; ++rb) {
+      if constexpr (c == 0) {
+        if (!full) {  // keys at or past the row's causal limit weigh zero (sc2 > 0)
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            if (blk_tok + 16 * (e >> 3) + 8 * h + (e & 7) >= row_c[rb]) acc[rb][e] = -INFINITY;
+        }
+        float mx = acc[rb][0];
+#pragma unroll
+        for (int e = 1; e < 8; ++e) mx = fmaxf(mx, acc[rb][e]);
+        sm_mx[rb] = mx;
+        asm volatile("" : "+v"(sm_mx[rb]));
+      } else if constexpr (c == 1) {
+#pragma unroll
+        for (int e = 8; e < 16; ++e) sm_mx[rb] = fmaxf(sm_mx[rb], acc[rb][e]);
+        asm volatile("" : "+v"(sm_mx[rb]));
+      } else if constexpr (c == 2) {
+        const float mx = half_swap_max(sm_mx[rb]) * sc2;
+        sm_move[rb] = mx > m_run[rb] + kLazyMax;  // also true on a row's first visible key
+        const float m_new = sm_move[rb] ? mx : m_run[rb];
+        sm_use[rb] = (m_new == -INFINITY) ? 0.f : m_new;
+        sm_alpha[rb] = sm_move[rb] ? fast_exp2(m_run[rb] - sm_use[rb]) : 1.f;
+        m_run[rb] = m_new;
+        sm_ls[rb] = 0.f;
+        asm volatile("" : "+v"(sm_use[rb]), "+v"(sm_alpha[rb]), "+v"(m_run[rb]));
+      } else if constexpr (c < 19) {
+        constexpr int e = c - 3;
+        acc[rb][e] = fast_exp2(fmaf(acc[rb][e], sc2, -sm_use[rb]));
+        sm_ls[rb] += acc[rb][e];
+        asm volatile("" : "+v"(acc[rb][e]), "+v"(sm_ls[rb]));
+      } else {
+        l_run[rb] = fmaf(l_run[rb], sm_alpha[rb], sm_ls[rb]);
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          u32x4 wv{pack_bf16x2(acc[rb][8 * st + 0], acc[rb][8 * st + 1]),
+                   pack_bf16x2(acc[rb][8 * st + 2], acc[rb][8 * st + 3]),
+                   pack_bf16x2(acc[rb][8 * st + 4], acc[rb][8 * st + 5]),
+                   pack_bf16x2(acc[rb][8 * st + 6], acc[rb][8 * st + 7])};
+          pb[rb][st] = __builtin_bit_cast(bf16x8, wv);
+        }
+        asm volatile("" : "+v"(pb[rb][0]), "+v"(pb[rb][1]), "+v"(l_run[rb]));
+      }
+    }
+  };
+  constexpr int kPieces = 20;
+  auto pv_softmax = [&](int jP, const bf16x8 (&pbP)[C::RB][2], int jS, f32x16 (&acc)[C::RB],
+                        bf16x8 (&pbS)[C::RB][2]) {
+    const unsigned char* vst = smem + ((jP / C::KB) % C::NS) * C::STAGE + (C::VSHARE ? 0 : C::KTILE);
+    const unsigned char* vblk = vst + (jP % C::KB) * 32 * C::VROWB + vl_row;
+    auto rd = [&](int i) {  // i = 2 db + st
+      const int db = i >> 1, st = i & 1;
+      const unsigned char* src = vblk + 16 * st * C::VROWB + chunk_phys<C::NCV>(4 * db, vc_lane, vfk) * 16;
+      const s16x4 lo = lds_read_tr16(src);
+      const s16x4 hi = lds_read_tr16(src + 4 * C::VROWB);
+      typedef short s16x8 __attribute__((ext_vector_type(8)));
+      return __builtin_bit_cast(bf16x8, s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+    };
+    constexpr int N = 2 * C::NDB;
+    constexpr int PD = C::PDV < N ? C::PDV : N;
+    bf16x8 ring[PD];
+#pragma unroll
+    for (int q = 0; q < PD; ++q) ring[q] = rd(q);
+    static_for<0, N>([&](auto slot) {
+      constexpr int i = decltype(slot)::value;
+      const bf16x8 a = ring[i % PD];
+      if (i + PD < N) ring[i % PD] = rd(i + PD);
+#pragma unroll
+      for (int rb = 0; rb < C::RB; ++rb) O[rb][i >> 1] = mfma32x32x16(a, pbP[rb][i & 1], O[rb][i >> 1]);
+      static_for<0, kPieces>([&](auto piece) {
+        constexpr int c = decltype(piece)::value;
+        if constexpr ((c * N) / kPieces == i) softmax_piece(piece, jS, acc, pbS);
+      });
+      __builtin_amdgcn_sched_barrier(0);
+    });
+#pragma unroll
+    for (int rb = 0; rb < C::RB; ++rb) {
+      if (__builtin_amdgcn_ballot_w64(sm_move[rb]) != 0) {
+#pragma unroll
+        for (int d = 0; d < C::NDB; ++d) O[rb][d] *= sm_alpha[rb];
+      }
+    }
+  };
   // Start of ring tile t: this wave's loads of t are complete once at most
   // (tiles issued after t) * KPW remain; the barrier then publishes every wave's
   // part and frees the stage of tile t-1, which the next issue refills.
@@ -489,24 +585,37 @@ __device__ __forceinline__ void m32_block(const KParams& p, unsigned char* smem,
   for (int t = 0; t < C::NS - 1; ++t)
     if (t < n_tiles) issue(t, t);
 
-  // One 32-key block at a time: S^T product (K operands read a few MFMA
-  // steps ahead), softmax, PV product.  The two waves of a SIMD run
+  // 32-key blocks: S^T product (K operands read a few MFMA steps ahead),
+  // softmax, PV product, with the softmax of block j in the shadow of the PV
+  // product of block j-1 inside a tile.  The two waves of a SIMD also run
   // independently between the tile barriers, so one's matrix work covers the
-  // other's softmax.  Blocks past this wave's last visible key are skipped;
-  // every wave still takes every tile's barrier.
-  const int nblk = n_tiles * C::KB;
+  // other's vector work.  Blocks past this wave's last visible key are
+  // skipped; every wave still takes every tile's barrier.
   f32x16 accA[C::RB];
   auto active = [&](int j) { return kv_lo + j * 32 < c_hi; };
-  {
-    for (int j = 0; j < nblk; ++j) {
-      if (j % C::KB == 0) tile_start(j / C::KB);
-      if (active(j)) {
-        s_product_ring(j, accA);
-        bf16x8 pb[C::RB][2];
-        softmax(j, accA, pb);
-        pv_product_ring(j, pb);
+  // Within a tile: S^T(j), then PV(j-1) with the softmax of block j in its
+  // shadow; the tile's first softmax runs alone and its last PV product
+  // before the next tile's barrier, which frees the stage for a refill.
+  for (int t = 0; t < n_tiles; ++t) {
+    tile_start(t);
+    const int j0 = t * C::KB;
+    if (!active(j0)) continue;
+    bf16x8 pb_cur[C::RB][2], pb_prev[C::RB][2];
+    s_product_ring(j0, accA);
+    softmax(j0, accA, pb_cur);
+    int j = j0;
+    for (int k = 1; k < C::KB; ++k) {
+      if (!active(j0 + k)) break;
+      j = j0 + k;
+#pragma unroll
+      for (int rb = 0; rb < C::RB; ++rb) {
+        pb_prev[rb][0] = pb_cur[rb][0];
+        pb_prev[rb][1] = pb_cur[rb][1];
       }
+      s_product_ring(j, accA);
+      pv_softmax(j - 1, pb_prev, j, accA, pb_cur);
     }
+    pv_product_ring(j, pb_cur);
   }
 
   // ---- full row sums
