@@ -25,9 +25,9 @@
 //     transposed V read, over all 64 banks (odd rows of 1152 bytes start half
 //     a bank row later), the rope chunks a 3-bit key;
 //   * one MFMA sequence per block carries two independent products, the S^T
-//     product of block j+1 and the PV product of block j, step by step, so
-//     each one's LDS operand reads have twice as long to arrive; the softmax
-//     of block j+1 follows; the running maximum moves only on jumps of more
+//     product of block j+1 (first) and the PV product of block j, and the
+//     softmax of block j+1 runs in pieces between the PV steps that follow
+//     its last S^T step; the running maximum moves only on jumps of more
 //     than 8 (log2 units), so O is rescaled rarely.
 // Paging follows the flashinfer.cake_fmha API page's contract (key j of
 // request b is token j % P of page block_tables[b][j / P]); Split-KV partials
