@@ -215,15 +215,30 @@ def gpu_clocks():
 
 
 class ClockSampler:
-    """Reads device 0's current sclk level from sysfs every millisecond on a
-    host thread while a timed region runs (the level read after the region
-    shows the idle clock, not the clock the kernels ran at)."""
+    """Reads device 0's current sclk level (and, where the driver exposes it,
+    its socket power) from sysfs every millisecond on a host thread while a
+    timed region runs (the level read after the region shows the idle clock,
+    not the clock the kernels ran at)."""
 
     def __init__(self, source):
+        import glob
         import threading
 
         self.path = os.path.join(source, "pp_dpm_sclk") if source else None
+        self.power_path, self.power_cap_w = None, None
+        if source:
+            for name in ("power1_average", "power1_input"):
+                hits = sorted(glob.glob(os.path.join(source, "hwmon", "hwmon*", name)))
+                if hits:
+                    self.power_path = hits[0]
+                    try:
+                        cap = os.path.join(os.path.dirname(hits[0]), "power1_cap")
+                        self.power_cap_w = int(open(cap).read().strip()) / 1e6
+                    except (OSError, ValueError):
+                        pass
+                    break
         self.samples = []
+        self.power_w = []
         self._stop = threading.Event()
         self._thread = threading.Thread(target=self._run, daemon=True)
 
@@ -238,6 +253,11 @@ class ClockSampler:
                         self.samples.append(int(m.group(1)))
             except OSError:
                 return
+            if self.power_path:
+                try:
+                    self.power_w.append(int(open(self.power_path).read().strip()) / 1e6)
+                except (OSError, ValueError):
+                    self.power_path = None
             self._stop.wait(0.001)
 
     def __enter__(self):
@@ -254,7 +274,14 @@ class ClockSampler:
         if not self.samples:
             return None
         v = sorted(self.samples)
-        return {"samples": len(v), "sclk_mhz_median": v[len(v) // 2], "sclk_mhz_min": v[0], "sclk_mhz_max": v[-1]}
+        out = {"samples": len(v), "sclk_mhz_median": v[len(v) // 2], "sclk_mhz_min": v[0], "sclk_mhz_max": v[-1]}
+        if self.power_w:
+            pw = sorted(self.power_w)
+            out["power_w_median"] = round(pw[len(pw) // 2], 1)
+            out["power_w_max"] = round(pw[-1], 1)
+            if self.power_cap_w:
+                out["power_cap_w"] = round(self.power_cap_w, 1)
+        return out
 
 
 # MI355X's shader clock climbs from about 1 GHz to 2.2-2.4 GHz over the first
