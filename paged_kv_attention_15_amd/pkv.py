@@ -345,6 +345,126 @@ def fill_args(prob, t: dict, num_splits: Optional[int] = None) -> PkvArgs:
     return a
 
 
+# ---------------------------------------------------------------- torch tensors in, pkv_args out
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return PKV_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return PKV_DTYPE_F32
+    if t.dtype in (getattr(torch, "float8_e4m3fn", None), torch.uint8):  # e4m3 codes, or their raw bytes
+        return PKV_DTYPE_FP8_E4M3
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def _stride(t, dim: int, natural: int) -> int:
+    """Element stride of `dim`; a dimension of extent 1 is never stepped, so
+    the contiguous value stands in for whatever its stride says."""
+    return natural if int(t.shape[dim]) == 1 else int(t.stride(dim))
+
+
+def args_from_tensors(q, k_pages, v_pages, block_tables, seq_lens, out, *, scale: float, max_kv_len: int,
+                      layout: str = "HND", q_indptr=None, max_q_len: Optional[int] = None, causal: bool = True,
+                      k_scale: float = 1.0, v_scale: float = 1.0, head_dim_v: Optional[int] = None, lse=None,
+                      err=None, sinks=None, v_block_tables=None, num_splits: int = 0,
+                      kernel: Optional[str] = None) -> PkvArgs:
+    """pkv_args for caller-owned device tensors: shapes, dtypes and element
+    strides are read off the tensors, nothing is copied.
+
+    q [total_q, Hq, D]; k_pages / v_pages HND [num_pages, Hkv, P, D] or NHD
+    [num_pages, P, Hkv, D] (v_pages None: MLA, V is the first head_dim_v
+    channels of the K rows); block_tables int32 [B, >= max pages];
+    seq_lens int32 [B]; out [total_q, Hq, Dv].  Decode when q_indptr is
+    None (every request has total_q / B rows), context otherwise (int32
+    [B + 1] row offsets; max_q_len is then the host-side bound on a request's
+    rows).  max_kv_len is the host-side bound on seq_lens that sizes the
+    plan."""
+    if layout not in ("HND", "NHD"):
+        raise ValueError("layout must be 'HND' or 'NHD'")
+    for name, t in (("q", q), ("k_pages", k_pages), ("out", out)) + ((("v_pages", v_pages),) if v_pages is not None else ()):
+        if t.stride(-1) != 1:
+            raise ValueError(f"{name}: the last (channel) dimension must be contiguous")
+    B = int(block_tables.shape[0])
+    total_q, Hq, D = (int(x) for x in q.shape)
+    def pool_strides(t):  # (page, head, token) element strides of a K or V pool
+        W_ = int(t.shape[3])
+        if layout == "HND":
+            return (_stride(t, 0, Hkv * P * W_), _stride(t, 1, P * W_), _stride(t, 2, W_))
+        return (_stride(t, 0, P * Hkv * W_), _stride(t, 2, W_), _stride(t, 1, Hkv * W_))
+
+    if layout == "HND":
+        num_pages, Hkv, P, Dk = (int(x) for x in k_pages.shape)
+    else:
+        num_pages, P, Hkv, Dk = (int(x) for x in k_pages.shape)
+    k_sp, k_sh, k_st = pool_strides(k_pages)
+    if Dk != D:
+        raise ValueError(f"q has {D} channels, the K rows {Dk}")
+    a = PkvArgs()
+    a.batch = B
+    a.num_qo_heads, a.num_kv_heads = Hq, Hkv
+    a.head_dim_qk = D
+    a.page_size = P
+    a.max_pages_per_seq = int(block_tables.shape[1])
+    a.table_stride = _stride(block_tables, 0, int(block_tables.shape[1]))
+    a.max_kv_len = int(max_kv_len)
+    a.total_q = total_q
+    a.num_pages = num_pages
+    if q_indptr is None:
+        if B == 0 or total_q % B:
+            raise ValueError("decode needs the same number of rows for every request (total_q % B == 0)")
+        a.q_len = total_q // B
+        a.max_q_len = a.q_len
+    else:
+        if max_q_len is None:
+            raise ValueError("context calls need max_q_len")
+        a.q_len = 0
+        a.max_q_len = int(max_q_len)
+        a.q_indptr = q_indptr.data_ptr()
+    a.q_dtype, a.kv_dtype, a.o_dtype = _dtype_code(q), _dtype_code(k_pages), _dtype_code(out)
+    a.layout = PKV_LAYOUT_HND if layout == "HND" else PKV_LAYOUT_NHD
+    a.causal = 1 if causal else 0
+    a.num_splits = int(num_splits)
+    a.q, a.k_pages = q.data_ptr(), k_pages.data_ptr()
+    a.q_stride_tok, a.q_stride_head = _stride(q, 0, Hq * D), _stride(q, 1, D)
+    a.k_stride_page, a.k_stride_head, a.k_stride_tok = k_sp, k_sh, k_st
+    if v_pages is None:
+        a.v_shares_k = 1
+        a.head_dim_v = int(head_dim_v if head_dim_v is not None else out.shape[2])
+        a.v_stride_page, a.v_stride_head, a.v_stride_tok = k_sp, k_sh, k_st
+    else:
+        a.head_dim_v = int(v_pages.shape[3])
+        a.v_pages = v_pages.data_ptr()
+        a.v_stride_page, a.v_stride_head, a.v_stride_tok = pool_strides(v_pages)
+    a.block_tables, a.seq_lens = block_tables.data_ptr(), seq_lens.data_ptr()
+    a.out = out.data_ptr()
+    a.o_stride_tok, a.o_stride_head = _stride(out, 0, Hq * int(out.shape[2])), _stride(out, 1, int(out.shape[2]))
+    a.lse_out = lse.data_ptr() if lse is not None else 0
+    a.err_word = err.data_ptr() if err is not None else 0
+    a.sinks = sinks.data_ptr() if sinks is not None else 0
+    a.v_block_tables = v_block_tables.data_ptr() if v_block_tables is not None else 0
+    a.scale, a.k_scale, a.v_scale = float(scale), float(k_scale), float(v_scale)
+    if kernel is not None:
+        a.kernel_hint = KERNEL_IDS[kernel]
+    return a
+
+
+def run_tensors(args: PkvArgs, stream=None, workspace=None):
+    """pkv_decode or pkv_context (by args.q_len) on `stream` (default: torch's
+    current stream), with `workspace` (a uint8 device tensor) or one
+    allocated here at the size pkv_workspace_bytes asks for.  Returns the
+    workspace so that a caller can keep it for the next call."""
+    torch = _torch()
+    is_ctx = args.q_len == 0
+    need = pkv_workspace_bytes(args, is_ctx)
+    if need > 0 and (workspace is None or workspace.numel() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=torch.device("cuda", torch.cuda.current_device()))
+    ws_ptr = int(workspace.data_ptr()) if (workspace is not None and need > 0) else 0
+    s = stream if stream is not None else torch.cuda.current_stream()
+    (pkv_context if is_ctx else pkv_decode)(args, ws_ptr, need, int(s.cuda_stream))
+    return workspace
+
+
 @dataclass
 class DeviceAppend:
     args: PkvAppendArgs

@@ -1,0 +1,94 @@
+"""Host-only check of the binding's tensor-level marshalling: pkv_args built
+from caller tensors (shapes, dtypes and element strides read off them) equals
+the pkv_args the test harness builds field by field for the same problem.
+No device memory and no compute call: CPU tensors stand in for device ones,
+and only their addresses are taken."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from paged_kv_attention_15_amd import pkv, workloads as W  # noqa: E402
+
+
+def _cpu_tensors(prob):
+    t = {"q": torch.from_numpy(prob.q.view(np.int16) if prob.q.dtype == np.uint16 else prob.q),
+         "k": torch.from_numpy(prob.k_pool.view(np.int16) if prob.k_pool.dtype == np.uint16 else prob.k_pool)}
+    if t["q"].dtype == torch.int16:
+        t["q"] = t["q"].view(torch.bfloat16)
+    if t["k"].dtype == torch.int16:
+        t["k"] = t["k"].view(torch.bfloat16)
+    if not prob.mla:
+        v = torch.from_numpy(prob.v_pool.view(np.int16) if prob.v_pool.dtype == np.uint16 else prob.v_pool)
+        t["v"] = v.view(torch.bfloat16) if v.dtype == torch.int16 else v
+    t["table"] = torch.from_numpy(prob.block_tables)
+    t["seq_lens"] = torch.from_numpy(prob.seq_lens)
+    t["q_indptr"] = torch.from_numpy(prob.q_indptr)
+    odt = torch.bfloat16 if prob.o_dtype == "bf16" else torch.float32
+    t["out"] = torch.empty((prob.total_q, prob.num_qo_heads, prob.head_dim_v), dtype=odt)
+    t["lse"] = torch.empty((prob.total_q, prob.num_qo_heads), dtype=torch.float32)
+    return t
+
+
+PROBLEMS = [
+    ("bf16 decode HND", lambda: W.make_problem(name="a", seed=1, batch=3, seq_lens=[5, 70, 130], q_lens=[1] * 3,
+                                               num_qo_heads=16, num_kv_heads=2, head_dim_qk=128, head_dim_v=128,
+                                               page_size=32, table_slack_pages=2)),
+    ("e4m3 decode NHD speculative", lambda: W.make_problem(name="b", seed=2, batch=2, seq_lens=[40, 300],
+                                                           q_lens=[2, 2], num_qo_heads=8, num_kv_heads=1,
+                                                           head_dim_qk=128, head_dim_v=128, page_size=16,
+                                                           layout="NHD", kv_dtype=W.E4M3)),
+    ("bf16 context", lambda: W.make_problem(name="c", seed=3, batch=2, seq_lens=[50, 90], q_lens=[7, 33],
+                                            num_qo_heads=8, num_kv_heads=2, head_dim_qk=128, head_dim_v=128,
+                                            page_size=32, is_decode=False)),
+    ("MLA decode", lambda: W.make_problem(name="d", seed=4, batch=2, seq_lens=[70, 33], q_lens=[1, 1],
+                                          num_qo_heads=16, num_kv_heads=1, head_dim_qk=576, head_dim_v=512,
+                                          page_size=64, mla=True, scale=1 / 24.0)),
+]
+
+
+@pytest.mark.parametrize("label,make", PROBLEMS, ids=[p[0] for p in PROBLEMS])
+def test_args_from_tensors_matches_the_field_by_field_args(label, make):
+    prob = make()
+    t = _cpu_tensors(prob)
+    ref = pkv.fill_args(prob, t)
+    ref.lse_out = t["lse"].data_ptr()
+    got = pkv.args_from_tensors(
+        t["q"], t["k"], t.get("v"), t["table"], t["seq_lens"], t["out"], scale=prob.scale,
+        max_kv_len=prob.max_kv_len, layout=prob.layout, q_indptr=None if prob.is_decode else t["q_indptr"],
+        max_q_len=None if prob.is_decode else prob.q_len, causal=prob.causal, k_scale=prob.k_scale,
+        v_scale=prob.v_scale, lse=t["lse"], num_splits=prob.num_splits)
+    if prob.is_decode:
+        ref.q_indptr = 0  # decode calls do not read it
+    for name, _ in pkv.PkvArgs._fields_:
+        assert getattr(got, name) == getattr(ref, name), (label, name, getattr(got, name), getattr(ref, name))
+
+
+def test_args_from_tensors_rejects_what_it_cannot_describe():
+    prob = PROBLEMS[0][1]()
+    t = _cpu_tensors(prob)
+    with pytest.raises(ValueError):
+        pkv.args_from_tensors(t["q"][:, :, ::2], t["k"], t["v"], t["table"], t["seq_lens"], t["out"],
+                              scale=prob.scale, max_kv_len=prob.max_kv_len)
+    with pytest.raises(ValueError):
+        pkv.args_from_tensors(t["q"], t["k"], t["v"], t["table"], t["seq_lens"], t["out"], scale=prob.scale,
+                              max_kv_len=prob.max_kv_len, q_indptr=t["q_indptr"])  # context without max_q_len
+    with pytest.raises(ValueError):
+        pkv.args_from_tensors(t["q"], t["k"], t["v"], t["table"], t["seq_lens"], t["out"], scale=prob.scale,
+                              max_kv_len=prob.max_kv_len, layout="HDN")
+
+
+def test_args_from_tensors_reads_strides_of_views():
+    # a pool whose pages sit 2 pages apart (every other page of a bigger pool) and
+    # an output written into every other head slot of a wider tensor
+    prob = PROBLEMS[0][1]()
+    t = _cpu_tensors(prob)
+    big = torch.zeros((2 * t["k"].shape[0],) + tuple(t["k"].shape[1:]), dtype=t["k"].dtype)
+    kv = big[::2]
+    wide = torch.zeros((prob.total_q, 2 * prob.num_qo_heads, prob.head_dim_v), dtype=t["out"].dtype)
+    out = wide[:, ::2]
+    a = pkv.args_from_tensors(t["q"], kv, kv, t["table"], t["seq_lens"], out, scale=prob.scale,
+                              max_kv_len=prob.max_kv_len)
+    assert a.k_stride_page == 2 * kv.shape[1] * kv.shape[2] * kv.shape[3]
+    assert (a.k_stride_head, a.k_stride_tok) == (kv.shape[2] * kv.shape[3], kv.shape[3])
+    assert (a.o_stride_tok, a.o_stride_head) == (2 * prob.num_qo_heads * prob.head_dim_v, 2 * prob.head_dim_v)
