@@ -465,6 +465,66 @@ def run_tensors(args: PkvArgs, stream=None, workspace=None):
     return workspace
 
 
+def append_args_from_tensors(qkv, cos_sin, q_weight, k_weight, q_indptr, seq_lens, block_tables, out_q, k_cache,
+                             v_cache, *, max_pos: int, norm_policy: int, eps: float, layout: str = "NHD",
+                             clear_tail: bool = True, k_scale: float = 1.0, v_scale: float = 1.0,
+                             q_quant: int = 0, upper_max: float = 448.0, q_scale_inv: float = 1.0, q_scale=None,
+                             q_scale_layout: int = 0, q_scale_stride: int = 0, err=None) -> PkvAppendArgs:
+    """pkv_append_args for caller-owned device tensors (the append producer of
+    include/pkv.h): qkv bf16 [T, (Hq + 2 Hkv) 128] with any token stride;
+    k_cache / v_cache NHD [num_pages, P, Hkv, >= 128] or HND [num_pages, Hkv,
+    P, >= 128] (bf16, or e4m3 codes as uint8 / float8_e4m3fn; channels past 128
+    are padding the producer leaves alone); block_tables int32 [B, pages];
+    q_indptr int32 [B + 1]; seq_lens int32 [B] (lengths after the append);
+    out_q [T, Hq, 128].  Every other field is passed through."""
+    if layout not in ("HND", "NHD"):
+        raise ValueError("layout must be 'HND' or 'NHD'")
+    if qkv.stride(-1) != 1 or k_cache.stride(-1) != 1 or v_cache.stride(-1) != 1:
+        raise ValueError("the channel dimension of qkv and the caches must be contiguous")
+    if tuple(k_cache.shape) != tuple(v_cache.shape):
+        raise ValueError("K and V caches must have the same shape")
+    a = PkvAppendArgs()
+    a.num_tokens = int(qkv.shape[0])
+    a.batch = int(block_tables.shape[0])
+    a.num_qo_heads = int(out_q.shape[1])
+    a.head_dim = 128
+    if layout == "NHD":
+        num_pages, P, Hkv, W_ = (int(x) for x in k_cache.shape)
+    else:
+        num_pages, Hkv, P, W_ = (int(x) for x in k_cache.shape)
+    if W_ < 128:
+        raise ValueError("cache rows need at least 128 channels")
+    a.num_kv_heads, a.page_size, a.num_pages = Hkv, P, num_pages
+    a.max_pages_per_seq = int(block_tables.shape[1])
+    a.table_stride = _stride(block_tables, 0, int(block_tables.shape[1]))
+    a.max_pos = int(max_pos)
+    a.norm_policy = int(norm_policy)
+    a.clear_tail = 1 if clear_tail else 0
+    a.kv_dtype = _dtype_code(k_cache)
+    a.eps, a.k_scale, a.v_scale = float(eps), float(k_scale), float(v_scale)
+    a.qkv = qkv.data_ptr()
+    a.qkv_stride_tok = _stride(qkv, 0, int(qkv.shape[1]))
+    a.cos_sin = cos_sin.data_ptr()
+    a.q_weight, a.k_weight = q_weight.data_ptr(), k_weight.data_ptr()
+    a.q_indptr, a.seq_lens, a.block_tables = q_indptr.data_ptr(), seq_lens.data_ptr(), block_tables.data_ptr()
+    a.out_q, a.k_cache, a.v_cache = out_q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr()
+    a.err_word = err.data_ptr() if err is not None else 0
+    a.q_quant = int(q_quant)
+    a.upper_max, a.q_scale_inv = float(upper_max), float(q_scale_inv)
+    a.q_scale_layout, a.q_scale_stride = int(q_scale_layout), int(q_scale_stride)
+    a.q_scale = q_scale.data_ptr() if q_scale is not None else 0
+    a.layout = PKV_LAYOUT_HND if layout == "HND" else PKV_LAYOUT_NHD
+    for prefix, t in (("k", k_cache), ("v", v_cache)):
+        if layout == "NHD":
+            sp, sh, st = _stride(t, 0, P * Hkv * W_), _stride(t, 2, W_), _stride(t, 1, Hkv * W_)
+        else:
+            sp, sh, st = _stride(t, 0, Hkv * P * W_), _stride(t, 1, P * W_), _stride(t, 2, W_)
+        setattr(a, f"{prefix}_stride_page", sp)
+        setattr(a, f"{prefix}_stride_head", sh)
+        setattr(a, f"{prefix}_stride_tok", st)
+    return a
+
+
 @dataclass
 class DeviceAppend:
     args: PkvAppendArgs

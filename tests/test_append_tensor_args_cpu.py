@@ -1,0 +1,43 @@
+"""Host-only check of the binding's tensor-level marshalling for the append
+producer: pkv_append_args built from caller tensors equals the args the test
+harness builds field by field for the same problem (CPU tensors stand in for
+device ones; only their addresses are taken)."""
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from paged_kv_attention_15_amd import pkv, workloads as W  # noqa: E402
+
+APPEND_PROBLEMS = [
+    ("bf16 NHD decode", lambda: W.make_append_problem(name="a", seed=3, new_lens=[1] * 4, seq_lens=[1, 16, 17, 90],
+                                                      num_qo_heads=16, num_kv_heads=2, page_size=16,
+                                                      norm_policy=2)),
+    ("e4m3 HND padded, dynamic q", lambda: W.make_append_problem(
+        name="b", seed=4, new_lens=[3, 0, 5], seq_lens=[10, 4, 40], num_qo_heads=8, num_kv_heads=1, page_size=32,
+        norm_policy=1, kv_dtype=W.E4M3, k_scale=0.05, v_scale=0.05, q_quant=1, q_scale_layout=1, q_scale_stride=8,
+        layout="HND", cache_pad=64)),
+    ("e4m3 NHD static q", lambda: W.make_append_problem(
+        name="c", seed=5, new_lens=[2, 2], seq_lens=[2, 70], num_qo_heads=8, num_kv_heads=2, page_size=64,
+        norm_policy=0, kv_dtype=W.E4M3, k_scale=0.1, v_scale=0.1, q_quant=2, q_scale_inv=2.0)),
+]
+
+
+def tensor_args(prob, t):
+    """The tensor-level call for a problem whose arrays live in the tensors of `t`."""
+    cache = (lambda x: x.view(torch.bfloat16)) if prob.kv_dtype == W.BF16 else (lambda x: x)
+    return pkv.append_args_from_tensors(
+        t["qkv"].view(torch.bfloat16), t["cos_sin"], t["q_w"].view(torch.bfloat16), t["k_w"].view(torch.bfloat16),
+        t["q_indptr"], t["seq_lens"], t["table"], t["out_q"], cache(t["k_cache"]), cache(t["v_cache"]),
+        max_pos=prob.max_pos, norm_policy=prob.norm_policy, eps=prob.eps, layout=prob.layout,
+        clear_tail=prob.clear_tail, k_scale=prob.k_scale, v_scale=prob.v_scale, q_quant=prob.q_quant,
+        upper_max=prob.upper_max, q_scale_inv=prob.q_scale_inv, q_scale=t.get("q_scale"),
+        q_scale_layout=prob.q_scale_layout, q_scale_stride=prob.q_scale_stride, err=t.get("err"))
+
+
+@pytest.mark.parametrize("label,make", APPEND_PROBLEMS, ids=[p[0] for p in APPEND_PROBLEMS])
+def test_append_args_from_tensors_matches_the_field_by_field_args(label, make):
+    prob = make()
+    da = pkv.upload_append(prob, "cpu")
+    got = tensor_args(prob, da.tensors)
+    for name, _ in pkv.PkvAppendArgs._fields_:
+        assert getattr(got, name) == getattr(da.args, name), (label, name, getattr(got, name), getattr(da.args, name))
