@@ -131,6 +131,14 @@ def _check(status: int) -> int:
     return status
 
 
+def _require_gpu_tensors(args) -> None:
+    """Arguments filled from tensors carry the tensors' device: refuse to
+    launch on pointers that are not device memory (a kernel would fault)."""
+    dev = getattr(args, "_tensor_device", None)
+    if dev is not None and dev.type != "cuda":
+        raise ValueError(f"the tensors behind these arguments are on {dev}, not on a GPU")
+
+
 # ---------------------------------------------------------------- entry points
 
 def pkv_abi_version() -> int:
@@ -160,17 +168,20 @@ PKV_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
 def pkv_decode_noalloc(args: PkvArgs, stream: int, check: bool = True) -> int:
+    _require_gpu_tensors(args)
     st = load_library().pkv_decode_noalloc(C.byref(args), C.c_void_p(stream))
     return _check(st) if check else st
 
 
 def pkv_decode(args: PkvArgs, workspace: int, workspace_bytes: int, stream: int, check: bool = True) -> int:
+    _require_gpu_tensors(args)
     st = load_library().pkv_decode(C.byref(args), C.c_void_p(workspace or None), workspace_bytes,
                                    C.c_void_p(stream or None))
     return _check(st) if check else st
 
 
 def pkv_context(args: PkvArgs, workspace: int, workspace_bytes: int, stream: int, check: bool = True) -> int:
+    _require_gpu_tensors(args)
     st = load_library().pkv_context(C.byref(args), C.c_void_p(workspace or None), workspace_bytes,
                                     C.c_void_p(stream or None))
     return _check(st) if check else st
@@ -189,6 +200,7 @@ def pkv_lse_merge(num_splits: int, num_rows: int, num_qo_heads: int, head_dim_v:
 # ---------------------------------------------------------------- torch marshalling
 
 def pkv_append(args: PkvAppendArgs, stream: int, check: bool = True) -> int:
+    _require_gpu_tensors(args)
     st = load_library().pkv_append(C.byref(args), C.c_void_p(stream or None))
     if check:
         _check(st)
@@ -358,6 +370,18 @@ def _dtype_code(t) -> int:
     raise ValueError(f"unsupported dtype {t.dtype}")
 
 
+def _check_tensors(device, named: dict) -> None:
+    """Every tensor on `device`; (tensor, dtypes) pairs also checked for dtype."""
+    for name, spec in named.items():
+        t, dtypes = spec if isinstance(spec, tuple) else (spec, None)
+        if t is None:
+            continue
+        if t.device != device:
+            raise ValueError(f"{name} is on {t.device}, the query on {device}")
+        if dtypes is not None and t.dtype not in dtypes:
+            raise ValueError(f"{name} must be {' or '.join(str(d) for d in dtypes)}, not {t.dtype}")
+
+
 def _stride(t, dim: int, natural: int) -> int:
     """Element stride of `dim`; a dimension of extent 1 is never stepped, so
     the contiguous value stands in for whatever its stride says."""
@@ -382,6 +406,12 @@ def args_from_tensors(q, k_pages, v_pages, block_tables, seq_lens, out, *, scale
     plan."""
     if layout not in ("HND", "NHD"):
         raise ValueError("layout must be 'HND' or 'NHD'")
+    torch = _torch()
+    i32, f32 = (torch.int32,), (torch.float32,)
+    _check_tensors(q.device, {"k_pages": k_pages, "v_pages": v_pages, "out": out,
+                              "block_tables": (block_tables, i32), "seq_lens": (seq_lens, i32),
+                              "q_indptr": (q_indptr, i32), "v_block_tables": (v_block_tables, i32),
+                              "lse": (lse, f32), "err": (err, i32), "sinks": (sinks, f32)})
     for name, t in (("q", q), ("k_pages", k_pages), ("out", out)) + ((("v_pages", v_pages),) if v_pages is not None else ()):
         if t.stride(-1) != 1:
             raise ValueError(f"{name}: the last (channel) dimension must be contiguous")
@@ -446,6 +476,7 @@ def args_from_tensors(q, k_pages, v_pages, block_tables, seq_lens, out, *, scale
     a.scale, a.k_scale, a.v_scale = float(scale), float(k_scale), float(v_scale)
     if kernel is not None:
         a.kernel_hint = KERNEL_IDS[kernel]
+    a._tensor_device = q.device
     return a
 
 
@@ -454,6 +485,7 @@ def run_tensors(args: PkvArgs, stream=None, workspace=None):
     current stream), with `workspace` (a uint8 device tensor) or one
     allocated here at the size pkv_workspace_bytes asks for.  Returns the
     workspace so that a caller can keep it for the next call."""
+    _require_gpu_tensors(args)
     torch = _torch()
     is_ctx = args.q_len == 0
     need = pkv_workspace_bytes(args, is_ctx)
@@ -479,6 +511,13 @@ def append_args_from_tensors(qkv, cos_sin, q_weight, k_weight, q_indptr, seq_len
     out_q [T, Hq, 128].  Every other field is passed through."""
     if layout not in ("HND", "NHD"):
         raise ValueError("layout must be 'HND' or 'NHD'")
+    torch = _torch()
+    i32, f32, b16 = (torch.int32,), (torch.float32,), (torch.bfloat16, torch.int16)
+    _check_tensors(qkv.device, {"qkv": (qkv, b16), "cos_sin": (cos_sin, f32), "q_weight": (q_weight, b16),
+                                "k_weight": (k_weight, b16), "q_indptr": (q_indptr, i32),
+                                "seq_lens": (seq_lens, i32), "block_tables": (block_tables, i32),
+                                "out_q": out_q, "k_cache": k_cache, "v_cache": v_cache,
+                                "q_scale": (q_scale, f32), "err": (err, i32)})
     if qkv.stride(-1) != 1 or k_cache.stride(-1) != 1 or v_cache.stride(-1) != 1:
         raise ValueError("the channel dimension of qkv and the caches must be contiguous")
     if tuple(k_cache.shape) != tuple(v_cache.shape):
@@ -514,6 +553,7 @@ def append_args_from_tensors(qkv, cos_sin, q_weight, k_weight, q_indptr, seq_len
     a.q_scale_layout, a.q_scale_stride = int(q_scale_layout), int(q_scale_stride)
     a.q_scale = q_scale.data_ptr() if q_scale is not None else 0
     a.layout = PKV_LAYOUT_HND if layout == "HND" else PKV_LAYOUT_NHD
+    a._tensor_device = qkv.device
     for prefix, t in (("k", k_cache), ("v", v_cache)):
         if layout == "NHD":
             sp, sh, st = _stride(t, 0, P * Hkv * W_), _stride(t, 2, W_), _stride(t, 1, Hkv * W_)

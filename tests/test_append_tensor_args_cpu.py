@@ -41,3 +41,19 @@ def test_append_args_from_tensors_matches_the_field_by_field_args(label, make):
     got = tensor_args(prob, da.tensors)
     for name, _ in pkv.PkvAppendArgs._fields_:
         assert getattr(got, name) == getattr(da.args, name), (label, name, getattr(got, name), getattr(da.args, name))
+
+
+def test_append_args_from_tensors_checks_dtypes_and_host_tensors():
+    prob = APPEND_PROBLEMS[0][1]()
+    da = pkv.upload_append(prob, "cpu")
+    t = dict(da.tensors)
+    t["seq_lens"] = t["seq_lens"].long()
+    with pytest.raises(ValueError, match="seq_lens"):
+        tensor_args(prob, t)
+    t = dict(da.tensors)
+    t["cos_sin"] = t["cos_sin"].double()
+    with pytest.raises(ValueError, match="cos_sin"):
+        tensor_args(prob, t)
+    a = tensor_args(prob, da.tensors)
+    with pytest.raises(ValueError, match="not on a GPU"):
+        pkv.pkv_append(a, 0)

@@ -92,3 +92,31 @@ def test_args_from_tensors_reads_strides_of_views():
     assert a.k_stride_page == 2 * kv.shape[1] * kv.shape[2] * kv.shape[3]
     assert (a.k_stride_head, a.k_stride_tok) == (kv.shape[2] * kv.shape[3], kv.shape[3])
     assert (a.o_stride_tok, a.o_stride_head) == (2 * prob.num_qo_heads * prob.head_dim_v, 2 * prob.head_dim_v)
+
+
+def test_args_from_tensors_checks_index_dtypes_and_devices():
+    prob = PROBLEMS[0][1]()
+    t = _cpu_tensors(prob)
+    kw = dict(scale=prob.scale, max_kv_len=prob.max_kv_len)
+    with pytest.raises(ValueError, match="seq_lens"):  # 64-bit lengths would be read as pairs of 32-bit words
+        pkv.args_from_tensors(t["q"], t["k"], t["v"], t["table"], t["seq_lens"].long(), t["out"], **kw)
+    with pytest.raises(ValueError, match="block_tables"):
+        pkv.args_from_tensors(t["q"], t["k"], t["v"], t["table"].long(), t["seq_lens"], t["out"], **kw)
+    with pytest.raises(ValueError, match="lse"):
+        pkv.args_from_tensors(t["q"], t["k"], t["v"], t["table"], t["seq_lens"], t["out"],
+                              lse=t["lse"].double(), **kw)
+    with pytest.raises(ValueError, match="k_pages"):  # every tensor on the query's device
+        pkv.args_from_tensors(t["q"], t["k"].to("meta"), t["v"], t["table"], t["seq_lens"], t["out"], **kw)
+
+
+def test_args_from_host_tensors_are_never_launched():
+    # host addresses in pkv_args would fault a kernel: the wrappers refuse them
+    # before the library is called
+    prob = PROBLEMS[0][1]()
+    t = _cpu_tensors(prob)
+    a = pkv.args_from_tensors(t["q"], t["k"], t["v"], t["table"], t["seq_lens"], t["out"], scale=prob.scale,
+                              max_kv_len=prob.max_kv_len)
+    for call in (lambda: pkv.pkv_decode(a, 0, 0, 0), lambda: pkv.pkv_context(a, 0, 0, 0),
+                 lambda: pkv.pkv_decode_noalloc(a, 0), lambda: pkv.run_tensors(a, stream=object())):
+        with pytest.raises(ValueError, match="not on a GPU"):
+            call()
