@@ -167,11 +167,10 @@ typedef struct pkv_args {
   /* Optional separate V page table [B, table_stride] (flashinfer.cake_fmha API
      page: a context profile with separate K/V page tables): value j of request
      b is read from page v_block_tables[b][j / P].  NULL: V shares block_tables.
-     Served by the families that keep a second page list: the register-staged
-     tiles (gqa_*, wide_*), the 32x32 context kernels (m32_ctx_*) and the
-     generic kernel, never by the balanced schedule; a kernel_hint of a
-     direct-to-LDS ring family (dma_*) or an MLA family returns
-     PKV_ERR_UNSUPPORTED.  Page indices are clamped and flagged like K's. */
+     Served by every D = 128 family (each keeps a second page list beside
+     the K list, also on the balanced schedule) and the generic kernel; a
+     kernel_hint of an MLA family returns PKV_ERR_UNSUPPORTED (its V rows are
+     the K rows).  Page indices are clamped and flagged like K's. */
   const int32_t* v_block_tables;
 
   int64_t q_stride_tok, q_stride_head;

@@ -176,13 +176,12 @@ bool mfma_eligible(const pkv_args* a) {
 bool kernel_supports(int32_t k, const pkv_args* a, bool is_context) {
   if (k == pkv::KERNEL_GENERIC) return a->head_dim_qk <= 1024 && a->head_dim_v <= 512;
   if (k <= pkv::KERNEL_GENERIC || k >= pkv::KERNEL_COUNT || !mfma_eligible(a)) return false;
-  // separate V tables: the register-staged families and the 32x32 context
-  // kernel keep a second page list; the direct-to-LDS ring families and the
-  // MLA kernels (whose V rows are the K rows) do not
+  // separate V tables: every D = 128 family keeps a second page list; the MLA
+  // kernels read V from the K rows and take none
   pkv::MfmaShape ring;
   const bool ring_family = pkv::dma_shape(k, &ring);
-  if (a->v_block_tables &&
-      (ring_family || k == pkv::KERNEL_MLA_BF16 || k == pkv::KERNEL_MLA_FP8 || k == pkv::KERNEL_MLA32_BF16))
+  if (a->v_block_tables && (k == pkv::KERNEL_MLA_BF16 || k == pkv::KERNEL_MLA_FP8 || k == pkv::KERNEL_MLA32_BF16 ||
+                            k == pkv::KERNEL_DMA_MLA_BF16 || k == pkv::KERNEL_DMA_MLA_FP8))
     return false;
   // the direct-to-LDS ring loaders form a page's address as a 64-bit base
   // plus a 32-bit product and offset: pages of 4 GiB or more go elsewhere
@@ -253,14 +252,6 @@ int32_t preferred_kernel(const pkv_args* a, bool is_context) {
   if (!mfma_eligible(a)) return pkv::KERNEL_GENERIC;
   const bool fp8 = a->kv_dtype == PKV_DTYPE_FP8_E4M3;
   const int G = a->num_qo_heads / a->num_kv_heads;
-  if (a->v_block_tables) {
-    // separate V tables: the families that keep a second page list
-    if (a->head_dim_qk != 128 || a->head_dim_v != 128 || a->v_shares_k) return pkv::KERNEL_GENERIC;
-    const int64_t rows = is_context ? (int64_t)a->max_q_len * G : (int64_t)a->q_len * G;
-    if (!is_context && rows <= 16) return fp8 ? pkv::KERNEL_GQA_FP8 : pkv::KERNEL_GQA_BF16;
-    if (is_context && !fp8) return pkv::KERNEL_M32_CTX_W8T128;
-    return fp8 ? pkv::KERNEL_WIDE_FP8 : pkv::KERNEL_WIDE_BF16;
-  }
   // Measured on MI355X (bf16 GQA decode B32/L4096, e4m3 ragged decode B16, MLA
   // B512/L4096, causal context B4 q511/L2047): register-staged tiles win for
   // bf16 decode, the direct-to-LDS ring for e4m3 decode (two-wave groups, four
@@ -336,12 +327,11 @@ pkv_status make_plan(const pkv_args* a, bool is_context, int num_cus, pkv_plan_i
   // Balanced decode schedule (GQA families, rows of a KV head in one block):
   // used when the units cannot fill the CUs, or on request (num_splits == -1).
   const bool gqa = is_gqa_family(kernel);
-  if (a->num_splits == -1 || (a->num_splits == 0 && gqa && units < num_cus && !a->v_block_tables)) {
+  if (a->num_splits == -1 || (a->num_splits == 0 && gqa && units < num_cus)) {
     if (!gqa || is_context)
       return fail(PKV_ERR_UNSUPPORTED, "the balanced schedule needs a GQA decode kernel family");
-    if (a->v_block_tables)
-      return fail(PKV_ERR_UNSUPPORTED, "the balanced schedule keeps one page list: no separate V tables");
-    const int64_t extra = (int64_t)a->max_pages_per_seq + a->batch + 2 + 3;  // page list, prefix, flag
+    // page list (and the V list), prefix, flag
+    const int64_t extra = (int64_t)a->max_pages_per_seq * (a->v_block_tables ? 2 : 1) + a->batch + 2 + 3;
     const int64_t lds = (int64_t)shp.lds_static + extra * 4;
     if (lds > 160 * 1024) {
       if (a->num_splits == -1) return fail(PKV_ERR_UNSUPPORTED, "balanced schedule: page table too wide for LDS");

@@ -165,6 +165,9 @@ __device__ __forceinline__ void dma_block(const KParams& p, unsigned char* smem,
 
   const int pg_lo = kv_lo >> p.log2_page;
   const int n_pg = n_tiles > 0 ? ((kv_hi - 1) >> p.log2_page) - pg_lo + 1 : 0;
+  // a separate V table (API page, separate K/V page tables) gets its own list
+  // right after the K list
+  int32_t* s_vpages = p.v_table ? s_pages + p.page_list_cap : s_pages;
   for (int i = tid; i < n_pg; i += C::NTHR) {
     int pg = p.table[(int64_t)b * p.table_stride + pg_lo + i];
     if (p.num_pages > 0 && (pg < 0 || pg >= p.num_pages)) {
@@ -172,6 +175,14 @@ __device__ __forceinline__ void dma_block(const KParams& p, unsigned char* smem,
       pg = min(max(pg, 0), p.num_pages - 1);
     }
     s_pages[i] = pg;
+    if (p.v_table) {
+      int vpg = p.v_table[(int64_t)b * p.table_stride + pg_lo + i];
+      if (p.num_pages > 0 && (vpg < 0 || vpg >= p.num_pages)) {
+        flag_error(p.err_word, PKV_DEVERR_PAGE_RANGE);
+        vpg = min(max(vpg, 0), p.num_pages - 1);
+      }
+      s_vpages[i] = vpg;
+    }
   }
 
   const float k_scale = p.k_scale_dev ? *p.k_scale_dev : p.k_scale;
@@ -265,8 +276,10 @@ __device__ __forceinline__ void dma_block(const KParams& p, unsigned char* smem,
     int pg[C::KPW];
 #pragma unroll
     for (int q = 0; q < C::KPW; ++q) {
+      const int I = min(wave * C::KPW + q, C::NI - 1);
       const int tok = min(tok0 + q_row[q], kv_hi - 1);
-      pg[q] = s_pages[(tok >> p.log2_page) - pg_lo];  // all page lookups first: one LDS round trip
+      const int32_t* list = I * 64 < C::KCH ? s_pages : s_vpages;  // wave-uniform: K or V chunks
+      pg[q] = list[(tok >> p.log2_page) - pg_lo];  // all page lookups first: one LDS round trip
     }
 #pragma unroll
     for (int q = 0; q < C::KPW; ++q) {
@@ -712,7 +725,8 @@ template <class C>
 __global__ __launch_bounds__(C::NTHR) void attn_dma_stream_kernel(const KParams p) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   int32_t* s_pages = (int32_t*)(smem + C::LDS);
-  int32_t* s_pfx = s_pages + p.page_list_cap;  // [B + 1] page prefix, then the reducer's flag word
+  // [B + 1] page prefix, then the reducer's flag word, after the page list(s)
+  int32_t* s_pfx = s_pages + p.page_list_cap * (p.v_table ? 2 : 1);
   int* s_flag = s_pfx + p.batch + 1;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -839,7 +853,7 @@ bool dma_shape(int32_t kernel, MfmaShape* s) {
 template <class C>
 static hipError_t launch_dma_cfg(const KParams& p, hipStream_t s) {
   static bool attr_done = false;  // idempotent; a race only repeats the same calls
-  const size_t extra = (size_t)p.page_list_cap + (p.stream ? (size_t)p.batch + 2 : 0);
+  const size_t extra = (size_t)p.page_list_cap * (p.v_table ? 2 : 1) + (p.stream ? (size_t)p.batch + 2 : 0);
   const size_t lds = C::LDS + ((extra + 3) & ~size_t(3)) * sizeof(int32_t);
   if (!attr_done) {
     hipError_t e = hipFuncSetAttribute((const void*)attn_dma_kernel<C>,

@@ -514,7 +514,8 @@ template <class C>
 __global__ __launch_bounds__(C::NTHR) void attn_mfma_stream_kernel(const KParams p) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   int32_t* s_pages = (int32_t*)(smem + C::LDS);
-  int32_t* s_pfx = s_pages + p.page_list_cap;  // [batch + 1] page prefix over requests
+  // [batch + 1] page prefix over requests, after the page list(s)
+  int32_t* s_pfx = s_pages + p.page_list_cap * (p.v_table ? 2 : 1);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int B = p.batch;
@@ -602,7 +603,6 @@ bool mfma_shape(int32_t kernel, MfmaShape* s) {
 template <class C>
 static hipError_t launch_cfg(const KParams& p, hipStream_t s) {
   static bool attr_done = false;  // idempotent; a race only repeats the same calls
-  if (p.stream && p.v_table) return hipErrorInvalidValue;  // the balanced schedule keeps one page list
   const size_t extra = (size_t)p.page_list_cap * (p.v_table ? 2 : 1) + (p.stream ? (size_t)p.batch + 1 : 0);
   const size_t lds = C::LDS + ((extra + 3) & ~size_t(3)) * sizeof(int32_t);
   if (!attr_done) {

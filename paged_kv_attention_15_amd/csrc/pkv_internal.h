@@ -73,7 +73,7 @@ struct KParams {
   // (request, KV head); null selects the separate reducer kernel
   int32_t* counters;
   const float* sinks;      // [num_qo_heads] sink logits, or null
-  const int32_t* v_table;  // separate V page table (generic kernel only), or null
+  const int32_t* v_table;  // separate V page table, or null (V pages then come from `table`)
 };
 
 struct LaunchShape {

@@ -350,24 +350,45 @@ def test_append_e4m3_needs_scales_and_empty_calls_are_noops():
     assert pkv.pkv_append(_append_args(num_tokens=0, clear_tail=0), 0, check=False) == pkv.PKV_OK
 
 
-def test_separate_value_tables_route_to_families_with_a_second_page_list():
+def test_separate_value_tables_are_served_by_every_d128_family():
+    # every D = 128 family keeps a second page list: a separate V table changes
+    # neither the kernel nor the schedule the planner picks, on either dtype
+    for kv in (pkv.PKV_DTYPE_BF16, pkv.PKV_DTYPE_FP8_E4M3):
+        a = _args_for(_fake())
+        a.q = a.k_pages = a.v_pages = a.out = 0x1000
+        a.kv_dtype = kv
+        shared = pkv.pkv_plan(a)
+        a.v_block_tables = 0x2000
+        sep = pkv.pkv_plan(a)
+        assert (sep.kernel, sep.schedule, sep.num_splits) == (shared.kernel, shared.schedule, shared.num_splits)
+        if kv == pkv.PKV_DTYPE_FP8_E4M3:
+            assert pkv.KERNEL_NAMES[sep.kernel] == "dma_gqa_fp8_n2" and sep.schedule == 1
+        a.num_splits = -1  # the balanced schedule on request
+        assert pkv.pkv_plan(a).schedule == 1
+        a.num_splits = 0
     a = _args_for(_fake())
     a.q = a.k_pages = a.v_pages = a.out = 0x1000
     a.v_block_tables = 0x2000
-    plan = pkv.pkv_plan(a)
-    assert pkv.KERNEL_NAMES[plan.kernel] == "gqa_bf16" and plan.schedule == 0  # never the balanced schedule
-    for name in ("dma_wide_bf16", "dma_wide_fp8"):  # the direct-to-LDS ring keeps one list
+    for name in ("dma_wide_bf16", "gqa_bf16", "wide_bf16", "generic"):
         a.kernel_hint = pkv.KERNEL_IDS[name]
-        assert pkv.pkv_plan(a, check=False).status == pkv.PKV_ERR_UNSUPPORTED
+        assert pkv.pkv_plan(a).kernel == a.kernel_hint
     a.kernel_hint = 0
-    a.num_splits = -1
-    assert pkv.pkv_plan(a, check=False).status == pkv.PKV_ERR_UNSUPPORTED
-    a.num_splits = 0
-    a.v_shares_k = 1
+    a.v_shares_k = 1  # V rows that are the K rows take no V table
     assert pkv.pkv_plan(a, check=False).status == pkv.PKV_ERR_INVALID_ARG
     a.v_shares_k = 0
     a.sinks = 0x2002
     assert pkv.pkv_plan(a, check=False).status == pkv.PKV_ERR_INVALID_ARG
+
+
+def test_mla_kernels_take_no_value_table():
+    a = _args_for(W.mla_b512_kv4096(batch=2, seq_len=64))
+    a.q = a.k_pages = a.out = 0x1000
+    a.v_shares_k = 0
+    a.v_pages = 0x1000
+    a.v_block_tables = 0x2000
+    for name in ("mla32_bf16", "dma_mla_bf16", "mla_bf16"):
+        a.kernel_hint = pkv.KERNEL_IDS[name]
+        assert pkv.pkv_plan(a, check=False).status == pkv.PKV_ERR_UNSUPPORTED, name
 
 
 def test_noalloc_refuses_a_plan_beyond_its_static_scratch():

@@ -152,6 +152,26 @@ def test_fused_merge_speculative_rows_and_empty_request():
     _fused_runs(prob, "dma_gqa_fp8_n2", expect_err=pkv.PKV_DEVERR_SEQ_LT_QLEN)
 
 
+def test_fused_merge_separate_value_tables():
+    prob = _gqa([1, 31, 64, 65, 700, 1300], hq=64, hkv=8, P=64, kv=W.E4M3, separate_v_table=True, seed=5)
+    say("case fused merge with separate V tables")
+    _fused_runs(prob, "dma_gqa_fp8_n2")
+
+
+def test_fp8_ragged_full_size_separate_value_tables():
+    # the e4m3 benchmark workload's shape with its V pages behind a table of their own
+    lens = W.ragged_log_uniform_lens(np.random.default_rng(0), 16, 512, 32768)
+    prob = W.make_problem(name="fp8-gqa-b16-ragged-vtab", seed=0, batch=16, seq_lens=lens, q_lens=[1] * 16,
+                          num_qo_heads=64,
+                          num_kv_heads=8, head_dim_qk=128, head_dim_v=128, page_size=64, kv_dtype=W.E4M3,
+                          q_dtype=W.BF16, o_dtype=W.BF16, separate_v_table=True)
+    dp = run_gpu(prob)
+    plan = pkv.pkv_plan(dp.args)
+    say(f"case {prob.name}: kernel={pkv.KERNEL_NAMES[plan.kernel]} schedule={plan.schedule}")
+    assert pkv.KERNEL_NAMES[plan.kernel] == "dma_gqa_fp8_n2" and plan.schedule == 1
+    compare(prob, dp, sample_pairs(prob, 96))
+
+
 def test_fused_merge_full_size_fp8():
     prob = W.gqa_fp8_b16_ragged()
     say(f"case {prob.name} fused merge (sampled)")
@@ -400,20 +420,26 @@ def test_sinks_mla(q_len):
     compare(prob, run_gpu(prob))
 
 
-# separate V page tables: the planner's choice per shape (register-staged
-# tiles for decode, the 32x32 kernel for bf16 context, the wide tiles for e4m3
-# context), forced split partitions, and the other families that keep a second
-# page list
+# separate V page tables: the planner's choice per shape (the same as with a
+# shared table: register-staged tiles for bf16 decode, the direct-to-LDS ring
+# on the balanced schedule for e4m3 decode, the 32x32 kernel for bf16
+# context, the ring's wide tiles for e4m3 context), forced split partitions
+# and the balanced schedule on request, and the other families
 @pytest.mark.parametrize("decode,kv,kernel,splits,expect", [
     (True, W.BF16, None, None, "gqa_bf16"),
-    (True, W.E4M3, None, None, "gqa_fp8"),
+    (True, W.E4M3, None, None, "dma_gqa_fp8_n2"),
     (True, W.BF16, None, 3, "gqa_bf16"),
+    (True, W.BF16, None, -1, "gqa_bf16"),
     (True, W.BF16, "generic", None, "generic"),
     (True, W.E4M3, "gqa_fp8", 2, "gqa_fp8"),
+    (True, W.E4M3, "gqa_fp8", -1, "gqa_fp8"),
+    (True, W.E4M3, "dma_gqa_fp8_n2", 3, "dma_gqa_fp8_n2"),
     (False, W.BF16, None, None, "m32_ctx_w8t128"),
     (False, W.BF16, "m32_ctx_w8t128", 3, "m32_ctx_w8t128"),
-    (False, W.E4M3, None, None, "wide_fp8"),
+    (False, W.E4M3, None, None, "dma_wide_fp8"),
+    (False, W.E4M3, "wide_fp8", None, "wide_fp8"),
     (False, W.BF16, "wide_bf16", None, "wide_bf16"),
+    (False, W.BF16, "dma_wide_bf16", 2, "dma_wide_bf16"),
     (False, W.BF16, "generic", None, "generic"),
 ])
 def test_separate_value_tables(decode, kv, kernel, splits, expect):
