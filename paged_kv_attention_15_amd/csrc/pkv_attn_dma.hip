@@ -111,7 +111,11 @@ __device__ __forceinline__ float ld_coherent(const float* ptr) {
   return __hip_atomic_load(const_cast<float*>(ptr), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <class C>
+// VT: the call has a separate V page table (a second page list after the K
+// list).  A template parameter rather than a test of p.v_table: the list
+// choice in the loader otherwise costs scalar registers the shared-table form
+// spills (about 3 % of the e4m3 decode).
+template <class C, bool VT = false>
 __device__ __forceinline__ void dma_block(const KParams& p, unsigned char* smem, int32_t* s_pages, const int b,
                                           const int g, const int rb, const int part_lo, const int part_hi,
                                           const int slot, const bool lead, const bool direct = false) {
@@ -167,7 +171,7 @@ __device__ __forceinline__ void dma_block(const KParams& p, unsigned char* smem,
   const int n_pg = n_tiles > 0 ? ((kv_hi - 1) >> p.log2_page) - pg_lo + 1 : 0;
   // a separate V table (API page, separate K/V page tables) gets its own list
   // right after the K list
-  int32_t* s_vpages = p.v_table ? s_pages + p.page_list_cap : s_pages;
+  int32_t* s_vpages = VT ? s_pages + p.page_list_cap : s_pages;
   for (int i = tid; i < n_pg; i += C::NTHR) {
     int pg = p.table[(int64_t)b * p.table_stride + pg_lo + i];
     if (p.num_pages > 0 && (pg < 0 || pg >= p.num_pages)) {
@@ -175,7 +179,7 @@ __device__ __forceinline__ void dma_block(const KParams& p, unsigned char* smem,
       pg = min(max(pg, 0), p.num_pages - 1);
     }
     s_pages[i] = pg;
-    if (p.v_table) {
+    if constexpr (VT) {
       int vpg = p.v_table[(int64_t)b * p.table_stride + pg_lo + i];
       if (p.num_pages > 0 && (vpg < 0 || vpg >= p.num_pages)) {
         flag_error(p.err_word, PKV_DEVERR_PAGE_RANGE);
@@ -278,7 +282,7 @@ __device__ __forceinline__ void dma_block(const KParams& p, unsigned char* smem,
     for (int q = 0; q < C::KPW; ++q) {
       const int I = min(wave * C::KPW + q, C::NI - 1);
       const int tok = min(tok0 + q_row[q], kv_hi - 1);
-      const int32_t* list = I * 64 < C::KCH ? s_pages : s_vpages;  // wave-uniform: K or V chunks
+      const int32_t* list = (VT && I * 64 >= C::KCH) ? s_vpages : s_pages;  // wave-uniform: K or V chunks
       pg[q] = list[(tok >> p.log2_page) - pg_lo];  // all page lookups first: one LDS round trip
     }
 #pragma unroll
@@ -582,7 +586,7 @@ __device__ __forceinline__ void dma_block(const KParams& p, unsigned char* smem,
 // memory and again from that XCD's L2, not twice from memory (measured on the
 // MLA decode with two speculative rows: 4.98 GB fetched per call before, 2.57
 // GB after, for 2.42 GB of KV).
-template <class C>
+template <class C, bool VT>
 __global__ __launch_bounds__(C::NTHR) void attn_dma_kernel(const KParams p) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   int32_t* s_pages = (int32_t*)(smem + C::LDS);
@@ -594,8 +598,8 @@ __global__ __launch_bounds__(C::NTHR) void attn_dma_kernel(const KParams p) {
   const int y = (int)((Lg / nx) % ny);
   const int z = (int)(Lg / ((int64_t)nx * ny));
   const int span = p.pages_per_split * p.page_size;
-  dma_block<C>(p, smem, s_pages, z, y / p.row_blocks, y % p.row_blocks, split * span, split * span + span, split,
-               split == 0);
+  dma_block<C, VT>(p, smem, s_pages, z, y / p.row_blocks, y % p.row_blocks, split * span, split * span + span,
+                   split, split == 0);
 }
 
 // Fused reducer of the balanced schedule.  Unit u = (request b, KV head g) owns
@@ -721,12 +725,12 @@ __device__ __forceinline__ void stream_arrive(const KParams& p, unsigned char* s
 }
 
 // Balanced schedule (see attn_mfma_stream_kernel): equal global page ranges per workgroup.
-template <class C>
+template <class C, bool VT>
 __global__ __launch_bounds__(C::NTHR) void attn_dma_stream_kernel(const KParams p) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   int32_t* s_pages = (int32_t*)(smem + C::LDS);
   // [B + 1] page prefix, then the reducer's flag word, after the page list(s)
-  int32_t* s_pfx = s_pages + p.page_list_cap * (p.v_table ? 2 : 1);
+  int32_t* s_pfx = s_pages + p.page_list_cap * (VT ? 2 : 1);
   int* s_flag = s_pfx + p.batch + 1;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -801,7 +805,7 @@ __global__ __launch_bounds__(C::NTHR) void attn_dma_stream_kernel(const KParams 
     if (seg_lo < seg_hi) {
       const int a = (int)(seg_lo - rs), e = (int)(seg_hi - rs);
       const bool whole = fused && a == 0 && e == npg;  // sole owner: final rows straight from the epilogue
-      dma_block<C>(p, smem, s_pages, b, g, 0, a * p.page_size, e * p.page_size, (int)(w + b * Hkv + g), a == 0,
+      dma_block<C, VT>(p, smem, s_pages, b, g, 0, a * p.page_size, e * p.page_size, (int)(w + b * Hkv + g), a == 0,
                    whole);
       if (fused && !whole) {
         StreamUnit su;
@@ -850,27 +854,37 @@ bool dma_shape(int32_t kernel, MfmaShape* s) {
   }
 }
 
-template <class C>
-static hipError_t launch_dma_cfg(const KParams& p, hipStream_t s) {
+template <class C, bool VT>
+static hipError_t launch_dma_form(const KParams& p, hipStream_t s) {
   static bool attr_done = false;  // idempotent; a race only repeats the same calls
-  const size_t extra = (size_t)p.page_list_cap * (p.v_table ? 2 : 1) + (p.stream ? (size_t)p.batch + 2 : 0);
+  const size_t extra = (size_t)p.page_list_cap * (VT ? 2 : 1) + (p.stream ? (size_t)p.batch + 2 : 0);
   const size_t lds = C::LDS + ((extra + 3) & ~size_t(3)) * sizeof(int32_t);
   if (!attr_done) {
-    hipError_t e = hipFuncSetAttribute((const void*)attn_dma_kernel<C>,
+    hipError_t e = hipFuncSetAttribute((const void*)attn_dma_kernel<C, VT>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (e != hipSuccess) return e;
-    e = hipFuncSetAttribute((const void*)attn_dma_stream_kernel<C>, hipFuncAttributeMaxDynamicSharedMemorySize,
+    e = hipFuncSetAttribute((const void*)attn_dma_stream_kernel<C, VT>, hipFuncAttributeMaxDynamicSharedMemorySize,
                             160 * 1024);
     if (e != hipSuccess) return e;
     attr_done = true;
   }
   if (p.stream) {
-    hipLaunchKernelGGL(attn_dma_stream_kernel<C>, dim3(p.num_wg), dim3(C::NTHR), lds, s, p);
+    hipLaunchKernelGGL((attn_dma_stream_kernel<C, VT>), dim3(p.num_wg), dim3(C::NTHR), lds, s, p);
   } else {
     dim3 grid(p.num_splits, p.num_kv_heads * p.row_blocks, p.batch);
-    hipLaunchKernelGGL(attn_dma_kernel<C>, grid, dim3(C::NTHR), lds, s, p);
+    hipLaunchKernelGGL((attn_dma_kernel<C, VT>), grid, dim3(C::NTHR), lds, s, p);
   }
   return hipGetLastError();
+}
+
+template <class C>
+static hipError_t launch_dma_cfg(const KParams& p, hipStream_t s) {
+  if (!p.v_table) return launch_dma_form<C, false>(p, s);
+  if constexpr (C::VSHARE) {
+    return hipErrorInvalidValue;  // V rows are the K rows: the planner never sends a V table here
+  } else {
+    return launch_dma_form<C, true>(p, s);
+  }
 }
 
 hipError_t launch_dma(int32_t kernel, const KParams& p, hipStream_t s) {
