@@ -36,3 +36,19 @@ def test_tensor_entry_matches_the_harness_path(label, make):
     assert torch.equal(out.view(torch.int16) if out.dtype == torch.bfloat16 else out,
                        ref_o.view(torch.int16) if ref_o.dtype == torch.bfloat16 else ref_o)
     assert torch.equal(lse, ref_l)
+
+
+@pytest.mark.gpu
+def test_tensor_entry_refuses_host_tensors_beside_device_ones():
+    # a host seq_lens beside device tensors would be read by a kernel through a
+    # host address: refused on the host, before any launch
+    prob = PROBLEMS[0][1]()
+    dp = pkv.upload(prob, "cuda", with_lse=False, with_err=False)
+    t = dp.tensors
+    out = torch.empty_like(dp.out)
+    with pytest.raises(ValueError, match="seq_lens"):
+        pkv.args_from_tensors(t["q"], t["k"], t.get("v"), t["table"], t["seq_lens"].cpu(), out, scale=prob.scale,
+                              max_kv_len=prob.max_kv_len, layout=prob.layout)
+    with pytest.raises(ValueError, match="block_tables"):
+        pkv.args_from_tensors(t["q"], t["k"], t.get("v"), t["table"].long(), t["seq_lens"], out, scale=prob.scale,
+                              max_kv_len=prob.max_kv_len, layout=prob.layout)
