@@ -63,8 +63,11 @@ constexpr int NI = BK + BK * ROPEB / 1024;  // 36 wave-instructions fill a stage
 constexpr int KPW = NI / NW;      // 9 per wave
 constexpr int NS = 4;             // ring stages
 constexpr int LDS = NS * STAGE;   // 144 KiB
+// Read-ahead of the operand rings: 3 measured about 1 % faster than 4 at one
+// query row (B512 L4096 q=1, four alternating pairs on one box; two query rows
+// unchanged), and 5 or 6 no faster than 4 (the chip is at its power limit)
 #ifndef PKV_MLA_PD
-#define PKV_MLA_PD 4
+#define PKV_MLA_PD 3
 #endif
 #ifndef PKV_MLA_PDV
 #define PKV_MLA_PDV PKV_MLA_PD
