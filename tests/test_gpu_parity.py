@@ -394,6 +394,28 @@ def test_sinks_decode(kernel, kv, splits, counters):
     compare(prob, dp, label=f"sinks {kernel}/{splits}/{counters}")
 
 
+# every contract option of a decode call at once: speculative rows (one
+# request with fewer keys than rows), sinks, a separate V table, NaN-poisoned
+# page tails and spare pages, on the balanced schedule with either reducer
+@pytest.mark.parametrize("kernel,kv,counters", [
+    ("dma_gqa_fp8_n2", W.E4M3, False), ("dma_gqa_fp8_n2", W.E4M3, True), ("gqa_bf16", W.BF16, False),
+    ("gqa_fp8", W.E4M3, False),
+])
+def test_decode_with_every_option_on_the_balanced_schedule(kernel, kv, counters):
+    prob = _gqa([1, 300, 77, 1300, 64], q_lens=[2] * 5, hq=16, hkv=2, P=64 if kv == W.E4M3 else 32, kv=kv,
+                sinks=True, separate_v_table=True, seed=9)
+    say(f"case every option {kernel} counters={counters}")
+    dp = pkv.upload(prob, "cuda", num_splits=-1, kernel=kernel, merge_counters=counters)
+    assert pkv.pkv_plan(dp.args).schedule == 1
+    for r in range(2 if counters else 1):
+        dp.tensors["out"].fill_(float("nan"))
+        dp.run()
+        torch.cuda.synchronize()
+        compare(prob, dp, label=f"every option {kernel}/{counters} run {r}", expect_err=pkv.PKV_DEVERR_SEQ_LT_QLEN)
+        if counters:
+            assert int(dp.tensors["counters"].abs().sum().item()) == 0
+
+
 def test_sinks_speculative_rows_with_an_empty_row():
     # request 0 has 3 rows over 2 keys: its first row sees no key and reports lse = sink
     prob = _gqa([2, 300, 77], q_lens=[3, 3, 3], hq=16, hkv=4, sinks=True)
