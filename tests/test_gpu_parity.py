@@ -244,6 +244,24 @@ def test_mla32_split_partitions(kernel, splits):
     compare(prob, dp, label=f"{kernel}/{splits}")
 
 
+# every context option at once: ragged rows (one request whose rows exceed its
+# keys, one with a single row), sinks, a separate V table, poisoned pages, NHD
+@pytest.mark.parametrize("kernel,kv,splits,layout", [
+    (None, W.BF16, None, W.HND), ("m32_ctx_w8t128", W.BF16, 3, W.NHD), ("dma_wide_fp8", W.E4M3, 2, W.HND),
+    ("wide_bf16", W.BF16, None, W.NHD),
+])
+def test_context_with_every_option(kernel, kv, splits, layout):
+    prob = W.make_problem(name="ctx-every", seed=21, batch=4, seq_lens=[70, 5, 333, 1], q_lens=[64, 7, 130, 1],
+                          num_qo_heads=16, num_kv_heads=2, head_dim_qk=128, head_dim_v=128, page_size=16,
+                          kv_dtype=kv, q_dtype=W.BF16, o_dtype=W.BF16, layout=layout, is_decode=False, poison=True,
+                          extra_page_frac=0.3, table_slack_pages=1, sinks=True, separate_v_table=True)
+    say(f"case every context option {kernel} {kv} splits={splits} {layout}")
+    dp = pkv.upload(prob, "cuda", kernel=kernel, num_splits=splits)
+    dp.run()
+    torch.cuda.synchronize()
+    compare(prob, dp, label=f"ctx every option {kernel}/{kv}/{splits}/{layout}", expect_err=pkv.PKV_DEVERR_SEQ_LT_QLEN)
+
+
 @pytest.mark.parametrize("q_len", [1, 2])
 def test_mla_full_size(q_len):
     prob = W.mla_b512_kv4096(q_len=q_len)
