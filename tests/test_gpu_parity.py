@@ -460,6 +460,23 @@ def test_sinks_mla(q_len):
     compare(prob, run_gpu(prob))
 
 
+# every MLA option at once: two speculative rows with a request shorter than
+# them, sinks, poisoned pages, Split-KV partitions, on each MLA family
+@pytest.mark.parametrize("kernel,kv,splits", [
+    ("mla32_bf16", W.BF16, 3), ("mla32_bf16", W.BF16, None), ("dma_mla_bf16", W.BF16, 2), ("dma_mla_fp8", W.E4M3, 3),
+])
+def test_mla_with_every_option(kernel, kv, splits):
+    prob = W.make_problem(name="mla-every", seed=23, batch=4, seq_lens=[1, 70, 300, 129], q_lens=[2] * 4,
+                          num_qo_heads=128, num_kv_heads=1, head_dim_qk=576, head_dim_v=512, page_size=64,
+                          kv_dtype=kv, mla=True, scale=1 / 24.0, poison=True, extra_page_frac=0.3,
+                          table_slack_pages=1, sinks=True)
+    say(f"case every MLA option {kernel} {kv} splits={splits}")
+    dp = pkv.upload(prob, "cuda", kernel=kernel, num_splits=splits)
+    dp.run()
+    torch.cuda.synchronize()
+    compare(prob, dp, label=f"mla every option {kernel}/{kv}/{splits}", expect_err=pkv.PKV_DEVERR_SEQ_LT_QLEN)
+
+
 # separate V page tables: the planner's choice per shape (the same as with a
 # shared table: register-staged tiles for bf16 decode, the direct-to-LDS ring
 # on the balanced schedule for e4m3 decode, the 32x32 kernel for bf16
